@@ -1,0 +1,83 @@
+"""Seeded synthetic weight matrices for the tests and the benchmark.
+
+This module only draws inputs. It holds none of the quantizer's arithmetic and is the one piece of code
+that the oracle's tests and the GPU path's tests share. Everything is generated on the host with numpy's
+PCG64 generator keyed by (seed, matrix id, stream), so a given call returns the same bytes on every
+machine with this numpy.
+
+bf16 matrices are returned as ``uint16`` arrays of bf16 bit patterns (binary64 draw -> binary32 ->
+bf16, each step round-to-nearest-even); fp32 matrices as ``float32``.
+
+Workloads (weights of real models are not available; these stand in for them):
+  * ``c1``: 256 x 1024 fp32, i.i.d. N(0, 0.02^2).
+  * ``c2``: 4096 x 4096 bf16 attention-projection shape: Student-t (nu = 4) scaled to std 0.02, with
+    round(0.001 * cols) whole columns multiplied by 20 (about 0.1 % of the entries) as outlier columns.
+  * ``c3``: 14336 x 4096 and 4096 x 14336 bf16 MLP up/down shapes: N(0, 0.015^2) with each row's std
+    multiplied by 2^U(-1, 1), i.e. log-uniform on [0.5, 2].
+  * ``c5``: one linear layer of a 7B-shaped transformer (q, k, v, o 4096 x 4096; gate, up 11008 x 4096;
+    down 4096 x 11008) bf16, Student-t (nu = 5) scaled to std 0.02, seeded by the layer index.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+C5_SHAPES = {
+    "q": (4096, 4096), "k": (4096, 4096), "v": (4096, 4096), "o": (4096, 4096),
+    "gate": (11008, 4096), "up": (11008, 4096), "down": (4096, 11008),
+}
+C5_ORDER = ("q", "k", "v", "o", "gate", "up", "down")
+
+
+def rng(seed: int, matrix_id: int = 0, stream: int = 0) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([int(seed), int(matrix_id), int(stream)])))
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round finite binary32 values to bf16 (nearest, ties to even) and return the bit patterns."""
+    u = np.ascontiguousarray(x, np.float32).view(np.uint32)
+    r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+def bf16_to_f32(h: np.ndarray) -> np.ndarray:
+    return (np.ascontiguousarray(h, np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def student_t(g: np.random.Generator, nu: float, shape, std: float) -> np.ndarray:
+    """Student-t draws scaled so that the population std is ``std`` (requires nu > 2)."""
+    return g.standard_t(nu, size=shape) * (std / np.sqrt(nu / (nu - 2.0)))
+
+
+def c1(seed: int = 0) -> np.ndarray:
+    g = rng(seed, 0)
+    return (g.standard_normal((256, 1024)) * 0.02).astype(np.float32)
+
+
+def c2(seed: int = 0, rows: int = 4096, cols: int = 4096) -> np.ndarray:
+    g = rng(seed, 0)
+    w = student_t(g, 4.0, (rows, cols), 0.02)
+    k = int(round(0.001 * cols))
+    cols_out = rng(seed, 0, 1).permutation(cols)[:k]
+    w[:, cols_out] *= 20.0
+    return bf16_bits(w.astype(np.float32))
+
+
+def c3(which: int, seed: int = 0) -> np.ndarray:
+    rows, cols = ((14336, 4096), (4096, 14336))[which]
+    g = rng(seed, which)
+    sigma = 0.015 * np.exp2(rng(seed, which, 1).uniform(-1.0, 1.0, size=(rows, 1)))
+    return bf16_bits((g.standard_normal((rows, cols)) * sigma).astype(np.float32))
+
+
+def c5(layer: int, name: str) -> np.ndarray:
+    rows, cols = C5_SHAPES[name]
+    g = rng(layer, C5_ORDER.index(name))
+    return bf16_bits(student_t(g, 5.0, (rows, cols), 0.02).astype(np.float32))
+
+
+def normal_bf16(rows: int, cols: int, seed: int, std: float = 0.02) -> np.ndarray:
+    return bf16_bits((rng(seed, 7).standard_normal((rows, cols)) * std).astype(np.float32))
+
+
+def normal_f32(rows: int, cols: int, seed: int, std: float = 0.02) -> np.ndarray:
+    return (rng(seed, 8).standard_normal((rows, cols)) * std).astype(np.float32)
