@@ -1,0 +1,198 @@
+#!/usr/bin/env python3
+"""Benchmark of the gfx950 NVFP4 weight quantizer on one MI355X.
+
+Workload: 4096 x 4096 bf16 attention-projection-shaped weights (Student-t, nu = 4, std 0.02, plus
+outlier columns scaled by 20). Twelve distinct matrices (384 MiB, more than the 256 MB Infinity Cache)
+stay resident in HBM and are visited in turn, so each step starts from HBM rather than from cache.
+
+One step = one matrix quantised in each of the four modes, back to back on one stream:
+MAX, FourOverSix, CJSO (8 rounds), SOAR (CJSO(8) + the 202-candidate search). `value` is the weight
+bytes quantised per second over the step (4 x 32 MiB per step). Per mode the JSON line also gives its
+own GB/s and its share of the relevant peak (HBM for MAX/FourOverSix/CJSO, FP32 vector for the search).
+
+The dominant kernel (the SOAR search) is timed live: the library records HIP events around each of
+its kernels on the stream it launches them on (the `stage_events` hook of the C ABI). Its achieved rate
+is algorithmic FLOPs / duration: per block 101 quantise scales x 16 elements x 9 FLOPs (one multiply
+for the scaled value, and for each of the two reconstruct scales one fused multiply-add for the
+residual and one for its square), against the 157.3 TFLOP/s FP32 vector peak.
+
+cpu_baseline: the oracle (plain C, one thread) on rows 0..255 of the first matrix in all four modes.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GB/s of weights quantized (and % HBM / % VALU peak) per mode, 4096×4096 bf16"
+PEAK_HBM = 8.0e12  # B/s, MI355X HBM3E
+PEAK_FP32 = 157.3e12  # FLOP/s, MI355X FP32 vector (packed FMA = 4 FLOP per lane-cycle)
+ROWS = COLS = 4096
+N_MATS = 12
+ITERS = 8
+MODES = (("max", 0), ("4o6", 0), ("cjso", ITERS), ("soar", ITERS))
+SEARCH_FLOPS_PER_BLOCK = 101 * 16 * 9
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_soar_traffic.json")
+KERNEL_NAMES = {
+    "max": ["k_amax", "k_quant"],
+    "4o6": ["k_amax", "k_quant"],
+    "cjso": ["k_amax", "k_cjso_init"] + ["k_cjso_iter"] * ITERS,
+    "soar": ["k_amax", "k_cjso_init"] + ["k_cjso_iter"] * ITERS + ["k_soar"],
+}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "nvfp4_block_scaled_elem_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def cpu_baseline(W0: np.ndarray) -> dict:
+    import oracle
+
+    sample = np.ascontiguousarray(W0[:256])
+    t0 = time.perf_counter()
+    for mode, iters in MODES:
+        oracle.quantize(sample, mode, iters)
+    dt = time.perf_counter() - t0
+    return {"value": round(len(MODES) * sample.nbytes / dt / 1e9, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"rows 0-255 of the first 4096x4096 matrix ({sample.size} elements), all four modes, "
+                      f"one thread, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the quantizer runs on a single device and --gpus {args.gpus} is not "
+              "supported (shard by matrix across processes instead)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import nvfp4_block_scaled_elem_amd as nv
+    import synth
+
+    dev = torch.device("cuda:0")
+    log("generating inputs")
+    W0 = synth.c2(0)
+    base = torch.from_numpy(W0.view(np.int16)).view(torch.bfloat16).to(dev)
+    # the other matrices: row rotations of the first with alternating sign (same distribution, new bytes)
+    mats = [base] + [(-1 if i % 2 else 1) * torch.roll(base, shifts=331 * i, dims=0) for i in range(1, N_MATS)]
+    mats = [m.contiguous() for m in mats]
+    out = {}
+    for mode, _ in MODES:
+        out[mode] = dict(
+            codes=torch.empty((ROWS, COLS // 2), dtype=torch.uint8, device=dev),
+            scales=torch.empty((ROWS, COLS // 16), dtype=torch.uint8, device=dev),
+            alpha=torch.empty(1, dtype=torch.float32, device=dev),
+            workspace=torch.empty(nv.workspace_bytes(ROWS, COLS, mode), dtype=torch.uint8, device=dev),
+            mchoice=torch.empty((ROWS, COLS // 16), dtype=torch.uint8, device=dev) if mode == "4o6" else None,
+            stats=torch.zeros(4, dtype=torch.int32, device=dev),
+        )
+    nk = {mode: nv.kernel_count(mode, iters) for mode, iters in MODES}
+
+    def step(s, events=None):
+        W = mats[s % N_MATS]
+        for mode, iters in MODES:
+            o = out[mode]
+            nv.quantize(W, mode, iters, codes=o["codes"], scales=o["scales"], alpha=o["alpha"],
+                        mchoice=o["mchoice"], stats=o["stats"], workspace=o["workspace"],
+                        stage_events=events[mode] if events else None)
+
+    log("warmup")
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+
+    evs = [{mode: [torch.cuda.Event(enable_timing=True) for _ in range(nk[mode] + 1)] for mode, _ in MODES}
+           for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(args.warmup + s, evs[s])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    # per-mode call times and per-kernel durations from the stage events (GPU clock)
+    per_mode = {}
+    kern = {}
+    for mode, iters in MODES:
+        calls = [e[mode][0].elapsed_time(e[mode][-1]) for e in evs]
+        dur = np.array([[e[mode][j].elapsed_time(e[mode][j + 1]) for j in range(nk[mode])] for e in evs])
+        call_ms = float(np.mean(calls))
+        gbps = ROWS * COLS * 2 / (call_ms * 1e-3) / 1e9
+        per_mode[mode] = {"ms": round(call_ms, 5), "GBps": round(gbps, 2), "frac_hbm_peak": round(gbps * 1e9 / PEAK_HBM, 4),
+                          "kernels_ms": {}}
+        for j, name in enumerate(KERNEL_NAMES[mode]):
+            key = name if name != "k_cjso_iter" else "k_cjso_iter(avg)"
+            per_mode[mode]["kernels_ms"].setdefault(key, []).append(float(dur[:, j].mean()))
+        per_mode[mode]["kernels_ms"] = {k: round(float(np.mean(v)), 5) for k, v in per_mode[mode]["kernels_ms"].items()}
+        kern[mode] = dur
+    nblk = ROWS * COLS // 16
+    t_search = float(kern["soar"][:, -1].mean()) * 1e-3
+    search_tflops = nblk * SEARCH_FLOPS_PER_BLOCK / t_search / 1e12
+    per_mode["soar"]["search_ms"] = round(t_search * 1e3, 5)
+    per_mode["soar"]["search_frac_fp32_peak"] = round(search_tflops * 1e12 / PEAK_FP32, 4)
+    m4 = int(out["4o6"]["stats"][1].item())
+    per_mode["4o6"]["m4_fraction"] = round(m4 / nblk, 4)
+    # HBM view of the memory-bound single passes: algorithmic bytes of the whole call (read W once,
+    # write codes and scales) over the call time
+    algo_bytes = ROWS * COLS * (2 + 0.5 + 1.0 / 16)
+    for mode in ("max", "4o6"):
+        per_mode[mode]["algo_GBps"] = round(algo_bytes / (per_mode[mode]["ms"] * 1e-3) / 1e9, 2)
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        if t.get("source_hash") == source_hash():
+            traffic = t.get("bytes_per_launch")
+    roofline = {"bound": "alu", "kernel": "k_soar (decoupled search)", "achieved": round(search_tflops, 3),
+                "peak": PEAK_FP32 / 1e12, "unit": "TFLOP/s", "frac": round(search_tflops * 1e12 / PEAK_FP32, 4),
+                "traffic": traffic, "algorithmic_flops_per_launch": nblk * SEARCH_FLOPS_PER_BLOCK,
+                "avg_launch_ms": round(t_search * 1e3, 5)}
+
+    value = len(MODES) * ROWS * COLS * 2 / (ms_per_step * 1e-3) / 1e9
+    line = {
+        "metric": METRIC, "value": round(value, 3), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "4096x4096 bf16 attention-projection weights, Student-t(nu=4) std 0.02 with 0.1% "
+                               "outlier columns x20; 12 resident matrices visited in turn; step = MAX, FourOverSix, "
+                               "CJSO(8), SOAR(8)", "rows": ROWS, "cols": COLS, "input_dtype": "bf16",
+                   "matrices": N_MATS, "cjso_iters": ITERS, "parallelism": "single GPU"},
+        "modes": per_mode,
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        line["cpu_baseline"] = cpu_baseline(W0)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,146 @@
+/*
+ * nvfp4.h - C ABI of the MI355X (gfx950) NVFP4 weight quantizer.
+ *
+ * What the calls compute:
+ *   NVFP4 quantisation of a weight matrix W into FP4 (E2M1) codes Q, one FP8 (E4M3) scale Delta_i per
+ *   block of 16 consecutive elements of a row, and one FP32 global scale alpha, so that
+ *   W ~ Q * Delta_i * alpha. The four modes are the ones the two pages describe:
+ *     NVFP4_MODE_MAX           the max rule of the SOAR page ("SOAR: Scale Optimization for Accurate
+ *                              Reconstruction in NVFP4 Quantization", quantisation equations):
+ *                              alpha = max|W| / (6*448), Delta_i = E4M3(max|W_i| / (6*alpha)).
+ *     NVFP4_MODE_FOUR_OVER_SIX the FourOverSix choice of the write-up "SOAR 周冠军笔记 07 |
+ *                              香草小张：NVFP4 量化改进与推测解码实践", section 02: per block, the M=4
+ *                              scale E4M3(1.5*Delta_i) replaces Delta_i when its squared reconstruction
+ *                              error is strictly smaller.
+ *     NVFP4_MODE_CJSO          the SOAR page's closed-form joint scale optimisation: from the max rule,
+ *                              `iters` rounds of {least-squares alpha, re-quantise, least-squares Delta_i
+ *                              rounded to E4M3, re-quantise}.
+ *     NVFP4_MODE_SOAR          CJSO followed by the SOAR page's decoupled search: per block, quantise with
+ *                              Delta_q = Delta_c * f (f = 0.50, 0.51, ..., 1.50) and reconstruct with
+ *                              Delta_d, one of the two E4M3 values around the unrounded CJSO scale; keep
+ *                              the least squared error (202 candidates, CJSO's own point first, strict <).
+ *   Arithmetic: scaled values are x = w * (1/(alpha*Delta)) in binary32, rounded to the nearest E2M1
+ *   value with ties to the even code and |x| > 6 saturating to 6 (a value rounding to 0 gets code 0);
+ *   every choice between candidates compares exact squared errors. The results are bit-identical to
+ *   the CPU oracle that defines them.
+ *
+ * Layout (row-major, contiguous, caller-owned):
+ *   W          [rows][cols] bf16 (nvfp4_quantize) or fp32 (nvfp4_quantize_f32), 16-byte aligned.
+ *   codes_out  [rows][cols/2] bytes, 8-byte aligned: byte k of a row holds column 2k in its low nibble
+ *              and column 2k+1 in its high nibble; a code is sign (bit 3) | index into
+ *              {0, 0.5, 1, 1.5, 2, 3, 4, 6}.
+ *   scales_out [rows][cols/16] E4M3 bytes (sign bit 0; at most 0x7E = 448).
+ *   alpha_out  one float. Dequantisation: w_hat = e2m1(code) * e4m3(scale) * alpha.
+ *   All pointers are device pointers (hipMalloc'd or torch CUDA tensors); `stream` is a hipStream_t
+ *   (NULL = the default stream).
+ *
+ * Calls are asynchronous: they validate their arguments on the host, enqueue kernels on `stream` and
+ * return. Results are valid once the stream has reached that point. The library keeps no pointer after
+ * the enqueued work ends and has no mutable global state: calls on different streams may overlap, and
+ * calls that share output buffers must be ordered by the caller.
+ *
+ * Errors: negative return values are reported synchronously and nothing is enqueued, except
+ * NVFP4_ERR_HIP (a launch or allocation failed; work enqueued before the failure may still run).
+ * Data-dependent conditions are reported in band: a NaN or an infinity anywhere in W gives
+ * alpha_out = NaN and all-zero codes and scales (and sets NVFP4_STATUS_NONFINITE in the stats); an
+ * all-zero W gives alpha = 0 with all-zero codes and scales.
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum nvfp4_mode {
+    NVFP4_MODE_MAX = 0,
+    NVFP4_MODE_FOUR_OVER_SIX = 1,
+    NVFP4_MODE_CJSO = 2,
+    NVFP4_MODE_SOAR = 3
+};
+
+enum nvfp4_dtype { NVFP4_DTYPE_BF16 = 0, NVFP4_DTYPE_F32 = 1 };
+
+enum nvfp4_error {
+    NVFP4_OK = 0,
+    NVFP4_ERR_INVALID_ARG = -1, /* null or misaligned pointer, rows/cols <= 0, unknown mode or dtype,
+                                   iters outside [0, 1000] */
+    NVFP4_ERR_SHAPE = -2,       /* cols % 16 != 0, or more than 2^40 elements */
+    NVFP4_ERR_WORKSPACE = -3,   /* caller workspace smaller than nvfp4_workspace_bytes() */
+    NVFP4_ERR_HIP = -4          /* a HIP call failed */
+};
+
+/* In-band status bits, written to nvfp4_stats_t.status by the device. */
+#define NVFP4_STATUS_NONFINITE 1u
+
+/* Optional per-call statistics in device memory (written by the call). */
+typedef struct nvfp4_stats {
+    uint32_t status;    /* NVFP4_STATUS_* bits */
+    uint32_t m4_blocks; /* FourOverSix: number of blocks that kept M=4 */
+    uint32_t reserved[2];
+} nvfp4_stats_t;
+
+/* Quantise a bf16 matrix. `iters` is the number of CJSO rounds (modes 2 and 3; ignored otherwise,
+ * 0 makes CJSO equal to MAX). A scratch workspace is taken from a stream-ordered pool and given
+ * back on the same stream. */
+int nvfp4_quantize(const void *W, int64_t rows, int64_t cols, int mode, int iters, uint8_t *codes_out,
+                   uint8_t *scales_out, float *alpha_out, void *stream);
+
+/* Same for an fp32 matrix. */
+int nvfp4_quantize_f32(const float *W, int64_t rows, int64_t cols, int mode, int iters,
+                       uint8_t *codes_out, uint8_t *scales_out, float *alpha_out, void *stream);
+
+/* Full argument set. */
+typedef struct nvfp4_args {
+    const void *W;
+    int dtype; /* enum nvfp4_dtype */
+    int64_t rows, cols;
+    int mode; /* enum nvfp4_mode */
+    int iters;
+    uint8_t *codes_out;
+    uint8_t *scales_out;
+    float *alpha_out;
+    uint8_t *mchoice_out;     /* nullable: [rows][cols/16] bytes, 1 where FourOverSix kept M=4 (mode 1) */
+    nvfp4_stats_t *stats_out; /* nullable, device memory */
+    void *workspace;          /* nullable: device memory of workspace_bytes, 256-byte aligned; NULL =
+                                 the library allocates on `stream` */
+    size_t workspace_bytes;
+    void *stream;             /* hipStream_t */
+    void *const *stage_events; /* nullable: nvfp4_kernel_count(mode, iters) + 1 hipEvent_t handles; the
+                                  call records stage_events[0] before its first kernel and
+                                  stage_events[j + 1] after kernel j, so each kernel can be timed on
+                                  `stream` */
+    int n_stage_events;
+} nvfp4_args_t;
+
+int nvfp4_quantize_ex(const nvfp4_args_t *args);
+
+/* Number of kernels one call of this mode enqueues (MAX and FourOverSix: 2; CJSO: iters + 2; SOAR:
+ * iters + 3; the last SOAR kernel is the decoupled search), or -1 for an unknown mode or bad iters. */
+int nvfp4_kernel_count(int mode, int iters);
+
+/* Device scratch needed by one call with these arguments (0 for an invalid shape). */
+size_t nvfp4_workspace_bytes(int64_t rows, int64_t cols, int mode);
+
+/* Round n binary32 values to E2M1 codes (one code per output byte, same rule as the quantiser:
+ * nearest, ties to the even code, saturating at 6, NaN -> 0, negative results that round to zero ->
+ * code 0). x and codes are device pointers. */
+int nvfp4_encode_e2m1(const float *x, int64_t n, uint8_t *codes, void *stream);
+
+/* Dequantise codes/scales/alpha (device pointers, layout above; alpha is a device pointer to one
+ * float) into out [rows][cols] as bf16 (out_dtype 0) or fp32 (out_dtype 1):
+ * out = e2m1(code) * e4m3(scale) * alpha, rounded once to the output type (SOAR page, dequantisation
+ * equation). */
+int nvfp4_dequantize(const uint8_t *codes, const uint8_t *scales, const float *alpha, int64_t rows,
+                     int64_t cols, void *out, int out_dtype, void *stream);
+
+/* Text of an nvfp4_error value. */
+const char *nvfp4_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,161 @@
+"""Python binding of the gfx950 NVFP4 weight quantizer (``libnvfp4.so``; C ABI in ``include/nvfp4.h``).
+
+Argument marshalling only: tensors are torch CUDA (HIP) tensors, every step of the computation runs in
+the HIP kernels behind the C ABI, and there is no CPU fallback. A missing library raises at first use.
+
+    codes, scales, alpha = quantize(W, "4o6")          # W: [rows, cols] bf16 or fp32, cols % 16 == 0
+    W_hat = dequantize(codes, scales, alpha, torch.bfloat16)
+
+Modes: "max" (max rule), "4o6" (FourOverSix), "cjso" (closed-form joint scale optimisation, ``iters``
+rounds), "soar" (CJSO then the decoupled quantise/dequantise scale search).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libnvfp4.so")
+
+MODES = {"max": 0, "4o6": 1, "cjso": 2, "soar": 3}
+DTYPES = {torch.bfloat16: 0, torch.float32: 1}
+STATUS_NONFINITE = 1
+
+
+class NVFP4Error(RuntimeError):
+    pass
+
+
+class _Args(ctypes.Structure):
+    _fields_ = [
+        ("W", ctypes.c_void_p), ("dtype", ctypes.c_int), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+        ("mode", ctypes.c_int), ("iters", ctypes.c_int), ("codes_out", ctypes.c_void_p),
+        ("scales_out", ctypes.c_void_p), ("alpha_out", ctypes.c_void_p), ("mchoice_out", ctypes.c_void_p),
+        ("stats_out", ctypes.c_void_p), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+        ("stream", ctypes.c_void_p), ("stage_events", ctypes.c_void_p), ("n_stage_events", ctypes.c_int),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise NVFP4Error(f"{LIB_PATH} is missing: build it with `python nvfp4_block_scaled_elem_amd/build.py`")
+        L = ctypes.CDLL(LIB_PATH)
+        i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+        L.nvfp4_quantize_ex.argtypes = [ctypes.POINTER(_Args)]
+        L.nvfp4_quantize_ex.restype = i32
+        L.nvfp4_quantize.argtypes = [vp, i64, i64, i32, i32, vp, vp, vp, vp]
+        L.nvfp4_quantize.restype = i32
+        L.nvfp4_quantize_f32.argtypes = [vp, i64, i64, i32, i32, vp, vp, vp, vp]
+        L.nvfp4_quantize_f32.restype = i32
+        L.nvfp4_workspace_bytes.argtypes = [i64, i64, i32]
+        L.nvfp4_workspace_bytes.restype = ctypes.c_size_t
+        L.nvfp4_kernel_count.argtypes = [i32, i32]
+        L.nvfp4_kernel_count.restype = i32
+        L.nvfp4_encode_e2m1.argtypes = [vp, i64, vp, vp]
+        L.nvfp4_encode_e2m1.restype = i32
+        L.nvfp4_dequantize.argtypes = [vp, vp, vp, i64, i64, vp, i32, vp]
+        L.nvfp4_dequantize.restype = i32
+        L.nvfp4_status_string.argtypes = [i32]
+        L.nvfp4_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().nvfp4_status_string(status).decode()
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise NVFP4Error(f"nvfp4: {status_string(status)} ({status})")
+
+
+def workspace_bytes(rows: int, cols: int, mode: str) -> int:
+    return int(lib().nvfp4_workspace_bytes(rows, cols, MODES[mode]))
+
+
+def kernel_count(mode: str, iters: int = 0) -> int:
+    return int(lib().nvfp4_kernel_count(MODES[mode], iters))
+
+
+def _stream_ptr(stream, device) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream
+
+
+def quantize(W: torch.Tensor, mode: str, iters: int = 0, *, codes=None, scales=None, alpha=None,
+             mchoice=None, stats=None, workspace=None, stream=None, stage_events=None):
+    """Quantise ``W`` ([rows, cols] bf16/fp32 CUDA tensor). Returns (codes [rows, cols//2] uint8,
+    scales [rows, cols//16] uint8 E4M3 bits, alpha [1] float32), all on W's device. Optional
+    preallocated outputs, an ``mchoice`` uint8 [rows, cols//16] tensor (FourOverSix), a ``stats``
+    int32 [4] tensor, a uint8 ``workspace`` tensor, a ``stream`` and a list of
+    ``torch.cuda.Event(enable_timing=True)`` stage events may be passed."""
+    if W.dim() != 2 or not W.is_cuda or not W.is_contiguous() or W.dtype not in DTYPES:
+        raise NVFP4Error("W must be a contiguous 2-D bf16 or fp32 CUDA tensor")
+    rows, cols = W.shape
+    dev = W.device
+    if codes is None:
+        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev)
+    if alpha is None:
+        alpha = torch.empty(1, dtype=torch.float32, device=dev)
+    for t in (codes, scales, alpha, mchoice, stats, workspace):
+        if t is not None and (not t.is_cuda or t.device != dev or not t.is_contiguous()):
+            raise NVFP4Error("outputs and workspace must be contiguous tensors on W's device")
+    need = workspace_bytes(rows, cols, mode) if cols % 16 == 0 and rows > 0 else 0
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    a = _Args()
+    a.W = W.data_ptr()
+    a.dtype = DTYPES[W.dtype]
+    a.rows, a.cols = rows, cols
+    a.mode = MODES[mode]
+    a.iters = iters
+    a.codes_out = codes.data_ptr()
+    a.scales_out = scales.data_ptr()
+    a.alpha_out = alpha.data_ptr()
+    a.mchoice_out = mchoice.data_ptr() if mchoice is not None else None
+    a.stats_out = stats.data_ptr() if stats is not None else None
+    a.workspace = workspace.data_ptr() if workspace is not None else None
+    a.workspace_bytes = workspace.numel() if workspace is not None else 0
+    a.stream = _stream_ptr(stream, dev)
+    ev_arr = None
+    if stage_events is not None:
+        for e in stage_events:  # torch creates the HIP event at its first record
+            if not e.cuda_event:
+                e.record(stream if stream is not None else torch.cuda.current_stream(dev))
+        ev_arr = (ctypes.c_void_p * len(stage_events))(*[e.cuda_event for e in stage_events])
+        a.stage_events = ctypes.cast(ev_arr, ctypes.c_void_p)
+        a.n_stage_events = len(stage_events)
+    _check(lib().nvfp4_quantize_ex(ctypes.byref(a)))
+    return codes, scales, alpha
+
+
+def encode_e2m1(x: torch.Tensor, stream=None) -> torch.Tensor:
+    """E2M1 codes (one per byte) of a contiguous fp32 CUDA tensor."""
+    if not x.is_cuda or x.dtype != torch.float32 or not x.is_contiguous():
+        raise NVFP4Error("x must be a contiguous fp32 CUDA tensor")
+    out = torch.empty(x.numel(), dtype=torch.uint8, device=x.device)
+    _check(lib().nvfp4_encode_e2m1(x.data_ptr(), x.numel(), out.data_ptr(), _stream_ptr(stream, x.device)))
+    return out.view(x.shape)
+
+
+def dequantize(codes: torch.Tensor, scales: torch.Tensor, alpha: torch.Tensor, dtype=torch.bfloat16,
+               stream=None) -> torch.Tensor:
+    """W_hat = e2m1(code) * e4m3(scale) * alpha as a [rows, cols] bf16 or fp32 tensor."""
+    rows, half = codes.shape
+    cols = 2 * half
+    out = torch.empty((rows, cols), dtype=dtype, device=codes.device)
+    _check(lib().nvfp4_dequantize(codes.data_ptr(), scales.data_ptr(), alpha.data_ptr(), rows, cols,
+                                  out.data_ptr(), DTYPES[dtype], _stream_ptr(stream, codes.device)))
+    return out

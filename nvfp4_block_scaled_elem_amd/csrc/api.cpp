@@ -1,0 +1,179 @@
+// C ABI of the gfx950 NVFP4 quantizer (declared in include/nvfp4.h): argument checks on the host, the
+// kernel sequence of each mode, and the stream-ordered scratch workspace.
+//
+// Kernel sequence per call (all on the caller's stream):
+//   MAX / FourOverSix : k_amax -> k_quant
+//   CJSO(T)           : k_amax -> k_cjso_init -> T x k_cjso_iter
+//   SOAR(T)           : CJSO(T) -> k_soar
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "launch.hpp"
+
+#define NVFP4_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr int kMaxIters = 1000;
+constexpr int64_t kMaxElems = (int64_t)1 << 40;
+
+int kernel_count(int mode, int iters) {
+    if (iters < 0 || iters > kMaxIters) return -1;
+    switch (mode) {
+        case NVFP4_MODE_MAX:
+        case NVFP4_MODE_FOUR_OVER_SIX: return 2;
+        case NVFP4_MODE_CJSO: return iters + 2;
+        case NVFP4_MODE_SOAR: return iters + 3;
+        default: return -1;
+    }
+}
+
+int check(const nvfp4_args_t *a) {
+    if (!a || !a->W || !a->codes_out || !a->scales_out || !a->alpha_out) return NVFP4_ERR_INVALID_ARG;
+    if (a->rows <= 0 || a->cols <= 0) return NVFP4_ERR_INVALID_ARG;
+    if (a->mode < NVFP4_MODE_MAX || a->mode > NVFP4_MODE_SOAR) return NVFP4_ERR_INVALID_ARG;
+    if (a->dtype != NVFP4_DTYPE_BF16 && a->dtype != NVFP4_DTYPE_F32) return NVFP4_ERR_INVALID_ARG;
+    if (a->iters < 0 || a->iters > kMaxIters) return NVFP4_ERR_INVALID_ARG;
+    if (a->cols % 16 != 0) return NVFP4_ERR_SHAPE;
+    if (a->rows > kMaxElems / a->cols) return NVFP4_ERR_SHAPE;
+    if (((uintptr_t)a->W & 15u) != 0 || ((uintptr_t)a->codes_out & 7u) != 0 || ((uintptr_t)a->alpha_out & 3u) != 0)
+        return NVFP4_ERR_INVALID_ARG;
+    if (a->workspace && ((uintptr_t)a->workspace & 255u) != 0) return NVFP4_ERR_INVALID_ARG;
+    if (a->stats_out && ((uintptr_t)a->stats_out & 3u) != 0) return NVFP4_ERR_INVALID_ARG;
+    if (a->stage_events && a->n_stage_events < kernel_count(a->mode, a->iters) + 1) return NVFP4_ERR_INVALID_ARG;
+    return NVFP4_OK;
+}
+
+// Records stage event j (profiling hook; no-op without events).
+bool mark(const nvfp4_args_t *a, int j) {
+    if (!a->stage_events) return true;
+    return hipEventRecord(static_cast<hipEvent_t>(a->stage_events[j]), static_cast<hipStream_t>(a->stream)) ==
+           hipSuccess;
+}
+
+int run(const nvfp4_args_t *a, void *ws_base) {
+    using namespace nvfp4;
+    hipStream_t st = static_cast<hipStream_t>(a->stream);
+    const bool f32 = a->dtype == NVFP4_DTYPE_F32;
+    const int64_t n = a->rows * a->cols, nblk = n / 16;
+    const Workspace ws = carve(ws_base, nblk);
+    const int ga = amax_groups(n * (f32 ? 4 : 2) / 16);
+    int j = 0;
+    if (!mark(a, j++)) return NVFP4_ERR_HIP;
+    if (launch_amax(a->W, f32, n, ws.amax_part, ga, a->stats_out, st) != hipSuccess || !mark(a, j++))
+        return NVFP4_ERR_HIP;
+    if (a->mode == NVFP4_MODE_MAX || a->mode == NVFP4_MODE_FOUR_OVER_SIX) {
+        const bool fos = a->mode == NVFP4_MODE_FOUR_OVER_SIX;
+        if (launch_quant(a->W, f32, fos, nblk, ws.amax_part, ga, a->codes_out, a->scales_out, a->alpha_out,
+                         fos ? a->mchoice_out : nullptr, a->stats_out, st) != hipSuccess ||
+            !mark(a, j++))
+            return NVFP4_ERR_HIP;
+        return NVFP4_OK;
+    }
+    const bool soar = a->mode == NVFP4_MODE_SOAR;
+    const int gc = cjso_groups(nblk);
+    if (launch_cjso_init(a->W, f32, soar, nblk, ws.amax_part, ga, a->iters, a->codes_out, a->scales_out, a->alpha_out,
+                         ws, gc, a->stats_out, st) != hipSuccess ||
+        !mark(a, j++))
+        return NVFP4_ERR_HIP;
+    for (int t = 1; t <= a->iters; ++t)
+        if (launch_cjso_iter(a->W, f32, soar, nblk, t, a->iters, a->codes_out, a->scales_out, a->alpha_out, ws, gc,
+                             st) != hipSuccess ||
+            !mark(a, j++))
+            return NVFP4_ERR_HIP;
+    if (soar && (launch_soar(a->W, f32, nblk, ws.alpha_state + (a->iters & 1), a->codes_out, a->scales_out,
+                             ws.brackets, st) != hipSuccess ||
+                 !mark(a, j++)))
+        return NVFP4_ERR_HIP;
+    return NVFP4_OK;
+}
+
+}  // namespace
+
+NVFP4_API int nvfp4_kernel_count(int mode, int iters) { return kernel_count(mode, iters); }
+
+NVFP4_API size_t nvfp4_workspace_bytes(int64_t rows, int64_t cols, int mode) {
+    if (rows <= 0 || cols <= 0 || cols % 16 != 0 || rows > kMaxElems / cols) return 0;
+    if (mode < NVFP4_MODE_MAX || mode > NVFP4_MODE_SOAR) return 0;
+    return nvfp4::workspace_bytes(rows * cols / 16, mode);
+}
+
+NVFP4_API int nvfp4_quantize_ex(const nvfp4_args_t *a) {
+    const int c = check(a);
+    if (c != NVFP4_OK) return c;
+    const size_t need = nvfp4::workspace_bytes(a->rows * a->cols / 16, a->mode);
+    if (a->workspace) {
+        if (a->workspace_bytes < need) return NVFP4_ERR_WORKSPACE;
+        return run(a, a->workspace);
+    }
+    hipStream_t st = static_cast<hipStream_t>(a->stream);
+    void *ws = nullptr;
+    if (hipMallocAsync(&ws, need, st) != hipSuccess) return NVFP4_ERR_HIP;
+    const int r = run(a, ws);
+    if (hipFreeAsync(ws, st) != hipSuccess) return NVFP4_ERR_HIP;
+    return r;
+}
+
+NVFP4_API int nvfp4_quantize(const void *W, int64_t rows, int64_t cols, int mode, int iters, uint8_t *codes_out,
+                             uint8_t *scales_out, float *alpha_out, void *stream) {
+    nvfp4_args_t a = {};
+    a.W = W;
+    a.dtype = NVFP4_DTYPE_BF16;
+    a.rows = rows;
+    a.cols = cols;
+    a.mode = mode;
+    a.iters = iters;
+    a.codes_out = codes_out;
+    a.scales_out = scales_out;
+    a.alpha_out = alpha_out;
+    a.stream = stream;
+    return nvfp4_quantize_ex(&a);
+}
+
+NVFP4_API int nvfp4_quantize_f32(const float *W, int64_t rows, int64_t cols, int mode, int iters, uint8_t *codes_out,
+                                 uint8_t *scales_out, float *alpha_out, void *stream) {
+    nvfp4_args_t a = {};
+    a.W = W;
+    a.dtype = NVFP4_DTYPE_F32;
+    a.rows = rows;
+    a.cols = cols;
+    a.mode = mode;
+    a.iters = iters;
+    a.codes_out = codes_out;
+    a.scales_out = scales_out;
+    a.alpha_out = alpha_out;
+    a.stream = stream;
+    return nvfp4_quantize_ex(&a);
+}
+
+NVFP4_API int nvfp4_encode_e2m1(const float *x, int64_t n, uint8_t *codes, void *stream) {
+    if (!x || !codes || n < 0) return NVFP4_ERR_INVALID_ARG;
+    if (((uintptr_t)codes & 7u) != 0 || ((uintptr_t)x & 3u) != 0) return NVFP4_ERR_INVALID_ARG;
+    if (n == 0) return NVFP4_OK;
+    return nvfp4::launch_encode_e2m1(x, n, codes, static_cast<hipStream_t>(stream)) == hipSuccess ? NVFP4_OK
+                                                                                                   : NVFP4_ERR_HIP;
+}
+
+NVFP4_API int nvfp4_dequantize(const uint8_t *codes, const uint8_t *scales, const float *alpha, int64_t rows,
+                               int64_t cols, void *out, int out_dtype, void *stream) {
+    if (!codes || !scales || !alpha || !out || rows <= 0 || cols <= 0) return NVFP4_ERR_INVALID_ARG;
+    if (out_dtype != NVFP4_DTYPE_BF16 && out_dtype != NVFP4_DTYPE_F32) return NVFP4_ERR_INVALID_ARG;
+    if (cols % 16 != 0 || rows > kMaxElems / cols) return NVFP4_ERR_SHAPE;
+    if (((uintptr_t)codes & 7u) != 0 || ((uintptr_t)out & 15u) != 0 || ((uintptr_t)alpha & 3u) != 0)
+        return NVFP4_ERR_INVALID_ARG;
+    return nvfp4::launch_dequant(codes, scales, alpha, rows * cols / 16, out, out_dtype == NVFP4_DTYPE_F32,
+                                 static_cast<hipStream_t>(stream)) == hipSuccess
+               ? NVFP4_OK
+               : NVFP4_ERR_HIP;
+}
+
+NVFP4_API const char *nvfp4_status_string(int status) {
+    switch (status) {
+        case NVFP4_OK: return "ok";
+        case NVFP4_ERR_INVALID_ARG: return "invalid argument";
+        case NVFP4_ERR_SHAPE: return "unsupported shape (cols must be a multiple of 16)";
+        case NVFP4_ERR_WORKSPACE: return "workspace too small";
+        case NVFP4_ERR_HIP: return "HIP launch or allocation failed";
+        default: return "unknown status";
+    }
+}

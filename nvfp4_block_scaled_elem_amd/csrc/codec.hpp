@@ -1,0 +1,125 @@
+// Device-side number formats and exact comparison helpers for the gfx950 NVFP4 quantizer.
+//
+// Formats (SOAR page, quantisation definitions; FourOverSix write-up, section 01):
+//   E2M1: sign | 2 exponent bits | 1 mantissa bit, magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6}.
+//   E4M3 (the "FN" variant): sign | 4 exponent bits (bias 7) | 3 mantissa bits, subnormals m*2^-9, no
+//   infinities, largest finite value 448 (code 0x7E).
+//
+// E2M1 rounding uses gfx950's v_cvt_scalef32_pk_fp4_f32 with a scale of 1.0. On every binary32 input
+// it returns the nearest E2M1 value with ties to the even code and saturates to +-6 (infinities
+// included); the two differences from the rule the quantiser follows are repaired where it matters:
+// a negative value that rounds to zero comes back as code 0x8 (cleared by e2m1_clear_negzero) and
+// NaN maps to a nonzero code (the callers never feed NaN to it). Decoding uses
+// v_cvt_scalef32_pk_bf16_fp4 / _pk_f32_fp4 (exact for all 16 codes).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t d) { return __uint_as_float(d << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t d) { return __uint_as_float(d & 0xFFFF0000u); }
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t d) { return __builtin_bit_cast(bf16x2, d); }
+
+// ---------------------------------------------------------------------------------------- E4M3
+
+// Value of a non-negative finite E4M3 code (0x00..0x7E).
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+    uint32_t e = c >> 3, m = c & 7u;
+    return e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
+}
+
+// Nearest E4M3 value to v >= 0 (ties to the even code), values >= 448 saturate to 448. Exact for any
+// binary64 v: v is scaled by a power of two so that the E4M3 spacing around it becomes 1, and the
+// integer rounding is done by rint (round half to even).
+__device__ __forceinline__ uint32_t e4m3_rne(double v) {
+    if (!(v > 0.0)) return 0u;
+    if (v >= 448.0) return 0x7Eu;
+    int e = ilogb(v);
+    e = e < -6 ? -6 : e;
+    double m = rint(ldexp(v, 3 - e));
+    uint32_t c = (uint32_t)(8 * (e + 6)) + (uint32_t)m;
+    return c > 0x7Eu ? 0x7Eu : c;
+}
+
+// The E4M3 codes around v >= 0: lo = largest value <= v, hi = smallest value >= v (both 448 when
+// v >= 448, both 0 when v <= 0).
+__device__ __forceinline__ void e4m3_bracket(double v, uint32_t &lo, uint32_t &hi) {
+    if (!(v > 0.0)) {
+        lo = hi = 0u;
+        return;
+    }
+    if (v >= 448.0) {
+        lo = hi = 0x7Eu;
+        return;
+    }
+    int e = ilogb(v);
+    e = e < -6 ? -6 : e;
+    double t = ldexp(v, 3 - e);
+    uint32_t base = (uint32_t)(8 * (e + 6));
+    lo = base + (uint32_t)floor(t);
+    hi = base + (uint32_t)ceil(t);
+    if (hi > 0x7Eu) hi = 0x7Eu;
+}
+
+// ---------------------------------------------------------------------------------------- E2M1
+
+// Eight binary32 values -> eight E2M1 codes packed in a dword (value 2k in the low nibble of byte k).
+__device__ __forceinline__ uint32_t e2m1_pack8(float x0, float x1, float x2, float x3, float x4, float x5,
+                                               float x6, float x7) {
+    uint32_t v = 0u;
+    v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, x0, x1, 1.0f, 0);
+    v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, x2, x3, 1.0f, 1);
+    v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, x4, x5, 1.0f, 2);
+    v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, x6, x7, 1.0f, 3);
+    return v;
+}
+
+// Code 0x8 (negative zero) -> 0x0 in every nibble; other codes unchanged.
+__device__ __forceinline__ uint32_t e2m1_clear_negzero(uint32_t c) {
+    uint32_t mag = c & 0x77777777u;
+    uint32_t nz = (mag + 0x77777777u) & 0x88888888u;  // bit 3 of a nibble set iff its magnitude != 0
+    return mag | (c & nz);
+}
+
+// Software E2M1 of one binary32 value (the rule spelled out: nearest magnitude, ties to the even
+// code, saturate above 6, NaN -> 0, sign only on nonzero codes). Used on rare blocks whose scale
+// reciprocal overflows, where w * r can be NaN.
+__device__ __forceinline__ uint32_t e2m1_soft(float x) {
+    float a = fabsf(x);
+    uint32_t i = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) + (uint32_t)(a >= 1.75f) +
+                 (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
+    return (i != 0u && __builtin_signbit(x)) ? (i | 8u) : i;
+}
+
+// ------------------------------------------------------------------------ exact double-double
+
+struct dd {
+    double hi, lo;
+};
+
+// a*b exactly, as an unevaluated sum hi + lo with hi = fl(a*b).
+__device__ __forceinline__ dd two_prod(double a, double b) {
+    double p = a * b;
+    return {p, fma(a, b, -p)};
+}
+
+// Exact order of two values held as (fl(x), x - fl(x)).
+__device__ __forceinline__ bool dd_less(dd a, dd b) { return a.hi < b.hi || (a.hi == b.hi && a.lo < b.lo); }
+__device__ __forceinline__ bool dd_equal(dd a, dd b) { return a.hi == b.hi && a.lo == b.lo; }
+
+// Sum of two non-negative double-doubles (relative error about 2^-104).
+__device__ __forceinline__ dd dd_add(dd a, dd b) {
+    double s = a.hi + b.hi;
+    double bb = s - a.hi;
+    double err = (a.hi - (s - bb)) + (b.hi - bb);
+    double lo = err + a.lo + b.lo;
+    double hi = s + lo;
+    return {hi, lo - (hi - s)};
+}
+
+}  // namespace nvfp4

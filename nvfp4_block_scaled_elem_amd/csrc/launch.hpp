@@ -1,0 +1,49 @@
+// Internal launchers of the gfx950 kernels (host side). Every launcher enqueues on `stream` and
+// returns the hipError_t of the launch. Shapes are validated by the C ABI before any launcher runs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/nvfp4.h"
+
+namespace nvfp4 {
+
+// Work-group counts of the reduction kernels: the global max pass and the persistent CJSO passes.
+// Their per-work-group partial results are what the next kernel reduces, so they stay small.
+constexpr int kAmaxThreads = 256;
+constexpr int kAmaxMaxGroups = 1024;
+constexpr int kCjsoThreads = 256;
+constexpr int kCjsoMaxGroups = 1024;
+
+int amax_groups(int64_t nchunks);
+int cjso_groups(int64_t nblk);
+
+// Scratch layout inside the workspace (byte offsets, 256-byte aligned pieces).
+struct Workspace {
+    uint32_t *amax_part;  // [kAmaxMaxGroups]   max |w| bits per work-group
+    float *alpha_state;   // [2]                alpha of the previous / current CJSO round
+    double *cjso_part;    // [2][kCjsoMaxGroups][4] (N.hi, N.lo, D.hi, D.lo) per work-group
+    uint16_t *brackets;   // [nblk]             E4M3 codes lo | hi << 8 around the unrounded CJSO scale
+};
+size_t workspace_bytes(int64_t nblk, int mode);
+Workspace carve(void *base, int64_t nblk);
+
+hipError_t launch_amax(const void *W, bool f32, int64_t n, uint32_t *amax_part, int groups, nvfp4_stats_t *stats,
+                       hipStream_t stream);
+hipError_t launch_quant(const void *W, bool f32, bool four_over_six, int64_t nblk, const uint32_t *amax_part,
+                        int amax_n, uint8_t *codes, uint8_t *scales, float *alpha_out, uint8_t *mchoice,
+                        nvfp4_stats_t *stats, hipStream_t stream);
+hipError_t launch_cjso_init(const void *W, bool f32, bool soar, int64_t nblk, const uint32_t *amax_part, int amax_n,
+                            int iters, uint8_t *codes, uint8_t *scales, float *alpha_out, const Workspace &ws,
+                            int groups, nvfp4_stats_t *stats, hipStream_t stream);
+hipError_t launch_cjso_iter(const void *W, bool f32, bool soar, int64_t nblk, int t, int iters, uint8_t *codes,
+                            uint8_t *scales, float *alpha_out, const Workspace &ws, int groups, hipStream_t stream);
+hipError_t launch_soar(const void *W, bool f32, int64_t nblk, const float *alpha, uint8_t *codes, uint8_t *scales,
+                       const uint16_t *brackets, hipStream_t stream);
+hipError_t launch_encode_e2m1(const float *x, int64_t n, uint8_t *codes, hipStream_t stream);
+hipError_t launch_dequant(const uint8_t *codes, const uint8_t *scales, const float *alpha, int64_t nblk, void *out,
+                          bool out_f32, hipStream_t stream);
+
+}  // namespace nvfp4

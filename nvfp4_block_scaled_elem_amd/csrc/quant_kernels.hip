@@ -1,0 +1,564 @@
+// gfx950 kernels for the global max, the max rule, FourOverSix, the CJSO rounds, E2M1 encoding and
+// dequantisation. All are bandwidth-bound passes over W: one lane owns one 16-element block (two 16-byte
+// loads for bf16), so the block max, the candidate codes and the block sums never leave registers.
+//
+// Device-wide dependencies (alpha needs all of W; each CJSO round needs the previous round's
+// least-squares sums) are kernel boundaries. Each producer writes one small partial per work-group and
+// every work-group of the consumer reduces those partials in a fixed order, so results are
+// deterministic and no atomics, counters or memsets are needed.
+#include <float.h>
+
+#include "block.hpp"
+#include "launch.hpp"
+
+namespace nvfp4 {
+
+// ------------------------------------------------------------------------------- reductions
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t m) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const uint32_t t = (uint32_t)__shfl_xor((int)m, o);
+        m = t > m ? t : m;
+    }
+    return m;
+}
+
+// Max of part[0..n) across the work-group; every thread gets the result.
+__device__ __forceinline__ uint32_t wg_max_parts(const uint32_t *part, int n) {
+    __shared__ uint32_t red[16];
+    uint32_t m = 0u;
+    for (int i = threadIdx.x; i < n; i += blockDim.x) m = part[i] > m ? part[i] : m;
+    m = wave_max_u32(m);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    m = 0u;
+    for (int i = 0; i < (int)(blockDim.x >> 6); ++i) m = red[i] > m ? red[i] : m;
+    return m;
+}
+
+// Work-group sum of two double-doubles (fixed order); the result is valid in thread 0.
+__device__ __forceinline__ void wg_sum_dd2(dd &N, dd &D) {
+    __shared__ double red[16][4];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const dd n2 = {__shfl_xor(N.hi, o), __shfl_xor(N.lo, o)};
+        const dd d2 = {__shfl_xor(D.hi, o), __shfl_xor(D.lo, o)};
+        N = dd_add(N, n2);
+        D = dd_add(D, d2);
+    }
+    if ((threadIdx.x & 63) == 0) {
+        red[threadIdx.x >> 6][0] = N.hi;
+        red[threadIdx.x >> 6][1] = N.lo;
+        red[threadIdx.x >> 6][2] = D.hi;
+        red[threadIdx.x >> 6][3] = D.lo;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        N = {red[0][0], red[0][1]};
+        D = {red[0][2], red[0][3]};
+        for (int i = 1; i < (int)(blockDim.x >> 6); ++i) {
+            N = dd_add(N, dd{red[i][0], red[i][1]});
+            D = dd_add(D, dd{red[i][2], red[i][3]});
+        }
+    }
+    __syncthreads();
+}
+
+// Sum of the CJSO partials part[0..n) (fixed order); every thread gets the result.
+__device__ __forceinline__ void wg_sum_parts(const double *part, int n, dd &N, dd &D) {
+    __shared__ double tot[4];
+    N = {0.0, 0.0};
+    D = {0.0, 0.0};
+    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+        N = dd_add(N, dd{part[4 * i], part[4 * i + 1]});
+        D = dd_add(D, dd{part[4 * i + 2], part[4 * i + 3]});
+    }
+    wg_sum_dd2(N, D);
+    if (threadIdx.x == 0) {
+        tot[0] = N.hi;
+        tot[1] = N.lo;
+        tot[2] = D.hi;
+        tot[3] = D.lo;
+    }
+    __syncthreads();
+    N = {tot[0], tot[1]};
+    D = {tot[2], tot[3]};
+}
+
+// SOAR page, global-scale step: alpha* = N / D (the least-squares minimiser over alpha), rounded once
+// to binary32. D = 0 (every code zero) keeps the previous alpha.
+__device__ __forceinline__ float alpha_from(dd N, dd D, float prev) {
+    if (!(D.hi > 0.0)) return prev;
+    double q = N.hi / D.hi;
+    const double rem = fma(-q, D.hi, N.hi) + N.lo - q * D.lo;
+    q = q + rem / D.hi;
+    return (float)q;
+}
+
+// SOAR page, max rule: alpha = max|W| / (M_FP4 * M_FP8) = max|W| / 2688, binary32.
+__device__ __forceinline__ float max_rule_alpha(uint32_t amax_bits) { return __uint_as_float(amax_bits) / 2688.0f; }
+
+// SOAR page, max rule: the argument max|W_i| / (alpha * M_FP4) of the block scale, in binary64 (both
+// operands carry at most 26 significant bits, so its E4M3 rounding is that of the real quotient).
+__device__ __forceinline__ double max_rule_quotient(float a, float alpha) {
+    return a == 0.0f ? 0.0 : (double)a / (6.0 * (double)alpha);
+}
+
+__device__ __forceinline__ void store_codes(uint8_t *codes, int64_t b, uint32_t c0, uint32_t c1) {
+    *reinterpret_cast<uint2 *>(codes + 8 * b) = make_uint2(e2m1_clear_negzero(c0), e2m1_clear_negzero(c1));
+}
+
+// ---------------------------------------------------------------------------------- global max
+
+// Per work-group max of |w| as binary32 bits (bf16 bits are widened), plus the non-finite test
+// (any NaN or infinity makes the max >= 0x7F800000). Zeroes the stats for this call.
+template <bool F32>
+__global__ __launch_bounds__(kAmaxThreads) void k_amax(const uint4 *__restrict__ W, int64_t nchunks,
+                                                       uint32_t *__restrict__ part, nvfp4_stats_t *stats) {
+    uint32_t m = 0u;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (; i + 3 * stride < nchunks; i += 4 * stride) {
+        uint4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = W[i + u * stride];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const uint32_t d[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                if (F32) {
+                    const uint32_t a = d[k] & 0x7FFFFFFFu;
+                    m = a > m ? a : m;
+                } else {
+                    const uint32_t lo = (d[k] & 0x7FFFu) << 16, hi = d[k] & 0x7FFF0000u;
+                    m = lo > m ? lo : m;
+                    m = hi > m ? hi : m;
+                }
+            }
+        }
+    }
+    for (; i < nchunks; i += stride) {
+        const uint4 v = W[i];
+        const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            if (F32) {
+                const uint32_t a = d[k] & 0x7FFFFFFFu;
+                m = a > m ? a : m;
+            } else {
+                const uint32_t lo = (d[k] & 0x7FFFu) << 16, hi = d[k] & 0x7FFF0000u;
+                m = lo > m ? lo : m;
+                m = hi > m ? hi : m;
+            }
+        }
+    }
+    __shared__ uint32_t red[kAmaxThreads / 64];
+    m = wave_max_u32(m);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int k = 1; k < kAmaxThreads / 64; ++k) m = red[k] > m ? red[k] : m;
+        part[blockIdx.x] = m;
+        if (blockIdx.x == 0 && stats) {
+            stats->status = 0u;
+            stats->m4_blocks = 0u;
+        }
+    }
+}
+
+// ------------------------------------------------------------------------- MAX and FourOverSix
+
+template <bool F32, bool FOS>
+__global__ __launch_bounds__(256) void k_quant(const void *__restrict__ W, int64_t nblk,
+                                               const uint32_t *__restrict__ amax_part, int amax_n,
+                                               uint8_t *__restrict__ codes, uint8_t *__restrict__ scales,
+                                               float *__restrict__ alpha_out, uint8_t *__restrict__ mchoice,
+                                               nvfp4_stats_t *stats) {
+    const uint32_t abits = wg_max_parts(amax_part, amax_n);
+    const bool nonfinite = abits >= 0x7F800000u;
+    const float alpha = max_rule_alpha(abits);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        *alpha_out = nonfinite ? __builtin_nanf("") : alpha;
+        if (stats && nonfinite) atomicOr(&stats->status, NVFP4_STATUS_NONFINITE);
+    }
+    const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    bool m4 = false;
+    if (b < nblk) {
+        uint32_t c0 = 0u, c1 = 0u, sc = 0u;
+        if (!nonfinite) {
+            Blk<F32> B;
+            B.load(W, b);
+            const float a = B.amax();
+            const uint32_t d6 = e4m3_rne(max_rule_quotient(a, alpha));
+            const float v6 = e4m3_value(d6);
+            sc = d6;
+            if constexpr (!FOS) {
+                encode_scale(B.w, alpha * v6, c0, c1);
+            } else {
+                // FourOverSix write-up, section 02: scale_m4 = fp8(scale_m6 * 1.5); keep M=4 iff its
+                // squared error is strictly smaller. With S_wq, S_qq exact and s_d = alpha*Delta exact in
+                // binary64, the error minus sum w^2 is s_d*(s_d*S_qq - 2*S_wq): the inner term is exact
+                // in binary64 and the product is held exactly as a double-double.
+                double w6, q6, w4, q4;
+                uint32_t e0, e1;
+                quant_sums(B, a, alpha * v6, c0, c1, w6, q6);
+                const uint32_t d4 = e4m3_rne(1.5 * (double)v6);
+                const float v4 = e4m3_value(d4);
+                quant_sums(B, a, alpha * v4, e0, e1, w4, q4);
+                const double sd6 = (double)alpha * (double)v6, sd4 = (double)alpha * (double)v4;
+                const dd j6 = two_prod(sd6, fma(sd6, q6, -2.0 * w6));
+                const dd j4 = two_prod(sd4, fma(sd4, q4, -2.0 * w4));
+                m4 = dd_less(j4, j6);
+                if (m4) {
+                    c0 = e0;
+                    c1 = e1;
+                    sc = d4;
+                }
+            }
+        }
+        store_codes(codes, b, c0, c1);
+        scales[b] = (uint8_t)sc;
+        if (FOS && mchoice) mchoice[b] = m4 ? 1 : 0;
+    }
+    if (FOS && stats) {
+        const unsigned long long bal = __ballot(m4);
+        if ((threadIdx.x & 63) == 0 && bal) atomicAdd(&stats->m4_blocks, (uint32_t)__popcll(bal));
+    }
+}
+
+// ----------------------------------------------------------------------------------------- CJSO
+
+// Max rule plus, when rounds follow, the least-squares sums of the first alpha-step.
+template <bool F32, bool SOAR>
+__global__ __launch_bounds__(kCjsoThreads) void k_cjso_init(const void *__restrict__ W, int64_t nblk,
+                                                            const uint32_t *__restrict__ amax_part, int amax_n,
+                                                            int iters, uint8_t *__restrict__ codes,
+                                                            uint8_t *__restrict__ scales, float *__restrict__ alpha_out,
+                                                            float *__restrict__ alpha_state,
+                                                            double *__restrict__ part_out,
+                                                            uint16_t *__restrict__ brackets, nvfp4_stats_t *stats) {
+    const uint32_t abits = wg_max_parts(amax_part, amax_n);
+    const bool nonfinite = abits >= 0x7F800000u;
+    const float alpha = max_rule_alpha(abits);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        const float av = nonfinite ? __builtin_nanf("") : alpha;
+        alpha_state[0] = av;
+        if (iters == 0) *alpha_out = av;
+        if (stats && nonfinite) atomicOr(&stats->status, NVFP4_STATUS_NONFINITE);
+    }
+    dd N = {0.0, 0.0}, D = {0.0, 0.0};
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblk; b += stride) {
+        if (nonfinite) {
+            store_codes(codes, b, 0u, 0u);
+            scales[b] = 0;
+            if (SOAR) brackets[b] = 0;
+            continue;
+        }
+        Blk<F32> B;
+        B.load(W, b);
+        const float a = B.amax();
+        const double q = max_rule_quotient(a, alpha);
+        const uint32_t d = e4m3_rne(q);
+        const float v = e4m3_value(d);
+        scales[b] = (uint8_t)d;
+        uint32_t c0, c1;
+        if (iters == 0) {
+            encode_scale(B.w, alpha * v, c0, c1);
+            store_codes(codes, b, c0, c1);
+            if (SOAR) {
+                uint32_t lo, hi;
+                e4m3_bracket(q, lo, hi);
+                brackets[b] = (uint16_t)(lo | (hi << 8));
+            }
+        } else {
+            double sw, sq;
+            quant_sums(B, a, alpha * v, c0, c1, sw, sq);
+            N = dd_add(N, two_prod((double)v, sw));
+            D = dd_add(D, dd{(double)v * (double)v * sq, 0.0});
+        }
+    }
+    if (iters > 0) {
+        wg_sum_dd2(N, D);
+        if (threadIdx.x == 0) {
+            part_out[4 * blockIdx.x + 0] = N.hi;
+            part_out[4 * blockIdx.x + 1] = N.lo;
+            part_out[4 * blockIdx.x + 2] = D.hi;
+            part_out[4 * blockIdx.x + 3] = D.lo;
+        }
+    }
+}
+
+// CJSO round t (1..iters): alpha-step from the previous round's sums, re-quantise, Delta-step (SOAR
+// page, block-scale closed form, rounded to E4M3), re-quantise; then the sums for round t+1, or, in the
+// last round, the codes (and for SOAR the E4M3 bracket of the unrounded block scale).
+template <bool F32, bool SOAR>
+__global__ __launch_bounds__(kCjsoThreads) void k_cjso_iter(const void *__restrict__ W, int64_t nblk, int t, int iters,
+                                                            const double *__restrict__ part_in, int n_part,
+                                                            double *__restrict__ part_out, float *alpha_state,
+                                                            float *__restrict__ alpha_out, uint8_t *__restrict__ codes,
+                                                            uint8_t *__restrict__ scales,
+                                                            uint16_t *__restrict__ brackets) {
+    const float prev = alpha_state[(t - 1) & 1];
+    if (prev != prev) {  // non-finite input: the outputs were zeroed by the first pass
+        if (blockIdx.x == 0 && threadIdx.x == 0) {
+            alpha_state[t & 1] = prev;
+            if (t == iters) *alpha_out = prev;
+        }
+        return;
+    }
+    dd N, D;
+    wg_sum_parts(part_in, n_part, N, D);
+    const float alpha = alpha_from(N, D, prev);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        alpha_state[t & 1] = alpha;
+        if (t == iters) *alpha_out = alpha;
+    }
+    const bool last = t == iters;
+    dd Nn = {0.0, 0.0}, Dn = {0.0, 0.0};
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblk; b += stride) {
+        Blk<F32> B;
+        B.load(W, b);
+        const float a = B.amax();
+        const uint32_t d = scales[b];
+        const float v = e4m3_value(d);
+        uint32_t c0, c1;
+        double sw, sq;
+        quant_sums(B, a, alpha * v, c0, c1, sw, sq);
+        double dstar = (double)v;
+        uint32_t dn = d;
+        if (sq > 0.0) {
+            dstar = sw / ((double)alpha * sq);
+            dn = e4m3_rne(dstar);
+        }
+        scales[b] = (uint8_t)dn;
+        const float vn = e4m3_value(dn);
+        quant_sums(B, a, alpha * vn, c0, c1, sw, sq);
+        if (!last) {
+            Nn = dd_add(Nn, two_prod((double)vn, sw));
+            Dn = dd_add(Dn, dd{(double)vn * (double)vn * sq, 0.0});
+        } else {
+            store_codes(codes, b, c0, c1);
+            if (SOAR) {
+                uint32_t lo, hi;
+                e4m3_bracket(dstar, lo, hi);
+                brackets[b] = (uint16_t)(lo | (hi << 8));
+            }
+        }
+    }
+    if (!last) {
+        wg_sum_dd2(Nn, Dn);
+        if (threadIdx.x == 0) {
+            part_out[4 * blockIdx.x + 0] = Nn.hi;
+            part_out[4 * blockIdx.x + 1] = Nn.lo;
+            part_out[4 * blockIdx.x + 2] = Dn.hi;
+            part_out[4 * blockIdx.x + 3] = Dn.lo;
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------ codec kernels
+
+// One code per output byte; 8 values per lane.
+__global__ __launch_bounds__(256) void k_encode_e2m1(const float *__restrict__ x, int64_t n,
+                                                     uint8_t *__restrict__ out) {
+    const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t base = 8 * g;
+    if (base >= n) return;
+    if (base + 8 <= n) {
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = x[base + j];
+        uint32_t c = e2m1_clear_negzero(e2m1_pack8(v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7]));
+        uint32_t lo = 0u, hi = 0u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t a = (v[j] != v[j]) ? 0u : ((c >> (4 * j)) & 15u);
+            const uint32_t b = (v[4 + j] != v[4 + j]) ? 0u : ((c >> (4 * (4 + j))) & 15u);
+            lo |= a << (8 * j);
+            hi |= b << (8 * j);
+        }
+        *reinterpret_cast<uint2 *>(out + base) = make_uint2(lo, hi);
+    } else {
+        for (int64_t i = base; i < n; ++i) out[i] = (uint8_t)e2m1_soft(x[i]);
+    }
+}
+
+// SOAR page, dequantisation: w_hat = Q * (alpha * Delta). q*Delta is exact in binary32 (at most 6
+// significant bits); the product with alpha is rounded once to the output type.
+template <bool OUTF32>
+__global__ __launch_bounds__(256) void k_dequant(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales,
+                                                 const float *__restrict__ alpha_p, int64_t nblk, void *__restrict__ out) {
+    const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= nblk) return;
+    const float alpha = *alpha_p;
+    const float dv = e4m3_value(scales[b] & 0x7Fu);
+    const uint2 c = *reinterpret_cast<const uint2 *>(codes + 8 * b);
+    float o[16];
+    const uint32_t cw[2] = {c.x, c.y};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        f32x2 q0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[h], 1.0f, 0);
+        f32x2 q1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[h], 1.0f, 1);
+        f32x2 q2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[h], 1.0f, 2);
+        f32x2 q3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[h], 1.0f, 3);
+        const float q[8] = {q0.x, q0.y, q1.x, q1.y, q2.x, q2.y, q3.x, q3.y};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float qd = q[j] * dv;  // exact
+            if (OUTF32) {
+                o[8 * h + j] = qd * alpha;
+            } else {
+                // round the exact product to bf16 once: p = f + e exactly with f = fl32(p); a bf16
+                // midpoint f is resolved by the sign of e.
+                const float f = qd * alpha;
+                const float e = fmaf(qd, alpha, -f);
+                uint32_t u = __float_as_uint(f);
+                const uint32_t low = u & 0xFFFFu;
+                if (low == 0x8000u && e != 0.0f) {
+                    const bool away = (e > 0.0f) == (f > 0.0f);
+                    u = away ? u + 0x8000u : u - 0x8000u;
+                } else {
+                    u = u + 0x7FFFu + ((u >> 16) & 1u);
+                }
+                o[8 * h + j] = __uint_as_float(u & 0xFFFF0000u);
+            }
+        }
+    }
+    if (OUTF32) {
+        float4 *dst = reinterpret_cast<float4 *>(out) + 4 * b;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) dst[k] = make_float4(o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]);
+    } else {
+        uint4 *dst = reinterpret_cast<uint4 *>(out) + 2 * b;
+        uint32_t p[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) p[k] = (__float_as_uint(o[2 * k]) >> 16) | (__float_as_uint(o[2 * k + 1]) & 0xFFFF0000u);
+        dst[0] = make_uint4(p[0], p[1], p[2], p[3]);
+        dst[1] = make_uint4(p[4], p[5], p[6], p[7]);
+    }
+}
+
+// ------------------------------------------------------------------------------------ launchers
+
+int amax_groups(int64_t nchunks) {
+    int64_t g = (nchunks + kAmaxThreads * 4 - 1) / (kAmaxThreads * 4);
+    return (int)(g < 1 ? 1 : (g > kAmaxMaxGroups ? kAmaxMaxGroups : g));
+}
+
+int cjso_groups(int64_t nblk) {
+    int64_t g = (nblk + kCjsoThreads - 1) / kCjsoThreads;
+    return (int)(g < 1 ? 1 : (g > kCjsoMaxGroups ? kCjsoMaxGroups : g));
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t workspace_bytes(int64_t nblk, int mode) {
+    size_t s = align256(sizeof(uint32_t) * kAmaxMaxGroups) + align256(2 * sizeof(float)) +
+               align256(sizeof(double) * 2 * kCjsoMaxGroups * 4);
+    if (mode == NVFP4_MODE_SOAR) s += align256(sizeof(uint16_t) * (size_t)nblk);
+    return s;
+}
+
+Workspace carve(void *base, int64_t nblk) {
+    (void)nblk;
+    char *p = static_cast<char *>(base);
+    Workspace w;
+    w.amax_part = reinterpret_cast<uint32_t *>(p);
+    p += align256(sizeof(uint32_t) * kAmaxMaxGroups);
+    w.alpha_state = reinterpret_cast<float *>(p);
+    p += align256(2 * sizeof(float));
+    w.cjso_part = reinterpret_cast<double *>(p);
+    p += align256(sizeof(double) * 2 * kCjsoMaxGroups * 4);
+    w.brackets = reinterpret_cast<uint16_t *>(p);
+    return w;
+}
+
+hipError_t launch_amax(const void *W, bool f32, int64_t n, uint32_t *amax_part, int groups, nvfp4_stats_t *stats,
+                       hipStream_t stream) {
+    const int64_t nchunks = n * (f32 ? 4 : 2) / 16;
+    if (f32)
+        hipLaunchKernelGGL(k_amax<true>, dim3(groups), dim3(kAmaxThreads), 0, stream, (const uint4 *)W, nchunks,
+                           amax_part, stats);
+    else
+        hipLaunchKernelGGL(k_amax<false>, dim3(groups), dim3(kAmaxThreads), 0, stream, (const uint4 *)W, nchunks,
+                           amax_part, stats);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant(const void *W, bool f32, bool fos, int64_t nblk, const uint32_t *amax_part, int amax_n,
+                        uint8_t *codes, uint8_t *scales, float *alpha_out, uint8_t *mchoice, nvfp4_stats_t *stats,
+                        hipStream_t stream) {
+    const dim3 grid((unsigned)((nblk + 255) / 256)), block(256);
+    if (f32) {
+        if (fos)
+            hipLaunchKernelGGL((k_quant<true, true>), grid, block, 0, stream, W, nblk, amax_part, amax_n, codes, scales,
+                               alpha_out, mchoice, stats);
+        else
+            hipLaunchKernelGGL((k_quant<true, false>), grid, block, 0, stream, W, nblk, amax_part, amax_n, codes,
+                               scales, alpha_out, mchoice, stats);
+    } else {
+        if (fos)
+            hipLaunchKernelGGL((k_quant<false, true>), grid, block, 0, stream, W, nblk, amax_part, amax_n, codes,
+                               scales, alpha_out, mchoice, stats);
+        else
+            hipLaunchKernelGGL((k_quant<false, false>), grid, block, 0, stream, W, nblk, amax_part, amax_n, codes,
+                               scales, alpha_out, mchoice, stats);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_cjso_init(const void *W, bool f32, bool soar, int64_t nblk, const uint32_t *amax_part, int amax_n,
+                            int iters, uint8_t *codes, uint8_t *scales, float *alpha_out, const Workspace &ws,
+                            int groups, nvfp4_stats_t *stats, hipStream_t stream) {
+    const dim3 grid(groups), block(kCjsoThreads);
+    double *part = ws.cjso_part;  // round 0 writes buffer 0
+#define NVFP4_INIT(F, S)                                                                                          \
+    hipLaunchKernelGGL((k_cjso_init<F, S>), grid, block, 0, stream, W, nblk, amax_part, amax_n, iters, codes, scales, \
+                       alpha_out, ws.alpha_state, part, ws.brackets, stats)
+    if (f32) {
+        if (soar) NVFP4_INIT(true, true); else NVFP4_INIT(true, false);
+    } else {
+        if (soar) NVFP4_INIT(false, true); else NVFP4_INIT(false, false);
+    }
+#undef NVFP4_INIT
+    return hipGetLastError();
+}
+
+hipError_t launch_cjso_iter(const void *W, bool f32, bool soar, int64_t nblk, int t, int iters, uint8_t *codes,
+                            uint8_t *scales, float *alpha_out, const Workspace &ws, int groups, hipStream_t stream) {
+    const dim3 grid(groups), block(kCjsoThreads);
+    const double *pin = ws.cjso_part + (size_t)((t - 1) & 1) * kCjsoMaxGroups * 4;
+    double *pout = ws.cjso_part + (size_t)(t & 1) * kCjsoMaxGroups * 4;
+#define NVFP4_ITER(F, S)                                                                                          \
+    hipLaunchKernelGGL((k_cjso_iter<F, S>), grid, block, 0, stream, W, nblk, t, iters, pin, groups, pout,           \
+                       ws.alpha_state, alpha_out, codes, scales, ws.brackets)
+    if (f32) {
+        if (soar) NVFP4_ITER(true, true); else NVFP4_ITER(true, false);
+    } else {
+        if (soar) NVFP4_ITER(false, true); else NVFP4_ITER(false, false);
+    }
+#undef NVFP4_ITER
+    return hipGetLastError();
+}
+
+hipError_t launch_encode_e2m1(const float *x, int64_t n, uint8_t *codes, hipStream_t stream) {
+    const int64_t lanes = (n + 7) / 8;
+    hipLaunchKernelGGL(k_encode_e2m1, dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, stream, x, n, codes);
+    return hipGetLastError();
+}
+
+hipError_t launch_dequant(const uint8_t *codes, const uint8_t *scales, const float *alpha, int64_t nblk, void *out,
+                          bool out_f32, hipStream_t stream) {
+    const dim3 grid((unsigned)((nblk + 255) / 256)), block(256);
+    if (out_f32)
+        hipLaunchKernelGGL(k_dequant<true>, grid, block, 0, stream, codes, scales, alpha, nblk, out);
+    else
+        hipLaunchKernelGGL(k_dequant<false>, grid, block, 0, stream, codes, scales, alpha, nblk, out);
+    return hipGetLastError();
+}
+
+}  // namespace nvfp4

@@ -1,0 +1,114 @@
+"""Write the full-size expected outputs that the GPU parity tests compare against.
+
+Every value here comes from the oracle (``oracle/``) run on the seeded inputs of ``synth``; nothing
+comes from the GPU path. The oracle takes minutes at these sizes (CJSO(8) on a 14336 x 4096 matrix is
+about two), too slow for a test, so this script runs it once and stores:
+  * full_size.json: per workload, the SHA-256 of the input bytes, and per mode alpha (binary32 bits),
+    the SHA-256 of the codes and of the scales, the FourOverSix M=4 block count and the MSE;
+  * <workload>_soar_sample.npz: for the SOAR search, the expected codes and scales of a fixed sample of
+    blocks (the oracle runs the search block by block from its own CJSO state).
+
+Run from the repository root:  python tests/golden/make_golden.py  [-j 8]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+from concurrent.futures import ProcessPoolExecutor
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(os.path.dirname(HERE))
+sys.path.insert(0, ROOT)
+
+import oracle  # noqa: E402
+import synth  # noqa: E402
+
+ITERS = 8
+SOAR_SAMPLE_STRIDE = 127  # every 127th block: ~8k blocks of a 4096 x 4096 matrix
+
+
+def workloads():
+    return {
+        "c2": lambda: synth.c2(0),
+        "c3_up": lambda: synth.c3(0, 0),
+        "c3_down": lambda: synth.c3(1, 0),
+        "c5_l0_q": lambda: synth.c5(0, "q"),
+        "c5_l0_gate": lambda: synth.c5(0, "gate"),
+        "c5_l0_down": lambda: synth.c5(0, "down"),
+    }
+
+
+# which modes are stored per workload (the configurations name them)
+PLAN = {
+    "c2": ["max", "4o6", "cjso", "soar"],
+    "c3_up": ["4o6", "cjso"],
+    "c3_down": ["4o6", "cjso"],
+    "c5_l0_q": ["4o6", "soar"],
+    "c5_l0_gate": ["4o6", "soar"],
+    "c5_l0_down": ["4o6", "soar"],
+}
+
+
+def sha(a: np.ndarray) -> str:
+    return hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()
+
+
+def f32_hex(x: float) -> str:
+    return "%08x" % int(np.float32(x).view(np.uint32))
+
+
+def sample_blocks(nblk: int) -> np.ndarray:
+    return np.arange(0, nblk, SOAR_SAMPLE_STRIDE, dtype=np.int64)
+
+
+def job(name: str, mode: str):
+    W = workloads()[name]()
+    out = {"input_sha256": sha(W), "shape": list(W.shape)}
+    if mode in ("max", "4o6"):
+        r = oracle.quantize(W, mode)
+        out.update(alpha=f32_hex(r["alpha"]), codes=sha(r["codes"]), scales=sha(r["scales"]),
+                   mse=oracle.mse(W, r["codes"], r["scales"], r["alpha"]))
+        if mode == "4o6":
+            out["m4_blocks"] = int(r["mchoice"].sum())
+    elif mode == "cjso":
+        r = oracle.quantize(W, "cjso", ITERS, trace=True)
+        out.update(alpha=f32_hex(r["alpha"]), codes=sha(r["codes"]), scales=sha(r["scales"]),
+                   alpha_trace=[f32_hex(a) for a in r["alpha_trace"]],
+                   mse=oracle.mse(W, r["codes"], r["scales"], r["alpha"]))
+    else:  # soar: CJSO state of the whole matrix, then the search on sampled blocks
+        r = oracle.quantize(W, "cjso", ITERS)
+        blocks = sample_blocks(r["scales"].size)
+        c, s = oracle.soar_blocks(W, r["alpha"], r["scales"], r["dstar"], blocks)
+        fname = f"{name}_soar_sample.npz"
+        np.savez_compressed(os.path.join(HERE, fname), blocks=blocks, codes=c, scales=s)
+        out.update(alpha=f32_hex(r["alpha"]), sample=fname, sample_codes=sha(c), sample_scales=sha(s),
+                   iters=ITERS)
+    if mode == "cjso":
+        out["iters"] = ITERS
+    return name, mode, out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("-j", type=int, default=4)
+    args = ap.parse_args()
+    jobs = [(n, m) for n, modes in PLAN.items() for m in modes]
+    result = {}
+    with ProcessPoolExecutor(max_workers=args.j) as ex:
+        for name, mode, out in ex.map(job, *zip(*jobs)):
+            result.setdefault(name, {"modes": {}})
+            result[name]["input_sha256"] = out.pop("input_sha256")
+            result[name]["shape"] = out.pop("shape")
+            result[name]["modes"][mode] = out
+            print(name, mode, out.get("alpha"), flush=True)
+    with open(os.path.join(HERE, "full_size.json"), "w") as f:
+        json.dump(result, f, indent=1, sort_keys=True)
+
+
+if __name__ == "__main__":
+    main()

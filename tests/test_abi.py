@@ -1,0 +1,106 @@
+"""The HIP library loads, exports every function include/nvfp4.h declares, and rejects bad arguments on
+the host before touching a device (CPU only: no call here passes validation)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import nvfp4_block_scaled_elem_amd as nv
+from nvfp4_block_scaled_elem_amd import build as nvbuild
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4.h")
+
+OK, INVALID, SHAPE, WORKSPACE = 0, -1, -2, -3
+FAKE = 0x100000  # never dereferenced: every call below fails validation first
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(nv.LIB_PATH):
+        nvbuild.build()
+    return nv.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nvfp4_\w+)\s*\(", text)))
+
+
+def test_every_declared_function_is_exported(L):
+    names = declared_functions()
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def args(**kw):
+    a = nv._Args()
+    a.W, a.dtype, a.rows, a.cols, a.mode, a.iters = FAKE, 0, 64, 256, 0, 0
+    a.codes_out, a.scales_out, a.alpha_out = FAKE, FAKE, FAKE
+    a.workspace, a.workspace_bytes = None, 0
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,err", [
+    (dict(W=None), INVALID), (dict(codes_out=None), INVALID), (dict(scales_out=None), INVALID),
+    (dict(alpha_out=None), INVALID), (dict(rows=0), INVALID), (dict(cols=-16), INVALID),
+    (dict(cols=24), SHAPE), (dict(rows=1 << 40, cols=1 << 20), SHAPE), (dict(mode=4), INVALID),
+    (dict(mode=-1), INVALID), (dict(dtype=2), INVALID), (dict(iters=-1), INVALID), (dict(iters=1001), INVALID),
+    (dict(W=FAKE + 8), INVALID), (dict(codes_out=FAKE + 4), INVALID), (dict(alpha_out=FAKE + 2), INVALID),
+    (dict(workspace=FAKE + 64, workspace_bytes=1 << 30), INVALID),
+    (dict(workspace=FAKE, workspace_bytes=16), WORKSPACE),
+    (dict(mode=3, iters=8, workspace=FAKE, workspace_bytes=1024), WORKSPACE),
+])
+def test_quantize_ex_rejects(L, kw, err):
+    a = args(**kw)
+    assert L.nvfp4_quantize_ex(ctypes.byref(a)) == err
+
+
+def test_quantize_ex_null_args(L):
+    assert L.nvfp4_quantize_ex(None) == INVALID
+
+
+def test_stage_events_count_checked(L):
+    ev = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    a = args(mode=2, iters=3)
+    a.stage_events = ctypes.cast(ev, ctypes.c_void_p)
+    a.n_stage_events = 2
+    assert L.nvfp4_quantize_ex(ctypes.byref(a)) == INVALID
+
+
+def test_plain_entry_points_reject(L):
+    assert L.nvfp4_quantize(None, 4, 16, 0, 0, FAKE, FAKE, FAKE, None) == INVALID
+    assert L.nvfp4_quantize(FAKE, 4, 17, 0, 0, FAKE, FAKE, FAKE, None) == SHAPE
+    assert L.nvfp4_quantize_f32(FAKE, 4, 16, 9, 0, FAKE, FAKE, FAKE, None) == INVALID
+    assert L.nvfp4_encode_e2m1(None, 10, FAKE, None) == INVALID
+    assert L.nvfp4_encode_e2m1(FAKE, 10, FAKE + 1, None) == INVALID
+    assert L.nvfp4_encode_e2m1(FAKE, 0, FAKE, None) == OK  # nothing to do
+    assert L.nvfp4_dequantize(FAKE, FAKE, FAKE, 4, 24, FAKE, 0, None) == SHAPE
+    assert L.nvfp4_dequantize(FAKE, FAKE, FAKE, 4, 32, FAKE, 3, None) == INVALID
+    assert L.nvfp4_dequantize(FAKE, FAKE, FAKE, 4, 32, FAKE + 8, 1, None) == INVALID
+
+
+def test_sizes_and_counts(L):
+    assert L.nvfp4_workspace_bytes(4096, 4096, 0) > 0
+    assert L.nvfp4_workspace_bytes(4096, 4096, 3) >= L.nvfp4_workspace_bytes(4096, 4096, 2) + 2 * 4096 * 256
+    assert L.nvfp4_workspace_bytes(4096, 4095, 0) == 0
+    assert L.nvfp4_workspace_bytes(4096, 4096, 5) == 0
+    assert [L.nvfp4_kernel_count(m, 8) for m in range(4)] == [2, 2, 10, 11]
+    assert L.nvfp4_kernel_count(2, 0) == 2 and L.nvfp4_kernel_count(3, 0) == 3
+    assert L.nvfp4_kernel_count(7, 0) == -1 and L.nvfp4_kernel_count(2, -1) == -1
+
+
+def test_status_strings(L):
+    for s in (OK, INVALID, SHAPE, WORKSPACE, -4, 99):
+        assert isinstance(nv.status_string(s), str) and nv.status_string(s)
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    with pytest.raises(nv.NVFP4Error):
+        nv.quantize(torch.zeros(4, 16, dtype=torch.bfloat16), "max")
