@@ -42,7 +42,8 @@ N_MATS = 12
 ITERS = 8
 MODES = (("max", 0), ("4o6", 0), ("cjso", ITERS), ("soar", ITERS))
 SEARCH_FLOPS_PER_BLOCK = 101 * 16 * 9
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_soar_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_k_soar_4096x4096.txt")
+COPY_BYTES = 256 << 20
 KERNEL_NAMES = {
     "max": ["k_amax", "k_quant"],
     "4o6": ["k_amax", "k_quant"],
@@ -83,6 +84,8 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 256 MiB device copy 5 times (scales the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the quantizer runs on a single device and --gpus {args.gpus} is not "
@@ -90,6 +93,15 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.calibrate_copy:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": COPY_BYTES, "launches": 5}))
+        return
 
     import nvfp4_block_scaled_elem_amd as nv
     import synth
@@ -109,7 +121,6 @@ def main():
             alpha=torch.empty(1, dtype=torch.float32, device=dev),
             workspace=torch.empty(nv.workspace_bytes(ROWS, COLS, mode), dtype=torch.uint8, device=dev),
             mchoice=torch.empty((ROWS, COLS // 16), dtype=torch.uint8, device=dev) if mode == "4o6" else None,
-            stats=torch.zeros(4, dtype=torch.int32, device=dev),
         )
     nk = {mode: nv.kernel_count(mode, iters) for mode, iters in MODES}
 
@@ -118,7 +129,7 @@ def main():
         for mode, iters in MODES:
             o = out[mode]
             nv.quantize(W, mode, iters, codes=o["codes"], scales=o["scales"], alpha=o["alpha"],
-                        mchoice=o["mchoice"], stats=o["stats"], workspace=o["workspace"],
+                        mchoice=o["mchoice"], workspace=o["workspace"],
                         stage_events=events[mode] if events else None)
 
     log("warmup")
@@ -126,16 +137,38 @@ def main():
         step(s)
     torch.cuda.synchronize()
 
-    evs = [{mode: [torch.cuda.Event(enable_timing=True) for _ in range(nk[mode] + 1)] for mode, _ in MODES}
-           for _ in range(args.steps)]
+    # timed region: K steps, nothing else on the stream
     log(f"timing {args.steps} steps")
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
-        step(args.warmup + s, evs[s])
+        step(args.warmup + s)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    # per-kernel durations: the same steps again with HIP events recorded by the library around each of
+    # its kernels on the stream they run on
+    n_ev = max(20, min(args.steps, 100))
+    evs = [{mode: [torch.cuda.Event(enable_timing=True) for _ in range(nk[mode] + 1)] for mode, _ in MODES}
+           for _ in range(n_ev)]
+    log(f"instrumented pass, {n_ev} steps")
+    for s in range(n_ev):
+        step(args.warmup + s, evs[s])
+    torch.cuda.synchronize()
+
+    # the same step replayed from HIP graphs (one per resident matrix), for the launch overhead
+    graphs = []
+    for m in range(N_MATS):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(m)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    tg0 = time.perf_counter()
+    for s in range(args.steps):
+        graphs[s % N_MATS].replay()
+    torch.cuda.synchronize()
+    graph_ms_per_step = (time.perf_counter() - tg0) * 1e3 / args.steps
 
     # per-mode call times and per-kernel durations from the stage events (GPU clock)
     per_mode = {}
@@ -157,7 +190,7 @@ def main():
     search_tflops = nblk * SEARCH_FLOPS_PER_BLOCK / t_search / 1e12
     per_mode["soar"]["search_ms"] = round(t_search * 1e3, 5)
     per_mode["soar"]["search_frac_fp32_peak"] = round(search_tflops * 1e12 / PEAK_FP32, 4)
-    m4 = int(out["4o6"]["stats"][1].item())
+    m4 = int(out["4o6"]["mchoice"].sum().item())
     per_mode["4o6"]["m4_fraction"] = round(m4 / nblk, 4)
     # HBM view of the memory-bound single passes: algorithmic bytes of the whole call (read W once,
     # write codes and scales) over the call time
@@ -165,12 +198,18 @@ def main():
     for mode in ("max", "4o6"):
         per_mode[mode]["algo_GBps"] = round(algo_bytes / (per_mode[mode]["ms"] * 1e-3) / 1e9, 2)
 
+    # HBM bytes per launch of the search kernel from the committed rocprofv3 counter summary, used only
+    # while the kernel sources are the ones it was taken with
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
+        fields = {}
         with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
-        if t.get("source_hash") == source_hash():
-            traffic = t.get("bytes_per_launch")
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    fields[k.strip()] = v.strip()
+        if fields.get("source_hash") == source_hash():
+            traffic = int(float(fields["bytes_per_launch"]))
     roofline = {"bound": "alu", "kernel": "k_soar (decoupled search)", "achieved": round(search_tflops, 3),
                 "peak": PEAK_FP32 / 1e12, "unit": "TFLOP/s", "frac": round(search_tflops * 1e12 / PEAK_FP32, 4),
                 "traffic": traffic, "algorithmic_flops_per_launch": nblk * SEARCH_FLOPS_PER_BLOCK,
@@ -186,6 +225,7 @@ def main():
                                "CJSO(8), SOAR(8)", "rows": ROWS, "cols": COLS, "input_dtype": "bf16",
                    "matrices": N_MATS, "cjso_iters": ITERS, "parallelism": "single GPU"},
         "modes": per_mode,
+        "graph_replay_ms_per_step": round(graph_ms_per_step, 5),
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:

@@ -17,7 +17,7 @@ import os
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libnvfp4.so")
+LIB_PATH = os.environ.get("NVFP4_LIB", os.path.join(HERE, "libnvfp4.so"))
 
 MODES = {"max": 0, "4o6": 1, "cjso": 2, "soar": 3}
 DTYPES = {torch.bfloat16: 0, torch.float32: 1}

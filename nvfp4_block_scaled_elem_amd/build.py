@@ -24,9 +24,10 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC] + FLAGS + [os.path.join(CSRC, s) for s in SOURCES] + ["-o", tmp]
+def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
+    """Compile the library to `out`; `defines` are extra -D settings of the tuning knobs in launch.hpp."""
+    tmp = out + ".tmp"
+    cmd = [HIPCC] + FLAGS + ["-D" + d for d in defines] + [os.path.join(CSRC, s) for s in SOURCES] + ["-o", tmp]
     r = subprocess.run(cmd, cwd=CSRC, capture_output=True, text=True)
     msgs = [l for l in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in l]
     if r.returncode != 0:
@@ -34,8 +35,8 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({r.returncode})")
     if verbose and msgs:
         print("\n".join(msgs))
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

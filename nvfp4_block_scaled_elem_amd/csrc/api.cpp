@@ -65,13 +65,13 @@ int run(const nvfp4_args_t *a, void *ws_base) {
     if (a->mode == NVFP4_MODE_MAX || a->mode == NVFP4_MODE_FOUR_OVER_SIX) {
         const bool fos = a->mode == NVFP4_MODE_FOUR_OVER_SIX;
         if (launch_quant(a->W, f32, fos, nblk, ws.amax_part, ga, a->codes_out, a->scales_out, a->alpha_out,
-                         fos ? a->mchoice_out : nullptr, a->stats_out, st) != hipSuccess ||
+                         fos ? a->mchoice_out : nullptr, a->stats_out, ws.m4_part, st) != hipSuccess ||
             !mark(a, j++))
             return NVFP4_ERR_HIP;
         return NVFP4_OK;
     }
     const bool soar = a->mode == NVFP4_MODE_SOAR;
-    const int gc = cjso_groups(nblk);
+    const int gc = stream_groups(nblk);
     if (launch_cjso_init(a->W, f32, soar, nblk, ws.amax_part, ga, a->iters, a->codes_out, a->scales_out, a->alpha_out,
                          ws, gc, a->stats_out, st) != hipSuccess ||
         !mark(a, j++))

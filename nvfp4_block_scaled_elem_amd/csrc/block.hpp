@@ -14,6 +14,17 @@
 
 namespace nvfp4 {
 
+// The raw bytes of a block, loaded ahead of use (bf16: 2 x 16 bytes, fp32: 4 x 16 bytes).
+template <bool F32>
+struct Raw {
+    uint4 v[F32 ? 4 : 2];
+    __device__ __forceinline__ void load(const void *W, int64_t b) {
+        const uint4 *s = reinterpret_cast<const uint4 *>(W) + (F32 ? 4 : 2) * b;
+#pragma unroll
+        for (int k = 0; k < (F32 ? 4 : 2); ++k) v[k] = s[k];
+    }
+};
+
 template <bool F32>
 struct Blk;
 
@@ -21,16 +32,19 @@ template <>
 struct Blk<false> {  // bf16 input: 32 bytes
     float w[16];
     uint32_t p[8];  // the raw bf16 pairs (element 2k low, 2k+1 high)
-    __device__ __forceinline__ void load(const void *W, int64_t b) {
-        const uint4 *s = reinterpret_cast<const uint4 *>(W) + 2 * b;
-        const uint4 a = s[0], c = s[1];
-        p[0] = a.x; p[1] = a.y; p[2] = a.z; p[3] = a.w;
-        p[4] = c.x; p[5] = c.y; p[6] = c.z; p[7] = c.w;
+    __device__ __forceinline__ void set(const Raw<false> &r) {
+        p[0] = r.v[0].x; p[1] = r.v[0].y; p[2] = r.v[0].z; p[3] = r.v[0].w;
+        p[4] = r.v[1].x; p[5] = r.v[1].y; p[6] = r.v[1].z; p[7] = r.v[1].w;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             w[2 * k] = bf16_lo(p[k]);
             w[2 * k + 1] = bf16_hi(p[k]);
         }
+    }
+    __device__ __forceinline__ void load(const void *W, int64_t b) {
+        Raw<false> r;
+        r.load(W, b);
+        set(r);
     }
     __device__ __forceinline__ float amax() const {
         float a = 0.0f;
@@ -43,13 +57,19 @@ struct Blk<false> {  // bf16 input: 32 bytes
 template <>
 struct Blk<true> {  // fp32 input: 64 bytes
     float w[16];
-    __device__ __forceinline__ void load(const void *W, int64_t b) {
-        const float4 *s = reinterpret_cast<const float4 *>(W) + 4 * b;
+    __device__ __forceinline__ void set(const Raw<true> &r) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            const float4 v = s[k];
-            w[4 * k] = v.x; w[4 * k + 1] = v.y; w[4 * k + 2] = v.z; w[4 * k + 3] = v.w;
+            w[4 * k] = __uint_as_float(r.v[k].x);
+            w[4 * k + 1] = __uint_as_float(r.v[k].y);
+            w[4 * k + 2] = __uint_as_float(r.v[k].z);
+            w[4 * k + 3] = __uint_as_float(r.v[k].w);
         }
+    }
+    __device__ __forceinline__ void load(const void *W, int64_t b) {
+        Raw<true> r;
+        r.load(W, b);
+        set(r);
     }
     __device__ __forceinline__ float amax() const {
         float a = 0.0f;
@@ -136,16 +156,53 @@ __device__ __forceinline__ void sums_f64(uint32_t c0, uint32_t c1, const float *
     acc_f64<3>(c1, w[14], w[15], sw, sq);
 }
 
-// Codes for the scale s and the exact sums of the block.
-template <bool F32>
-__device__ __forceinline__ void quant_sums(const Blk<F32> &B, float amax, float s, uint32_t &c0, uint32_t &c1,
-                                           double &sw, double &sq) {
-    if (s == 0.0f) {
-        c0 = c1 = 0u;
-        sw = sq = 0.0;
-        return;
+// s = fl(alpha * Delta) and r = fl(1/s) (0 for s = 0) for every E4M3 code, built once per work-group.
+// lim[c] = 2^(ilogb(s)+13): a bf16 block's binary32 S_wq below it is exact (see the header; the
+// products w*q are all >= 0, so every partial sum is at most the final one).
+struct ScaleTab {
+    float s[128];
+    float r[128];
+    float lim[128];
+};
+
+__device__ __forceinline__ void build_scale_tab(ScaleTab &T, float alpha) {
+    for (int c = threadIdx.x; c < 128; c += blockDim.x) {
+        const float s = c < 0x7F ? alpha * e4m3_value((uint32_t)c) : 0.0f;
+        T.s[c] = s;
+        T.r[c] = s == 0.0f ? 0.0f : 1.0f / s;
+        T.lim[c] = s > 0.0f ? ldexpf(1.0f, ilogbf(s) + 13) : INFINITY;  // s = 0: every sum is 0
     }
-    const float r = 1.0f / s;
+    __syncthreads();
+}
+
+// Codes and exact sums for table entry d, without the block max: the binary32 sums are taken first and
+// kept when S_wq is below the exactness limit, else the block is summed again in binary64.
+template <bool F32>
+__device__ __forceinline__ void quant_sums_t(const Blk<F32> &B, const ScaleTab &T, uint32_t d, uint32_t &c0,
+                                             uint32_t &c1, double &sw, double &sq) {
+    const float r = T.r[d];
+    const bool rfin = finite_pos(r);
+    if (rfin)
+        encode16(B.w, r, c0, c1);
+    else
+        encode16_soft(B.w, r, c0, c1);
+    if constexpr (!F32) {
+        float a, q;
+        sums_bf16(c0, c1, B.p, a, q);
+        if (rfin && a < T.lim[d]) {
+            sw = a;
+            sq = q;
+            return;
+        }
+    }
+    sums_f64(c0, c1, B.w, sw, sq);
+}
+
+// Codes for the scale s (reciprocal r = fl(1/s), or 0 when s = 0: every code is then 0) and the exact
+// sums of the block.
+template <bool F32>
+__device__ __forceinline__ void quant_sums_r(const Blk<F32> &B, float amax, float s, float r, uint32_t &c0,
+                                             uint32_t &c1, double &sw, double &sq) {
     const bool rfin = finite_pos(r);
     if (rfin)
         encode16(B.w, r, c0, c1);
@@ -161,6 +218,22 @@ __device__ __forceinline__ void quant_sums(const Blk<F32> &B, float amax, float 
         }
     }
     sums_f64(c0, c1, B.w, sw, sq);
+}
+
+template <bool F32>
+__device__ __forceinline__ void quant_sums(const Blk<F32> &B, float amax, float s, uint32_t &c0, uint32_t &c1,
+                                           double &sw, double &sq) {
+    quant_sums_r(B, amax, s, s == 0.0f ? 0.0f : 1.0f / s, c0, c1, sw, sq);
+}
+
+// Running sum hi + lo of exact binary64 terms: TwoSum into hi, errors gathered in lo (renormalised by
+// dd_add when partial sums are combined).
+__device__ __forceinline__ void acc2(dd &A, double x_hi, double x_lo) {
+    const double s = A.hi + x_hi;
+    const double bb = s - A.hi;
+    const double e = (A.hi - (s - bb)) + (x_hi - bb);
+    A.hi = s;
+    A.lo += e + x_lo;
 }
 
 }  // namespace nvfp4

@@ -10,22 +10,42 @@
 
 namespace nvfp4 {
 
-// Work-group counts of the reduction kernels: the global max pass and the persistent CJSO passes.
-// Their per-work-group partial results are what the next kernel reduces, so they stay small.
+// Work-group counts of the reduction kernels: the global max pass and the streaming per-block passes
+// (MAX, FourOverSix, CJSO). Their per-work-group partial results are what every work-group of the next
+// kernel reduces, so the streaming passes use a fixed grid of at most two work-groups per CU and each
+// thread walks its blocks kChunk at a time. The defaults are the fastest of the settings measured on
+// an MI355X for a 4096 x 4096 matrix; the macros exist so that other settings can be built and timed.
+#ifndef NVFP4_STREAM_THREADS
+#define NVFP4_STREAM_THREADS 512
+#endif
+#ifndef NVFP4_STREAM_GROUPS
+#define NVFP4_STREAM_GROUPS 512
+#endif
+#ifndef NVFP4_CHUNK
+#define NVFP4_CHUNK 2
+#endif
+#ifndef NVFP4_PREFETCH_FIRST  // issue the first loads before the work-group prologue
+#define NVFP4_PREFETCH_FIRST 0
+#endif
+#ifndef NVFP4_SUM_GUARD  // CJSO rounds: exactness guard on the binary32 sum instead of the block max
+#define NVFP4_SUM_GUARD 0
+#endif
 constexpr int kAmaxThreads = 256;
 constexpr int kAmaxMaxGroups = 1024;
-constexpr int kCjsoThreads = 256;
-constexpr int kCjsoMaxGroups = 1024;
+constexpr int kStreamThreads = NVFP4_STREAM_THREADS;
+constexpr int kStreamMaxGroups = NVFP4_STREAM_GROUPS;
+constexpr int kChunk = NVFP4_CHUNK;
 
 int amax_groups(int64_t nchunks);
-int cjso_groups(int64_t nblk);
+int stream_groups(int64_t nblk);
 
 // Scratch layout inside the workspace (byte offsets, 256-byte aligned pieces).
 struct Workspace {
     uint32_t *amax_part;  // [kAmaxMaxGroups]   max |w| bits per work-group
     float *alpha_state;   // [2]                alpha of the previous / current CJSO round
-    double *cjso_part;    // [2][kCjsoMaxGroups][4] (N.hi, N.lo, D.hi, D.lo) per work-group
-    uint16_t *brackets;   // [nblk]             E4M3 codes lo | hi << 8 around the unrounded CJSO scale
+    double *cjso_part;    // [2][kStreamMaxGroups][4] (N.hi, N.lo, D.hi, D.lo) per work-group
+    uint16_t *brackets;   // [nblk]             E4M3 codes lo | hi << 8 around the unrounded CJSO scale (SOAR)
+    uint32_t *m4_part;    // [kStreamMaxGroups] FourOverSix M=4 counts per work-group (same offset)
 };
 size_t workspace_bytes(int64_t nblk, int mode);
 Workspace carve(void *base, int64_t nblk);
@@ -34,7 +54,7 @@ hipError_t launch_amax(const void *W, bool f32, int64_t n, uint32_t *amax_part, 
                        hipStream_t stream);
 hipError_t launch_quant(const void *W, bool f32, bool four_over_six, int64_t nblk, const uint32_t *amax_part,
                         int amax_n, uint8_t *codes, uint8_t *scales, float *alpha_out, uint8_t *mchoice,
-                        nvfp4_stats_t *stats, hipStream_t stream);
+                        nvfp4_stats_t *stats, uint32_t *m4_part, hipStream_t stream);
 hipError_t launch_cjso_init(const void *W, bool f32, bool soar, int64_t nblk, const uint32_t *amax_part, int amax_n,
                             int iters, uint8_t *codes, uint8_t *scales, float *alpha_out, const Workspace &ws,
                             int groups, nvfp4_stats_t *stats, hipStream_t stream);

@@ -109,6 +109,48 @@ __device__ __forceinline__ void store_codes(uint8_t *codes, int64_t b, uint32_t 
     *reinterpret_cast<uint2 *>(codes + 8 * b) = make_uint2(e2m1_clear_negzero(c0), e2m1_clear_negzero(c1));
 }
 
+// Visit this thread's blocks b = gid, gid + S, gid + 2S, ... (S = all threads of the grid), issuing the
+// loads of kChunk blocks before processing any of them so that each lane keeps several 16-byte loads in
+// flight.
+// The loads of a chunk (its blocks and, when `sc_in` is given, their scale bytes) are all issued before
+// any of its blocks is processed; with NVFP4_PREFETCH_FIRST the first chunk's loads also precede
+// `prologue` (run by every thread of the work-group). f(b, B, sc) gets the block and its scale byte.
+template <bool F32, class P, class F>
+__device__ __forceinline__ void for_my_blocks(const void *__restrict__ W, const uint8_t *__restrict__ sc_in,
+                                              int64_t nblk, P &&prologue, F &&f) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    int64_t base = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    Raw<F32> r[kChunk];
+    uint32_t sc[kChunk];
+    auto load = [&] {
+#pragma unroll
+        for (int c = 0; c < kChunk; ++c) {
+            const int64_t b = base + c * stride;
+            sc[c] = 0u;
+            if (b < nblk) {
+                r[c].load(W, b);
+                if (sc_in) sc[c] = sc_in[b];
+            }
+        }
+    };
+    if (!NVFP4_PREFETCH_FIRST) prologue();
+    load();
+    if (NVFP4_PREFETCH_FIRST) prologue();
+    while (base < nblk) {
+#pragma unroll
+        for (int c = 0; c < kChunk; ++c) {
+            const int64_t b = base + c * stride;
+            if (b < nblk) {
+                Blk<F32> B;
+                B.set(r[c]);
+                f(b, B, sc[c]);
+            }
+        }
+        base += kChunk * stride;
+        load();
+    }
+}
+
 // ---------------------------------------------------------------------------------- global max
 
 // Per work-group max of |w| as binary32 bits (bf16 bits are widened), plus the non-finite test
@@ -171,42 +213,53 @@ __global__ __launch_bounds__(kAmaxThreads) void k_amax(const uint4 *__restrict__
 // ------------------------------------------------------------------------- MAX and FourOverSix
 
 template <bool F32, bool FOS>
-__global__ __launch_bounds__(256) void k_quant(const void *__restrict__ W, int64_t nblk,
-                                               const uint32_t *__restrict__ amax_part, int amax_n,
-                                               uint8_t *__restrict__ codes, uint8_t *__restrict__ scales,
-                                               float *__restrict__ alpha_out, uint8_t *__restrict__ mchoice,
-                                               nvfp4_stats_t *stats) {
+__global__ __launch_bounds__(kStreamThreads) void k_quant(const void *__restrict__ W, int64_t nblk,
+                                                          const uint32_t *__restrict__ amax_part, int amax_n,
+                                                          uint8_t *__restrict__ codes, uint8_t *__restrict__ scales,
+                                                          float *__restrict__ alpha_out, uint8_t *__restrict__ mchoice,
+                                                          nvfp4_stats_t *stats, uint32_t *__restrict__ m4_part) {
     const uint32_t abits = wg_max_parts(amax_part, amax_n);
     const bool nonfinite = abits >= 0x7F800000u;
     const float alpha = max_rule_alpha(abits);
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         *alpha_out = nonfinite ? __builtin_nanf("") : alpha;
-        if (stats && nonfinite) atomicOr(&stats->status, NVFP4_STATUS_NONFINITE);
+        if (stats) stats->status = nonfinite ? NVFP4_STATUS_NONFINITE : 0u;
     }
-    const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    bool m4 = false;
-    if (b < nblk) {
-        uint32_t c0 = 0u, c1 = 0u, sc = 0u;
-        if (!nonfinite) {
-            Blk<F32> B;
-            B.load(W, b);
+    __shared__ ScaleTab T;
+    uint32_t m4count = 0u;
+    if (nonfinite) {
+        const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+        for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblk; b += stride) {
+            store_codes(codes, b, 0u, 0u);
+            scales[b] = 0;
+            if (FOS && mchoice) mchoice[b] = 0;
+        }
+    } else {
+        for_my_blocks<F32>(W, nullptr, nblk, [&] { build_scale_tab(T, alpha); },
+                           [&](int64_t b, const Blk<F32> &B, uint32_t) {
+            uint32_t c0, c1, sc;
+            bool m4 = false;
             const float a = B.amax();
             const uint32_t d6 = e4m3_rne(max_rule_quotient(a, alpha));
             const float v6 = e4m3_value(d6);
             sc = d6;
             if constexpr (!FOS) {
-                encode_scale(B.w, alpha * v6, c0, c1);
+                const float r = T.r[d6];
+                if (finite_pos(r))
+                    encode16(B.w, r, c0, c1);
+                else
+                    encode16_soft(B.w, r, c0, c1);
             } else {
-                // FourOverSix write-up, section 02: scale_m4 = fp8(scale_m6 * 1.5); keep M=4 iff its
-                // squared error is strictly smaller. With S_wq, S_qq exact and s_d = alpha*Delta exact in
-                // binary64, the error minus sum w^2 is s_d*(s_d*S_qq - 2*S_wq): the inner term is exact
-                // in binary64 and the product is held exactly as a double-double.
+                // FourOverSix write-up, section 02: scale_m4 = fp8(scale_m6 * 1.5); keep M=4 iff its squared
+                // error is strictly smaller. With S_wq, S_qq exact and s_d = alpha*Delta exact in binary64,
+                // the error minus sum w^2 is s_d*(s_d*S_qq - 2*S_wq): the inner term is exact in binary64
+                // and the product is held exactly as a double-double.
                 double w6, q6, w4, q4;
                 uint32_t e0, e1;
-                quant_sums(B, a, alpha * v6, c0, c1, w6, q6);
+                quant_sums_r(B, a, T.s[d6], T.r[d6], c0, c1, w6, q6);
                 const uint32_t d4 = e4m3_rne(1.5 * (double)v6);
                 const float v4 = e4m3_value(d4);
-                quant_sums(B, a, alpha * v4, e0, e1, w4, q4);
+                quant_sums_r(B, a, T.s[d4], T.r[d4], e0, e1, w4, q4);
                 const double sd6 = (double)alpha * (double)v6, sd4 = (double)alpha * (double)v4;
                 const dd j6 = two_prod(sd6, fma(sd6, q6, -2.0 * w6));
                 const dd j4 = two_prod(sd4, fma(sd4, q4, -2.0 * w4));
@@ -216,29 +269,51 @@ __global__ __launch_bounds__(256) void k_quant(const void *__restrict__ W, int64
                     c1 = e1;
                     sc = d4;
                 }
+                if (mchoice) mchoice[b] = m4 ? 1 : 0;
+                m4count += m4 ? 1u : 0u;
             }
+            store_codes(codes, b, c0, c1);
+            scales[b] = (uint8_t)sc;
+        });
+    }
+    if (FOS && m4_part) {  // per work-group count of M=4 blocks (summed by k_count only if asked)
+        __shared__ uint32_t cnt[kStreamThreads / 64];
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) m4count += (uint32_t)__shfl_xor((int)m4count, o);
+        if ((threadIdx.x & 63) == 0) cnt[threadIdx.x >> 6] = m4count;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            uint32_t t = 0u;
+            for (int i = 0; i < kStreamThreads / 64; ++i) t += cnt[i];
+            m4_part[blockIdx.x] = t;
         }
-        store_codes(codes, b, c0, c1);
-        scales[b] = (uint8_t)sc;
-        if (FOS && mchoice) mchoice[b] = m4 ? 1 : 0;
     }
-    if (FOS && stats) {
-        const unsigned long long bal = __ballot(m4);
-        if ((threadIdx.x & 63) == 0 && bal) atomicAdd(&stats->m4_blocks, (uint32_t)__popcll(bal));
-    }
+}
+
+// stats->m4_blocks = sum of the per-work-group counts (one work-group, fixed order).
+__global__ __launch_bounds__(256) void k_count(const uint32_t *__restrict__ part, int64_t n, nvfp4_stats_t *stats) {
+    __shared__ uint32_t red[4];
+    uint32_t c = 0u;
+    for (int64_t i = threadIdx.x; i < n; i += blockDim.x) c += part[i];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) c += (uint32_t)__shfl_xor((int)c, o);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = c;
+    __syncthreads();
+    if (threadIdx.x == 0) stats->m4_blocks = red[0] + red[1] + red[2] + red[3];
 }
 
 // ----------------------------------------------------------------------------------------- CJSO
 
 // Max rule plus, when rounds follow, the least-squares sums of the first alpha-step.
 template <bool F32, bool SOAR>
-__global__ __launch_bounds__(kCjsoThreads) void k_cjso_init(const void *__restrict__ W, int64_t nblk,
-                                                            const uint32_t *__restrict__ amax_part, int amax_n,
-                                                            int iters, uint8_t *__restrict__ codes,
-                                                            uint8_t *__restrict__ scales, float *__restrict__ alpha_out,
-                                                            float *__restrict__ alpha_state,
-                                                            double *__restrict__ part_out,
-                                                            uint16_t *__restrict__ brackets, nvfp4_stats_t *stats) {
+__global__ __launch_bounds__(kStreamThreads) void k_cjso_init(const void *__restrict__ W, int64_t nblk,
+                                                              const uint32_t *__restrict__ amax_part, int amax_n,
+                                                              int iters, uint8_t *__restrict__ codes,
+                                                              uint8_t *__restrict__ scales,
+                                                              float *__restrict__ alpha_out,
+                                                              float *__restrict__ alpha_state,
+                                                              double *__restrict__ part_out,
+                                                              uint16_t *__restrict__ brackets, nvfp4_stats_t *stats) {
     const uint32_t abits = wg_max_parts(amax_part, amax_n);
     const bool nonfinite = abits >= 0x7F800000u;
     const float alpha = max_rule_alpha(abits);
@@ -246,39 +321,46 @@ __global__ __launch_bounds__(kCjsoThreads) void k_cjso_init(const void *__restri
         const float av = nonfinite ? __builtin_nanf("") : alpha;
         alpha_state[0] = av;
         if (iters == 0) *alpha_out = av;
-        if (stats && nonfinite) atomicOr(&stats->status, NVFP4_STATUS_NONFINITE);
+        if (stats) stats->status = nonfinite ? NVFP4_STATUS_NONFINITE : 0u;
     }
+    __shared__ ScaleTab T;
     dd N = {0.0, 0.0}, D = {0.0, 0.0};
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblk; b += stride) {
-        if (nonfinite) {
+    if (nonfinite) {
+        const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+        for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblk; b += stride) {
             store_codes(codes, b, 0u, 0u);
             scales[b] = 0;
             if (SOAR) brackets[b] = 0;
-            continue;
         }
-        Blk<F32> B;
-        B.load(W, b);
-        const float a = B.amax();
-        const double q = max_rule_quotient(a, alpha);
-        const uint32_t d = e4m3_rne(q);
-        const float v = e4m3_value(d);
-        scales[b] = (uint8_t)d;
-        uint32_t c0, c1;
-        if (iters == 0) {
-            encode_scale(B.w, alpha * v, c0, c1);
-            store_codes(codes, b, c0, c1);
-            if (SOAR) {
-                uint32_t lo, hi;
-                e4m3_bracket(q, lo, hi);
-                brackets[b] = (uint16_t)(lo | (hi << 8));
+    } else {
+        for_my_blocks<F32>(W, nullptr, nblk, [&] { build_scale_tab(T, alpha); },
+                           [&](int64_t b, const Blk<F32> &B, uint32_t) {
+            const float a = B.amax();
+            const double q = max_rule_quotient(a, alpha);
+            const uint32_t d = e4m3_rne(q);
+            const float v = e4m3_value(d);
+            scales[b] = (uint8_t)d;
+            uint32_t c0, c1;
+            if (iters == 0) {
+                const float r = T.r[d];
+                if (finite_pos(r))
+                    encode16(B.w, r, c0, c1);
+                else
+                    encode16_soft(B.w, r, c0, c1);
+                store_codes(codes, b, c0, c1);
+                if (SOAR) {
+                    uint32_t lo, hi;
+                    e4m3_bracket(q, lo, hi);
+                    brackets[b] = (uint16_t)(lo | (hi << 8));
+                }
+            } else {
+                double sw, sq;
+                quant_sums_t(B, T, d, c0, c1, sw, sq);
+                const dd t = two_prod((double)v, sw);
+                acc2(N, t.hi, t.lo);
+                acc2(D, (double)v * (double)v * sq, 0.0);
             }
-        } else {
-            double sw, sq;
-            quant_sums(B, a, alpha * v, c0, c1, sw, sq);
-            N = dd_add(N, two_prod((double)v, sw));
-            D = dd_add(D, dd{(double)v * (double)v * sq, 0.0});
-        }
+        });
     }
     if (iters > 0) {
         wg_sum_dd2(N, D);
@@ -295,12 +377,12 @@ __global__ __launch_bounds__(kCjsoThreads) void k_cjso_init(const void *__restri
 // page, block-scale closed form, rounded to E4M3), re-quantise; then the sums for round t+1, or, in the
 // last round, the codes (and for SOAR the E4M3 bracket of the unrounded block scale).
 template <bool F32, bool SOAR>
-__global__ __launch_bounds__(kCjsoThreads) void k_cjso_iter(const void *__restrict__ W, int64_t nblk, int t, int iters,
-                                                            const double *__restrict__ part_in, int n_part,
-                                                            double *__restrict__ part_out, float *alpha_state,
-                                                            float *__restrict__ alpha_out, uint8_t *__restrict__ codes,
-                                                            uint8_t *__restrict__ scales,
-                                                            uint16_t *__restrict__ brackets) {
+__global__ __launch_bounds__(kStreamThreads) void k_cjso_iter(const void *__restrict__ W, int64_t nblk, int t,
+                                                              int iters, const double *__restrict__ part_in,
+                                                              int n_part, double *__restrict__ part_out,
+                                                              float *alpha_state, float *__restrict__ alpha_out,
+                                                              uint8_t *__restrict__ codes, uint8_t *__restrict__ scales,
+                                                              uint16_t *__restrict__ brackets) {
     const float prev = alpha_state[(t - 1) & 1];
     if (prev != prev) {  // non-finite input: the outputs were zeroed by the first pass
         if (blockIdx.x == 0 && threadIdx.x == 0) {
@@ -309,25 +391,30 @@ __global__ __launch_bounds__(kCjsoThreads) void k_cjso_iter(const void *__restri
         }
         return;
     }
-    dd N, D;
-    wg_sum_parts(part_in, n_part, N, D);
-    const float alpha = alpha_from(N, D, prev);
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
-        alpha_state[t & 1] = alpha;
-        if (t == iters) *alpha_out = alpha;
-    }
     const bool last = t == iters;
+    __shared__ ScaleTab T;
+    float alpha = prev;
     dd Nn = {0.0, 0.0}, Dn = {0.0, 0.0};
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblk; b += stride) {
-        Blk<F32> B;
-        B.load(W, b);
-        const float a = B.amax();
-        const uint32_t d = scales[b];
+    auto prologue = [&] {
+        dd N, D;
+        wg_sum_parts(part_in, n_part, N, D);
+        alpha = alpha_from(N, D, prev);
+        if (blockIdx.x == 0 && threadIdx.x == 0) {
+            alpha_state[t & 1] = alpha;
+            if (t == iters) *alpha_out = alpha;
+        }
+        build_scale_tab(T, alpha);
+    };
+    for_my_blocks<F32>(W, scales, nblk, prologue, [&](int64_t b, const Blk<F32> &B, uint32_t d) {
         const float v = e4m3_value(d);
         uint32_t c0, c1;
         double sw, sq;
-        quant_sums(B, a, alpha * v, c0, c1, sw, sq);
+#if NVFP4_SUM_GUARD
+        quant_sums_t(B, T, d, c0, c1, sw, sq);
+#else
+        const float a = B.amax();
+        quant_sums_r(B, a, T.s[d], T.r[d], c0, c1, sw, sq);
+#endif
         double dstar = (double)v;
         uint32_t dn = d;
         if (sq > 0.0) {
@@ -336,10 +423,15 @@ __global__ __launch_bounds__(kCjsoThreads) void k_cjso_iter(const void *__restri
         }
         scales[b] = (uint8_t)dn;
         const float vn = e4m3_value(dn);
-        quant_sums(B, a, alpha * vn, c0, c1, sw, sq);
+#if NVFP4_SUM_GUARD
+        quant_sums_t(B, T, dn, c0, c1, sw, sq);
+#else
+        quant_sums_r(B, a, T.s[dn], T.r[dn], c0, c1, sw, sq);
+#endif
         if (!last) {
-            Nn = dd_add(Nn, two_prod((double)vn, sw));
-            Dn = dd_add(Dn, dd{(double)vn * (double)vn * sq, 0.0});
+            const dd tn = two_prod((double)vn, sw);
+            acc2(Nn, tn.hi, tn.lo);
+            acc2(Dn, (double)vn * (double)vn * sq, 0.0);
         } else {
             store_codes(codes, b, c0, c1);
             if (SOAR) {
@@ -348,7 +440,7 @@ __global__ __launch_bounds__(kCjsoThreads) void k_cjso_iter(const void *__restri
                 brackets[b] = (uint16_t)(lo | (hi << 8));
             }
         }
-    }
+    });
     if (!last) {
         wg_sum_dd2(Nn, Dn);
         if (threadIdx.x == 0) {
@@ -449,16 +541,17 @@ int amax_groups(int64_t nchunks) {
     return (int)(g < 1 ? 1 : (g > kAmaxMaxGroups ? kAmaxMaxGroups : g));
 }
 
-int cjso_groups(int64_t nblk) {
-    int64_t g = (nblk + kCjsoThreads - 1) / kCjsoThreads;
-    return (int)(g < 1 ? 1 : (g > kCjsoMaxGroups ? kCjsoMaxGroups : g));
+int stream_groups(int64_t nblk) {
+    int64_t g = (nblk + (int64_t)kStreamThreads * kChunk - 1) / ((int64_t)kStreamThreads * kChunk);
+    return (int)(g < 1 ? 1 : (g > kStreamMaxGroups ? kStreamMaxGroups : g));
 }
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t workspace_bytes(int64_t nblk, int mode) {
     size_t s = align256(sizeof(uint32_t) * kAmaxMaxGroups) + align256(2 * sizeof(float)) +
-               align256(sizeof(double) * 2 * kCjsoMaxGroups * 4);
+               align256(sizeof(double) * 2 * kStreamMaxGroups * 4);
+    if (mode == NVFP4_MODE_FOUR_OVER_SIX) s += align256(sizeof(uint32_t) * kStreamMaxGroups);
     if (mode == NVFP4_MODE_SOAR) s += align256(sizeof(uint16_t) * (size_t)nblk);
     return s;
 }
@@ -472,8 +565,9 @@ Workspace carve(void *base, int64_t nblk) {
     w.alpha_state = reinterpret_cast<float *>(p);
     p += align256(2 * sizeof(float));
     w.cjso_part = reinterpret_cast<double *>(p);
-    p += align256(sizeof(double) * 2 * kCjsoMaxGroups * 4);
-    w.brackets = reinterpret_cast<uint16_t *>(p);
+    p += align256(sizeof(double) * 2 * kStreamMaxGroups * 4);
+    w.brackets = reinterpret_cast<uint16_t *>(p);  // SOAR only
+    w.m4_part = reinterpret_cast<uint32_t *>(p);    // FourOverSix only (same offset: the modes differ)
     return w;
 }
 
@@ -491,30 +585,33 @@ hipError_t launch_amax(const void *W, bool f32, int64_t n, uint32_t *amax_part, 
 
 hipError_t launch_quant(const void *W, bool f32, bool fos, int64_t nblk, const uint32_t *amax_part, int amax_n,
                         uint8_t *codes, uint8_t *scales, float *alpha_out, uint8_t *mchoice, nvfp4_stats_t *stats,
-                        hipStream_t stream) {
-    const dim3 grid((unsigned)((nblk + 255) / 256)), block(256);
+                        uint32_t *m4_part, hipStream_t stream) {
+    const int groups = stream_groups(nblk);
+    const dim3 grid(groups), block(kStreamThreads);
+    uint32_t *mp = (fos && stats) ? m4_part : nullptr;
     if (f32) {
         if (fos)
             hipLaunchKernelGGL((k_quant<true, true>), grid, block, 0, stream, W, nblk, amax_part, amax_n, codes, scales,
-                               alpha_out, mchoice, stats);
+                               alpha_out, mchoice, stats, mp);
         else
             hipLaunchKernelGGL((k_quant<true, false>), grid, block, 0, stream, W, nblk, amax_part, amax_n, codes,
-                               scales, alpha_out, mchoice, stats);
+                               scales, alpha_out, mchoice, stats, mp);
     } else {
         if (fos)
             hipLaunchKernelGGL((k_quant<false, true>), grid, block, 0, stream, W, nblk, amax_part, amax_n, codes,
-                               scales, alpha_out, mchoice, stats);
+                               scales, alpha_out, mchoice, stats, mp);
         else
             hipLaunchKernelGGL((k_quant<false, false>), grid, block, 0, stream, W, nblk, amax_part, amax_n, codes,
-                               scales, alpha_out, mchoice, stats);
+                               scales, alpha_out, mchoice, stats, mp);
     }
+    if (mp) hipLaunchKernelGGL(k_count, dim3(1), dim3(256), 0, stream, mp, groups, stats);
     return hipGetLastError();
 }
 
 hipError_t launch_cjso_init(const void *W, bool f32, bool soar, int64_t nblk, const uint32_t *amax_part, int amax_n,
                             int iters, uint8_t *codes, uint8_t *scales, float *alpha_out, const Workspace &ws,
                             int groups, nvfp4_stats_t *stats, hipStream_t stream) {
-    const dim3 grid(groups), block(kCjsoThreads);
+    const dim3 grid(groups), block(kStreamThreads);
     double *part = ws.cjso_part;  // round 0 writes buffer 0
 #define NVFP4_INIT(F, S)                                                                                          \
     hipLaunchKernelGGL((k_cjso_init<F, S>), grid, block, 0, stream, W, nblk, amax_part, amax_n, iters, codes, scales, \
@@ -530,9 +627,9 @@ hipError_t launch_cjso_init(const void *W, bool f32, bool soar, int64_t nblk, co
 
 hipError_t launch_cjso_iter(const void *W, bool f32, bool soar, int64_t nblk, int t, int iters, uint8_t *codes,
                             uint8_t *scales, float *alpha_out, const Workspace &ws, int groups, hipStream_t stream) {
-    const dim3 grid(groups), block(kCjsoThreads);
-    const double *pin = ws.cjso_part + (size_t)((t - 1) & 1) * kCjsoMaxGroups * 4;
-    double *pout = ws.cjso_part + (size_t)(t & 1) * kCjsoMaxGroups * 4;
+    const dim3 grid(groups), block(kStreamThreads);
+    const double *pin = ws.cjso_part + (size_t)((t - 1) & 1) * kStreamMaxGroups * 4;
+    double *pout = ws.cjso_part + (size_t)(t & 1) * kStreamMaxGroups * 4;
 #define NVFP4_ITER(F, S)                                                                                          \
     hipLaunchKernelGGL((k_cjso_iter<F, S>), grid, block, 0, stream, W, nblk, t, iters, pin, groups, pout,           \
                        ws.alpha_state, alpha_out, codes, scales, ws.brackets)

@@ -46,22 +46,23 @@ __device__ __forceinline__ void block_sums_k(const Blk<F32> &B, float r, bool rf
     }
 }
 
+// First minimum over k of A'_d(k) = (s_d/2)*S_qq(k) - S_wq(k) (= A_d(k)/2, exact in binary64) for
+// d = lo and hi. The reciprocal of the next k is read from LDS one step ahead.
 template <bool F32, bool FAST>
 __device__ __forceinline__ void scan(const Blk<F32> &B, const float *__restrict__ rtab, uint32_t dc, bool rfin,
-                                     double slo, double shi, bool c_is_lo, double &best_lo, int &k_lo, double &best_hi,
-                                     int &k_hi, double &a_c) {
+                                     double hlo, double hhi, double &best_lo, int &k_lo, double &best_hi,
+                                     int &k_hi) {
     best_lo = INFINITY;
     best_hi = INFINITY;
     k_lo = 0;
     k_hi = 0;
-    a_c = 0.0;
+    float r = rtab[dc];
     for (int k = 0; k < kSoarK; ++k) {
-        const float r = rtab[k * kTabStride + dc];
+        const float rn = rtab[(k + 1 < kSoarK ? k + 1 : k) * kTabStride + dc];
         double sw = 0.0, sq = 0.0;
         block_sums_k<F32, FAST>(B, r, rfin, sw, sq);
-        const double m2sw = -2.0 * sw;
-        const double alo = fma(slo, sq, m2sw);
-        const double ahi = fma(shi, sq, m2sw);
+        const double alo = fma(hlo, sq, -sw);
+        const double ahi = fma(hhi, sq, -sw);
         if (alo < best_lo) {
             best_lo = alo;
             k_lo = k;
@@ -70,8 +71,39 @@ __device__ __forceinline__ void scan(const Blk<F32> &B, const float *__restrict_
             best_hi = ahi;
             k_hi = k;
         }
-        if (k == 50) a_c = c_is_lo ? alo : ahi;
+        r = rn;
     }
+}
+
+// Same minimum through packed keys: key_d(k) = A'_d(k) + C + k*u. A' lies on the lattice 2^L Z with
+// |A'| < 2^M = C, and u = 2^(L-7), so every key is a non-negative multiple of u below 2^(M+2): exact in
+// binary64 when M - L <= 44 (checked per block by the caller), ordered like (A', k), and the running
+// minimum is one v_min_f64 per reconstruct scale.
+template <bool F32>
+__device__ __forceinline__ void scan_keys(const Blk<F32> &B, const float *__restrict__ rtab, uint32_t dc, double hlo,
+                                          double hhi, double C, double u, double &key_lo, double &key_hi) {
+    key_lo = INFINITY;
+    key_hi = INFINITY;
+    double kc = C;
+    float r = rtab[dc];
+    for (int k = 0; k < kSoarK; ++k) {
+        const float rn = rtab[(k + 1 < kSoarK ? k + 1 : k) * kTabStride + dc];
+        double sw = 0.0, sq = 0.0;
+        block_sums_k<F32, true>(B, r, true, sw, sq);
+        const double t = kc - sw;
+        key_lo = fmin(key_lo, fma(hlo, sq, t));
+        key_hi = fmin(key_hi, fma(hhi, sq, t));
+        kc += u;
+        r = rn;
+    }
+}
+
+// (A', k) of a packed key (see scan_keys).
+__device__ __forceinline__ void unpack_key(double key, int L, double C, double &a, int &k) {
+    const double K = ldexp(key, 7 - L);
+    const double kk = K - 128.0 * floor(K * (1.0 / 128.0));
+    k = (int)kk;
+    a = ldexp(K - kk, L - 7) - C;
 }
 
 template <bool F32>
@@ -107,19 +139,38 @@ __global__ __launch_bounds__(kSoarThreads) void k_soar(const void *__restrict__ 
     const float r0 = rtab[dc];
     const bool rfin = finite_pos(r0);  // s grows with k, so r_0 bounds every reciprocal
     const float smin = alpha * (e4m3_value(dc) * 0.5f);
+    // s_d = alpha * Delta_d exactly; errors are compared through s_d * A'_d with A'_d = A_d / 2
     const double slo = (double)alpha * (double)e4m3_value(lo);
     const double shi = (double)alpha * (double)e4m3_value(hi);
+    const double hlo = 0.5 * slo, hhi = 0.5 * shi;
     const bool c_is_lo = dc == lo;
-    double best_lo, best_hi, a_c;
+    double best_lo, best_hi, a_c, sw50, sq50;
     int k_lo, k_hi;
     if constexpr (!F32) {
-        if (rfin && a <= 32.0f * smin && a <= 0x1p100f)
-            scan<F32, true>(B, rtab, dc, rfin, slo, shi, c_is_lo, best_lo, k_lo, best_hi, k_hi, a_c);
-        else
-            scan<F32, false>(B, rtab, dc, rfin, slo, shi, c_is_lo, best_lo, k_lo, best_hi, k_hi, a_c);
+        // lattice 2^L and bound 2^M of A' = h*S_qq - S_wq (see block.hpp and scan_keys)
+        const int L = min(ilogb(hlo) - 29, ilogbf(smin) - 11);
+        const int M = max(ilogb(hhi) + 11, ilogbf(a) + 8);
+        const bool fast = rfin && a <= 32.0f * smin && a <= 0x1p100f;
+        if (fast && hlo > 0.0 && smin > 0.0f && M - L <= 44) {
+            const double C = ldexp(1.0, M), u = ldexp(1.0, L - 7);
+            double key_lo, key_hi;
+            scan_keys<F32>(B, rtab, dc, hlo, hhi, C, u, key_lo, key_hi);
+            unpack_key(key_lo, L, C, best_lo, k_lo);
+            unpack_key(key_hi, L, C, best_hi, k_hi);
+            block_sums_k<F32, true>(B, rtab[50 * kTabStride + dc], rfin, sw50, sq50);
+        } else if (fast) {
+            scan<F32, true>(B, rtab, dc, rfin, hlo, hhi, best_lo, k_lo, best_hi, k_hi);
+            block_sums_k<F32, true>(B, rtab[50 * kTabStride + dc], rfin, sw50, sq50);
+        } else {
+            scan<F32, false>(B, rtab, dc, rfin, hlo, hhi, best_lo, k_lo, best_hi, k_hi);
+            block_sums_k<F32, false>(B, rtab[50 * kTabStride + dc], rfin, sw50, sq50);
+        }
     } else {
-        scan<F32, false>(B, rtab, dc, rfin, slo, shi, c_is_lo, best_lo, k_lo, best_hi, k_hi, a_c);
+        scan<F32, false>(B, rtab, dc, rfin, hlo, hhi, best_lo, k_lo, best_hi, k_hi);
+        block_sums_k<F32, false>(B, rtab[50 * kTabStride + dc], rfin, sw50, sq50);
     }
+    // the incumbent: Delta_q = Delta_c * f_50 = Delta_c, Delta_d = Delta_c
+    a_c = fma(c_is_lo ? hlo : hhi, sq50, -sw50);
     // a zero reconstruction scale makes every candidate's error sum w^2: the first one (k = 0) stands
     if (slo == 0.0) {
         best_lo = 0.0;
