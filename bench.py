@@ -6,9 +6,12 @@ outlier columns scaled by 20). Twelve distinct matrices (384 MiB, more than the 
 stay resident in HBM and are visited in turn, so each step starts from HBM rather than from cache.
 
 One step = one matrix quantised in each of the four modes, back to back on one stream:
-MAX, FourOverSix, CJSO (8 rounds), SOAR (CJSO(8) + the 202-candidate search). `value` is the weight
-bytes quantised per second over the step (4 x 32 MiB per step). Per mode the JSON line also gives its
-own GB/s and its share of the relevant peak (HBM for MAX/FourOverSix/CJSO, FP32 vector for the search).
+MAX, FourOverSix, CJSO (8 rounds), SOAR (CJSO(8) + the 202-candidate search). Consecutive steps (different
+matrices, separate outputs and workspaces) alternate between two HIP streams, the way a model's
+independent weight matrices are quantised; `single_stream_ms_per_step` gives the same steps on one
+stream. `value` is the weight bytes quantised per second (4 x 32 MiB per step). Per mode the JSON line
+also gives its own GB/s and its share of the relevant peak (HBM for MAX/FourOverSix/CJSO, FP32 vector
+for the search).
 
 The dominant kernel (the SOAR search) is timed live: the library records HIP events around each of
 its kernels on the stream it launches them on (the `stage_events` hook of the C ABI). Its achieved rate
@@ -23,6 +26,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 from __future__ import annotations
 
 import argparse
+import contextlib
 import hashlib
 import json
 import os
@@ -56,10 +60,14 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+# the sources the search kernel (and so its counter figures) is built from
+SEARCH_SOURCES = ("soar_kernel.hip", "block.hpp", "codec.hpp", "launch.hpp")
+
+
 def source_hash() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "nvfp4_block_scaled_elem_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in SEARCH_SOURCES:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -84,6 +92,7 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--streams", type=int, default=2, help="HIP streams that consecutive steps alternate over")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device copy 5 times (scales the HBM byte counters)")
     args = ap.parse_args()
@@ -113,38 +122,53 @@ def main():
     # the other matrices: row rotations of the first with alternating sign (same distribution, new bytes)
     mats = [base] + [(-1 if i % 2 else 1) * torch.roll(base, shifts=331 * i, dims=0) for i in range(1, N_MATS)]
     mats = [m.contiguous() for m in mats]
-    out = {}
-    for mode, _ in MODES:
-        out[mode] = dict(
-            codes=torch.empty((ROWS, COLS // 2), dtype=torch.uint8, device=dev),
-            scales=torch.empty((ROWS, COLS // 16), dtype=torch.uint8, device=dev),
-            alpha=torch.empty(1, dtype=torch.float32, device=dev),
-            workspace=torch.empty(nv.workspace_bytes(ROWS, COLS, mode), dtype=torch.uint8, device=dev),
-            mchoice=torch.empty((ROWS, COLS // 16), dtype=torch.uint8, device=dev) if mode == "4o6" else None,
-        )
+    n_streams = max(1, args.streams)
+    streams = [torch.cuda.Stream(device=dev) for _ in range(n_streams)]
+    outs = []
+    for _ in range(n_streams):
+        out = {}
+        for mode, _ in MODES:
+            out[mode] = dict(
+                codes=torch.empty((ROWS, COLS // 2), dtype=torch.uint8, device=dev),
+                scales=torch.empty((ROWS, COLS // 16), dtype=torch.uint8, device=dev),
+                alpha=torch.empty(1, dtype=torch.float32, device=dev),
+                workspace=torch.empty(nv.workspace_bytes(ROWS, COLS, mode), dtype=torch.uint8, device=dev),
+                mchoice=torch.empty((ROWS, COLS // 16), dtype=torch.uint8, device=dev) if mode == "4o6" else None,
+            )
+        outs.append(out)
+    out = outs[0]
     nk = {mode: nv.kernel_count(mode, iters) for mode, iters in MODES}
 
-    def step(s, events=None):
+    def step(s, events=None, n=n_streams, modes=MODES, own_streams=True):
+        # own_streams=False keeps the caller's current stream (graph capture, the instrumented pass)
         W = mats[s % N_MATS]
-        for mode, iters in MODES:
-            o = out[mode]
-            nv.quantize(W, mode, iters, codes=o["codes"], scales=o["scales"], alpha=o["alpha"],
-                        mchoice=o["mchoice"], workspace=o["workspace"],
-                        stage_events=events[mode] if events else None)
+        k = s % n
+        with torch.cuda.stream(streams[k]) if own_streams else contextlib.nullcontext():
+            for mode, iters in modes:
+                o = outs[k][mode]
+                nv.quantize(W, mode, iters, codes=o["codes"], scales=o["scales"], alpha=o["alpha"],
+                            mchoice=o["mchoice"], workspace=o["workspace"],
+                            stage_events=events[mode] if events else None)
+
+    def timed(n, modes=MODES):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(args.steps):
+            step(args.warmup + s, n=n, modes=modes)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / args.steps
 
     log("warmup")
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()
 
-    # timed region: K steps, nothing else on the stream
-    log(f"timing {args.steps} steps")
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        step(args.warmup + s)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    # timed region: K steps, consecutive steps alternating over the streams
+    log(f"timing {args.steps} steps on {n_streams} stream(s)")
+    ms_per_step = timed(n_streams)
+    single_ms_per_step = timed(1) if n_streams > 1 else ms_per_step
+    # each mode alone on one stream, no events: the per-mode call time
+    mode_ms = {mode: timed(1, ((mode, iters),)) for mode, iters in MODES}
 
     # per-kernel durations: the same steps again with HIP events recorded by the library around each of
     # its kernels on the stream they run on
@@ -153,7 +177,7 @@ def main():
            for _ in range(n_ev)]
     log(f"instrumented pass, {n_ev} steps")
     for s in range(n_ev):
-        step(args.warmup + s, evs[s])
+        step(args.warmup + s, evs[s], n=1, own_streams=False)
     torch.cuda.synchronize()
 
     # the same step replayed from HIP graphs (one per resident matrix), for the launch overhead
@@ -161,7 +185,7 @@ def main():
     for m in range(N_MATS):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            step(m)
+            step(m, n=1, own_streams=False)
         graphs.append(g)
     torch.cuda.synchronize()
     tg0 = time.perf_counter()
@@ -176,10 +200,10 @@ def main():
     for mode, iters in MODES:
         calls = [e[mode][0].elapsed_time(e[mode][-1]) for e in evs]
         dur = np.array([[e[mode][j].elapsed_time(e[mode][j + 1]) for j in range(nk[mode])] for e in evs])
-        call_ms = float(np.mean(calls))
+        call_ms = mode_ms[mode]
         gbps = ROWS * COLS * 2 / (call_ms * 1e-3) / 1e9
         per_mode[mode] = {"ms": round(call_ms, 5), "GBps": round(gbps, 2), "frac_hbm_peak": round(gbps * 1e9 / PEAK_HBM, 4),
-                          "kernels_ms": {}}
+                          "ms_with_events": round(float(np.mean(calls)), 5), "kernels_ms": {}}
         for j, name in enumerate(KERNEL_NAMES[mode]):
             key = name if name != "k_cjso_iter" else "k_cjso_iter(avg)"
             per_mode[mode]["kernels_ms"].setdefault(key, []).append(float(dur[:, j].mean()))
@@ -222,9 +246,11 @@ def main():
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": "4096x4096 bf16 attention-projection weights, Student-t(nu=4) std 0.02 with 0.1% "
                                "outlier columns x20; 12 resident matrices visited in turn; step = MAX, FourOverSix, "
-                               "CJSO(8), SOAR(8)", "rows": ROWS, "cols": COLS, "input_dtype": "bf16",
+                               "CJSO(8), SOAR(8) of one matrix; consecutive steps on alternating streams", "rows": ROWS, "cols": COLS, "input_dtype": "bf16",
                    "matrices": N_MATS, "cjso_iters": ITERS, "parallelism": "single GPU"},
         "modes": per_mode,
+        "streams": n_streams,
+        "single_stream_ms_per_step": round(single_ms_per_step, 5),
         "graph_replay_ms_per_step": round(graph_ms_per_step, 5),
         "roofline": roofline,
     }

@@ -27,6 +27,9 @@ namespace nvfp4 {
 #ifndef NVFP4_PREFETCH_FIRST  // issue the first loads before the work-group prologue
 #define NVFP4_PREFETCH_FIRST 0
 #endif
+#ifndef NVFP4_PIPELINE  // streaming kernels: load block i+1 while block i is processed
+#define NVFP4_PIPELINE 1
+#endif
 #ifndef NVFP4_SUM_GUARD  // CJSO rounds: exactness guard on the binary32 sum instead of the block max
 #define NVFP4_SUM_GUARD 0
 #endif

@@ -118,6 +118,44 @@ __device__ __forceinline__ void store_codes(uint8_t *codes, int64_t b, uint32_t 
 template <bool F32, class P, class F>
 __device__ __forceinline__ void for_my_blocks(const void *__restrict__ W, const uint8_t *__restrict__ sc_in,
                                               int64_t nblk, P &&prologue, F &&f) {
+#if NVFP4_PIPELINE
+    // Two-stage software pipeline, unrolled so that no register copy waits on a load: the loads of the
+    // next block (index clamped into range, so the last one re-reads a valid block) are in flight while
+    // the current one is processed.
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    prologue();
+    if (b >= nblk) return;
+    const int64_t last = nblk - 1;
+    Raw<F32> ra, rb;
+    uint32_t sa = 0u, sb = 0u;
+    ra.load(W, b);
+    if (sc_in) sa = sc_in[b];
+    for (;;) {
+        int64_t bn = b + stride;
+        const int64_t cb = bn < last ? bn : last;
+        rb.load(W, cb);
+        if (sc_in) sb = sc_in[cb];
+        {
+            Blk<F32> B;
+            B.set(ra);
+            f(b, B, sa);
+        }
+        if (bn >= nblk) break;
+        b = bn;
+        bn = b + stride;
+        const int64_t ca = bn < last ? bn : last;
+        ra.load(W, ca);
+        if (sc_in) sa = sc_in[ca];
+        {
+            Blk<F32> B;
+            B.set(rb);
+            f(b, B, sb);
+        }
+        if (bn >= nblk) break;
+        b = bn;
+    }
+#else
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     int64_t base = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     Raw<F32> r[kChunk];
@@ -149,6 +187,7 @@ __device__ __forceinline__ void for_my_blocks(const void *__restrict__ W, const 
         base += kChunk * stride;
         load();
     }
+#endif
 }
 
 // ---------------------------------------------------------------------------------- global max
