@@ -114,7 +114,14 @@ typedef struct nvfp4_args {
                                   stage_events[j + 1] after kernel j, so each kernel can be timed on
                                   `stream` */
     int n_stage_events;
+    unsigned flags; /* NVFP4_FLAG_* bits (0 for the defaults) */
 } nvfp4_args_t;
+
+/* SOAR: visit all 202 candidates of every block. Without it the search evaluates, per reconstruct
+ * scale, only the two or three quantise scales next to it, which is exact: the block error is
+ * unimodal in the quantise scale around that window (the kernel source gives the argument), so the
+ * outputs are identical either way. The flag exists to check that and to time the full search. */
+#define NVFP4_FLAG_FULL_SEARCH 1u
 
 int nvfp4_quantize_ex(const nvfp4_args_t *args);
 

@@ -21,6 +21,7 @@ LIB_PATH = os.environ.get("NVFP4_LIB", os.path.join(HERE, "libnvfp4.so"))
 
 MODES = {"max": 0, "4o6": 1, "cjso": 2, "soar": 3}
 DTYPES = {torch.bfloat16: 0, torch.float32: 1}
+FLAG_FULL_SEARCH = 1  # NVFP4_FLAG_FULL_SEARCH
 STATUS_NONFINITE = 1
 
 
@@ -35,6 +36,7 @@ class _Args(ctypes.Structure):
         ("scales_out", ctypes.c_void_p), ("alpha_out", ctypes.c_void_p), ("mchoice_out", ctypes.c_void_p),
         ("stats_out", ctypes.c_void_p), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
         ("stream", ctypes.c_void_p), ("stage_events", ctypes.c_void_p), ("n_stage_events", ctypes.c_int),
+        ("flags", ctypes.c_uint),
     ]
 
 
@@ -93,12 +95,13 @@ def _stream_ptr(stream, device) -> int:
 
 
 def quantize(W: torch.Tensor, mode: str, iters: int = 0, *, codes=None, scales=None, alpha=None,
-             mchoice=None, stats=None, workspace=None, stream=None, stage_events=None):
+             mchoice=None, stats=None, workspace=None, stream=None, stage_events=None, full_search=False):
     """Quantise ``W`` ([rows, cols] bf16/fp32 CUDA tensor). Returns (codes [rows, cols//2] uint8,
     scales [rows, cols//16] uint8 E4M3 bits, alpha [1] float32), all on W's device. Optional
     preallocated outputs, an ``mchoice`` uint8 [rows, cols//16] tensor (FourOverSix), a ``stats``
     int32 [4] tensor, a uint8 ``workspace`` tensor, a ``stream`` and a list of
-    ``torch.cuda.Event(enable_timing=True)`` stage events may be passed."""
+    ``torch.cuda.Event(enable_timing=True)`` stage events may be passed. ``full_search`` makes the
+    SOAR search visit all 202 candidates of every block (same outputs; NVFP4_FLAG_FULL_SEARCH)."""
     if W.dim() != 2 or not W.is_cuda or not W.is_contiguous() or W.dtype not in DTYPES:
         raise NVFP4Error("W must be a contiguous 2-D bf16 or fp32 CUDA tensor")
     rows, cols = W.shape
@@ -129,6 +132,7 @@ def quantize(W: torch.Tensor, mode: str, iters: int = 0, *, codes=None, scales=N
     a.workspace = workspace.data_ptr() if workspace is not None else None
     a.workspace_bytes = workspace.numel() if workspace is not None else 0
     a.stream = _stream_ptr(stream, dev)
+    a.flags = FLAG_FULL_SEARCH if full_search else 0
     ev_arr = None
     if stage_events is not None:
         for e in stage_events:  # torch creates the HIP event at its first record

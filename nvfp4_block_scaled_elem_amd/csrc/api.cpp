@@ -41,6 +41,7 @@ int check(const nvfp4_args_t *a) {
     if (a->workspace && ((uintptr_t)a->workspace & 255u) != 0) return NVFP4_ERR_INVALID_ARG;
     if (a->stats_out && ((uintptr_t)a->stats_out & 3u) != 0) return NVFP4_ERR_INVALID_ARG;
     if (a->stage_events && a->n_stage_events < kernel_count(a->mode, a->iters) + 1) return NVFP4_ERR_INVALID_ARG;
+    if (a->flags & ~NVFP4_FLAG_FULL_SEARCH) return NVFP4_ERR_INVALID_ARG;
     return NVFP4_OK;
 }
 
@@ -82,7 +83,7 @@ int run(const nvfp4_args_t *a, void *ws_base) {
             !mark(a, j++))
             return NVFP4_ERR_HIP;
     if (soar && (launch_soar(a->W, f32, nblk, ws.alpha_state + (a->iters & 1), a->codes_out, a->scales_out,
-                             ws.brackets, st) != hipSuccess ||
+                             ws.brackets, (a->flags & NVFP4_FLAG_FULL_SEARCH) != 0, st) != hipSuccess ||
                  !mark(a, j++)))
         return NVFP4_ERR_HIP;
     return NVFP4_OK;

@@ -55,6 +55,7 @@ def args(**kw):
     (dict(workspace=FAKE + 64, workspace_bytes=1 << 30), INVALID),
     (dict(workspace=FAKE, workspace_bytes=16), WORKSPACE),
     (dict(mode=3, iters=8, workspace=FAKE, workspace_bytes=1024), WORKSPACE),
+    (dict(flags=2), INVALID), (dict(flags=0x80000000), INVALID),
 ])
 def test_quantize_ex_rejects(L, kw, err):
     a = args(**kw)
@@ -104,3 +105,23 @@ def test_binding_rejects_cpu_tensors():
     import torch
     with pytest.raises(nv.NVFP4Error):
         nv.quantize(torch.zeros(4, 16, dtype=torch.bfloat16), "max")
+
+
+def test_args_struct_layout_matches_header(tmp_path):
+    """The binding's ctypes struct has the C compiler's size and field offsets for nvfp4_args_t."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no host C compiler")
+    fields = [f for f, _ in nv._Args._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text("#include <stdio.h>\n#include <stddef.h>\n#include \"nvfp4.h\"\nint main(void) {\n"
+                   + 'printf("%zu\\n", sizeof(nvfp4_args_t));\n'
+                   + "".join(f'printf("%zu\\n", offsetof(nvfp4_args_t, {f}));\n' for f in fields)
+                   + "return 0; }\n")
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    out = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()]
+    assert out[0] == ctypes.sizeof(nv._Args)
+    assert out[1:] == [getattr(nv._Args, f).offset for f in fields]

@@ -7,6 +7,7 @@ bit-exact (codes, scales, alpha, M=4 choices); CJSO and SOAR are held to the sam
 stricter than the stated tolerance (alpha within 1e-6 relative, codes and scales on at least 99.99 % of
 blocks, MSE within 1e-5 relative) — the tolerance checks run first so a failure says which bar broke.
 """
+import functools
 import hashlib
 import json
 import os
@@ -45,13 +46,13 @@ def to_dev(W: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(W).cuda()
 
 
-def run(W: np.ndarray, mode: str, iters: int = 0, dev_W=None):
-    say(f"gpu quantize mode={mode} iters={iters} shape={W.shape} dtype={W.dtype}")
+def run(W: np.ndarray, mode: str, iters: int = 0, dev_W=None, full_search=False):
+    say(f"gpu quantize mode={mode} iters={iters} shape={W.shape} dtype={W.dtype} full_search={full_search}")
     Wd = to_dev(W) if dev_W is None else dev_W
     rows, cols = W.shape
     mch = torch.zeros((rows, cols // 16), dtype=torch.uint8, device="cuda") if mode == "4o6" else None
     stats = torch.zeros(4, dtype=torch.int32, device="cuda")
-    codes, scales, alpha = nv.quantize(Wd, mode, iters, mchoice=mch, stats=stats)
+    codes, scales, alpha = nv.quantize(Wd, mode, iters, mchoice=mch, stats=stats, full_search=full_search)
     torch.cuda.synchronize()
     out = {"codes": codes.cpu().numpy(), "scales": scales.cpu().numpy(), "alpha": float(alpha.cpu()[0]),
            "stats": stats.cpu().numpy()}
@@ -301,6 +302,73 @@ def test_dequantize_matches_oracle(mode):
     e = np.maximum(e, -125)
     ref = np.ldexp(np.rint(np.ldexp(exact, 8 - e)), e - 8).astype(np.float32)  # nearest 8-bit significand
     assert np.array_equal(bf, (ref.view(np.uint32) >> 16).astype(np.uint16))
+
+
+# ------------------------------------------------------------- windowed search vs the full scan
+
+def coarse_bf16(seed, rows=64, cols=256):
+    """Few distinct magnitudes (multiples of 2^-8 up to 3 * 2^-6) and many zeros: errors of different
+    candidates often tie exactly."""
+    g = np.random.default_rng(seed)
+    v = g.integers(-3, 4, size=(rows, cols)).astype(np.float32)
+    v *= g.choice([1.0, 0.5, 0.25], size=(rows, cols)).astype(np.float32)
+    v[g.random((rows, cols)) < g.uniform(0.2, 0.9)] = 0
+    v *= np.float32(2.0 ** -6)
+    return (v.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def sparse_bf16(seed, rows=64, cols=256):
+    """One to three small odd integers per block times a power of two."""
+    g = np.random.default_rng(1000 + seed)
+    v = np.zeros((rows * cols // 16, 16), np.float32)
+    for i in range(v.shape[0]):
+        n = int(g.integers(1, 4))
+        pos = g.choice(16, size=n, replace=False)
+        v[i, pos] = g.choice([1, 2, 3, 5, 6, 7, 9, 11, 13], size=n) * g.choice([-1, 1], size=n)
+    v *= np.float32(2.0 ** int(g.integers(-9, -3)))
+    v = v.reshape(rows, cols)
+    return (v.view(np.uint32) >> 16).astype(np.uint16)
+
+
+WINDOW_CASES = {
+    "c2_4096x4096": lambda: synth.c2(0),
+    "c3_up_14336x4096": lambda: synth.c3(0, 0),
+    "c5_l0_down_4096x11008": lambda: synth.c5(0, "down"),
+    "on_grid": lambda: indep.on_grid_matrix(64, 256, -10, 7)[0],
+    "on_grid_tiny_alpha": lambda: indep.on_grid_matrix(64, 256, -120, 3)[0],
+    "coarse_0": lambda: coarse_bf16(0),
+    "coarse_1": lambda: coarse_bf16(1),
+    "sparse_0": lambda: sparse_bf16(0),
+    "sparse_1": lambda: sparse_bf16(1),
+    "ragged_3x48": lambda: synth.normal_bf16(3, 48, 5),
+}
+
+
+@functools.lru_cache(maxsize=1)
+def window_input(name):
+    return WINDOW_CASES[name]()
+
+
+@pytest.mark.parametrize("iters", [0, 2, 8])
+@pytest.mark.parametrize("name", list(WINDOW_CASES))
+def test_soar_window_equals_full_search(name, iters):
+    """The default search (two or three quantise scales per reconstruct scale) and the 202-candidate
+    scan give the same codes and scales on every block."""
+    W = window_input(name)
+    Wd = to_dev(W)
+    a = run(W, "soar", iters, dev_W=Wd)
+    b = run(W, "soar", iters, dev_W=Wd, full_search=True)
+    assert f32_bits(a["alpha"]) == f32_bits(b["alpha"])
+    diff = ~(np.all(a["codes"].reshape(-1, 8) == b["codes"].reshape(-1, 8), axis=1)
+             & (a["scales"].reshape(-1) == b["scales"].reshape(-1)))
+    assert not diff.any(), f"{diff.sum()} blocks differ, first {np.flatnonzero(diff)[:5]}"
+
+
+@pytest.mark.parametrize("gen", [coarse_bf16, sparse_bf16])
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_soar_tie_prone_inputs_match_oracle(gen, seed):
+    W = gen(seed)
+    compare_live(W, "soar", 8)
 
 
 # -------------------------------------------------------------------------- full-size digests
