@@ -156,6 +156,15 @@ __device__ __forceinline__ void sums_f64(uint32_t c0, uint32_t c1, const float *
     acc_f64<3>(c1, w[14], w[15], sw, sq);
 }
 
+// Work-group barrier for data exchanged through LDS only. The fences cover the local address space, so
+// global loads and stores still in flight (a block prefetched before a kernel's prologue, a partial
+// result written for the next kernel) are not waited for, unlike __syncthreads.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // s = fl(alpha * Delta) and r = fl(1/s) (0 for s = 0) for every E4M3 code, built once per work-group.
 // lim[c] = 2^(ilogb(s)+13): a bf16 block's binary32 S_wq below it is exact (see the header; the
 // products w*q are all >= 0, so every partial sum is at most the final one).
@@ -165,14 +174,15 @@ struct ScaleTab {
     float lim[128];
 };
 
+template <int THREADS>
 __device__ __forceinline__ void build_scale_tab(ScaleTab &T, float alpha) {
-    for (int c = threadIdx.x; c < 128; c += blockDim.x) {
+    for (int c = threadIdx.x; c < 128; c += THREADS) {
         const float s = c < 0x7F ? alpha * e4m3_value((uint32_t)c) : 0.0f;
         T.s[c] = s;
         T.r[c] = s == 0.0f ? 0.0f : 1.0f / s;
         T.lim[c] = s > 0.0f ? ldexpf(1.0f, ilogbf(s) + 13) : INFINITY;  // s = 0: every sum is 0
     }
-    __syncthreads();
+    lds_barrier();
 }
 
 // Codes and exact sums for table entry d, without the block max: the binary32 sums are taken first and

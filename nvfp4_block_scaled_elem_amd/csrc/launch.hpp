@@ -12,32 +12,21 @@ namespace nvfp4 {
 
 // Work-group counts of the reduction kernels: the global max pass and the streaming per-block passes
 // (MAX, FourOverSix, CJSO). Their per-work-group partial results are what every work-group of the next
-// kernel reduces, so the streaming passes use a fixed grid of at most two work-groups per CU and each
-// thread walks its blocks kChunk at a time. The defaults are the fastest of the settings measured on
-// an MI355X for a 4096 x 4096 matrix; the macros exist so that other settings can be built and timed.
+// kernel reduces, so the streaming passes use a fixed grid of at most two work-groups per CU, each
+// thread walking at least kMinBlocksPerThread blocks (its loads of block i+1 overlap block i). The
+// defaults are the fastest of the settings measured on an MI355X for a 4096 x 4096 matrix; the macros
+// exist so that other settings can be built and timed.
 #ifndef NVFP4_STREAM_THREADS
 #define NVFP4_STREAM_THREADS 512
 #endif
 #ifndef NVFP4_STREAM_GROUPS
 #define NVFP4_STREAM_GROUPS 512
 #endif
-#ifndef NVFP4_CHUNK
-#define NVFP4_CHUNK 2
-#endif
-#ifndef NVFP4_PREFETCH_FIRST  // issue the first loads before the work-group prologue
-#define NVFP4_PREFETCH_FIRST 0
-#endif
-#ifndef NVFP4_PIPELINE  // streaming kernels: load block i+1 while block i is processed
-#define NVFP4_PIPELINE 1
-#endif
-#ifndef NVFP4_SUM_GUARD  // CJSO rounds: exactness guard on the binary32 sum instead of the block max
-#define NVFP4_SUM_GUARD 0
-#endif
 constexpr int kAmaxThreads = 256;
 constexpr int kAmaxMaxGroups = 1024;
 constexpr int kStreamThreads = NVFP4_STREAM_THREADS;
 constexpr int kStreamMaxGroups = NVFP4_STREAM_GROUPS;
-constexpr int kChunk = NVFP4_CHUNK;
+constexpr int kMinBlocksPerThread = 2;
 
 int amax_groups(int64_t nchunks);
 int stream_groups(int64_t nblk);

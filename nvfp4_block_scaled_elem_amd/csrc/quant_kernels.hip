@@ -24,16 +24,14 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t m) {
     return m;
 }
 
-// Max of part[0..n) across the work-group; every thread gets the result.
-__device__ __forceinline__ uint32_t wg_max_parts(const uint32_t *part, int n) {
+// Max over the work-group of one value per thread; every thread gets the result.
+__device__ __forceinline__ uint32_t wg_max(uint32_t m) {
     __shared__ uint32_t red[16];
-    uint32_t m = 0u;
-    for (int i = threadIdx.x; i < n; i += blockDim.x) m = part[i] > m ? part[i] : m;
     m = wave_max_u32(m);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
-    __syncthreads();
+    lds_barrier();
     m = 0u;
-    for (int i = 0; i < (int)(blockDim.x >> 6); ++i) m = red[i] > m ? red[i] : m;
+    for (int i = 0; i < kStreamThreads / 64; ++i) m = red[i] > m ? red[i] : m;
     return m;
 }
 
@@ -53,38 +51,73 @@ __device__ __forceinline__ void wg_sum_dd2(dd &N, dd &D) {
         red[threadIdx.x >> 6][2] = D.hi;
         red[threadIdx.x >> 6][3] = D.lo;
     }
-    __syncthreads();
+    lds_barrier();
     if (threadIdx.x == 0) {
         N = {red[0][0], red[0][1]};
         D = {red[0][2], red[0][3]};
-        for (int i = 1; i < (int)(blockDim.x >> 6); ++i) {
+        for (int i = 1; i < kStreamThreads / 64; ++i) {
             N = dd_add(N, dd{red[i][0], red[i][1]});
             D = dd_add(D, dd{red[i][2], red[i][3]});
         }
     }
-    __syncthreads();
 }
 
-// Sum of the CJSO partials part[0..n) (fixed order); every thread gets the result.
-__device__ __forceinline__ void wg_sum_parts(const double *part, int n, dd &N, dd &D) {
-    __shared__ double tot[4];
-    N = {0.0, 0.0};
-    D = {0.0, 0.0};
-    for (int i = threadIdx.x; i < n; i += blockDim.x) {
-        N = dd_add(N, dd{part[4 * i], part[4 * i + 1]});
-        D = dd_add(D, dd{part[4 * i + 2], part[4 * i + 3]});
+// A kernel's prologue reads the previous kernel's per-work-group partials. Each thread loads its share
+// first (before the block prefetch, so that waiting for these loads does not wait for the prefetch)
+// and reduces it afterwards.
+constexpr int kAmaxPerThread = (kAmaxMaxGroups + kStreamThreads - 1) / kStreamThreads;
+constexpr int kPartPerThread = (kStreamMaxGroups + kStreamThreads - 1) / kStreamThreads;
+
+struct AmaxShare {
+    uint32_t v[kAmaxPerThread];
+    __device__ __forceinline__ void load(const uint32_t *part, int n) {
+#pragma unroll
+        for (int k = 0; k < kAmaxPerThread; ++k) {
+            const int i = (int)threadIdx.x + k * kStreamThreads;
+            v[k] = i < n ? part[i] : 0u;
+        }
     }
-    wg_sum_dd2(N, D);
-    if (threadIdx.x == 0) {
-        tot[0] = N.hi;
-        tot[1] = N.lo;
-        tot[2] = D.hi;
-        tot[3] = D.lo;
+    // max of part[0..n) over the work-group (every thread gets it)
+    __device__ __forceinline__ uint32_t reduce() const {
+        uint32_t m = 0u;
+#pragma unroll
+        for (int k = 0; k < kAmaxPerThread; ++k) m = v[k] > m ? v[k] : m;
+        return wg_max(m);
     }
-    __syncthreads();
-    N = {tot[0], tot[1]};
-    D = {tot[2], tot[3]};
-}
+};
+
+struct CjsoShare {
+    double v[kPartPerThread][4];
+    __device__ __forceinline__ void load(const double *part, int n) {
+#pragma unroll
+        for (int k = 0; k < kPartPerThread; ++k) {
+            const int i = (int)threadIdx.x + k * kStreamThreads;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[k][j] = i < n ? part[4 * i + j] : 0.0;
+        }
+    }
+    // sum of the partials (fixed order); every thread gets it
+    __device__ __forceinline__ void reduce(dd &N, dd &D) const {
+        __shared__ double tot[4];
+        N = {0.0, 0.0};
+        D = {0.0, 0.0};
+#pragma unroll
+        for (int k = 0; k < kPartPerThread; ++k) {
+            N = dd_add(N, dd{v[k][0], v[k][1]});
+            D = dd_add(D, dd{v[k][2], v[k][3]});
+        }
+        wg_sum_dd2(N, D);
+        if (threadIdx.x == 0) {
+            tot[0] = N.hi;
+            tot[1] = N.lo;
+            tot[2] = D.hi;
+            tot[3] = D.lo;
+        }
+        lds_barrier();
+        N = {tot[0], tot[1]};
+        D = {tot[2], tot[3]};
+    }
+};
 
 // SOAR page, global-scale step: alpha* = N / D (the least-squares minimiser over alpha), rounded once
 // to binary32. D = 0 (every code zero) keeps the previous alpha.
@@ -109,28 +142,29 @@ __device__ __forceinline__ void store_codes(uint8_t *codes, int64_t b, uint32_t 
     *reinterpret_cast<uint2 *>(codes + 8 * b) = make_uint2(e2m1_clear_negzero(c0), e2m1_clear_negzero(c1));
 }
 
-// Visit this thread's blocks b = gid, gid + S, gid + 2S, ... (S = all threads of the grid), issuing the
-// loads of kChunk blocks before processing any of them so that each lane keeps several 16-byte loads in
-// flight.
-// The loads of a chunk (its blocks and, when `sc_in` is given, their scale bytes) are all issued before
-// any of its blocks is processed; with NVFP4_PREFETCH_FIRST the first chunk's loads also precede
-// `prologue` (run by every thread of the work-group). f(b, B, sc) gets the block and its scale byte.
-template <bool F32, class P, class F>
-__device__ __forceinline__ void for_my_blocks(const void *__restrict__ W, const uint8_t *__restrict__ sc_in,
-                                              int64_t nblk, P &&prologue, F &&f) {
-#if NVFP4_PIPELINE
-    // Two-stage software pipeline, unrolled so that no register copy waits on a load: the loads of the
-    // next block (index clamped into range, so the last one re-reads a valid block) are in flight while
-    // the current one is processed.
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    prologue();
-    if (b >= nblk) return;
+// Visit this thread's blocks b = gid, gid + S, gid + 2S, ... (S = all threads of the grid) in a
+// two-stage software pipeline: the loads of the next block (index clamped into range, so the last one
+// re-reads a valid block) are in flight while the current one is processed. The loop is unrolled by two
+// so that no register copy waits on a load. `pre` issues the prologue's own loads, then the first
+// block's loads are issued, then `post` (run by every thread of the work-group) finishes the prologue;
+// it returns false to skip the blocks (the function then returns false). f(b, B, sc) gets the block
+// and, when `sc_in` is given, its scale byte.
+template <bool F32, class Pre, class Post, class F>
+__device__ __forceinline__ bool for_my_blocks(const void *__restrict__ W, const uint8_t *__restrict__ sc_in,
+                                              int64_t nblk, Pre &&pre, Post &&post, F &&f) {
+    const int64_t stride = (int64_t)gridDim.x * kStreamThreads;
+    int64_t b = (int64_t)blockIdx.x * kStreamThreads + threadIdx.x;
     const int64_t last = nblk - 1;
     Raw<F32> ra, rb;
     uint32_t sa = 0u, sb = 0u;
-    ra.load(W, b);
-    if (sc_in) sa = sc_in[b];
+    pre();
+    {
+        const int64_t c = b < last ? b : last;
+        ra.load(W, c);
+        if (sc_in) sa = sc_in[c];
+    }
+    if (!post()) return false;
+    if (b >= nblk) return true;
     for (;;) {
         int64_t bn = b + stride;
         const int64_t cb = bn < last ? bn : last;
@@ -155,39 +189,7 @@ __device__ __forceinline__ void for_my_blocks(const void *__restrict__ W, const 
         if (bn >= nblk) break;
         b = bn;
     }
-#else
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    int64_t base = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    Raw<F32> r[kChunk];
-    uint32_t sc[kChunk];
-    auto load = [&] {
-#pragma unroll
-        for (int c = 0; c < kChunk; ++c) {
-            const int64_t b = base + c * stride;
-            sc[c] = 0u;
-            if (b < nblk) {
-                r[c].load(W, b);
-                if (sc_in) sc[c] = sc_in[b];
-            }
-        }
-    };
-    if (!NVFP4_PREFETCH_FIRST) prologue();
-    load();
-    if (NVFP4_PREFETCH_FIRST) prologue();
-    while (base < nblk) {
-#pragma unroll
-        for (int c = 0; c < kChunk; ++c) {
-            const int64_t b = base + c * stride;
-            if (b < nblk) {
-                Blk<F32> B;
-                B.set(r[c]);
-                f(b, B, sc[c]);
-            }
-        }
-        base += kChunk * stride;
-        load();
-    }
-#endif
+    return true;
 }
 
 // ---------------------------------------------------------------------------------- global max
@@ -198,8 +200,8 @@ template <bool F32>
 __global__ __launch_bounds__(kAmaxThreads) void k_amax(const uint4 *__restrict__ W, int64_t nchunks,
                                                        uint32_t *__restrict__ part, nvfp4_stats_t *stats) {
     uint32_t m = 0u;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * kAmaxThreads;
+    int64_t i = (int64_t)blockIdx.x * kAmaxThreads + threadIdx.x;
     for (; i + 3 * stride < nchunks; i += 4 * stride) {
         uint4 v[4];
 #pragma unroll
@@ -257,25 +259,25 @@ __global__ __launch_bounds__(kStreamThreads) void k_quant(const void *__restrict
                                                           uint8_t *__restrict__ codes, uint8_t *__restrict__ scales,
                                                           float *__restrict__ alpha_out, uint8_t *__restrict__ mchoice,
                                                           nvfp4_stats_t *stats, uint32_t *__restrict__ m4_part) {
-    const uint32_t abits = wg_max_parts(amax_part, amax_n);
-    const bool nonfinite = abits >= 0x7F800000u;
-    const float alpha = max_rule_alpha(abits);
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
-        *alpha_out = nonfinite ? __builtin_nanf("") : alpha;
-        if (stats) stats->status = nonfinite ? NVFP4_STATUS_NONFINITE : 0u;
-    }
     __shared__ ScaleTab T;
+    AmaxShare am;
+    float alpha = 0.0f;
     uint32_t m4count = 0u;
-    if (nonfinite) {
-        const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-        for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblk; b += stride) {
-            store_codes(codes, b, 0u, 0u);
-            scales[b] = 0;
-            if (FOS && mchoice) mchoice[b] = 0;
+    auto pre = [&] { am.load(amax_part, amax_n); };
+    auto post = [&] {
+        const uint32_t abits = am.reduce();
+        const bool nonfinite = abits >= 0x7F800000u;
+        alpha = max_rule_alpha(abits);
+        if (blockIdx.x == 0 && threadIdx.x == 0) {
+            *alpha_out = nonfinite ? __builtin_nanf("") : alpha;
+            if (stats) stats->status = nonfinite ? NVFP4_STATUS_NONFINITE : 0u;
         }
-    } else {
-        for_my_blocks<F32>(W, nullptr, nblk, [&] { build_scale_tab(T, alpha); },
-                           [&](int64_t b, const Blk<F32> &B, uint32_t) {
+        if (nonfinite) return false;
+        build_scale_tab<kStreamThreads>(T, alpha);
+        return true;
+    };
+    const bool finite = for_my_blocks<F32>(W, nullptr, nblk, pre, post,
+                                           [&](int64_t b, const Blk<F32> &B, uint32_t) {
             uint32_t c0, c1, sc;
             bool m4 = false;
             const float a = B.amax();
@@ -314,6 +316,13 @@ __global__ __launch_bounds__(kStreamThreads) void k_quant(const void *__restrict
             store_codes(codes, b, c0, c1);
             scales[b] = (uint8_t)sc;
         });
+    if (!finite) {  // non-finite input: all-zero codes and scales
+        const int64_t stride = (int64_t)gridDim.x * kStreamThreads;
+        for (int64_t b = (int64_t)blockIdx.x * kStreamThreads + threadIdx.x; b < nblk; b += stride) {
+            store_codes(codes, b, 0u, 0u);
+            scales[b] = 0;
+            if (FOS && mchoice) mchoice[b] = 0;
+        }
     }
     if (FOS && m4_part) {  // per work-group count of M=4 blocks (summed by k_count only if asked)
         __shared__ uint32_t cnt[kStreamThreads / 64];
@@ -330,10 +339,12 @@ __global__ __launch_bounds__(kStreamThreads) void k_quant(const void *__restrict
 }
 
 // stats->m4_blocks = sum of the per-work-group counts (one work-group, fixed order).
-__global__ __launch_bounds__(256) void k_count(const uint32_t *__restrict__ part, int64_t n, nvfp4_stats_t *stats) {
-    __shared__ uint32_t red[4];
+constexpr int kCountThreads = 256;
+__global__ __launch_bounds__(kCountThreads) void k_count(const uint32_t *__restrict__ part, int64_t n,
+                                                         nvfp4_stats_t *stats) {
+    __shared__ uint32_t red[kCountThreads / 64];
     uint32_t c = 0u;
-    for (int64_t i = threadIdx.x; i < n; i += blockDim.x) c += part[i];
+    for (int64_t i = threadIdx.x; i < n; i += kCountThreads) c += part[i];
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) c += (uint32_t)__shfl_xor((int)c, o);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = c;
@@ -353,53 +364,60 @@ __global__ __launch_bounds__(kStreamThreads) void k_cjso_init(const void *__rest
                                                               float *__restrict__ alpha_state,
                                                               double *__restrict__ part_out,
                                                               uint16_t *__restrict__ brackets, nvfp4_stats_t *stats) {
-    const uint32_t abits = wg_max_parts(amax_part, amax_n);
-    const bool nonfinite = abits >= 0x7F800000u;
-    const float alpha = max_rule_alpha(abits);
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
-        const float av = nonfinite ? __builtin_nanf("") : alpha;
-        alpha_state[0] = av;
-        if (iters == 0) *alpha_out = av;
-        if (stats) stats->status = nonfinite ? NVFP4_STATUS_NONFINITE : 0u;
-    }
     __shared__ ScaleTab T;
+    AmaxShare am;
+    float alpha = 0.0f;
     dd N = {0.0, 0.0}, D = {0.0, 0.0};
-    if (nonfinite) {
-        const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-        for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblk; b += stride) {
+    auto pre = [&] { am.load(amax_part, amax_n); };
+    auto post = [&] {
+        const uint32_t abits = am.reduce();
+        const bool nonfinite = abits >= 0x7F800000u;
+        alpha = max_rule_alpha(abits);
+        if (blockIdx.x == 0 && threadIdx.x == 0) {
+            const float av = nonfinite ? __builtin_nanf("") : alpha;
+            alpha_state[0] = av;
+            if (iters == 0) *alpha_out = av;
+            if (stats) stats->status = nonfinite ? NVFP4_STATUS_NONFINITE : 0u;
+        }
+        if (nonfinite) return false;
+        build_scale_tab<kStreamThreads>(T, alpha);
+        return true;
+    };
+    const bool finite = for_my_blocks<F32>(W, nullptr, nblk, pre, post,
+                                           [&](int64_t b, const Blk<F32> &B, uint32_t) {
+        const float a = B.amax();
+        const double q = max_rule_quotient(a, alpha);
+        const uint32_t d = e4m3_rne(q);
+        const float v = e4m3_value(d);
+        scales[b] = (uint8_t)d;
+        uint32_t c0, c1;
+        if (iters == 0) {
+            const float r = T.r[d];
+            if (finite_pos(r))
+                encode16(B.w, r, c0, c1);
+            else
+                encode16_soft(B.w, r, c0, c1);
+            store_codes(codes, b, c0, c1);
+            if (SOAR) {
+                uint32_t lo, hi;
+                e4m3_bracket(q, lo, hi);
+                brackets[b] = (uint16_t)(lo | (hi << 8));
+            }
+        } else {
+            double sw, sq;
+            quant_sums_t(B, T, d, c0, c1, sw, sq);
+            const dd t = two_prod((double)v, sw);
+            acc2(N, t.hi, t.lo);
+            acc2(D, (double)v * (double)v * sq, 0.0);
+        }
+    });
+    if (!finite) {  // non-finite input: all-zero outputs; the rounds see alpha = NaN and stop
+        const int64_t stride = (int64_t)gridDim.x * kStreamThreads;
+        for (int64_t b = (int64_t)blockIdx.x * kStreamThreads + threadIdx.x; b < nblk; b += stride) {
             store_codes(codes, b, 0u, 0u);
             scales[b] = 0;
             if (SOAR) brackets[b] = 0;
         }
-    } else {
-        for_my_blocks<F32>(W, nullptr, nblk, [&] { build_scale_tab(T, alpha); },
-                           [&](int64_t b, const Blk<F32> &B, uint32_t) {
-            const float a = B.amax();
-            const double q = max_rule_quotient(a, alpha);
-            const uint32_t d = e4m3_rne(q);
-            const float v = e4m3_value(d);
-            scales[b] = (uint8_t)d;
-            uint32_t c0, c1;
-            if (iters == 0) {
-                const float r = T.r[d];
-                if (finite_pos(r))
-                    encode16(B.w, r, c0, c1);
-                else
-                    encode16_soft(B.w, r, c0, c1);
-                store_codes(codes, b, c0, c1);
-                if (SOAR) {
-                    uint32_t lo, hi;
-                    e4m3_bracket(q, lo, hi);
-                    brackets[b] = (uint16_t)(lo | (hi << 8));
-                }
-            } else {
-                double sw, sq;
-                quant_sums_t(B, T, d, c0, c1, sw, sq);
-                const dd t = two_prod((double)v, sw);
-                acc2(N, t.hi, t.lo);
-                acc2(D, (double)v * (double)v * sq, 0.0);
-            }
-        });
     }
     if (iters > 0) {
         wg_sum_dd2(N, D);
@@ -414,46 +432,44 @@ __global__ __launch_bounds__(kStreamThreads) void k_cjso_init(const void *__rest
 
 // CJSO round t (1..iters): alpha-step from the previous round's sums, re-quantise, Delta-step (SOAR
 // page, block-scale closed form, rounded to E4M3), re-quantise; then the sums for round t+1, or, in the
-// last round, the codes (and for SOAR the E4M3 bracket of the unrounded block scale).
-template <bool F32, bool SOAR>
+// last round (LAST), the codes (and for SOAR the E4M3 bracket of the unrounded block scale).
+template <bool F32, bool SOAR, bool LAST>
 __global__ __launch_bounds__(kStreamThreads) void k_cjso_iter(const void *__restrict__ W, int64_t nblk, int t,
-                                                              int iters, const double *__restrict__ part_in,
-                                                              int n_part, double *__restrict__ part_out,
-                                                              float *alpha_state, float *__restrict__ alpha_out,
+                                                              const double *__restrict__ part_in, int n_part,
+                                                              double *__restrict__ part_out, float *alpha_state,
+                                                              float *__restrict__ alpha_out,
                                                               uint8_t *__restrict__ codes, uint8_t *__restrict__ scales,
                                                               uint16_t *__restrict__ brackets) {
-    const float prev = alpha_state[(t - 1) & 1];
-    if (prev != prev) {  // non-finite input: the outputs were zeroed by the first pass
-        if (blockIdx.x == 0 && threadIdx.x == 0) {
-            alpha_state[t & 1] = prev;
-            if (t == iters) *alpha_out = prev;
-        }
-        return;
-    }
-    const bool last = t == iters;
     __shared__ ScaleTab T;
-    float alpha = prev;
+    CjsoShare sh;
+    float alpha = 0.0f;
     dd Nn = {0.0, 0.0}, Dn = {0.0, 0.0};
-    auto prologue = [&] {
+    auto pre = [&] { sh.load(part_in, n_part); };
+    auto post = [&] {
+        const float prev = alpha_state[(t - 1) & 1];
+        if (prev != prev) {  // non-finite input: the outputs were zeroed by the first pass
+            if (blockIdx.x == 0 && threadIdx.x == 0) {
+                alpha_state[t & 1] = prev;
+                if (LAST) *alpha_out = prev;
+            }
+            return false;
+        }
         dd N, D;
-        wg_sum_parts(part_in, n_part, N, D);
+        sh.reduce(N, D);
         alpha = alpha_from(N, D, prev);
         if (blockIdx.x == 0 && threadIdx.x == 0) {
             alpha_state[t & 1] = alpha;
-            if (t == iters) *alpha_out = alpha;
+            if (LAST) *alpha_out = alpha;
         }
-        build_scale_tab(T, alpha);
+        build_scale_tab<kStreamThreads>(T, alpha);
+        return true;
     };
-    for_my_blocks<F32>(W, scales, nblk, prologue, [&](int64_t b, const Blk<F32> &B, uint32_t d) {
+    if (!for_my_blocks<F32>(W, scales, nblk, pre, post, [&](int64_t b, const Blk<F32> &B, uint32_t d) {
         const float v = e4m3_value(d);
         uint32_t c0, c1;
         double sw, sq;
-#if NVFP4_SUM_GUARD
-        quant_sums_t(B, T, d, c0, c1, sw, sq);
-#else
         const float a = B.amax();
         quant_sums_r(B, a, T.s[d], T.r[d], c0, c1, sw, sq);
-#endif
         double dstar = (double)v;
         uint32_t dn = d;
         if (sq > 0.0) {
@@ -462,12 +478,8 @@ __global__ __launch_bounds__(kStreamThreads) void k_cjso_iter(const void *__rest
         }
         scales[b] = (uint8_t)dn;
         const float vn = e4m3_value(dn);
-#if NVFP4_SUM_GUARD
-        quant_sums_t(B, T, dn, c0, c1, sw, sq);
-#else
         quant_sums_r(B, a, T.s[dn], T.r[dn], c0, c1, sw, sq);
-#endif
-        if (!last) {
+        if (!LAST) {
             const dd tn = two_prod((double)vn, sw);
             acc2(Nn, tn.hi, tn.lo);
             acc2(Dn, (double)vn * (double)vn * sq, 0.0);
@@ -479,8 +491,9 @@ __global__ __launch_bounds__(kStreamThreads) void k_cjso_iter(const void *__rest
                 brackets[b] = (uint16_t)(lo | (hi << 8));
             }
         }
-    });
-    if (!last) {
+    }))
+        return;
+    if (!LAST) {
         wg_sum_dd2(Nn, Dn);
         if (threadIdx.x == 0) {
             part_out[4 * blockIdx.x + 0] = Nn.hi;
@@ -581,7 +594,8 @@ int amax_groups(int64_t nchunks) {
 }
 
 int stream_groups(int64_t nblk) {
-    int64_t g = (nblk + (int64_t)kStreamThreads * kChunk - 1) / ((int64_t)kStreamThreads * kChunk);
+    int64_t g = (nblk + (int64_t)kStreamThreads * kMinBlocksPerThread - 1) /
+                ((int64_t)kStreamThreads * kMinBlocksPerThread);
     return (int)(g < 1 ? 1 : (g > kStreamMaxGroups ? kStreamMaxGroups : g));
 }
 
@@ -643,7 +657,7 @@ hipError_t launch_quant(const void *W, bool f32, bool fos, int64_t nblk, const u
             hipLaunchKernelGGL((k_quant<false, false>), grid, block, 0, stream, W, nblk, amax_part, amax_n, codes,
                                scales, alpha_out, mchoice, stats, mp);
     }
-    if (mp) hipLaunchKernelGGL(k_count, dim3(1), dim3(256), 0, stream, mp, groups, stats);
+    if (mp) hipLaunchKernelGGL(k_count, dim3(1), dim3(kCountThreads), 0, stream, mp, groups, stats);
     return hipGetLastError();
 }
 
@@ -669,14 +683,19 @@ hipError_t launch_cjso_iter(const void *W, bool f32, bool soar, int64_t nblk, in
     const dim3 grid(groups), block(kStreamThreads);
     const double *pin = ws.cjso_part + (size_t)((t - 1) & 1) * kStreamMaxGroups * 4;
     double *pout = ws.cjso_part + (size_t)(t & 1) * kStreamMaxGroups * 4;
-#define NVFP4_ITER(F, S)                                                                                          \
-    hipLaunchKernelGGL((k_cjso_iter<F, S>), grid, block, 0, stream, W, nblk, t, iters, pin, groups, pout,           \
+#define NVFP4_ITER(F, S, L)                                                                                       \
+    hipLaunchKernelGGL((k_cjso_iter<F, S, L>), grid, block, 0, stream, W, nblk, t, pin, groups, pout,              \
                        ws.alpha_state, alpha_out, codes, scales, ws.brackets)
+#define NVFP4_ITER_L(F, S)                                                                                        \
+    do {                                                                                                          \
+        if (t == iters) NVFP4_ITER(F, S, true); else NVFP4_ITER(F, S, false);                                     \
+    } while (0)
     if (f32) {
-        if (soar) NVFP4_ITER(true, true); else NVFP4_ITER(true, false);
+        if (soar) NVFP4_ITER_L(true, true); else NVFP4_ITER_L(true, false);
     } else {
-        if (soar) NVFP4_ITER(false, true); else NVFP4_ITER(false, false);
+        if (soar) NVFP4_ITER_L(false, true); else NVFP4_ITER_L(false, false);
     }
+#undef NVFP4_ITER_L
 #undef NVFP4_ITER
     return hipGetLastError();
 }

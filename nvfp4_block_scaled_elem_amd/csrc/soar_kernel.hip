@@ -148,7 +148,7 @@ __global__ __launch_bounds__(kSoarThreads) void k_soar(const void *__restrict__ 
     if (threadIdx.x < kSoarK) ftab[threadIdx.x] = (float)((double)(50 + threadIdx.x) / 100.0);
     __syncthreads();
 
-    const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t b = (int64_t)blockIdx.x * kSoarThreads + threadIdx.x;
     if (b >= nblk) return;
     const uint32_t dc = scales[b];
     if (dc == 0u) return;  // Delta_c = 0: every candidate quantises to 0 and ties; codes and scale stay 0
