@@ -6,22 +6,24 @@ outlier columns scaled by 20). Twelve distinct matrices (384 MiB, more than the 
 stay resident in HBM and are visited in turn, so each step starts from HBM rather than from cache.
 
 One step = one matrix quantised in each of the four modes, back to back on one stream:
-MAX, FourOverSix, CJSO (8 rounds), SOAR (CJSO(8) + the 202-candidate search). Consecutive steps (different
+MAX, FourOverSix, CJSO (8 rounds), SOAR (CJSO(8) + the decoupled search). Consecutive steps (different
 matrices, separate outputs and workspaces) alternate between two HIP streams, the way a model's
 independent weight matrices are quantised; `single_stream_ms_per_step` gives the same steps on one
 stream. `value` is the weight bytes quantised per second (4 x 32 MiB per step). Per mode the JSON line
-also gives its own GB/s and its share of the relevant peak (HBM for MAX/FourOverSix/CJSO, FP32 vector
-for the search).
+also gives its own GB/s and its share of the HBM peak.
 
-The dominant kernel (the SOAR search) is timed live: the library records HIP events around each of
-its kernels on the stream it launches them on (the `stage_events` hook of the C ABI). Its achieved rate
-is algorithmic FLOPs / duration: per block 101 quantise scales x 16 elements x 9 FLOPs (one multiply
-for the scaled value, and for each of the two reconstruct scales one fused multiply-add for the
-residual and one for its square), against the 157.3 TFLOP/s FP32 vector peak.
+The dominant kernel is the CJSO round (k_cjso_iter): sixteen of them per step. It is timed live: the
+library records HIP events around each of its kernels on the stream it launches them on (the
+`stage_events` hook of the C ABI). Its achieved rate is algorithmic bytes / duration against the 8 TB/s
+HBM peak; a round that is not the last reads the block (2 B per element) and its scale byte and writes
+the new scale byte: 2.125 B per element. The search is reported the same way (2.75 B per element:
+read the block, its scale and its two-byte scale bracket; write codes and scale), and once more with
+NVFP4_FLAG_FULL_SEARCH (all 202 candidates) against the FP32 vector peak: per block 101 quantise
+scales x 16 elements x 9 FLOPs.
 
 cpu_baseline: the oracle (plain C, one thread) on rows 0..255 of the first matrix in all four modes.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--streams S]
 """
 from __future__ import annotations
 
@@ -46,7 +48,9 @@ N_MATS = 12
 ITERS = 8
 MODES = (("max", 0), ("4o6", 0), ("cjso", ITERS), ("soar", ITERS))
 SEARCH_FLOPS_PER_BLOCK = 101 * 16 * 9
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_k_soar_4096x4096.txt")
+ROUND_BYTES_PER_ELEM = 2 + 1 / 16 + 1 / 16  # CJSO round (not the last): read W and scale, write scale
+SEARCH_BYTES_PER_ELEM = 2 + 1 / 16 + 2 / 16 + 1 / 2 + 1 / 16  # read W, scale, bracket; write codes, scale
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_k_cjso_iter_4096x4096.txt")
 COPY_BYTES = 256 << 20
 KERNEL_NAMES = {
     "max": ["k_amax", "k_quant"],
@@ -60,14 +64,14 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-# the sources the search kernel (and so its counter figures) is built from
-SEARCH_SOURCES = ("soar_kernel.hip", "block.hpp", "codec.hpp", "launch.hpp")
+# the sources the CJSO round kernel (and so its counter figures) is built from
+ROUND_SOURCES = ("quant_kernels.hip", "block.hpp", "codec.hpp", "launch.hpp")
 
 
 def source_hash() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "nvfp4_block_scaled_elem_amd", "csrc")
-    for name in SEARCH_SOURCES:
+    for name in ROUND_SOURCES:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -179,6 +183,25 @@ def main():
     for s in range(n_ev):
         step(args.warmup + s, evs[s], n=1, own_streams=False)
     torch.cuda.synchronize()
+    # CJSO calls with only two events, before round 1 and after round ITERS-1: the average round as the
+    # rounds run back to back (per-kernel events add a gap in front of every kernel)
+    o = outs[0]["cjso"]
+    span_ev = []
+    for s in range(n_ev):
+        ev = [None] * (nk["cjso"] + 1)
+        ev[2] = torch.cuda.Event(enable_timing=True)
+        ev[2 + ITERS - 1] = torch.cuda.Event(enable_timing=True)
+        nv.quantize(mats[(args.warmup + s) % N_MATS], "cjso", ITERS, codes=o["codes"], scales=o["scales"],
+                    alpha=o["alpha"], workspace=o["workspace"], stage_events=ev)
+        span_ev.append((ev[2], ev[2 + ITERS - 1]))
+    torch.cuda.synchronize()
+    # the SOAR call again with the 202-candidate search (same outputs), for its kernel time
+    o = outs[0]["soar"]
+    full_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nk["soar"] + 1)] for _ in range(n_ev)]
+    for s in range(n_ev):
+        nv.quantize(mats[(args.warmup + s) % N_MATS], "soar", ITERS, codes=o["codes"], scales=o["scales"],
+                    alpha=o["alpha"], workspace=o["workspace"], stage_events=full_ev[s], full_search=True)
+    torch.cuda.synchronize()
 
     # the same step replayed from HIP graphs (one per resident matrix), for the launch overhead
     graphs = []
@@ -210,19 +233,34 @@ def main():
         per_mode[mode]["kernels_ms"] = {k: round(float(np.mean(v)), 5) for k, v in per_mode[mode]["kernels_ms"].items()}
         kern[mode] = dur
     nblk = ROWS * COLS // 16
+    nel = ROWS * COLS
+    # CJSO rounds other than the last: the span of rounds 1 .. ITERS-1 over their number
+    t_round = float(np.mean([a.elapsed_time(b) for a, b in span_ev])) / (ITERS - 1) * 1e-3
+    rounds = np.concatenate([kern[m][:, 2:2 + ITERS - 1].reshape(-1) for m in ("cjso", "soar")])
+    per_mode["cjso"]["round_ms_per_kernel_events"] = round(float(rounds.mean()), 5)
+    round_gbps = nel * ROUND_BYTES_PER_ELEM / t_round / 1e9
+    per_mode["cjso"]["round_ms"] = round(t_round * 1e3, 5)
+    per_mode["cjso"]["round_algo_GBps"] = round(round_gbps, 2)
+    per_mode["cjso"]["round_frac_hbm_peak"] = round(round_gbps * 1e9 / PEAK_HBM, 4)
     t_search = float(kern["soar"][:, -1].mean()) * 1e-3
-    search_tflops = nblk * SEARCH_FLOPS_PER_BLOCK / t_search / 1e12
-    per_mode["soar"]["search_ms"] = round(t_search * 1e3, 5)
-    per_mode["soar"]["search_frac_fp32_peak"] = round(search_tflops * 1e12 / PEAK_FP32, 4)
+    search_gbps = nel * SEARCH_BYTES_PER_ELEM / t_search / 1e9
+    t_full = float(np.mean([e[-2].elapsed_time(e[-1]) for e in full_ev])) * 1e-3
+    full_tflops = nblk * SEARCH_FLOPS_PER_BLOCK / t_full / 1e12
+    per_mode["soar"].update({
+        "search_ms": round(t_search * 1e3, 5), "search_algo_GBps": round(search_gbps, 2),
+        "search_frac_hbm_peak": round(search_gbps * 1e9 / PEAK_HBM, 4),
+        "full_search_ms": round(t_full * 1e3, 5), "full_search_TFLOPs": round(full_tflops, 3),
+        "full_search_frac_fp32_peak": round(full_tflops * 1e12 / PEAK_FP32, 4),
+    })
     m4 = int(out["4o6"]["mchoice"].sum().item())
     per_mode["4o6"]["m4_fraction"] = round(m4 / nblk, 4)
     # HBM view of the memory-bound single passes: algorithmic bytes of the whole call (read W once,
     # write codes and scales) over the call time
-    algo_bytes = ROWS * COLS * (2 + 0.5 + 1.0 / 16)
+    algo_bytes = nel * (2 + 0.5 + 1.0 / 16)
     for mode in ("max", "4o6"):
         per_mode[mode]["algo_GBps"] = round(algo_bytes / (per_mode[mode]["ms"] * 1e-3) / 1e9, 2)
 
-    # HBM bytes per launch of the search kernel from the committed rocprofv3 counter summary, used only
+    # HBM bytes per launch of the CJSO round from the committed rocprofv3 counter summary, used only
     # while the kernel sources are the ones it was taken with
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
@@ -234,10 +272,11 @@ def main():
                     fields[k.strip()] = v.strip()
         if fields.get("source_hash") == source_hash():
             traffic = int(float(fields["bytes_per_launch"]))
-    roofline = {"bound": "alu", "kernel": "k_soar (decoupled search)", "achieved": round(search_tflops, 3),
-                "peak": PEAK_FP32 / 1e12, "unit": "TFLOP/s", "frac": round(search_tflops * 1e12 / PEAK_FP32, 4),
-                "traffic": traffic, "algorithmic_flops_per_launch": nblk * SEARCH_FLOPS_PER_BLOCK,
-                "avg_launch_ms": round(t_search * 1e3, 5)}
+    roofline = {"bound": "hbm", "kernel": "k_cjso_iter (CJSO round other than the last)",
+                "achieved": round(round_gbps, 2), "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                "frac": round(round_gbps * 1e9 / PEAK_HBM, 4), "traffic": traffic,
+                "algorithmic_bytes_per_launch": int(nel * ROUND_BYTES_PER_ELEM),
+                "avg_launch_ms": round(t_round * 1e3, 5), "launches_per_step": 2 * (ITERS - 1)}
 
     value = len(MODES) * ROWS * COLS * 2 / (ms_per_step * 1e-3) / 1e9
     line = {

@@ -112,7 +112,7 @@ typedef struct nvfp4_args {
     void *const *stage_events; /* nullable: nvfp4_kernel_count(mode, iters) + 1 hipEvent_t handles; the
                                   call records stage_events[0] before its first kernel and
                                   stage_events[j + 1] after kernel j, so each kernel can be timed on
-                                  `stream` */
+                                  `stream`; NULL entries are skipped (fewer records, smaller gaps) */
     int n_stage_events;
     unsigned flags; /* NVFP4_FLAG_* bits (0 for the defaults) */
 } nvfp4_args_t;

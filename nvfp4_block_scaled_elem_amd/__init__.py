@@ -100,7 +100,7 @@ def quantize(W: torch.Tensor, mode: str, iters: int = 0, *, codes=None, scales=N
     scales [rows, cols//16] uint8 E4M3 bits, alpha [1] float32), all on W's device. Optional
     preallocated outputs, an ``mchoice`` uint8 [rows, cols//16] tensor (FourOverSix), a ``stats``
     int32 [4] tensor, a uint8 ``workspace`` tensor, a ``stream`` and a list of
-    ``torch.cuda.Event(enable_timing=True)`` stage events may be passed. ``full_search`` makes the
+    ``torch.cuda.Event(enable_timing=True)`` stage events (None entries are skipped) may be passed. ``full_search`` makes the
     SOAR search visit all 202 candidates of every block (same outputs; NVFP4_FLAG_FULL_SEARCH)."""
     if W.dim() != 2 or not W.is_cuda or not W.is_contiguous() or W.dtype not in DTYPES:
         raise NVFP4Error("W must be a contiguous 2-D bf16 or fp32 CUDA tensor")
@@ -136,9 +136,10 @@ def quantize(W: torch.Tensor, mode: str, iters: int = 0, *, codes=None, scales=N
     ev_arr = None
     if stage_events is not None:
         for e in stage_events:  # torch creates the HIP event at its first record
-            if not e.cuda_event:
+            if e is not None and not e.cuda_event:
                 e.record(stream if stream is not None else torch.cuda.current_stream(dev))
-        ev_arr = (ctypes.c_void_p * len(stage_events))(*[e.cuda_event for e in stage_events])
+        ev_arr = (ctypes.c_void_p * len(stage_events))(
+            *[e.cuda_event if e is not None else None for e in stage_events])
         a.stage_events = ctypes.cast(ev_arr, ctypes.c_void_p)
         a.n_stage_events = len(stage_events)
     _check(lib().nvfp4_quantize_ex(ctypes.byref(a)))

@@ -45,9 +45,9 @@ int check(const nvfp4_args_t *a) {
     return NVFP4_OK;
 }
 
-// Records stage event j (profiling hook; no-op without events).
+// Records stage event j (profiling hook; no-op without events or for a NULL entry).
 bool mark(const nvfp4_args_t *a, int j) {
-    if (!a->stage_events) return true;
+    if (!a->stage_events || !a->stage_events[j]) return true;
     return hipEventRecord(static_cast<hipEvent_t>(a->stage_events[j]), static_cast<hipStream_t>(a->stream)) ==
            hipSuccess;
 }

@@ -133,12 +133,19 @@ __device__ __forceinline__ void sums_bf16(uint32_t c0, uint32_t c1, const uint32
     acc_bf16<3>(c1, p[7], sw, sq);
 }
 
+// The value itself, opaque to the optimiser: keeps the widening of w for the rare binary64 path inside
+// that path (the compiler otherwise hoists it in front of the branch, onto every block).
+__device__ __forceinline__ float opaque(float x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
 template <int SEL>
 __device__ __forceinline__ void acc_f64(uint32_t c, float w0, float w1, double &sw, double &sq) {
     const f32x2 q = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, SEL);
     const double q0 = (double)q.x, q1 = (double)q.y;
-    sw = fma((double)w0, q0, sw);
-    sw = fma((double)w1, q1, sw);
+    sw = fma((double)opaque(w0), q0, sw);
+    sw = fma((double)opaque(w1), q1, sw);
     sq = fma(q0, q0, sq);
     sq = fma(q1, q1, sq);
 }
@@ -166,12 +173,9 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // s = fl(alpha * Delta) and r = fl(1/s) (0 for s = 0) for every E4M3 code, built once per work-group.
-// lim[c] = 2^(ilogb(s)+13): a bf16 block's binary32 S_wq below it is exact (see the header; the
-// products w*q are all >= 0, so every partial sum is at most the final one).
 struct ScaleTab {
     float s[128];
     float r[128];
-    float lim[128];
 };
 
 template <int THREADS>
@@ -180,32 +184,8 @@ __device__ __forceinline__ void build_scale_tab(ScaleTab &T, float alpha) {
         const float s = c < 0x7F ? alpha * e4m3_value((uint32_t)c) : 0.0f;
         T.s[c] = s;
         T.r[c] = s == 0.0f ? 0.0f : 1.0f / s;
-        T.lim[c] = s > 0.0f ? ldexpf(1.0f, ilogbf(s) + 13) : INFINITY;  // s = 0: every sum is 0
     }
     lds_barrier();
-}
-
-// Codes and exact sums for table entry d, without the block max: the binary32 sums are taken first and
-// kept when S_wq is below the exactness limit, else the block is summed again in binary64.
-template <bool F32>
-__device__ __forceinline__ void quant_sums_t(const Blk<F32> &B, const ScaleTab &T, uint32_t d, uint32_t &c0,
-                                             uint32_t &c1, double &sw, double &sq) {
-    const float r = T.r[d];
-    const bool rfin = finite_pos(r);
-    if (rfin)
-        encode16(B.w, r, c0, c1);
-    else
-        encode16_soft(B.w, r, c0, c1);
-    if constexpr (!F32) {
-        float a, q;
-        sums_bf16(c0, c1, B.p, a, q);
-        if (rfin && a < T.lim[d]) {
-            sw = a;
-            sq = q;
-            return;
-        }
-    }
-    sums_f64(c0, c1, B.w, sw, sq);
 }
 
 // Codes for the scale s (reciprocal r = fl(1/s), or 0 when s = 0: every code is then 0) and the exact

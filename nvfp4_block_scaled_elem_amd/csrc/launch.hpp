@@ -22,6 +22,9 @@ namespace nvfp4 {
 #ifndef NVFP4_STREAM_GROUPS
 #define NVFP4_STREAM_GROUPS 512
 #endif
+#ifndef NVFP4_DEPTH  // bf16 blocks held in flight per thread by the streaming passes
+#define NVFP4_DEPTH 2
+#endif
 constexpr int kAmaxThreads = 256;
 constexpr int kAmaxMaxGroups = 1024;
 constexpr int kStreamThreads = NVFP4_STREAM_THREADS;

@@ -142,54 +142,51 @@ __device__ __forceinline__ void store_codes(uint8_t *codes, int64_t b, uint32_t 
     *reinterpret_cast<uint2 *>(codes + 8 * b) = make_uint2(e2m1_clear_negzero(c0), e2m1_clear_negzero(c1));
 }
 
-// Visit this thread's blocks b = gid, gid + S, gid + 2S, ... (S = all threads of the grid) in a
-// two-stage software pipeline: the loads of the next block (index clamped into range, so the last one
-// re-reads a valid block) are in flight while the current one is processed. The loop is unrolled by two
-// so that no register copy waits on a load. `pre` issues the prologue's own loads, then the first
-// block's loads are issued, then `post` (run by every thread of the work-group) finishes the prologue;
-// it returns false to skip the blocks (the function then returns false). f(b, B, sc) gets the block
-// and, when `sc_in` is given, its scale byte.
+// Visit this thread's blocks b = gid, gid + S, gid + 2S, ... (S = all threads of the grid) through a
+// ring of kDepth blocks in registers: the loads of block i + kDepth are issued as soon as block i has
+// been unpacked, so kDepth - 1 blocks are in flight while one is processed (indices past the end are
+// clamped to the last block, a cached re-read). The ring is unrolled, so no register copy waits on a
+// load. `pre` issues the prologue's own loads, then the first kDepth blocks are requested, then `post`
+// (run by every thread of the work-group) finishes the prologue; it returns false to skip the blocks
+// (the function then returns false). f(b, B, sc) gets the block and, when `sc_in` is given, its scale
+// byte.
+template <bool F32>
+constexpr int kDepth = F32 ? 2 : NVFP4_DEPTH;
+
 template <bool F32, class Pre, class Post, class F>
 __device__ __forceinline__ bool for_my_blocks(const void *__restrict__ W, const uint8_t *__restrict__ sc_in,
                                               int64_t nblk, Pre &&pre, Post &&post, F &&f) {
+    constexpr int D = kDepth<F32>;
     const int64_t stride = (int64_t)gridDim.x * kStreamThreads;
     int64_t b = (int64_t)blockIdx.x * kStreamThreads + threadIdx.x;
     const int64_t last = nblk - 1;
-    Raw<F32> ra, rb;
-    uint32_t sa = 0u, sb = 0u;
+    Raw<F32> r[D];
+    uint32_t sc[D];
     pre();
-    {
-        const int64_t c = b < last ? b : last;
-        ra.load(W, c);
-        if (sc_in) sa = sc_in[c];
+#pragma unroll
+    for (int k = 0; k < D; ++k) {
+        const int64_t bk = b + k * stride;
+        const int64_t c = bk < last ? bk : last;
+        r[k].load(W, c);
+        sc[k] = sc_in ? (uint32_t)sc_in[c] : 0u;
     }
     if (!post()) return false;
     if (b >= nblk) return true;
     for (;;) {
-        int64_t bn = b + stride;
-        const int64_t cb = bn < last ? bn : last;
-        rb.load(W, cb);
-        if (sc_in) sb = sc_in[cb];
-        {
+#pragma unroll
+        for (int k = 0; k < D; ++k) {
             Blk<F32> B;
-            B.set(ra);
-            f(b, B, sa);
+            B.set(r[k]);
+            const uint32_t s = sc[k];
+            const int64_t bn = b + D * stride;
+            const int64_t c = bn < last ? bn : last;
+            r[k].load(W, c);
+            if (sc_in) sc[k] = sc_in[c];
+            f(b, B, s);
+            b += stride;
+            if (b >= nblk) return true;
         }
-        if (bn >= nblk) break;
-        b = bn;
-        bn = b + stride;
-        const int64_t ca = bn < last ? bn : last;
-        ra.load(W, ca);
-        if (sc_in) sa = sc_in[ca];
-        {
-            Blk<F32> B;
-            B.set(rb);
-            f(b, B, sb);
-        }
-        if (bn >= nblk) break;
-        b = bn;
     }
-    return true;
 }
 
 // ---------------------------------------------------------------------------------- global max
@@ -254,7 +251,7 @@ __global__ __launch_bounds__(kAmaxThreads) void k_amax(const uint4 *__restrict__
 // ------------------------------------------------------------------------- MAX and FourOverSix
 
 template <bool F32, bool FOS>
-__global__ __launch_bounds__(kStreamThreads) void k_quant(const void *__restrict__ W, int64_t nblk,
+__global__ __launch_bounds__(kStreamThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_quant(const void *__restrict__ W, int64_t nblk,
                                                           const uint32_t *__restrict__ amax_part, int amax_n,
                                                           uint8_t *__restrict__ codes, uint8_t *__restrict__ scales,
                                                           float *__restrict__ alpha_out, uint8_t *__restrict__ mchoice,
@@ -354,11 +351,12 @@ __global__ __launch_bounds__(kCountThreads) void k_count(const uint32_t *__restr
 
 // ----------------------------------------------------------------------------------------- CJSO
 
-// Max rule plus, when rounds follow, the least-squares sums of the first alpha-step.
-template <bool F32, bool SOAR>
-__global__ __launch_bounds__(kStreamThreads) void k_cjso_init(const void *__restrict__ W, int64_t nblk,
+// Max rule plus, when rounds follow (ROUNDS), the least-squares sums of the first alpha-step; without
+// rounds the max-rule codes (and for SOAR the E4M3 bracket of the unrounded block scale) are final.
+template <bool F32, bool SOAR, bool ROUNDS>
+__global__ __launch_bounds__(kStreamThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_cjso_init(const void *__restrict__ W, int64_t nblk,
                                                               const uint32_t *__restrict__ amax_part, int amax_n,
-                                                              int iters, uint8_t *__restrict__ codes,
+                                                              uint8_t *__restrict__ codes,
                                                               uint8_t *__restrict__ scales,
                                                               float *__restrict__ alpha_out,
                                                               float *__restrict__ alpha_state,
@@ -376,7 +374,7 @@ __global__ __launch_bounds__(kStreamThreads) void k_cjso_init(const void *__rest
         if (blockIdx.x == 0 && threadIdx.x == 0) {
             const float av = nonfinite ? __builtin_nanf("") : alpha;
             alpha_state[0] = av;
-            if (iters == 0) *alpha_out = av;
+            if (!ROUNDS) *alpha_out = av;
             if (stats) stats->status = nonfinite ? NVFP4_STATUS_NONFINITE : 0u;
         }
         if (nonfinite) return false;
@@ -391,7 +389,7 @@ __global__ __launch_bounds__(kStreamThreads) void k_cjso_init(const void *__rest
         const float v = e4m3_value(d);
         scales[b] = (uint8_t)d;
         uint32_t c0, c1;
-        if (iters == 0) {
+        if constexpr (!ROUNDS) {
             const float r = T.r[d];
             if (finite_pos(r))
                 encode16(B.w, r, c0, c1);
@@ -405,7 +403,7 @@ __global__ __launch_bounds__(kStreamThreads) void k_cjso_init(const void *__rest
             }
         } else {
             double sw, sq;
-            quant_sums_t(B, T, d, c0, c1, sw, sq);
+            quant_sums_r(B, a, T.s[d], T.r[d], c0, c1, sw, sq);
             const dd t = two_prod((double)v, sw);
             acc2(N, t.hi, t.lo);
             acc2(D, (double)v * (double)v * sq, 0.0);
@@ -419,7 +417,7 @@ __global__ __launch_bounds__(kStreamThreads) void k_cjso_init(const void *__rest
             if (SOAR) brackets[b] = 0;
         }
     }
-    if (iters > 0) {
+    if (ROUNDS) {
         wg_sum_dd2(N, D);
         if (threadIdx.x == 0) {
             part_out[4 * blockIdx.x + 0] = N.hi;
@@ -434,7 +432,7 @@ __global__ __launch_bounds__(kStreamThreads) void k_cjso_init(const void *__rest
 // page, block-scale closed form, rounded to E4M3), re-quantise; then the sums for round t+1, or, in the
 // last round (LAST), the codes (and for SOAR the E4M3 bracket of the unrounded block scale).
 template <bool F32, bool SOAR, bool LAST>
-__global__ __launch_bounds__(kStreamThreads) void k_cjso_iter(const void *__restrict__ W, int64_t nblk, int t,
+__global__ __launch_bounds__(kStreamThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_cjso_iter(const void *__restrict__ W, int64_t nblk, int t,
                                                               const double *__restrict__ part_in, int n_part,
                                                               double *__restrict__ part_out, float *alpha_state,
                                                               float *__restrict__ alpha_out,
@@ -478,8 +476,12 @@ __global__ __launch_bounds__(kStreamThreads) void k_cjso_iter(const void *__rest
         }
         scales[b] = (uint8_t)dn;
         const float vn = e4m3_value(dn);
-        quant_sums_r(B, a, T.s[dn], T.r[dn], c0, c1, sw, sq);
+        // an unchanged scale re-quantises to the same codes and sums (the common case once the rounds
+        // settle; a wave skips this when none of its blocks changed)
+        if (dn != d) quant_sums_r(B, a, T.s[dn], T.r[dn], c0, c1, sw, sq);
         if (!LAST) {
+            // vn has 4 significant bits, S_wq at most 53 and S_qq at most 12: v*S_wq needs the exact
+            // product, v^2*S_qq is exact in binary64
             const dd tn = two_prod((double)vn, sw);
             acc2(Nn, tn.hi, tn.lo);
             acc2(Dn, (double)vn * (double)vn * sq, 0.0);
@@ -666,14 +668,19 @@ hipError_t launch_cjso_init(const void *W, bool f32, bool soar, int64_t nblk, co
                             int groups, nvfp4_stats_t *stats, hipStream_t stream) {
     const dim3 grid(groups), block(kStreamThreads);
     double *part = ws.cjso_part;  // round 0 writes buffer 0
-#define NVFP4_INIT(F, S)                                                                                          \
-    hipLaunchKernelGGL((k_cjso_init<F, S>), grid, block, 0, stream, W, nblk, amax_part, amax_n, iters, codes, scales, \
+#define NVFP4_INIT(F, S, R)                                                                                       \
+    hipLaunchKernelGGL((k_cjso_init<F, S, R>), grid, block, 0, stream, W, nblk, amax_part, amax_n, codes, scales,    \
                        alpha_out, ws.alpha_state, part, ws.brackets, stats)
+#define NVFP4_INIT_R(F, S)                                                                                        \
+    do {                                                                                                          \
+        if (iters > 0) NVFP4_INIT(F, S, true); else NVFP4_INIT(F, S, false);                                      \
+    } while (0)
     if (f32) {
-        if (soar) NVFP4_INIT(true, true); else NVFP4_INIT(true, false);
+        if (soar) NVFP4_INIT_R(true, true); else NVFP4_INIT_R(true, false);
     } else {
-        if (soar) NVFP4_INIT(false, true); else NVFP4_INIT(false, false);
+        if (soar) NVFP4_INIT_R(false, true); else NVFP4_INIT_R(false, false);
     }
+#undef NVFP4_INIT_R
 #undef NVFP4_INIT
     return hipGetLastError();
 }

@@ -270,6 +270,14 @@ def test_stage_events():
     torch.cuda.synchronize()
     t = [ev[j].elapsed_time(ev[j + 1]) for j in range(n)]
     assert len(t) == 6 and all(x >= 0 for x in t)
+    # NULL entries are skipped: a span over the three rounds, same outputs as without events
+    sparse = [None] * (n + 1)
+    sparse[2], sparse[5] = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c1, s1, a1 = nv.quantize(Wd, "soar", 3, stage_events=sparse)
+    c0, s0, a0 = nv.quantize(Wd, "soar", 3)
+    torch.cuda.synchronize()
+    assert sparse[2].elapsed_time(sparse[5]) >= 0
+    assert torch.equal(c0, c1) and torch.equal(s0, s1) and torch.equal(a0, a1)
 
 
 # ------------------------------------------------------------------------------ codec kernels
