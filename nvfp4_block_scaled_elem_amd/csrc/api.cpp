@@ -72,7 +72,7 @@ int run(const nvfp4_args_t *a, void *ws_base) {
         return NVFP4_OK;
     }
     const bool soar = a->mode == NVFP4_MODE_SOAR;
-    const int gc = stream_groups(nblk);
+    const int gc = cjso_groups(nblk);
     if (launch_cjso_init(a->W, f32, soar, nblk, ws.amax_part, ga, a->iters, a->codes_out, a->scales_out, a->alpha_out,
                          ws, gc, a->stats_out, st) != hipSuccess ||
         !mark(a, j++))

@@ -10,37 +10,51 @@
 
 namespace nvfp4 {
 
-// Work-group counts of the reduction kernels: the global max pass and the streaming per-block passes
-// (MAX, FourOverSix, CJSO). Their per-work-group partial results are what every work-group of the next
-// kernel reduces, so the streaming passes use a fixed grid of at most two work-groups per CU, each
-// thread walking at least kMinBlocksPerThread blocks (its loads of block i+1 overlap block i). The
-// defaults are the fastest of the settings measured on an MI355X for a 4096 x 4096 matrix; the macros
-// exist so that other settings can be built and timed.
-#ifndef NVFP4_STREAM_THREADS
-#define NVFP4_STREAM_THREADS 512
+// Shapes of the streaming passes. Each pass writes one partial result per work-group that every
+// work-group of the next kernel reduces, so they use a fixed grid (at most G work-groups of T threads,
+// each thread walking at least kMinBlocksPerThread blocks) and keep D blocks per thread in flight in a
+// register ring. The MAX/FourOverSix pass (k_quant) and the CJSO passes (k_cjso_init, k_cjso_iter) are
+// tuned separately: the defaults are the fastest of the settings timed on an MI355X for a 4096 x 4096
+// matrix, and the macros exist so that other settings can be built and timed.
+#ifndef NVFP4_QUANT_THREADS
+#define NVFP4_QUANT_THREADS 512
 #endif
-#ifndef NVFP4_STREAM_GROUPS
-#define NVFP4_STREAM_GROUPS 512
+#ifndef NVFP4_QUANT_GROUPS
+#define NVFP4_QUANT_GROUPS 512
 #endif
-#ifndef NVFP4_DEPTH  // bf16 blocks held in flight per thread by the streaming passes
-#define NVFP4_DEPTH 2
+#ifndef NVFP4_QUANT_DEPTH
+#define NVFP4_QUANT_DEPTH 2
+#endif
+#ifndef NVFP4_CJSO_THREADS
+#define NVFP4_CJSO_THREADS 256
+#endif
+#ifndef NVFP4_CJSO_GROUPS
+#define NVFP4_CJSO_GROUPS 512
+#endif
+#ifndef NVFP4_CJSO_DEPTH
+#define NVFP4_CJSO_DEPTH 1
 #endif
 constexpr int kAmaxThreads = 256;
 constexpr int kAmaxMaxGroups = 1024;
-constexpr int kStreamThreads = NVFP4_STREAM_THREADS;
-constexpr int kStreamMaxGroups = NVFP4_STREAM_GROUPS;
+constexpr int kQuantThreads = NVFP4_QUANT_THREADS;
+constexpr int kQuantGroups = NVFP4_QUANT_GROUPS;
+constexpr int kQuantDepth = NVFP4_QUANT_DEPTH;
+constexpr int kCjsoThreads = NVFP4_CJSO_THREADS;
+constexpr int kCjsoGroups = NVFP4_CJSO_GROUPS;
+constexpr int kCjsoDepth = NVFP4_CJSO_DEPTH;
 constexpr int kMinBlocksPerThread = 2;
 
 int amax_groups(int64_t nchunks);
-int stream_groups(int64_t nblk);
+int quant_groups(int64_t nblk);
+int cjso_groups(int64_t nblk);
 
 // Scratch layout inside the workspace (byte offsets, 256-byte aligned pieces).
 struct Workspace {
     uint32_t *amax_part;  // [kAmaxMaxGroups]   max |w| bits per work-group
     float *alpha_state;   // [2]                alpha of the previous / current CJSO round
-    double *cjso_part;    // [2][kStreamMaxGroups][4] (N.hi, N.lo, D.hi, D.lo) per work-group
+    double *cjso_part;    // [2][kCjsoGroups][4] (N.hi, N.lo, D.hi, D.lo) per work-group
     uint16_t *brackets;   // [nblk]             E4M3 codes lo | hi << 8 around the unrounded CJSO scale (SOAR)
-    uint32_t *m4_part;    // [kStreamMaxGroups] FourOverSix M=4 counts per work-group (same offset)
+    uint32_t *m4_part;    // [kQuantGroups] FourOverSix M=4 counts per work-group (same offset)
 };
 size_t workspace_bytes(int64_t nblk, int mode);
 Workspace carve(void *base, int64_t nblk);

@@ -24,20 +24,23 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t m) {
     return m;
 }
 
-// Max over the work-group of one value per thread; every thread gets the result.
+// Max over the work-group (T threads) of one value per thread; every thread gets the result.
+template <int T>
 __device__ __forceinline__ uint32_t wg_max(uint32_t m) {
-    __shared__ uint32_t red[16];
+    __shared__ uint32_t red[T / 64];
     m = wave_max_u32(m);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
     lds_barrier();
     m = 0u;
-    for (int i = 0; i < kStreamThreads / 64; ++i) m = red[i] > m ? red[i] : m;
+#pragma unroll
+    for (int i = 0; i < T / 64; ++i) m = red[i] > m ? red[i] : m;
     return m;
 }
 
-// Work-group sum of two double-doubles (fixed order); the result is valid in thread 0.
+// Work-group sum (T threads) of two double-doubles (fixed order); the result is valid in thread 0.
+template <int T>
 __device__ __forceinline__ void wg_sum_dd2(dd &N, dd &D) {
-    __shared__ double red[16][4];
+    __shared__ double red[T / 64][4];
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
         const dd n2 = {__shfl_xor(N.hi, o), __shfl_xor(N.lo, o)};
@@ -55,7 +58,7 @@ __device__ __forceinline__ void wg_sum_dd2(dd &N, dd &D) {
     if (threadIdx.x == 0) {
         N = {red[0][0], red[0][1]};
         D = {red[0][2], red[0][3]};
-        for (int i = 1; i < kStreamThreads / 64; ++i) {
+        for (int i = 1; i < T / 64; ++i) {
             N = dd_add(N, dd{red[i][0], red[i][1]});
             D = dd_add(D, dd{red[i][2], red[i][3]});
         }
@@ -64,16 +67,15 @@ __device__ __forceinline__ void wg_sum_dd2(dd &N, dd &D) {
 
 // A kernel's prologue reads the previous kernel's per-work-group partials. Each thread loads its share
 // first (before the block prefetch, so that waiting for these loads does not wait for the prefetch)
-// and reduces it afterwards.
-constexpr int kAmaxPerThread = (kAmaxMaxGroups + kStreamThreads - 1) / kStreamThreads;
-constexpr int kPartPerThread = (kStreamMaxGroups + kStreamThreads - 1) / kStreamThreads;
-
+// and reduces it afterwards. T = threads of the reading kernel, G = most partials.
+template <int T>
 struct AmaxShare {
-    uint32_t v[kAmaxPerThread];
+    static constexpr int K = (kAmaxMaxGroups + T - 1) / T;
+    uint32_t v[K];
     __device__ __forceinline__ void load(const uint32_t *part, int n) {
 #pragma unroll
-        for (int k = 0; k < kAmaxPerThread; ++k) {
-            const int i = (int)threadIdx.x + k * kStreamThreads;
+        for (int k = 0; k < K; ++k) {
+            const int i = (int)threadIdx.x + k * T;
             v[k] = i < n ? part[i] : 0u;
         }
     }
@@ -81,17 +83,19 @@ struct AmaxShare {
     __device__ __forceinline__ uint32_t reduce() const {
         uint32_t m = 0u;
 #pragma unroll
-        for (int k = 0; k < kAmaxPerThread; ++k) m = v[k] > m ? v[k] : m;
-        return wg_max(m);
+        for (int k = 0; k < K; ++k) m = v[k] > m ? v[k] : m;
+        return wg_max<T>(m);
     }
 };
 
+template <int T, int G>
 struct CjsoShare {
-    double v[kPartPerThread][4];
+    static constexpr int K = (G + T - 1) / T;
+    double v[K][4];
     __device__ __forceinline__ void load(const double *part, int n) {
 #pragma unroll
-        for (int k = 0; k < kPartPerThread; ++k) {
-            const int i = (int)threadIdx.x + k * kStreamThreads;
+        for (int k = 0; k < K; ++k) {
+            const int i = (int)threadIdx.x + k * T;
 #pragma unroll
             for (int j = 0; j < 4; ++j) v[k][j] = i < n ? part[4 * i + j] : 0.0;
         }
@@ -102,11 +106,11 @@ struct CjsoShare {
         N = {0.0, 0.0};
         D = {0.0, 0.0};
 #pragma unroll
-        for (int k = 0; k < kPartPerThread; ++k) {
+        for (int k = 0; k < K; ++k) {
             N = dd_add(N, dd{v[k][0], v[k][1]});
             D = dd_add(D, dd{v[k][2], v[k][3]});
         }
-        wg_sum_dd2(N, D);
+        wg_sum_dd2<T>(N, D);
         if (threadIdx.x == 0) {
             tot[0] = N.hi;
             tot[1] = N.lo;
@@ -142,23 +146,19 @@ __device__ __forceinline__ void store_codes(uint8_t *codes, int64_t b, uint32_t 
     *reinterpret_cast<uint2 *>(codes + 8 * b) = make_uint2(e2m1_clear_negzero(c0), e2m1_clear_negzero(c1));
 }
 
-// Visit this thread's blocks b = gid, gid + S, gid + 2S, ... (S = all threads of the grid) through a
-// ring of kDepth blocks in registers: the loads of block i + kDepth are issued as soon as block i has
-// been unpacked, so kDepth - 1 blocks are in flight while one is processed (indices past the end are
-// clamped to the last block, a cached re-read). The ring is unrolled, so no register copy waits on a
-// load. `pre` issues the prologue's own loads, then the first kDepth blocks are requested, then `post`
-// (run by every thread of the work-group) finishes the prologue; it returns false to skip the blocks
-// (the function then returns false). f(b, B, sc) gets the block and, when `sc_in` is given, its scale
-// byte.
-template <bool F32>
-constexpr int kDepth = F32 ? 2 : NVFP4_DEPTH;
-
-template <bool F32, class Pre, class Post, class F>
+// Visit this thread's blocks b = gid, gid + S, gid + 2S, ... (S = all T * gridDim threads) through a
+// ring of DEPTH blocks in registers: the loads of block i + DEPTH are issued as soon as block i has been
+// unpacked, so DEPTH blocks are in flight while one is processed (indices past the end are clamped to
+// the last block, a cached re-read). The ring is unrolled, so no register copy waits on a load. `pre`
+// issues the prologue's own loads, then the first DEPTH blocks are requested, then `post` (run by every
+// thread of the work-group) finishes the prologue; it returns false to skip the blocks (the function
+// then returns false). f(b, B, sc) gets the block and, when `sc_in` is given, its scale byte.
+template <int T, int DEPTH, bool F32, class Pre, class Post, class F>
 __device__ __forceinline__ bool for_my_blocks(const void *__restrict__ W, const uint8_t *__restrict__ sc_in,
                                               int64_t nblk, Pre &&pre, Post &&post, F &&f) {
-    constexpr int D = kDepth<F32>;
-    const int64_t stride = (int64_t)gridDim.x * kStreamThreads;
-    int64_t b = (int64_t)blockIdx.x * kStreamThreads + threadIdx.x;
+    constexpr int D = DEPTH;
+    const int64_t stride = (int64_t)gridDim.x * T;
+    int64_t b = (int64_t)blockIdx.x * T + threadIdx.x;
     const int64_t last = nblk - 1;
     Raw<F32> r[D];
     uint32_t sc[D];
@@ -251,13 +251,13 @@ __global__ __launch_bounds__(kAmaxThreads) void k_amax(const uint4 *__restrict__
 // ------------------------------------------------------------------------- MAX and FourOverSix
 
 template <bool F32, bool FOS>
-__global__ __launch_bounds__(kStreamThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_quant(const void *__restrict__ W, int64_t nblk,
+__global__ __launch_bounds__(kQuantThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_quant(const void *__restrict__ W, int64_t nblk,
                                                           const uint32_t *__restrict__ amax_part, int amax_n,
                                                           uint8_t *__restrict__ codes, uint8_t *__restrict__ scales,
                                                           float *__restrict__ alpha_out, uint8_t *__restrict__ mchoice,
                                                           nvfp4_stats_t *stats, uint32_t *__restrict__ m4_part) {
     __shared__ ScaleTab T;
-    AmaxShare am;
+    AmaxShare<kQuantThreads> am;
     float alpha = 0.0f;
     uint32_t m4count = 0u;
     auto pre = [&] { am.load(amax_part, amax_n); };
@@ -270,10 +270,10 @@ __global__ __launch_bounds__(kStreamThreads) __attribute__((amdgpu_waves_per_eu(
             if (stats) stats->status = nonfinite ? NVFP4_STATUS_NONFINITE : 0u;
         }
         if (nonfinite) return false;
-        build_scale_tab<kStreamThreads>(T, alpha);
+        build_scale_tab<kQuantThreads>(T, alpha);
         return true;
     };
-    const bool finite = for_my_blocks<F32>(W, nullptr, nblk, pre, post,
+    const bool finite = for_my_blocks<kQuantThreads, kQuantDepth, F32>(W, nullptr, nblk, pre, post,
                                            [&](int64_t b, const Blk<F32> &B, uint32_t) {
             uint32_t c0, c1, sc;
             bool m4 = false;
@@ -314,22 +314,22 @@ __global__ __launch_bounds__(kStreamThreads) __attribute__((amdgpu_waves_per_eu(
             scales[b] = (uint8_t)sc;
         });
     if (!finite) {  // non-finite input: all-zero codes and scales
-        const int64_t stride = (int64_t)gridDim.x * kStreamThreads;
-        for (int64_t b = (int64_t)blockIdx.x * kStreamThreads + threadIdx.x; b < nblk; b += stride) {
+        const int64_t stride = (int64_t)gridDim.x * kQuantThreads;
+        for (int64_t b = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x; b < nblk; b += stride) {
             store_codes(codes, b, 0u, 0u);
             scales[b] = 0;
             if (FOS && mchoice) mchoice[b] = 0;
         }
     }
     if (FOS && m4_part) {  // per work-group count of M=4 blocks (summed by k_count only if asked)
-        __shared__ uint32_t cnt[kStreamThreads / 64];
+        __shared__ uint32_t cnt[kQuantThreads / 64];
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) m4count += (uint32_t)__shfl_xor((int)m4count, o);
         if ((threadIdx.x & 63) == 0) cnt[threadIdx.x >> 6] = m4count;
         __syncthreads();
         if (threadIdx.x == 0) {
             uint32_t t = 0u;
-            for (int i = 0; i < kStreamThreads / 64; ++i) t += cnt[i];
+            for (int i = 0; i < kQuantThreads / 64; ++i) t += cnt[i];
             m4_part[blockIdx.x] = t;
         }
     }
@@ -354,7 +354,7 @@ __global__ __launch_bounds__(kCountThreads) void k_count(const uint32_t *__restr
 // Max rule plus, when rounds follow (ROUNDS), the least-squares sums of the first alpha-step; without
 // rounds the max-rule codes (and for SOAR the E4M3 bracket of the unrounded block scale) are final.
 template <bool F32, bool SOAR, bool ROUNDS>
-__global__ __launch_bounds__(kStreamThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_cjso_init(const void *__restrict__ W, int64_t nblk,
+__global__ __launch_bounds__(kCjsoThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_cjso_init(const void *__restrict__ W, int64_t nblk,
                                                               const uint32_t *__restrict__ amax_part, int amax_n,
                                                               uint8_t *__restrict__ codes,
                                                               uint8_t *__restrict__ scales,
@@ -363,7 +363,7 @@ __global__ __launch_bounds__(kStreamThreads) __attribute__((amdgpu_waves_per_eu(
                                                               double *__restrict__ part_out,
                                                               uint16_t *__restrict__ brackets, nvfp4_stats_t *stats) {
     __shared__ ScaleTab T;
-    AmaxShare am;
+    AmaxShare<kCjsoThreads> am;
     float alpha = 0.0f;
     dd N = {0.0, 0.0}, D = {0.0, 0.0};
     auto pre = [&] { am.load(amax_part, amax_n); };
@@ -378,10 +378,10 @@ __global__ __launch_bounds__(kStreamThreads) __attribute__((amdgpu_waves_per_eu(
             if (stats) stats->status = nonfinite ? NVFP4_STATUS_NONFINITE : 0u;
         }
         if (nonfinite) return false;
-        build_scale_tab<kStreamThreads>(T, alpha);
+        build_scale_tab<kCjsoThreads>(T, alpha);
         return true;
     };
-    const bool finite = for_my_blocks<F32>(W, nullptr, nblk, pre, post,
+    const bool finite = for_my_blocks<kCjsoThreads, kCjsoDepth, F32>(W, nullptr, nblk, pre, post,
                                            [&](int64_t b, const Blk<F32> &B, uint32_t) {
         const float a = B.amax();
         const double q = max_rule_quotient(a, alpha);
@@ -410,15 +410,15 @@ __global__ __launch_bounds__(kStreamThreads) __attribute__((amdgpu_waves_per_eu(
         }
     });
     if (!finite) {  // non-finite input: all-zero outputs; the rounds see alpha = NaN and stop
-        const int64_t stride = (int64_t)gridDim.x * kStreamThreads;
-        for (int64_t b = (int64_t)blockIdx.x * kStreamThreads + threadIdx.x; b < nblk; b += stride) {
+        const int64_t stride = (int64_t)gridDim.x * kCjsoThreads;
+        for (int64_t b = (int64_t)blockIdx.x * kCjsoThreads + threadIdx.x; b < nblk; b += stride) {
             store_codes(codes, b, 0u, 0u);
             scales[b] = 0;
             if (SOAR) brackets[b] = 0;
         }
     }
     if (ROUNDS) {
-        wg_sum_dd2(N, D);
+        wg_sum_dd2<kCjsoThreads>(N, D);
         if (threadIdx.x == 0) {
             part_out[4 * blockIdx.x + 0] = N.hi;
             part_out[4 * blockIdx.x + 1] = N.lo;
@@ -432,14 +432,14 @@ __global__ __launch_bounds__(kStreamThreads) __attribute__((amdgpu_waves_per_eu(
 // page, block-scale closed form, rounded to E4M3), re-quantise; then the sums for round t+1, or, in the
 // last round (LAST), the codes (and for SOAR the E4M3 bracket of the unrounded block scale).
 template <bool F32, bool SOAR, bool LAST>
-__global__ __launch_bounds__(kStreamThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_cjso_iter(const void *__restrict__ W, int64_t nblk, int t,
+__global__ __launch_bounds__(kCjsoThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_cjso_iter(const void *__restrict__ W, int64_t nblk, int t,
                                                               const double *__restrict__ part_in, int n_part,
                                                               double *__restrict__ part_out, float *alpha_state,
                                                               float *__restrict__ alpha_out,
                                                               uint8_t *__restrict__ codes, uint8_t *__restrict__ scales,
                                                               uint16_t *__restrict__ brackets) {
     __shared__ ScaleTab T;
-    CjsoShare sh;
+    CjsoShare<kCjsoThreads, kCjsoGroups> sh;
     float alpha = 0.0f;
     dd Nn = {0.0, 0.0}, Dn = {0.0, 0.0};
     auto pre = [&] { sh.load(part_in, n_part); };
@@ -459,10 +459,10 @@ __global__ __launch_bounds__(kStreamThreads) __attribute__((amdgpu_waves_per_eu(
             alpha_state[t & 1] = alpha;
             if (LAST) *alpha_out = alpha;
         }
-        build_scale_tab<kStreamThreads>(T, alpha);
+        build_scale_tab<kCjsoThreads>(T, alpha);
         return true;
     };
-    if (!for_my_blocks<F32>(W, scales, nblk, pre, post, [&](int64_t b, const Blk<F32> &B, uint32_t d) {
+    if (!for_my_blocks<kCjsoThreads, kCjsoDepth, F32>(W, scales, nblk, pre, post, [&](int64_t b, const Blk<F32> &B, uint32_t d) {
         const float v = e4m3_value(d);
         uint32_t c0, c1;
         double sw, sq;
@@ -496,7 +496,7 @@ __global__ __launch_bounds__(kStreamThreads) __attribute__((amdgpu_waves_per_eu(
     }))
         return;
     if (!LAST) {
-        wg_sum_dd2(Nn, Dn);
+        wg_sum_dd2<kCjsoThreads>(Nn, Dn);
         if (threadIdx.x == 0) {
             part_out[4 * blockIdx.x + 0] = Nn.hi;
             part_out[4 * blockIdx.x + 1] = Nn.lo;
@@ -595,18 +595,19 @@ int amax_groups(int64_t nchunks) {
     return (int)(g < 1 ? 1 : (g > kAmaxMaxGroups ? kAmaxMaxGroups : g));
 }
 
-int stream_groups(int64_t nblk) {
-    int64_t g = (nblk + (int64_t)kStreamThreads * kMinBlocksPerThread - 1) /
-                ((int64_t)kStreamThreads * kMinBlocksPerThread);
-    return (int)(g < 1 ? 1 : (g > kStreamMaxGroups ? kStreamMaxGroups : g));
+static int stream_groups(int64_t nblk, int threads, int max_groups) {
+    int64_t g = (nblk + (int64_t)threads * kMinBlocksPerThread - 1) / ((int64_t)threads * kMinBlocksPerThread);
+    return (int)(g < 1 ? 1 : (g > max_groups ? max_groups : g));
 }
+int quant_groups(int64_t nblk) { return stream_groups(nblk, kQuantThreads, kQuantGroups); }
+int cjso_groups(int64_t nblk) { return stream_groups(nblk, kCjsoThreads, kCjsoGroups); }
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t workspace_bytes(int64_t nblk, int mode) {
     size_t s = align256(sizeof(uint32_t) * kAmaxMaxGroups) + align256(2 * sizeof(float)) +
-               align256(sizeof(double) * 2 * kStreamMaxGroups * 4);
-    if (mode == NVFP4_MODE_FOUR_OVER_SIX) s += align256(sizeof(uint32_t) * kStreamMaxGroups);
+               align256(sizeof(double) * 2 * kCjsoGroups * 4);
+    if (mode == NVFP4_MODE_FOUR_OVER_SIX) s += align256(sizeof(uint32_t) * kQuantGroups);
     if (mode == NVFP4_MODE_SOAR) s += align256(sizeof(uint16_t) * (size_t)nblk);
     return s;
 }
@@ -620,7 +621,7 @@ Workspace carve(void *base, int64_t nblk) {
     w.alpha_state = reinterpret_cast<float *>(p);
     p += align256(2 * sizeof(float));
     w.cjso_part = reinterpret_cast<double *>(p);
-    p += align256(sizeof(double) * 2 * kStreamMaxGroups * 4);
+    p += align256(sizeof(double) * 2 * kCjsoGroups * 4);
     w.brackets = reinterpret_cast<uint16_t *>(p);  // SOAR only
     w.m4_part = reinterpret_cast<uint32_t *>(p);    // FourOverSix only (same offset: the modes differ)
     return w;
@@ -641,8 +642,8 @@ hipError_t launch_amax(const void *W, bool f32, int64_t n, uint32_t *amax_part, 
 hipError_t launch_quant(const void *W, bool f32, bool fos, int64_t nblk, const uint32_t *amax_part, int amax_n,
                         uint8_t *codes, uint8_t *scales, float *alpha_out, uint8_t *mchoice, nvfp4_stats_t *stats,
                         uint32_t *m4_part, hipStream_t stream) {
-    const int groups = stream_groups(nblk);
-    const dim3 grid(groups), block(kStreamThreads);
+    const int groups = quant_groups(nblk);
+    const dim3 grid(groups), block(kQuantThreads);
     uint32_t *mp = (fos && stats) ? m4_part : nullptr;
     if (f32) {
         if (fos)
@@ -666,7 +667,7 @@ hipError_t launch_quant(const void *W, bool f32, bool fos, int64_t nblk, const u
 hipError_t launch_cjso_init(const void *W, bool f32, bool soar, int64_t nblk, const uint32_t *amax_part, int amax_n,
                             int iters, uint8_t *codes, uint8_t *scales, float *alpha_out, const Workspace &ws,
                             int groups, nvfp4_stats_t *stats, hipStream_t stream) {
-    const dim3 grid(groups), block(kStreamThreads);
+    const dim3 grid(groups), block(kCjsoThreads);
     double *part = ws.cjso_part;  // round 0 writes buffer 0
 #define NVFP4_INIT(F, S, R)                                                                                       \
     hipLaunchKernelGGL((k_cjso_init<F, S, R>), grid, block, 0, stream, W, nblk, amax_part, amax_n, codes, scales,    \
@@ -687,9 +688,9 @@ hipError_t launch_cjso_init(const void *W, bool f32, bool soar, int64_t nblk, co
 
 hipError_t launch_cjso_iter(const void *W, bool f32, bool soar, int64_t nblk, int t, int iters, uint8_t *codes,
                             uint8_t *scales, float *alpha_out, const Workspace &ws, int groups, hipStream_t stream) {
-    const dim3 grid(groups), block(kStreamThreads);
-    const double *pin = ws.cjso_part + (size_t)((t - 1) & 1) * kStreamMaxGroups * 4;
-    double *pout = ws.cjso_part + (size_t)(t & 1) * kStreamMaxGroups * 4;
+    const dim3 grid(groups), block(kCjsoThreads);
+    const double *pin = ws.cjso_part + (size_t)((t - 1) & 1) * kCjsoGroups * 4;
+    double *pout = ws.cjso_part + (size_t)(t & 1) * kCjsoGroups * 4;
 #define NVFP4_ITER(F, S, L)                                                                                       \
     hipLaunchKernelGGL((k_cjso_iter<F, S, L>), grid, block, 0, stream, W, nblk, t, pin, groups, pout,              \
                        ws.alpha_state, alpha_out, codes, scales, ws.brackets)
