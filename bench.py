@@ -21,6 +21,9 @@ read the block, its scale and its two-byte scale bracket; write codes and scale)
 NVFP4_FLAG_FULL_SEARCH (all 202 candidates) against the FP32 vector peak: per block 101 quantise
 scales x 16 elements x 9 FLOPs.
 
+c5_whole_model: the 224 matrices of a 7B-shaped model (32 layers; 12.95 GB bf16) quantised one after
+another in each mode, total time and aggregate GB/s (skipped with --no-c5).
+
 cpu_baseline: the oracle (plain C, one thread) on rows 0..255 of the first matrix in all four modes.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--streams S]
@@ -90,6 +93,69 @@ def cpu_baseline(W0: np.ndarray) -> dict:
                       f"one thread, {dt:.1f} s"}
 
 
+C5_SHAPES = {"q": (4096, 4096), "k": (4096, 4096), "v": (4096, 4096), "o": (4096, 4096),
+             "gate": (11008, 4096), "up": (11008, 4096), "down": (4096, 11008)}
+C5_LAYERS = 32
+
+
+def c5_pass(torch, nv, dev, streams):
+    """Whole-model workload: 32 layers x {q, k, v, o 4096x4096; gate, up 11008x4096; down 4096x11008}
+    bf16 (224 matrices, 12.95 GB), resident in HBM, quantised matrix by matrix in each mode (consecutive
+    matrices alternate over the streams). Returns total time and aggregate GB/s per mode. The weights
+    follow the same recipe as the parity inputs (Student-t, nu = 5, std 0.02) but are drawn on the GPU
+    with torch's generator, so that the pass takes seconds."""
+    log("c5: generating 224 matrices on the GPU")
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+    mats = []
+    for layer in range(C5_LAYERS):
+        for name, (r, c) in C5_SHAPES.items():
+            z = torch.randn((r, c), generator=g, device=dev)
+            chi = torch.zeros((r, c), device=dev)
+            for _ in range(5):
+                chi += torch.randn((r, c), generator=g, device=dev).square()
+            t = z / torch.sqrt(chi / 5.0) * (0.02 / (5.0 / 3.0) ** 0.5)
+            mats.append(t.to(torch.bfloat16))
+            del z, chi, t
+    torch.cuda.synchronize()
+    total_bytes = sum(m.numel() * 2 for m in mats)
+    n_streams = len(streams)
+    bufs = []
+    for k in range(n_streams):
+        b = {}
+        for mode, _ in MODES:
+            b[mode] = dict(workspace=torch.empty(nv.workspace_bytes(11008, 4096, mode), dtype=torch.uint8, device=dev))
+        b["codes"] = {shape: torch.empty((shape[0], shape[1] // 2), dtype=torch.uint8, device=dev)
+                      for shape in set(C5_SHAPES.values())}
+        b["scales"] = {shape: torch.empty((shape[0], shape[1] // 16), dtype=torch.uint8, device=dev)
+                       for shape in set(C5_SHAPES.values())}
+        b["alpha"] = torch.empty(1, dtype=torch.float32, device=dev)
+        bufs.append(b)
+
+    def run(mode, iters):
+        for i, W in enumerate(mats):
+            k = i % n_streams
+            b = bufs[k]
+            shape = tuple(W.shape)
+            with torch.cuda.stream(streams[k]):
+                nv.quantize(W, mode, iters, codes=b["codes"][shape], scales=b["scales"][shape], alpha=b["alpha"],
+                            workspace=b[mode]["workspace"])
+
+    out = {"matrices": len(mats), "bytes": total_bytes, "streams": n_streams, "modes": {}}
+    for mode, iters in MODES:
+        run(mode, iters)  # warm-up pass
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        run(mode, iters)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        out["modes"][mode] = {"total_ms": round(dt * 1e3, 3), "GBps": round(total_bytes / dt / 1e9, 2)}
+        log(f"c5 {mode}: {dt * 1e3:.1f} ms")
+    del mats
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -97,6 +163,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--streams", type=int, default=2, help="HIP streams that consecutive steps alternate over")
+    ap.add_argument("--no-c5", action="store_true", help="skip the whole-model (224 matrices) pass")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device copy 5 times (scales the HBM byte counters)")
     args = ap.parse_args()
@@ -278,6 +345,8 @@ def main():
                 "algorithmic_bytes_per_launch": int(nel * ROUND_BYTES_PER_ELEM),
                 "avg_launch_ms": round(t_round * 1e3, 5), "launches_per_step": 2 * (ITERS - 1)}
 
+    c5 = None if args.no_c5 else c5_pass(torch, nv, dev, streams)
+
     value = len(MODES) * ROWS * COLS * 2 / (ms_per_step * 1e-3) / 1e9
     line = {
         "metric": METRIC, "value": round(value, 3), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -293,6 +362,8 @@ def main():
         "graph_replay_ms_per_step": round(graph_ms_per_step, 5),
         "roofline": roofline,
     }
+    if c5 is not None:
+        line["c5_whole_model"] = c5
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         line["cpu_baseline"] = cpu_baseline(W0)
