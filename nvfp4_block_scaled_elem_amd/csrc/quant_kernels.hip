@@ -15,12 +15,50 @@ namespace nvfp4 {
 
 // ------------------------------------------------------------------------------- reductions
 
+// Wave-wide reductions on the VALU through DPP (no LDS round trips): swaps within quads (xor 1, xor 2),
+// the half-row and row mirrors (which pair the two quads of each half-row, then the two half-rows of
+// each row), then the row broadcasts of lane 15 to rows 1 and 3 and of lane 31 to rows 2 and 3. Rows
+// left out by a step's row mask receive `old` = 0, the identity, so lane 63 ends with the total.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROWS, 0xF, false);
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double dpp_f64(double x) {
+    const uint64_t u = (uint64_t)__double_as_longlong(x);
+    const uint64_t lo = dpp_u32<CTRL, ROWS>((uint32_t)u), hi = dpp_u32<CTRL, ROWS>((uint32_t)(u >> 32));
+    return __longlong_as_double((long long)((hi << 32) | lo));
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140,
+              kDppBcast15 = 0x142, kDppBcast31 = 0x143;
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ void dd2_step(dd &N, dd &D) {
+    const dd n2 = {dpp_f64<CTRL, ROWS>(N.hi), dpp_f64<CTRL, ROWS>(N.lo)};
+    const dd d2 = {dpp_f64<CTRL, ROWS>(D.hi), dpp_f64<CTRL, ROWS>(D.lo)};
+    N = dd_add(N, n2);
+    D = dd_add(D, d2);
+}
+
+// Sum of two double-doubles over the wave (fixed order); valid in lane 63.
+__device__ __forceinline__ void wave_sum_dd2(dd &N, dd &D) {
+    dd2_step<kDppXor1, 0xF>(N, D);
+    dd2_step<kDppXor2, 0xF>(N, D);
+    dd2_step<kDppHalfMirror, 0xF>(N, D);
+    dd2_step<kDppMirror, 0xF>(N, D);
+    dd2_step<kDppBcast15, 0xA>(N, D);
+    dd2_step<kDppBcast31, 0xC>(N, D);
+}
+
+// Max over the wave; valid in lane 63.
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t m) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const uint32_t t = (uint32_t)__shfl_xor((int)m, o);
-        m = t > m ? t : m;
-    }
+    uint32_t t;
+    t = dpp_u32<kDppXor1, 0xF>(m); m = t > m ? t : m;
+    t = dpp_u32<kDppXor2, 0xF>(m); m = t > m ? t : m;
+    t = dpp_u32<kDppHalfMirror, 0xF>(m); m = t > m ? t : m;
+    t = dpp_u32<kDppMirror, 0xF>(m); m = t > m ? t : m;
+    t = dpp_u32<kDppBcast15, 0xA>(m); m = t > m ? t : m;
+    t = dpp_u32<kDppBcast31, 0xC>(m); m = t > m ? t : m;
     return m;
 }
 
@@ -29,7 +67,7 @@ template <int T>
 __device__ __forceinline__ uint32_t wg_max(uint32_t m) {
     __shared__ uint32_t red[T / 64];
     m = wave_max_u32(m);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    if ((threadIdx.x & 63) == 63) red[threadIdx.x >> 6] = m;
     lds_barrier();
     m = 0u;
 #pragma unroll
@@ -41,14 +79,8 @@ __device__ __forceinline__ uint32_t wg_max(uint32_t m) {
 template <int T>
 __device__ __forceinline__ void wg_sum_dd2(dd &N, dd &D) {
     __shared__ double red[T / 64][4];
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const dd n2 = {__shfl_xor(N.hi, o), __shfl_xor(N.lo, o)};
-        const dd d2 = {__shfl_xor(D.hi, o), __shfl_xor(D.lo, o)};
-        N = dd_add(N, n2);
-        D = dd_add(D, d2);
-    }
-    if ((threadIdx.x & 63) == 0) {
+    wave_sum_dd2(N, D);
+    if ((threadIdx.x & 63) == 63) {
         red[threadIdx.x >> 6][0] = N.hi;
         red[threadIdx.x >> 6][1] = N.lo;
         red[threadIdx.x >> 6][2] = D.hi;
@@ -236,9 +268,10 @@ __global__ __launch_bounds__(kAmaxThreads) void k_amax(const uint4 *__restrict__
     }
     __shared__ uint32_t red[kAmaxThreads / 64];
     m = wave_max_u32(m);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    if ((threadIdx.x & 63) == 63) red[threadIdx.x >> 6] = m;
     __syncthreads();
     if (threadIdx.x == 0) {
+        m = red[0];
         for (int k = 1; k < kAmaxThreads / 64; ++k) m = red[k] > m ? red[k] : m;
         part[blockIdx.x] = m;
         if (blockIdx.x == 0 && stats) {
