@@ -144,6 +144,20 @@ int nvfp4_encode_e2m1(const float *x, int64_t n, uint8_t *codes, void *stream);
 int nvfp4_dequantize(const uint8_t *codes, const uint8_t *scales, const float *alpha, int64_t rows,
                      int64_t cols, void *out, int out_dtype, void *stream);
 
+/* Reconstruction statistics of an encoding of W (SOAR page, dequantisation: w is reconstructed as
+ * e2m1(code) * e4m3(scale) * alpha). W is [rows][cols] of dtype (enum nvfp4_dtype); codes, scales and
+ * alpha are laid out as the quantiser writes them (scale sign bits are ignored). All pointers are device
+ * pointers. On completion of the stream work:
+ *   sse_out[0]  = sum over elements of d^2, d = w - (q * alpha) * Delta formed in binary64 (exact up to the
+ *                 rounding of that difference) and the squares summed as double-doubles, then rounded to
+ *                 binary64 (mean squared error = sse / (rows * cols));
+ *   hist_out[c] = number of elements whose 4-bit code is c, c = 0..15.
+ * Scratch is taken from a stream-ordered pool and given back on the same stream. Errors: as
+ * nvfp4_quantize (arguments are checked on the host; nothing is enqueued on error). */
+int nvfp4_error_stats(const void *W, int dtype, int64_t rows, int64_t cols, const uint8_t *codes,
+                      const uint8_t *scales, const float *alpha, double *sse_out,
+                      unsigned long long *hist_out, void *stream);
+
 /* Text of an nvfp4_error value. */
 const char *nvfp4_status_string(int status);
 

@@ -51,6 +51,8 @@ def lib() -> ctypes.CDLL:
             raise NVFP4Error(f"{LIB_PATH} is missing: build it with `python nvfp4_block_scaled_elem_amd/build.py`")
         L = ctypes.CDLL(LIB_PATH)
         i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+        L.nvfp4_error_stats.argtypes = [vp, i32, i64, i64, vp, vp, vp, vp, vp, vp]
+        L.nvfp4_error_stats.restype = i32
         L.nvfp4_quantize_ex.argtypes = [ctypes.POINTER(_Args)]
         L.nvfp4_quantize_ex.restype = i32
         L.nvfp4_quantize.argtypes = [vp, i64, i64, i32, i32, vp, vp, vp, vp]
@@ -164,3 +166,23 @@ def dequantize(codes: torch.Tensor, scales: torch.Tensor, alpha: torch.Tensor, d
     _check(lib().nvfp4_dequantize(codes.data_ptr(), scales.data_ptr(), alpha.data_ptr(), rows, cols,
                                   out.data_ptr(), DTYPES[dtype], _stream_ptr(stream, codes.device)))
     return out
+
+
+def error_stats(W: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, alpha: torch.Tensor, stream=None):
+    """Reconstruction statistics of an encoding of ``W`` (all CUDA tensors, as quantize returns them):
+    returns (sse float64 tensor [1], hist int64 tensor [16]) on W's device, where sse is the sum of squared
+    differences between W and e2m1(code) * e4m3(scale) * alpha and hist[c] counts the elements with code c."""
+    if W.dim() != 2 or not W.is_cuda or not W.is_contiguous() or W.dtype not in DTYPES:
+        raise NVFP4Error("W must be a contiguous 2-D bf16 or fp32 CUDA tensor")
+    rows, cols = W.shape
+    dev = W.device
+    for t in (codes, scales, alpha):
+        if not t.is_cuda or t.device != dev or not t.is_contiguous():
+            raise NVFP4Error("codes, scales and alpha must be contiguous tensors on W's device")
+    if codes.numel() != rows * cols // 2 or scales.numel() != rows * cols // 16 or alpha.numel() < 1:
+        raise NVFP4Error("codes, scales or alpha do not match W's shape")
+    sse = torch.empty(1, dtype=torch.float64, device=dev)
+    hist = torch.empty(16, dtype=torch.int64, device=dev)
+    _check(lib().nvfp4_error_stats(W.data_ptr(), DTYPES[W.dtype], rows, cols, codes.data_ptr(), scales.data_ptr(),
+                                   alpha.data_ptr(), sse.data_ptr(), hist.data_ptr(), _stream_ptr(stream, dev)))
+    return sse, hist

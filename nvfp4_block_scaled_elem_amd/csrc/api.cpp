@@ -168,6 +168,25 @@ NVFP4_API int nvfp4_dequantize(const uint8_t *codes, const uint8_t *scales, cons
                : NVFP4_ERR_HIP;
 }
 
+NVFP4_API int nvfp4_error_stats(const void *W, int dtype, int64_t rows, int64_t cols, const uint8_t *codes,
+                                const uint8_t *scales, const float *alpha, double *sse_out,
+                                unsigned long long *hist_out, void *stream) {
+    if (!W || !codes || !scales || !alpha || !sse_out || !hist_out || rows <= 0 || cols <= 0)
+        return NVFP4_ERR_INVALID_ARG;
+    if (dtype != NVFP4_DTYPE_BF16 && dtype != NVFP4_DTYPE_F32) return NVFP4_ERR_INVALID_ARG;
+    if (cols % 16 != 0 || rows > kMaxElems / cols) return NVFP4_ERR_SHAPE;
+    if (((uintptr_t)W & 15u) != 0 || ((uintptr_t)codes & 7u) != 0 || ((uintptr_t)alpha & 3u) != 0 ||
+        ((uintptr_t)sse_out & 7u) != 0 || ((uintptr_t)hist_out & 7u) != 0)
+        return NVFP4_ERR_INVALID_ARG;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    void *ws = nullptr;
+    if (hipMallocAsync(&ws, nvfp4::stats_workspace_bytes(), st) != hipSuccess) return NVFP4_ERR_HIP;
+    const bool ok = nvfp4::launch_stats(W, dtype == NVFP4_DTYPE_F32, rows * cols / 16, codes, scales, alpha, sse_out,
+                                        hist_out, ws, st) == hipSuccess;
+    if (hipFreeAsync(ws, st) != hipSuccess) return NVFP4_ERR_HIP;
+    return ok ? NVFP4_OK : NVFP4_ERR_HIP;
+}
+
 NVFP4_API const char *nvfp4_status_string(int status) {
     switch (status) {
         case NVFP4_OK: return "ok";

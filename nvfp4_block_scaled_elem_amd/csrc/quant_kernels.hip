@@ -621,6 +621,77 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t *__restrict__ cod
     }
 }
 
+// --------------------------------------------------------------------------- error statistics
+
+// Reconstruction error and code histogram of an encoding (SOAR page, dequantisation: the reconstruction
+// of w is Q * alpha * Delta). Per element d = fl64(w - (q*alpha)*Delta) (q*alpha and the product with
+// Delta are exact in binary64), and d^2 is summed exactly as a double-double; each work-group writes its
+// sum and its 16 code counts, and k_stats_final adds the partials in a fixed order.
+constexpr int kStatThreads = 256;
+constexpr int kStatMaxGroups = 512;
+
+template <bool F32>
+__global__ __launch_bounds__(kStatThreads) void k_stats(const void *__restrict__ W, int64_t nblk,
+                                                        const uint8_t *__restrict__ codes,
+                                                        const uint8_t *__restrict__ scales,
+                                                        const float *__restrict__ alpha_p, double *__restrict__ part,
+                                                        uint32_t *__restrict__ part_hist) {
+    __shared__ uint32_t hist[16];
+    if (threadIdx.x < 16) hist[threadIdx.x] = 0u;
+    lds_barrier();
+    const double alpha = (double)*alpha_p;
+    dd S = {0.0, 0.0}, Z = {0.0, 0.0};
+    const int64_t stride = (int64_t)gridDim.x * kStatThreads;
+    for (int64_t b = (int64_t)blockIdx.x * kStatThreads + threadIdx.x; b < nblk; b += stride) {
+        Blk<F32> B;
+        B.load(W, b);
+        const uint2 c = *reinterpret_cast<const uint2 *>(codes + 8 * b);
+        const double dv = (double)e4m3_value(scales[b] & 0x7Fu);
+        const uint32_t cw[2] = {c.x, c.y};
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const f32x2 q = p == 0   ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[h], 1.0f, 0)
+                                : p == 1 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[h], 1.0f, 1)
+                                : p == 2 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[h], 1.0f, 2)
+                                         : __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[h], 1.0f, 3);
+                const int j = 8 * h + 2 * p;
+                const double d0 = (double)B.w[j] - (double)q.x * alpha * dv;
+                const double d1 = (double)B.w[j + 1] - (double)q.y * alpha * dv;
+                const dd e0 = two_prod(d0, d0), e1 = two_prod(d1, d1);
+                acc2(S, e0.hi, e0.lo);
+                acc2(S, e1.hi, e1.lo);
+                atomicAdd(&hist[(cw[h] >> (8 * p)) & 15u], 1u);
+                atomicAdd(&hist[(cw[h] >> (8 * p + 4)) & 15u], 1u);
+            }
+        }
+    }
+    wg_sum_dd2<kStatThreads>(S, Z);
+    lds_barrier();
+    if (threadIdx.x == 0) {
+        part[2 * blockIdx.x] = S.hi;
+        part[2 * blockIdx.x + 1] = S.lo;
+    }
+    if (threadIdx.x < 16) part_hist[16 * blockIdx.x + threadIdx.x] = hist[threadIdx.x];
+}
+
+// sse_out = sum of the partial sums (fixed order), hist_out[i] = sum of the partial counts of code i.
+__global__ __launch_bounds__(kStatThreads) void k_stats_final(const double *__restrict__ part,
+                                                              const uint32_t *__restrict__ part_hist, int groups,
+                                                              double *__restrict__ sse_out,
+                                                              unsigned long long *__restrict__ hist_out) {
+    dd S = {0.0, 0.0}, Z = {0.0, 0.0};
+    for (int g = threadIdx.x; g < groups; g += kStatThreads) S = dd_add(S, dd{part[2 * g], part[2 * g + 1]});
+    wg_sum_dd2<kStatThreads>(S, Z);
+    if (threadIdx.x == 0) *sse_out = S.hi + S.lo;
+    if (threadIdx.x < 16) {
+        unsigned long long n = 0ull;
+        for (int g = 0; g < groups; ++g) n += part_hist[16 * g + threadIdx.x];
+        hist_out[threadIdx.x] = n;
+    }
+}
+
 // ------------------------------------------------------------------------------------ launchers
 
 int amax_groups(int64_t nchunks) {
@@ -744,6 +815,29 @@ hipError_t launch_cjso_iter(const void *W, bool f32, bool soar, int64_t nblk, in
 hipError_t launch_encode_e2m1(const float *x, int64_t n, uint8_t *codes, hipStream_t stream) {
     const int64_t lanes = (n + 7) / 8;
     hipLaunchKernelGGL(k_encode_e2m1, dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, stream, x, n, codes);
+    return hipGetLastError();
+}
+
+size_t stats_workspace_bytes() {
+    return align256(sizeof(double) * 2 * kStatMaxGroups) + align256(sizeof(uint32_t) * 16 * kStatMaxGroups);
+}
+
+hipError_t launch_stats(const void *W, bool f32, int64_t nblk, const uint8_t *codes, const uint8_t *scales,
+                        const float *alpha, double *sse_out, unsigned long long *hist_out, void *workspace,
+                        hipStream_t stream) {
+    int64_t g = (nblk + 4 * kStatThreads - 1) / (4 * kStatThreads);
+    const int groups = (int)(g < 1 ? 1 : (g > kStatMaxGroups ? kStatMaxGroups : g));
+    double *part = static_cast<double *>(workspace);
+    uint32_t *part_hist = reinterpret_cast<uint32_t *>(static_cast<char *>(workspace) +
+                                                       align256(sizeof(double) * 2 * kStatMaxGroups));
+    if (f32)
+        hipLaunchKernelGGL(k_stats<true>, dim3(groups), dim3(kStatThreads), 0, stream, W, nblk, codes, scales, alpha,
+                           part, part_hist);
+    else
+        hipLaunchKernelGGL(k_stats<false>, dim3(groups), dim3(kStatThreads), 0, stream, W, nblk, codes, scales, alpha,
+                           part, part_hist);
+    hipLaunchKernelGGL(k_stats_final, dim3(1), dim3(kStatThreads), 0, stream, part, part_hist, groups, sse_out,
+                       hist_out);
     return hipGetLastError();
 }
 

@@ -86,6 +86,17 @@ def test_plain_entry_points_reject(L):
     assert L.nvfp4_dequantize(FAKE, FAKE, FAKE, 4, 32, FAKE + 8, 1, None) == INVALID
 
 
+def test_error_stats_rejects(L):
+    f = L.nvfp4_error_stats
+    assert f(None, 0, 4, 16, FAKE, FAKE, FAKE, FAKE, FAKE, None) == INVALID
+    assert f(FAKE, 2, 4, 16, FAKE, FAKE, FAKE, FAKE, FAKE, None) == INVALID
+    assert f(FAKE, 0, 4, 24, FAKE, FAKE, FAKE, FAKE, FAKE, None) == SHAPE
+    assert f(FAKE, 0, 0, 16, FAKE, FAKE, FAKE, FAKE, FAKE, None) == INVALID
+    assert f(FAKE + 8, 0, 4, 16, FAKE, FAKE, FAKE, FAKE, FAKE, None) == INVALID
+    assert f(FAKE, 0, 4, 16, FAKE, FAKE, FAKE, FAKE + 4, FAKE, None) == INVALID
+    assert f(FAKE, 1, 4, 16, FAKE, FAKE, FAKE, FAKE, None, None) == INVALID
+
+
 def test_sizes_and_counts(L):
     assert L.nvfp4_workspace_bytes(4096, 4096, 0) > 0
     assert L.nvfp4_workspace_bytes(4096, 4096, 3) >= L.nvfp4_workspace_bytes(4096, 4096, 2) + 2 * 4096 * 256

@@ -379,6 +379,40 @@ def test_soar_tie_prone_inputs_match_oracle(gen, seed):
     compare_live(W, "soar", 8)
 
 
+# ------------------------------------------------------------------------------ error statistics
+
+STATS_CASES = {
+    "c1_fp32_max": (lambda: synth.c1(0), "max", 0),
+    "c1_fp32_4o6": (lambda: synth.c1(0), "4o6", 0),
+    "c2_rows_soar": (lambda: synth.c2(0, 128, 1024), "soar", 8),
+    "ragged_cjso": (lambda: synth.normal_bf16(3, 48, 5), "cjso", 3),
+    "on_grid_max": (lambda: indep.on_grid_matrix(32, 256, -10, 7)[0], "max", 0),
+    "c2_full_4o6": (lambda: synth.c2(0), "4o6", 0),
+}
+
+
+@pytest.mark.parametrize("name", list(STATS_CASES))
+def test_error_stats_match_oracle(name):
+    """nvfp4_error_stats against the oracle's MSE (exact sum of the binary64 differences) and a numpy
+    histogram of the codes."""
+    gen, mode, iters = STATS_CASES[name]
+    W = gen()
+    Wd = to_dev(W)
+    codes, scales, alpha = nv.quantize(Wd, mode, iters)
+    sse, hist = nv.error_stats(Wd, codes, scales, alpha)
+    torch.cuda.synchronize()
+    c, s_, a = codes.cpu().numpy(), scales.cpu().numpy(), float(alpha.cpu()[0])
+    n = W.size
+    ref = oracle.mse(W, c, s_, a) * n
+    got = float(sse.cpu()[0])
+    if ref == 0.0:
+        assert got == 0.0
+    else:
+        assert abs(got - ref) <= 1e-12 * ref, (got, ref)
+    nib = np.stack([c & 15, c >> 4], axis=-1).reshape(-1)
+    assert np.array_equal(hist.cpu().numpy(), np.bincount(nib, minlength=16))
+
+
 # -------------------------------------------------------------------------- full-size digests
 
 def golden():
