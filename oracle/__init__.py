@@ -45,6 +45,8 @@ def lib():
         vp, i64, i32, u8p = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
         L.nvfp4_ref_quantize.argtypes = [vp, i32, i64, i64, i32, i32, u8p, u8p, vp, u8p, vp, vp]
         L.nvfp4_ref_quantize.restype = i32
+        L.nvfp4_ref_quantize_ex.argtypes = [vp, i32, i64, i64, i32, i32, i32, u8p, u8p, vp, u8p, vp, vp]
+        L.nvfp4_ref_quantize_ex.restype = i32
         L.nvfp4_ref_soar_blocks.argtypes = [vp, i32, i64, i64, ctypes.c_float, u8p, vp, vp, i64, u8p, u8p]
         L.nvfp4_ref_soar_blocks.restype = i32
         L.nvfp4_ref_mse.argtypes = [vp, i32, i64, i64, u8p, u8p, ctypes.c_float]
@@ -93,9 +95,13 @@ def _dtype_code(W: np.ndarray) -> int:
     raise TypeError("W must be uint16 (bf16 bits) or float32")
 
 
-def quantize(W: np.ndarray, mode: str, iters: int = 0, *, trace: bool = False):
+INITS = {"max": 0, "4o6": 1}
+
+
+def quantize(W: np.ndarray, mode: str, iters: int = 0, *, trace: bool = False, init: str = "max"):
     """Run the oracle on a whole matrix. Returns a dict with codes, scales, alpha, status and, by
-    mode, mchoice (4o6), dstar (cjso/soar) and alpha_trace (when asked)."""
+    mode, mchoice (4o6), dstar (cjso/soar) and alpha_trace (when asked). `init` is CJSO's starting
+    point ("max" or "4o6"; cjso/soar only)."""
     W = np.ascontiguousarray(W)
     rows, cols = W.shape
     nblk = rows * cols // 16
@@ -105,9 +111,9 @@ def quantize(W: np.ndarray, mode: str, iters: int = 0, *, trace: bool = False):
     dstar = np.zeros((rows, cols // 16), np.float64)
     alpha = ctypes.c_float(0.0)
     tr = np.zeros(iters + 1, np.float32)
-    st = lib().nvfp4_ref_quantize(_ptr(W), _dtype_code(W), rows, cols, MODES[mode], iters, _ptr(codes),
-                                  _ptr(scales), ctypes.byref(alpha), _ptr(mch), _ptr(dstar),
-                                  _ptr(tr) if trace else None)
+    st = lib().nvfp4_ref_quantize_ex(_ptr(W), _dtype_code(W), rows, cols, MODES[mode], iters, INITS[init],
+                                     _ptr(codes), _ptr(scales), ctypes.byref(alpha), _ptr(mch), _ptr(dstar),
+                                     _ptr(tr) if trace else None)
     if st < 0:
         raise ValueError(f"oracle rejected the arguments (status {st})")
     out = {"codes": codes, "scales": scales, "alpha": alpha.value, "status": st}

@@ -34,6 +34,9 @@
  *      Delta_d first). alpha is left as CJSO produced it.
  *   R9 Blocks are 16 consecutive elements of a row; input with a NaN or an infinity yields alpha = NaN
  *      and all-zero codes and scales; an all-zero matrix yields alpha = 0.
+ *   R10 CJSO started from FourOverSix (a composition the pages suggest, not a mode they define): the
+ *      first scales are FourOverSix's choice under the max-rule alpha; the "unrounded" value of a chosen
+ *      Delta4 is 1.5*Delta6, the quantity FourOverSix rounds to get it (for Delta6 it is max|w|/(6 alpha)).
  *
  * Build: gcc -O2 -std=gnu11 -ffp-contract=off (no fast-math): every float expression below is the
  * IEEE operation it spells, in the order written.
@@ -230,16 +233,47 @@ int nvfp4_ref_delta_step(const float *w16, const uint8_t *codes16, float alpha, 
     return 1;
 }
 
-/* [SOAR] CJSO: start from the max rule, then repeat {global-scale step, re-quantise, block-scale step,
+/* [4/6] §02 for one block under alpha a: the max-rule scale Delta6 = E4M3(max|w|/(6a)) and
+ * Delta4 = fp8(1.5·Delta6) (the product is exact; fp8 saturates per R2); M=4 is kept iff its block error
+ * is strictly smaller (mse = error/16, the same order). Writes the block's codes and scale; returns
+ * 1 for M=4. *dstar gets the unrounded value of the chosen scale: max|w|/(6a) for M=6, 1.5·Delta6 for
+ * M=4 (R10). */
+static int four_over_six_block(const float *wb, float a, uint8_t *c16, uint8_t *dcode, double *dstar) {
+    uint8_t c4[16];
+    double q6 = max_rule_quotient(block_amax(wb), a);
+    unsigned d6 = nvfp4_ref_e4m3_rne(q6);
+    unsigned d4 = nvfp4_ref_e4m3_rne(1.5 * nvfp4_ref_e4m3_value(d6));
+    quad e6, e4;
+    nvfp4_ref_quantize_block(wb, a, (float)nvfp4_ref_e4m3_value(d6), c16);
+    nvfp4_ref_quantize_block(wb, a, (float)nvfp4_ref_e4m3_value(d4), c4);
+    e6 = block_err(wb, c16, a, nvfp4_ref_e4m3_value(d6));
+    e4 = block_err(wb, c4, a, nvfp4_ref_e4m3_value(d4));
+    *dcode = (uint8_t)d6;
+    *dstar = q6;
+    if (e4 < e6) {
+        memcpy(c16, c4, 16);
+        *dcode = (uint8_t)d4;
+        *dstar = 1.5 * nvfp4_ref_e4m3_value(d6);
+        return 1;
+    }
+    return 0;
+}
+
+/* [SOAR] CJSO: start from the max rule (or, with init = NVFP4_REF_INIT_4O6, from FourOverSix's choice of
+ * block scale under the max-rule alpha), then repeat {global-scale step, re-quantise, block-scale step,
  * re-quantise} (R7). The stored block scale is FP8, so each Delta-step rounds Delta_i* to E4M3 (the
  * page notes that this rounding reaches both quantisation and dequantisation). On return dcode[] holds
  * the E4M3 scales, dstar[] the last unrounded scales and codes16[] one code per element. */
-static void cjso(const float *w, int64_t nblk, int iters, float amax, float *alpha, uint8_t *dcode,
+static void cjso(const float *w, int64_t nblk, int iters, int init, float amax, float *alpha, uint8_t *dcode,
                  double *dstar, uint8_t *codes16, float *alpha_trace) {
     int64_t i;
     int t;
     *alpha = max_rule_alpha(amax);
     for (i = 0; i < nblk; ++i) {
+        if (init == NVFP4_REF_INIT_4O6) {
+            four_over_six_block(w + 16 * i, *alpha, codes16 + 16 * i, &dcode[i], &dstar[i]);
+            continue;
+        }
         dstar[i] = max_rule_quotient(block_amax(w + 16 * i), *alpha);
         dcode[i] = (uint8_t)nvfp4_ref_e4m3_rne(dstar[i]);
         nvfp4_ref_quantize_block(w + 16 * i, *alpha, (float)nvfp4_ref_e4m3_value(dcode[i]), codes16 + 16 * i);
@@ -334,6 +368,13 @@ static int bad_shape(int64_t rows, int64_t cols, int dtype) {
 int nvfp4_ref_quantize(const void *W, int dtype, int64_t rows, int64_t cols, int mode, int iters,
                        uint8_t *codes, uint8_t *scales, float *alpha, uint8_t *mchoice, double *dstar,
                        float *alpha_trace) {
+    return nvfp4_ref_quantize_ex(W, dtype, rows, cols, mode, iters, NVFP4_REF_INIT_MAX, codes, scales, alpha,
+                                 mchoice, dstar, alpha_trace);
+}
+
+int nvfp4_ref_quantize_ex(const void *W, int dtype, int64_t rows, int64_t cols, int mode, int iters, int init,
+                          uint8_t *codes, uint8_t *scales, float *alpha, uint8_t *mchoice, double *dstar,
+                          float *alpha_trace) {
     int64_t n, nblk, i;
     float *w, amax = 0.0f;
     uint8_t *c16, *dcode;
@@ -342,6 +383,7 @@ int nvfp4_ref_quantize(const void *W, int dtype, int64_t rows, int64_t cols, int
 
     if (!W || !codes || !scales || !alpha || bad_shape(rows, cols, dtype) || mode < 0 || mode > 3 || iters < 0)
         return -1;
+    if (init != NVFP4_REF_INIT_MAX && (init != NVFP4_REF_INIT_4O6 || mode < NVFP4_REF_CJSO)) return -1;
     n = rows * cols;
     nblk = n / 16;
     w = widen(W, dtype, n);
@@ -370,31 +412,22 @@ int nvfp4_ref_quantize(const void *W, int dtype, int64_t rows, int64_t cols, int
 
     if (mode == NVFP4_REF_MAX || mode == NVFP4_REF_FOUR_OVER_SIX) {
         float a = max_rule_alpha(amax);
-        uint8_t c4[16];
         *alpha = a;
         for (i = 0; i < nblk; ++i) {
             const float *wb = w + 16 * i;
+            if (mode == NVFP4_REF_FOUR_OVER_SIX) {
+                double unused;
+                int m4 = four_over_six_block(wb, a, c16 + 16 * i, &dcode[i], &unused);
+                if (mchoice) mchoice[i] = (uint8_t)m4;
+                continue;
+            }
             unsigned d6 = nvfp4_ref_e4m3_rne(max_rule_quotient(block_amax(wb), a));
             nvfp4_ref_quantize_block(wb, a, (float)nvfp4_ref_e4m3_value(d6), c16 + 16 * i);
             dcode[i] = (uint8_t)d6;
-            if (mode == NVFP4_REF_FOUR_OVER_SIX) {
-                /* [4/6] §02: scale_m4 = fp8(scale_m6 · 1.5) (the product is exact; fp8 saturates per R2);
-                 * keep M=4 iff its block error is strictly smaller (mse = error/16, the same order). */
-                unsigned d4 = nvfp4_ref_e4m3_rne(1.5 * nvfp4_ref_e4m3_value(d6));
-                quad e6, e4;
-                nvfp4_ref_quantize_block(wb, a, (float)nvfp4_ref_e4m3_value(d4), c4);
-                e6 = block_err(wb, c16 + 16 * i, a, nvfp4_ref_e4m3_value(d6));
-                e4 = block_err(wb, c4, a, nvfp4_ref_e4m3_value(d4));
-                if (e4 < e6) {
-                    memcpy(c16 + 16 * i, c4, 16);
-                    dcode[i] = (uint8_t)d4;
-                    if (mchoice) mchoice[i] = 1;
-                }
-            }
         }
         if (alpha_trace) alpha_trace[0] = a;
     } else {
-        cjso(w, nblk, iters, amax, alpha, dcode, ds, c16, alpha_trace);
+        cjso(w, nblk, iters, init, amax, alpha, dcode, ds, c16, alpha_trace);
         if (mode == NVFP4_REF_SOAR)
             for (i = 0; i < nblk; ++i) soar_block(w + 16 * i, *alpha, dcode[i], ds[i], c16 + 16 * i, &dcode[i]);
         if (dstar) memcpy(dstar, ds, (size_t)nblk * sizeof(double));

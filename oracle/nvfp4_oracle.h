@@ -20,6 +20,8 @@ extern "C" {
 
 enum { NVFP4_REF_BF16 = 0, NVFP4_REF_F32 = 1 };
 enum { NVFP4_REF_MAX = 0, NVFP4_REF_FOUR_OVER_SIX = 1, NVFP4_REF_CJSO = 2, NVFP4_REF_SOAR = 3 };
+/* Starting point of CJSO (and so of SOAR): the max rule, or FourOverSix's block scales. */
+enum { NVFP4_REF_INIT_MAX = 0, NVFP4_REF_INIT_4O6 = 1 };
 
 /* Returns 0, 1 when W holds a NaN or an infinity (then alpha = NaN and every code, scale and mchoice
  * byte is 0), or -1 on a bad argument (null pointer, rows or cols <= 0, cols % 16 != 0, unknown
@@ -31,6 +33,13 @@ enum { NVFP4_REF_MAX = 0, NVFP4_REF_FOUR_OVER_SIX = 1, NVFP4_REF_CJSO = 2, NVFP4
 int nvfp4_ref_quantize(const void *W, int dtype, int64_t rows, int64_t cols, int mode, int iters,
                        uint8_t *codes, uint8_t *scales, float *alpha, uint8_t *mchoice, double *dstar,
                        float *alpha_trace);
+
+/* Same, with CJSO/SOAR started from `init` (NVFP4_REF_INIT_*; modes 0 and 1 accept only INIT_MAX). With
+ * INIT_4O6 the first scales are FourOverSix's (alpha from the max rule); mchoice is written only in
+ * mode 1. */
+int nvfp4_ref_quantize_ex(const void *W, int dtype, int64_t rows, int64_t cols, int mode, int iters, int init,
+                          uint8_t *codes, uint8_t *scales, float *alpha, uint8_t *mchoice, double *dstar,
+                          float *alpha_trace);
 
 /* Decoupled-scale search on selected blocks, given the CJSO state of the whole matrix (alpha, the
  * E4M3 block scales dcode[] and the pre-rounding scales dstar[], one per block of the matrix).

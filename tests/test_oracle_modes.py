@@ -304,3 +304,80 @@ def test_tiny_magnitude_matrix_is_consistent():
 def test_bad_arguments():
     with pytest.raises(ValueError):
         oracle.quantize(np.zeros((4, 24), np.float32), "max")
+
+
+# ------------------------------------------------------------------- CJSO / SOAR from FourOverSix
+
+@pytest.mark.parametrize("gen", [lambda: synth.c1(0)[:64], lambda: synth.c2(0, 64, 512),
+                                 lambda: indep.on_grid_matrix(16, 128, -6, 2)[0]])
+def test_init_4o6_zero_rounds_equals_4o6(gen):
+    """With no rounds, CJSO started from FourOverSix is FourOverSix (codes, scales, alpha)."""
+    W = gen()
+    r4 = oracle.quantize(W, "4o6")
+    rc = oracle.quantize(W, "cjso", 0, init="4o6")
+    assert rc["alpha"] == r4["alpha"]
+    assert np.array_equal(rc["codes"], r4["codes"]) and np.array_equal(rc["scales"], r4["scales"])
+
+
+def test_init_4o6_unrounded_scales():
+    """The unrounded starting scale (what the search brackets at T = 0) is max|w|/(6 alpha) where
+    FourOverSix kept M=6 and 1.5 * Delta6 where it took M=4 (Delta6 = the max rule's scale)."""
+    W = synth.c2(0, 64, 512)
+    rm = oracle.quantize(W, "max")
+    r4 = oracle.quantize(W, "4o6")
+    rc = oracle.quantize(W, "cjso", 0, init="4o6")
+    alpha = rm["alpha"]
+    w = indep.as_f32(W).reshape(-1, 16).astype(np.float64)
+    amax = np.abs(w).max(axis=1)
+    d6 = indep.E4M3_POS[rm["scales"].reshape(-1)]
+    m4 = r4["mchoice"].reshape(-1).astype(bool)
+    want = np.where(m4, 1.5 * d6, amax / (6.0 * float(np.float32(alpha))))
+    assert m4.any() and (~m4).any()
+    assert np.array_equal(rc["dstar"].reshape(-1)[m4], want[m4])
+    assert np.allclose(rc["dstar"].reshape(-1)[~m4], want[~m4], rtol=1e-15, atol=0)
+
+
+def test_soar_from_4o6_never_worse_and_matches_rescoring():
+    """SOAR from FourOverSix: per block no worse than its CJSO point, and its choice equals an
+    independent scoring of the 202 candidates plus the incumbent."""
+    W = synth.normal_bf16(16, 256, seed=21)
+    rc = oracle.quantize(W, "cjso", 3, init="4o6")
+    rs = oracle.quantize(W, "soar", 3, init="4o6")
+    assert rs["alpha"] == rc["alpha"]
+    ec = indep.block_errors(W, rc["codes"], rc["scales"], rc["alpha"])
+    es = indep.block_errors(W, rs["codes"], rs["scales"], rs["alpha"])
+    assert np.all(es <= ec * (1 + 1e-12))
+    alpha = rc["alpha"]
+    w = indep.as_f32(W).reshape(-1, 16)
+    fk = [indep.nearest_f32(Fraction(50 + k, 100)) for k in range(101)]
+    dc_all, ds_all = rc["scales"].reshape(-1), rc["dstar"].reshape(-1)
+    got_codes, got_scales = indep.unpack(rs["codes"]).reshape(-1, 16), rs["scales"].reshape(-1)
+    ambiguous = 0
+    for b in range(0, w.shape[0], 7):
+        dcv = indep.E4M3_POS[dc_all[b]]
+        lo = min(int(np.searchsorted(indep.E4M3_POS, ds_all[b], side="right") - 1), 0x7E)
+        hi = lo if (indep.E4M3_POS[lo] == ds_all[b] or lo == 0x7E) else lo + 1
+        best_c = indep.quantize_block_np(w[b], alpha, dcv)
+        best_e, best_s = indep.block_err_np(w[b], best_c, alpha, dcv), dc_all[b]
+        errs = [best_e]
+        for k in range(101):
+            c = indep.quantize_block_np(w[b], alpha, np.float32(np.float32(dcv) * fk[k]))
+            for d in (lo, hi):
+                e = indep.block_err_np(w[b], c, alpha, indep.E4M3_POS[d])
+                errs.append(e)
+                if e < best_e:
+                    best_c, best_e, best_s = c, e, d
+        errs = np.array(errs)
+        # binary64 scoring cannot order errors closer than its rounding: such blocks are skipped
+        if np.sum(np.abs(errs - best_e) <= 1e-12 * best_e) > np.sum(errs == best_e):
+            ambiguous += 1
+            continue
+        assert got_scales[b] == best_s and np.array_equal(got_codes[b], best_c), b
+    assert ambiguous < 3
+
+
+def test_init_4o6_rejected_for_max_and_4o6():
+    W = synth.c1(0)[:4]
+    for mode in ("max", "4o6"):
+        with pytest.raises(ValueError):
+            oracle.quantize(W, mode, 0, init="4o6")
