@@ -122,6 +122,11 @@ typedef struct nvfp4_args {
  * unimodal in the quantise scale around that window (the kernel source gives the argument), so the
  * outputs are identical either way. The flag exists to check that and to time the full search. */
 #define NVFP4_FLAG_FULL_SEARCH 1u
+/* CJSO and SOAR: start from FourOverSix's block scales (each block's M=6 or M=4 choice, FourOverSix
+ * write-up, section 02) instead of the max rule; alpha still starts from the max rule. For SOAR with no
+ * rounds, the unrounded scale whose E4M3 neighbours the search tries is max|w|/(6 alpha), or 1.5*Delta6
+ * for a block that took M=4. Not accepted for modes 0 and 1. */
+#define NVFP4_FLAG_INIT_4O6 2u
 
 int nvfp4_quantize_ex(const nvfp4_args_t *args);
 

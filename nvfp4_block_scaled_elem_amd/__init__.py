@@ -22,6 +22,8 @@ LIB_PATH = os.environ.get("NVFP4_LIB", os.path.join(HERE, "libnvfp4.so"))
 MODES = {"max": 0, "4o6": 1, "cjso": 2, "soar": 3}
 DTYPES = {torch.bfloat16: 0, torch.float32: 1}
 FLAG_FULL_SEARCH = 1  # NVFP4_FLAG_FULL_SEARCH
+FLAG_INIT_4O6 = 2  # NVFP4_FLAG_INIT_4O6
+INITS = {"max": 0, "4o6": FLAG_INIT_4O6}
 STATUS_NONFINITE = 1
 
 
@@ -97,13 +99,15 @@ def _stream_ptr(stream, device) -> int:
 
 
 def quantize(W: torch.Tensor, mode: str, iters: int = 0, *, codes=None, scales=None, alpha=None,
-             mchoice=None, stats=None, workspace=None, stream=None, stage_events=None, full_search=False):
+             mchoice=None, stats=None, workspace=None, stream=None, stage_events=None, full_search=False,
+             init="max"):
     """Quantise ``W`` ([rows, cols] bf16/fp32 CUDA tensor). Returns (codes [rows, cols//2] uint8,
     scales [rows, cols//16] uint8 E4M3 bits, alpha [1] float32), all on W's device. Optional
     preallocated outputs, an ``mchoice`` uint8 [rows, cols//16] tensor (FourOverSix), a ``stats``
     int32 [4] tensor, a uint8 ``workspace`` tensor, a ``stream`` and a list of
     ``torch.cuda.Event(enable_timing=True)`` stage events (None entries are skipped) may be passed. ``full_search`` makes the
-    SOAR search visit all 202 candidates of every block (same outputs; NVFP4_FLAG_FULL_SEARCH)."""
+    SOAR search visit all 202 candidates of every block (same outputs; NVFP4_FLAG_FULL_SEARCH); ``init``
+    is CJSO's starting point, "max" or "4o6" (NVFP4_FLAG_INIT_4O6; modes cjso and soar)."""
     if W.dim() != 2 or not W.is_cuda or not W.is_contiguous() or W.dtype not in DTYPES:
         raise NVFP4Error("W must be a contiguous 2-D bf16 or fp32 CUDA tensor")
     rows, cols = W.shape
@@ -134,7 +138,9 @@ def quantize(W: torch.Tensor, mode: str, iters: int = 0, *, codes=None, scales=N
     a.workspace = workspace.data_ptr() if workspace is not None else None
     a.workspace_bytes = workspace.numel() if workspace is not None else 0
     a.stream = _stream_ptr(stream, dev)
-    a.flags = FLAG_FULL_SEARCH if full_search else 0
+    if init not in INITS:
+        raise NVFP4Error(f"unknown init {init!r}")
+    a.flags = (FLAG_FULL_SEARCH if full_search else 0) | INITS[init]
     ev_arr = None
     if stage_events is not None:
         for e in stage_events:  # torch creates the HIP event at its first record

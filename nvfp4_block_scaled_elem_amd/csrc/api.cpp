@@ -41,7 +41,9 @@ int check(const nvfp4_args_t *a) {
     if (a->workspace && ((uintptr_t)a->workspace & 255u) != 0) return NVFP4_ERR_INVALID_ARG;
     if (a->stats_out && ((uintptr_t)a->stats_out & 3u) != 0) return NVFP4_ERR_INVALID_ARG;
     if (a->stage_events && a->n_stage_events < kernel_count(a->mode, a->iters) + 1) return NVFP4_ERR_INVALID_ARG;
-    if (a->flags & ~NVFP4_FLAG_FULL_SEARCH) return NVFP4_ERR_INVALID_ARG;
+    if (a->flags & ~(NVFP4_FLAG_FULL_SEARCH | NVFP4_FLAG_INIT_4O6)) return NVFP4_ERR_INVALID_ARG;
+    if ((a->flags & NVFP4_FLAG_INIT_4O6) && a->mode != NVFP4_MODE_CJSO && a->mode != NVFP4_MODE_SOAR)
+        return NVFP4_ERR_INVALID_ARG;
     return NVFP4_OK;
 }
 
@@ -73,8 +75,9 @@ int run(const nvfp4_args_t *a, void *ws_base) {
     }
     const bool soar = a->mode == NVFP4_MODE_SOAR;
     const int gc = cjso_groups(nblk);
-    if (launch_cjso_init(a->W, f32, soar, nblk, ws.amax_part, ga, a->iters, a->codes_out, a->scales_out, a->alpha_out,
-                         ws, gc, a->stats_out, st) != hipSuccess ||
+    const bool fos_init = (a->flags & NVFP4_FLAG_INIT_4O6) != 0;
+    if (launch_cjso_init(a->W, f32, soar, fos_init, nblk, ws.amax_part, ga, a->iters, a->codes_out, a->scales_out,
+                         a->alpha_out, ws, gc, a->stats_out, st) != hipSuccess ||
         !mark(a, j++))
         return NVFP4_ERR_HIP;
     for (int t = 1; t <= a->iters; ++t)

@@ -64,9 +64,9 @@ hipError_t launch_amax(const void *W, bool f32, int64_t n, uint32_t *amax_part, 
 hipError_t launch_quant(const void *W, bool f32, bool four_over_six, int64_t nblk, const uint32_t *amax_part,
                         int amax_n, uint8_t *codes, uint8_t *scales, float *alpha_out, uint8_t *mchoice,
                         nvfp4_stats_t *stats, uint32_t *m4_part, hipStream_t stream);
-hipError_t launch_cjso_init(const void *W, bool f32, bool soar, int64_t nblk, const uint32_t *amax_part, int amax_n,
-                            int iters, uint8_t *codes, uint8_t *scales, float *alpha_out, const Workspace &ws,
-                            int groups, nvfp4_stats_t *stats, hipStream_t stream);
+hipError_t launch_cjso_init(const void *W, bool f32, bool soar, bool fos, int64_t nblk, const uint32_t *amax_part,
+                            int amax_n, int iters, uint8_t *codes, uint8_t *scales, float *alpha_out,
+                            const Workspace &ws, int groups, nvfp4_stats_t *stats, hipStream_t stream);
 hipError_t launch_cjso_iter(const void *W, bool f32, bool soar, int64_t nblk, int t, int iters, uint8_t *codes,
                             uint8_t *scales, float *alpha_out, const Workspace &ws, int groups, hipStream_t stream);
 hipError_t launch_soar(const void *W, bool f32, int64_t nblk, const float *alpha, uint8_t *codes, uint8_t *scales,

@@ -283,6 +283,35 @@ __global__ __launch_bounds__(kAmaxThreads) void k_amax(const uint4 *__restrict__
 
 // ------------------------------------------------------------------------- MAX and FourOverSix
 
+// FourOverSix write-up, section 02, for one block under alpha: scale_m4 = fp8(scale_m6 * 1.5); M=4 is
+// kept iff its squared error is strictly smaller. With S_wq, S_qq exact and s_d = alpha*Delta exact in
+// binary64, the error minus sum w^2 is s_d*(s_d*S_qq - 2*S_wq): the inner term is exact in binary64 and
+// the product is held exactly as a double-double. In: d6 (the max-rule scale). Out: the chosen scale d,
+// its codes and sums; returns whether M=4 was taken.
+template <bool F32>
+__device__ __forceinline__ bool fos_choice(const Blk<F32> &B, float a, const ScaleTab &T, float alpha, uint32_t d6,
+                                           uint32_t &d, uint32_t &c0, uint32_t &c1, double &sw, double &sq) {
+    const float v6 = e4m3_value(d6);
+    double w6, q6, w4, q4;
+    uint32_t e0, e1;
+    quant_sums_r(B, a, T.s[d6], T.r[d6], c0, c1, w6, q6);
+    const uint32_t d4 = e4m3_rne(1.5 * (double)v6);
+    const float v4 = e4m3_value(d4);
+    quant_sums_r(B, a, T.s[d4], T.r[d4], e0, e1, w4, q4);
+    const double sd6 = (double)alpha * (double)v6, sd4 = (double)alpha * (double)v4;
+    const dd j6 = two_prod(sd6, fma(sd6, q6, -2.0 * w6));
+    const dd j4 = two_prod(sd4, fma(sd4, q4, -2.0 * w4));
+    const bool m4 = dd_less(j4, j6);
+    d = m4 ? d4 : d6;
+    sw = m4 ? w4 : w6;
+    sq = m4 ? q4 : q6;
+    if (m4) {
+        c0 = e0;
+        c1 = e1;
+    }
+    return m4;
+}
+
 template <bool F32, bool FOS>
 __global__ __launch_bounds__(kQuantThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_quant(const void *__restrict__ W, int64_t nblk,
                                                           const uint32_t *__restrict__ amax_part, int amax_n,
@@ -321,25 +350,8 @@ __global__ __launch_bounds__(kQuantThreads) __attribute__((amdgpu_waves_per_eu(4
                 else
                     encode16_soft(B.w, r, c0, c1);
             } else {
-                // FourOverSix write-up, section 02: scale_m4 = fp8(scale_m6 * 1.5); keep M=4 iff its squared
-                // error is strictly smaller. With S_wq, S_qq exact and s_d = alpha*Delta exact in binary64,
-                // the error minus sum w^2 is s_d*(s_d*S_qq - 2*S_wq): the inner term is exact in binary64
-                // and the product is held exactly as a double-double.
-                double w6, q6, w4, q4;
-                uint32_t e0, e1;
-                quant_sums_r(B, a, T.s[d6], T.r[d6], c0, c1, w6, q6);
-                const uint32_t d4 = e4m3_rne(1.5 * (double)v6);
-                const float v4 = e4m3_value(d4);
-                quant_sums_r(B, a, T.s[d4], T.r[d4], e0, e1, w4, q4);
-                const double sd6 = (double)alpha * (double)v6, sd4 = (double)alpha * (double)v4;
-                const dd j6 = two_prod(sd6, fma(sd6, q6, -2.0 * w6));
-                const dd j4 = two_prod(sd4, fma(sd4, q4, -2.0 * w4));
-                m4 = dd_less(j4, j6);
-                if (m4) {
-                    c0 = e0;
-                    c1 = e1;
-                    sc = d4;
-                }
+                double sw, sq;
+                m4 = fos_choice(B, a, T, alpha, d6, sc, c0, c1, sw, sq);
                 if (mchoice) mchoice[b] = m4 ? 1 : 0;
                 m4count += m4 ? 1u : 0u;
             }
@@ -384,9 +396,11 @@ __global__ __launch_bounds__(kCountThreads) void k_count(const uint32_t *__restr
 
 // ----------------------------------------------------------------------------------------- CJSO
 
-// Max rule plus, when rounds follow (ROUNDS), the least-squares sums of the first alpha-step; without
-// rounds the max-rule codes (and for SOAR the E4M3 bracket of the unrounded block scale) are final.
-template <bool F32, bool SOAR, bool ROUNDS>
+// Max rule (or, with FOS, FourOverSix's choice of block scale under the max-rule alpha) plus, when rounds
+// follow (ROUNDS), the least-squares sums of the first alpha-step; without rounds these codes (and for
+// SOAR the E4M3 bracket of the unrounded block scale: max|w|/(6 alpha), or 1.5*Delta6 where FourOverSix
+// took M=4) are final.
+template <bool F32, bool SOAR, bool ROUNDS, bool FOS>
 __global__ __launch_bounds__(kCjsoThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_cjso_init(const void *__restrict__ W, int64_t nblk,
                                                               const uint32_t *__restrict__ amax_part, int amax_n,
                                                               uint8_t *__restrict__ codes,
@@ -418,25 +432,32 @@ __global__ __launch_bounds__(kCjsoThreads) __attribute__((amdgpu_waves_per_eu(4)
                                            [&](int64_t b, const Blk<F32> &B, uint32_t) {
         const float a = B.amax();
         const double q = max_rule_quotient(a, alpha);
-        const uint32_t d = e4m3_rne(q);
+        uint32_t d = e4m3_rne(q);
+        double dstar = q;
+        uint32_t c0, c1;
+        double sw, sq;
+        if constexpr (FOS) {
+            const uint32_t d6 = d;
+            if (fos_choice(B, a, T, alpha, d6, d, c0, c1, sw, sq)) dstar = 1.5 * (double)e4m3_value(d6);
+        }
         const float v = e4m3_value(d);
         scales[b] = (uint8_t)d;
-        uint32_t c0, c1;
         if constexpr (!ROUNDS) {
-            const float r = T.r[d];
-            if (finite_pos(r))
-                encode16(B.w, r, c0, c1);
-            else
-                encode16_soft(B.w, r, c0, c1);
+            if constexpr (!FOS) {
+                const float r = T.r[d];
+                if (finite_pos(r))
+                    encode16(B.w, r, c0, c1);
+                else
+                    encode16_soft(B.w, r, c0, c1);
+            }
             store_codes(codes, b, c0, c1);
             if (SOAR) {
                 uint32_t lo, hi;
-                e4m3_bracket(q, lo, hi);
+                e4m3_bracket(dstar, lo, hi);
                 brackets[b] = (uint16_t)(lo | (hi << 8));
             }
         } else {
-            double sw, sq;
-            quant_sums_r(B, a, T.s[d], T.r[d], c0, c1, sw, sq);
+            if constexpr (!FOS) quant_sums_r(B, a, T.s[d], T.r[d], c0, c1, sw, sq);
             const dd t = two_prod((double)v, sw);
             acc2(N, t.hi, t.lo);
             acc2(D, (double)v * (double)v * sq, 0.0);
@@ -768,17 +789,21 @@ hipError_t launch_quant(const void *W, bool f32, bool fos, int64_t nblk, const u
     return hipGetLastError();
 }
 
-hipError_t launch_cjso_init(const void *W, bool f32, bool soar, int64_t nblk, const uint32_t *amax_part, int amax_n,
-                            int iters, uint8_t *codes, uint8_t *scales, float *alpha_out, const Workspace &ws,
-                            int groups, nvfp4_stats_t *stats, hipStream_t stream) {
+hipError_t launch_cjso_init(const void *W, bool f32, bool soar, bool fos, int64_t nblk, const uint32_t *amax_part,
+                            int amax_n, int iters, uint8_t *codes, uint8_t *scales, float *alpha_out,
+                            const Workspace &ws, int groups, nvfp4_stats_t *stats, hipStream_t stream) {
     const dim3 grid(groups), block(kCjsoThreads);
     double *part = ws.cjso_part;  // round 0 writes buffer 0
-#define NVFP4_INIT(F, S, R)                                                                                       \
-    hipLaunchKernelGGL((k_cjso_init<F, S, R>), grid, block, 0, stream, W, nblk, amax_part, amax_n, codes, scales,    \
+#define NVFP4_INIT(F, S, R, O)                                                                                    \
+    hipLaunchKernelGGL((k_cjso_init<F, S, R, O>), grid, block, 0, stream, W, nblk, amax_part, amax_n, codes, scales, \
                        alpha_out, ws.alpha_state, part, ws.brackets, stats)
+#define NVFP4_INIT_O(F, S, R)                                                                                     \
+    do {                                                                                                          \
+        if (fos) NVFP4_INIT(F, S, R, true); else NVFP4_INIT(F, S, R, false);                                      \
+    } while (0)
 #define NVFP4_INIT_R(F, S)                                                                                        \
     do {                                                                                                          \
-        if (iters > 0) NVFP4_INIT(F, S, true); else NVFP4_INIT(F, S, false);                                      \
+        if (iters > 0) NVFP4_INIT_O(F, S, true); else NVFP4_INIT_O(F, S, false);                                  \
     } while (0)
     if (f32) {
         if (soar) NVFP4_INIT_R(true, true); else NVFP4_INIT_R(true, false);
@@ -786,6 +811,7 @@ hipError_t launch_cjso_init(const void *W, bool f32, bool soar, int64_t nblk, co
         if (soar) NVFP4_INIT_R(false, true); else NVFP4_INIT_R(false, false);
     }
 #undef NVFP4_INIT_R
+#undef NVFP4_INIT_O
 #undef NVFP4_INIT
     return hipGetLastError();
 }

@@ -55,7 +55,8 @@ def args(**kw):
     (dict(workspace=FAKE + 64, workspace_bytes=1 << 30), INVALID),
     (dict(workspace=FAKE, workspace_bytes=16), WORKSPACE),
     (dict(mode=3, iters=8, workspace=FAKE, workspace_bytes=1024), WORKSPACE),
-    (dict(flags=2), INVALID), (dict(flags=0x80000000), INVALID),
+    (dict(flags=4), INVALID), (dict(flags=0x80000000), INVALID), (dict(flags=2, mode=0), INVALID),
+    (dict(flags=2, mode=1), INVALID),
 ])
 def test_quantize_ex_rejects(L, kw, err):
     a = args(**kw)

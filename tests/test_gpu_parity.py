@@ -46,13 +46,15 @@ def to_dev(W: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(W).cuda()
 
 
-def run(W: np.ndarray, mode: str, iters: int = 0, dev_W=None, full_search=False):
-    say(f"gpu quantize mode={mode} iters={iters} shape={W.shape} dtype={W.dtype} full_search={full_search}")
+def run(W: np.ndarray, mode: str, iters: int = 0, dev_W=None, full_search=False, init="max"):
+    say(f"gpu quantize mode={mode} iters={iters} shape={W.shape} dtype={W.dtype} full_search={full_search} "
+        f"init={init}")
     Wd = to_dev(W) if dev_W is None else dev_W
     rows, cols = W.shape
     mch = torch.zeros((rows, cols // 16), dtype=torch.uint8, device="cuda") if mode == "4o6" else None
     stats = torch.zeros(4, dtype=torch.int32, device="cuda")
-    codes, scales, alpha = nv.quantize(Wd, mode, iters, mchoice=mch, stats=stats, full_search=full_search)
+    codes, scales, alpha = nv.quantize(Wd, mode, iters, mchoice=mch, stats=stats, full_search=full_search,
+                                       init=init)
     torch.cuda.synchronize()
     out = {"codes": codes.cpu().numpy(), "scales": scales.cpu().numpy(), "alpha": float(alpha.cpu()[0]),
            "stats": stats.cpu().numpy()}
@@ -377,6 +379,35 @@ def test_soar_window_equals_full_search(name, iters):
 def test_soar_tie_prone_inputs_match_oracle(gen, seed):
     W = gen(seed)
     compare_live(W, "soar", 8)
+
+
+# ------------------------------------------------------------------- CJSO / SOAR from FourOverSix
+
+INIT_CASES = {
+    "c1_fp32": lambda: synth.c1(0),
+    "ragged_3x48": lambda: synth.normal_bf16(3, 48, 5),
+    "c2_rows": lambda: synth.c2(0, 128, 1024),
+    "c3_rows": lambda: synth.c3(0, 0)[:64],
+    "on_grid": lambda: indep.on_grid_matrix(32, 256, -10, 7)[0],
+}
+
+
+@pytest.mark.parametrize("mode,iters", [("cjso", 0), ("cjso", 3), ("cjso", 8), ("soar", 0), ("soar", 8)])
+@pytest.mark.parametrize("name", list(INIT_CASES))
+def test_init_4o6_matches_oracle(name, mode, iters):
+    W = INIT_CASES[name]()
+    g = run(W, mode, iters, init="4o6")
+    r = oracle.quantize(W, mode, iters, init="4o6")
+    assert_tolerance(W, g, r)
+    assert_exact(g, r, mode)
+
+
+def test_init_4o6_zero_rounds_is_4o6():
+    W = synth.c2(0, 256, 1024)
+    a = run(W, "cjso", 0, init="4o6")
+    b = run(W, "4o6", 0)
+    assert np.array_equal(a["codes"], b["codes"]) and np.array_equal(a["scales"], b["scales"])
+    assert f32_bits(a["alpha"]) == f32_bits(b["alpha"])
 
 
 # ------------------------------------------------------------------------------ error statistics
