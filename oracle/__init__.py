@@ -47,6 +47,8 @@ def lib():
         L.nvfp4_ref_quantize.restype = i32
         L.nvfp4_ref_quantize_ex.argtypes = [vp, i32, i64, i64, i32, i32, i32, u8p, u8p, vp, u8p, vp, vp]
         L.nvfp4_ref_quantize_ex.restype = i32
+        L.nvfp4_ref_matmul.argtypes = [vp, i32, i64, i64, u8p, u8p, ctypes.c_float, i64, vp]
+        L.nvfp4_ref_matmul.restype = i32
         L.nvfp4_ref_soar_blocks.argtypes = [vp, i32, i64, i64, ctypes.c_float, u8p, vp, vp, i64, u8p, u8p]
         L.nvfp4_ref_soar_blocks.restype = i32
         L.nvfp4_ref_mse.argtypes = [vp, i32, i64, i64, u8p, u8p, ctypes.c_float]
@@ -141,6 +143,22 @@ def soar_blocks(W: np.ndarray, alpha: float, dcode: np.ndarray, dstar: np.ndarra
     if st < 0:
         raise ValueError("oracle rejected the arguments")
     return codes, scales
+
+
+def matmul(X: np.ndarray, codes: np.ndarray, scales: np.ndarray, alpha: float, N: int) -> np.ndarray:
+    """Y = X @ What.T for an NVFP4 [N][K] weight matrix (codes [N][K/2], scales [N][K/16], alpha):
+    exact products summed in binary128, returned as float64 [M][N]."""
+    X = np.ascontiguousarray(X)
+    M, K = X.shape
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scales = np.ascontiguousarray(scales, np.uint8)
+    if K % 16 != 0 or codes.size != N * K // 2 or scales.size != N * K // 16:
+        raise ValueError("codes and scales do not describe an [N][K] NVFP4 matrix")
+    Y = np.zeros((M, N), np.float64)
+    st = lib().nvfp4_ref_matmul(_ptr(X), _dtype_code(X), M, K, _ptr(codes), _ptr(scales), alpha, N, _ptr(Y))
+    if st < 0:
+        raise ValueError("oracle rejected the arguments")
+    return Y
 
 
 def mse(W: np.ndarray, codes: np.ndarray, scales: np.ndarray, alpha: float) -> float:

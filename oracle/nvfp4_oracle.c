@@ -475,6 +475,33 @@ void nvfp4_ref_dequantize(const uint8_t *codes, const uint8_t *scales, float alp
     }
 }
 
+/* Y[m][n] = sum_k X[m][k] * What[n][k] with What = e2m1(code) * e4m3(scale) * alpha, the reconstruction
+ * the SOAR page defines (dequantisation equation), applied to a weight matrix [N][K] stored as the
+ * quantiser writes it: the product a W4A16 matrix multiply computes. Each product is exact in
+ * binary128 (X has at most 24 significant bits, the weight 2 + 4 + 24) and the sum over k is taken in
+ * binary128 in k order; Y is that sum rounded to binary64. X is [M][K] bf16 or fp32. */
+int nvfp4_ref_matmul(const void *X, int x_dtype, int64_t M, int64_t K, const uint8_t *codes,
+                     const uint8_t *scales, float alpha, int64_t N, double *Y) {
+    int64_t m, n, k;
+    float *x;
+    if (!X || !codes || !scales || !Y || bad_shape(M, K, x_dtype) || N <= 0) return -1;
+    x = widen(X, x_dtype, M * K);
+    if (!x) return -2;
+    for (m = 0; m < M; ++m)
+        for (n = 0; n < N; ++n) {
+            quad acc = 0;
+            for (k = 0; k < K; ++k) {
+                int64_t i = n * K + k;
+                unsigned c = (codes[i / 2] >> (4 * (i & 1))) & 15u;
+                quad wv = (quad)nvfp4_ref_e2m1_value(c) * (quad)nvfp4_ref_e4m3_value(scales[i / 16]) * (quad)alpha;
+                acc += (quad)x[m * K + k] * wv;
+            }
+            Y[m * N + n] = (double)acc;
+        }
+    free(x);
+    return 0;
+}
+
 double nvfp4_ref_mse(const void *W, int dtype, int64_t rows, int64_t cols, const uint8_t *codes,
                      const uint8_t *scales, float alpha) {
     int64_t n = rows * cols, nblk = n / 16, i;

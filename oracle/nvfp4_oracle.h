@@ -49,6 +49,12 @@ int nvfp4_ref_soar_blocks(const void *W, int dtype, int64_t rows, int64_t cols, 
                           uint8_t *codes_sel, uint8_t *scales_sel);
 
 /* Mean squared reconstruction error sum((w - e2m1(code)*e4m3(scale)*alpha)^2)/n of an output triple. */
+/* W4A16 product Y = X * What^T (What = dequantised [N][K] weights), exact products summed in binary128,
+ * rounded to binary64. X is [M][K] (x_dtype), codes/scales/alpha as written by the quantiser for the
+ * [N][K] matrix, Y is [M][N]. */
+int nvfp4_ref_matmul(const void *X, int x_dtype, int64_t M, int64_t K, const uint8_t *codes,
+                     const uint8_t *scales, float alpha, int64_t N, double *Y);
+
 double nvfp4_ref_mse(const void *W, int dtype, int64_t rows, int64_t cols, const uint8_t *codes,
                      const uint8_t *scales, float alpha);
 
