@@ -21,6 +21,9 @@ read the block, its scale and its two-byte scale bracket; write codes and scale)
 NVFP4_FLAG_FULL_SEARCH (all 202 candidates) against the FP32 vector peak: per block 101 quantise
 scales x 16 elements x 9 FLOPs.
 
+w4a16: the W4A16 product the format is for, Y = X @ What.T with the quantised 4096 x 4096 weights, at
+M = 1 (GB/s against HBM peak) and M = 4096 (TFLOP/s against the 2.5 PFLOP/s bf16 MFMA peak).
+
 c5_whole_model: the 224 matrices of a 7B-shaped model (32 layers; 12.95 GB bf16) quantised one after
 another in each mode, total time and aggregate GB/s (skipped with --no-c5).
 
@@ -91,6 +94,40 @@ def cpu_baseline(W0: np.ndarray) -> dict:
     return {"value": round(len(MODES) * sample.nbytes / dt / 1e9, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"rows 0-255 of the first 4096x4096 matrix ({sample.size} elements), all four modes, "
                       f"one thread, {dt:.1f} s"}
+
+
+PEAK_BF16_MFMA = 2.5e15  # FLOP/s, MI355X dense bf16 matrix peak
+
+
+def w4a16_pass(torch, nv, dev, W):
+    """The consumer of the format: Y = X @ What.T with the 4096 x 4096 weights quantised (FourOverSix)
+    and bf16 activations, for M = 1 (one token: bound by reading 0.5625 B per weight) and M = 4096 (bf16
+    MFMA). Times are HIP-event averages over repeated calls on the current stream."""
+    codes, scales, alpha = nv.quantize(W, "4o6")
+    n, k = W.shape
+    out = {"weights": f"{n}x{k} NVFP4 (FourOverSix)", "cases": {}}
+    for m in (1, 4096):
+        X = (torch.randn((m, k), device=dev) * 0.5).to(torch.bfloat16)
+        for _ in range(3):
+            nv.matmul(X, codes, scales, alpha)
+        reps = 50 if m == 1 else 10
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            nv.matmul(X, codes, scales, alpha)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        wbytes = n * k // 2 + n * k // 16
+        moved = wbytes + m * k * 2 + m * n * 2
+        flops = 2.0 * m * n * k
+        out["cases"][f"M={m}"] = {
+            "ms": round(ms, 5), "GBps": round(moved / (ms * 1e-3) / 1e9, 1),
+            "frac_hbm_peak": round(moved / (ms * 1e-3) / PEAK_HBM, 4),
+            "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 2),
+            "frac_bf16_mfma_peak": round(flops / (ms * 1e-3) / PEAK_BF16_MFMA, 4)}
+        log(f"w4a16 M={m}: {ms * 1e3:.1f} us")
+    return out
 
 
 C5_SHAPES = {"q": (4096, 4096), "k": (4096, 4096), "v": (4096, 4096), "o": (4096, 4096),
@@ -345,6 +382,7 @@ def main():
                 "algorithmic_bytes_per_launch": int(nel * ROUND_BYTES_PER_ELEM),
                 "avg_launch_ms": round(t_round * 1e3, 5), "launches_per_step": 2 * (ITERS - 1)}
 
+    w4a16 = w4a16_pass(torch, nv, dev, mats[0])
     c5 = None if args.no_c5 else c5_pass(torch, nv, dev, streams)
 
     value = len(MODES) * ROWS * COLS * 2 / (ms_per_step * 1e-3) / 1e9
@@ -362,6 +400,7 @@ def main():
         "graph_replay_ms_per_step": round(graph_ms_per_step, 5),
         "roofline": roofline,
     }
+    line["w4a16"] = w4a16
     if c5 is not None:
         line["c5_whole_model"] = c5
     if not args.no_cpu_baseline:

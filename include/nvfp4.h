@@ -163,6 +163,17 @@ int nvfp4_error_stats(const void *W, int dtype, int64_t rows, int64_t cols, cons
                       const uint8_t *scales, const float *alpha, double *sse_out,
                       unsigned long long *hist_out, void *stream);
 
+/* W4A16 product with NVFP4 weights, the use the format exists for: Y[M][N] = X[M][K] * What[N][K]^T with
+ * What = e2m1(code) * e4m3(scale) * alpha (SOAR page, dequantisation equation), for a weight matrix [N][K]
+ * stored as the quantiser writes it (codes [N][K/2], scales [N][K/16], alpha one float). X is bf16
+ * [M][K] row-major; Y is [M][N] of y_dtype (NVFP4_DTYPE_BF16 or _F32). All pointers are device pointers;
+ * X, codes and Y 16-byte aligned, K % 16 == 0, M <= 8388480. Arithmetic: every q * Delta is a bf16 value,
+ * so the products with X are exact; the sum over k is accumulated in fp32 (bf16 MFMA for M > 4, packed
+ * bf16 dot products for M <= 4) in an order the caller does not control, then multiplied by alpha and
+ * rounded once to the output type. Enqueued on `stream`; argument errors are returned synchronously. */
+int nvfp4_matmul(const void *X, int64_t M, int64_t K, const uint8_t *codes, const uint8_t *scales,
+                 const float *alpha, int64_t N, void *Y, int y_dtype, void *stream);
+
 /* Text of an nvfp4_error value. */
 const char *nvfp4_status_string(int status);
 

@@ -55,6 +55,8 @@ def lib() -> ctypes.CDLL:
         i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
         L.nvfp4_error_stats.argtypes = [vp, i32, i64, i64, vp, vp, vp, vp, vp, vp]
         L.nvfp4_error_stats.restype = i32
+        L.nvfp4_matmul.argtypes = [vp, i64, i64, vp, vp, vp, i64, vp, i32, vp]
+        L.nvfp4_matmul.restype = i32
         L.nvfp4_quantize_ex.argtypes = [ctypes.POINTER(_Args)]
         L.nvfp4_quantize_ex.restype = i32
         L.nvfp4_quantize.argtypes = [vp, i64, i64, i32, i32, vp, vp, vp, vp]
@@ -192,3 +194,27 @@ def error_stats(W: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, alph
     _check(lib().nvfp4_error_stats(W.data_ptr(), DTYPES[W.dtype], rows, cols, codes.data_ptr(), scales.data_ptr(),
                                    alpha.data_ptr(), sse.data_ptr(), hist.data_ptr(), _stream_ptr(stream, dev)))
     return sse, hist
+
+
+def matmul(X: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, alpha: torch.Tensor,
+           out_dtype=torch.bfloat16, stream=None) -> torch.Tensor:
+    """W4A16 product Y = X @ What.T with NVFP4 weights (codes [N, K/2], scales [N, K/16], alpha [1] as
+    quantize returns them for an [N, K] matrix) and bf16 activations X [M, K]; Y is [M, N] bf16 or fp32."""
+    if X.dim() != 2 or not X.is_cuda or not X.is_contiguous() or X.dtype != torch.bfloat16:
+        raise NVFP4Error("X must be a contiguous 2-D bf16 CUDA tensor")
+    M, K = X.shape
+    dev = X.device
+    if codes.dim() != 2 or codes.shape[1] * 2 != K:
+        raise NVFP4Error("codes must be [N, K/2]")
+    N = codes.shape[0]
+    for t in (codes, scales, alpha):
+        if not t.is_cuda or t.device != dev or not t.is_contiguous():
+            raise NVFP4Error("codes, scales and alpha must be contiguous tensors on X's device")
+    if scales.numel() != N * K // 16 or alpha.numel() < 1:
+        raise NVFP4Error("scales or alpha do not match the weight shape")
+    if out_dtype not in DTYPES:
+        raise NVFP4Error("out_dtype must be bf16 or fp32")
+    Y = torch.empty((M, N), dtype=out_dtype, device=dev)
+    _check(lib().nvfp4_matmul(X.data_ptr(), M, K, codes.data_ptr(), scales.data_ptr(), alpha.data_ptr(), N,
+                              Y.data_ptr(), DTYPES[out_dtype], _stream_ptr(stream, dev)))
+    return Y

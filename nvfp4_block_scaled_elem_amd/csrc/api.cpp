@@ -190,6 +190,20 @@ NVFP4_API int nvfp4_error_stats(const void *W, int dtype, int64_t rows, int64_t 
     return ok ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 
+NVFP4_API int nvfp4_matmul(const void *X, int64_t M, int64_t K, const uint8_t *codes, const uint8_t *scales,
+                           const float *alpha, int64_t N, void *Y, int y_dtype, void *stream) {
+    if (!X || !codes || !scales || !alpha || !Y || M <= 0 || K <= 0 || N <= 0) return NVFP4_ERR_INVALID_ARG;
+    if (y_dtype != NVFP4_DTYPE_BF16 && y_dtype != NVFP4_DTYPE_F32) return NVFP4_ERR_INVALID_ARG;
+    if (K % 16 != 0 || M > 8388480 || N > kMaxElems / K || M > kMaxElems / K || M > kMaxElems / N) return NVFP4_ERR_SHAPE;
+    if (((uintptr_t)X & 15u) != 0 || ((uintptr_t)codes & 15u) != 0 || ((uintptr_t)Y & 15u) != 0 ||
+        ((uintptr_t)alpha & 3u) != 0)
+        return NVFP4_ERR_INVALID_ARG;
+    return nvfp4::launch_w4a16(static_cast<const uint16_t *>(X), M, K, codes, scales, alpha, N, Y,
+                               y_dtype == NVFP4_DTYPE_F32, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? NVFP4_OK
+               : NVFP4_ERR_HIP;
+}
+
 NVFP4_API const char *nvfp4_status_string(int status) {
     switch (status) {
         case NVFP4_OK: return "ok";

@@ -1,0 +1,105 @@
+"""GPU W4A16 product with NVFP4 weights against the oracle (nvfp4_ref_matmul: exact products summed in
+binary128). Identity and one-hot activations make every output a single exact product, so those cases
+must match exactly; general activations are held to the fp32 accumulation bound
+|y - y_exact| <= (K * 2^-23 + 2^-22) * alpha * sum_k |x * q * Delta| (+ 2^-8 |y| for bf16 output)."""
+import numpy as np
+import pytest
+import torch
+
+import nvfp4_block_scaled_elem_amd as nv
+import oracle
+import synth
+from tests import indep
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def bf16_dev(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def encoded_weights(n, k, seed, mode="4o6"):
+    W = synth.normal_bf16(n, k, seed)
+    codes, scales, alpha = nv.quantize(bf16_dev(W), mode, 2 if mode in ("cjso", "soar") else 0)
+    torch.cuda.synchronize()
+    return codes, scales, alpha
+
+
+def check(X, codes, scales, alpha, out_dtype):
+    M, K = X.shape
+    N = codes.shape[0]
+    say(f"w4a16 M={M} N={N} K={K} out={out_dtype}")
+    Y = nv.matmul(bf16_dev(X), codes, scales, alpha, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    c, s, a = codes.cpu().numpy(), scales.cpu().numpy(), float(alpha.cpu()[0])
+    ref = oracle.matmul(X, c, s, a, N)
+    got = Y.float().cpu().numpy().astype(np.float64)
+    x = indep.as_f32(X).astype(np.float64)
+    wh = np.abs(oracle.dequantize(c, s, a, N, K))
+    mag = np.abs(x) @ wh.T
+    bound = (K * 2.0 ** -23 + 2.0 ** -22) * mag
+    if out_dtype == torch.bfloat16:
+        bound = bound + 2.0 ** -8 * np.abs(ref) + 1e-38
+    err = np.abs(got - ref)
+    assert np.all(err <= bound), f"max excess {(err - bound).max()}"
+    return got, ref
+
+
+SHAPES = [(1, 256, 1024), (2, 96, 160), (3, 64, 272), (4, 130, 64),   # GEMV path (M <= 4)
+          (5, 200, 272), (64, 128, 512), (130, 260, 528), (128, 256, 1024)]  # MFMA path
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("m,n,k", SHAPES)
+def test_w4a16_matches_oracle(m, n, k, out_dtype):
+    codes, scales, alpha = encoded_weights(n, k, seed=m + n + k)
+    X = synth.normal_bf16(m, k, seed=3 * m + 1, std=1.0)
+    check(X, codes, scales, alpha, out_dtype)
+
+
+@pytest.mark.parametrize("k", [64, 160, 512])
+@pytest.mark.parametrize("n", [32, 200])
+def test_w4a16_identity_is_exact(n, k):
+    """X = I (M = K > 4: the MFMA path) and its first rows (M <= 4: the GEMV path): one product per
+    output, so the fp32 results equal the oracle's exactly."""
+    codes, scales, alpha = encoded_weights(n, k, seed=n * k, mode="soar")
+    eye = (np.eye(k, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    for X in (eye, eye[:3] if k > 3 else eye):
+        got, ref = check(X, codes, scales, alpha, torch.float32)
+        assert np.array_equal(got, ref.astype(np.float32).astype(np.float64))
+
+
+def test_w4a16_one_hot_rows_are_exact():
+    n, k = 96, 256
+    codes, scales, alpha = encoded_weights(n, k, seed=9)
+    X = np.zeros((8, k), np.float32)
+    for i in range(8):
+        X[i, (37 * i + 5) % k] = (-1.0) ** i * (1.0 + i / 8.0)
+    Xb = (X.view(np.uint32) >> 16).astype(np.uint16)
+    for rows in (Xb[:2], Xb):
+        got, ref = check(rows, codes, scales, alpha, torch.float32)
+        assert np.array_equal(got, ref.astype(np.float32).astype(np.float64))
+
+
+def test_w4a16_full_size_sample():
+    """4096 x 4096 weights with M = 1 and M = 64: sampled outputs against the oracle."""
+    n = k = 4096
+    W = synth.c2(0)
+    codes, scales, alpha = nv.quantize(bf16_dev(W), "4o6")
+    c, s, a = codes.cpu().numpy(), scales.cpu().numpy(), float(alpha.cpu()[0])
+    rows = np.arange(0, n, 61)
+    for m in (1, 64):
+        X = synth.normal_bf16(m, k, seed=m, std=1.0)
+        say(f"w4a16 full size M={m}")
+        Y = nv.matmul(bf16_dev(X), codes, scales, alpha, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        got = Y.cpu().numpy().astype(np.float64)[:, rows]
+        ref = oracle.matmul(X, c.reshape(n, k // 2)[rows], s.reshape(n, k // 16)[rows], a, rows.size)
+        x = indep.as_f32(X).astype(np.float64)
+        wh = np.abs(oracle.dequantize(c.reshape(n, k // 2)[rows], s.reshape(n, k // 16)[rows], a, rows.size, k))
+        bound = (k * 2.0 ** -23 + 2.0 ** -22) * (np.abs(x) @ wh.T)
+        assert np.all(np.abs(got - ref) <= bound)
