@@ -102,19 +102,26 @@ PEAK_BF16_MFMA = 2.5e15  # FLOP/s, MI355X dense bf16 matrix peak
 def w4a16_pass(torch, nv, dev, W):
     """The consumer of the format: Y = X @ What.T with the 4096 x 4096 weights quantised (FourOverSix)
     and bf16 activations, for M = 1 (one token: bound by reading 0.5625 B per weight) and M = 4096 (bf16
-    MFMA). Times are HIP-event averages over repeated calls on the current stream."""
+    MFMA). Times are HIP-event averages over a graph of repeated calls on the current stream."""
     codes, scales, alpha = nv.quantize(W, "4o6")
     n, k = W.shape
     out = {"weights": f"{n}x{k} NVFP4 (FourOverSix)", "cases": {}}
     for m in (1, 4096):
         X = (torch.randn((m, k), device=dev) * 0.5).to(torch.bfloat16)
+        Y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        reps = 200 if m == 1 else 20
         for _ in range(3):
-            nv.matmul(X, codes, scales, alpha)
-        reps = 50 if m == 1 else 10
+            nv.matmul(X, codes, scales, alpha, out=Y)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()  # the calls back to back on the device, without host overhead between them
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                nv.matmul(X, codes, scales, alpha, out=Y)
+        g.replay()
+        torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        for _ in range(reps):
-            nv.matmul(X, codes, scales, alpha)
+        g.replay()
         e1.record()
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / reps

@@ -197,9 +197,10 @@ def error_stats(W: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, alph
 
 
 def matmul(X: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, alpha: torch.Tensor,
-           out_dtype=torch.bfloat16, stream=None) -> torch.Tensor:
+           out_dtype=torch.bfloat16, stream=None, out: torch.Tensor = None) -> torch.Tensor:
     """W4A16 product Y = X @ What.T with NVFP4 weights (codes [N, K/2], scales [N, K/16], alpha [1] as
-    quantize returns them for an [N, K] matrix) and bf16 activations X [M, K]; Y is [M, N] bf16 or fp32."""
+    quantize returns them for an [N, K] matrix) and bf16 activations X [M, K]; Y is [M, N] bf16 or fp32,
+    written into `out` when one is given (contiguous, on X's device, of that shape and out_dtype)."""
     if X.dim() != 2 or not X.is_cuda or not X.is_contiguous() or X.dtype != torch.bfloat16:
         raise NVFP4Error("X must be a contiguous 2-D bf16 CUDA tensor")
     M, K = X.shape
@@ -214,7 +215,13 @@ def matmul(X: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, alpha: to
         raise NVFP4Error("scales or alpha do not match the weight shape")
     if out_dtype not in DTYPES:
         raise NVFP4Error("out_dtype must be bf16 or fp32")
-    Y = torch.empty((M, N), dtype=out_dtype, device=dev)
+    if out is None:
+        Y = torch.empty((M, N), dtype=out_dtype, device=dev)
+    else:
+        if (out.shape != (M, N) or out.dtype != out_dtype or not out.is_cuda or out.device != dev
+                or not out.is_contiguous()):
+            raise NVFP4Error("out must be a contiguous [M, N] tensor of out_dtype on X's device")
+        Y = out
     _check(lib().nvfp4_matmul(X.data_ptr(), M, K, codes.data_ptr(), scales.data_ptr(), alpha.data_ptr(), N,
                               Y.data_ptr(), DTYPES[out_dtype], _stream_ptr(stream, dev)))
     return Y

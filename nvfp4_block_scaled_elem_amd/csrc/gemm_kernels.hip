@@ -9,12 +9,13 @@
 // output type). Only the accumulation order differs from an exact product.
 //
 // Two kernels:
-//   k_w4a16_gemm: 128 x 128 output tile per work-group (4 waves, 64 x 64 each as 2 x 2 tiles of
+//   k_w4a16_gemm: 256 x 128 output tile per work-group (4 waves, 128 x 64 each as 4 x 2 tiles of
 //     v_mfma_f32_32x32x16_bf16), K in steps of 64 through LDS: the X tile is copied, the weight tile is
-//     decoded to bf16 (codes -> binary32 q, times Delta, high half) as it is stored.
+//     decoded to bf16 (codes -> binary32 q, times Delta, high half) once per work-group as it is stored,
+//     and the next step's loads are in flight while the matrix cores work on this one.
 //   k_w4a16_gemv: M <= 4 (decoding one token per row, say): bound by reading the 0.5625 bytes per weight
-//     once; X sits in LDS, each wave takes whole rows n, each lane 32 consecutive k at a time, and the
-//     row sum is a DPP wave reduction.
+//     once; each wave requests all codes of its 4 rows n up front, X sits in LDS, each lane takes 32
+//     consecutive k per 2048-k chunk, and the row sums are DPP wave reductions.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -27,8 +28,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kGemmThreads = 256;
-constexpr int kBM = 128, kBN = 128, kBK = 64;
-constexpr int kLdsStride = kBK + 8;  // bf16 per LDS row: the padding spreads rows over the banks
+constexpr int kBM = 256, kBN = 128, kBK = 64;
+constexpr int kLdsStride = kBK + 8;  // bf16 per LDS row: the padding spreads the rows a wave reads over the banks
 
 // 8 codes (one dword) and their scale value -> 8 dequantised weights (without alpha) as bf16 pairs.
 __device__ __forceinline__ uint4 dequant8(uint32_t c, float dv) {
@@ -57,77 +58,103 @@ __device__ __forceinline__ void store_y(void *Y, int64_t idx, float v) {
         static_cast<uint16_t *>(Y)[idx] = to_bf16(v);
 }
 
+// One K step of a work-group's operands, held in registers between the global loads and the LDS stores:
+// the X tile (256 rows x 64 k, 8 x 16 bytes per thread) and the weight tile (128 rows n x 64 k: 16 bytes
+// of codes = 32 k and their two scale bytes per thread). Rows and k past the matrix read as zeros.
+struct GemmStage {
+    uint4 x[8];
+    uint4 c;
+    uint32_t sc;
+};
+
+__device__ __forceinline__ void gemm_load(GemmStage &S, const uint16_t *__restrict__ X, int64_t M, int64_t K,
+                                          const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales,
+                                          int64_t N, int64_t m0, int64_t n0, int64_t k0, int tid) {
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+        const int idx = tid + p * kGemmThreads;  // row idx / 8, 8-element group idx % 8
+        const int64_t m = m0 + (idx >> 3), k = k0 + 8 * (idx & 7);
+        S.x[p] = make_uint4(0u, 0u, 0u, 0u);
+        if (m < M && k < K) S.x[p] = *reinterpret_cast<const uint4 *>(X + m * K + k);  // K % 16 == 0
+    }
+    const int64_t n = n0 + (tid >> 1), k = k0 + 32 * (tid & 1);
+    S.c = make_uint4(0u, 0u, 0u, 0u);
+    S.sc = 0u;
+    if (n < N && k < K) {
+        const int64_t e = n * K + k;  // element index, a multiple of 16
+        if (k + 32 <= K) {
+            S.c = *reinterpret_cast<const uint4 *>(codes + e / 2);
+            S.sc = (uint32_t)scales[e / 16] | ((uint32_t)scales[e / 16 + 1] << 8);
+        } else {  // K % 32 == 16: the last 16 k of the row
+            const uint2 c2 = *reinterpret_cast<const uint2 *>(codes + e / 2);
+            S.c = make_uint4(c2.x, c2.y, 0u, 0u);
+            S.sc = (uint32_t)scales[e / 16];
+        }
+    }
+}
+
+__device__ __forceinline__ void gemm_store(const GemmStage &S, uint16_t *xs, uint16_t *ws, int tid) {
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+        const int idx = tid + p * kGemmThreads;
+        *reinterpret_cast<uint4 *>(&xs[(idx >> 3) * kLdsStride + 8 * (idx & 7)]) = S.x[p];
+    }
+    const float d0 = e4m3_value(S.sc & 0x7Fu), d1 = e4m3_value((S.sc >> 8) & 0x7Fu);
+    uint16_t *dst = &ws[(tid >> 1) * kLdsStride + 32 * (tid & 1)];
+    *reinterpret_cast<uint4 *>(dst) = dequant8(S.c.x, d0);
+    *reinterpret_cast<uint4 *>(dst + 8) = dequant8(S.c.y, d0);
+    *reinterpret_cast<uint4 *>(dst + 16) = dequant8(S.c.z, d1);
+    *reinterpret_cast<uint4 *>(dst + 24) = dequant8(S.c.w, d1);
+}
+
+// 256 x 128 output tile per work-group, 4 waves of 128 x 64 (4 x 2 tiles of v_mfma_f32_32x32x16_bf16).
+// The loads of K step t + 1 are issued into registers before the products of step t, so they are in
+// flight while the matrix cores run; one LDS buffer (55 KB) leaves room for two work-groups per CU.
+// Work-groups go to the 8 XCDs round robin; the tile order is remapped so that each XCD takes a
+// contiguous band of tiles and its L2 holds the few X row blocks that band needs.
 template <bool OUTF32>
-__global__ __launch_bounds__(kGemmThreads) void k_w4a16_gemm(const uint16_t *__restrict__ X, int64_t M, int64_t K,
+__global__ __launch_bounds__(kGemmThreads, 2) void k_w4a16_gemm(const uint16_t *__restrict__ X, int64_t M, int64_t K,
                                                              const uint8_t *__restrict__ codes,
                                                              const uint8_t *__restrict__ scales,
                                                              const float *__restrict__ alpha_p, int64_t N,
-                                                             void *__restrict__ Y) {
+                                                             void *__restrict__ Y, unsigned tiles_n) {
     __shared__ __attribute__((aligned(16))) uint16_t xs[kBM * kLdsStride];
     __shared__ __attribute__((aligned(16))) uint16_t ws[kBN * kLdsStride];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t m0 = (int64_t)blockIdx.y * kBM, n0 = (int64_t)blockIdx.x * kBN;
-    const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;  // the wave's 64 x 64 corner of the tile
-    f32x16 acc[2][2] = {};
-
+    const unsigned total = gridDim.x;  // 1-D grid: tiles_m * tiles_n tiles, row-major
+    unsigned b = blockIdx.x;
+    if (total % 8 == 0) b = (b % 8) * (total / 8) + b / 8;
+    const int64_t m0 = (int64_t)(b / tiles_n) * kBM, n0 = (int64_t)(b % tiles_n) * kBN;
+    const int wm = (wave >> 1) * 128, wn = (wave & 1) * 64;  // the wave's 128 x 64 corner of the tile
+    f32x16 acc[4][2] = {};
+    GemmStage S;
+    gemm_load(S, X, M, K, codes, scales, N, m0, n0, 0, tid);
     for (int64_t k0 = 0; k0 < K; k0 += kBK) {
-        // X tile: 128 rows x 64 k, 4 x 16 bytes per thread (rows past M and k past K read as zeros)
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const int idx = tid + p * kGemmThreads;  // 0..1023: row idx / 8, 8-element group idx % 8
-            const int r = idx >> 3, g = idx & 7;
-            const int64_t m = m0 + r, k = k0 + 8 * g;
-            uint4 v = make_uint4(0u, 0u, 0u, 0u);
-            if (m < M && k < K) v = *reinterpret_cast<const uint4 *>(X + m * K + k);  // K % 16 == 0
-            *reinterpret_cast<uint4 *>(&xs[r * kLdsStride + 8 * g]) = v;
-        }
-        // weight tile: 128 rows n x 64 k = 32 bytes of codes per row; a thread decodes 16 bytes (32 k)
-        {
-            const int r = tid >> 1, h = tid & 1;
-            const int64_t n = n0 + r, k = k0 + 32 * h;
-            uint4 c = make_uint4(0u, 0u, 0u, 0u);
-            float d0 = 0.0f, d1 = 0.0f;
-            if (n < N && k < K) {
-                const int64_t e = n * K + k;  // element index, a multiple of 32
-                if (k + 32 <= K) {
-                    c = *reinterpret_cast<const uint4 *>(codes + e / 2);
-                } else {  // K % 32 == 16: the last 16 k of the row
-                    const uint2 c2 = *reinterpret_cast<const uint2 *>(codes + e / 2);
-                    c = make_uint4(c2.x, c2.y, 0u, 0u);
-                }
-                d0 = e4m3_value(scales[e / 16] & 0x7Fu);
-                if (k + 16 < K) d1 = e4m3_value(scales[e / 16 + 1] & 0x7Fu);
-            }
-            uint16_t *dst = &ws[r * kLdsStride + 32 * h];
-            *reinterpret_cast<uint4 *>(dst) = dequant8(c.x, d0);
-            *reinterpret_cast<uint4 *>(dst + 8) = dequant8(c.y, d0);
-            *reinterpret_cast<uint4 *>(dst + 16) = dequant8(c.z, d1);
-            *reinterpret_cast<uint4 *>(dst + 24) = dequant8(c.w, d1);
-        }
+        gemm_store(S, xs, ws, tid);
         __syncthreads();
+        if (k0 + kBK < K) gemm_load(S, X, M, K, codes, scales, N, m0, n0, k0 + kBK, tid);
 #pragma unroll
         for (int kk = 0; kk < kBK; kk += 16) {
-            bf16x8 a[2], b[2];
+            bf16x8 a[4], bb[2];
+            // A operand: row (lane % 32) of a 32-row tile, k = 8 * (lane / 32) .. + 7; B: column lane % 32
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                // A operand: row (lane % 32) of the 32-row tile, k = 8 * (lane / 32) .. + 7
-                a[i] = *reinterpret_cast<const bf16x8 *>(
-                    &xs[(wm + 32 * i + (lane & 31)) * kLdsStride + kk + 8 * (lane >> 5)]);
-                // B operand: column n = lane % 32 of the tile, the same k
-                b[i] = *reinterpret_cast<const bf16x8 *>(
-                    &ws[(wn + 32 * i + (lane & 31)) * kLdsStride + kk + 8 * (lane >> 5)]);
-            }
+            for (int i = 0; i < 4; ++i)
+                a[i] = *reinterpret_cast<const bf16x8 *>(&xs[(wm + 32 * i + (lane & 31)) * kLdsStride + kk + 8 * (lane >> 5)]);
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int j = 0; j < 2; ++j)
+                bb[j] = *reinterpret_cast<const bf16x8 *>(&ws[(wn + 32 * j + (lane & 31)) * kLdsStride + kk + 8 * (lane >> 5)]);
 #pragma unroll
-                for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bb[j], acc[i][j], 0, 0, 0);
         }
         __syncthreads();
     }
     // D layout: element e of lane l is row 8 * (e / 4) + 4 * (l / 32) + e % 4, column l % 32
     const float alpha = *alpha_p;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -154,10 +181,14 @@ __device__ __forceinline__ float wave_sum_f32(float x) {
     return x;
 }
 
-// X (M rows, K <= the LDS budget) is copied to LDS once per work-group; each wave then takes rows
-// n = global wave, + total waves, ...; lane l handles k = 32 * (l + 64 i) .. + 31 (16 bytes of codes,
-// two scales) and accumulates M dot products in fp32.
-template <int MM, bool OUTF32>
+// Each wave owns kGemvRows consecutive rows n and, before anything else, requests all of their codes and
+// scales (lane l takes k = 32 * (l + 64 c) .. + 31 of chunk c < CH, 16 bytes of codes): the whole weight
+// matrix is in flight at once, which is what a read-once product needs. Meanwhile the work-group copies X
+// (MM rows, K <= the LDS budget) to LDS; then each lane decodes its weights, forms MM fp32 dot products
+// with packed bf16 dot instructions, and a DPP wave reduction gives each row's sums.
+constexpr int kGemvRows = 4;
+
+template <int MM, int CH, bool OUTF32>
 __global__ __launch_bounds__(kGemvThreads) void k_w4a16_gemv(const uint16_t *__restrict__ X, int64_t K,
                                                              const uint8_t *__restrict__ codes,
                                                              const uint8_t *__restrict__ scales,
@@ -165,30 +196,45 @@ __global__ __launch_bounds__(kGemvThreads) void k_w4a16_gemv(const uint16_t *__r
                                                              void *__restrict__ Y) {
     extern __shared__ __attribute__((aligned(16))) uint16_t xl[];  // [MM][K]
     const int tid = threadIdx.x, lane = tid & 63;
+    const int64_t n0 = ((int64_t)blockIdx.x * (kGemvThreads / 64) + (tid >> 6)) * kGemvRows;
+    uint4 c[kGemvRows][CH];
+    uint32_t sc[kGemvRows][CH];  // the chunk's two scale bytes
+#pragma unroll
+    for (int r = 0; r < kGemvRows; ++r)
+#pragma unroll
+        for (int ch = 0; ch < CH; ++ch) {
+            const int64_t n = n0 + r, k = 32 * (lane + 64 * ch);
+            c[r][ch] = make_uint4(0u, 0u, 0u, 0u);
+            sc[r][ch] = 0u;
+            if (n < N && k < K) {
+                const int64_t e = n * K + k;
+                if (k + 32 <= K) {
+                    c[r][ch] = *reinterpret_cast<const uint4 *>(codes + e / 2);
+                    sc[r][ch] = (uint32_t)scales[e / 16] | ((uint32_t)scales[e / 16 + 1] << 8);
+                } else {  // the row's last 16 k (K % 32 == 16)
+                    const uint2 c2 = *reinterpret_cast<const uint2 *>(codes + e / 2);
+                    c[r][ch] = make_uint4(c2.x, c2.y, 0u, 0u);
+                    sc[r][ch] = (uint32_t)scales[e / 16];
+                }
+            }
+        }
     for (int64_t i = tid; i < MM * K / 8; i += kGemvThreads)
         reinterpret_cast<uint4 *>(xl)[i] = reinterpret_cast<const uint4 *>(X)[i];
     __syncthreads();
     const float alpha = *alpha_p;
-    const int64_t waves = (int64_t)gridDim.x * (kGemvThreads / 64);
-    for (int64_t n = (int64_t)blockIdx.x * (kGemvThreads / 64) + (tid >> 6); n < N; n += waves) {
+#pragma unroll
+    for (int r = 0; r < kGemvRows; ++r) {
         float s[MM];
 #pragma unroll
         for (int m = 0; m < MM; ++m) s[m] = 0.0f;
-        for (int64_t k = 32 * lane; k < K; k += 32 * 64) {
-            const int64_t e = n * K + k;
-            const bool whole = k + 32 <= K;  // else the row's last 16 k (K % 32 == 16)
-            uint4 c;
-            float d1 = 0.0f;
-            if (whole) {
-                c = *reinterpret_cast<const uint4 *>(codes + e / 2);
-                d1 = e4m3_value(scales[e / 16 + 1] & 0x7Fu);
-            } else {
-                const uint2 c2 = *reinterpret_cast<const uint2 *>(codes + e / 2);
-                c = make_uint4(c2.x, c2.y, 0u, 0u);
-            }
-            const float d0 = e4m3_value(scales[e / 16] & 0x7Fu);
-            const uint4 w[4] = {dequant8(c.x, d0), dequant8(c.y, d0), dequant8(c.z, d1), dequant8(c.w, d1)};
-            const int nq = whole ? 4 : 2;
+#pragma unroll
+        for (int ch = 0; ch < CH; ++ch) {
+            const int64_t k = 32 * (lane + 64 * ch);
+            if (k >= K) break;
+            const int nq = k + 32 <= K ? 4 : 2;
+            const float d0 = e4m3_value(sc[r][ch] & 0x7Fu), d1 = e4m3_value((sc[r][ch] >> 8) & 0x7Fu);
+            const uint4 w[4] = {dequant8(c[r][ch].x, d0), dequant8(c[r][ch].y, d0), dequant8(c[r][ch].z, d1),
+                                dequant8(c[r][ch].w, d1)};
 #pragma unroll
             for (int m = 0; m < MM; ++m) {
                 const uint4 *xr = reinterpret_cast<const uint4 *>(xl + m * K + k);
@@ -205,10 +251,11 @@ __global__ __launch_bounds__(kGemvThreads) void k_w4a16_gemv(const uint16_t *__r
                 }
             }
         }
+        const int64_t n = n0 + r;
 #pragma unroll
         for (int m = 0; m < MM; ++m) {
             const float t = wave_sum_f32(s[m]);
-            if (lane == 63) store_y<OUTF32>(Y, m * N + n, alpha * t);
+            if (lane == 63 && n < N) store_y<OUTF32>(Y, m * N + n, alpha * t);
         }
     }
 }
@@ -217,16 +264,23 @@ size_t gemv_lds_bytes(int64_t M, int64_t K) { return (size_t)(M * K * 2); }
 
 hipError_t launch_w4a16(const uint16_t *X, int64_t M, int64_t K, const uint8_t *codes, const uint8_t *scales,
                         const float *alpha, int64_t N, void *Y, bool out_f32, hipStream_t stream) {
-    if (M <= kGemvMaxM && gemv_lds_bytes(M, K) <= 64 * 1024) {
-        const int64_t blocks = (N + (kGemvThreads / 64) - 1) / (kGemvThreads / 64);
-        const dim3 grid((unsigned)(blocks < 1024 ? blocks : 1024)), block(kGemvThreads);
+    const int64_t chunks = (K + 2047) / 2048;  // 2048 k per chunk: 32 per lane
+    if (M <= kGemvMaxM && gemv_lds_bytes(M, K) <= 64 * 1024 && chunks <= 8) {
+        const int64_t waves = (N + kGemvRows - 1) / kGemvRows;
+        const dim3 grid((unsigned)((waves + kGemvThreads / 64 - 1) / (kGemvThreads / 64))), block(kGemvThreads);
         const size_t lds = gemv_lds_bytes(M, K);
-#define NVFP4_GEMV(MM)                                                                                            \
+#define NVFP4_GEMV3(MM, CH)                                                                                       \
     do {                                                                                                          \
         if (out_f32)                                                                                              \
-            hipLaunchKernelGGL((k_w4a16_gemv<MM, true>), grid, block, lds, stream, X, K, codes, scales, alpha, N, Y); \
+            hipLaunchKernelGGL((k_w4a16_gemv<MM, CH, true>), grid, block, lds, stream, X, K, codes, scales, alpha, N, \
+                               Y);                                                                                \
         else                                                                                                      \
-            hipLaunchKernelGGL((k_w4a16_gemv<MM, false>), grid, block, lds, stream, X, K, codes, scales, alpha, N, Y); \
+            hipLaunchKernelGGL((k_w4a16_gemv<MM, CH, false>), grid, block, lds, stream, X, K, codes, scales, alpha,  \
+                               N, Y);                                                                             \
+    } while (0)
+#define NVFP4_GEMV(MM)                                                                                            \
+    do {                                                                                                          \
+        if (chunks <= 2) NVFP4_GEMV3(MM, 2); else if (chunks <= 4) NVFP4_GEMV3(MM, 4); else NVFP4_GEMV3(MM, 8);    \
     } while (0)
         switch (M) {
             case 1: NVFP4_GEMV(1); break;
@@ -235,13 +289,17 @@ hipError_t launch_w4a16(const uint16_t *X, int64_t M, int64_t K, const uint8_t *
             default: NVFP4_GEMV(4); break;
         }
 #undef NVFP4_GEMV
+#undef NVFP4_GEMV3
         return hipGetLastError();
     }
-    const dim3 grid((unsigned)((N + kBN - 1) / kBN), (unsigned)((M + kBM - 1) / kBM)), block(kGemmThreads);
+    const int64_t tiles_n = (N + kBN - 1) / kBN, tiles_m = (M + kBM - 1) / kBM;
+    const dim3 grid((unsigned)(tiles_n * tiles_m)), block(kGemmThreads);
     if (out_f32)
-        hipLaunchKernelGGL(k_w4a16_gemm<true>, grid, block, 0, stream, X, M, K, codes, scales, alpha, N, Y);
+        hipLaunchKernelGGL(k_w4a16_gemm<true>, grid, block, 0, stream, X, M, K, codes, scales, alpha, N, Y,
+                           (unsigned)tiles_n);
     else
-        hipLaunchKernelGGL(k_w4a16_gemm<false>, grid, block, 0, stream, X, M, K, codes, scales, alpha, N, Y);
+        hipLaunchKernelGGL(k_w4a16_gemm<false>, grid, block, 0, stream, X, M, K, codes, scales, alpha, N, Y,
+                           (unsigned)tiles_n);
     return hipGetLastError();
 }
 

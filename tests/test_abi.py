@@ -98,6 +98,21 @@ def test_error_stats_rejects(L):
     assert f(FAKE, 1, 4, 16, FAKE, FAKE, FAKE, FAKE, None, None) == INVALID
 
 
+def test_matmul_rejects(L):
+    f = L.nvfp4_matmul
+    assert f(None, 1, 32, FAKE, FAKE, FAKE, 8, FAKE, 0, None) == INVALID
+    assert f(FAKE, 0, 32, FAKE, FAKE, FAKE, 8, FAKE, 0, None) == INVALID
+    assert f(FAKE, 1, 32, FAKE, FAKE, FAKE, 0, FAKE, 0, None) == INVALID
+    assert f(FAKE, 1, 32, FAKE, FAKE, FAKE, 8, FAKE, 2, None) == INVALID  # output dtype
+    assert f(FAKE, 1, 24, FAKE, FAKE, FAKE, 8, FAKE, 0, None) == SHAPE  # K % 16
+    assert f(FAKE, 1, 16, FAKE, FAKE, FAKE, (1 << 27) + 1, FAKE, 0, None) == SHAPE
+    assert f(FAKE, 1 << 20, 16, FAKE, FAKE, FAKE, 1 << 19, FAKE, 0, None) == SHAPE  # 2^24 tiles
+    assert f(FAKE + 8, 1, 32, FAKE, FAKE, FAKE, 8, FAKE, 0, None) == INVALID  # alignment
+    assert f(FAKE, 1, 32, FAKE + 8, FAKE, FAKE, 8, FAKE, 0, None) == INVALID
+    assert f(FAKE, 1, 32, FAKE, FAKE, FAKE + 2, 8, FAKE, 0, None) == INVALID
+    assert f(FAKE, 1, 32, FAKE, FAKE, FAKE, 8, FAKE + 8, 0, None) == INVALID
+
+
 def test_sizes_and_counts(L):
     assert L.nvfp4_workspace_bytes(4096, 4096, 0) > 0
     assert L.nvfp4_workspace_bytes(4096, 4096, 3) >= L.nvfp4_workspace_bytes(4096, 4096, 2) + 2 * 4096 * 256
