@@ -167,7 +167,7 @@ int nvfp4_error_stats(const void *W, int dtype, int64_t rows, int64_t cols, cons
  * What = e2m1(code) * e4m3(scale) * alpha (SOAR page, dequantisation equation), for a weight matrix [N][K]
  * stored as the quantiser writes it (codes [N][K/2], scales [N][K/16], alpha one float). X is bf16
  * [M][K] row-major; Y is [M][N] of y_dtype (NVFP4_DTYPE_BF16 or _F32). All pointers are device pointers;
- * X, codes and Y 16-byte aligned; K % 16 == 0, N <= 2^27 and fewer than 2^24 output tiles of 256 x 128
+ * X, codes and Y 16-byte aligned; K % 16 == 0, N <= 2^25 and fewer than 2^24 output tiles of 256 x 128
  * (else NVFP4_ERR_SHAPE). Arithmetic: every q * Delta is a bf16 value,
  * so the products with X are exact; the sum over k is accumulated in fp32 (bf16 MFMA for M > 4, packed
  * bf16 dot products for M <= 4) in an order the caller does not control, then multiplied by alpha and

@@ -194,7 +194,7 @@ NVFP4_API int nvfp4_matmul(const void *X, int64_t M, int64_t K, const uint8_t *c
                            const float *alpha, int64_t N, void *Y, int y_dtype, void *stream) {
     if (!X || !codes || !scales || !alpha || !Y || M <= 0 || K <= 0 || N <= 0) return NVFP4_ERR_INVALID_ARG;
     if (y_dtype != NVFP4_DTYPE_BF16 && y_dtype != NVFP4_DTYPE_F32) return NVFP4_ERR_INVALID_ARG;
-    if (K % 16 != 0 || N > ((int64_t)1 << 27) || N > kMaxElems / K || M > kMaxElems / K || M > kMaxElems / N ||
+    if (K % 16 != 0 || N > ((int64_t)1 << 25) || N > kMaxElems / K || M > kMaxElems / K || M > kMaxElems / N ||
         ((M + 255) / 256) * ((N + 127) / 128) >= ((int64_t)1 << 24))
         return NVFP4_ERR_SHAPE;
     if (((uintptr_t)X & 15u) != 0 || ((uintptr_t)codes & 15u) != 0 || ((uintptr_t)Y & 15u) != 0 ||

@@ -167,7 +167,13 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_w4a16_gemm(const uint16_t *
 
 // ------------------------------------------------------------------------------------------- GEMV
 
-constexpr int kGemvThreads = 256;
+#ifndef NVFP4_GEMV_THREADS
+#define NVFP4_GEMV_THREADS 1024
+#endif
+#ifndef NVFP4_GEMV_ROWS
+#define NVFP4_GEMV_ROWS 1
+#endif
+constexpr int kGemvThreads = NVFP4_GEMV_THREADS;
 constexpr int kGemvMaxM = 4;
 
 // Wave sum on the VALU (DPP; the total ends in lane 63).
@@ -181,12 +187,13 @@ __device__ __forceinline__ float wave_sum_f32(float x) {
     return x;
 }
 
-// Each wave owns kGemvRows consecutive rows n and, before anything else, requests all of their codes and
-// scales (lane l takes k = 32 * (l + 64 c) .. + 31 of chunk c < CH, 16 bytes of codes): the whole weight
-// matrix is in flight at once, which is what a read-once product needs. Meanwhile the work-group copies X
-// (MM rows, K <= the LDS budget) to LDS; then each lane decodes its weights, forms MM fp32 dot products
-// with packed bf16 dot instructions, and a DPP wave reduction gives each row's sums.
-constexpr int kGemvRows = 4;
+// Each wave owns kGemvRows consecutive rows n (one by default: with 16 waves per work-group the most
+// loads are in flight) and, before anything else, requests all of their codes and scales (lane l takes
+// k = 32 * (l + 64 c) .. + 31 of chunk c < CH, 16 bytes of codes): the whole weight matrix is in flight
+// at once, which is what a read-once product needs. Meanwhile the work-group copies X (MM rows, up to
+// kGemvMaxLds bytes) to LDS; then each lane decodes its weights, forms MM fp32 dot products with packed
+// bf16 dot instructions, and a DPP wave reduction gives each row's sums.
+constexpr int kGemvRows = NVFP4_GEMV_ROWS;
 
 template <int MM, int CH, bool OUTF32>
 __global__ __launch_bounds__(kGemvThreads) void k_w4a16_gemv(const uint16_t *__restrict__ X, int64_t K,
@@ -261,36 +268,45 @@ __global__ __launch_bounds__(kGemvThreads) void k_w4a16_gemv(const uint16_t *__r
 }
 
 size_t gemv_lds_bytes(int64_t M, int64_t K) { return (size_t)(M * K * 2); }
+constexpr size_t kGemvMaxLds = 128 * 1024;
+
+// Launch of one GEMV instantiation; the kernel is allowed the large dynamic LDS size once per process
+// (the attribute is per function; two threads setting it at once set the same value).
+template <int MM, int CH, bool OUTF32>
+hipError_t gemv_launch(dim3 grid, size_t lds, hipStream_t stream, const uint16_t *X, int64_t K,
+                       const uint8_t *codes, const uint8_t *scales, const float *alpha, int64_t N, void *Y) {
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_w4a16_gemv<MM, CH, OUTF32>),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemvMaxLds);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL((k_w4a16_gemv<MM, CH, OUTF32>), grid, dim3(kGemvThreads), lds, stream, X, K, codes, scales,
+                       alpha, N, Y);
+    return hipGetLastError();
+}
 
 hipError_t launch_w4a16(const uint16_t *X, int64_t M, int64_t K, const uint8_t *codes, const uint8_t *scales,
                         const float *alpha, int64_t N, void *Y, bool out_f32, hipStream_t stream) {
     const int64_t chunks = (K + 2047) / 2048;  // 2048 k per chunk: 32 per lane
-    if (M <= kGemvMaxM && gemv_lds_bytes(M, K) <= 64 * 1024 && chunks <= 8) {
+    if (M <= kGemvMaxM && gemv_lds_bytes(M, K) <= kGemvMaxLds && chunks <= 8) {
         const int64_t waves = (N + kGemvRows - 1) / kGemvRows;
-        const dim3 grid((unsigned)((waves + kGemvThreads / 64 - 1) / (kGemvThreads / 64))), block(kGemvThreads);
+        const dim3 grid((unsigned)((waves + kGemvThreads / 64 - 1) / (kGemvThreads / 64)));
         const size_t lds = gemv_lds_bytes(M, K);
-#define NVFP4_GEMV3(MM, CH)                                                                                       \
-    do {                                                                                                          \
-        if (out_f32)                                                                                              \
-            hipLaunchKernelGGL((k_w4a16_gemv<MM, CH, true>), grid, block, lds, stream, X, K, codes, scales, alpha, N, \
-                               Y);                                                                                \
-        else                                                                                                      \
-            hipLaunchKernelGGL((k_w4a16_gemv<MM, CH, false>), grid, block, lds, stream, X, K, codes, scales, alpha,  \
-                               N, Y);                                                                             \
-    } while (0)
-#define NVFP4_GEMV(MM)                                                                                            \
-    do {                                                                                                          \
-        if (chunks <= 2) NVFP4_GEMV3(MM, 2); else if (chunks <= 4) NVFP4_GEMV3(MM, 4); else NVFP4_GEMV3(MM, 8);    \
+#define NVFP4_GEMV3(MM, CH)                                                                                      \
+    return out_f32 ? gemv_launch<MM, CH, true>(grid, lds, stream, X, K, codes, scales, alpha, N, Y)               \
+                   : gemv_launch<MM, CH, false>(grid, lds, stream, X, K, codes, scales, alpha, N, Y)
+#define NVFP4_GEMV(MM)                                                                                           \
+    do {                                                                                                         \
+        if (chunks <= 2) NVFP4_GEMV3(MM, 2);                                                                     \
+        if (chunks <= 4) NVFP4_GEMV3(MM, 4);                                                                     \
+        NVFP4_GEMV3(MM, 8);                                                                                      \
     } while (0)
         switch (M) {
-            case 1: NVFP4_GEMV(1); break;
-            case 2: NVFP4_GEMV(2); break;
-            case 3: NVFP4_GEMV(3); break;
-            default: NVFP4_GEMV(4); break;
+            case 1: NVFP4_GEMV(1);
+            case 2: NVFP4_GEMV(2);
+            case 3: NVFP4_GEMV(3);
+            default: NVFP4_GEMV(4);
         }
 #undef NVFP4_GEMV
 #undef NVFP4_GEMV3
-        return hipGetLastError();
     }
     const int64_t tiles_n = (N + kBN - 1) / kBN, tiles_m = (M + kBM - 1) / kBM;
     const dim3 grid((unsigned)(tiles_n * tiles_m)), block(kGemmThreads);

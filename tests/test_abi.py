@@ -105,7 +105,7 @@ def test_matmul_rejects(L):
     assert f(FAKE, 1, 32, FAKE, FAKE, FAKE, 0, FAKE, 0, None) == INVALID
     assert f(FAKE, 1, 32, FAKE, FAKE, FAKE, 8, FAKE, 2, None) == INVALID  # output dtype
     assert f(FAKE, 1, 24, FAKE, FAKE, FAKE, 8, FAKE, 0, None) == SHAPE  # K % 16
-    assert f(FAKE, 1, 16, FAKE, FAKE, FAKE, (1 << 27) + 1, FAKE, 0, None) == SHAPE
+    assert f(FAKE, 1, 16, FAKE, FAKE, FAKE, (1 << 25) + 1, FAKE, 0, None) == SHAPE
     assert f(FAKE, 1 << 20, 16, FAKE, FAKE, FAKE, 1 << 19, FAKE, 0, None) == SHAPE  # 2^24 tiles
     assert f(FAKE + 8, 1, 32, FAKE, FAKE, FAKE, 8, FAKE, 0, None) == INVALID  # alignment
     assert f(FAKE, 1, 32, FAKE + 8, FAKE, FAKE, 8, FAKE, 0, None) == INVALID

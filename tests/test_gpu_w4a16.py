@@ -51,6 +51,7 @@ def check(X, codes, scales, alpha, out_dtype):
 
 SHAPES = [(1, 256, 1024), (2, 96, 160), (3, 64, 272), (4, 130, 64),   # GEMV path (M <= 4), 2 chunks
           (1, 70, 4112), (3, 9, 6160), (2, 33, 12304), (4, 5, 8192),  # GEMV with 4 and 8 chunks of 2048 k
+          (4, 37, 11008), (4, 40, 16384),  # X of 88 KB and 128 KB (the GEMV's LDS limit)
           (1, 21, 16400),  # M = 1 past the GEMV's K limit: the MFMA path
           (5, 200, 272), (64, 128, 512), (130, 260, 528), (128, 256, 1024),  # MFMA path, one row of tiles
           (300, 136, 96), (512, 512, 160), (260, 1100, 48)]  # several 256 x 128 tiles (8 | 8 tiles: remapped)
