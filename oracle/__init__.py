@@ -51,6 +51,13 @@ def lib():
         L.nvfp4_ref_matmul.restype = i32
         L.nvfp4_ref_soar_blocks.argtypes = [vp, i32, i64, i64, ctypes.c_float, u8p, vp, vp, i64, u8p, u8p]
         L.nvfp4_ref_soar_blocks.restype = i32
+        L.nvfp4_ref_soar_blocks_search.argtypes = [vp, i32, i64, i64, ctypes.c_float, u8p, vp, vp, i64,
+                                                   i32, i32, i32, i32, u8p, u8p]
+        L.nvfp4_ref_soar_blocks_search.restype = i32
+        L.nvfp4_ref_quantize_search.argtypes = [vp, i32, i64, i64, i32, i32, i32, i32, i32, i32, u8p, u8p, vp, vp]
+        L.nvfp4_ref_quantize_search.restype = i32
+        L.nvfp4_ref_grid_multiplier.argtypes = [i32, i32, i32]
+        L.nvfp4_ref_grid_multiplier.restype = ctypes.c_float
         L.nvfp4_ref_mse.argtypes = [vp, i32, i64, i64, u8p, u8p, ctypes.c_float]
         L.nvfp4_ref_mse.restype = ctypes.c_double
         L.nvfp4_ref_dequantize.argtypes = [u8p, u8p, ctypes.c_float, i64, i64, vp]
@@ -98,6 +105,8 @@ def _dtype_code(W: np.ndarray) -> int:
 
 
 INITS = {"max": 0, "4o6": 1}
+DD_RULES = {"cjso": 0, "quant": 1, "lsq": 2}  # NVFP4_REF_DD_*
+PAGES_GRID = (50, 100, 101)  # f_k = (50 + k) / 100, k = 0..100
 
 
 def quantize(W: np.ndarray, mode: str, iters: int = 0, *, trace: bool = False, init: str = "max"):
@@ -129,8 +138,34 @@ def quantize(W: np.ndarray, mode: str, iters: int = 0, *, trace: bool = False, i
     return out
 
 
-def soar_blocks(W: np.ndarray, alpha: float, dcode: np.ndarray, dstar: np.ndarray, blocks: np.ndarray):
-    """Decoupled search on the listed blocks, given the CJSO state. Returns (codes[nsel, 8], scales[nsel])."""
+def quantize_search(W: np.ndarray, iters: int, *, grid=PAGES_GRID, dd_rule: str = "cjso", init: str = "max"):
+    """SOAR with a configurable search: grid = (num0, den, count) gives f_k = nearest binary32 of
+    (num0 + k) / den for k < count; dd_rule picks each candidate's reconstruct pair ("cjso": around the
+    unrounded CJSO scale, the pages' rule; "quant": around Delta_q; "lsq": around the least-squares
+    scale of the candidate's codes). Returns a dict with codes, scales, alpha, status and dstar."""
+    W = np.ascontiguousarray(W)
+    rows, cols = W.shape
+    codes = np.zeros((rows, cols // 2), np.uint8)
+    scales = np.zeros((rows, cols // 16), np.uint8)
+    dstar = np.zeros((rows, cols // 16), np.float64)
+    alpha = ctypes.c_float(0.0)
+    num0, den, count = grid
+    st = lib().nvfp4_ref_quantize_search(_ptr(W), _dtype_code(W), rows, cols, iters, INITS[init], num0, den, count,
+                                         DD_RULES[dd_rule], _ptr(codes), _ptr(scales), ctypes.byref(alpha),
+                                         _ptr(dstar))
+    if st < 0:
+        raise ValueError(f"oracle rejected the arguments (status {st})")
+    return {"codes": codes, "scales": scales, "alpha": alpha.value, "status": st, "dstar": dstar}
+
+
+def grid_multiplier(num0: int, den: int, k: int) -> float:
+    return lib().nvfp4_ref_grid_multiplier(num0, den, k)
+
+
+def soar_blocks(W: np.ndarray, alpha: float, dcode: np.ndarray, dstar: np.ndarray, blocks: np.ndarray, *,
+                grid=PAGES_GRID, dd_rule: str = "cjso"):
+    """Decoupled search on the listed blocks, given the CJSO state (and optionally a search of
+    quantize_search). Returns (codes[nsel, 8], scales[nsel])."""
     W = np.ascontiguousarray(W)
     rows, cols = W.shape
     dcode = np.ascontiguousarray(dcode, np.uint8).reshape(-1)
@@ -138,8 +173,9 @@ def soar_blocks(W: np.ndarray, alpha: float, dcode: np.ndarray, dstar: np.ndarra
     blocks = np.ascontiguousarray(blocks, np.int64)
     codes = np.zeros((blocks.size, 8), np.uint8)
     scales = np.zeros(blocks.size, np.uint8)
-    st = lib().nvfp4_ref_soar_blocks(_ptr(W), _dtype_code(W), rows, cols, alpha, _ptr(dcode), _ptr(dstar),
-                                     _ptr(blocks), blocks.size, _ptr(codes), _ptr(scales))
+    st = lib().nvfp4_ref_soar_blocks_search(_ptr(W), _dtype_code(W), rows, cols, alpha, _ptr(dcode), _ptr(dstar),
+                                            _ptr(blocks), blocks.size, *grid, DD_RULES[dd_rule], _ptr(codes),
+                                            _ptr(scales))
     if st < 0:
         raise ValueError("oracle rejected the arguments")
     return codes, scales

@@ -37,6 +37,12 @@
  *   R10 CJSO started from FourOverSix (a composition the pages suggest, not a mode they define): the
  *      first scales are FourOverSix's choice under the max-rule alpha; the "unrounded" value of a chosen
  *      Delta4 is 1.5*Delta6, the quantity FourOverSix rounds to get it (for Delta6 it is max|w|/(6 alpha)).
+ *   R11 Search variants (not modes the pages define): the grid f_k = binary32 nearest (num0+k)/den,
+ *      k < count (R8 is 50, 100, 101); and the reconstruct pair of each candidate taken as the E4M3
+ *      values bracketing either its Delta_q or the least-squares scale of its own codes (the block-scale
+ *      step's binary64 quotient; a block whose codes are all zero keeps {Delta_c, Delta_c}), in place of
+ *      R8's bracket of the unrounded CJSO scale. The incumbent, the visiting order and the strict
+ *      improvement rule stay as in R8.
  *
  * Build: gcc -O2 -std=gnu11 -ffp-contract=off (no fast-math): every float expression below is the
  * IEEE operation it spells, in the order written.
@@ -302,29 +308,57 @@ static void cjso(const float *w, int64_t nblk, int iters, int init, float amax, 
 /* Decoupled quantise / dequantise scale search                                                      */
 /* ------------------------------------------------------------------------------------------------ */
 
+/* The search's multiplier grid and the rule that gives each candidate its two reconstruct scales.
+ * The pages fix one grid (R8) and one rule; the others are the variants R11 describes. */
+typedef struct {
+    int num0, den, count, dd_rule;
+} search_cfg;
+
+static const search_cfg pages_search = {50, 100, 101, NVFP4_REF_DD_CJSO};
+
+/* f_k = the binary32 value nearest (num0+k)/den. The binary64 quotient of the two integers is within
+ * half a binary64 ulp of the rational, and for den <= 2^24 that cannot land on a binary32 midpoint
+ * unless the rational is one, so converting it to binary32 rounds the rational itself (R8, R11). */
+float nvfp4_ref_grid_multiplier(int num0, int den, int k) { return (float)((double)(num0 + k) / (double)den); }
+
 /* [SOAR] Delta_q is perturbed multiplicatively over [0.5, 1.5] in steps of 0.01: f_k for k = 0..100 is
- * the binary32 value nearest to (50+k)/100 (R8; the binary64 quotient is never a binary32 midpoint). */
-float nvfp4_ref_search_multiplier(int k) { return (float)((double)(50 + k) / 100.0); }
+ * the binary32 value nearest to (50+k)/100 (R8). */
+float nvfp4_ref_search_multiplier(int k) { return nvfp4_ref_grid_multiplier(50, 100, k); }
+
+static int bad_search(int num0, int den, int count, int dd_rule) {
+    return den < 1 || den > (1 << 24) || num0 < 1 || count < 1 || count > 1024 ||
+           (int64_t)num0 + count - 1 > 16 * (int64_t)den || dd_rule < NVFP4_REF_DD_CJSO ||
+           dd_rule > NVFP4_REF_DD_LSQ;
+}
 
 /* [SOAR] for one block: Delta_q (high precision) quantises, Delta_d (E4M3) reconstructs. Start from the
- * CJSO scale (Delta_d = Delta_q = Delta_c); try Delta_q = fl(Delta_c·f_k) against Delta_d in {lo, hi},
- * the E4M3 values bracketing the unrounded CJSO scale (R8); keep the least error. */
-static void soar_block(const float *w16, float alpha, unsigned dc, double dstar, uint8_t *codes16,
-                       uint8_t *scale) {
-    unsigned lo, hi, dd[2];
+ * CJSO scale (Delta_d = Delta_q = Delta_c); try Delta_q = fl(Delta_c·f_k) against two values of
+ * Delta_d and keep the least error. The pages' rule (R8) takes the E4M3 values bracketing the unrounded
+ * CJSO scale for every candidate; the R11 rules bracket the candidate's Delta_q, or the least-squares
+ * scale of the candidate's own codes (the block-scale step applied to them). */
+static void soar_block(const float *w16, float alpha, unsigned dc, double dstar, const search_cfg *cfg,
+                       uint8_t *codes16, uint8_t *scale) {
+    unsigned dd[2];
     float dcv = (float)nvfp4_ref_e4m3_value(dc);
     uint8_t cand[16];
     quad best;
     int k, m;
-    nvfp4_ref_e4m3_bracket(dstar, &lo, &hi);
-    dd[0] = lo;
-    dd[1] = hi;
+    nvfp4_ref_e4m3_bracket(dstar, &dd[0], &dd[1]);
     nvfp4_ref_quantize_block(w16, alpha, dcv, codes16);
     best = block_err(w16, codes16, alpha, (double)dcv);
     *scale = (uint8_t)dc;
-    for (k = 0; k <= 100; ++k) {
-        float dq = dcv * nvfp4_ref_search_multiplier(k);
+    for (k = 0; k < cfg->count; ++k) {
+        float dq = dcv * nvfp4_ref_grid_multiplier(cfg->num0, cfg->den, k);
         nvfp4_ref_quantize_block(w16, alpha, dq, cand);
+        if (cfg->dd_rule == NVFP4_REF_DD_QUANT) {
+            nvfp4_ref_e4m3_bracket((double)dq, &dd[0], &dd[1]);
+        } else if (cfg->dd_rule == NVFP4_REF_DD_LSQ) {
+            double ls;
+            if (nvfp4_ref_delta_step(w16, cand, alpha, &ls))
+                nvfp4_ref_e4m3_bracket(ls, &dd[0], &dd[1]);
+            else /* every code is zero: every scale reconstructs zero */
+                dd[0] = dd[1] = dc;
+        }
         for (m = 0; m < 2; ++m) {
             quad e = block_err(w16, cand, alpha, nvfp4_ref_e4m3_value(dd[m]));
             if (e < best) {
@@ -372,9 +406,33 @@ int nvfp4_ref_quantize(const void *W, int dtype, int64_t rows, int64_t cols, int
                                  mchoice, dstar, alpha_trace);
 }
 
+static int quantize_impl(const void *W, int dtype, int64_t rows, int64_t cols, int mode, int iters, int init,
+                         const search_cfg *cfg, uint8_t *codes, uint8_t *scales, float *alpha, uint8_t *mchoice,
+                         double *dstar, float *alpha_trace);
+
 int nvfp4_ref_quantize_ex(const void *W, int dtype, int64_t rows, int64_t cols, int mode, int iters, int init,
                           uint8_t *codes, uint8_t *scales, float *alpha, uint8_t *mchoice, double *dstar,
                           float *alpha_trace) {
+    return quantize_impl(W, dtype, rows, cols, mode, iters, init, &pages_search, codes, scales, alpha, mchoice,
+                         dstar, alpha_trace);
+}
+
+int nvfp4_ref_quantize_search(const void *W, int dtype, int64_t rows, int64_t cols, int iters, int init,
+                              int num0, int den, int count, int dd_rule, uint8_t *codes, uint8_t *scales,
+                              float *alpha, double *dstar) {
+    search_cfg cfg;
+    if (bad_search(num0, den, count, dd_rule)) return -1;
+    cfg.num0 = num0;
+    cfg.den = den;
+    cfg.count = count;
+    cfg.dd_rule = dd_rule;
+    return quantize_impl(W, dtype, rows, cols, NVFP4_REF_SOAR, iters, init, &cfg, codes, scales, alpha, NULL,
+                         dstar, NULL);
+}
+
+static int quantize_impl(const void *W, int dtype, int64_t rows, int64_t cols, int mode, int iters, int init,
+                         const search_cfg *cfg, uint8_t *codes, uint8_t *scales, float *alpha, uint8_t *mchoice,
+                         double *dstar, float *alpha_trace) {
     int64_t n, nblk, i;
     float *w, amax = 0.0f;
     uint8_t *c16, *dcode;
@@ -429,7 +487,8 @@ int nvfp4_ref_quantize_ex(const void *W, int dtype, int64_t rows, int64_t cols, 
     } else {
         cjso(w, nblk, iters, init, amax, alpha, dcode, ds, c16, alpha_trace);
         if (mode == NVFP4_REF_SOAR)
-            for (i = 0; i < nblk; ++i) soar_block(w + 16 * i, *alpha, dcode[i], ds[i], c16 + 16 * i, &dcode[i]);
+            for (i = 0; i < nblk; ++i)
+                soar_block(w + 16 * i, *alpha, dcode[i], ds[i], cfg, c16 + 16 * i, &dcode[i]);
         if (dstar) memcpy(dstar, ds, (size_t)nblk * sizeof(double));
     }
     pack_codes(c16, nblk, codes);
@@ -441,9 +500,24 @@ int nvfp4_ref_quantize_ex(const void *W, int dtype, int64_t rows, int64_t cols, 
 int nvfp4_ref_soar_blocks(const void *W, int dtype, int64_t rows, int64_t cols, float alpha,
                           const uint8_t *dcode, const double *dstar, const int64_t *blocks, int64_t nsel,
                           uint8_t *codes_sel, uint8_t *scales_sel) {
+    return nvfp4_ref_soar_blocks_search(W, dtype, rows, cols, alpha, dcode, dstar, blocks, nsel, pages_search.num0,
+                                        pages_search.den, pages_search.count, pages_search.dd_rule, codes_sel,
+                                        scales_sel);
+}
+
+int nvfp4_ref_soar_blocks_search(const void *W, int dtype, int64_t rows, int64_t cols, float alpha,
+                                 const uint8_t *dcode, const double *dstar, const int64_t *blocks, int64_t nsel,
+                                 int num0, int den, int count, int dd_rule, uint8_t *codes_sel,
+                                 uint8_t *scales_sel) {
     int64_t nblk, s;
-    if (!W || !dcode || !dstar || !blocks || !codes_sel || !scales_sel || bad_shape(rows, cols, dtype) || nsel < 0)
+    search_cfg cfg;
+    if (!W || !dcode || !dstar || !blocks || !codes_sel || !scales_sel || bad_shape(rows, cols, dtype) ||
+        nsel < 0 || bad_search(num0, den, count, dd_rule))
         return -1;
+    cfg.num0 = num0;
+    cfg.den = den;
+    cfg.count = count;
+    cfg.dd_rule = dd_rule;
     nblk = rows * cols / 16;
     for (s = 0; s < nsel; ++s) {
         int64_t b = blocks[s];
@@ -460,7 +534,7 @@ int nvfp4_ref_soar_blocks(const void *W, int dtype, int64_t rows, int64_t cols, 
                 memcpy(&w16[j], &u, 4);
             }
         }
-        soar_block(w16, alpha, dcode[b], dstar[b], c16, &scales_sel[s]);
+        soar_block(w16, alpha, dcode[b], dstar[b], &cfg, c16, &scales_sel[s]);
         pack_codes(c16, 1, codes_sel + 8 * s);
     }
     return 0;

@@ -41,12 +41,30 @@ int nvfp4_ref_quantize_ex(const void *W, int dtype, int64_t rows, int64_t cols, 
                           uint8_t *codes, uint8_t *scales, float *alpha, uint8_t *mchoice, double *dstar,
                           float *alpha_trace);
 
+/* Reconstruct-scale rules of the decoupled search (R8, R11): the E4M3 pair bracketing the unrounded
+ * CJSO scale (the pages' rule), the candidate's quantisation scale Delta_q, or the least-squares scale
+ * of the candidate's own codes. */
+enum { NVFP4_REF_DD_CJSO = 0, NVFP4_REF_DD_QUANT = 1, NVFP4_REF_DD_LSQ = 2 };
+
+/* SOAR (mode 3) with a configurable search: multipliers f_k = binary32 nearest (num0 + k)/den for
+ * k = 0..count-1 and reconstruct pairs by dd_rule. (50, 100, 101, NVFP4_REF_DD_CJSO) is the search of
+ * nvfp4_ref_quantize_ex. Returns as nvfp4_ref_quantize_ex, and -1 for a grid outside 1 <= den <= 2^24,
+ * num0 >= 1, 1 <= count <= 1024, (num0 + count - 1) / den <= 16, or an unknown rule. */
+int nvfp4_ref_quantize_search(const void *W, int dtype, int64_t rows, int64_t cols, int iters, int init,
+                              int num0, int den, int count, int dd_rule, uint8_t *codes, uint8_t *scales,
+                              float *alpha, double *dstar);
+
 /* Decoupled-scale search on selected blocks, given the CJSO state of the whole matrix (alpha, the
  * E4M3 block scales dcode[] and the pre-rounding scales dstar[], one per block of the matrix).
  * blocks[] lists nsel block indices; codes_sel is nsel*8 bytes, scales_sel nsel bytes. */
 int nvfp4_ref_soar_blocks(const void *W, int dtype, int64_t rows, int64_t cols, float alpha,
                           const uint8_t *dcode, const double *dstar, const int64_t *blocks, int64_t nsel,
                           uint8_t *codes_sel, uint8_t *scales_sel);
+/* The same with the search of nvfp4_ref_quantize_search. */
+int nvfp4_ref_soar_blocks_search(const void *W, int dtype, int64_t rows, int64_t cols, float alpha,
+                                 const uint8_t *dcode, const double *dstar, const int64_t *blocks, int64_t nsel,
+                                 int num0, int den, int count, int dd_rule, uint8_t *codes_sel,
+                                 uint8_t *scales_sel);
 
 /* Mean squared reconstruction error sum((w - e2m1(code)*e4m3(scale)*alpha)^2)/n of an output triple. */
 /* W4A16 product Y = X * What^T (What = dequantised [N][K] weights), exact products summed in binary128,
@@ -69,6 +87,7 @@ double nvfp4_ref_e4m3_value(unsigned code);
 unsigned nvfp4_ref_e4m3_rne(double v);
 void nvfp4_ref_e4m3_bracket(double v, unsigned *lo, unsigned *hi);
 float nvfp4_ref_search_multiplier(int k);
+float nvfp4_ref_grid_multiplier(int num0, int den, int k);
 void nvfp4_ref_e2m1_codes(const float *x, int64_t n, uint8_t *out);
 void nvfp4_ref_e4m3_rne_many(const double *v, int64_t n, uint8_t *out);
 void nvfp4_ref_quantize_block(const float *w16, float alpha, float delta, uint8_t *codes16);
