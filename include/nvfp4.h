@@ -64,6 +64,15 @@ enum nvfp4_mode {
 
 enum nvfp4_dtype { NVFP4_DTYPE_BF16 = 0, NVFP4_DTYPE_F32 = 1 };
 
+/* How the SOAR search picks each candidate's two E4M3 reconstruct scales Delta_d (SOAR page, decoupled
+ * search: "the two E4M3 values nearest the current value"). CJSO: the pair around the unrounded CJSO
+ * scale, for every candidate (the reading of the page the default search takes). QUANT: the pair
+ * around the candidate's quantisation scale Delta_q. LSQ: the pair around the least-squares scale of
+ * the candidate's own codes (the block-scale step applied to them; a candidate whose codes are all
+ * zero keeps Delta_c). */
+enum nvfp4_dd_rule { NVFP4_DD_CJSO = 0, NVFP4_DD_QUANT = 1, NVFP4_DD_LSQ = 2 };
+#define NVFP4_SEARCH_MAX_COUNT 1024
+
 enum nvfp4_error {
     NVFP4_OK = 0,
     NVFP4_ERR_INVALID_ARG = -1, /* null or misaligned pointer, rows/cols <= 0, unknown mode or dtype,
@@ -115,6 +124,13 @@ typedef struct nvfp4_args {
                                   `stream`; NULL entries are skipped (fewer records, smaller gaps) */
     int n_stage_events;
     unsigned flags; /* NVFP4_FLAG_* bits (0 for the defaults) */
+    /* SOAR search grid (mode 3; all three 0 elsewhere and for the page's grid, f_k = (50 + k)/100 for
+     * k = 0..100): multipliers f_k = the binary32 value nearest (search_num0 + k) / search_den for
+     * k < search_count, with 1 <= search_den <= 2^24, search_num0 >= 1,
+     * 1 <= search_count <= NVFP4_SEARCH_MAX_COUNT and search_num0 + search_count - 1 <= 16 * search_den
+     * (multipliers at most 16). Any other setting is NVFP4_ERR_INVALID_ARG. */
+    int search_num0, search_den, search_count;
+    int dd_rule; /* enum nvfp4_dd_rule (mode 3; 0 elsewhere). QUANT and LSQ scan every multiplier. */
 } nvfp4_args_t;
 
 /* SOAR: visit all 202 candidates of every block. Without it the search evaluates, per reconstruct

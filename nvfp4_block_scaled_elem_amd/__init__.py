@@ -24,6 +24,8 @@ DTYPES = {torch.bfloat16: 0, torch.float32: 1}
 FLAG_FULL_SEARCH = 1  # NVFP4_FLAG_FULL_SEARCH
 FLAG_INIT_4O6 = 2  # NVFP4_FLAG_INIT_4O6
 INITS = {"max": 0, "4o6": FLAG_INIT_4O6}
+DD_RULES = {"cjso": 0, "quant": 1, "lsq": 2}  # enum nvfp4_dd_rule
+SEARCH_MAX_COUNT = 1024
 STATUS_NONFINITE = 1
 
 
@@ -38,7 +40,8 @@ class _Args(ctypes.Structure):
         ("scales_out", ctypes.c_void_p), ("alpha_out", ctypes.c_void_p), ("mchoice_out", ctypes.c_void_p),
         ("stats_out", ctypes.c_void_p), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
         ("stream", ctypes.c_void_p), ("stage_events", ctypes.c_void_p), ("n_stage_events", ctypes.c_int),
-        ("flags", ctypes.c_uint),
+        ("flags", ctypes.c_uint), ("search_num0", ctypes.c_int), ("search_den", ctypes.c_int),
+        ("search_count", ctypes.c_int), ("dd_rule", ctypes.c_int),
     ]
 
 
@@ -102,14 +105,17 @@ def _stream_ptr(stream, device) -> int:
 
 def quantize(W: torch.Tensor, mode: str, iters: int = 0, *, codes=None, scales=None, alpha=None,
              mchoice=None, stats=None, workspace=None, stream=None, stage_events=None, full_search=False,
-             init="max"):
+             init="max", grid=None, dd_rule="cjso"):
     """Quantise ``W`` ([rows, cols] bf16/fp32 CUDA tensor). Returns (codes [rows, cols//2] uint8,
     scales [rows, cols//16] uint8 E4M3 bits, alpha [1] float32), all on W's device. Optional
     preallocated outputs, an ``mchoice`` uint8 [rows, cols//16] tensor (FourOverSix), a ``stats``
     int32 [4] tensor, a uint8 ``workspace`` tensor, a ``stream`` and a list of
     ``torch.cuda.Event(enable_timing=True)`` stage events (None entries are skipped) may be passed. ``full_search`` makes the
     SOAR search visit all 202 candidates of every block (same outputs; NVFP4_FLAG_FULL_SEARCH); ``init``
-    is CJSO's starting point, "max" or "4o6" (NVFP4_FLAG_INIT_4O6; modes cjso and soar)."""
+    is CJSO's starting point, "max" or "4o6" (NVFP4_FLAG_INIT_4O6; modes cjso and soar). For mode soar,
+    ``grid`` = (num0, den, count) sets the search multipliers (nearest binary32 of (num0 + k)/den,
+    k < count; None for the page's 50, 100, 101) and ``dd_rule`` ("cjso", "quant" or "lsq") the rule
+    for each candidate's reconstruct scales."""
     if W.dim() != 2 or not W.is_cuda or not W.is_contiguous() or W.dtype not in DTYPES:
         raise NVFP4Error("W must be a contiguous 2-D bf16 or fp32 CUDA tensor")
     rows, cols = W.shape
@@ -143,6 +149,11 @@ def quantize(W: torch.Tensor, mode: str, iters: int = 0, *, codes=None, scales=N
     if init not in INITS:
         raise NVFP4Error(f"unknown init {init!r}")
     a.flags = (FLAG_FULL_SEARCH if full_search else 0) | INITS[init]
+    if dd_rule not in DD_RULES:
+        raise NVFP4Error(f"unknown dd_rule {dd_rule!r}")
+    a.dd_rule = DD_RULES[dd_rule]
+    if grid is not None:
+        a.search_num0, a.search_den, a.search_count = (int(v) for v in grid)
     ev_arr = None
     if stage_events is not None:
         for e in stage_events:  # torch creates the HIP event at its first record

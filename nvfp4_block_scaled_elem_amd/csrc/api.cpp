@@ -44,6 +44,16 @@ int check(const nvfp4_args_t *a) {
     if (a->flags & ~(NVFP4_FLAG_FULL_SEARCH | NVFP4_FLAG_INIT_4O6)) return NVFP4_ERR_INVALID_ARG;
     if ((a->flags & NVFP4_FLAG_INIT_4O6) && a->mode != NVFP4_MODE_CJSO && a->mode != NVFP4_MODE_SOAR)
         return NVFP4_ERR_INVALID_ARG;
+    const bool pages_grid = a->search_num0 == 0 && a->search_den == 0 && a->search_count == 0;
+    if (!pages_grid || a->dd_rule != NVFP4_DD_CJSO) {
+        if (a->mode != NVFP4_MODE_SOAR) return NVFP4_ERR_INVALID_ARG;
+        if (a->dd_rule < NVFP4_DD_CJSO || a->dd_rule > NVFP4_DD_LSQ) return NVFP4_ERR_INVALID_ARG;
+        if (!pages_grid &&
+            (a->search_den < 1 || a->search_den > (1 << 24) || a->search_num0 < 1 || a->search_count < 1 ||
+             a->search_count > NVFP4_SEARCH_MAX_COUNT ||
+             (int64_t)a->search_num0 + a->search_count - 1 > 16 * (int64_t)a->search_den))
+            return NVFP4_ERR_INVALID_ARG;
+    }
     return NVFP4_OK;
 }
 
@@ -85,10 +95,15 @@ int run(const nvfp4_args_t *a, void *ws_base) {
                              st) != hipSuccess ||
             !mark(a, j++))
             return NVFP4_ERR_HIP;
-    if (soar && (launch_soar(a->W, f32, nblk, ws.alpha_state + (a->iters & 1), a->codes_out, a->scales_out,
-                             ws.brackets, (a->flags & NVFP4_FLAG_FULL_SEARCH) != 0, st) != hipSuccess ||
-                 !mark(a, j++)))
-        return NVFP4_ERR_HIP;
+    if (soar) {
+        const bool pages_grid = a->search_count == 0;
+        if (launch_soar(a->W, f32, nblk, ws.alpha_state + (a->iters & 1), a->codes_out, a->scales_out, ws.brackets,
+                        (a->flags & NVFP4_FLAG_FULL_SEARCH) != 0, pages_grid ? 50 : a->search_num0,
+                        pages_grid ? 100 : a->search_den, pages_grid ? 101 : a->search_count, a->dd_rule,
+                        st) != hipSuccess ||
+            !mark(a, j++))
+            return NVFP4_ERR_HIP;
+    }
     return NVFP4_OK;
 }
 

@@ -70,7 +70,8 @@ hipError_t launch_cjso_init(const void *W, bool f32, bool soar, bool fos, int64_
 hipError_t launch_cjso_iter(const void *W, bool f32, bool soar, int64_t nblk, int t, int iters, uint8_t *codes,
                             uint8_t *scales, float *alpha_out, const Workspace &ws, int groups, hipStream_t stream);
 hipError_t launch_soar(const void *W, bool f32, int64_t nblk, const float *alpha, uint8_t *codes, uint8_t *scales,
-                       const uint16_t *brackets, bool full_search, hipStream_t stream);
+                       const uint16_t *brackets, bool full_search, int num0, int den, int count, int rule,
+                       hipStream_t stream);
 hipError_t launch_encode_e2m1(const float *x, int64_t n, uint8_t *codes, hipStream_t stream);
 hipError_t launch_w4a16(const uint16_t *X, int64_t M, int64_t K, const uint8_t *codes, const uint8_t *scales,
                         const float *alpha, int64_t N, void *Y, bool out_f32, hipStream_t stream);

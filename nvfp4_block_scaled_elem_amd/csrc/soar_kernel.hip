@@ -2,32 +2,36 @@
 // Scale Optimization for Accurate Reconstruction in NVFP4 Quantization", decoupled search).
 //
 // Per block: the CJSO scale Delta_c (E4M3) and the E4M3 pair {lo, hi} around its unrounded value are
-// given. Candidates are Delta_q = fl(Delta_c * f_k), f_k the binary32 value nearest (50+k)/100,
-// k = 0..100 (quantise), times Delta_d in {lo, hi} (reconstruct): 202 candidates. The CJSO point
-// (k = 50, Delta_d = Delta_c) is the incumbent; candidates are visited k = 0..100, lo before hi, and
-// replace it only when their squared error is strictly smaller.
+// given. Candidates are Delta_q = fl(Delta_c * f_k) (quantise), f_k the binary32 value nearest
+// (num0 + k) / den for k < count (the page's grid: 50, 100, 101, i.e. 0.50 .. 1.50 in steps of 0.01),
+// each against two reconstruct scales Delta_d. The page's rule takes {lo, hi} for every candidate;
+// two variants take the E4M3 pair around the candidate's own Delta_q, or around the least-squares scale
+// of the candidate's codes. The CJSO point (Delta_q = Delta_d = Delta_c) is the incumbent; candidates
+// are visited in k order, the lower Delta_d first, and replace it only when their squared error is
+// strictly smaller.
 //
 // Error of candidate (k, d): sum w^2 + 2 s_d A_d(k), A_d(k) = (s_d/2) S_qq(k) - S_wq(k), with
 // s_d = alpha * Delta_d and S_qq, S_wq the sums of q^2 and |w| q over the block's code magnitudes q at
 // quantisation scale s_k = fl(alpha * Delta_q(k)).
 //
-// Exact search on a window. A_d(k) = sum_j psi_j(q_j(k)) with psi_j(m) = (s_d/2) m^2 - |w_j| m, a convex
-// function of m whose minimisers over the E2M1 grid are the grid points nearest |w_j| / s_d. Each
-// magnitude q_j(k) is non-increasing in k (s_k grows with k, so fl(w_j * fl(1/s_k)) shrinks, and E2M1
-// rounding is monotone). Hence, for every j:
+// Exact search on a window (the page's rule, where Delta_d does not depend on k). A_d(k) =
+// sum_j psi_j(q_j(k)) with psi_j(m) = (s_d/2) m^2 - |w_j| m, a convex function of m whose minimisers
+// over the E2M1 grid are the grid points nearest |w_j| / s_d. Each magnitude q_j(k) is non-increasing
+// in k (the multipliers increase with k, so s_k does not decrease, fl(w_j * fl(1/s_k)) does not grow,
+// and E2M1 rounding is monotone). Hence, for every j:
 //   * while s_k < s_d (1 - 2^-20) the computed |x_j| = fl(|w_j| / s_k) exceeds |w_j| / s_d, so q_j(k)
 //     is at or above every nearest grid point and psi_j(q_j(k)) does not increase with k;
 //   * while s_k > s_d (1 + 2^-20) q_j(k) is at or below every nearest grid point and psi_j(q_j(k))
 //     does not decrease with k.
 // (The margin covers the two binary32 roundings of r = fl(1/s_k) and x = fl(w r), 2^-24 each.) With
 // K1 the last k of the first kind and K2 the first of the second, A_d does not increase on [0, K1]
-// and does not decrease on [K2, 100], so its minimum lies in [K1, K2], which holds two or three k
-// (s_k moves by about 1 % per step). The first minimiser in k order is the window's first minimiser,
-// unless that is K1 itself: then every k < K1 with A_d(k) = A_d(K1) has exactly the same codes (a
-// larger magnitude strictly raises psi_j there), so it only matters when the two reconstruct scales
-// tie exactly, and that rare case walks down to the first k with the codes of K1.
-// The full 101-step scan remains for blocks outside the exactness window of the binary32 sums or of
-// binary64 A_d, and for fp32 input.
+// and does not decrease on [K2, count), so its minimum lies in [K1, K2], which holds two or three k on
+// the page's grid (s_k moves by about 1 % per step). The first minimiser in k order is the window's
+// first minimiser, unless that is K1 itself: then every k < K1 with A_d(k) = A_d(K1) has exactly the same
+// codes (a larger magnitude strictly raises psi_j there), so it only matters when the two reconstruct
+// scales tie exactly, and that rare case walks down to the first k with the codes of K1.
+// The full scan over k remains for blocks outside the exactness window of the binary32 sums or of
+// binary64 A_d, for fp32 input, and for the two variant rules.
 #include <float.h>
 
 #include "block.hpp"
@@ -36,7 +40,12 @@
 namespace nvfp4 {
 
 constexpr int kSoarThreads = 256;
-constexpr int kSoarK = 101;
+constexpr int kMaxGrid = 1024;  // multipliers per search (NVFP4_SEARCH_MAX_COUNT)
+
+struct SearchCfg {
+    int num0, den, count;  // f_k = binary32 nearest (num0 + k) / den, k < count
+    int rule;              // NVFP4_DD_*
+};
 
 // s_k = fl(alpha * fl(Delta_c * f_k)) and its reciprocal (0 for a zero scale: every code is then 0).
 __device__ __forceinline__ float quant_scale(float alpha, float vc, const float *ftab, int k) {
@@ -66,14 +75,14 @@ __device__ __forceinline__ void block_sums_k(const Blk<F32> &B, float r, bool rf
 
 // Full scan: first minimum over k of A_d(k) for d = lo and hi.
 template <bool F32, bool FAST>
-__device__ __forceinline__ void scan(const Blk<F32> &B, const float *__restrict__ ftab, float alpha, float vc,
-                                     bool rfin, double hlo, double hhi, double &best_lo, int &k_lo, double &best_hi,
-                                     int &k_hi) {
+__device__ __forceinline__ void scan(const Blk<F32> &B, const float *__restrict__ ftab, int count, float alpha,
+                                     float vc, bool rfin, double hlo, double hhi, double &best_lo, int &k_lo,
+                                     double &best_hi, int &k_hi) {
     best_lo = INFINITY;
     best_hi = INFINITY;
     k_lo = 0;
     k_hi = 0;
-    for (int k = 0; k < kSoarK; ++k) {
+    for (int k = 0; k < count; ++k) {
         double sw = 0.0, sq = 0.0;
         block_sums_k<F32, FAST>(B, recip(quant_scale(alpha, vc, ftab, k)), rfin, sw, sq);
         const double alo = fma(hlo, sq, -sw);
@@ -89,32 +98,43 @@ __device__ __forceinline__ void scan(const Blk<F32> &B, const float *__restrict_
     }
 }
 
-// A_d at quantisation scale index k (bf16 block inside the exactness window), with its codes.
-__device__ __forceinline__ double eval_k(const Blk<false> &B, float alpha, float vc, const float *ftab, int k,
-                                         double h, uint32_t &c0, uint32_t &c1) {
-    encode16(B.w, 1.0f / quant_scale(alpha, vc, ftab, k), c0, c1);
+// A_d at quantisation scale s (bf16 block inside the exactness window), with its codes.
+__device__ __forceinline__ double eval_s(const Blk<false> &B, float s, double h, uint32_t &c0, uint32_t &c1) {
+    encode16(B.w, 1.0f / s, c0, c1);
     float sw, sq;
     sums_bf16(c0, c1, B.p, sw, sq);
     return fma(h, (double)sq, -(double)sw);
 }
 
-// The window [kA, kB] for reconstruct scale s_d (exact in binary64): kA = max(K1, 0), kB = min(K2, 100)
-// with K1 the last k with s_d > s_k (1 + 2^-20) (-1 if none) and K2 the first k with
-// s_d < s_k (1 - 2^-20) (101 if none). Both products are exact in binary64. The search starts from the
-// k where s_k would equal s_d and walks to the exact bounds.
-__device__ __forceinline__ void window(float alpha, float vc, float vd, double sd, const float *ftab, int &kA,
-                                       int &kB) {
+__device__ __forceinline__ double eval_k(const Blk<false> &B, float alpha, float vc, const float *ftab, int k,
+                                         double h, uint32_t &c0, uint32_t &c1) {
+    return eval_s(B, quant_scale(alpha, vc, ftab, k), h, c0, c1);
+}
+
+// The window [kA, kB] for reconstruct scale s_d (exact in binary64): kA = max(K1, 0),
+// kB = min(K2, count - 1) with K1 the last k with s_d > s_k (1 + 2^-20) (-1 if none) and K2 the first k
+// with s_d < s_k (1 - 2^-20) (count if none). Both products are exact in binary64. The search starts
+// near the k where s_k would equal s_d and walks to the exact bounds.
+// The grid's constants for the window's starting guess: last index, den and num0 as binary32.
+struct GridGuess {
+    int last;
+    float den, num0;
+};
+
+__device__ __forceinline__ void window(float alpha, float vc, float vd, double sd, const float *ftab,
+                                       const GridGuess &g, int &kA, int &kB) {
     const double up = 1.0 + 0x1p-20, dn = 1.0 - 0x1p-20;
+    const int last = g.last;
     auto below = [&](int k) { return sd > (double)quant_scale(alpha, vc, ftab, k) * up; };
     auto above = [&](int k) { return sd < (double)quant_scale(alpha, vc, ftab, k) * dn; };
-    int k1 = (int)floorf(100.0f * (vd * __builtin_amdgcn_rcpf(vc))) - 50;
-    k1 = k1 < -1 ? -1 : (k1 > 100 ? 100 : k1);
-    while (k1 < 100 && below(k1 + 1)) ++k1;
+    const float guess = floorf(g.den * (vd * __builtin_amdgcn_rcpf(vc))) - g.num0;
+    int k1 = guess < -1.0f ? -1 : (guess > (float)last ? last : (int)guess);
+    while (k1 < last && below(k1 + 1)) ++k1;
     while (k1 >= 0 && !below(k1)) --k1;
     int k2 = k1 + 1;
-    while (k2 <= 100 && !above(k2)) ++k2;
+    while (k2 <= last && !above(k2)) ++k2;
     kA = k1 > 0 ? k1 : 0;
-    kB = k2 < 100 ? k2 : 100;
+    kB = k2 < last ? k2 : last;
 }
 
 // First k <= kA whose codes equal those at kA (the start of A_d's plateau ending at kA).
@@ -137,30 +157,101 @@ struct Pick {
     uint32_t c0, c1;
 };
 
+// The variant rules: every candidate k brings its own reconstruct pair, so the whole grid is scanned.
+// Errors are compared through J = s_d * A_d (exact double-double products of binary64 values); the
+// current best starts as the incumbent's.
 template <bool F32>
+__device__ __forceinline__ void scan_rule(const Blk<F32> &B, const float *__restrict__ ftab, const SearchCfg &g,
+                                          float alpha, float vc, uint32_t dc, bool fast, bool rfin, dd &best,
+                                          uint32_t &db, float &sb) {
+    for (int k = 0; k < g.count; ++k) {
+        const float dq = vc * ftab[k];
+        const float sk = alpha * dq;
+        double sw = 0.0, sq = 0.0;
+        if (fast)
+            block_sums_k<F32, true>(B, recip(sk), rfin, sw, sq);
+        else
+            block_sums_k<F32, false>(B, recip(sk), rfin, sw, sq);
+        uint32_t lo, hi;
+        if (g.rule == NVFP4_DD_QUANT) {
+            e4m3_bracket((double)dq, lo, hi);
+        } else if (sq > 0.0) {  // NVFP4_DD_LSQ: the block-scale step's quotient for these codes
+            e4m3_bracket(sw / ((double)alpha * sq), lo, hi);
+        } else {  // every code is zero: every scale reconstructs zero
+            lo = hi = dc;
+        }
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const uint32_t d = m ? hi : lo;
+            const double sd = (double)alpha * (double)e4m3_value(d);
+            const dd j = two_prod(sd, fma(0.5 * sd, sq, -sw));
+            if (dd_less(j, best)) {
+                best = j;
+                db = d;
+                sb = sk;
+            }
+        }
+    }
+}
+
+// Instantiations: the page's search (its grid as constants), another grid with the page's rule, and the
+// variant reconstruct-pair rules. Separate instantiations keep the page's search compact.
+enum SearchKind { kPagesSearch = 0, kGridSearch = 1, kRuleSearch = 2 };
+
+template <bool F32, int KIND>
 __global__ __launch_bounds__(kSoarThreads) void k_soar(const void *__restrict__ W, int64_t nblk,
                                                        const float *__restrict__ alpha_p, uint8_t *__restrict__ codes,
                                                        uint8_t *__restrict__ scales,
-                                                       const uint16_t *__restrict__ brackets, bool full_search) {
-    __shared__ float ftab[kSoarK];
+                                                       const uint16_t *__restrict__ brackets, bool full_search,
+                                                       SearchCfg g) {
+    constexpr bool RULES = KIND == kRuleSearch;
+    if constexpr (KIND == kPagesSearch) g = SearchCfg{50, 100, 101, NVFP4_DD_CJSO};
+    __shared__ float ftab[kMaxGrid];
     const float alpha = *alpha_p;
     if (alpha != alpha) return;  // non-finite input: outputs already zero
-    if (threadIdx.x < kSoarK) ftab[threadIdx.x] = (float)((double)(50 + threadIdx.x) / 100.0);
+    for (int i = threadIdx.x; i < g.count; i += kSoarThreads)
+        ftab[i] = (float)((double)(g.num0 + i) / (double)g.den);
     __syncthreads();
 
     const int64_t b = (int64_t)blockIdx.x * kSoarThreads + threadIdx.x;
     if (b >= nblk) return;
     const uint32_t dc = scales[b];
     if (dc == 0u) return;  // Delta_c = 0: every candidate quantises to 0 and ties; codes and scale stay 0
-    const uint32_t br = brackets[b];
-    const uint32_t lo = br & 0xFFu, hi = br >> 8;
     Blk<F32> B;
     B.load(W, b);
     const float a = B.amax();
     const float vc = e4m3_value(dc);
-    const float r0 = recip(quant_scale(alpha, vc, ftab, 0));
-    const bool rfin = finite_pos(r0);  // s grows with k, so r_0 bounds every reciprocal
-    const float smin = quant_scale(alpha, vc, ftab, 0);
+    const float sc = alpha * vc;  // the incumbent's quantisation scale (Delta_q = Delta_c)
+    // the smallest quantisation scale of the search: the multipliers increase with k
+    const float smin = fminf(quant_scale(alpha, vc, ftab, 0), sc);
+    const bool rfin = finite_pos(recip(smin));  // bounds every reciprocal
+    uint32_t c0, c1;  // codes of the chosen candidate
+    uint32_t db;
+
+    if constexpr (RULES) {
+        const bool fast = !F32 && rfin && a <= 32.0f * smin && a <= 0x1p100f;
+        const double sdc = (double)alpha * (double)vc;
+        double sw, sq;
+        if (fast)
+            block_sums_k<F32, true>(B, recip(sc), rfin, sw, sq);
+        else
+            block_sums_k<F32, false>(B, recip(sc), rfin, sw, sq);
+        dd best = two_prod(sdc, fma(0.5 * sdc, sq, -sw));
+        float sb = sc;
+        db = dc;
+        scan_rule<F32>(B, ftab, g, alpha, vc, dc, fast, rfin, best, db, sb);
+        const float r = recip(sb);
+        if (rfin)
+            encode16(B.w, r, c0, c1);
+        else
+            encode16_soft(B.w, r, c0, c1);
+        *reinterpret_cast<uint2 *>(codes + 8 * b) = make_uint2(e2m1_clear_negzero(c0), e2m1_clear_negzero(c1));
+        scales[b] = (uint8_t)db;
+        return;
+    } else {
+
+    const uint32_t br = brackets[b];
+    const uint32_t lo = br & 0xFFu, hi = br >> 8;
     // s_d = alpha * Delta_d exactly; errors are compared through s_d * A_d
     const float vlo = e4m3_value(lo), vhi = e4m3_value(hi);
     const double slo = (double)alpha * (double)vlo;
@@ -169,9 +260,6 @@ __global__ __launch_bounds__(kSoarThreads) void k_soar(const void *__restrict__ 
     const bool c_is_lo = dc == lo;
     double best_lo, best_hi, a_c;
     int k_lo, k_hi;
-    uint32_t c0, c1;  // codes of the chosen candidate
-    int kb;
-    uint32_t db;
 
     bool windowed = false;
     if constexpr (!F32) {
@@ -183,33 +271,33 @@ __global__ __launch_bounds__(kSoarThreads) void k_soar(const void *__restrict__ 
     }
     if constexpr (!F32) {
         if (windowed) {
-            // own window (d = Delta_c) always holds k = 50, the incumbent; the other scale's window is
-            // evaluated in full
+            // the incumbent, then the first minimiser of A_d in each reconstruct scale's window
             const double sd_c = c_is_lo ? slo : shi, h_c = c_is_lo ? hlo : hhi;
+            uint32_t i0, i1;
+            a_c = eval_s(B, sc, h_c, i0, i1);
+            // own window (d = Delta_c) first, then the other scale's
             const float vo = c_is_lo ? vhi : vlo;
             const double sd_o = c_is_lo ? shi : slo, h_o = c_is_lo ? hhi : hlo;
-            uint32_t i0, i1;
-            a_c = eval_k(B, alpha, vc, ftab, 50, h_c, i0, i1);
             Pick pc, po;
             int kA, kB;
-            window(alpha, vc, vc, sd_c, ftab, kA, kB);
-            pc.a = a_c;
-            pc.k = 50;
+            const GridGuess gg{g.count - 1, (float)g.den, (float)g.num0};
+            window(alpha, vc, vc, sd_c, ftab, gg, kA, kB);
+            pc.a = INFINITY;
+            pc.k = kA;
             pc.kA = kA;
-            pc.c0 = i0;
-            pc.c1 = i1;
+            pc.c0 = pc.c1 = 0u;
             for (int k = kA; k <= kB; ++k) {
-                if (k == 50) continue;
-                uint32_t d0, d1;
-                const double v = eval_k(B, alpha, vc, ftab, k, h_c, d0, d1);
-                if (v < pc.a || (v == pc.a && k < pc.k)) {
+                uint32_t d0 = i0, d1 = i1;
+                // a multiplier of exactly 1 reproduces the incumbent
+                const double v = quant_scale(alpha, vc, ftab, k) == sc ? a_c : eval_k(B, alpha, vc, ftab, k, h_c, d0, d1);
+                if (v < pc.a) {
                     pc.a = v;
                     pc.k = k;
                     pc.c0 = d0;
                     pc.c1 = d1;
                 }
             }
-            window(alpha, vc, vo, sd_o, ftab, kA, kB);
+            window(alpha, vc, vo, sd_o, ftab, gg, kA, kB);
             po.a = INFINITY;
             po.k = kA;
             po.kA = kA;
@@ -230,7 +318,7 @@ __global__ __launch_bounds__(kSoarThreads) void k_soar(const void *__restrict__ 
             const dd jlo = two_prod(slo, pl.a);
             const dd jhi = two_prod(shi, ph.a);
             const dd jmin = dd_less(jhi, jlo) ? jhi : jlo;
-            if (dd_equal(jc, jmin)) {
+            if (!dd_less(jmin, jc)) {  // no candidate is strictly better than the incumbent
                 db = dc;
                 c0 = i0;
                 c1 = i1;
@@ -259,18 +347,18 @@ __global__ __launch_bounds__(kSoarThreads) void k_soar(const void *__restrict__ 
     }
 
     // full scan
-    double sw50, sq50;
-    const float r50 = recip(quant_scale(alpha, vc, ftab, 50));
+    double swc, sqc;
+    const float rc = recip(sc);
     const bool fast = !F32 && rfin && a <= 32.0f * smin && a <= 0x1p100f;
     if (fast) {
-        scan<F32, true>(B, ftab, alpha, vc, rfin, hlo, hhi, best_lo, k_lo, best_hi, k_hi);
-        block_sums_k<F32, true>(B, r50, rfin, sw50, sq50);
+        scan<F32, true>(B, ftab, g.count, alpha, vc, rfin, hlo, hhi, best_lo, k_lo, best_hi, k_hi);
+        block_sums_k<F32, true>(B, rc, rfin, swc, sqc);
     } else {
-        scan<F32, false>(B, ftab, alpha, vc, rfin, hlo, hhi, best_lo, k_lo, best_hi, k_hi);
-        block_sums_k<F32, false>(B, r50, rfin, sw50, sq50);
+        scan<F32, false>(B, ftab, g.count, alpha, vc, rfin, hlo, hhi, best_lo, k_lo, best_hi, k_hi);
+        block_sums_k<F32, false>(B, rc, rfin, swc, sqc);
     }
-    // the incumbent: Delta_q = Delta_c * f_50 = Delta_c, Delta_d = Delta_c
-    a_c = fma(c_is_lo ? hlo : hhi, sq50, -sw50);
+    // the incumbent: Delta_q = Delta_d = Delta_c
+    a_c = fma(c_is_lo ? hlo : hhi, sqc, -swc);
     // a zero reconstruction scale makes every candidate's error sum w^2: the first one (k = 0) stands
     if (slo == 0.0) {
         best_lo = 0.0;
@@ -284,40 +372,50 @@ __global__ __launch_bounds__(kSoarThreads) void k_soar(const void *__restrict__ 
     const dd jlo = two_prod(slo, best_lo);
     const dd jhi = two_prod(shi, best_hi);
     const dd jmin = dd_less(jhi, jlo) ? jhi : jlo;
-    if (dd_equal(jc, jmin)) {
-        kb = 50;
+    float sb;
+    if (!dd_less(jmin, jc)) {
+        sb = sc;
         db = dc;
-    } else if (dd_less(jlo, jhi)) {
-        kb = k_lo;
-        db = lo;
-    } else if (dd_less(jhi, jlo)) {
-        kb = k_hi;
-        db = hi;
-    } else if (k_lo <= k_hi) {
-        kb = k_lo;
+    } else if (dd_less(jlo, jhi) || (!dd_less(jhi, jlo) && k_lo <= k_hi)) {
+        sb = quant_scale(alpha, vc, ftab, k_lo);
         db = lo;
     } else {
-        kb = k_hi;
+        sb = quant_scale(alpha, vc, ftab, k_hi);
         db = hi;
     }
-    const float r = recip(quant_scale(alpha, vc, ftab, kb));
+    const float r = recip(sb);
     if (rfin)
         encode16(B.w, r, c0, c1);
     else
         encode16_soft(B.w, r, c0, c1);
     *reinterpret_cast<uint2 *>(codes + 8 * b) = make_uint2(e2m1_clear_negzero(c0), e2m1_clear_negzero(c1));
     scales[b] = (uint8_t)db;
+    }
 }
 
 hipError_t launch_soar(const void *W, bool f32, int64_t nblk, const float *alpha, uint8_t *codes, uint8_t *scales,
-                       const uint16_t *brackets, bool full_search, hipStream_t stream) {
+                       const uint16_t *brackets, bool full_search, int num0, int den, int count, int rule,
+                       hipStream_t stream) {
+    if (count < 1 || count > kMaxGrid) return hipErrorInvalidValue;
+    const SearchCfg g{num0, den, count, rule};
     const dim3 grid((unsigned)((nblk + kSoarThreads - 1) / kSoarThreads)), block(kSoarThreads);
+    const int kind = rule != NVFP4_DD_CJSO                          ? kRuleSearch
+                     : (num0 == 50 && den == 100 && count == 101) ? kPagesSearch
+                                                                  : kGridSearch;
+#define NVFP4_SOAR(F, KIND) \
+    hipLaunchKernelGGL((k_soar<F, KIND>), grid, block, 0, stream, W, nblk, alpha, codes, scales, brackets, full_search, g)
+#define NVFP4_SOAR_KIND(F)                                  \
+    do {                                                    \
+        if (kind == kRuleSearch) NVFP4_SOAR(F, kRuleSearch); \
+        else if (kind == kGridSearch) NVFP4_SOAR(F, kGridSearch); \
+        else NVFP4_SOAR(F, kPagesSearch);                   \
+    } while (0)
     if (f32)
-        hipLaunchKernelGGL(k_soar<true>, grid, block, 0, stream, W, nblk, alpha, codes, scales, brackets,
-                           full_search);
+        NVFP4_SOAR_KIND(true);
     else
-        hipLaunchKernelGGL(k_soar<false>, grid, block, 0, stream, W, nblk, alpha, codes, scales, brackets,
-                           full_search);
+        NVFP4_SOAR_KIND(false);
+#undef NVFP4_SOAR_KIND
+#undef NVFP4_SOAR
     return hipGetLastError();
 }
 

@@ -6,9 +6,12 @@ about two), too slow for a test, so this script runs it once and stores:
   * full_size.json: per workload, the SHA-256 of the input bytes, and per mode alpha (binary32 bits),
     the SHA-256 of the codes and of the scales, the FourOverSix M=4 block count and the MSE;
   * <workload>_soar_sample.npz: for the SOAR search, the expected codes and scales of a fixed sample of
-    blocks (the oracle runs the search block by block from its own CJSO state).
+    blocks (the oracle runs the search block by block from its own CJSO state), and for the workloads
+    in SEARCH_VARIANTS the same for other search grids and reconstruct-pair rules (keys
+    <variant>_codes, <variant>_scales).
 
-Run from the repository root:  python tests/golden/make_golden.py  [-j 8]
+Run from the repository root:  python tests/golden/make_golden.py  [-j 8] [--only c2:soar ...]
+(--only reruns the named jobs and keeps the other entries of full_size.json.)
 """
 from __future__ import annotations
 
@@ -54,6 +57,13 @@ PLAN = {
 }
 
 
+# search variants stored beside the page's search: name -> ((num0, den, count), reconstruct-pair rule)
+SEARCH_VARIANTS = {
+    "c2": {"fine_lsq": ((100, 200, 201), "lsq"), "coarse_quant": ((1, 4, 7), "quant"),
+           "wide_cjso": ((1, 20, 60), "cjso")},
+}
+
+
 def sha(a: np.ndarray) -> str:
     return hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()
 
@@ -85,9 +95,16 @@ def job(name: str, mode: str):
         blocks = sample_blocks(r["scales"].size)
         c, s = oracle.soar_blocks(W, r["alpha"], r["scales"], r["dstar"], blocks)
         fname = f"{name}_soar_sample.npz"
-        np.savez_compressed(os.path.join(HERE, fname), blocks=blocks, codes=c, scales=s)
+        extra, variants = {}, {}
+        for vname, (grid, rule) in SEARCH_VARIANTS.get(name, {}).items():
+            vc, vs = oracle.soar_blocks(W, r["alpha"], r["scales"], r["dstar"], blocks, grid=grid, dd_rule=rule)
+            extra[f"{vname}_codes"], extra[f"{vname}_scales"] = vc, vs
+            variants[vname] = {"grid": list(grid), "dd_rule": rule, "codes": sha(vc), "scales": sha(vs)}
+        np.savez_compressed(os.path.join(HERE, fname), blocks=blocks, codes=c, scales=s, **extra)
         out.update(alpha=f32_hex(r["alpha"]), sample=fname, sample_codes=sha(c), sample_scales=sha(s),
                    iters=ITERS)
+        if variants:
+            out["search_variants"] = variants
     if mode == "cjso":
         out["iters"] = ITERS
     return name, mode, out
@@ -96,9 +113,14 @@ def job(name: str, mode: str):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("-j", type=int, default=4)
+    ap.add_argument("--only", nargs="*", default=None, help="jobs as workload:mode")
     args = ap.parse_args()
     jobs = [(n, m) for n, modes in PLAN.items() for m in modes]
     result = {}
+    if args.only:
+        jobs = [j for j in jobs if f"{j[0]}:{j[1]}" in args.only]
+        with open(os.path.join(HERE, "full_size.json")) as f:
+            result = json.load(f)
     with ProcessPoolExecutor(max_workers=args.j) as ex:
         for name, mode, out in ex.map(job, *zip(*jobs)):
             result.setdefault(name, {"modes": {}})

@@ -57,6 +57,18 @@ def args(**kw):
     (dict(mode=3, iters=8, workspace=FAKE, workspace_bytes=1024), WORKSPACE),
     (dict(flags=4), INVALID), (dict(flags=0x80000000), INVALID), (dict(flags=2, mode=0), INVALID),
     (dict(flags=2, mode=1), INVALID),
+    # search settings: SOAR only, valid grids and rules only (a valid one reaches the workspace check)
+    (dict(mode=2, dd_rule=1), INVALID), (dict(mode=2, search_num0=1, search_den=2, search_count=3), INVALID),
+    (dict(mode=3, dd_rule=3), INVALID), (dict(mode=3, dd_rule=-1), INVALID),
+    (dict(mode=3, search_num0=0, search_den=100, search_count=101), INVALID),
+    (dict(mode=3, search_num0=50, search_den=0, search_count=101), INVALID),
+    (dict(mode=3, search_num0=50, search_den=100, search_count=0), INVALID),
+    (dict(mode=3, search_num0=50, search_den=100, search_count=1025), INVALID),
+    (dict(mode=3, search_num0=1, search_den=1, search_count=17), INVALID),
+    (dict(mode=3, search_num0=1, search_den=(1 << 24) + 1, search_count=1), INVALID),
+    (dict(mode=3, search_num0=1, search_den=2, search_count=3, workspace=FAKE, workspace_bytes=16), WORKSPACE),
+    (dict(mode=3, search_num0=1, search_den=1, search_count=16, dd_rule=2, workspace=FAKE, workspace_bytes=16),
+     WORKSPACE),
 ])
 def test_quantize_ex_rejects(L, kw, err):
     a = args(**kw)

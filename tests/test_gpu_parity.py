@@ -46,15 +46,16 @@ def to_dev(W: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(W).cuda()
 
 
-def run(W: np.ndarray, mode: str, iters: int = 0, dev_W=None, full_search=False, init="max"):
+def run(W: np.ndarray, mode: str, iters: int = 0, dev_W=None, full_search=False, init="max", grid=None,
+        dd_rule="cjso"):
     say(f"gpu quantize mode={mode} iters={iters} shape={W.shape} dtype={W.dtype} full_search={full_search} "
-        f"init={init}")
+        f"init={init} grid={grid} dd_rule={dd_rule}")
     Wd = to_dev(W) if dev_W is None else dev_W
     rows, cols = W.shape
     mch = torch.zeros((rows, cols // 16), dtype=torch.uint8, device="cuda") if mode == "4o6" else None
     stats = torch.zeros(4, dtype=torch.int32, device="cuda")
     codes, scales, alpha = nv.quantize(Wd, mode, iters, mchoice=mch, stats=stats, full_search=full_search,
-                                       init=init)
+                                       init=init, grid=grid, dd_rule=dd_rule)
     torch.cuda.synchronize()
     out = {"codes": codes.cpu().numpy(), "scales": scales.cpu().numpy(), "alpha": float(alpha.cpu()[0]),
            "stats": stats.cpu().numpy()}
@@ -410,6 +411,59 @@ def test_init_4o6_zero_rounds_is_4o6():
     assert f32_bits(a["alpha"]) == f32_bits(b["alpha"])
 
 
+# ---------------------------------------------------------------- search grids and reconstruct rules
+
+SEARCH_CASES = {
+    "c1_fp32_rows": lambda: np.ascontiguousarray(synth.c1(0)[:64]),
+    "ragged_3x48": lambda: synth.normal_bf16(3, 48, 5),
+    "c2_rows": lambda: synth.c2(0, 64, 1024),
+    "on_grid_tiny_alpha": lambda: indep.on_grid_matrix(32, 256, -120, 3)[0],
+    "coarse_0": lambda: coarse_bf16(0),
+    "sparse_1": lambda: sparse_bf16(1),
+}
+SEARCHES = [((50, 100, 101), "quant"), ((50, 100, 101), "lsq"), ((1, 4, 7), "cjso"), ((100, 200, 201), "cjso"),
+            ((1, 1, 16), "lsq"), ((45, 100, 13), "quant"), ((12345, 16777213, 9), "cjso"),
+            ((1, 20, 60), "lsq")]
+
+
+@pytest.mark.parametrize("grid,rule", SEARCHES)
+@pytest.mark.parametrize("name", list(SEARCH_CASES))
+def test_search_variants_match_oracle(name, grid, rule):
+    W = SEARCH_CASES[name]()
+    iters = 3
+    g = run(W, "soar", iters, grid=grid, dd_rule=rule)
+    r = oracle.quantize_search(W, iters, grid=grid, dd_rule=rule)
+    assert_exact(g, r, "soar")
+
+
+@pytest.mark.parametrize("grid", [(1, 4, 7), (100, 200, 201), (12345, 16777213, 9), (1, 20, 60), (7, 7, 1)])
+@pytest.mark.parametrize("name", ["c2_4096x4096", "coarse_1", "on_grid", "ragged_3x48"])
+def test_search_grid_window_equals_full_scan(name, grid):
+    """The windowed search stays exact on other grids: it only needs the multipliers to increase."""
+    W = window_input(name)
+    Wd = to_dev(W)
+    a = run(W, "soar", 2, dev_W=Wd, grid=grid)
+    b = run(W, "soar", 2, dev_W=Wd, grid=grid, full_search=True)
+    assert f32_bits(a["alpha"]) == f32_bits(b["alpha"])
+    diff = ~(np.all(a["codes"].reshape(-1, 8) == b["codes"].reshape(-1, 8), axis=1)
+             & (a["scales"].reshape(-1) == b["scales"].reshape(-1)))
+    assert not diff.any(), f"{diff.sum()} blocks differ, first {np.flatnonzero(diff)[:5]}"
+
+
+def test_search_variant_with_init_4o6():
+    W = synth.c2(0, 64, 512)
+    g = run(W, "soar", 2, init="4o6", grid=(1, 4, 7), dd_rule="lsq")
+    r = oracle.quantize_search(W, 2, init="4o6", grid=(1, 4, 7), dd_rule="lsq")
+    assert_exact(g, r, "soar")
+
+
+def test_pages_search_spelled_out_is_the_default():
+    W = synth.c2(0, 64, 1024)
+    a = run(W, "soar", 2)
+    b = run(W, "soar", 2, grid=(50, 100, 101), dd_rule="cjso")
+    assert np.array_equal(a["codes"], b["codes"]) and np.array_equal(a["scales"], b["scales"])
+
+
 # ------------------------------------------------------------------------------ error statistics
 
 STATS_CASES = {
@@ -483,6 +537,12 @@ def test_full_size(name):
             same = np.all(gc == d["codes"], axis=1) & (gs == d["scales"])
             assert same.mean() >= 0.9999, f"{(~same).sum()} sampled blocks differ"
             assert same.all(), f"{(~same).sum()} sampled blocks differ"
+            for vname, v in exp.get("search_variants", {}).items():
+                gv = run(W, mode, iters, dev_W=Wd, grid=tuple(v["grid"]), dd_rule=v["dd_rule"])
+                assert "%08x" % f32_bits(gv["alpha"]) == exp["alpha"], vname
+                same = (np.all(gv["codes"].reshape(-1, 8)[blocks] == d[f"{vname}_codes"], axis=1)
+                        & (gv["scales"].reshape(-1)[blocks] == d[f"{vname}_scales"]))
+                assert same.all(), f"{vname}: {(~same).sum()} sampled blocks differ"
             continue
         if mode == "cjso":
             # tolerance first (MSE), then bit-exactness through the digests
