@@ -13,11 +13,13 @@
 //     v_mfma_f32_32x32x16_bf16), K in steps of 64 through LDS: the X tile is copied, the weight tile is
 //     decoded to bf16 (codes -> binary32 q, times Delta, high half) once per work-group as it is stored,
 //     and the next step's loads are in flight while the matrix cores work on this one.
-//   k_w4a16_gemv: M <= 4 (decoding one token per row, say): bound by reading the 0.5625 bytes per weight
-//     once; each wave requests all codes of its 4 rows n up front, X sits in LDS, each lane takes 32
-//     consecutive k per 2048-k chunk, and the row sums are DPP wave reductions.
+//   k_w4a16_gemv: M <= 16 with X up to 128 KB (decoding a few tokens): bound by reading the 0.5625 bytes
+//     per weight once; each wave requests all codes of its row n up front, X sits in LDS, each lane
+//     takes 32 consecutive k per 2048-k chunk, and the row sums are DPP wave reductions.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <algorithm>
 
 #include "codec.hpp"
 #include "launch.hpp"
@@ -67,22 +69,25 @@ struct GemmStage {
     uint32_t sc;
 };
 
+// k < kend is loaded (kend = K, or the end of a split-K slice: a multiple of the K step); K is the row
+// length.
 __device__ __forceinline__ void gemm_load(GemmStage &S, const uint16_t *__restrict__ X, int64_t M, int64_t K,
-                                          const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales,
-                                          int64_t N, int64_t m0, int64_t n0, int64_t k0, int tid) {
+                                          int64_t kend, const uint8_t *__restrict__ codes,
+                                          const uint8_t *__restrict__ scales, int64_t N, int64_t m0, int64_t n0,
+                                          int64_t k0, int tid) {
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
         const int idx = tid + p * kGemmThreads;  // row idx / 8, 8-element group idx % 8
         const int64_t m = m0 + (idx >> 3), k = k0 + 8 * (idx & 7);
         S.x[p] = make_uint4(0u, 0u, 0u, 0u);
-        if (m < M && k < K) S.x[p] = *reinterpret_cast<const uint4 *>(X + m * K + k);  // K % 16 == 0
+        if (m < M && k < kend) S.x[p] = *reinterpret_cast<const uint4 *>(X + m * K + k);  // K % 16 == 0
     }
     const int64_t n = n0 + (tid >> 1), k = k0 + 32 * (tid & 1);
     S.c = make_uint4(0u, 0u, 0u, 0u);
     S.sc = 0u;
-    if (n < N && k < K) {
+    if (n < N && k < kend) {
         const int64_t e = n * K + k;  // element index, a multiple of 16
-        if (k + 32 <= K) {
+        if (k + 32 <= kend) {
             S.c = *reinterpret_cast<const uint4 *>(codes + e / 2);
             S.sc = (uint32_t)scales[e / 16] | ((uint32_t)scales[e / 16 + 1] << 8);
         } else {  // K % 32 == 16: the last 16 k of the row
@@ -112,27 +117,33 @@ __device__ __forceinline__ void gemm_store(const GemmStage &S, uint16_t *xs, uin
 // flight while the matrix cores run; one LDS buffer (55 KB) leaves room for two work-groups per CU.
 // Work-groups go to the 8 XCDs round robin; the tile order is remapped so that each XCD takes a
 // contiguous band of tiles and its L2 holds the few X row blocks that band needs.
+// Split K (when the tiles alone are too few to fill the chip): work-group b takes tile b % tiles and
+// the K slice b / tiles of kslice elements, and writes its fp32 sums without alpha to
+// part[slice][M][N]; k_w4a16_reduce adds the slices in order. With one slice it writes Y directly.
 template <bool OUTF32>
 __global__ __launch_bounds__(kGemmThreads, 2) void k_w4a16_gemm(const uint16_t *__restrict__ X, int64_t M, int64_t K,
                                                              const uint8_t *__restrict__ codes,
                                                              const uint8_t *__restrict__ scales,
                                                              const float *__restrict__ alpha_p, int64_t N,
-                                                             void *__restrict__ Y, unsigned tiles_n) {
+                                                             void *__restrict__ Y, unsigned tiles_n, unsigned tiles,
+                                                             int64_t kslice, float *__restrict__ part) {
     __shared__ __attribute__((aligned(16))) uint16_t xs[kBM * kLdsStride];
     __shared__ __attribute__((aligned(16))) uint16_t ws[kBN * kLdsStride];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const unsigned total = gridDim.x;  // 1-D grid: tiles_m * tiles_n tiles, row-major
+    const unsigned total = gridDim.x;  // 1-D grid: slices * tiles_m * tiles_n, tiles row-major
     unsigned b = blockIdx.x;
     if (total % 8 == 0) b = (b % 8) * (total / 8) + b / 8;
-    const int64_t m0 = (int64_t)(b / tiles_n) * kBM, n0 = (int64_t)(b % tiles_n) * kBN;
+    const unsigned slice = b / tiles, t = b % tiles;
+    const int64_t m0 = (int64_t)(t / tiles_n) * kBM, n0 = (int64_t)(t % tiles_n) * kBN;
+    const int64_t kbeg = (int64_t)slice * kslice, kend = min(K, kbeg + kslice);
     const int wm = (wave >> 1) * 128, wn = (wave & 1) * 64;  // the wave's 128 x 64 corner of the tile
     f32x16 acc[4][2] = {};
     GemmStage S;
-    gemm_load(S, X, M, K, codes, scales, N, m0, n0, 0, tid);
-    for (int64_t k0 = 0; k0 < K; k0 += kBK) {
+    gemm_load(S, X, M, K, kend, codes, scales, N, m0, n0, kbeg, tid);
+    for (int64_t k0 = kbeg; k0 < kend; k0 += kBK) {
         gemm_store(S, xs, ws, tid);
         __syncthreads();
-        if (k0 + kBK < K) gemm_load(S, X, M, K, codes, scales, N, m0, n0, k0 + kBK, tid);
+        if (k0 + kBK < kend) gemm_load(S, X, M, K, kend, codes, scales, N, m0, n0, k0 + kBK, tid);
 #pragma unroll
         for (int kk = 0; kk < kBK; kk += 16) {
             bf16x8 a[4], bb[2];
@@ -153,6 +164,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_w4a16_gemm(const uint16_t *
     }
     // D layout: element e of lane l is row 8 * (e / 4) + 4 * (l / 32) + e % 4, column l % 32
     const float alpha = *alpha_p;
+    float *const dst = part ? part + (int64_t)slice * M * N : nullptr;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -161,8 +173,29 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_w4a16_gemm(const uint16_t *
             for (int e = 0; e < 16; ++e) {
                 const int64_t m = m0 + wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
                 const int64_t n = n0 + wn + 32 * j + (lane & 31);
-                if (m < M && n < N) store_y<OUTF32>(Y, m * N + n, alpha * acc[i][j][e]);
+                if (m < M && n < N) {
+                    if (dst)
+                        dst[m * N + n] = acc[i][j][e];
+                    else
+                        store_y<OUTF32>(Y, m * N + n, alpha * acc[i][j][e]);
+                }
             }
+}
+
+constexpr int kReduceThreads = 256;
+
+// Y = alpha * (sum of the split-K slices, added in slice order), rounded once to the output type.
+template <bool OUTF32>
+__global__ __launch_bounds__(kReduceThreads) void k_w4a16_reduce(const float *__restrict__ part, int slices,
+                                                                 int64_t n, const float *__restrict__ alpha_p,
+                                                                 void *__restrict__ Y) {
+    const float alpha = *alpha_p;
+    for (int64_t i = (int64_t)blockIdx.x * kReduceThreads + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * kReduceThreads) {
+        float acc = part[i];
+        for (int sl = 1; sl < slices; ++sl) acc += part[(int64_t)sl * n + i];
+        store_y<OUTF32>(Y, i, alpha * acc);
+    }
 }
 
 // ------------------------------------------------------------------------------------------- GEMV
@@ -174,7 +207,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_w4a16_gemm(const uint16_t *
 #define NVFP4_GEMV_ROWS 1
 #endif
 constexpr int kGemvThreads = NVFP4_GEMV_THREADS;
-constexpr int kGemvMaxM = 4;
+constexpr int kGemvMaxM = 16;
 
 // Wave sum on the VALU (DPP; the total ends in lane 63).
 __device__ __forceinline__ float wave_sum_f32(float x) {
@@ -190,13 +223,15 @@ __device__ __forceinline__ float wave_sum_f32(float x) {
 // Each wave owns kGemvRows consecutive rows n (one by default: with 16 waves per work-group the most
 // loads are in flight) and, before anything else, requests all of their codes and scales (lane l takes
 // k = 32 * (l + 64 c) .. + 31 of chunk c < CH, 16 bytes of codes): the whole weight matrix is in flight
-// at once, which is what a read-once product needs. Meanwhile the work-group copies X (MM rows, up to
-// kGemvMaxLds bytes) to LDS; then each lane decodes its weights, forms MM fp32 dot products with packed
-// bf16 dot instructions, and a DPP wave reduction gives each row's sums.
+// at once, which is what a read-once product needs. Meanwhile the work-group copies X (M rows, up to
+// kGemvMaxLds bytes) to LDS; then each lane decodes its weights once, forms an fp32 dot product with
+// packed bf16 dot instructions for each of the M rows of X, and DPP wave reductions give the sums.
+// MM >= M is the compiled row count (M = 5 runs as 6, and so on); rows past M are neither computed
+// nor stored.
 constexpr int kGemvRows = NVFP4_GEMV_ROWS;
 
 template <int MM, int CH, bool OUTF32>
-__global__ __launch_bounds__(kGemvThreads) void k_w4a16_gemv(const uint16_t *__restrict__ X, int64_t K,
+__global__ __launch_bounds__(kGemvThreads) void k_w4a16_gemv(const uint16_t *__restrict__ X, int M, int64_t K,
                                                              const uint8_t *__restrict__ codes,
                                                              const uint8_t *__restrict__ scales,
                                                              const float *__restrict__ alpha_p, int64_t N,
@@ -225,7 +260,7 @@ __global__ __launch_bounds__(kGemvThreads) void k_w4a16_gemv(const uint16_t *__r
                 }
             }
         }
-    for (int64_t i = tid; i < MM * K / 8; i += kGemvThreads)
+    for (int64_t i = tid; i < M * K / 8; i += kGemvThreads)
         reinterpret_cast<uint4 *>(xl)[i] = reinterpret_cast<const uint4 *>(X)[i];
     __syncthreads();
     const float alpha = *alpha_p;
@@ -244,6 +279,7 @@ __global__ __launch_bounds__(kGemvThreads) void k_w4a16_gemv(const uint16_t *__r
                                 dequant8(c[r][ch].w, d1)};
 #pragma unroll
             for (int m = 0; m < MM; ++m) {
+                if (m >= M) break;
                 const uint4 *xr = reinterpret_cast<const uint4 *>(xl + m * K + k);
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
@@ -261,6 +297,7 @@ __global__ __launch_bounds__(kGemvThreads) void k_w4a16_gemv(const uint16_t *__r
         const int64_t n = n0 + r;
 #pragma unroll
         for (int m = 0; m < MM; ++m) {
+            if (m >= M) break;
             const float t = wave_sum_f32(s[m]);
             if (lane == 63 && n < N) store_y<OUTF32>(Y, m * N + n, alpha * t);
         }
@@ -273,14 +310,47 @@ constexpr size_t kGemvMaxLds = 128 * 1024;
 // Launch of one GEMV instantiation; the kernel is allowed the large dynamic LDS size once per process
 // (the attribute is per function; two threads setting it at once set the same value).
 template <int MM, int CH, bool OUTF32>
-hipError_t gemv_launch(dim3 grid, size_t lds, hipStream_t stream, const uint16_t *X, int64_t K,
+hipError_t gemv_launch(dim3 grid, size_t lds, hipStream_t stream, const uint16_t *X, int M, int64_t K,
                        const uint8_t *codes, const uint8_t *scales, const float *alpha, int64_t N, void *Y) {
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_w4a16_gemv<MM, CH, OUTF32>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemvMaxLds);
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((k_w4a16_gemv<MM, CH, OUTF32>), grid, dim3(kGemvThreads), lds, stream, X, K, codes, scales,
-                       alpha, N, Y);
+    hipLaunchKernelGGL((k_w4a16_gemv<MM, CH, OUTF32>), grid, dim3(kGemvThreads), lds, stream, X, M, K, codes,
+                       scales, alpha, N, Y);
     return hipGetLastError();
+}
+
+// The chunk count for MM compiled rows. X takes M * K * 2 <= kGemvMaxLds bytes with M > MM / 2 (the
+// smallest M each MM serves: 5 -> 6, 7 -> 8, 9 -> 12, 13 -> 16), so more than 4 chunks (K > 8192) only
+// occur for M <= 7, i.e. MM <= 8.
+template <int MM>
+hipError_t gemv_dispatch(int64_t chunks, bool out_f32, dim3 grid, size_t lds, hipStream_t stream, const uint16_t *X,
+                         int M, int64_t K, const uint8_t *codes, const uint8_t *scales, const float *alpha, int64_t N,
+                         void *Y) {
+#define NVFP4_GEMV3(CH)                                                                                          \
+    return out_f32 ? gemv_launch<MM, CH, true>(grid, lds, stream, X, M, K, codes, scales, alpha, N, Y)            \
+                   : gemv_launch<MM, CH, false>(grid, lds, stream, X, M, K, codes, scales, alpha, N, Y)
+    if (chunks <= 2) NVFP4_GEMV3(2);
+    if (chunks <= 4) NVFP4_GEMV3(4);
+    if constexpr (MM <= 8) {
+        if (chunks <= 8) NVFP4_GEMV3(8);
+    }
+#undef NVFP4_GEMV3
+    return hipErrorInvalidValue;  // not reached: the caller checks the X size
+}
+
+// Split K when the output tiles alone give fewer than 512 work-groups (two per CU): slices of at least four
+// K steps, as many as bring the count to 512, and a partial buffer of at most 1 GiB.
+void split_k(int64_t tiles, int64_t M, int64_t N, int64_t K, int64_t &slices, int64_t &kslice) {
+    slices = 1;
+    kslice = K;
+    const int64_t steps = (K + kBK - 1) / kBK;
+    int64_t want = (512 + tiles - 1) / tiles;
+    want = std::min(want, steps / 4);
+    while (want > 1 && want * M * N * (int64_t)sizeof(float) > ((int64_t)1 << 30)) --want;
+    if (want <= 1) return;
+    kslice = (steps + want - 1) / want * kBK;
+    slices = (K + kslice - 1) / kslice;
 }
 
 hipError_t launch_w4a16(const uint16_t *X, int64_t M, int64_t K, const uint8_t *codes, const uint8_t *scales,
@@ -290,33 +360,56 @@ hipError_t launch_w4a16(const uint16_t *X, int64_t M, int64_t K, const uint8_t *
         const int64_t waves = (N + kGemvRows - 1) / kGemvRows;
         const dim3 grid((unsigned)((waves + kGemvThreads / 64 - 1) / (kGemvThreads / 64)));
         const size_t lds = gemv_lds_bytes(M, K);
-#define NVFP4_GEMV3(MM, CH)                                                                                      \
-    return out_f32 ? gemv_launch<MM, CH, true>(grid, lds, stream, X, K, codes, scales, alpha, N, Y)               \
-                   : gemv_launch<MM, CH, false>(grid, lds, stream, X, K, codes, scales, alpha, N, Y)
-#define NVFP4_GEMV(MM)                                                                                           \
-    do {                                                                                                         \
-        if (chunks <= 2) NVFP4_GEMV3(MM, 2);                                                                     \
-        if (chunks <= 4) NVFP4_GEMV3(MM, 4);                                                                     \
-        NVFP4_GEMV3(MM, 8);                                                                                      \
-    } while (0)
+        const int m = (int)M;
         switch (M) {
-            case 1: NVFP4_GEMV(1);
-            case 2: NVFP4_GEMV(2);
-            case 3: NVFP4_GEMV(3);
-            default: NVFP4_GEMV(4);
+            case 1: return gemv_dispatch<1>(chunks, out_f32, grid, lds, stream, X, m, K, codes, scales, alpha, N, Y);
+            case 2: return gemv_dispatch<2>(chunks, out_f32, grid, lds, stream, X, m, K, codes, scales, alpha, N, Y);
+            case 3: return gemv_dispatch<3>(chunks, out_f32, grid, lds, stream, X, m, K, codes, scales, alpha, N, Y);
+            case 4: return gemv_dispatch<4>(chunks, out_f32, grid, lds, stream, X, m, K, codes, scales, alpha, N, Y);
+            case 5:
+            case 6: return gemv_dispatch<6>(chunks, out_f32, grid, lds, stream, X, m, K, codes, scales, alpha, N, Y);
+            case 7:
+            case 8: return gemv_dispatch<8>(chunks, out_f32, grid, lds, stream, X, m, K, codes, scales, alpha, N, Y);
+            case 9:
+            case 10:
+            case 11:
+            case 12: return gemv_dispatch<12>(chunks, out_f32, grid, lds, stream, X, m, K, codes, scales, alpha, N, Y);
+            default: return gemv_dispatch<16>(chunks, out_f32, grid, lds, stream, X, m, K, codes, scales, alpha, N, Y);
         }
-#undef NVFP4_GEMV
-#undef NVFP4_GEMV3
     }
-    const int64_t tiles_n = (N + kBN - 1) / kBN, tiles_m = (M + kBM - 1) / kBM;
-    const dim3 grid((unsigned)(tiles_n * tiles_m)), block(kGemmThreads);
+    const int64_t tiles_n = (N + kBN - 1) / kBN, tiles_m = (M + kBM - 1) / kBM, tiles = tiles_n * tiles_m;
+    int64_t slices = 1, kslice = K;
+    split_k(tiles, M, N, K, slices, kslice);
+    float *part = nullptr;
+    if (slices > 1) {
+        if (hipMallocAsync(reinterpret_cast<void **>(&part), (size_t)(slices * M * N) * sizeof(float), stream) !=
+            hipSuccess)
+            return hipErrorOutOfMemory;
+    }
+    const dim3 grid((unsigned)(tiles * slices)), block(kGemmThreads);
     if (out_f32)
         hipLaunchKernelGGL(k_w4a16_gemm<true>, grid, block, 0, stream, X, M, K, codes, scales, alpha, N, Y,
-                           (unsigned)tiles_n);
+                           (unsigned)tiles_n, (unsigned)tiles, kslice, part);
     else
         hipLaunchKernelGGL(k_w4a16_gemm<false>, grid, block, 0, stream, X, M, K, codes, scales, alpha, N, Y,
-                           (unsigned)tiles_n);
-    return hipGetLastError();
+                           (unsigned)tiles_n, (unsigned)tiles, kslice, part);
+    hipError_t err = hipGetLastError();
+    if (slices > 1) {
+        if (err == hipSuccess) {
+            const int64_t n = M * N;
+            const dim3 rgrid((unsigned)std::min<int64_t>((n + kReduceThreads - 1) / kReduceThreads, 4096));
+            if (out_f32)
+                hipLaunchKernelGGL(k_w4a16_reduce<true>, rgrid, dim3(kReduceThreads), 0, stream, part, (int)slices,
+                                   n, alpha, Y);
+            else
+                hipLaunchKernelGGL(k_w4a16_reduce<false>, rgrid, dim3(kReduceThreads), 0, stream, part,
+                                   (int)slices, n, alpha, Y);
+            err = hipGetLastError();
+        }
+        const hipError_t ferr = hipFreeAsync(part, stream);
+        if (err == hipSuccess) err = ferr;
+    }
+    return err;
 }
 
 }  // namespace nvfp4
