@@ -39,9 +39,10 @@ __device__ __forceinline__ uint4 dequant8(uint32_t c, float dv) {
     const f32x2 q1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 1);
     const f32x2 q2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 2);
     const f32x2 q3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 3);
-    // q*dv is exact and has at most 6 significant bits: its high 16 bits are the bf16 value
+    // q*dv is exact and has at most 6 significant bits: its high 16 bits are the bf16 value. The byte
+    // permute takes bytes 2, 3 of a*dv (selectors 2, 3: the second operand) and of b*dv (6, 7: the first).
     auto pair = [&](float a, float b) {
-        return (__float_as_uint(a * dv) >> 16) | (__float_as_uint(b * dv) & 0xFFFF0000u);
+        return __builtin_amdgcn_perm(__float_as_uint(b * dv), __float_as_uint(a * dv), 0x07060302u);
     };
     return make_uint4(pair(q0.x, q0.y), pair(q1.x, q1.y), pair(q2.x, q2.y), pair(q3.x, q3.y));
 }
@@ -98,6 +99,17 @@ __device__ __forceinline__ void gemm_load(GemmStage &S, const uint16_t *__restri
     }
 }
 
+// The unmasked form for a work-group whose tile and K slice lie inside the matrices: xp points at X row
+// m0 + tid / 8, column k0 + 8 (tid % 8) (row p of the thread adds 32 p K), cp at the codes of weight row
+// n0 + tid / 2 from k0 + 32 (tid % 2), sp at their two scale bytes.
+__device__ __forceinline__ void gemm_load_full(GemmStage &S, const uint16_t *__restrict__ xp, int64_t K,
+                                               const uint8_t *__restrict__ cp, const uint8_t *__restrict__ sp) {
+#pragma unroll
+    for (int p = 0; p < 8; ++p) S.x[p] = *reinterpret_cast<const uint4 *>(xp + p * 32 * K);
+    S.c = *reinterpret_cast<const uint4 *>(cp);
+    S.sc = (uint32_t)sp[0] | ((uint32_t)sp[1] << 8);
+}
+
 __device__ __forceinline__ void gemm_store(const GemmStage &S, uint16_t *xs, uint16_t *ws, int tid) {
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
@@ -139,11 +151,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_w4a16_gemm(const uint16_t *
     const int wm = (wave >> 1) * 128, wn = (wave & 1) * 64;  // the wave's 128 x 64 corner of the tile
     f32x16 acc[4][2] = {};
     GemmStage S;
-    gemm_load(S, X, M, K, kend, codes, scales, N, m0, n0, kbeg, tid);
-    for (int64_t k0 = kbeg; k0 < kend; k0 += kBK) {
-        gemm_store(S, xs, ws, tid);
-        __syncthreads();
-        if (k0 + kBK < kend) gemm_load(S, X, M, K, kend, codes, scales, N, m0, n0, k0 + kBK, tid);
+    // the products of one K step from the staged tiles
+    auto mfma_step = [&]() {
 #pragma unroll
         for (int kk = 0; kk < kBK; kk += 16) {
             bf16x8 a[4], bb[2];
@@ -160,26 +169,53 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_w4a16_gemm(const uint16_t *
                 for (int j = 0; j < 2; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bb[j], acc[i][j], 0, 0, 0);
         }
-        __syncthreads();
+    };
+    const bool full = m0 + kBM <= M && n0 + kBN <= N && (kend - kbeg) % kBK == 0;  // uniform
+    if (full) {
+        const uint16_t *xp = X + (m0 + (tid >> 3)) * K + kbeg + 8 * (tid & 7);
+        const int64_t e = (n0 + (tid >> 1)) * K + kbeg + 32 * (tid & 1);  // element index, a multiple of 16
+        const uint8_t *cp = codes + e / 2, *sp = scales + e / 16;
+        gemm_load_full(S, xp, K, cp, sp);
+        for (int64_t k0 = kbeg; k0 < kend; k0 += kBK) {
+            gemm_store(S, xs, ws, tid);
+            __syncthreads();
+            xp += kBK;
+            cp += kBK / 2;
+            sp += kBK / 16;
+            if (k0 + kBK < kend) gemm_load_full(S, xp, K, cp, sp);
+            mfma_step();
+            __syncthreads();
+        }
+    } else {
+        gemm_load(S, X, M, K, kend, codes, scales, N, m0, n0, kbeg, tid);
+        for (int64_t k0 = kbeg; k0 < kend; k0 += kBK) {
+            gemm_store(S, xs, ws, tid);
+            __syncthreads();
+            if (k0 + kBK < kend) gemm_load(S, X, M, K, kend, codes, scales, N, m0, n0, k0 + kBK, tid);
+            mfma_step();
+            __syncthreads();
+        }
     }
     // D layout: element e of lane l is row 8 * (e / 4) + 4 * (l / 32) + e % 4, column l % 32
     const float alpha = *alpha_p;
     float *const dst = part ? part + (int64_t)slice * M * N : nullptr;
+    const int64_t mb = m0 + wm + 4 * (lane >> 5), nb = n0 + wn + (lane & 31);  // the lane's first row, column
+    const int64_t yb = mb * N + nb;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int e = 0; e < 16; ++e) {
+            const int r = 32 * i + 8 * (e >> 2) + (e & 3);  // row offset from mb
+            const int64_t yr = yb + r * N;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int64_t m = m0 + wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-                const int64_t n = n0 + wn + 32 * j + (lane & 31);
-                if (m < M && n < N) {
-                    if (dst)
-                        dst[m * N + n] = acc[i][j][e];
-                    else
-                        store_y<OUTF32>(Y, m * N + n, alpha * acc[i][j][e]);
-                }
+            for (int j = 0; j < 2; ++j) {
+                if (!full && (mb + r >= M || nb + 32 * j >= N)) continue;
+                if (dst)
+                    dst[yr + 32 * j] = acc[i][j][e];
+                else
+                    store_y<OUTF32>(Y, yr + 32 * j, alpha * acc[i][j][e]);
             }
+        }
 }
 
 constexpr int kReduceThreads = 256;
