@@ -25,9 +25,14 @@ w4a16: the W4A16 product the format is for, Y = X @ What.T with the quantised 40
 M = 1 (GB/s against HBM peak) and M = 4096 (TFLOP/s against the 2.5 PFLOP/s bf16 MFMA peak).
 
 c5_whole_model: the 224 matrices of a 7B-shaped model (32 layers; 12.95 GB bf16) quantised one after
-another in each mode, total time and aggregate GB/s (skipped with --no-c5).
+another in each mode, total time and aggregate GB/s, and the same for its 128 square 4096 x 4096
+matrices alone (skipped with --no-c5).
 
-cpu_baseline: the oracle (plain C, one thread) on rows 0..255 of the first matrix in all four modes.
+hbm_attainable: a plain 1 GiB device copy timed on the box (read + write bytes / time): the streaming
+rate a kernel can reach here, beside the 8 TB/s figure the roofline uses.
+
+cpu_baseline: the oracle (plain C, one thread) on rows 0..255 of the first matrix in all four modes;
+speedup_vs_cpu is value / cpu_baseline.value.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--streams S]
 """
@@ -176,8 +181,10 @@ def c5_pass(torch, nv, dev, streams):
         b["alpha"] = torch.empty(1, dtype=torch.float32, device=dev)
         bufs.append(b)
 
-    def run(mode, iters):
+    def run(mode, iters, which=None):
         for i, W in enumerate(mats):
+            if which is not None and not which(W):
+                continue
             k = i % n_streams
             b = bufs[k]
             shape = tuple(W.shape)
@@ -185,7 +192,10 @@ def c5_pass(torch, nv, dev, streams):
                 nv.quantize(W, mode, iters, codes=b["codes"][shape], scales=b["scales"][shape], alpha=b["alpha"],
                             workspace=b[mode]["workspace"])
 
-    out = {"matrices": len(mats), "bytes": total_bytes, "streams": n_streams, "modes": {}}
+    square = lambda W: tuple(W.shape) == (4096, 4096)  # noqa: E731
+    sq_bytes = sum(m.numel() * 2 for m in mats if square(m))
+    out = {"matrices": len(mats), "bytes": total_bytes, "streams": n_streams, "modes": {},
+           "square_4096": {"matrices": sum(1 for m in mats if square(m)), "bytes": sq_bytes, "modes": {}}}
     for mode, iters in MODES:
         run(mode, iters)  # warm-up pass
         torch.cuda.synchronize()
@@ -194,10 +204,37 @@ def c5_pass(torch, nv, dev, streams):
         torch.cuda.synchronize()
         dt = time.perf_counter() - t0
         out["modes"][mode] = {"total_ms": round(dt * 1e3, 3), "GBps": round(total_bytes / dt / 1e9, 2)}
-        log(f"c5 {mode}: {dt * 1e3:.1f} ms")
+        t0 = time.perf_counter()
+        run(mode, iters, square)
+        torch.cuda.synchronize()
+        dq = time.perf_counter() - t0
+        out["square_4096"]["modes"][mode] = {"total_ms": round(dq * 1e3, 3), "GBps": round(sq_bytes / dq / 1e9, 2)}
+        log(f"c5 {mode}: {dt * 1e3:.1f} ms; square matrices {dq * 1e3:.1f} ms")
     del mats
     torch.cuda.empty_cache()
     return out
+
+
+def hbm_attainable(torch, dev) -> dict:
+    """A plain 1 GiB device copy (torch's copy kernel), median of 10: read + write bytes per second."""
+    n = (1 << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    ts = []
+    for _ in range(10):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e-3)
+    t = sorted(ts)[len(ts) // 2]
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"copy_GBps": round(2 * n * 4 / t / 1e9, 1), "frac_of_peak": round(2 * n * 4 / t / PEAK_HBM, 4),
+            "kind": "1 GiB device copy, read + write bytes, median of 10"}
 
 
 def main():
@@ -390,6 +427,7 @@ def main():
                 "avg_launch_ms": round(t_round * 1e3, 5), "launches_per_step": 2 * (ITERS - 1)}
 
     w4a16 = w4a16_pass(torch, nv, dev, mats[0])
+    attainable = hbm_attainable(torch, dev)
     c5 = None if args.no_c5 else c5_pass(torch, nv, dev, streams)
 
     value = len(MODES) * ROWS * COLS * 2 / (ms_per_step * 1e-3) / 1e9
@@ -408,11 +446,13 @@ def main():
         "roofline": roofline,
     }
     line["w4a16"] = w4a16
+    line["hbm_attainable"] = attainable
     if c5 is not None:
         line["c5_whole_model"] = c5
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         line["cpu_baseline"] = cpu_baseline(W0)
+        line["speedup_vs_cpu"] = round(line["value"] / line["cpu_baseline"]["value"], 1)
     print(json.dumps(line), flush=True)
 
 
