@@ -7,9 +7,10 @@ stay resident in HBM and are visited in turn, so each step starts from HBM rathe
 
 One step = one matrix quantised in each of the four modes, back to back on one stream:
 MAX, FourOverSix, CJSO (8 rounds), SOAR (CJSO(8) + the decoupled search). Consecutive steps (different
-matrices, separate outputs and workspaces) alternate between two HIP streams, the way a model's
-independent weight matrices are quantised; `single_stream_ms_per_step` gives the same steps on one
-stream. `value` is the weight bytes quantised per second (4 x 32 MiB per step). Per mode the JSON line
+matrices, separate outputs and workspaces) rotate over three HIP streams, the way a model's
+independent weight matrices are quantised (three streams and torch's default stream use the four
+hardware queues a process gets; two streams give about 10 % less, four share a queue and lose);
+`single_stream_ms_per_step` gives the same steps on one stream. `value` is the weight bytes quantised per second (4 x 32 MiB per step). Per mode the JSON line
 also gives its own GB/s and its share of the HBM peak.
 
 The dominant kernel is the CJSO round (k_cjso_iter): sixteen of them per step. It is timed live: the
@@ -243,7 +244,7 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--streams", type=int, default=2, help="HIP streams that consecutive steps alternate over")
+    ap.add_argument("--streams", type=int, default=3, help="HIP streams that consecutive steps rotate over")
     ap.add_argument("--no-c5", action="store_true", help="skip the whole-model (224 matrices) pass")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device copy 5 times (scales the HBM byte counters)")
