@@ -186,7 +186,7 @@ int nvfp4_error_stats(const void *W, int dtype, int64_t rows, int64_t cols, cons
  * X, codes and Y 16-byte aligned; K % 16 == 0, N <= 2^25 and fewer than 2^24 output tiles of 256 x 128
  * (else NVFP4_ERR_SHAPE). Arithmetic: every q * Delta is a bf16 value,
  * so the products with X are exact; the sum over k is accumulated in fp32 (packed bf16 dot products when
- * M <= 16, M * K * 2 <= 128 KiB and K <= 16384; bf16 MFMA otherwise) in an order the caller does not
+ * M <= 4, M * K * 2 <= 128 KiB and K <= 16384; bf16 MFMA otherwise) in an order the caller does not
  * control, then multiplied by alpha and
  * rounded once to the output type. When the output tiles are too few to fill the GPU, K is split and the
  * slices' fp32 sums (slices * M * N * 4 bytes, at most 1 GiB) go through scratch taken from a

@@ -13,9 +13,11 @@
 //     v_mfma_f32_32x32x16_bf16), K in steps of 64 through LDS: the X tile is copied, the weight tile is
 //     decoded to bf16 (codes -> binary32 q, times Delta, high half) once per work-group as it is stored,
 //     and the next step's loads are in flight while the matrix cores work on this one.
-//   k_w4a16_gemv: M <= 16 with X up to 128 KB (decoding a few tokens): bound by reading the 0.5625 bytes
-//     per weight once; each wave requests all codes of its row n up front, X sits in LDS, each lane
-//     takes 32 consecutive k per 2048-k chunk, and the row sums are DPP wave reductions.
+//   k_w4a16_gemv: M <= 4 with X up to 128 KB (decoding one or a few tokens): bound by reading the 0.5625
+//     bytes per weight once; each wave requests all codes of its row n up front, X sits in LDS, each
+//     lane takes 32 consecutive k per 2048-k chunk, and the row sums are DPP wave reductions.
+//   k_w4a16_skinny: M <= 64 otherwise: 16 weight rows per work-group, K split over its 16 waves, the
+//     products on v_mfma_f32_16x16x32_bf16 with weights decoded straight into the A operand.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -28,6 +30,7 @@ namespace nvfp4 {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kGemmThreads = 256;
 constexpr int kBM = 256, kBN = 128, kBK = 64;
@@ -234,6 +237,96 @@ __global__ __launch_bounds__(kReduceThreads) void k_w4a16_reduce(const float *__
     }
 }
 
+// -------------------------------------------------------------------------------------- skinny MFMA
+
+// Few rows of X (M <= 64): a work-group owns 16 weight rows n and its 16 waves split K into chunks of
+// 128 k (wave w takes chunks w, w + 16, ...). Products run on v_mfma_f32_16x16x32_bf16 with the weights as
+// the A operand (16 rows n) and X^T as the B operand (16 columns m per tile, MT tiles). The MFMA sums
+// over its 32 k slots in any order, so each slot is mapped to the k that makes the loads contiguous:
+// in chunk c, lane l (row or column l % 16, group g = l / 16) supplies for MFMA i (0..3) the 8 values at
+// k = 128 c + 32 g + 8 i .. + 7, for the weights and for X alike. A lane thus loads 16 bytes of codes
+// (two 16-blocks, two scale bytes) per chunk and decodes them straight into the A operand, and 64
+// contiguous bytes of each of its X rows. Weights are read once; X (at most 64 x K bf16) comes from L2.
+// The 16 waves' partial tiles are added through LDS in wave order, and alpha is applied once.
+constexpr int kSkinnyThreads = 1024, kSkinnyWaves = kSkinnyThreads / 64, kSkinnyMaxM = 64;
+
+template <int MT, bool OUTF32>
+__global__ __launch_bounds__(kSkinnyThreads) void k_w4a16_skinny(const uint16_t *__restrict__ X, int M, int64_t K,
+                                                                 const uint8_t *__restrict__ codes,
+                                                                 const uint8_t *__restrict__ scales,
+                                                                 const float *__restrict__ alpha_p, int64_t N,
+                                                                 void *__restrict__ Y) {
+    __shared__ float red[kSkinnyWaves][MT][256];  // each wave's 16 x 16 tiles, lane-major
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r16 = lane & 15, g = lane >> 4;
+    const int64_t n0 = (int64_t)blockIdx.x * 16, n = n0 + r16;
+    const int64_t nch = (K + 127) / 128;
+    f32x4 acc[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    // the lane's codes (16 bytes) and scale bytes of chunk c; zeros past the row or past N
+    auto load_w = [&](int64_t c, uint4 &cv, uint32_t &sv) {
+        const int64_t k = 128 * c + 32 * g;
+        cv = make_uint4(0u, 0u, 0u, 0u);
+        sv = 0u;
+        if (n < N && k < K) {
+            const int64_t e = n * K + k;  // element index, a multiple of 16
+            if (k + 32 <= K) {
+                cv = *reinterpret_cast<const uint4 *>(codes + e / 2);
+                sv = (uint32_t)scales[e / 16] | ((uint32_t)scales[e / 16 + 1] << 8);
+            } else {  // K % 32 == 16: the row's last 16 k
+                const uint2 c2 = *reinterpret_cast<const uint2 *>(codes + e / 2);
+                cv = make_uint4(c2.x, c2.y, 0u, 0u);
+                sv = scales[e / 16];
+            }
+        }
+    };
+    int64_t c = wave;
+    uint4 cv;
+    uint32_t sv;
+    if (c < nch) load_w(c, cv, sv);
+    for (; c < nch; c += kSkinnyWaves) {
+        const uint4 cur = cv;
+        const uint32_t scur = sv;
+        if (c + kSkinnyWaves < nch) load_w(c + kSkinnyWaves, cv, sv);  // next chunk's weights in flight
+        const int64_t k = 128 * c + 32 * g;
+        // X rows m = 16 t + r16 at k .. k + 31 (zeros past M or past K; K % 16 == 0)
+        uint4 xv[MT][4];
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+            const int m = 16 * t + r16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                xv[t][i] = make_uint4(0u, 0u, 0u, 0u);
+                if (m < M && k + 8 * i < K) xv[t][i] = *reinterpret_cast<const uint4 *>(X + (int64_t)m * K + k + 8 * i);
+            }
+        }
+        const float d0 = e4m3_value(scur & 0x7Fu), d1 = e4m3_value((scur >> 8) & 0x7Fu);
+        const uint4 w[4] = {dequant8(cur.x, d0), dequant8(cur.y, d0), dequant8(cur.z, d1), dequant8(cur.w, d1)};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int t = 0; t < MT; ++t)
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w[i]),
+                                                                 __builtin_bit_cast(bf16x8, xv[t][i]), acc[t], 0, 0, 0);
+    }
+    // D layout: element r of lane l is row n0 + 4 (l / 16) + r, column m = 16 t + l % 16
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[wave][t][lane * 4 + r] = acc[t][r];
+    __syncthreads();
+    const float alpha = *alpha_p;
+    for (int o = tid; o < MT * 256; o += kSkinnyThreads) {  // o = 256 t + 4 lane + r
+        const int t = o >> 8, l = (o >> 2) & 63, r = o & 3;
+        float sum = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kSkinnyWaves; ++w) sum += red[w][t][o & 255];
+        const int64_t nn = n0 + 4 * (l >> 4) + r;
+        const int m = 16 * t + (l & 15);
+        if (nn < N && m < M) store_y<OUTF32>(Y, (int64_t)m * N + nn, alpha * sum);
+    }
+}
+
 // ------------------------------------------------------------------------------------------- GEMV
 
 #ifndef NVFP4_GEMV_THREADS
@@ -242,8 +335,11 @@ __global__ __launch_bounds__(kReduceThreads) void k_w4a16_reduce(const float *__
 #ifndef NVFP4_GEMV_ROWS
 #define NVFP4_GEMV_ROWS 1
 #endif
+#ifndef NVFP4_GEMV_MAX_M
+#define NVFP4_GEMV_MAX_M 4  // the GEMV serves M up to this; the skinny MFMA kernel the rest up to 64
+#endif
 constexpr int kGemvThreads = NVFP4_GEMV_THREADS;
-constexpr int kGemvMaxM = 16;
+constexpr int kGemvMaxM = NVFP4_GEMV_MAX_M;
 
 // Wave sum on the VALU (DPP; the total ends in lane 63).
 __device__ __forceinline__ float wave_sum_f32(float x) {
@@ -262,8 +358,7 @@ __device__ __forceinline__ float wave_sum_f32(float x) {
 // at once, which is what a read-once product needs. Meanwhile the work-group copies X (M rows, up to
 // kGemvMaxLds bytes) to LDS; then each lane decodes its weights once, forms an fp32 dot product with
 // packed bf16 dot instructions for each of the M rows of X, and DPP wave reductions give the sums.
-// MM >= M is the compiled row count (M = 5 runs as 6, and so on); rows past M are neither computed
-// nor stored.
+// MM >= M is the compiled row count; rows past M are neither computed nor stored.
 constexpr int kGemvRows = NVFP4_GEMV_ROWS;
 
 template <int MM, int CH, bool OUTF32>
@@ -356,9 +451,7 @@ hipError_t gemv_launch(dim3 grid, size_t lds, hipStream_t stream, const uint16_t
     return hipGetLastError();
 }
 
-// The chunk count for MM compiled rows. X takes M * K * 2 <= kGemvMaxLds bytes with M > MM / 2 (the
-// smallest M each MM serves: 5 -> 6, 7 -> 8, 9 -> 12, 13 -> 16), so more than 4 chunks (K > 8192) only
-// occur for M <= 7, i.e. MM <= 8.
+// The chunk count for MM rows of X (K <= 16384: at most 8 chunks).
 template <int MM>
 hipError_t gemv_dispatch(int64_t chunks, bool out_f32, dim3 grid, size_t lds, hipStream_t stream, const uint16_t *X,
                          int M, int64_t K, const uint8_t *codes, const uint8_t *scales, const float *alpha, int64_t N,
@@ -368,11 +461,8 @@ hipError_t gemv_dispatch(int64_t chunks, bool out_f32, dim3 grid, size_t lds, hi
                    : gemv_launch<MM, CH, false>(grid, lds, stream, X, M, K, codes, scales, alpha, N, Y)
     if (chunks <= 2) NVFP4_GEMV3(2);
     if (chunks <= 4) NVFP4_GEMV3(4);
-    if constexpr (MM <= 8) {
-        if (chunks <= 8) NVFP4_GEMV3(8);
-    }
+    NVFP4_GEMV3(8);
 #undef NVFP4_GEMV3
-    return hipErrorInvalidValue;  // not reached: the caller checks the X size
 }
 
 // Split K when the output tiles alone give fewer than 512 work-groups (two per CU): slices of at least four
@@ -397,21 +487,34 @@ hipError_t launch_w4a16(const uint16_t *X, int64_t M, int64_t K, const uint8_t *
         const dim3 grid((unsigned)((waves + kGemvThreads / 64 - 1) / (kGemvThreads / 64)));
         const size_t lds = gemv_lds_bytes(M, K);
         const int m = (int)M;
+        static_assert(kGemvMaxM <= 4, "the GEMV is compiled for 1 to 4 rows of X");
         switch (M) {
             case 1: return gemv_dispatch<1>(chunks, out_f32, grid, lds, stream, X, m, K, codes, scales, alpha, N, Y);
             case 2: return gemv_dispatch<2>(chunks, out_f32, grid, lds, stream, X, m, K, codes, scales, alpha, N, Y);
             case 3: return gemv_dispatch<3>(chunks, out_f32, grid, lds, stream, X, m, K, codes, scales, alpha, N, Y);
-            case 4: return gemv_dispatch<4>(chunks, out_f32, grid, lds, stream, X, m, K, codes, scales, alpha, N, Y);
-            case 5:
-            case 6: return gemv_dispatch<6>(chunks, out_f32, grid, lds, stream, X, m, K, codes, scales, alpha, N, Y);
-            case 7:
-            case 8: return gemv_dispatch<8>(chunks, out_f32, grid, lds, stream, X, m, K, codes, scales, alpha, N, Y);
-            case 9:
-            case 10:
-            case 11:
-            case 12: return gemv_dispatch<12>(chunks, out_f32, grid, lds, stream, X, m, K, codes, scales, alpha, N, Y);
-            default: return gemv_dispatch<16>(chunks, out_f32, grid, lds, stream, X, m, K, codes, scales, alpha, N, Y);
+            default: return gemv_dispatch<4>(chunks, out_f32, grid, lds, stream, X, m, K, codes, scales, alpha, N, Y);
         }
+    }
+    if (M <= kSkinnyMaxM) {
+        const dim3 grid((unsigned)((N + 15) / 16)), block(kSkinnyThreads);
+        const int m = (int)M;
+#define NVFP4_SKINNY(MT)                                                                                          \
+    do {                                                                                                          \
+        if (out_f32)                                                                                              \
+            hipLaunchKernelGGL((k_w4a16_skinny<MT, true>), grid, block, 0, stream, X, m, K, codes, scales, alpha, N,  \
+                               Y);                                                                                \
+        else                                                                                                      \
+            hipLaunchKernelGGL((k_w4a16_skinny<MT, false>), grid, block, 0, stream, X, m, K, codes, scales, alpha,   \
+                               N, Y);                                                                             \
+    } while (0)
+        switch ((M + 15) / 16) {
+            case 1: NVFP4_SKINNY(1); break;
+            case 2: NVFP4_SKINNY(2); break;
+            case 3: NVFP4_SKINNY(3); break;
+            default: NVFP4_SKINNY(4); break;
+        }
+#undef NVFP4_SKINNY
+        return hipGetLastError();
     }
     const int64_t tiles_n = (N + kBN - 1) / kBN, tiles_m = (M + kBM - 1) / kBM, tiles = tiles_n * tiles_m;
     int64_t slices = 1, kslice = K;

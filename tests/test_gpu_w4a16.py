@@ -49,13 +49,14 @@ def check(X, codes, scales, alpha, out_dtype):
     return got, ref
 
 
-SHAPES = [(1, 256, 1024), (2, 96, 160), (3, 64, 272), (4, 130, 64),   # GEMV path (M <= 16), 2 chunks
+SHAPES = [(1, 256, 1024), (2, 96, 160), (3, 64, 272), (4, 130, 64),   # GEMV path (M <= 4), 2 chunks
           (1, 70, 4112), (3, 9, 6160), (2, 33, 12304), (4, 5, 8192),  # GEMV with 4 and 8 chunks of 2048 k
           (4, 37, 11008), (4, 40, 16384),  # X of 88 KB and 128 KB (the GEMV's LDS limit)
-          (5, 200, 272), (7, 50, 9360), (9, 33, 7280), (12, 20, 1024), (13, 40, 5040),  # M run as 6, 8, 12, 16
-          (16, 64, 4096),  # 16 rows of X, 128 KB
-          (1, 21, 16400), (16, 24, 4112), (17, 64, 512),  # past the GEMV's K, LDS and M limits: MFMA path
-          (64, 128, 512), (130, 260, 528), (128, 256, 1024),  # MFMA path, one row of tiles
+          (1, 21, 16400), (4, 24, 16400),  # past the GEMV's K limit: skinny MFMA path (M <= 64)
+          (5, 200, 272), (7, 50, 9360), (9, 33, 7280), (12, 20, 1024), (13, 40, 5040), (16, 64, 4096),
+          (16, 24, 4112), (17, 64, 512),
+          (33, 50, 400), (48, 17, 4112), (64, 100, 2064), (20, 7, 16), (40, 33, 48),  # skinny: 1-4 tiles of 16 m
+          (65, 40, 320), (130, 260, 528), (128, 256, 1024),  # 256 x 128 MFMA tiles, K split
           (300, 136, 96), (512, 512, 160), (260, 1100, 48)]  # several 256 x 128 tiles (8 | 8 tiles: remapped)
 
 
@@ -92,13 +93,14 @@ def test_w4a16_one_hot_rows_are_exact():
 
 
 def test_w4a16_full_size_sample():
-    """4096 x 4096 weights with M = 1, 8 and 64: sampled outputs against the oracle."""
+    """4096 x 4096 weights with M = 1 (GEMV), 8 and 64 (skinny MFMA) and 256 (MFMA tiles, K split):
+    sampled outputs against the oracle."""
     n = k = 4096
     W = synth.c2(0)
     codes, scales, alpha = nv.quantize(bf16_dev(W), "4o6")
     c, s, a = codes.cpu().numpy(), scales.cpu().numpy(), float(alpha.cpu()[0])
     rows = np.arange(0, n, 61)
-    for m in (1, 8, 64):
+    for m in (1, 8, 64, 256):
         X = synth.normal_bf16(m, k, seed=m, std=1.0)
         say(f"w4a16 full size M={m}")
         Y = nv.matmul(bf16_dev(X), codes, scales, alpha, out_dtype=torch.float32)
