@@ -8,16 +8,17 @@
 // fp32, and alpha multiplies the fp32 sum once at the end (y = fl(alpha * acc), then rounded to the
 // output type). Only the accumulation order differs from an exact product.
 //
-// Two kernels:
-//   k_w4a16_gemm: 256 x 128 output tile per work-group (4 waves, 128 x 64 each as 4 x 2 tiles of
-//     v_mfma_f32_32x32x16_bf16), K in steps of 64 through LDS: the X tile is copied, the weight tile is
-//     decoded to bf16 (codes -> binary32 q, times Delta, high half) once per work-group as it is stored,
-//     and the next step's loads are in flight while the matrix cores work on this one.
-//   k_w4a16_gemv: M <= 4 with X up to 128 KB (decoding one or a few tokens): bound by reading the 0.5625
+// Kernels, by the number M of rows of X:
+//   k_w4a16_gemv (M <= 4, X up to 128 KB; decoding one or a few tokens): bound by reading the 0.5625
 //     bytes per weight once; each wave requests all codes of its row n up front, X sits in LDS, each
 //     lane takes 32 consecutive k per 2048-k chunk, and the row sums are DPP wave reductions.
-//   k_w4a16_skinny: M <= 64 otherwise: 16 weight rows per work-group, K split over its 16 waves, the
+//   k_w4a16_skinny (M <= 64 otherwise): 16 weight rows per work-group, K split over its 16 waves, the
 //     products on v_mfma_f32_16x16x32_bf16 with weights decoded straight into the A operand.
+//   k_w4a16_gemm (M > 64): 256 x 128 output tile per work-group (4 waves, 128 x 64 each as 4 x 2 tiles of
+//     v_mfma_f32_32x32x16_bf16), K in steps of 64 through LDS: the X tile is copied, the weight tile is
+//     decoded to bf16 (codes -> binary32 q, times Delta, high half) once per work-group as it is stored,
+//     and the next step's loads are in flight while the matrix cores work on this one. When the tiles
+//     are too few to fill the GPU, K is split and k_w4a16_reduce adds the slices.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -50,9 +51,10 @@ __device__ __forceinline__ uint4 dequant8(uint32_t c, float dv) {
     return make_uint4(pair(q0.x, q0.y), pair(q1.x, q1.y), pair(q2.x, q2.y), pair(q3.x, q3.y));
 }
 
-// Round binary32 to bf16 (nearest, ties to even; the values here are finite).
+// Round binary32 to bf16 (nearest, ties to even; infinities stay, a NaN stays a quiet NaN).
 __device__ __forceinline__ uint16_t to_bf16(float f) {
     const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
     return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
