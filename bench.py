@@ -23,7 +23,7 @@ NVFP4_FLAG_FULL_SEARCH (all 202 candidates) against the FP32 vector peak: per bl
 scales x 16 elements x 9 FLOPs.
 
 w4a16: the W4A16 product the format is for, Y = X @ What.T with the quantised 4096 x 4096 weights, at
-M = 1 (GB/s against HBM peak) and M = 4096 (TFLOP/s against the 2.5 PFLOP/s bf16 MFMA peak).
+M = 1 and 16 (GB/s against HBM peak), 256 and 4096 (TFLOP/s against the 2.5 PFLOP/s bf16 MFMA peak).
 
 c5_whole_model: the 224 matrices of a 7B-shaped model (32 layers; 12.95 GB bf16) quantised one after
 another in each mode, total time and aggregate GB/s, and the same for its 128 square 4096 x 4096
@@ -107,15 +107,18 @@ PEAK_BF16_MFMA = 2.5e15  # FLOP/s, MI355X dense bf16 matrix peak
 
 def w4a16_pass(torch, nv, dev, W):
     """The consumer of the format: Y = X @ What.T with the 4096 x 4096 weights quantised (FourOverSix)
-    and bf16 activations, for M = 1 (one token: bound by reading 0.5625 B per weight) and M = 4096 (bf16
-    MFMA). Times are HIP-event averages over a graph of repeated calls on the current stream."""
+    and bf16 activations, for M = 1 (one token, the GEMV: bound by reading 0.5625 B per weight), M = 16
+    (the skinny MFMA kernel), M = 256 (256 x 128 MFMA tiles with K split) and M = 4096 (the same tiles,
+    bf16 MFMA-bound). Times are HIP-event averages over a graph of repeated calls on the current stream."""
     codes, scales, alpha = nv.quantize(W, "4o6")
     n, k = W.shape
     out = {"weights": f"{n}x{k} NVFP4 (FourOverSix)", "cases": {}}
-    for m in (1, 4096):
+    kernels = {1: "k_w4a16_gemv", 16: "k_w4a16_skinny", 256: "k_w4a16_gemm + k_w4a16_reduce (K split)",
+               4096: "k_w4a16_gemm"}
+    for m in (1, 16, 256, 4096):
         X = (torch.randn((m, k), device=dev) * 0.5).to(torch.bfloat16)
         Y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
-        reps = 200 if m == 1 else 20
+        reps = 200 if m <= 16 else 20
         for _ in range(3):
             nv.matmul(X, codes, scales, alpha, out=Y)
         torch.cuda.synchronize()
@@ -135,7 +138,7 @@ def w4a16_pass(torch, nv, dev, W):
         moved = wbytes + m * k * 2 + m * n * 2
         flops = 2.0 * m * n * k
         out["cases"][f"M={m}"] = {
-            "ms": round(ms, 5), "GBps": round(moved / (ms * 1e-3) / 1e9, 1),
+            "kernel": kernels[m], "ms": round(ms, 5), "GBps": round(moved / (ms * 1e-3) / 1e9, 1),
             "frac_hbm_peak": round(moved / (ms * 1e-3) / PEAK_HBM, 4),
             "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 2),
             "frac_bf16_mfma_peak": round(flops / (ms * 1e-3) / PEAK_BF16_MFMA, 4)}

@@ -440,14 +440,17 @@ __global__ __launch_bounds__(kGemvThreads) void k_w4a16_gemv(const uint16_t *__r
 size_t gemv_lds_bytes(int64_t M, int64_t K) { return (size_t)(M * K * 2); }
 constexpr size_t kGemvMaxLds = 128 * 1024;
 
-// Launch of one GEMV instantiation; the kernel is allowed the large dynamic LDS size once per process
-// (the attribute is per function; two threads setting it at once set the same value).
+// Launch of one GEMV instantiation. Above 64 KB of dynamic LDS the kernel must be allowed the larger
+// size on the current device; the attribute is set before each such launch (a cheap host call), so
+// it holds on whichever device the caller has made current.
 template <int MM, int CH, bool OUTF32>
 hipError_t gemv_launch(dim3 grid, size_t lds, hipStream_t stream, const uint16_t *X, int M, int64_t K,
                        const uint8_t *codes, const uint8_t *scales, const float *alpha, int64_t N, void *Y) {
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_w4a16_gemv<MM, CH, OUTF32>),
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemvMaxLds);
-    if (attr != hipSuccess) return attr;
+    if (lds > 64 * 1024) {
+        const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_w4a16_gemv<MM, CH, OUTF32>),
+                                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemvMaxLds);
+        if (attr != hipSuccess) return attr;
+    }
     hipLaunchKernelGGL((k_w4a16_gemv<MM, CH, OUTF32>), grid, dim3(kGemvThreads), lds, stream, X, M, K, codes,
                        scales, alpha, N, Y);
     return hipGetLastError();
