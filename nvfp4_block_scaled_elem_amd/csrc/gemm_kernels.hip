@@ -132,6 +132,8 @@ __device__ __forceinline__ void gemm_store(const GemmStage &S, uint16_t *xs, uin
 // 256 x 128 output tile per work-group, 4 waves of 128 x 64 (4 x 2 tiles of v_mfma_f32_32x32x16_bf16).
 // The loads of K step t + 1 are issued into registers before the products of step t, so they are in
 // flight while the matrix cores run; one LDS buffer (55 KB) leaves room for two work-groups per CU.
+// Waves raise their issue priority for the products, so a SIMD serves the work-group at its matrix
+// step before the other one's decode and stores.
 // Work-groups go to the 8 XCDs round robin; the tile order is remapped so that each XCD takes a
 // contiguous band of tiles and its L2 holds the few X row blocks that band needs.
 // Split K (when the tiles alone are too few to fill the chip): work-group b takes tile b % tiles and
@@ -188,7 +190,9 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_w4a16_gemm(const uint16_t *
             cp += kBK / 2;
             sp += kBK / 16;
             if (k0 + kBK < kend) gemm_load_full(S, xp, K, cp, sp);
+            __builtin_amdgcn_s_setprio(1);
             mfma_step();
+            __builtin_amdgcn_s_setprio(0);
             __syncthreads();
         }
     } else {
@@ -197,7 +201,9 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_w4a16_gemm(const uint16_t *
             gemm_store(S, xs, ws, tid);
             __syncthreads();
             if (k0 + kBK < kend) gemm_load(S, X, M, K, kend, codes, scales, N, m0, n0, k0 + kBK, tid);
+            __builtin_amdgcn_s_setprio(1);
             mfma_step();
+            __builtin_amdgcn_s_setprio(0);
             __syncthreads();
         }
     }
