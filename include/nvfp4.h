@@ -77,7 +77,7 @@ enum nvfp4_error {
     NVFP4_OK = 0,
     NVFP4_ERR_INVALID_ARG = -1, /* null or misaligned pointer, rows/cols <= 0, unknown mode or dtype,
                                    iters outside [0, 1000] */
-    NVFP4_ERR_SHAPE = -2,       /* cols % 16 != 0, or more than 2^40 elements */
+    NVFP4_ERR_SHAPE = -2,       /* cols % 16 != 0, or more than 2^35 elements */
     NVFP4_ERR_WORKSPACE = -3,   /* caller workspace smaller than nvfp4_workspace_bytes() */
     NVFP4_ERR_HIP = -4          /* a HIP call failed */
 };
@@ -155,7 +155,7 @@ size_t nvfp4_workspace_bytes(int64_t rows, int64_t cols, int mode);
 
 /* Round n binary32 values to E2M1 codes (one code per output byte, same rule as the quantiser:
  * nearest, ties to the even code, saturating at 6, NaN -> 0, negative results that round to zero ->
- * code 0). x and codes are device pointers. */
+ * code 0). x and codes are device pointers; n <= 2^35 (else NVFP4_ERR_SHAPE). */
 int nvfp4_encode_e2m1(const float *x, int64_t n, uint8_t *codes, void *stream);
 
 /* Dequantise codes/scales/alpha (device pointers, layout above; alpha is a device pointer to one

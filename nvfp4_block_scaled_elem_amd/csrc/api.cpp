@@ -15,7 +15,9 @@
 namespace {
 
 constexpr int kMaxIters = 1000;
-constexpr int64_t kMaxElems = (int64_t)1 << 40;
+// At most 2^35 elements per matrix (64 GiB of bf16): kernels with one thread per 16-element block or per
+// 8 values then stay below 2^32 threads per grid.
+constexpr int64_t kMaxElems = (int64_t)1 << 35;
 
 int kernel_count(int mode, int iters) {
     if (iters < 0 || iters > kMaxIters) return -1;
@@ -167,6 +169,7 @@ NVFP4_API int nvfp4_quantize_f32(const float *W, int64_t rows, int64_t cols, int
 
 NVFP4_API int nvfp4_encode_e2m1(const float *x, int64_t n, uint8_t *codes, void *stream) {
     if (!x || !codes || n < 0) return NVFP4_ERR_INVALID_ARG;
+    if (n > kMaxElems) return NVFP4_ERR_SHAPE;
     if (((uintptr_t)codes & 7u) != 0 || ((uintptr_t)x & 3u) != 0) return NVFP4_ERR_INVALID_ARG;
     if (n == 0) return NVFP4_OK;
     return nvfp4::launch_encode_e2m1(x, n, codes, static_cast<hipStream_t>(stream)) == hipSuccess ? NVFP4_OK

@@ -49,7 +49,8 @@ def args(**kw):
 @pytest.mark.parametrize("kw,err", [
     (dict(W=None), INVALID), (dict(codes_out=None), INVALID), (dict(scales_out=None), INVALID),
     (dict(alpha_out=None), INVALID), (dict(rows=0), INVALID), (dict(cols=-16), INVALID),
-    (dict(cols=24), SHAPE), (dict(rows=1 << 40, cols=1 << 20), SHAPE), (dict(mode=4), INVALID),
+    (dict(cols=24), SHAPE), (dict(rows=1 << 40, cols=1 << 20), SHAPE), (dict(rows=(1 << 31) + 1, cols=16), SHAPE),
+    (dict(mode=4), INVALID),
     (dict(mode=-1), INVALID), (dict(dtype=2), INVALID), (dict(iters=-1), INVALID), (dict(iters=1001), INVALID),
     (dict(W=FAKE + 8), INVALID), (dict(codes_out=FAKE + 4), INVALID), (dict(alpha_out=FAKE + 2), INVALID),
     (dict(workspace=FAKE + 64, workspace_bytes=1 << 30), INVALID),
@@ -94,6 +95,7 @@ def test_plain_entry_points_reject(L):
     assert L.nvfp4_encode_e2m1(None, 10, FAKE, None) == INVALID
     assert L.nvfp4_encode_e2m1(FAKE, 10, FAKE + 1, None) == INVALID
     assert L.nvfp4_encode_e2m1(FAKE, 0, FAKE, None) == OK  # nothing to do
+    assert L.nvfp4_encode_e2m1(FAKE, (1 << 35) + 1, FAKE, None) == SHAPE
     assert L.nvfp4_dequantize(FAKE, FAKE, FAKE, 4, 24, FAKE, 0, None) == SHAPE
     assert L.nvfp4_dequantize(FAKE, FAKE, FAKE, 4, 32, FAKE, 3, None) == INVALID
     assert L.nvfp4_dequantize(FAKE, FAKE, FAKE, 4, 32, FAKE + 8, 1, None) == INVALID
