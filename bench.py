@@ -432,6 +432,8 @@ def main():
 
     w4a16 = w4a16_pass(torch, nv, dev, mats[0])
     attainable = hbm_attainable(torch, dev)
+    # the same rate against what a plain copy reaches on this machine (context for the fraction of peak)
+    roofline["frac_of_attainable"] = round(round_gbps / attainable["copy_GBps"], 4)
     c5 = None if args.no_c5 else c5_pass(torch, nv, dev, streams)
 
     value = len(MODES) * ROWS * COLS * 2 / (ms_per_step * 1e-3) / 1e9
