@@ -111,3 +111,43 @@ def test_w4a16_full_size_sample():
         wh = np.abs(oracle.dequantize(c.reshape(n, k // 2)[rows], s.reshape(n, k // 16)[rows], a, rows.size, k))
         bound = (k * 2.0 ** -23 + 2.0 ** -22) * (np.abs(x) @ wh.T)
         assert np.all(np.abs(got - ref) <= bound)
+
+
+def test_w4a16_graph_replays_match_eager():
+    """Every kernel path captured in one graph (GEMV, skinny, K split with its stream-ordered scratch,
+    plain tiles), replayed three times with eager work in between: each replay equals the eager result."""
+    n = 256
+    w = {1024: encoded_weights(n, 1024, 21), 128: encoded_weights(n, 128, 23)}  # K = 128 never splits
+    cases = [(1, 1024), (16, 1024), (96, 1024), (512, 1024), (300, 128)]  # GEMV, skinny, split, split, tiles
+    xs = {c: bf16_dev(synth.normal_bf16(c[0], c[1], seed=100 + c[0], std=1.0)) for c in cases}
+    eager = {c: nv.matmul(xs[c], *w[c[1]]) for c in cases}
+    torch.cuda.synchronize()
+    outs = {c: torch.empty((c[0], n), dtype=torch.bfloat16, device="cuda") for c in cases}
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for c in cases:
+            nv.matmul(xs[c], *w[c[1]], out=outs[c])
+    for rep in range(3):
+        for y in outs.values():
+            y.fill_(0)
+        g.replay()
+        torch.cuda.synchronize()
+        for c in cases:
+            assert torch.equal(outs[c], eager[c]), (rep, c)
+        nv.matmul(xs[cases[0]], *w[1024])  # eager work between replays
+        torch.cuda.synchronize()
+
+
+def test_w4a16_on_a_side_stream():
+    n, k = 200, 512
+    codes, scales, alpha = encoded_weights(n, k, 22)
+    X = bf16_dev(synth.normal_bf16(40, k, seed=7, std=1.0))
+    ref = nv.matmul(X, codes, scales, alpha)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        Y = nv.matmul(X, codes, scales, alpha)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    assert torch.equal(Y, ref)
