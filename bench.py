@@ -29,6 +29,9 @@ c5_whole_model: the 224 matrices of a 7B-shaped model (32 layers; 12.95 GB bf16)
 another in each mode, total time and aggregate GB/s, and the same for its 128 square 4096 x 4096
 matrices alone (skipped with --no-c5).
 
+quality: the reconstruction MSE of each mode and search variant on the first matrix (GPU error statistics),
+and its ratio to the max rule's.
+
 hbm_attainable: a plain 1 GiB device copy timed on the box (read + write bytes / time): the streaming
 rate a kernel can reach here, beside the 8 TB/s figure the roofline uses.
 
@@ -216,6 +219,28 @@ def c5_pass(torch, nv, dev, streams):
         log(f"c5 {mode}: {dt * 1e3:.1f} ms; square matrices {dq * 1e3:.1f} ms")
     del mats
     torch.cuda.empty_cache()
+    return out
+
+
+def quality_pass(torch, nv, W) -> dict:
+    """Reconstruction error of each mode (and of the search variants) on one matrix, from the GPU error
+    statistics: MSE = SSE / n, and its ratio to the max rule's."""
+    n = W.numel()
+    runs = [("max", {}), ("4o6", {}), ("cjso", {"iters": ITERS}), ("cjso", {"iters": ITERS, "init": "4o6"}),
+            ("soar", {"iters": ITERS}), ("soar", {"iters": ITERS, "init": "4o6"}),
+            ("soar", {"iters": ITERS, "grid": (100, 200, 201)}), ("soar", {"iters": ITERS, "dd_rule": "quant"}),
+            ("soar", {"iters": ITERS, "dd_rule": "lsq"})]
+    out = {}
+    for mode, kw in runs:
+        kw = dict(kw)
+        iters = kw.pop("iters", 0)
+        codes, scales, alpha = nv.quantize(W, mode, iters, **kw)
+        sse, _ = nv.error_stats(W, codes, scales, alpha)
+        name = mode + "".join(f" {k}={v}" for k, v in kw.items())
+        out[name] = {"mse": float(sse.item()) / n}
+    base = out["max"]["mse"]
+    for v in out.values():
+        v["vs_max"] = round(v["mse"] / base, 5)
     return out
 
 
@@ -431,6 +456,7 @@ def main():
                 "avg_launch_ms": round(t_round * 1e3, 5), "launches_per_step": 2 * (ITERS - 1)}
 
     w4a16 = w4a16_pass(torch, nv, dev, mats[0])
+    quality = quality_pass(torch, nv, mats[0])
     attainable = hbm_attainable(torch, dev)
     # the same rate against what a plain copy reaches on this machine (context for the fraction of peak)
     roofline["frac_of_attainable"] = round(round_gbps / attainable["copy_GBps"], 4)
@@ -452,6 +478,7 @@ def main():
         "roofline": roofline,
     }
     line["w4a16"] = w4a16
+    line["quality"] = quality
     line["hbm_attainable"] = attainable
     if c5 is not None:
         line["c5_whole_model"] = c5
