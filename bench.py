@@ -30,7 +30,7 @@ another in each mode, total time and aggregate GB/s, and the same for its 128 sq
 matrices alone (skipped with --no-c5).
 
 quality: the reconstruction MSE of each mode and search variant on the first matrix (GPU error statistics),
-and its ratio to the max rule's.
+its ratio to the max rule's, and the time of one call with those settings.
 
 hbm_attainable: a plain 1 GiB device copy timed on the box (read + write bytes / time): the streaming
 rate a kernel can reach here, beside the 8 TB/s figure the roofline uses.
@@ -237,7 +237,14 @@ def quality_pass(torch, nv, W) -> dict:
         codes, scales, alpha = nv.quantize(W, mode, iters, **kw)
         sse, _ = nv.error_stats(W, codes, scales, alpha)
         name = mode + "".join(f" {k}={v}" for k, v in kw.items())
-        out[name] = {"mse": float(sse.item()) / n}
+        # one more call of the same settings, timed alone (the variants scan the whole grid)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        nv.quantize(W, mode, iters, codes=codes, scales=scales, alpha=alpha, **kw)
+        e1.record()
+        torch.cuda.synchronize()
+        out[name] = {"mse": float(sse.item()) / n, "call_ms": round(e0.elapsed_time(e1), 4)}
     base = out["max"]["mse"]
     for v in out.values():
         v["vs_max"] = round(v["mse"] / base, 5)
