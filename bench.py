@@ -32,6 +32,9 @@ matrices alone (skipped with --no-c5).
 quality: the reconstruction MSE of each mode and search variant on the first matrix (GPU error statistics),
 its ratio to the max rule's, and the time of one call with those settings.
 
+c3_mlp: the MLP-shaped matrices (14336 x 4096 and 4096 x 14336 bf16) in FourOverSix and CJSO(8): time,
+GB/s, the M=4 share and the MSE per matrix.
+
 hbm_attainable: a plain 1 GiB device copy timed on the box (read + write bytes / time): the streaming
 rate a kernel can reach here, beside the 8 TB/s figure the roofline uses.
 
@@ -251,6 +254,41 @@ def quality_pass(torch, nv, W) -> dict:
     return out
 
 
+def c3_pass(torch, nv, dev) -> dict:
+    """The MLP-shaped matrices (14336 x 4096 up, 4096 x 14336 down; N(0, 0.015^2) with per-row std
+    log-uniform in [0.5, 2]x, the parity inputs' host generator): FourOverSix then CJSO(8), per matrix
+    the call time (HIP events, mean of 5 calls after a warm-up), GB/s, the M=4 share and the MSE."""
+    import synth
+
+    out = {}
+    for which, name in ((0, "up_14336x4096"), (1, "down_4096x14336")):
+        W0 = synth.c3(which, 0)
+        W = torch.from_numpy(W0.view(np.int16)).view(torch.bfloat16).to(dev)
+        rows, cols = W.shape
+        res = {}
+        for mode, iters in (("4o6", 0), ("cjso", ITERS)):
+            mch = torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev) if mode == "4o6" else None
+            codes, scales, alpha = nv.quantize(W, mode, iters, mchoice=mch)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(5):
+                nv.quantize(W, mode, iters, codes=codes, scales=scales, alpha=alpha, mchoice=mch)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / 5
+            sse, _ = nv.error_stats(W, codes, scales, alpha)
+            r = {"ms": round(ms, 4), "GBps": round(W.numel() * 2 / (ms * 1e-3) / 1e9, 1),
+                 "mse": float(sse.item()) / W.numel()}
+            if mch is not None:
+                r["m4_fraction"] = round(float(mch.float().mean().item()), 4)
+            res[mode] = r
+        out[name] = res
+        del W
+    torch.cuda.empty_cache()
+    return out
+
+
 def hbm_attainable(torch, dev) -> dict:
     """A plain 1 GiB device copy (torch's copy kernel), median of 10: read + write bytes per second."""
     n = (1 << 30) // 4
@@ -464,6 +502,7 @@ def main():
 
     w4a16 = w4a16_pass(torch, nv, dev, mats[0])
     quality = quality_pass(torch, nv, mats[0])
+    c3 = c3_pass(torch, nv, dev)
     attainable = hbm_attainable(torch, dev)
     # the same rate against what a plain copy reaches on this machine (context for the fraction of peak)
     roofline["frac_of_attainable"] = round(round_gbps / attainable["copy_GBps"], 4)
@@ -486,6 +525,7 @@ def main():
     }
     line["w4a16"] = w4a16
     line["quality"] = quality
+    line["c3_mlp"] = c3
     line["hbm_attainable"] = attainable
     if c5 is not None:
         line["c5_whole_model"] = c5
