@@ -35,6 +35,9 @@ its ratio to the max rule's, and the time of one call with those settings.
 c3_mlp: the MLP-shaped matrices (14336 x 4096 and 4096 x 14336 bf16) in FourOverSix and CJSO(8): time,
 GB/s, the M=4 share and the MSE per matrix.
 
+roofline.anatomy: the CJSO round timed the same way at 4096 and 16384 rows; the difference gives the
+round's marginal streaming rate and, extrapolated to zero rows, the fixed cost every launch pays.
+
 hbm_attainable: a plain 1 GiB device copy timed on the box (read + write bytes / time): the streaming
 rate a kernel can reach here, beside the 8 TB/s figure the roofline uses.
 
@@ -289,6 +292,50 @@ def c3_pass(torch, nv, dev) -> dict:
     return out
 
 
+def round_anatomy(torch, nv, dev, nk_cjso) -> dict:
+    """The CJSO round at two heights (4096 and 16384 rows, 4096 columns; six resident matrices each, drawn
+    on the GPU with the whole-model recipe). Round time = span of rounds 1..ITERS-1 over their number
+    (HIP events, median of 18 calls). The difference of the two gives the marginal streaming rate of the
+    round (algorithmic bytes per extra row over time per extra row) and, extrapolated to zero rows, the
+    fixed cost of one launch: the split between what the matrix size pays and what every launch pays."""
+    log("round anatomy: 4096 and 16384 rows")
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    t = {}
+    for rows in (4096, 16384):
+        mats = []
+        for _ in range(6):
+            z = torch.randn((rows, COLS), generator=g, device=dev)
+            chi = torch.zeros((rows, COLS), device=dev)
+            for _ in range(5):
+                chi += torch.randn((rows, COLS), generator=g, device=dev).square()
+            mats.append((z / torch.sqrt(chi / 5.0) * (0.02 / (5.0 / 3.0) ** 0.5)).to(torch.bfloat16))
+            del z, chi
+        o = dict(codes=torch.empty((rows, COLS // 2), dtype=torch.uint8, device=dev),
+                 scales=torch.empty((rows, COLS // 16), dtype=torch.uint8, device=dev),
+                 alpha=torch.empty(1, dtype=torch.float32, device=dev),
+                 workspace=torch.empty(nv.workspace_bytes(rows, COLS, "cjso"), dtype=torch.uint8, device=dev))
+        for i in range(6):
+            nv.quantize(mats[i], "cjso", ITERS, **o)
+        spans = []
+        for s in range(18):
+            ev = [None] * (nk_cjso + 1)
+            ev[2] = torch.cuda.Event(enable_timing=True)
+            ev[2 + ITERS - 1] = torch.cuda.Event(enable_timing=True)
+            nv.quantize(mats[s % 6], "cjso", ITERS, stage_events=ev, **o)
+            spans.append((ev[2], ev[2 + ITERS - 1]))
+        torch.cuda.synchronize()
+        t[rows] = float(np.median([a.elapsed_time(b) for a, b in spans])) / (ITERS - 1) * 1e-3
+        del mats, o
+        torch.cuda.empty_cache()
+    extra_bytes = (16384 - 4096) * COLS * ROUND_BYTES_PER_ELEM
+    marginal = extra_bytes / (t[16384] - t[4096])
+    fixed = t[4096] - 4096 * COLS * ROUND_BYTES_PER_ELEM / marginal
+    return {"round_ms_4096_rows": round(t[4096] * 1e3, 5), "round_ms_16384_rows": round(t[16384] * 1e3, 5),
+            "marginal_GBps": round(marginal / 1e9, 1), "fixed_us_per_launch": round(fixed * 1e6, 2),
+            "method": "two heights, 4096 columns, GPU-drawn Student-t(5) weights; rounds 1..7 span / 7"}
+
+
 def hbm_attainable(torch, dev) -> dict:
     """A plain 1 GiB device copy (torch's copy kernel), median of 10: read + write bytes per second."""
     n = (1 << 30) // 4
@@ -503,9 +550,12 @@ def main():
     w4a16 = w4a16_pass(torch, nv, dev, mats[0])
     quality = quality_pass(torch, nv, mats[0])
     c3 = c3_pass(torch, nv, dev)
+    anatomy = round_anatomy(torch, nv, dev, nk["cjso"])
     attainable = hbm_attainable(torch, dev)
     # the same rate against what a plain copy reaches on this machine (context for the fraction of peak)
     roofline["frac_of_attainable"] = round(round_gbps / attainable["copy_GBps"], 4)
+    anatomy["marginal_frac_of_attainable"] = round(anatomy["marginal_GBps"] / attainable["copy_GBps"], 4)
+    roofline["anatomy"] = anatomy
     c5 = None if args.no_c5 else c5_pass(torch, nv, dev, streams)
 
     value = len(MODES) * ROWS * COLS * 2 / (ms_per_step * 1e-3) / 1e9
