@@ -35,6 +35,9 @@ its ratio to the max rule's, and the time of one call with those settings.
 c3_mlp: the MLP-shaped matrices (14336 x 4096 and 4096 x 14336 bf16) in FourOverSix and CJSO(8): time,
 GB/s, the M=4 share and the MSE per matrix.
 
+step_roofline: the algorithmic bytes of every kernel of a step (25 passes over W and the outputs)
+over the timed step time, against the HBM peak and the measured copy rate.
+
 roofline.anatomy: the CJSO round timed the same way at 4096 and 16384 rows; the difference gives the
 round's marginal streaming rate and, extrapolated to zero rows, the fixed cost every launch pays.
 
@@ -71,6 +74,17 @@ MODES = (("max", 0), ("4o6", 0), ("cjso", ITERS), ("soar", ITERS))
 SEARCH_FLOPS_PER_BLOCK = 101 * 16 * 9
 ROUND_BYTES_PER_ELEM = 2 + 1 / 16 + 1 / 16  # CJSO round (not the last): read W and scale, write scale
 SEARCH_BYTES_PER_ELEM = 2 + 1 / 16 + 2 / 16 + 1 / 2 + 1 / 16  # read W, scale, bracket; write codes, scale
+# algorithmic bytes per element of every kernel of a step (each reads the bf16 block once; outputs as
+# written): codes 1/2, scale and M=4 map 1/16 each, the SOAR bracket 2/16
+STEP_KERNEL_BYTES_PER_ELEM = {
+    "max": [2, 2 + 1 / 2 + 1 / 16],  # k_amax; k_quant: codes and scale
+    "4o6": [2, 2 + 1 / 2 + 1 / 16 + 1 / 16],  # k_amax; k_quant: codes, scale and the M=4 map
+    # k_amax; k_cjso_init: new scale; ITERS-1 rounds; the last round: read scale, write scale and codes
+    "cjso": [2, 2 + 1 / 16] + [ROUND_BYTES_PER_ELEM] * (ITERS - 1) + [2 + 1 / 16 + 1 / 16 + 1 / 2],
+    # as CJSO, the last round also writes the bracket; then the search
+    "soar": [2, 2 + 1 / 16] + [ROUND_BYTES_PER_ELEM] * (ITERS - 1) + [2 + 1 / 16 + 1 / 16 + 1 / 2 + 2 / 16,
+                                                                      SEARCH_BYTES_PER_ELEM],
+}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_k_cjso_iter_4096x4096.txt")
 COPY_BYTES = 256 << 20
 KERNEL_NAMES = {
@@ -79,6 +93,7 @@ KERNEL_NAMES = {
     "cjso": ["k_amax", "k_cjso_init"] + ["k_cjso_iter"] * ITERS,
     "soar": ["k_amax", "k_cjso_init"] + ["k_cjso_iter"] * ITERS + ["k_soar"],
 }
+assert {m: len(v) for m, v in STEP_KERNEL_BYTES_PER_ELEM.items()} == {m: len(v) for m, v in KERNEL_NAMES.items()}
 
 
 def log(msg):
@@ -556,6 +571,13 @@ def main():
     roofline["frac_of_attainable"] = round(round_gbps / attainable["copy_GBps"], 4)
     anatomy["marginal_frac_of_attainable"] = round(anatomy["marginal_GBps"] / attainable["copy_GBps"], 4)
     roofline["anatomy"] = anatomy
+    # the step as a whole: every kernel's algorithmic bytes over the timed step (streams overlapping)
+    step_bytes = nel * sum(sum(v) for v in STEP_KERNEL_BYTES_PER_ELEM.values())
+    step_gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
+    step_roofline = {"algorithmic_bytes_per_step": int(step_bytes), "passes_over_W": sum(
+        len(v) for v in STEP_KERNEL_BYTES_PER_ELEM.values()), "GBps": round(step_gbps, 1),
+        "frac_of_peak": round(step_gbps * 1e9 / PEAK_HBM, 4),
+        "frac_of_attainable": round(step_gbps / attainable["copy_GBps"], 4)}
     c5 = None if args.no_c5 else c5_pass(torch, nv, dev, streams)
 
     value = len(MODES) * ROWS * COLS * 2 / (ms_per_step * 1e-3) / 1e9
@@ -572,6 +594,7 @@ def main():
         "single_stream_ms_per_step": round(single_ms_per_step, 5),
         "graph_replay_ms_per_step": round(graph_ms_per_step, 5),
         "roofline": roofline,
+        "step_roofline": step_roofline,
     }
     line["w4a16"] = w4a16
     line["quality"] = quality
