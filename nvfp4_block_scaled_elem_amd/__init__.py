@@ -97,6 +97,20 @@ def kernel_count(mode: str, iters: int = 0) -> int:
     return int(lib().nvfp4_kernel_count(MODES[mode], iters))
 
 
+STATS_BYTES = 16  # sizeof(nvfp4_stats_t)
+
+
+def _check_buffer(t, name: str, nbytes: int, dev, dtype=None) -> None:
+    """A caller-supplied buffer must be a contiguous tensor on `dev`, of `dtype` when one is given, holding
+    at least `nbytes` bytes: the kernels write through its pointer without knowing its size."""
+    if not t.is_cuda or t.device != dev or not t.is_contiguous():
+        raise NVFP4Error(f"{name} must be a contiguous tensor on {dev}")
+    if dtype is not None and t.dtype != dtype:
+        raise NVFP4Error(f"{name} must be {dtype}, got {t.dtype}")
+    if t.numel() * t.element_size() < nbytes:
+        raise NVFP4Error(f"{name} holds {t.numel() * t.element_size()} bytes, {nbytes} needed")
+
+
 def _stream_ptr(stream, device) -> int:
     if stream is None:
         stream = torch.cuda.current_stream(device)
@@ -126,9 +140,18 @@ def quantize(W: torch.Tensor, mode: str, iters: int = 0, *, codes=None, scales=N
         scales = torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev)
     if alpha is None:
         alpha = torch.empty(1, dtype=torch.float32, device=dev)
-    for t in (codes, scales, alpha, mchoice, stats, workspace):
-        if t is not None and (not t.is_cuda or t.device != dev or not t.is_contiguous()):
-            raise NVFP4Error("outputs and workspace must be contiguous tensors on W's device")
+    if mode not in MODES:
+        raise NVFP4Error(f"unknown mode {mode!r}")
+    nel = rows * cols
+    _check_buffer(codes, "codes", nel // 2, dev, torch.uint8)
+    _check_buffer(scales, "scales", nel // 16, dev, torch.uint8)
+    _check_buffer(alpha, "alpha", 4, dev, torch.float32)
+    if mchoice is not None:
+        _check_buffer(mchoice, "mchoice", nel // 16, dev, torch.uint8)
+    if stats is not None:
+        _check_buffer(stats, "stats", STATS_BYTES, dev)
+    if workspace is not None:
+        _check_buffer(workspace, "workspace", 0, dev)
     need = workspace_bytes(rows, cols, mode) if cols % 16 == 0 and rows > 0 else 0
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -144,7 +167,7 @@ def quantize(W: torch.Tensor, mode: str, iters: int = 0, *, codes=None, scales=N
     a.mchoice_out = mchoice.data_ptr() if mchoice is not None else None
     a.stats_out = stats.data_ptr() if stats is not None else None
     a.workspace = workspace.data_ptr() if workspace is not None else None
-    a.workspace_bytes = workspace.numel() if workspace is not None else 0
+    a.workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     a.stream = _stream_ptr(stream, dev)
     if init not in INITS:
         raise NVFP4Error(f"unknown init {init!r}")
@@ -163,7 +186,8 @@ def quantize(W: torch.Tensor, mode: str, iters: int = 0, *, codes=None, scales=N
             *[e.cuda_event if e is not None else None for e in stage_events])
         a.stage_events = ctypes.cast(ev_arr, ctypes.c_void_p)
         a.n_stage_events = len(stage_events)
-    _check(lib().nvfp4_quantize_ex(ctypes.byref(a)))
+    with torch.cuda.device(dev):
+        _check(lib().nvfp4_quantize_ex(ctypes.byref(a)))
     return codes, scales, alpha
 
 
@@ -172,18 +196,28 @@ def encode_e2m1(x: torch.Tensor, stream=None) -> torch.Tensor:
     if not x.is_cuda or x.dtype != torch.float32 or not x.is_contiguous():
         raise NVFP4Error("x must be a contiguous fp32 CUDA tensor")
     out = torch.empty(x.numel(), dtype=torch.uint8, device=x.device)
-    _check(lib().nvfp4_encode_e2m1(x.data_ptr(), x.numel(), out.data_ptr(), _stream_ptr(stream, x.device)))
+    with torch.cuda.device(x.device):
+        _check(lib().nvfp4_encode_e2m1(x.data_ptr(), x.numel(), out.data_ptr(), _stream_ptr(stream, x.device)))
     return out.view(x.shape)
 
 
 def dequantize(codes: torch.Tensor, scales: torch.Tensor, alpha: torch.Tensor, dtype=torch.bfloat16,
                stream=None) -> torch.Tensor:
     """W_hat = e2m1(code) * e4m3(scale) * alpha as a [rows, cols] bf16 or fp32 tensor."""
+    if codes.dim() != 2:
+        raise NVFP4Error("codes must be [rows, cols/2]")
+    if dtype not in DTYPES:
+        raise NVFP4Error("dtype must be bf16 or fp32")
     rows, half = codes.shape
     cols = 2 * half
-    out = torch.empty((rows, cols), dtype=dtype, device=codes.device)
-    _check(lib().nvfp4_dequantize(codes.data_ptr(), scales.data_ptr(), alpha.data_ptr(), rows, cols,
-                                  out.data_ptr(), DTYPES[dtype], _stream_ptr(stream, codes.device)))
+    dev = codes.device
+    _check_buffer(codes, "codes", rows * half, dev, torch.uint8)
+    _check_buffer(scales, "scales", rows * cols // 16, dev, torch.uint8)
+    _check_buffer(alpha, "alpha", 4, dev, torch.float32)
+    out = torch.empty((rows, cols), dtype=dtype, device=dev)
+    with torch.cuda.device(dev):
+        _check(lib().nvfp4_dequantize(codes.data_ptr(), scales.data_ptr(), alpha.data_ptr(), rows, cols,
+                                      out.data_ptr(), DTYPES[dtype], _stream_ptr(stream, dev)))
     return out
 
 
@@ -195,15 +229,15 @@ def error_stats(W: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, alph
         raise NVFP4Error("W must be a contiguous 2-D bf16 or fp32 CUDA tensor")
     rows, cols = W.shape
     dev = W.device
-    for t in (codes, scales, alpha):
-        if not t.is_cuda or t.device != dev or not t.is_contiguous():
-            raise NVFP4Error("codes, scales and alpha must be contiguous tensors on W's device")
-    if codes.numel() != rows * cols // 2 or scales.numel() != rows * cols // 16 or alpha.numel() < 1:
-        raise NVFP4Error("codes, scales or alpha do not match W's shape")
+    _check_buffer(codes, "codes", rows * cols // 2, dev, torch.uint8)
+    _check_buffer(scales, "scales", rows * cols // 16, dev, torch.uint8)
+    _check_buffer(alpha, "alpha", 4, dev, torch.float32)
     sse = torch.empty(1, dtype=torch.float64, device=dev)
     hist = torch.empty(16, dtype=torch.int64, device=dev)
-    _check(lib().nvfp4_error_stats(W.data_ptr(), DTYPES[W.dtype], rows, cols, codes.data_ptr(), scales.data_ptr(),
-                                   alpha.data_ptr(), sse.data_ptr(), hist.data_ptr(), _stream_ptr(stream, dev)))
+    with torch.cuda.device(dev):
+        _check(lib().nvfp4_error_stats(W.data_ptr(), DTYPES[W.dtype], rows, cols, codes.data_ptr(),
+                                       scales.data_ptr(), alpha.data_ptr(), sse.data_ptr(), hist.data_ptr(),
+                                       _stream_ptr(stream, dev)))
     return sse, hist
 
 
@@ -219,11 +253,9 @@ def matmul(X: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, alpha: to
     if codes.dim() != 2 or codes.shape[1] * 2 != K:
         raise NVFP4Error("codes must be [N, K/2]")
     N = codes.shape[0]
-    for t in (codes, scales, alpha):
-        if not t.is_cuda or t.device != dev or not t.is_contiguous():
-            raise NVFP4Error("codes, scales and alpha must be contiguous tensors on X's device")
-    if scales.numel() != N * K // 16 or alpha.numel() < 1:
-        raise NVFP4Error("scales or alpha do not match the weight shape")
+    _check_buffer(codes, "codes", N * K // 2, dev, torch.uint8)
+    _check_buffer(scales, "scales", N * K // 16, dev, torch.uint8)
+    _check_buffer(alpha, "alpha", 4, dev, torch.float32)
     if out_dtype not in DTYPES:
         raise NVFP4Error("out_dtype must be bf16 or fp32")
     if out is None:
@@ -233,6 +265,7 @@ def matmul(X: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, alpha: to
                 or not out.is_contiguous()):
             raise NVFP4Error("out must be a contiguous [M, N] tensor of out_dtype on X's device")
         Y = out
-    _check(lib().nvfp4_matmul(X.data_ptr(), M, K, codes.data_ptr(), scales.data_ptr(), alpha.data_ptr(), N,
-                              Y.data_ptr(), DTYPES[out_dtype], _stream_ptr(stream, dev)))
+    with torch.cuda.device(dev):
+        _check(lib().nvfp4_matmul(X.data_ptr(), M, K, codes.data_ptr(), scales.data_ptr(), alpha.data_ptr(), N,
+                                  Y.data_ptr(), DTYPES[out_dtype], _stream_ptr(stream, dev)))
     return Y

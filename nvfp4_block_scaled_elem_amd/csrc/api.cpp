@@ -228,7 +228,7 @@ NVFP4_API const char *nvfp4_status_string(int status) {
     switch (status) {
         case NVFP4_OK: return "ok";
         case NVFP4_ERR_INVALID_ARG: return "invalid argument";
-        case NVFP4_ERR_SHAPE: return "unsupported shape (cols must be a multiple of 16)";
+        case NVFP4_ERR_SHAPE: return "unsupported shape (a dimension that must be a multiple of 16 is not, or a size limit is exceeded)";
         case NVFP4_ERR_WORKSPACE: return "workspace too small";
         case NVFP4_ERR_HIP: return "HIP launch or allocation failed";
         default: return "unknown status";
