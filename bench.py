@@ -381,6 +381,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--streams", type=int, default=3, help="HIP streams that consecutive steps rotate over")
     ap.add_argument("--no-c5", action="store_true", help="skip the whole-model (224 matrices) pass")
+    ap.add_argument("--only-4096", action="store_true",
+                    help="skip the passes on other shapes (MLP matrices, round anatomy), so that a profiler "
+                         "averaging per kernel sees only 4096x4096 launches")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device copy 5 times (scales the HBM byte counters)")
     args = ap.parse_args()
@@ -564,13 +567,14 @@ def main():
 
     w4a16 = w4a16_pass(torch, nv, dev, mats[0])
     quality = quality_pass(torch, nv, mats[0])
-    c3 = c3_pass(torch, nv, dev)
-    anatomy = round_anatomy(torch, nv, dev, nk["cjso"])
+    c3 = None if args.only_4096 else c3_pass(torch, nv, dev)
+    anatomy = None if args.only_4096 else round_anatomy(torch, nv, dev, nk["cjso"])
     attainable = hbm_attainable(torch, dev)
     # the same rate against what a plain copy reaches on this machine (context for the fraction of peak)
     roofline["frac_of_attainable"] = round(round_gbps / attainable["copy_GBps"], 4)
-    anatomy["marginal_frac_of_attainable"] = round(anatomy["marginal_GBps"] / attainable["copy_GBps"], 4)
-    roofline["anatomy"] = anatomy
+    if anatomy is not None:
+        anatomy["marginal_frac_of_attainable"] = round(anatomy["marginal_GBps"] / attainable["copy_GBps"], 4)
+        roofline["anatomy"] = anatomy
     # the step as a whole: every kernel's algorithmic bytes over the timed step (streams overlapping)
     step_bytes = nel * sum(sum(v) for v in STEP_KERNEL_BYTES_PER_ELEM.values())
     step_gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
@@ -598,7 +602,8 @@ def main():
     }
     line["w4a16"] = w4a16
     line["quality"] = quality
-    line["c3_mlp"] = c3
+    if c3 is not None:
+        line["c3_mlp"] = c3
     line["hbm_attainable"] = attainable
     if c5 is not None:
         line["c5_whole_model"] = c5

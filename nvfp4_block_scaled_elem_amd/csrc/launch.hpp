@@ -35,7 +35,7 @@ namespace nvfp4 {
 #define NVFP4_CJSO_DEPTH 1
 #endif
 constexpr int kAmaxThreads = 256;
-constexpr int kAmaxMaxGroups = 1024;
+constexpr int kAmaxMaxGroups = 512;
 constexpr int kQuantThreads = NVFP4_QUANT_THREADS;
 constexpr int kQuantGroups = NVFP4_QUANT_GROUPS;
 constexpr int kQuantDepth = NVFP4_QUANT_DEPTH;
