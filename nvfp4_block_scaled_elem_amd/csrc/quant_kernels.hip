@@ -702,14 +702,33 @@ __global__ __launch_bounds__(kStatThreads) void k_stats_final(const double *__re
                                                               const uint32_t *__restrict__ part_hist, int groups,
                                                               double *__restrict__ sse_out,
                                                               unsigned long long *__restrict__ hist_out) {
+    // code counts: thread t adds code t % 16 over every 16th work-group (eight independent loads at a
+    // time, consecutive threads on consecutive words), then the 16 slices of each code are added
+    constexpr int kSlices = kStatThreads / 16;
+    __shared__ unsigned long long slice[kStatThreads];
+    const int code = threadIdx.x & 15, first = threadIdx.x >> 4;
+    unsigned long long n = 0ull;
+    for (int g0 = first; g0 < groups; g0 += 8 * kSlices) {
+        uint32_t v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int g = g0 + u * kSlices;
+            v[u] = g < groups ? part_hist[16 * g + code] : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) n += v[u];
+    }
+    slice[threadIdx.x] = n;
+    lds_barrier();
     dd S = {0.0, 0.0}, Z = {0.0, 0.0};
     for (int g = threadIdx.x; g < groups; g += kStatThreads) S = dd_add(S, dd{part[2 * g], part[2 * g + 1]});
     wg_sum_dd2<kStatThreads>(S, Z);
     if (threadIdx.x == 0) *sse_out = S.hi + S.lo;
     if (threadIdx.x < 16) {
-        unsigned long long n = 0ull;
-        for (int g = 0; g < groups; ++g) n += part_hist[16 * g + threadIdx.x];
-        hist_out[threadIdx.x] = n;
+        unsigned long long t = 0ull;
+#pragma unroll
+        for (int k = 0; k < kSlices; ++k) t += slice[16 * k + threadIdx.x];
+        hist_out[threadIdx.x] = t;
     }
 }
 
