@@ -136,20 +136,20 @@ def w4a16_pass(torch, nv, dev, W):
     bf16 MFMA-bound). Times are HIP-event averages over a graph of repeated calls on the current stream."""
     codes, scales, alpha = nv.quantize(W, "4o6")
     n, k = W.shape
-    out = {"weights": f"{n}x{k} NVFP4 (FourOverSix)", "cases": {}}
-    kernels = {1: "k_w4a16_gemv", 16: "k_w4a16_skinny", 256: "k_w4a16_gemm + k_w4a16_reduce (K split)",
-               4096: "k_w4a16_gemm"}
-    for m in (1, 16, 256, 4096):
-        X = (torch.randn((m, k), device=dev) * 0.5).to(torch.bfloat16)
-        Y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
-        reps = 200 if m <= 16 else 20
+    # context: torch's dense bf16 product (hipBLASLt) on the dequantised weights, same shapes and timing
+    WT = nv.dequantize(codes, scales, alpha, torch.bfloat16).t().contiguous()  # [k, n]
+    out = {"weights": f"{n}x{k} NVFP4 (FourOverSix)", "cases": {},
+           "dense_ref": "torch.matmul bf16 (hipBLASLt) with the dequantised weights, timed the same way"}
+
+    def graph_ms(call, Y, reps):
         for _ in range(3):
-            nv.matmul(X, codes, scales, alpha, out=Y)
+            call()
         torch.cuda.synchronize()
+        eager = Y.clone()
         g = torch.cuda.CUDAGraph()  # the calls back to back on the device, without host overhead between them
         with torch.cuda.graph(g):
             for _ in range(reps):
-                nv.matmul(X, codes, scales, alpha, out=Y)
+                call()
         g.replay()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -157,7 +157,19 @@ def w4a16_pass(torch, nv, dev, W):
         g.replay()
         e1.record()
         torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / reps
+        # a replay must reproduce the eager result (library calls inside a graph are checked, not trusted)
+        return e0.elapsed_time(e1) / reps if torch.equal(Y, eager) else None
+    kernels = {1: "k_w4a16_gemv", 16: "k_w4a16_skinny", 256: "k_w4a16_gemm + k_w4a16_reduce (K split)",
+               4096: "k_w4a16_gemm"}
+    for m in (1, 16, 256, 4096):
+        X = (torch.randn((m, k), device=dev) * 0.5).to(torch.bfloat16)
+        Y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        reps = 200 if m <= 16 else 20
+        ms = graph_ms(lambda: nv.matmul(X, codes, scales, alpha, out=Y), Y, reps)
+        if ms is None:
+            raise RuntimeError(f"W4A16 product, M={m}: a graph replay differs from the eager call")
+        Yd = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        dense_ms = graph_ms(lambda: torch.matmul(X, WT, out=Yd), Yd, reps)
         wbytes = n * k // 2 + n * k // 16
         moved = wbytes + m * k * 2 + m * n * 2
         flops = 2.0 * m * n * k
@@ -165,8 +177,10 @@ def w4a16_pass(torch, nv, dev, W):
             "kernel": kernels[m], "ms": round(ms, 5), "GBps": round(moved / (ms * 1e-3) / 1e9, 1),
             "frac_hbm_peak": round(moved / (ms * 1e-3) / PEAK_HBM, 4),
             "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 2),
-            "frac_bf16_mfma_peak": round(flops / (ms * 1e-3) / PEAK_BF16_MFMA, 4)}
-        log(f"w4a16 M={m}: {ms * 1e3:.1f} us")
+            "frac_bf16_mfma_peak": round(flops / (ms * 1e-3) / PEAK_BF16_MFMA, 4),
+            "dense_ref_ms": None if dense_ms is None else round(dense_ms, 5),
+            "speedup_vs_dense": None if dense_ms is None else round(dense_ms / ms, 2)}
+        log(f"w4a16 M={m}: {ms * 1e3:.1f} us (dense bf16 {dense_ms if dense_ms is None else round(dense_ms * 1e3, 1)} us)")
     return out
 
 
