@@ -29,6 +29,9 @@ c5_whole_model: the 224 matrices of a 7B-shaped model (32 layers; 12.95 GB bf16)
 another in each mode, total time and aggregate GB/s, and the same for its 128 square 4096 x 4096
 matrices alone (skipped with --no-c5).
 
+cold_warm: one call per mode timed alone, "cold" after a 1 GiB fill has evicted the Infinity Cache,
+and "warm" repeated at once.
+
 quality: the reconstruction MSE of each mode and search variant on the first matrix (GPU error statistics),
 its ratio to the max rule's, and the time of one call with those settings.
 
@@ -121,9 +124,16 @@ def cpu_baseline(W0: np.ndarray) -> dict:
     for mode, iters in MODES:
         oracle.quantize(sample, mode, iters)
     dt = time.perf_counter() - t0
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": round(len(MODES) * sample.nbytes / dt / 1e9, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"rows 0-255 of the first 4096x4096 matrix ({sample.size} elements), all four modes, "
-                      f"one thread, {dt:.1f} s"}
+                      f"one thread, {dt:.1f} s",
+            "host": {"nproc": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)), "cpu_model": model}}
 
 
 PEAK_BF16_MFMA = 2.5e15  # FLOP/s, MI355X dense bf16 matrix peak
@@ -365,6 +375,40 @@ def round_anatomy(torch, nv, dev, nk_cjso) -> dict:
             "method": "two heights, 4096 columns, GPU-drawn Student-t(5) weights; rounds 1..7 span / 7"}
 
 
+def cold_warm_pass(torch, nv, W, outs) -> dict:
+    """One call per mode on the first matrix, timed with HIP events around the call: "cold" after a 1 GiB
+    fill has evicted the Infinity Cache and the L2s (outside the timed region), "warm" for the same call
+    repeated at once. Median of 10 of each."""
+    dev = W.device
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    res = {}
+    for mode, iters in MODES:
+        o = outs[mode]
+        call = lambda: nv.quantize(W, mode, iters, codes=o["codes"], scales=o["scales"],  # noqa: E731
+                                   alpha=o["alpha"], mchoice=o["mchoice"], workspace=o["workspace"])
+        cold, warm = [], []
+        for r in range(10):
+            flush.fill_(r)
+            torch.cuda.synchronize()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            ev[0].record()
+            call()
+            ev[1].record()
+            ev[2].record()
+            call()
+            ev[3].record()
+            torch.cuda.synchronize()
+            cold.append(ev[0].elapsed_time(ev[1]))
+            warm.append(ev[2].elapsed_time(ev[3]))
+        c, w = float(np.median(cold)), float(np.median(warm))
+        res[mode] = {"cold_ms": round(c, 5), "warm_ms": round(w, 5),
+                     "cold_GBps": round(W.numel() * 2 / (c * 1e-3) / 1e9, 1),
+                     "warm_GBps": round(W.numel() * 2 / (w * 1e-3) / 1e9, 1)}
+    del flush
+    torch.cuda.empty_cache()
+    return res
+
+
 def hbm_attainable(torch, dev) -> dict:
     """A plain 1 GiB device copy (torch's copy kernel), median of 10: read + write bytes per second."""
     n = (1 << 30) // 4
@@ -579,6 +623,7 @@ def main():
                 "algorithmic_bytes_per_launch": int(nel * ROUND_BYTES_PER_ELEM),
                 "avg_launch_ms": round(t_round * 1e3, 5), "launches_per_step": 2 * (ITERS - 1)}
 
+    cold_warm = cold_warm_pass(torch, nv, mats[0], outs[0])
     w4a16 = w4a16_pass(torch, nv, dev, mats[0])
     quality = quality_pass(torch, nv, mats[0])
     c3 = None if args.only_4096 else c3_pass(torch, nv, dev)
@@ -606,7 +651,8 @@ def main():
         "config": {"workload": "4096x4096 bf16 attention-projection weights, Student-t(nu=4) std 0.02 with 0.1% "
                                "outlier columns x20; 12 resident matrices visited in turn; step = MAX, FourOverSix, "
                                "CJSO(8), SOAR(8) of one matrix; consecutive steps on alternating streams", "rows": ROWS, "cols": COLS, "input_dtype": "bf16",
-                   "matrices": N_MATS, "cjso_iters": ITERS, "parallelism": "single GPU"},
+                   "matrices": N_MATS, "cjso_iters": ITERS, "parallelism": "single GPU",
+                   "input_sha256": hashlib.sha256(W0.tobytes()).hexdigest()},
         "modes": per_mode,
         "streams": n_streams,
         "single_stream_ms_per_step": round(single_ms_per_step, 5),
@@ -614,6 +660,7 @@ def main():
         "roofline": roofline,
         "step_roofline": step_roofline,
     }
+    line["cold_warm"] = cold_warm
     line["w4a16"] = w4a16
     line["quality"] = quality
     if c3 is not None:
