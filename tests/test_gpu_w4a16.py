@@ -93,19 +93,23 @@ def test_w4a16_one_hot_rows_are_exact():
 
 
 def test_w4a16_full_size_sample():
-    """4096 x 4096 weights with M = 1 (GEMV), 8 and 64 (skinny MFMA) and 256 (MFMA tiles, K split):
-    sampled outputs against the oracle."""
+    """4096 x 4096 weights with M = 1 (GEMV), 8, 16 and 64 (skinny MFMA), 256 (MFMA tiles, K split) and
+    4096 (MFMA tiles, whole K: the bench's cases and more): sampled outputs against the oracle. Each
+    output depends only on its own row of X, so every 61st weight row is checked against every row of X
+    (every 61st for M = 4096)."""
     n = k = 4096
     W = synth.c2(0)
     codes, scales, alpha = nv.quantize(bf16_dev(W), "4o6")
     c, s, a = codes.cpu().numpy(), scales.cpu().numpy(), float(alpha.cpu()[0])
     rows = np.arange(0, n, 61)
-    for m in (1, 8, 64, 256):
+    for m in (1, 8, 16, 64, 256, 4096):
         X = synth.normal_bf16(m, k, seed=m, std=1.0)
         say(f"w4a16 full size M={m}")
         Y = nv.matmul(bf16_dev(X), codes, scales, alpha, out_dtype=torch.float32)
         torch.cuda.synchronize()
-        got = Y.cpu().numpy().astype(np.float64)[:, rows]
+        xrows = np.arange(0, m, 61) if m > 256 else np.arange(m)
+        got = Y.cpu().numpy().astype(np.float64)[xrows][:, rows]
+        X = np.ascontiguousarray(X[xrows])
         ref = oracle.matmul(X, c.reshape(n, k // 2)[rows], s.reshape(n, k // 16)[rows], a, rows.size)
         x = indep.as_f32(X).astype(np.float64)
         wh = np.abs(oracle.dequantize(c.reshape(n, k // 2)[rows], s.reshape(n, k // 16)[rows], a, rows.size, k))
