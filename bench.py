@@ -32,6 +32,8 @@ matrices alone (skipped with --no-c5).
 cold_warm: one call per mode timed alone, "cold" after a 1 GiB fill has evicted the Infinity Cache,
 and "warm" repeated at once.
 
+fp32_input: the first matrix widened to fp32, one warm call per mode (the binary32 input path).
+
 quality: the reconstruction MSE of each mode and search variant on the first matrix (GPU error statistics),
 its ratio to the max rule's, and the time of one call with those settings.
 
@@ -409,6 +411,28 @@ def cold_warm_pass(torch, nv, W, outs) -> dict:
     return res
 
 
+def fp32_pass(torch, nv, W) -> dict:
+    """The first matrix widened to fp32 (64 MiB; the same values), one warm call per mode timed with HIP
+    events (median of 5): the binary32 input path. Its search has no exactness window (every block scans
+    all 202 candidates), and its block sums run in binary64."""
+    Wf = W.float().contiguous()
+    res = {}
+    for mode, iters in MODES:
+        nv.quantize(Wf, mode, iters)
+        ts = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            nv.quantize(Wf, mode, iters)
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ms = float(np.median(ts))
+        res[mode] = {"ms": round(ms, 5), "GBps": round(Wf.numel() * 4 / (ms * 1e-3) / 1e9, 1)}
+    del Wf
+    return res
+
+
 def hbm_attainable(torch, dev) -> dict:
     """A plain 1 GiB device copy (torch's copy kernel), median of 10: read + write bytes per second."""
     n = (1 << 30) // 4
@@ -624,6 +648,7 @@ def main():
                 "avg_launch_ms": round(t_round * 1e3, 5), "launches_per_step": 2 * (ITERS - 1)}
 
     cold_warm = cold_warm_pass(torch, nv, mats[0], outs[0])
+    fp32 = fp32_pass(torch, nv, mats[0])
     w4a16 = w4a16_pass(torch, nv, dev, mats[0])
     quality = quality_pass(torch, nv, mats[0])
     c3 = None if args.only_4096 else c3_pass(torch, nv, dev)
@@ -661,6 +686,7 @@ def main():
         "step_roofline": step_roofline,
     }
     line["cold_warm"] = cold_warm
+    line["fp32_input"] = fp32
     line["w4a16"] = w4a16
     line["quality"] = quality
     if c3 is not None:

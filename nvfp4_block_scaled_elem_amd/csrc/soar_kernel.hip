@@ -30,8 +30,8 @@
 // first minimiser, unless that is K1 itself: then every k < K1 with A_d(k) = A_d(K1) has exactly the same
 // codes (a larger magnitude strictly raises psi_j there), so it only matters when the two reconstruct
 // scales tie exactly, and that rare case walks down to the first k with the codes of K1.
-// The full scan over k remains for blocks outside the exactness window of the binary32 sums or of
-// binary64 A_d, for fp32 input, and for the two variant rules.
+// The full scan over k remains for blocks outside the exactness window of the block sums or of
+// binary64 A_d, and for the two variant rules.
 #include <float.h>
 
 #include "block.hpp"
@@ -98,17 +98,27 @@ __device__ __forceinline__ void scan(const Blk<F32> &B, const float *__restrict_
     }
 }
 
-// A_d at quantisation scale s (bf16 block inside the exactness window), with its codes.
-__device__ __forceinline__ double eval_s(const Blk<false> &B, float s, double h, uint32_t &c0, uint32_t &c1) {
+// A_d at quantisation scale s (a block inside the exactness window), with its codes. bf16 blocks sum in
+// binary32 dot products (exact there), fp32 blocks in binary64 (each product has at most 26 significant
+// bits and the sums stay on a lattice of about 40 bits, so they are exact too).
+template <bool F32>
+__device__ __forceinline__ double eval_s(const Blk<F32> &B, float s, double h, uint32_t &c0, uint32_t &c1) {
     encode16(B.w, 1.0f / s, c0, c1);
-    float sw, sq;
-    sums_bf16(c0, c1, B.p, sw, sq);
-    return fma(h, (double)sq, -(double)sw);
+    if constexpr (F32) {
+        double sw, sq;
+        sums_f64(c0, c1, B.w, sw, sq);
+        return fma(h, sq, -sw);
+    } else {
+        float sw, sq;
+        sums_bf16(c0, c1, B.p, sw, sq);
+        return fma(h, (double)sq, -(double)sw);
+    }
 }
 
-__device__ __forceinline__ double eval_k(const Blk<false> &B, float alpha, float vc, const float *ftab, int k,
+template <bool F32>
+__device__ __forceinline__ double eval_k(const Blk<F32> &B, float alpha, float vc, const float *ftab, int k,
                                          double h, uint32_t &c0, uint32_t &c1) {
-    return eval_s(B, quant_scale(alpha, vc, ftab, k), h, c0, c1);
+    return eval_s<F32>(B, quant_scale(alpha, vc, ftab, k), h, c0, c1);
 }
 
 // The window [kA, kB] for reconstruct scale s_d (exact in binary64): kA = max(K1, 0),
@@ -138,7 +148,8 @@ __device__ __forceinline__ void window(float alpha, float vc, float vd, double s
 }
 
 // First k <= kA whose codes equal those at kA (the start of A_d's plateau ending at kA).
-__device__ __forceinline__ int plateau_start(const Blk<false> &B, float alpha, float vc, const float *ftab, int kA,
+template <bool F32>
+__device__ __forceinline__ int plateau_start(const Blk<F32> &B, float alpha, float vc, const float *ftab, int kA,
                                              uint32_t c0, uint32_t c1) {
     int k = kA;
     while (k > 0) {
@@ -261,15 +272,18 @@ __global__ __launch_bounds__(kSoarThreads) void k_soar(const void *__restrict__ 
     double best_lo, best_hi, a_c;
     int k_lo, k_hi;
 
+    // A_d lies on the lattice 2^L with |A_d| < 2^M: exact in binary64 when M - L <= 53. A product w q
+    // with q != 0 has |w| >= 2^(E-3) (2^E <= smin), so its lowest bit is at least 2^(E-11) for bf16
+    // (8 significant bits, q a multiple of 1/2) and 2^(E-27) for fp32 (24 bits); s_d / 2 * S_qq is a
+    // multiple of 2^(ilogb(s_d / 2) - 29) (alpha * Delta_d has at most 28 bits, S_qq is a multiple of 1/4).
     bool windowed = false;
-    if constexpr (!F32) {
-        // A_d lies on the lattice 2^L with |A_d| < 2^M (see block.hpp): exact in binary64 when M - L <= 53
-        const int L = min(ilogb(hlo) - 29, ilogbf(smin) - 11);
+    {
+        const int L = min(ilogb(hlo) - 29, ilogbf(smin) - (F32 ? 27 : 11));
         const int M = max(ilogb(hhi) + 11, ilogbf(a) + 8);
         windowed = !full_search && rfin && a <= 32.0f * smin && a <= 0x1p100f && hlo > 0.0 && smin > 0.0f &&
                    M - L <= 53;
     }
-    if constexpr (!F32) {
+    {
         if (windowed) {
             // the incumbent, then the first minimiser of A_d in each reconstruct scale's window
             const double sd_c = c_is_lo ? slo : shi, h_c = c_is_lo ? hlo : hhi;

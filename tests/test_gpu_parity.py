@@ -352,6 +352,13 @@ WINDOW_CASES = {
     "sparse_0": lambda: sparse_bf16(0),
     "sparse_1": lambda: sparse_bf16(1),
     "ragged_3x48": lambda: synth.normal_bf16(3, 48, 5),
+    # fp32 input: the same window with binary64 block sums
+    "c1_fp32": lambda: synth.c1(0),
+    "c2_widened_fp32": lambda: np.ascontiguousarray(indep.as_f32(synth.c2(0))),
+    "normal_fp32": lambda: synth.normal_f32(512, 2048, seed=7),
+    "coarse_fp32": lambda: np.ascontiguousarray(indep.as_f32(coarse_bf16(2))),
+    "sparse_fp32": lambda: np.ascontiguousarray(indep.as_f32(sparse_bf16(2))),
+    "ragged_fp32_3x48": lambda: synth.normal_f32(3, 48, seed=5),
 }
 
 
