@@ -387,6 +387,7 @@ def test_soar_window_equals_full_search(name, iters):
 def test_soar_tie_prone_inputs_match_oracle(gen, seed):
     W = gen(seed)
     compare_live(W, "soar", 8)
+    compare_live(np.ascontiguousarray(indep.as_f32(W)), "soar", 8)  # the same values as fp32 input
 
 
 # ------------------------------------------------------------------- CJSO / SOAR from FourOverSix
