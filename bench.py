@@ -13,7 +13,8 @@ hardware queues a process gets; two streams give about 10 % less, four share a q
 `single_stream_ms_per_step` gives the same steps on one stream. `value` is the weight bytes quantised per second (4 x 32 MiB per step). Per mode the JSON line
 also gives its own GB/s and its share of the HBM peak.
 
-The dominant kernel is the CJSO round (k_cjso_iter): sixteen of them per step. It is timed live: the
+The dominant kernel is the CJSO round (k_cjso_iter): sixteen launches per step, fourteen of them rounds
+other than the last (the roofline kernel). It is timed live: the
 library records HIP events around each of its kernels on the stream it launches them on (the
 `stage_events` hook of the C ABI). Its achieved rate is algorithmic bytes / duration against the 8 TB/s
 HBM peak; a round that is not the last reads the block (2 B per element) and its scale byte and writes
@@ -52,7 +53,8 @@ rate a kernel can reach here, beside the 8 TB/s figure the roofline uses.
 cpu_baseline: the oracle (plain C, one thread) on rows 0..255 of the first matrix in all four modes;
 speedup_vs_cpu is value / cpu_baseline.value.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--streams S]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--streams S] [--no-c5]
+                       [--only-4096] [--calibrate-copy]
 """
 from __future__ import annotations
 
