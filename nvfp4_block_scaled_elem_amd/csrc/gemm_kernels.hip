@@ -15,10 +15,11 @@
 //   k_w4a16_skinny (M <= 64 otherwise): 16 weight rows per work-group, K split over its 16 waves, the
 //     products on v_mfma_f32_16x16x32_bf16 with weights decoded straight into the A operand.
 //   k_w4a16_gemm (M > 64): 256 x 128 output tile per work-group (4 waves, 128 x 64 each as 4 x 2 tiles of
-//     v_mfma_f32_32x32x16_bf16), K in steps of 64 through LDS: the X tile is copied, the weight tile is
-//     decoded to bf16 (codes -> binary32 q, times Delta, high half) once per work-group as it is stored,
-//     and the next step's loads are in flight while the matrix cores work on this one. When the tiles
-//     are too few to fill the GPU, K is split and k_w4a16_reduce adds the slices.
+//     v_mfma_f32_32x32x16_bf16; 256 x 64 with waves of 64 x 64 for M <= 512), K in steps of 64 through
+//     LDS: the X tile is copied, the weight tile is decoded to bf16 (codes -> binary32 q, times Delta,
+//     high half) once per work-group as it is stored, and the next step's loads are in flight while the
+//     matrix cores work on this one. When the tiles are too few to fill the GPU, K is split and
+//     k_w4a16_reduce adds the slices.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -35,6 +36,18 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kGemmThreads = 256;
 constexpr int kBM = 256, kBN = 128, kBK = 64;
+
+// Tile shapes: 256 x TN outputs per work-group, TN = 128 (large M) or 64 (fewer rows of X, so that more
+// tiles and fewer K slices fill the GPU). Four waves: 2 x 2 of 128 x 64 for TN = 128, 4 x 1 of 64 x 64
+// for TN = 64. A weight row of a K step (64 k, 32 bytes of codes) is loaded by 256 / TN threads.
+template <int TN>
+struct TileCfg {
+    static constexpr int kWavesN = TN == 128 ? 2 : 1, kWavesM = 4 / kWavesN;
+    static constexpr int kWaveM = kBM / kWavesM, kWaveN = TN / kWavesN;  // the wave's corner of the tile
+    static constexpr int kMI = kWaveM / 32, kNJ = kWaveN / 32;            // 32 x 32 MFMA tiles per wave
+    static constexpr int kRowThreads = kGemmThreads / TN;                // threads per weight row
+    static constexpr int kThreadK = kBK / kRowThreads;                   // k per thread: 32 or 16
+};
 constexpr int kLdsStride = kBK + 8;  // bf16 per LDS row: the padding spreads the rows a wave reads over the banks
 
 // 8 codes (one dword) and their scale value -> 8 dequantised weights (without alpha) as bf16 pairs.
@@ -77,6 +90,7 @@ struct GemmStage {
 
 // k < kend is loaded (kend = K, or the end of a split-K slice: a multiple of the K step); K is the row
 // length.
+template <int TN>
 __device__ __forceinline__ void gemm_load(GemmStage &S, const uint16_t *__restrict__ X, int64_t M, int64_t K,
                                           int64_t kend, const uint8_t *__restrict__ codes,
                                           const uint8_t *__restrict__ scales, int64_t N, int64_t m0, int64_t n0,
@@ -88,12 +102,17 @@ __device__ __forceinline__ void gemm_load(GemmStage &S, const uint16_t *__restri
         S.x[p] = make_uint4(0u, 0u, 0u, 0u);
         if (m < M && k < kend) S.x[p] = *reinterpret_cast<const uint4 *>(X + m * K + k);  // K % 16 == 0
     }
-    const int64_t n = n0 + (tid >> 1), k = k0 + 32 * (tid & 1);
+    using C = TileCfg<TN>;
+    const int64_t n = n0 + tid / C::kRowThreads, k = k0 + C::kThreadK * (tid % C::kRowThreads);
     S.c = make_uint4(0u, 0u, 0u, 0u);
     S.sc = 0u;
     if (n < N && k < kend) {
         const int64_t e = n * K + k;  // element index, a multiple of 16
-        if (k + 32 <= kend) {
+        if (C::kThreadK == 16) {  // 16 k: 8 bytes of codes, one scale byte (K % 16 == 0)
+            const uint2 c2 = *reinterpret_cast<const uint2 *>(codes + e / 2);
+            S.c = make_uint4(c2.x, c2.y, 0u, 0u);
+            S.sc = (uint32_t)scales[e / 16];
+        } else if (k + 32 <= kend) {
             S.c = *reinterpret_cast<const uint4 *>(codes + e / 2);
             S.sc = (uint32_t)scales[e / 16] | ((uint32_t)scales[e / 16 + 1] << 8);
         } else {  // K % 32 == 16: the last 16 k of the row
@@ -106,32 +125,44 @@ __device__ __forceinline__ void gemm_load(GemmStage &S, const uint16_t *__restri
 
 // The unmasked form for a work-group whose tile and K slice lie inside the matrices: xp points at X row
 // m0 + tid / 8, column k0 + 8 (tid % 8) (row p of the thread adds 32 p K), cp at the codes of weight row
-// n0 + tid / 2 from k0 + 32 (tid % 2), sp at their two scale bytes.
+// n0 + tid / R from k0 + kThreadK (tid % R) (R threads per weight row), sp at their scale bytes.
+template <int TN>
 __device__ __forceinline__ void gemm_load_full(GemmStage &S, const uint16_t *__restrict__ xp, int64_t K,
                                                const uint8_t *__restrict__ cp, const uint8_t *__restrict__ sp) {
 #pragma unroll
     for (int p = 0; p < 8; ++p) S.x[p] = *reinterpret_cast<const uint4 *>(xp + p * 32 * K);
-    S.c = *reinterpret_cast<const uint4 *>(cp);
-    S.sc = (uint32_t)sp[0] | ((uint32_t)sp[1] << 8);
+    if (TileCfg<TN>::kThreadK == 16) {
+        const uint2 c2 = *reinterpret_cast<const uint2 *>(cp);
+        S.c = make_uint4(c2.x, c2.y, 0u, 0u);
+        S.sc = (uint32_t)sp[0];
+    } else {
+        S.c = *reinterpret_cast<const uint4 *>(cp);
+        S.sc = (uint32_t)sp[0] | ((uint32_t)sp[1] << 8);
+    }
 }
 
+template <int TN>
 __device__ __forceinline__ void gemm_store(const GemmStage &S, uint16_t *xs, uint16_t *ws, int tid) {
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
         const int idx = tid + p * kGemmThreads;
         *reinterpret_cast<uint4 *>(&xs[(idx >> 3) * kLdsStride + 8 * (idx & 7)]) = S.x[p];
     }
-    const float d0 = e4m3_value(S.sc & 0x7Fu), d1 = e4m3_value((S.sc >> 8) & 0x7Fu);
-    uint16_t *dst = &ws[(tid >> 1) * kLdsStride + 32 * (tid & 1)];
+    using C = TileCfg<TN>;
+    const float d0 = e4m3_value(S.sc & 0x7Fu);
+    uint16_t *dst = &ws[(tid / C::kRowThreads) * kLdsStride + C::kThreadK * (tid % C::kRowThreads)];
     *reinterpret_cast<uint4 *>(dst) = dequant8(S.c.x, d0);
     *reinterpret_cast<uint4 *>(dst + 8) = dequant8(S.c.y, d0);
-    *reinterpret_cast<uint4 *>(dst + 16) = dequant8(S.c.z, d1);
-    *reinterpret_cast<uint4 *>(dst + 24) = dequant8(S.c.w, d1);
+    if (C::kThreadK == 32) {
+        const float d1 = e4m3_value((S.sc >> 8) & 0x7Fu);
+        *reinterpret_cast<uint4 *>(dst + 16) = dequant8(S.c.z, d1);
+        *reinterpret_cast<uint4 *>(dst + 24) = dequant8(S.c.w, d1);
+    }
 }
 
-// 256 x 128 output tile per work-group, 4 waves of 128 x 64 (4 x 2 tiles of v_mfma_f32_32x32x16_bf16).
-// The loads of K step t + 1 are issued into registers before the products of step t, so they are in
-// flight while the matrix cores run; one LDS buffer (55 KB) leaves room for two work-groups per CU.
+// 256 x TN output tile per work-group (TileCfg: 4 waves of 128 x 64 for TN = 128, of 64 x 64 for TN = 64,
+// each as tiles of v_mfma_f32_32x32x16_bf16). The loads of K step t + 1 are issued into registers before the products of step t, so they are in
+// flight while the matrix cores run; one LDS buffer (55 KB; 46 KB for TN = 64) leaves room for two work-groups per CU.
 // Waves raise their issue priority for the products, so a SIMD serves the work-group at its matrix
 // step before the other one's decode and stores.
 // Work-groups go to the 8 XCDs round robin; the tile order is remapped so that each XCD takes a
@@ -139,7 +170,7 @@ __device__ __forceinline__ void gemm_store(const GemmStage &S, uint16_t *xs, uin
 // Split K (when the tiles alone are too few to fill the chip): work-group b takes tile b % tiles and
 // the K slice b / tiles of kslice elements, and writes its fp32 sums without alpha to
 // part[slice][M][N]; k_w4a16_reduce adds the slices in order. With one slice it writes Y directly.
-template <bool OUTF32>
+template <int TN, bool OUTF32>
 __global__ __launch_bounds__(kGemmThreads, 2) void k_w4a16_gemm(const uint16_t *__restrict__ X, int64_t M, int64_t K,
                                                              const uint8_t *__restrict__ codes,
                                                              const uint8_t *__restrict__ scales,
@@ -147,60 +178,62 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_w4a16_gemm(const uint16_t *
                                                              void *__restrict__ Y, unsigned tiles_n, unsigned tiles,
                                                              int64_t kslice, float *__restrict__ part) {
     __shared__ __attribute__((aligned(16))) uint16_t xs[kBM * kLdsStride];
-    __shared__ __attribute__((aligned(16))) uint16_t ws[kBN * kLdsStride];
+    __shared__ __attribute__((aligned(16))) uint16_t ws[TN * kLdsStride];
+    using C = TileCfg<TN>;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const unsigned total = gridDim.x;  // 1-D grid: slices * tiles_m * tiles_n, tiles row-major
     unsigned b = blockIdx.x;
     if (total % 8 == 0) b = (b % 8) * (total / 8) + b / 8;
     const unsigned slice = b / tiles, t = b % tiles;
-    const int64_t m0 = (int64_t)(t / tiles_n) * kBM, n0 = (int64_t)(t % tiles_n) * kBN;
+    const int64_t m0 = (int64_t)(t / tiles_n) * kBM, n0 = (int64_t)(t % tiles_n) * TN;
     const int64_t kbeg = (int64_t)slice * kslice, kend = min(K, kbeg + kslice);
-    const int wm = (wave >> 1) * 128, wn = (wave & 1) * 64;  // the wave's 128 x 64 corner of the tile
-    f32x16 acc[4][2] = {};
+    const int wm = (wave / C::kWavesN) * C::kWaveM, wn = (wave % C::kWavesN) * C::kWaveN;  // the wave's corner
+    f32x16 acc[C::kMI][C::kNJ] = {};
     GemmStage S;
     // the products of one K step from the staged tiles
     auto mfma_step = [&]() {
 #pragma unroll
         for (int kk = 0; kk < kBK; kk += 16) {
-            bf16x8 a[4], bb[2];
+            bf16x8 a[C::kMI], bb[C::kNJ];
             // A operand: row (lane % 32) of a 32-row tile, k = 8 * (lane / 32) .. + 7; B: column lane % 32
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < C::kMI; ++i)
                 a[i] = *reinterpret_cast<const bf16x8 *>(&xs[(wm + 32 * i + (lane & 31)) * kLdsStride + kk + 8 * (lane >> 5)]);
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < C::kNJ; ++j)
                 bb[j] = *reinterpret_cast<const bf16x8 *>(&ws[(wn + 32 * j + (lane & 31)) * kLdsStride + kk + 8 * (lane >> 5)]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < C::kMI; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
+                for (int j = 0; j < C::kNJ; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bb[j], acc[i][j], 0, 0, 0);
         }
     };
-    const bool full = m0 + kBM <= M && n0 + kBN <= N && (kend - kbeg) % kBK == 0;  // uniform
+    const bool full = m0 + kBM <= M && n0 + TN <= N && (kend - kbeg) % kBK == 0;  // uniform
     if (full) {
         const uint16_t *xp = X + (m0 + (tid >> 3)) * K + kbeg + 8 * (tid & 7);
-        const int64_t e = (n0 + (tid >> 1)) * K + kbeg + 32 * (tid & 1);  // element index, a multiple of 16
+        // element index, a multiple of 16
+        const int64_t e = (n0 + tid / C::kRowThreads) * K + kbeg + C::kThreadK * (tid % C::kRowThreads);
         const uint8_t *cp = codes + e / 2, *sp = scales + e / 16;
-        gemm_load_full(S, xp, K, cp, sp);
+        gemm_load_full<TN>(S, xp, K, cp, sp);
         for (int64_t k0 = kbeg; k0 < kend; k0 += kBK) {
-            gemm_store(S, xs, ws, tid);
+            gemm_store<TN>(S, xs, ws, tid);
             __syncthreads();
             xp += kBK;
             cp += kBK / 2;
             sp += kBK / 16;
-            if (k0 + kBK < kend) gemm_load_full(S, xp, K, cp, sp);
+            if (k0 + kBK < kend) gemm_load_full<TN>(S, xp, K, cp, sp);
             __builtin_amdgcn_s_setprio(1);
             mfma_step();
             __builtin_amdgcn_s_setprio(0);
             __syncthreads();
         }
     } else {
-        gemm_load(S, X, M, K, kend, codes, scales, N, m0, n0, kbeg, tid);
+        gemm_load<TN>(S, X, M, K, kend, codes, scales, N, m0, n0, kbeg, tid);
         for (int64_t k0 = kbeg; k0 < kend; k0 += kBK) {
-            gemm_store(S, xs, ws, tid);
+            gemm_store<TN>(S, xs, ws, tid);
             __syncthreads();
-            if (k0 + kBK < kend) gemm_load(S, X, M, K, kend, codes, scales, N, m0, n0, k0 + kBK, tid);
+            if (k0 + kBK < kend) gemm_load<TN>(S, X, M, K, kend, codes, scales, N, m0, n0, k0 + kBK, tid);
             __builtin_amdgcn_s_setprio(1);
             mfma_step();
             __builtin_amdgcn_s_setprio(0);
@@ -213,13 +246,13 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_w4a16_gemm(const uint16_t *
     const int64_t mb = m0 + wm + 4 * (lane >> 5), nb = n0 + wn + (lane & 31);  // the lane's first row, column
     const int64_t yb = mb * N + nb;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < C::kMI; ++i)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
             const int r = 32 * i + 8 * (e >> 2) + (e & 3);  // row offset from mb
             const int64_t yr = yb + r * N;
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
+            for (int j = 0; j < C::kNJ; ++j) {
                 if (!full && (mb + r >= M || nb + 32 * j >= N)) continue;
                 if (dst)
                     dst[yr + 32 * j] = acc[i][j][e];
@@ -478,11 +511,14 @@ hipError_t gemv_dispatch(int64_t chunks, bool out_f32, dim3 grid, size_t lds, hi
 
 // Split K when the output tiles alone give fewer than 512 work-groups (two per CU): slices of at least four
 // K steps, as many as bring the count to 512, and a partial buffer of at most 1 GiB.
+#ifndef NVFP4_SPLIT_TARGET
+#define NVFP4_SPLIT_TARGET 512
+#endif
 void split_k(int64_t tiles, int64_t M, int64_t N, int64_t K, int64_t &slices, int64_t &kslice) {
     slices = 1;
     kslice = K;
     const int64_t steps = (K + kBK - 1) / kBK;
-    int64_t want = (512 + tiles - 1) / tiles;
+    int64_t want = (NVFP4_SPLIT_TARGET + tiles - 1) / tiles;
     want = std::min(want, steps / 4);
     while (want > 1 && want * M * N * (int64_t)sizeof(float) > ((int64_t)1 << 30)) --want;
     if (want <= 1) return;
@@ -527,7 +563,13 @@ hipError_t launch_w4a16(const uint16_t *X, int64_t M, int64_t K, const uint8_t *
 #undef NVFP4_SKINNY
         return hipGetLastError();
     }
-    const int64_t tiles_n = (N + kBN - 1) / kBN, tiles_m = (M + kBM - 1) / kBM, tiles = tiles_n * tiles_m;
+#ifndef NVFP4_NARROW_MAX_M
+#define NVFP4_NARROW_MAX_M 512
+#endif
+    // 256 x 64 tiles up to 512 rows of X: twice the tiles, so K is split into half as many, longer
+    // slices (13-15 % faster than 256 x 128 at 65 <= M <= 256 on 4096 x 4096 weights, equal from 1024)
+    const int tn = M <= NVFP4_NARROW_MAX_M ? 64 : kBN;
+    const int64_t tiles_n = (N + tn - 1) / tn, tiles_m = (M + kBM - 1) / kBM, tiles = tiles_n * tiles_m;
     int64_t slices = 1, kslice = K;
     split_k(tiles, M, N, K, slices, kslice);
     float *part = nullptr;
@@ -537,12 +579,15 @@ hipError_t launch_w4a16(const uint16_t *X, int64_t M, int64_t K, const uint8_t *
             return hipErrorOutOfMemory;
     }
     const dim3 grid((unsigned)(tiles * slices)), block(kGemmThreads);
-    if (out_f32)
-        hipLaunchKernelGGL(k_w4a16_gemm<true>, grid, block, 0, stream, X, M, K, codes, scales, alpha, N, Y,
-                           (unsigned)tiles_n, (unsigned)tiles, kslice, part);
-    else
-        hipLaunchKernelGGL(k_w4a16_gemm<false>, grid, block, 0, stream, X, M, K, codes, scales, alpha, N, Y,
-                           (unsigned)tiles_n, (unsigned)tiles, kslice, part);
+#define NVFP4_GEMM(TN, F)                                                                                     \
+    hipLaunchKernelGGL((k_w4a16_gemm<TN, F>), grid, block, 0, stream, X, M, K, codes, scales, alpha, N, Y,           \
+                       (unsigned)tiles_n, (unsigned)tiles, kslice, part)
+    if (tn == 64) {
+        if (out_f32) NVFP4_GEMM(64, true); else NVFP4_GEMM(64, false);
+    } else {
+        if (out_f32) NVFP4_GEMM(128, true); else NVFP4_GEMM(128, false);
+    }
+#undef NVFP4_GEMM
     hipError_t err = hipGetLastError();
     if (slices > 1) {
         if (err == hipSuccess) {
