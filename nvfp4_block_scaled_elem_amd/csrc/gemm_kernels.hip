@@ -15,7 +15,8 @@
 //   k_w4a16_skinny (M <= 64 otherwise): 16 weight rows per work-group, K split over its 16 waves, the
 //     products on v_mfma_f32_16x16x32_bf16 with weights decoded straight into the A operand.
 //   k_w4a16_gemm (M > 64): 256 x 128 output tile per work-group (4 waves, 128 x 64 each as 4 x 2 tiles of
-//     v_mfma_f32_32x32x16_bf16; 256 x 64 with waves of 64 x 64 for M <= 512), K in steps of 64 through
+//     v_mfma_f32_32x32x16_bf16; 256 x 64 for M <= 512 and 128 x 128 when the 256 x 128 tiles would not
+//     fill the GPU, both with waves of 64 x 64), K in steps of 64 through
 //     LDS: the X tile is copied, the weight tile is decoded to bf16 (codes -> binary32 q, times Delta,
 //     high half) once per work-group as it is stored, and the next step's loads are in flight while the
 //     matrix cores work on this one. When the tiles are too few to fill the GPU, K is split and
@@ -37,13 +38,16 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kGemmThreads = 256;
 constexpr int kBM = 256, kBN = 128, kBK = 64;
 
-// Tile shapes: 256 x TN outputs per work-group, TN = 128 (large M) or 64 (fewer rows of X, so that more
-// tiles and fewer K slices fill the GPU). Four waves: 2 x 2 of 128 x 64 for TN = 128, 4 x 1 of 64 x 64
-// for TN = 64. A weight row of a K step (64 k, 32 bytes of codes) is loaded by 256 / TN threads.
-template <int TN>
+// Tile shapes: TM x TN outputs per work-group: 256 x 128 (large M), 128 x 128 (middle M: more
+// work-groups, three per CU) and 256 x 64 (few rows of X: more tiles, so fewer and longer K slices).
+// Four waves: 2 x 2 for TN = 128 (128 x 64 or 64 x 64 each), 4 x 1 of 64 x 64 for TN = 64. A K step
+// (64 k) of X is TM / 32 16-byte loads per thread; a weight row of it (32 bytes of codes) is loaded by
+// 256 / TN threads.
+template <int TM, int TN>
 struct TileCfg {
+    static constexpr int kXLoads = TM / 32;
     static constexpr int kWavesN = TN == 128 ? 2 : 1, kWavesM = 4 / kWavesN;
-    static constexpr int kWaveM = kBM / kWavesM, kWaveN = TN / kWavesN;  // the wave's corner of the tile
+    static constexpr int kWaveM = TM / kWavesM, kWaveN = TN / kWavesN;  // the wave's corner of the tile
     static constexpr int kMI = kWaveM / 32, kNJ = kWaveN / 32;            // 32 x 32 MFMA tiles per wave
     static constexpr int kRowThreads = kGemmThreads / TN;                // threads per weight row
     static constexpr int kThreadK = kBK / kRowThreads;                   // k per thread: 32 or 16
@@ -82,27 +86,28 @@ __device__ __forceinline__ void store_y(void *Y, int64_t idx, float v) {
 // One K step of a work-group's operands, held in registers between the global loads and the LDS stores:
 // the X tile (256 rows x 64 k, 8 x 16 bytes per thread) and the weight tile (128 rows n x 64 k: 16 bytes
 // of codes = 32 k and their two scale bytes per thread). Rows and k past the matrix read as zeros.
+template <int TM>
 struct GemmStage {
-    uint4 x[8];
+    uint4 x[TM / 32];
     uint4 c;
     uint32_t sc;
 };
 
 // k < kend is loaded (kend = K, or the end of a split-K slice: a multiple of the K step); K is the row
 // length.
-template <int TN>
-__device__ __forceinline__ void gemm_load(GemmStage &S, const uint16_t *__restrict__ X, int64_t M, int64_t K,
+template <int TM, int TN>
+__device__ __forceinline__ void gemm_load(GemmStage<TM> &S, const uint16_t *__restrict__ X, int64_t M, int64_t K,
                                           int64_t kend, const uint8_t *__restrict__ codes,
                                           const uint8_t *__restrict__ scales, int64_t N, int64_t m0, int64_t n0,
                                           int64_t k0, int tid) {
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
+    for (int p = 0; p < TM / 32; ++p) {
         const int idx = tid + p * kGemmThreads;  // row idx / 8, 8-element group idx % 8
         const int64_t m = m0 + (idx >> 3), k = k0 + 8 * (idx & 7);
         S.x[p] = make_uint4(0u, 0u, 0u, 0u);
         if (m < M && k < kend) S.x[p] = *reinterpret_cast<const uint4 *>(X + m * K + k);  // K % 16 == 0
     }
-    using C = TileCfg<TN>;
+    using C = TileCfg<TM, TN>;
     const int64_t n = n0 + tid / C::kRowThreads, k = k0 + C::kThreadK * (tid % C::kRowThreads);
     S.c = make_uint4(0u, 0u, 0u, 0u);
     S.sc = 0u;
@@ -126,12 +131,12 @@ __device__ __forceinline__ void gemm_load(GemmStage &S, const uint16_t *__restri
 // The unmasked form for a work-group whose tile and K slice lie inside the matrices: xp points at X row
 // m0 + tid / 8, column k0 + 8 (tid % 8) (row p of the thread adds 32 p K), cp at the codes of weight row
 // n0 + tid / R from k0 + kThreadK (tid % R) (R threads per weight row), sp at their scale bytes.
-template <int TN>
-__device__ __forceinline__ void gemm_load_full(GemmStage &S, const uint16_t *__restrict__ xp, int64_t K,
+template <int TM, int TN>
+__device__ __forceinline__ void gemm_load_full(GemmStage<TM> &S, const uint16_t *__restrict__ xp, int64_t K,
                                                const uint8_t *__restrict__ cp, const uint8_t *__restrict__ sp) {
 #pragma unroll
-    for (int p = 0; p < 8; ++p) S.x[p] = *reinterpret_cast<const uint4 *>(xp + p * 32 * K);
-    if (TileCfg<TN>::kThreadK == 16) {
+    for (int p = 0; p < TM / 32; ++p) S.x[p] = *reinterpret_cast<const uint4 *>(xp + p * 32 * K);
+    if (TileCfg<TM, TN>::kThreadK == 16) {
         const uint2 c2 = *reinterpret_cast<const uint2 *>(cp);
         S.c = make_uint4(c2.x, c2.y, 0u, 0u);
         S.sc = (uint32_t)sp[0];
@@ -141,14 +146,14 @@ __device__ __forceinline__ void gemm_load_full(GemmStage &S, const uint16_t *__r
     }
 }
 
-template <int TN>
-__device__ __forceinline__ void gemm_store(const GemmStage &S, uint16_t *xs, uint16_t *ws, int tid) {
+template <int TM, int TN>
+__device__ __forceinline__ void gemm_store(const GemmStage<TM> &S, uint16_t *xs, uint16_t *ws, int tid) {
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
+    for (int p = 0; p < TM / 32; ++p) {
         const int idx = tid + p * kGemmThreads;
         *reinterpret_cast<uint4 *>(&xs[(idx >> 3) * kLdsStride + 8 * (idx & 7)]) = S.x[p];
     }
-    using C = TileCfg<TN>;
+    using C = TileCfg<TM, TN>;
     const float d0 = e4m3_value(S.sc & 0x7Fu);
     uint16_t *dst = &ws[(tid / C::kRowThreads) * kLdsStride + C::kThreadK * (tid % C::kRowThreads)];
     *reinterpret_cast<uint4 *>(dst) = dequant8(S.c.x, d0);
@@ -170,26 +175,26 @@ __device__ __forceinline__ void gemm_store(const GemmStage &S, uint16_t *xs, uin
 // Split K (when the tiles alone are too few to fill the chip): work-group b takes tile b % tiles and
 // the K slice b / tiles of kslice elements, and writes its fp32 sums without alpha to
 // part[slice][M][N]; k_w4a16_reduce adds the slices in order. With one slice it writes Y directly.
-template <int TN, bool OUTF32>
+template <int TM, int TN, bool OUTF32>
 __global__ __launch_bounds__(kGemmThreads, 2) void k_w4a16_gemm(const uint16_t *__restrict__ X, int64_t M, int64_t K,
                                                              const uint8_t *__restrict__ codes,
                                                              const uint8_t *__restrict__ scales,
                                                              const float *__restrict__ alpha_p, int64_t N,
                                                              void *__restrict__ Y, unsigned tiles_n, unsigned tiles,
                                                              int64_t kslice, float *__restrict__ part) {
-    __shared__ __attribute__((aligned(16))) uint16_t xs[kBM * kLdsStride];
+    __shared__ __attribute__((aligned(16))) uint16_t xs[TM * kLdsStride];
     __shared__ __attribute__((aligned(16))) uint16_t ws[TN * kLdsStride];
-    using C = TileCfg<TN>;
+    using C = TileCfg<TM, TN>;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const unsigned total = gridDim.x;  // 1-D grid: slices * tiles_m * tiles_n, tiles row-major
     unsigned b = blockIdx.x;
     if (total % 8 == 0) b = (b % 8) * (total / 8) + b / 8;
     const unsigned slice = b / tiles, t = b % tiles;
-    const int64_t m0 = (int64_t)(t / tiles_n) * kBM, n0 = (int64_t)(t % tiles_n) * TN;
+    const int64_t m0 = (int64_t)(t / tiles_n) * TM, n0 = (int64_t)(t % tiles_n) * TN;
     const int64_t kbeg = (int64_t)slice * kslice, kend = min(K, kbeg + kslice);
     const int wm = (wave / C::kWavesN) * C::kWaveM, wn = (wave % C::kWavesN) * C::kWaveN;  // the wave's corner
     f32x16 acc[C::kMI][C::kNJ] = {};
-    GemmStage S;
+    GemmStage<TM> S;
     // the products of one K step from the staged tiles
     auto mfma_step = [&]() {
 #pragma unroll
@@ -209,31 +214,31 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_w4a16_gemm(const uint16_t *
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bb[j], acc[i][j], 0, 0, 0);
         }
     };
-    const bool full = m0 + kBM <= M && n0 + TN <= N && (kend - kbeg) % kBK == 0;  // uniform
+    const bool full = m0 + TM <= M && n0 + TN <= N && (kend - kbeg) % kBK == 0;  // uniform
     if (full) {
         const uint16_t *xp = X + (m0 + (tid >> 3)) * K + kbeg + 8 * (tid & 7);
         // element index, a multiple of 16
         const int64_t e = (n0 + tid / C::kRowThreads) * K + kbeg + C::kThreadK * (tid % C::kRowThreads);
         const uint8_t *cp = codes + e / 2, *sp = scales + e / 16;
-        gemm_load_full<TN>(S, xp, K, cp, sp);
+        gemm_load_full<TM, TN>(S, xp, K, cp, sp);
         for (int64_t k0 = kbeg; k0 < kend; k0 += kBK) {
-            gemm_store<TN>(S, xs, ws, tid);
+            gemm_store<TM, TN>(S, xs, ws, tid);
             __syncthreads();
             xp += kBK;
             cp += kBK / 2;
             sp += kBK / 16;
-            if (k0 + kBK < kend) gemm_load_full<TN>(S, xp, K, cp, sp);
+            if (k0 + kBK < kend) gemm_load_full<TM, TN>(S, xp, K, cp, sp);
             __builtin_amdgcn_s_setprio(1);
             mfma_step();
             __builtin_amdgcn_s_setprio(0);
             __syncthreads();
         }
     } else {
-        gemm_load<TN>(S, X, M, K, kend, codes, scales, N, m0, n0, kbeg, tid);
+        gemm_load<TM, TN>(S, X, M, K, kend, codes, scales, N, m0, n0, kbeg, tid);
         for (int64_t k0 = kbeg; k0 < kend; k0 += kBK) {
-            gemm_store<TN>(S, xs, ws, tid);
+            gemm_store<TM, TN>(S, xs, ws, tid);
             __syncthreads();
-            if (k0 + kBK < kend) gemm_load<TN>(S, X, M, K, kend, codes, scales, N, m0, n0, k0 + kBK, tid);
+            if (k0 + kBK < kend) gemm_load<TM, TN>(S, X, M, K, kend, codes, scales, N, m0, n0, k0 + kBK, tid);
             __builtin_amdgcn_s_setprio(1);
             mfma_step();
             __builtin_amdgcn_s_setprio(0);
@@ -566,10 +571,16 @@ hipError_t launch_w4a16(const uint16_t *X, int64_t M, int64_t K, const uint8_t *
 #ifndef NVFP4_NARROW_MAX_M
 #define NVFP4_NARROW_MAX_M 512
 #endif
-    // 256 x 64 tiles up to 512 rows of X: twice the tiles, so K is split into half as many, longer
-    // slices (13-15 % faster than 256 x 128 at 65 <= M <= 256 on 4096 x 4096 weights, equal from 1024)
-    const int tn = M <= NVFP4_NARROW_MAX_M ? 64 : kBN;
-    const int64_t tiles_n = (N + tn - 1) / tn, tiles_m = (M + kBM - 1) / kBM, tiles = tiles_n * tiles_m;
+    // Tile shape by the rows of X (timed on 4096 x 4096 weights): 256 x 64 up to 512 rows (twice the
+    // tiles, so K is split into half as many, longer slices: 13-15 % faster than 256 x 128 at
+    // 65 <= M <= 256); above that 256 x 128 when those tiles alone give two work-groups per CU, else
+    // 128 x 128 (three work-groups per CU and no split: 7 % faster at M = 1024, 16-17 % at 2048 and
+    // 3072; 256 x 128 is 20-25 % faster than 128 x 128 once it fills the GPU, M = 4096 and 8192).
+    const bool narrow = M <= NVFP4_NARROW_MAX_M;
+    const bool tall = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN) >= 512;
+    const int tm = narrow || tall ? kBM : 128;
+    const int tn = narrow ? 64 : kBN;
+    const int64_t tiles_n = (N + tn - 1) / tn, tiles_m = (M + tm - 1) / tm, tiles = tiles_n * tiles_m;
     int64_t slices = 1, kslice = K;
     split_k(tiles, M, N, K, slices, kslice);
     float *part = nullptr;
@@ -579,14 +590,21 @@ hipError_t launch_w4a16(const uint16_t *X, int64_t M, int64_t K, const uint8_t *
             return hipErrorOutOfMemory;
     }
     const dim3 grid((unsigned)(tiles * slices)), block(kGemmThreads);
-#define NVFP4_GEMM(TN, F)                                                                                     \
-    hipLaunchKernelGGL((k_w4a16_gemm<TN, F>), grid, block, 0, stream, X, M, K, codes, scales, alpha, N, Y,           \
-                       (unsigned)tiles_n, (unsigned)tiles, kslice, part)
-    if (tn == 64) {
-        if (out_f32) NVFP4_GEMM(64, true); else NVFP4_GEMM(64, false);
-    } else {
-        if (out_f32) NVFP4_GEMM(128, true); else NVFP4_GEMM(128, false);
-    }
+#define NVFP4_GEMM(TM, TN)                                                                                    \
+    do {                                                                                                      \
+        if (out_f32)                                                                                          \
+            hipLaunchKernelGGL((k_w4a16_gemm<TM, TN, true>), grid, block, 0, stream, X, M, K, codes, scales, alpha, \
+                               N, Y, (unsigned)tiles_n, (unsigned)tiles, kslice, part);                         \
+        else                                                                                                  \
+            hipLaunchKernelGGL((k_w4a16_gemm<TM, TN, false>), grid, block, 0, stream, X, M, K, codes, scales,      \
+                               alpha, N, Y, (unsigned)tiles_n, (unsigned)tiles, kslice, part);                  \
+    } while (0)
+    if (tn == 64)
+        NVFP4_GEMM(256, 64);
+    else if (tm == 128)
+        NVFP4_GEMM(128, 128);
+    else
+        NVFP4_GEMM(256, 128);
 #undef NVFP4_GEMM
     hipError_t err = hipGetLastError();
     if (slices > 1) {
