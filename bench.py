@@ -170,7 +170,7 @@ PEAK_BF16_MFMA = 2.5e15  # FLOP/s, MI355X dense bf16 matrix peak
 def w4a16_pass(torch, nv, dev, W):
     """The consumer of the format: Y = X @ What.T with the 4096 x 4096 weights quantised (FourOverSix)
     and bf16 activations, for M = 1 (one token, the GEMV: bound by reading 0.5625 B per weight), M = 16
-    (the skinny MFMA kernel), M = 256 (256 x 64 MFMA tiles with K split) and M = 4096 (256 x 128 tiles,
+    (the skinny MFMA kernel), M = 256 (128 x 64 MFMA tiles with K split) and M = 4096 (256 x 128 tiles,
     bf16 MFMA-bound). Times are HIP-event averages over a graph of repeated calls on the current stream."""
     codes, scales, alpha = nv.quantize(W, "4o6")
     n, k = W.shape
@@ -197,7 +197,7 @@ def w4a16_pass(torch, nv, dev, W):
         torch.cuda.synchronize()
         # a replay must reproduce the eager result (library calls inside a graph are checked, not trusted)
         return e0.elapsed_time(e1) / reps if torch.equal(Y, eager) else None
-    kernels = {1: "k_w4a16_gemv", 16: "k_w4a16_skinny", 256: "k_w4a16_gemm 256x64 tiles + k_w4a16_reduce (K split)",
+    kernels = {1: "k_w4a16_gemv", 16: "k_w4a16_skinny", 256: "k_w4a16_gemm 128x64 tiles + k_w4a16_reduce (K split)",
                4096: "k_w4a16_gemm 256x128 tiles"}
     for m in (1, 16, 256, 4096):
         X = (torch.randn((m, k), device=dev) * 0.5).to(torch.bfloat16)

@@ -15,8 +15,8 @@
 //   k_w4a16_skinny (M <= 64 otherwise): 16 weight rows per work-group, K split over its 16 waves, the
 //     products on v_mfma_f32_16x16x32_bf16 with weights decoded straight into the A operand.
 //   k_w4a16_gemm (M > 64): 256 x 128 output tile per work-group (4 waves, 128 x 64 each as 4 x 2 tiles of
-//     v_mfma_f32_32x32x16_bf16; 256 x 64 for M <= 512 and 128 x 128 when the 256 x 128 tiles would not
-//     fill the GPU, both with waves of 64 x 64), K in steps of 64 through
+//     v_mfma_f32_32x32x16_bf16; 128 x 64 for M <= 512 and 128 x 128 when the 256 x 128 tiles would not
+//     fill the GPU), K in steps of 64 through
 //     LDS: the X tile is copied, the weight tile is decoded to bf16 (codes -> binary32 q, times Delta,
 //     high half) once per work-group as it is stored, and the next step's loads are in flight while the
 //     matrix cores work on this one. When the tiles are too few to fill the GPU, K is split and
@@ -39,8 +39,8 @@ constexpr int kGemmThreads = 256;
 constexpr int kBM = 256, kBN = 128, kBK = 64;
 
 // Tile shapes: TM x TN outputs per work-group: 256 x 128 (large M), 128 x 128 (middle M: more
-// work-groups, three per CU) and 256 x 64 (few rows of X: more tiles, so fewer and longer K slices).
-// Four waves: 2 x 2 for TN = 128 (128 x 64 or 64 x 64 each), 4 x 1 of 64 x 64 for TN = 64. A K step
+// work-groups, three per CU) and 128 x 64 (few rows of X: more tiles, so fewer and longer K slices).
+// Four waves: 2 x 2 for TN = 128 (128 x 64 or 64 x 64 each), 4 x 1 of 32 x 64 for TN = 64. A K step
 // (64 k) of X is TM / 32 16-byte loads per thread; a weight row of it (32 bytes of codes) is loaded by
 // 256 / TN threads.
 template <int TM, int TN>
@@ -165,9 +165,10 @@ __device__ __forceinline__ void gemm_store(const GemmStage<TM> &S, uint16_t *xs,
     }
 }
 
-// 256 x TN output tile per work-group (TileCfg: 4 waves of 128 x 64 for TN = 128, of 64 x 64 for TN = 64,
-// each as tiles of v_mfma_f32_32x32x16_bf16). The loads of K step t + 1 are issued into registers before the products of step t, so they are in
-// flight while the matrix cores run; one LDS buffer (55 KB; 46 KB for TN = 64) leaves room for two work-groups per CU.
+// TM x TN output tile per work-group (TileCfg: 4 waves of 128 x 64, 64 x 64 or 32 x 64, each as tiles of
+// v_mfma_f32_32x32x16_bf16). The loads of K step t + 1 are issued into registers before the products of step t, so they are in
+// flight while the matrix cores run; one LDS buffer (55 KB for 256 x 128, less for the smaller tiles) leaves room for at least two work-groups
+// per CU.
 // Waves raise their issue priority for the products, so a SIMD serves the work-group at its matrix
 // step before the other one's decode and stores.
 // Work-groups go to the 8 XCDs round robin; the tile order is remapped so that each XCD takes a
@@ -571,14 +572,14 @@ hipError_t launch_w4a16(const uint16_t *X, int64_t M, int64_t K, const uint8_t *
 #ifndef NVFP4_NARROW_MAX_M
 #define NVFP4_NARROW_MAX_M 512
 #endif
-    // Tile shape by the rows of X (timed on 4096 x 4096 weights): 256 x 64 up to 512 rows (twice the
-    // tiles, so K is split into half as many, longer slices: 13-15 % faster than 256 x 128 at
+    // Tile shape by the rows of X (timed on 4096 x 4096 weights): 128 x 64 up to 512 rows (four times the
+    // tiles of 256 x 128, so K is split into a quarter as many, longer slices: 25-30 % faster at
     // 65 <= M <= 256); above that 256 x 128 when those tiles alone give two work-groups per CU, else
     // 128 x 128 (three work-groups per CU and no split: 7 % faster at M = 1024, 16-17 % at 2048 and
     // 3072; 256 x 128 is 20-25 % faster than 128 x 128 once it fills the GPU, M = 4096 and 8192).
     const bool narrow = M <= NVFP4_NARROW_MAX_M;
     const bool tall = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN) >= 512;
-    const int tm = narrow || tall ? kBM : 128;
+    const int tm = tall && !narrow ? kBM : 128;
     const int tn = narrow ? 64 : kBN;
     const int64_t tiles_n = (N + tn - 1) / tn, tiles_m = (M + tm - 1) / tm, tiles = tiles_n * tiles_m;
     int64_t slices = 1, kslice = K;
@@ -600,7 +601,7 @@ hipError_t launch_w4a16(const uint16_t *X, int64_t M, int64_t K, const uint8_t *
                                alpha, N, Y, (unsigned)tiles_n, (unsigned)tiles, kslice, part);                  \
     } while (0)
     if (tn == 64)
-        NVFP4_GEMM(256, 64);
+        NVFP4_GEMM(128, 64);
     else if (tm == 128)
         NVFP4_GEMM(128, 128);
     else

@@ -56,8 +56,8 @@ SHAPES = [(1, 256, 1024), (2, 96, 160), (3, 64, 272), (4, 130, 64),   # GEMV pat
           (5, 200, 272), (7, 50, 9360), (9, 33, 7280), (12, 20, 1024), (13, 40, 5040), (16, 64, 4096),
           (16, 24, 4112), (17, 64, 512),
           (33, 50, 400), (48, 17, 4112), (64, 100, 2064), (20, 7, 16), (40, 33, 48),  # skinny: 1-4 tiles of 16 m
-          (65, 40, 320), (130, 260, 528), (128, 256, 1024),  # 256 x 64 MFMA tiles (M <= 512), K split
-          (300, 136, 96), (512, 512, 160), (260, 1100, 48),  # several 256 x 64 tiles (8 | 8 tiles: remapped)
+          (65, 40, 320), (130, 260, 528), (128, 256, 1024),  # 128 x 64 MFMA tiles (M <= 512), K split
+          (300, 136, 96), (512, 512, 160), (260, 1100, 48),  # several 128 x 64 tiles (8 | tiles: remapped)
           (513, 200, 144), (1024, 256, 128), (2048, 130, 96),  # 128 x 128 tiles (512 < M <= 2048)
           (2049, 136, 48)]  # 256 x 128 tiles (M > 2048)
 
@@ -95,7 +95,7 @@ def test_w4a16_one_hot_rows_are_exact():
 
 
 def test_w4a16_full_size_sample():
-    """4096 x 4096 weights with M = 1 (GEMV), 8, 16 and 64 (skinny MFMA), 256 (256 x 64 tiles, K split),
+    """4096 x 4096 weights with M = 1 (GEMV), 8, 16 and 64 (skinny MFMA), 256 (128 x 64 tiles, K split),
     1024 (128 x 128 tiles) and 4096 (256 x 128 tiles, whole K): the bench's cases and the other tile
     shapes, sampled outputs against the oracle. Each output depends only on its own row of X, so every
     61st weight row is checked against every row of X (every 61st for M > 256)."""
