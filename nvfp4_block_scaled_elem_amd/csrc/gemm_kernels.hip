@@ -45,7 +45,6 @@ constexpr int kBM = 256, kBN = 128, kBK = 64;
 // 256 / TN threads.
 template <int TM, int TN>
 struct TileCfg {
-    static constexpr int kXLoads = TM / 32;
     static constexpr int kWavesN = TN == 128 ? 2 : 1, kWavesM = 4 / kWavesN;
     static constexpr int kWaveM = TM / kWavesM, kWaveN = TN / kWavesN;  // the wave's corner of the tile
     static constexpr int kMI = kWaveM / 32, kNJ = kWaveN / 32;            // 32 x 32 MFMA tiles per wave
