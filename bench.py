@@ -24,7 +24,8 @@ NVFP4_FLAG_FULL_SEARCH (all 202 candidates) against the FP32 vector peak: per bl
 scales x 16 elements x 9 FLOPs.
 
 w4a16: the W4A16 product the format is for, Y = X @ What.T with the quantised 4096 x 4096 weights, at
-M = 1 and 16 (GB/s against HBM peak), 256 and 4096 (TFLOP/s against the 2.5 PFLOP/s bf16 MFMA peak).
+M = 1, 16 and 64 (GB/s against HBM peak), 256, 1024 and 4096 (TFLOP/s against the 2.5 PFLOP/s bf16 MFMA
+peak), each beside torch's dense bf16 product.
 
 c5_whole_model: the 224 matrices of a 7B-shaped model (32 layers; 12.95 GB bf16) quantised one after
 another in each mode, total time and aggregate GB/s, and the same for its 128 square 4096 x 4096
@@ -169,9 +170,9 @@ PEAK_BF16_MFMA = 2.5e15  # FLOP/s, MI355X dense bf16 matrix peak
 
 def w4a16_pass(torch, nv, dev, W):
     """The consumer of the format: Y = X @ What.T with the 4096 x 4096 weights quantised (FourOverSix)
-    and bf16 activations, for M = 1 (one token, the GEMV: bound by reading 0.5625 B per weight), M = 16
-    (the skinny MFMA kernel), M = 256 (128 x 64 MFMA tiles with K split) and M = 4096 (256 x 128 tiles,
-    bf16 MFMA-bound). Times are HIP-event averages over a graph of repeated calls on the current stream."""
+    and bf16 activations, one case per kernel shape: M = 1 (one token, the GEMV: bound by reading 0.5625 B
+    per weight), M = 16 and 64 (the skinny MFMA kernel), M = 256 (128 x 64 MFMA tiles with K split),
+    M = 1024 (128 x 128 tiles) and M = 4096 (256 x 128 tiles, bf16 MFMA-bound). Times are HIP-event averages over a graph of repeated calls on the current stream."""
     codes, scales, alpha = nv.quantize(W, "4o6")
     n, k = W.shape
     # context: torch's dense bf16 product (hipBLASLt) on the dequantised weights, same shapes and timing
@@ -197,12 +198,13 @@ def w4a16_pass(torch, nv, dev, W):
         torch.cuda.synchronize()
         # a replay must reproduce the eager result (library calls inside a graph are checked, not trusted)
         return e0.elapsed_time(e1) / reps if torch.equal(Y, eager) else None
-    kernels = {1: "k_w4a16_gemv", 16: "k_w4a16_skinny", 256: "k_w4a16_gemm 128x64 tiles + k_w4a16_reduce (K split)",
+    kernels = {1: "k_w4a16_gemv", 16: "k_w4a16_skinny", 64: "k_w4a16_skinny (4 tiles of X)",
+               256: "k_w4a16_gemm 128x64 tiles + k_w4a16_reduce (K split)", 1024: "k_w4a16_gemm 128x128 tiles",
                4096: "k_w4a16_gemm 256x128 tiles"}
-    for m in (1, 16, 256, 4096):
+    for m in (1, 16, 64, 256, 1024, 4096):
         X = (torch.randn((m, k), device=dev) * 0.5).to(torch.bfloat16)
         Y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
-        reps = 200 if m <= 16 else 20
+        reps = 200 if m <= 64 else 20
         ms = graph_ms(lambda: nv.matmul(X, codes, scales, alpha, out=Y), Y, reps)
         if ms is None:
             raise RuntimeError(f"W4A16 product, M={m}: a graph replay differs from the eager call")
