@@ -16,6 +16,10 @@ Workloads (weights of real models are not available; these stand in for them):
     multiplied by 2^U(-1, 1), i.e. log-uniform on [0.5, 2].
   * ``c5``: one linear layer of a 7B-shaped transformer (q, k, v, o 4096 x 4096; gate, up 11008 x 4096;
     down 4096 x 11008) bf16, Student-t (nu = 5) scaled to std 0.02, seeded by the layer index.
+  * ``activations`` / ``hessian``: calibration inputs of a linear layer for GPTQ (no real activations
+    are available): per-feature scales 2^U(-2, 2), a rank-8 component shared by all features so that
+    they correlate, optionally some features that are always zero; ``hessian`` returns their second
+    moment X^T X / n in binary64, the matrix GPTQ takes as input.
 """
 from __future__ import annotations
 
@@ -81,3 +85,22 @@ def normal_bf16(rows: int, cols: int, seed: int, std: float = 0.02) -> np.ndarra
 
 def normal_f32(rows: int, cols: int, seed: int, std: float = 0.02) -> np.ndarray:
     return (rng(seed, 8).standard_normal((rows, cols)) * std).astype(np.float32)
+
+
+def activations(n: int, cols: int, seed: int, dead: int = 0) -> np.ndarray:
+    """n calibration input vectors of a layer with `cols` inputs, binary64 [n, cols]."""
+    g = rng(seed, 9)
+    sigma = np.exp2(g.uniform(-2.0, 2.0, size=cols))
+    shared = g.standard_normal((n, 8)) @ g.standard_normal((8, cols)) / np.sqrt(8.0)
+    X = (g.standard_normal((n, cols)) + 0.5 * shared) * sigma
+    if dead:
+        X[:, rng(seed, 9, 1).permutation(cols)[:dead]] = 0.0
+    return X
+
+
+def hessian(cols: int, seed: int, n: int = 0, dead: int = 0) -> np.ndarray:
+    """X^T X / n of `activations` (n = 2 cols unless given): symmetric positive semi-definite, binary64."""
+    n = n or 2 * cols
+    X = activations(n, cols, seed, dead)
+    H = X.T @ X / n
+    return (H + H.T) / 2.0  # exactly symmetric whatever order the product summed in
