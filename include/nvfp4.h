@@ -195,6 +195,46 @@ int nvfp4_error_stats(const void *W, int dtype, int64_t rows, int64_t cols, cons
 int nvfp4_matmul(const void *X, int64_t M, int64_t K, const uint8_t *codes, const uint8_t *scales,
                  const float *alpha, int64_t N, void *Y, int y_dtype, void *stream);
 
+/* GPTQ with the FourOverSix block scales fixed first (FourOverSix write-up, section 03: every block's
+ * scale and its M = 6 / M = 4 choice are settled before GPTQ's weight iterations, which then run inside
+ * that frame; GPTQ as published by Frantar, Ashkboos, Hoefler and Alistarh, 2022).
+ *
+ * Steps:
+ *   1. The frame. scales_out and alpha_out are exactly nvfp4_quantize's FourOverSix result for W.
+ *   2. GPTQ's preparation of H [cols][cols], the second moment of the layer's inputs. Inputs with a zero
+ *      diagonal are dead: their weights count as zero and their diagonal as one. Every diagonal entry then
+ *      gains percdamp * mean(diagonal).
+ *   3. The columns in order. Each is quantised to the nearest E2M1 value of w~ / s in binary64, where
+ *      s = fl32(alpha * Delta) of its block (ties to the even code; s = 0 gives code 0). Its error is spread
+ *      over the later columns as GPTQ specifies: given the columns already fixed, the later weights are the
+ *      minimiser of the H-weighted error. All of this runs in binary64.
+ *   codes_out gets the resulting codes.
+ *
+ * Arguments:
+ *   W           [rows][cols], dtype bf16 or fp32, 16-byte aligned.
+ *   H           device binary64, row-major, symmetric; only its upper triangle (H[i][j], i <= j) is read.
+ *   percdamp    finite and >= 0 (GPTQ's usual value is 0.01).
+ *   codes_out, scales_out, alpha_out
+ *               as for nvfp4_quantize.
+ *   workspace   nullable; 256-byte aligned, of nvfp4_gptq_workspace_bytes(rows, cols) bytes, about
+ *               8 * (cols^2 + rows * cols) bytes. NULL = the library allocates on `stream` and gives the
+ *               scratch back on `stream`.
+ *
+ * Limits: cols % 16 == 0, cols <= 32768, rows <= 65535 * 64 and rows * cols <= 2^32 (else
+ *         NVFP4_ERR_SHAPE).
+ *
+ * Errors:
+ *   - Arguments are checked on the host, as for nvfp4_quantize.
+ *   - If the damped H is not positive definite in binary64 (a Cholesky pivot that is not positive and
+ *     finite), alpha_out = NaN and every code is 0 when the stream work ends.
+ *   - A NaN or infinity in W gives FourOverSix's in-band result (alpha NaN, all-zero codes and scales). */
+int nvfp4_gptq(const void *W, int dtype, int64_t rows, int64_t cols, const double *H, double percdamp,
+               uint8_t *codes_out, uint8_t *scales_out, float *alpha_out, void *workspace,
+               size_t workspace_bytes, void *stream);
+
+/* Device scratch one nvfp4_gptq call needs (0 for an invalid shape). */
+size_t nvfp4_gptq_workspace_bytes(int64_t rows, int64_t cols);
+
 /* Text of an nvfp4_error value. */
 const char *nvfp4_status_string(int status);
 

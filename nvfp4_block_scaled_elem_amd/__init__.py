@@ -74,6 +74,10 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_encode_e2m1.restype = i32
         L.nvfp4_dequantize.argtypes = [vp, vp, vp, i64, i64, vp, i32, vp]
         L.nvfp4_dequantize.restype = i32
+        L.nvfp4_gptq.argtypes = [vp, i32, i64, i64, vp, ctypes.c_double, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.nvfp4_gptq.restype = i32
+        L.nvfp4_gptq_workspace_bytes.argtypes = [i64, i64]
+        L.nvfp4_gptq_workspace_bytes.restype = ctypes.c_size_t
         L.nvfp4_status_string.argtypes = [i32]
         L.nvfp4_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -188,6 +192,48 @@ def quantize(W: torch.Tensor, mode: str, iters: int = 0, *, codes=None, scales=N
         a.n_stage_events = len(stage_events)
     with torch.cuda.device(dev):
         _check(lib().nvfp4_quantize_ex(ctypes.byref(a)))
+    return codes, scales, alpha
+
+
+def gptq_workspace_bytes(rows: int, cols: int) -> int:
+    return int(lib().nvfp4_gptq_workspace_bytes(rows, cols))
+
+
+def gptq(W: torch.Tensor, H: torch.Tensor, percdamp: float = 0.01, *, codes=None, scales=None, alpha=None,
+         workspace=None, stream=None):
+    """GPTQ codes for ``W`` ([rows, cols] bf16/fp32 CUDA tensor) inside the FourOverSix frame (block
+    scales and alpha fixed first), with ``H`` the [cols, cols] float64 second moment of the layer's
+    inputs (symmetric; its upper triangle is read) and GPTQ's damping fraction ``percdamp``. Returns
+    (codes, scales, alpha) laid out as ``quantize`` returns them; alpha is NaN if the damped H is not
+    positive definite. Optional preallocated outputs, a uint8 ``workspace`` tensor and a ``stream``."""
+    if W.dim() != 2 or not W.is_cuda or not W.is_contiguous() or W.dtype not in DTYPES:
+        raise NVFP4Error("W must be a contiguous 2-D bf16 or fp32 CUDA tensor")
+    rows, cols = W.shape
+    dev = W.device
+    if H.dim() != 2 or tuple(H.shape) != (cols, cols):
+        raise NVFP4Error("H must be [cols, cols]")
+    _check_buffer(H, "H", cols * cols * 8, dev, torch.float64)
+    if codes is None:
+        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev)
+    if alpha is None:
+        alpha = torch.empty(1, dtype=torch.float32, device=dev)
+    nel = rows * cols
+    _check_buffer(codes, "codes", nel // 2, dev, torch.uint8)
+    _check_buffer(scales, "scales", nel // 16, dev, torch.uint8)
+    _check_buffer(alpha, "alpha", 4, dev, torch.float32)
+    if workspace is not None:
+        _check_buffer(workspace, "workspace", 0, dev)
+    need = gptq_workspace_bytes(rows, cols)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        _check(lib().nvfp4_gptq(W.data_ptr(), DTYPES[W.dtype], rows, cols, H.data_ptr(), float(percdamp),
+                                codes.data_ptr(), scales.data_ptr(), alpha.data_ptr(),
+                                workspace.data_ptr() if workspace is not None else None,
+                                workspace.numel() * workspace.element_size() if workspace is not None else 0,
+                                _stream_ptr(stream, dev)))
     return codes, scales, alpha
 
 

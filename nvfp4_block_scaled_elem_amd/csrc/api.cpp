@@ -6,6 +6,7 @@
 //   CJSO(T)           : k_amax -> k_cjso_init -> T x k_cjso_iter
 //   SOAR(T)           : CJSO(T) -> k_soar
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 
 #include "launch.hpp"
@@ -222,6 +223,49 @@ NVFP4_API int nvfp4_matmul(const void *X, int64_t M, int64_t K, const uint8_t *c
                                y_dtype == NVFP4_DTYPE_F32, static_cast<hipStream_t>(stream)) == hipSuccess
                ? NVFP4_OK
                : NVFP4_ERR_HIP;
+}
+
+namespace {
+constexpr int64_t kGptqMaxCols = 32768;
+constexpr int64_t kGptqMaxElems = (int64_t)1 << 32;
+constexpr int64_t kGptqMaxRows = (int64_t)65535 * 64;  // row tiles of 64 along the update grid's y
+
+bool gptq_shape_ok(int64_t rows, int64_t cols) {
+    return cols % 16 == 0 && cols <= kGptqMaxCols && rows <= kGptqMaxElems / cols && rows <= kGptqMaxRows;
+}
+}  // namespace
+
+NVFP4_API size_t nvfp4_gptq_workspace_bytes(int64_t rows, int64_t cols) {
+    if (rows <= 0 || cols <= 0 || !gptq_shape_ok(rows, cols)) return 0;
+    return nvfp4::gptq_workspace_bytes(rows, cols);
+}
+
+NVFP4_API int nvfp4_gptq(const void *W, int dtype, int64_t rows, int64_t cols, const double *H, double percdamp,
+                         uint8_t *codes_out, uint8_t *scales_out, float *alpha_out, void *workspace,
+                         size_t workspace_bytes, void *stream) {
+    if (!W || !H || !codes_out || !scales_out || !alpha_out || rows <= 0 || cols <= 0) return NVFP4_ERR_INVALID_ARG;
+    if (dtype != NVFP4_DTYPE_BF16 && dtype != NVFP4_DTYPE_F32) return NVFP4_ERR_INVALID_ARG;
+    if (!(percdamp >= 0.0) || !(percdamp < INFINITY)) return NVFP4_ERR_INVALID_ARG;
+    if (!gptq_shape_ok(rows, cols)) return NVFP4_ERR_SHAPE;
+    if (((uintptr_t)W & 15u) != 0 || ((uintptr_t)H & 7u) != 0 || ((uintptr_t)codes_out & 7u) != 0 ||
+        ((uintptr_t)alpha_out & 3u) != 0 || (workspace && ((uintptr_t)workspace & 255u) != 0))
+        return NVFP4_ERR_INVALID_ARG;
+    const size_t need = nvfp4::gptq_workspace_bytes(rows, cols);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const bool f32 = dtype == NVFP4_DTYPE_F32;
+    if (workspace) {
+        if (workspace_bytes < need) return NVFP4_ERR_WORKSPACE;
+        return nvfp4::launch_gptq(W, f32, rows, cols, H, percdamp, codes_out, scales_out, alpha_out, workspace,
+                                  st) == hipSuccess
+                   ? NVFP4_OK
+                   : NVFP4_ERR_HIP;
+    }
+    void *ws = nullptr;
+    if (hipMallocAsync(&ws, need, st) != hipSuccess) return NVFP4_ERR_HIP;
+    const bool ok =
+        nvfp4::launch_gptq(W, f32, rows, cols, H, percdamp, codes_out, scales_out, alpha_out, ws, st) == hipSuccess;
+    if (hipFreeAsync(ws, st) != hipSuccess) return NVFP4_ERR_HIP;
+    return ok ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 
 NVFP4_API const char *nvfp4_status_string(int status) {

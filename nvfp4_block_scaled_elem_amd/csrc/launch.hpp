@@ -79,6 +79,9 @@ size_t stats_workspace_bytes();
 hipError_t launch_stats(const void *W, bool f32, int64_t nblk, const uint8_t *codes, const uint8_t *scales,
                         const float *alpha, double *sse_out, unsigned long long *hist_out, void *workspace,
                         hipStream_t stream);
+size_t gptq_workspace_bytes(int64_t rows, int64_t cols);
+hipError_t launch_gptq(const void *W, bool f32, int64_t rows, int64_t cols, const double *H, double percdamp,
+                       uint8_t *codes, uint8_t *scales, float *alpha, void *workspace, hipStream_t stream);
 hipError_t launch_dequant(const uint8_t *codes, const uint8_t *scales, const float *alpha, int64_t nblk, void *out,
                           bool out_f32, hipStream_t stream);
 

@@ -166,3 +166,32 @@ def test_args_struct_layout_matches_header(tmp_path):
     out = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()]
     assert out[0] == ctypes.sizeof(nv._Args)
     assert out[1:] == [getattr(nv._Args, f).offset for f in fields]
+
+
+def test_gptq_rejects(L):
+    f = L.nvfp4_gptq
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_double,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                  ctypes.c_void_p]
+
+    def call(W=FAKE, dtype=0, rows=64, cols=256, H=FAKE, damp=0.01, codes=FAKE, scales=FAKE, alpha=FAKE, ws=None,
+             wsb=0):
+        return f(W, dtype, rows, cols, H, damp, codes, scales, alpha, ws, wsb, None)
+
+    assert call(W=None) == INVALID and call(H=None) == INVALID and call(codes=None) == INVALID
+    assert call(scales=None) == INVALID and call(alpha=None) == INVALID
+    assert call(rows=0) == INVALID and call(cols=-16) == INVALID and call(dtype=2) == INVALID
+    assert call(damp=-0.01) == INVALID and call(damp=float("nan")) == INVALID and call(damp=float("inf")) == INVALID
+    assert call(cols=24) == SHAPE and call(cols=32784) == SHAPE
+    assert call(rows=(1 << 32) // 256 + 1) == SHAPE and call(rows=65535 * 64 + 1, cols=16) == SHAPE
+    assert call(W=FAKE + 8) == INVALID and call(H=FAKE + 4) == INVALID and call(codes=FAKE + 4) == INVALID
+    assert call(alpha=FAKE + 2) == INVALID and call(ws=FAKE + 64, wsb=1 << 30) == INVALID
+    assert call(ws=FAKE, wsb=1024) == WORKSPACE
+
+
+def test_gptq_workspace_bytes(L):
+    f = L.nvfp4_gptq_workspace_bytes
+    f.argtypes = [ctypes.c_int64, ctypes.c_int64]
+    f.restype = ctypes.c_size_t
+    assert f(4096, 4096) >= 8 * (4096 * 4096 + 4096 * 4096)
+    assert f(4096, 4095) == 0 and f(0, 16) == 0 and f(16, 32784) == 0
