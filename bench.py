@@ -151,6 +151,7 @@ def cpu_baseline(W0: np.ndarray) -> dict:
         list(pool.map(work, samples))
     dtn = time.perf_counter() - t0
     alln = len(MODES) * sum(x.nbytes for x in samples) / dtn
+    gptq_leg = gptq_cpu_sample(W0)
     model = ""
     try:
         with open("/proc/cpuinfo") as f:
@@ -162,10 +163,69 @@ def cpu_baseline(W0: np.ndarray) -> dict:
                       f"({256 * 4096} elements), all four modes, {dtn:.1f} s",
             "single_thread": {"value": round(one / 1e9, 6), "unit": "GB/s",
                               "sample": f"rows 0-255, all four modes, {dt1:.1f} s"},
+            "gptq": gptq_leg,
             "host": {"nproc": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)), "cpu_model": model}}
 
 
+def gptq_cpu_sample(W0: np.ndarray, rows: int = 32) -> dict:
+    """The GPTQ oracle (binary64 numpy) on the same 4096 x 4096 problem, its column sweep limited to
+    `rows` rows (the frame and H^-1 are computed in full); the whole matrix is extrapolated from the
+    sweep's share per row, and labelled so."""
+    import synth
+    from oracle import gptq as og
+
+    H = synth.hessian(W0.shape[1], 0, n=GPTQ_INPUTS)
+    t0 = time.perf_counter()
+    og.gptq(W0, H, 0.01, rows=np.arange(1))
+    fixed = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    og.gptq(W0, H, 0.01, rows=np.arange(rows))
+    dt = time.perf_counter() - t0
+    per_row = max(dt - fixed, 0.0) / (rows - 1)
+    whole = fixed + per_row * W0.shape[0]
+    return {"sample": f"oracle column sweep on rows 0-{rows - 1} (frame and H^-1 in full), {dt:.1f} s",
+            "extrapolated_whole_matrix_s": round(whole, 2),
+            "TFLOPs_extrapolated": round(gptq_flops(*W0.shape) / whole / 1e12, 5)}
+
+
 PEAK_BF16_MFMA = 2.5e15  # FLOP/s, MI355X dense bf16 matrix peak
+PEAK_FP64 = 78.6e12  # FLOP/s, MI355X FP64 vector (and FP64 matrix) peak
+GPTQ_INPUTS = 8192  # synthetic calibration input vectors behind the second moment H
+
+
+def gptq_flops(rows: int, cols: int) -> float:
+    """Algorithmic FLOPs of one GPTQ call: the Cholesky factorisation (cols^3 / 3 multiply-adds) and the
+    column sweep (each row's column j takes j multiply-adds for the errors before it: rows * cols^2 / 2)."""
+    return 2.0 * (cols ** 3 / 3.0 + rows * cols ** 2 / 2.0)
+
+
+def gptq_pass(torch, nv, dev, W):
+    """GPTQ inside the FourOverSix frame (nvfp4_gptq) on the 4096 x 4096 weights, with the binary64
+    second moment of GPTQ_INPUTS synthetic inputs; workspace preallocated; HIP-event average of
+    repeated calls on the current stream."""
+    import synth
+
+    rows, cols = W.shape
+    H = torch.from_numpy(synth.hessian(cols, 0, n=GPTQ_INPUTS)).to(dev)
+    ws = torch.empty(nv.gptq_workspace_bytes(rows, cols), dtype=torch.uint8, device=dev)
+    for _ in range(2):
+        nv.gptq(W, H, 0.01, workspace=ws)
+    torch.cuda.synchronize()
+    reps = 10
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        nv.gptq(W, H, 0.01, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    flops = gptq_flops(rows, cols)
+    log(f"gptq {rows}x{cols}: {ms:.2f} ms")
+    return {"workload": f"{rows}x{cols} bf16 weights, H = second moment of {GPTQ_INPUTS} synthetic inputs "
+                        f"(binary64), percdamp 0.01", "ms": round(ms, 4),
+            "algorithmic_flops": flops, "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 3),
+            "frac_fp64_peak": round(flops / (ms * 1e-3) / PEAK_FP64, 4),
+            "workspace_bytes": int(ws.numel())}
 
 
 def w4a16_pass(torch, nv, dev, W):
@@ -678,6 +738,7 @@ def main():
     cold_warm = cold_warm_pass(torch, nv, mats[0], outs[0])
     fp32 = fp32_pass(torch, nv, mats[0])
     w4a16 = w4a16_pass(torch, nv, dev, mats[0])
+    gptq = gptq_pass(torch, nv, dev, mats[0])
     quality = quality_pass(torch, nv, mats[0])
     c3 = None if args.only_4096 else c3_pass(torch, nv, dev)
     anatomy = None if args.only_4096 else round_anatomy(torch, nv, dev, nk["cjso"])
@@ -716,6 +777,7 @@ def main():
     line["cold_warm"] = cold_warm
     line["fp32_input"] = fp32
     line["w4a16"] = w4a16
+    line["gptq"] = gptq
     line["quality"] = quality
     if c3 is not None:
         line["c3_mlp"] = c3

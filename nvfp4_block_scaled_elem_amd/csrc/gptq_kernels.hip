@@ -20,10 +20,10 @@
 //   k_gptq_prep     dead inputs (zero diagonal) and the damping lambda = percdamp * mean(diag)
 //   k_gptq_reverse  A = P (H with dead diagonals 1, + lambda I) P, lower triangle
 //   k_chol_diag,    blocked right-looking Cholesky of A in place, panels of 64 columns: the diagonal
-//   k_chol_trsm,    block (one work-group), the rows below it (one lane per row), then the trailing
-//   k_chol_update   lower triangle (64 x 64 fp64 tiles)
-//   k_gptq_cols     columns [b0, b0 + 64): one thread per weight row walks them in order (target,
-//                   E2M1 code, error e_j)
+//   k_chol_trsm,    block (one wave, rows in registers), the rows below it (a wave per 16 rows), then
+//   k_chol_update   the trailing lower triangle (64 x 64 fp64 tiles)
+//   k_gptq_cols     columns [b0, b0 + 64), a wave per 16 rows, in order (target, E2M1 code, error e_j),
+//                   each column's errors folded into the block's later columns at once
 //   k_gptq_update   S[:, k] += sum over the block of e_i V_ik for every later column k (fp64 tiles)
 // S holds sum_{i<b0} e_i V_ik for the columns not yet reached. Block 0's update writes it, so it needs no
 // clearing.
@@ -44,6 +44,45 @@ constexpr int kPanel = 64;           // Cholesky panel width = GPTQ column block
 constexpr int kLd = kPanel + 1;      // LDS row stride in doubles: rows land on different banks
 constexpr int kTile = 64;            // output tile of the fp64 update kernels (64 x 64, 4 x 4 per thread)
 constexpr int kPrepThreads = 1024;
+
+// A 64 x 64 tile of doubles into LDS by 256 threads: element (r, c) (c fastest across threads) is
+// src[off(r, c)] where ok(r, c), else fill(r, c), stored at lds[pos(r, c)]. All 16 loads of a thread
+// are issued before any is waited for (a masked element reads src[0], which exists, and is discarded).
+template <class Off, class Ok, class Fill, class Pos>
+__device__ __forceinline__ void load_tile(double *lds, const double *__restrict__ src, Off off, Ok ok, Fill fill,
+                                          Pos pos) {
+    double v[16];
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+        const int idx = threadIdx.x + 256 * it, r = idx >> 6, c = idx & 63;
+        v[it] = src[ok(r, c) ? off(r, c) : 0];
+    }
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+        const int idx = threadIdx.x + 256 * it, r = idx >> 6, c = idx & 63;
+        lds[pos(r, c)] = ok(r, c) ? v[it] : fill(r, c);
+    }
+}
+
+// The same for a 64-thread work-group (one wave): all 64 loads of a lane issued before any is used.
+template <class Off, class Ok, class Fill>
+__device__ __forceinline__ void load_tile_wave(double *lds, const double *__restrict__ src, Off off, Ok ok,
+                                               Fill fill) {
+    const int c = threadIdx.x;
+    double v[kPanel];
+#pragma unroll
+    for (int r = 0; r < kPanel; ++r) v[r] = src[ok(r, c) ? off(r, c) : 0];
+#pragma unroll
+    for (int r = 0; r < kPanel; ++r) lds[r * kLd + c] = ok(r, c) ? v[r] : fill(r, c);
+}
+
+// x of lane `lane` (a compile-time constant after unrolling) in every lane.
+__device__ __forceinline__ double readlane_f64(double x, int lane) {
+    const unsigned long long u = __double_as_longlong(x);
+    const unsigned lo = __builtin_amdgcn_readlane((int)(unsigned)u, lane);
+    const unsigned hi = __builtin_amdgcn_readlane((int)(unsigned)(u >> 32), lane);
+    return __longlong_as_double(((unsigned long long)hi << 32) | lo);
+}
 
 __global__ __launch_bounds__(kPrepThreads) void k_gptq_prep(const double *__restrict__ H, int64_t K, double percdamp,
                                                             double *__restrict__ damp, uint8_t *__restrict__ dead,
@@ -83,73 +122,77 @@ __global__ __launch_bounds__(256) void k_gptq_reverse(const double *__restrict__
     }
 }
 
-// Diagonal block of panel [p0, p0 + nb), factored in LDS by one work-group and written back. Padded to
-// 64 columns with an identity so that the loops have fixed bounds. A pivot that is not positive and
-// finite sets *flag.
-__global__ __launch_bounds__(256) void k_chol_diag(double *__restrict__ A, int64_t K, int64_t p0,
-                                                   int *__restrict__ flag) {
-    __shared__ double L[kPanel * kLd];
+// Diagonal block of panel [p0, p0 + nb), factored by one wave: lane r holds row r in registers
+// (padded to 64 with an identity). Column c: the pivot and the column's entries come from their lanes
+// by readlane, so no step waits on LDS or a barrier. Entries above the diagonal are computed and
+// discarded. A pivot that is not positive and finite sets *flag.
+__global__ __launch_bounds__(64) void k_chol_diag(double *__restrict__ A, int64_t K, int64_t p0,
+                                                  int *__restrict__ flag) {
     const int nb = (int)min<int64_t>(kPanel, K - p0);
-    const int tid = threadIdx.x;
-    for (int idx = tid; idx < kPanel * kPanel; idx += 256) {
-        const int r = idx / kPanel, c = idx % kPanel;
-        double v = r == c ? 1.0 : 0.0;
-        if (r < nb && c <= r) v = A[(p0 + r) * K + p0 + c];
-        L[r * kLd + c] = v;
-    }
-    __syncthreads();
-    // column c: every row r >= c (lane r of wave 0) computes the pivot from row c's finished entries,
-    // then its own entry of column c
-    bool bad = false;
+    const int r = threadIdx.x;
+    double a[kPanel];
+#pragma unroll
     for (int c = 0; c < kPanel; ++c) {
-        if (tid >= c && tid < kPanel) {
-            double s = L[c * kLd + c];
-            for (int t = 0; t < c; ++t) s -= L[c * kLd + t] * L[c * kLd + t];
-            if (!(s > 0.0) || !(s < INFINITY)) bad = true;
-            const double d = sqrt(s);
-            if (tid == c) {
-                L[c * kLd + c] = d;
-            } else {
-                double x = L[tid * kLd + c];
-                for (int t = 0; t < c; ++t) x -= L[tid * kLd + t] * L[c * kLd + t];
-                L[tid * kLd + c] = x / d;
-            }
-        }
-        __syncthreads();
+        const bool ok = r < nb && c <= r;
+        a[c] = A[ok ? (p0 + r) * K + p0 + c : 0];
     }
-    if (bad && tid < nb) flag[0] = 1;
-    for (int idx = tid; idx < nb * nb; idx += 256) {
-        const int r = idx / nb, c = idx % nb;
-        if (c <= r) A[(p0 + r) * K + p0 + c] = L[r * kLd + c];
+#pragma unroll
+    for (int c = 0; c < kPanel; ++c) {
+        const bool ok = r < nb && c <= r;
+        a[c] = ok ? a[c] : (r == c ? 1.0 : 0.0);
     }
+    bool bad = false;
+#pragma unroll
+    for (int c = 0; c < kPanel; ++c) {
+        const double s = readlane_f64(a[c], c);  // a_cc after the earlier columns
+        bad = bad || !(s > 0.0) || !(s < INFINITY);
+        const double d = sqrt(s);
+        a[c] = r == c ? d : a[c] / d;  // l_rc for r > c
+#pragma unroll
+        for (int t = c + 1; t < kPanel; ++t) a[t] -= a[c] * readlane_f64(a[c], t);  // a_rt -= l_rc l_tc
+    }
+    if (bad && r == 0) flag[0] = 1;
+#pragma unroll
+    for (int c = 0; c < kPanel; ++c)
+        if (r < nb && c <= r) A[(p0 + r) * K + p0 + c] = a[c];
 }
 
-// Rows below the diagonal block of panel [p0, p0 + nb), 64 per work-group (one wave): L21 = A21 L11^-T
-// by forward substitution, one row per lane, the row kept in LDS (L11 factored by k_chol_diag).
-constexpr int kTrsmRows = 64;
-__global__ __launch_bounds__(kTrsmRows) void k_chol_trsm(double *__restrict__ A, int64_t K, int64_t p0) {
-    __shared__ double L[kPanel * kLd], X[kTrsmRows * kLd];
+// Rows below the diagonal block of panel [p0, p0 + nb): L21 = A21 L11^-T. One wave per 16 rows: lane
+// (rr, cg) = (lane % 16, lane / 16) holds columns 16 cg .. 16 cg + 15 of row rr. Column c: its holders
+// divide by L_cc, the finished value goes to the row's other lanes by shuffle, and every lane subtracts
+// it from its later columns. No barriers after the load of L11.
+__global__ __launch_bounds__(64) void k_chol_trsm(double *__restrict__ A, int64_t K, int64_t p0) {
+    __shared__ double L[kPanel * kLd];
     const int nb = (int)min<int64_t>(kPanel, K - p0);
-    const int tid = threadIdx.x;
-    const int64_t r0 = p0 + nb + (int64_t)blockIdx.x * kTrsmRows;
-    for (int idx = tid; idx < kPanel * kPanel; idx += kTrsmRows) {
-        const int r = idx / kPanel, c = idx % kPanel;
-        double v = r == c ? 1.0 : 0.0;
-        if (r < nb && c <= r) v = A[(p0 + r) * K + p0 + c];
-        L[r * kLd + c] = v;
-        X[r * kLd + c] = (r0 + r < K && c < nb) ? A[(r0 + r) * K + p0 + c] : 0.0;
-    }
+    load_tile_wave(
+        L, A, [&](int r, int c) { return (p0 + r) * K + p0 + c; }, [&](int r, int c) { return r < nb && c <= r; },
+        [](int r, int c) { return r == c ? 1.0 : 0.0; });
+    const int lane = threadIdx.x, rr = lane & 15, cg = lane >> 4;
+    const int64_t row = p0 + nb + (int64_t)blockIdx.x * 16 + rr;
+    const bool in = row < K && 16 * cg < nb;  // nb % 16 == 0: a chunk is whole or absent
+    const double *src = A + (in ? row * K + p0 + 16 * cg : 0);
+    double x[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) x[v] = src[v];
     __syncthreads();
-    double *x = X + tid * kLd;
-    for (int c = 0; c < nb; ++c) {
-        double v = x[c];
-        for (int t = 0; t < c; ++t) v -= x[t] * L[c * kLd + t];
-        x[c] = v / L[c * kLd + c];
+    for (int cgs = 0; 16 * cgs < nb; ++cgs) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int c = 16 * cgs + v;
+            const double xv = x[v] / L[c * kLd + c];
+            if (cg == cgs) x[v] = xv;
+            const double xc = __shfl(xv, rr + 16 * cgs);
+#pragma unroll
+            for (int v2 = 0; v2 < 16; ++v2) {
+                const int k = 16 * cg + v2;
+                if (k > c) x[v2] -= xc * L[k * kLd + c];
+            }
+        }
     }
-    __syncthreads();
-    for (int idx = tid; idx < kTrsmRows * kPanel; idx += kTrsmRows) {
-        const int r = idx / kPanel, c = idx % kPanel;
-        if (r0 + r < K && c < nb) A[(r0 + r) * K + p0 + c] = X[r * kLd + c];
+    if (in) {
+        double *dst = A + row * K + p0 + 16 * cg;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) dst[v] = x[v];
     }
 }
 
@@ -161,11 +204,14 @@ __global__ __launch_bounds__(256) void k_chol_update(double *__restrict__ A, int
     __shared__ double Pi[kTile * kLd], Pj[kTile * kLd];
     const int64_t p1 = p0 + nb, i0 = p1 + (int64_t)ti * kTile, j0 = p1 + (int64_t)tj * kTile;
     const int tid = threadIdx.x;
-    for (int idx = tid; idx < kTile * kPanel; idx += 256) {
-        const int r = idx / kPanel, t = idx % kPanel;
-        Pi[r * kLd + t] = (i0 + r < K && t < nb) ? A[(i0 + r) * K + p0 + t] : 0.0;
-        Pj[r * kLd + t] = (j0 + r < K && t < nb) ? A[(j0 + r) * K + p0 + t] : 0.0;
-    }
+    const auto zero = [](int, int) { return 0.0; };
+    const auto at = [](int r, int t) { return r * kLd + t; };
+    load_tile(
+        Pi, A, [&](int r, int t) { return (i0 + r) * K + p0 + t; }, [&](int r, int t) { return i0 + r < K && t < nb; },
+        zero, at);
+    load_tile(
+        Pj, A, [&](int r, int t) { return (j0 + r) * K + p0 + t; }, [&](int r, int t) { return j0 + r < K && t < nb; },
+        zero, at);
     __syncthreads();
     const int ty = tid / 16, tx = tid % 16;
     double acc[4][4] = {};
@@ -181,18 +227,21 @@ __global__ __launch_bounds__(256) void k_chol_update(double *__restrict__ A, int
 #pragma unroll
             for (int v = 0; v < 4; ++v) acc[u][v] += a[u] * b[v];
     }
+    double old[4][4];  // all 16 loads issued before the stores
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             const int64_t i = i0 + ty + 16 * u, j = j0 + tx + 16 * v;
-            if (i < K && j <= i) A[i * K + j] -= acc[u][v];
+            old[u][v] = A[i < K && j <= i ? i * K + j : 0];
         }
-}
-
-__device__ __forceinline__ double load_w(const void *W, bool f32, int64_t idx) {
-    if (f32) return (double)static_cast<const float *>(W)[idx];
-    return (double)__uint_as_float((uint32_t) static_cast<const uint16_t *>(W)[idx] << 16);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int64_t i = i0 + ty + 16 * u, j = j0 + tx + 16 * v;
+            if (i < K && j <= i) A[i * K + j] = old[u][v] - acc[u][v];
+        }
 }
 
 // E2M1 index of the nearest magnitude to a >= 0 (ties to the even index, 6 beyond 5).
@@ -200,43 +249,68 @@ __device__ __forceinline__ uint32_t e2m1_index64(double a) {
     return (uint32_t)(a > 0.25) + (a >= 0.75) + (a > 1.25) + (a >= 1.75) + (a > 2.5) + (a >= 3.5) + (a > 5.0);
 }
 
-// Columns [b0, b0 + nb) of every row: one thread per row, columns in order.
-__global__ __launch_bounds__(256) void k_gptq_cols(const void *__restrict__ W, bool f32, int64_t R, int64_t K,
-                                                   int64_t b0, int nb, const double *__restrict__ A,
-                                                   const uint8_t *__restrict__ dead,
-                                                   const uint8_t *__restrict__ scales,
-                                                   const float *__restrict__ alpha_p,
-                                                   const double *__restrict__ S, double *__restrict__ E,
-                                                   uint8_t *__restrict__ codes) {
+// Columns [b0, b0 + nb), one wave per 16 rows. Lane (rr, cg) = (lane % 16, lane / 16) holds columns
+// b0 + 16 cg .. + 15 of row rr (one NVFP4 block, so one scale): their weights and running sums
+// acc = S + sum over the block's earlier columns of e_i V_ik. Column j: its holders turn their sum into the
+// target, code and error e_j; e_j reaches the row's other lanes by shuffle; every lane adds e_j V_jk to its
+// later columns. No barriers after the load of V.
+template <bool F32>
+__global__ __launch_bounds__(64) void k_gptq_cols(const void *__restrict__ W, int64_t R, int64_t K, int64_t b0,
+                                                  int nb, const double *__restrict__ A,
+                                                  const uint8_t *__restrict__ dead,
+                                                  const uint8_t *__restrict__ scales,
+                                                  const float *__restrict__ alpha_p, const double *__restrict__ S,
+                                                  double *__restrict__ E, uint8_t *__restrict__ codes) {
     __shared__ double V[kPanel * kLd];  // V[i][j] = V_(b0+i, b0+j) for i <= j, identity padding
-    const int tid = threadIdx.x;
-    for (int idx = tid; idx < kPanel * kPanel; idx += 256) {
-        const int i = idx / kPanel, j = idx % kPanel;
-        double v = i == j ? 1.0 : 0.0;
-        if (j < nb && i <= j) v = A[(K - 1 - b0 - i) * K + (K - 1 - b0 - j)];
-        V[i * kLd + j] = v;
+    load_tile_wave(
+        V, A, [&](int i, int j) { return (K - 1 - b0 - i) * K + (K - 1 - b0 - j); },
+        [&](int i, int j) { return j < nb && i <= j; }, [](int i, int j) { return i == j ? 1.0 : 0.0; });
+    const int lane = threadIdx.x, rr = lane & 15, cg = lane >> 4;
+    const int64_t row = (int64_t)blockIdx.x * 16 + rr;
+    const bool in = row < R && 16 * cg < nb;  // nb % 16 == 0: a chunk is whole or absent
+    const int64_t base = in ? row * K + b0 + 16 * cg : 0;  // element index, a multiple of 16
+    // every load of the lane issued before any is used (masked lanes read element 0 and discard it)
+    double acc[16], w[16];
+    const double *sp = S + (b0 > 0 ? base : 0);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[v] = sp[v];
+    uint32_t wr[16];
+    if (F32) {
+        const uint4 *wp = reinterpret_cast<const uint4 *>(static_cast<const float *>(W) + base);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint4 t = wp[q];
+            wr[4 * q] = t.x, wr[4 * q + 1] = t.y, wr[4 * q + 2] = t.z, wr[4 * q + 3] = t.w;
+        }
+    } else {
+        const uint4 *wp = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(W) + base);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const uint4 t = wp[q];
+            const uint32_t d[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+            for (int h = 0; h < 4; ++h) wr[8 * q + 2 * h] = d[h] << 16, wr[8 * q + 2 * h + 1] = d[h] & 0xFFFF0000u;
+        }
     }
-    __syncthreads();
-    const int64_t r = (int64_t)blockIdx.x * 256 + tid;
-    if (r >= R) return;
+    const uint4 dd = *reinterpret_cast<const uint4 *>(dead + (in ? b0 + 16 * cg : 0));
+    const uint32_t sb = scales[in ? base / 16 : 0];
     const float alpha = *alpha_p;
-    double e[kPanel];
-    uint32_t packed[kPanel / 8] = {};
+    const uint32_t dw[4] = {dd.x, dd.y, dd.z, dd.w};
 #pragma unroll
-    for (int g = 0; g < kPanel / 16; ++g) {
-        if (16 * g >= nb) break;
-        const int64_t col16 = b0 + 16 * g;
-        const float s32 = alpha * e4m3_value(scales[r * (K / 16) + col16 / 16]);  // fl32(alpha * Delta)
-        const double s = (double)s32;
+    for (int v = 0; v < 16; ++v) {
+        const bool isdead = ((dw[v / 4] >> (8 * (v % 4))) & 0xFFu) != 0;
+        acc[v] = in && b0 > 0 ? acc[v] : 0.0;
+        w[v] = in && !isdead ? (double)__uint_as_float(wr[v]) : 0.0;
+    }
+    const double s = in ? (double)(alpha * e4m3_value(sb)) : 0.0;  // fl32(alpha Delta) of the lane's block
+    __syncthreads();
+    double ev[16];
+    uint32_t packed[2] = {0u, 0u};
+    for (int cgs = 0; 16 * cgs < nb; ++cgs) {
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-            const int j = 16 * g + u;
-            const int64_t col = b0 + j;
-            const double w = dead[col] ? 0.0 : load_w(W, f32, r * K + col);
-            double acc = b0 > 0 ? S[r * K + col] : 0.0;
-#pragma unroll
-            for (int i = 0; i < j; ++i) acc += e[i] * V[i * kLd + j];
-            const double t = w + acc / V[j * kLd + j];
+        for (int v = 0; v < 16; ++v) {
+            const int j = 16 * cgs + v;
+            const double t = w[v] + acc[v] / V[j * kLd + j];
             uint32_t code = 0;
             double deq = 0.0;
             if (s > 0.0) {
@@ -244,20 +318,28 @@ __global__ __launch_bounds__(256) void k_gptq_cols(const void *__restrict__ W, b
                 const uint32_t idx = e2m1_index64(fabs(x));
                 const bool neg = x < 0.0 && idx > 0;
                 code = idx | (neg ? 8u : 0u);
-                const double mag = idx < 4 ? 0.5 * idx : (idx == 7 ? 6.0 : (double)(idx - 2));  // {0,..,1.5}, 2, 3, 4, 6
+                const double mag = idx < 4 ? 0.5 * idx : (idx == 7 ? 6.0 : (double)(idx - 2));
                 deq = (neg ? -mag : mag) * s;
             }
-            e[j] = w - deq;
-            packed[j / 8] |= code << (4 * (j % 8));
+            const double e = w[v] - deq;
+            if (cg == cgs) {
+                ev[v] = e;
+                packed[v / 8] |= code << (4 * (v % 8));
+            }
+            const double ej = __shfl(e, rr + 16 * cgs);
+#pragma unroll
+            for (int v2 = 0; v2 < 16; ++v2) {
+                const int k = 16 * cg + v2;
+                if (k > j) acc[v2] += ej * V[j * kLd + k];
+            }
         }
     }
+    if (in) {
+        double *ep = E + row * kPanel + 16 * cg;
 #pragma unroll
-    for (int j = 0; j < kPanel; ++j)
-        if (j < nb) E[r * kPanel + j] = e[j];
-    uint32_t *dst = reinterpret_cast<uint32_t *>(codes + r * (K / 2) + b0 / 2);  // 8-byte aligned: b0 % 16 == 0
-#pragma unroll
-    for (int q = 0; q < kPanel / 8; ++q)
-        if (8 * q < nb) dst[q] = packed[q];
+        for (int v = 0; v < 16; ++v) ep[v] = ev[v];
+        *reinterpret_cast<uint2 *>(codes + base / 2) = make_uint2(packed[0], packed[1]);  // 8-byte aligned
+    }
 }
 
 // S[r][k] (=, or += after block 0) sum_{i < nb} E[r][i] V_(b0+i, k) for k in [b0 + nb, K), 64 x 64 tiles.
@@ -267,14 +349,14 @@ __global__ __launch_bounds__(256) void k_gptq_update(const double *__restrict__ 
     __shared__ double Et[kTile * kLd], Vt[kTile * kLd];
     const int64_t r0 = (int64_t)blockIdx.y * kTile, k0 = b0 + nb + (int64_t)blockIdx.x * kTile;
     const int tid = threadIdx.x;
-    for (int idx = tid; idx < kTile * kPanel; idx += 256) {
-        const int a = idx / kPanel, i = idx % kPanel;
-        Et[a * kLd + i] = (r0 + a < R && i < nb) ? E[(r0 + a) * kPanel + i] : 0.0;
-    }
-    for (int idx = tid; idx < kPanel * kTile; idx += 256) {
-        const int i = idx / kTile, kk = idx % kTile;  // consecutive threads: consecutive (descending) A columns
-        Vt[kk * kLd + i] = (k0 + kk < K && i < nb) ? A[(K - 1 - b0 - i) * K + (K - 1 - k0 - kk)] : 0.0;
-    }
+    const auto zero = [](int, int) { return 0.0; };
+    load_tile(
+        Et, E, [&](int a, int i) { return (r0 + a) * kPanel + i; }, [&](int a, int i) { return r0 + a < R && i < nb; },
+        zero, [](int a, int i) { return a * kLd + i; });
+    // row i of the block, consecutive threads on consecutive (descending) A columns; stored transposed
+    load_tile(
+        Vt, A, [&](int i, int kk) { return (K - 1 - b0 - i) * K + (K - 1 - k0 - kk); },
+        [&](int i, int kk) { return k0 + kk < K && i < nb; }, zero, [](int i, int kk) { return kk * kLd + i; });
     __syncthreads();
     const int ty = tid / 16, tx = tid % 16;
     double acc[4][4] = {};
@@ -291,12 +373,20 @@ __global__ __launch_bounds__(256) void k_gptq_update(const double *__restrict__ 
             for (int v = 0; v < 4; ++v) acc[u][v] += a[u] * b[v];
     }
     const bool first = b0 == 0;
+    double old[4][4];  // all 16 loads issued before the stores
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             const int64_t r = r0 + ty + 16 * u, k = k0 + tx + 16 * v;
-            if (r < R && k < K) S[r * K + k] = first ? acc[u][v] : S[r * K + k] + acc[u][v];
+            old[u][v] = first ? 0.0 : S[r < R && k < K ? r * K + k : 0];
+        }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int64_t r = r0 + ty + 16 * u, k = k0 + tx + 16 * v;
+            if (r < R && k < K) S[r * K + k] = first ? acc[u][v] : old[u][v] + acc[u][v];
         }
 }
 
@@ -351,18 +441,22 @@ hipError_t launch_gptq(const void *W, bool f32, int64_t R, int64_t K, const doub
     for (int64_t p0 = 0; p0 < K; p0 += kPanel) {
         const int nb = (int)std::min<int64_t>(kPanel, K - p0);
         const int64_t below = K - p0 - nb;
-        hipLaunchKernelGGL(k_chol_diag, dim3(1), dim3(256), 0, stream, A, K, p0, flag);
+        hipLaunchKernelGGL(k_chol_diag, dim3(1), dim3(64), 0, stream, A, K, p0, flag);
         if (below > 0) {
-            hipLaunchKernelGGL(k_chol_trsm, dim3((unsigned)((below + kTrsmRows - 1) / kTrsmRows)), dim3(kTrsmRows), 0,
-                               stream, A, K, p0);
+            hipLaunchKernelGGL(k_chol_trsm, dim3((unsigned)((below + 15) / 16)), dim3(64), 0, stream, A, K, p0);
             const unsigned t = (unsigned)((below + kTile - 1) / kTile);
             hipLaunchKernelGGL(k_chol_update, dim3(t, t), dim3(256), 0, stream, A, K, p0, nb);
         }
     }
     for (int64_t b0 = 0; b0 < K; b0 += kPanel) {
         const int nb = (int)std::min<int64_t>(kPanel, K - b0);
-        hipLaunchKernelGGL(k_gptq_cols, dim3((unsigned)((R + 255) / 256)), dim3(256), 0, stream, W, f32, R, K, b0,
-                           nb, A, dead, scales, alpha, S, E, codes);
+        const dim3 grid((unsigned)((R + 15) / 16));
+        if (f32)
+            hipLaunchKernelGGL(k_gptq_cols<true>, grid, dim3(64), 0, stream, W, R, K, b0, nb, A, dead, scales, alpha,
+                               S, E, codes);
+        else
+            hipLaunchKernelGGL(k_gptq_cols<false>, grid, dim3(64), 0, stream, W, R, K, b0, nb, A, dead, scales, alpha,
+                               S, E, codes);
         const int64_t later = K - b0 - nb;
         if (later > 0)
             hipLaunchKernelGGL(k_gptq_update,
