@@ -149,7 +149,7 @@ __global__ __launch_bounds__(64) void k_chol_diag(double *__restrict__ A, int64_
         const double d = sqrt(s);
         a[c] = r == c ? d : a[c] / d;  // l_rc for r > c
 #pragma unroll
-        for (int t = c + 1; t < kPanel; ++t) a[t] -= a[c] * readlane_f64(a[c], t);  // a_rt -= l_rc l_tc
+        for (int t = c + 1; t < kPanel; ++t) a[t] = fma(-a[c], readlane_f64(a[c], t), a[t]);  // a_rt -= l_rc l_tc
     }
     if (bad && r == 0) flag[0] = 1;
 #pragma unroll
@@ -182,10 +182,13 @@ __global__ __launch_bounds__(64) void k_chol_trsm(double *__restrict__ A, int64_
             const double xv = x[v] / L[c * kLd + c];
             if (cg == cgs) x[v] = xv;
             const double xc = __shfl(xv, rr + 16 * cgs);
+            // unmasked (a zero multiplier leaves earlier columns exactly as they are), so the 16 LDS
+            // reads are issued together
 #pragma unroll
             for (int v2 = 0; v2 < 16; ++v2) {
                 const int k = 16 * cg + v2;
-                if (k > c) x[v2] -= xc * L[k * kLd + c];
+                const double lkc = L[k * kLd + c];
+                x[v2] = fma(k > c ? -xc : 0.0, lkc, x[v2]);
             }
         }
     }
@@ -225,7 +228,7 @@ __global__ __launch_bounds__(256) void k_chol_update(double *__restrict__ A, int
 #pragma unroll
         for (int u = 0; u < 4; ++u)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) acc[u][v] += a[u] * b[v];
+            for (int v = 0; v < 4; ++v) acc[u][v] = fma(a[u], b[v], acc[u][v]);
     }
     double old[4][4];  // all 16 loads issued before the stores
 #pragma unroll
@@ -304,33 +307,33 @@ __global__ __launch_bounds__(64) void k_gptq_cols(const void *__restrict__ W, in
     }
     const double s = in ? (double)(alpha * e4m3_value(sb)) : 0.0;  // fl32(alpha Delta) of the lane's block
     __syncthreads();
-    double ev[16];
+    double ev[16] = {};
     uint32_t packed[2] = {0u, 0u};
     for (int cgs = 0; 16 * cgs < nb; ++cgs) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             const int j = 16 * cgs + v;
+            // branch-free: a block scale that is not positive (s = 0, or NaN) gives code 0 and no dequantised value
             const double t = w[v] + acc[v] / V[j * kLd + j];
-            uint32_t code = 0;
-            double deq = 0.0;
-            if (s > 0.0) {
-                const double x = t / s;
-                const uint32_t idx = e2m1_index64(fabs(x));
-                const bool neg = x < 0.0 && idx > 0;
-                code = idx | (neg ? 8u : 0u);
-                const double mag = idx < 4 ? 0.5 * idx : (idx == 7 ? 6.0 : (double)(idx - 2));
-                deq = (neg ? -mag : mag) * s;
-            }
+            const bool live = s > 0.0;
+            const double x = t / (live ? s : 1.0);
+            const uint32_t idx = live ? e2m1_index64(fabs(x)) : 0u;
+            const bool neg = x < 0.0 && idx > 0;
+            const uint32_t code = idx | (neg ? 8u : 0u);
+            const double mag = idx < 4 ? 0.5 * idx : (idx == 7 ? 6.0 : (double)(idx - 2));
+            const double deq = live ? (neg ? -mag : mag) * s : 0.0;
             const double e = w[v] - deq;
-            if (cg == cgs) {
-                ev[v] = e;
-                packed[v / 8] |= code << (4 * (v % 8));
-            }
+            const bool own = cg == cgs;
+            ev[v] = own ? e : ev[v];
+            packed[v / 8] |= (own ? code : 0u) << (4 * (v % 8));
             const double ej = __shfl(e, rr + 16 * cgs);
+            // unmasked (a zero multiplier leaves earlier columns exactly as they are), so the 16 LDS
+            // reads are issued together
 #pragma unroll
             for (int v2 = 0; v2 < 16; ++v2) {
                 const int k = 16 * cg + v2;
-                if (k > j) acc[v2] += ej * V[j * kLd + k];
+                const double vjk = V[j * kLd + k];
+                acc[v2] = fma(k > j ? ej : 0.0, vjk, acc[v2]);
             }
         }
     }
@@ -370,7 +373,7 @@ __global__ __launch_bounds__(256) void k_gptq_update(const double *__restrict__ 
 #pragma unroll
         for (int u = 0; u < 4; ++u)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) acc[u][v] += a[u] * b[v];
+            for (int v = 0; v < 4; ++v) acc[u][v] = fma(a[u], b[v], acc[u][v]);
     }
     const bool first = b0 == 0;
     double old[4][4];  // all 16 loads issued before the stores
