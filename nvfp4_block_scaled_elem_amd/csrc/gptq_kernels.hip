@@ -21,12 +21,15 @@
 //   k_gptq_reverse  A = P (H with dead diagonals 1, + lambda I) P, lower triangle
 //   k_chol_diag,    blocked right-looking Cholesky of A in place, panels of 64 columns: the diagonal
 //   k_chol_trsm,    block (one wave, rows in registers), the rows below it (a wave per 16 rows), then
-//   k_chol_update   the trailing lower triangle (64 x 64 fp64 tiles)
+//   k_chol_update   the trailing lower triangle (64 x 64 tiles on the fp64 matrix cores)
+//   k_gptq_pack_v   V's diagonal 64 x 64 blocks, packed contiguously for the sweep
 //   k_gptq_cols     columns [b0, b0 + 64), a wave per 16 rows, in order (target, E2M1 code, error e_j),
 //                   each column's errors folded into the block's later columns at once
-//   k_gptq_update   S[:, k] += sum over the block of e_i V_ik for every later column k (fp64 tiles)
-// S holds sum_{i<b0} e_i V_ik for the columns not yet reached. Block 0's update writes it, so it needs no
-// clearing.
+//   k_gptq_update   S[:, k] += sum over a run of blocks of e_i V_ik for later columns k (fp64 matrix
+//                   cores, 64 x 64 tiles): after each block for the rest of its group of 4 blocks, after a
+//                   group for every column beyond it
+// S holds sum_{i<b0} e_i V_ik for the columns not yet reached. The updates whose reduction starts at column 0
+// write it, so it needs no clearing.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -44,6 +47,7 @@ constexpr int kPanel = 64;           // Cholesky panel width = GPTQ column block
 constexpr int kLd = kPanel + 1;      // LDS row stride in doubles: rows land on different banks
 constexpr int kTile = 64;            // output tile of the fp64 update kernels (64 x 64, 4 x 4 per thread)
 constexpr int kPrepThreads = 1024;
+constexpr int kSuper = 256;          // column blocks are grouped by 4: S beyond a group is updated once per group
 
 // A 64 x 64 tile of doubles into LDS by 256 threads: element (r, c) (c fastest across threads) is
 // src[off(r, c)] where ok(r, c), else fill(r, c), stored at lds[pos(r, c)]. All 16 loads of a thread
@@ -83,6 +87,36 @@ __device__ __forceinline__ double readlane_f64(double x, int lane) {
     const unsigned hi = __builtin_amdgcn_readlane((int)(unsigned)(u >> 32), lane);
     return __longlong_as_double(((unsigned long long)hi << 32) | lo);
 }
+
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+// One 64-deep step of a 64 x 64 output tile on the fp64 matrix cores: out[r][c] += sum_i P[r][i] Q[c][i]
+// with P and Q staged in LDS (row stride kLd). Wave w computes the 32 x 32 quadrant (wm, wn) =
+// (32 (w / 2), 32 (w % 2)) as 2 x 2 tiles of v_mfma_f64_16x16x4f64, whose lane layout (checked on the
+// device with integer inputs) is: lane l holds A[l % 16][l / 16] and B[l / 16][l % 16], and register q of
+// the result holds D[4 q + l / 16][l % 16].
+__device__ __forceinline__ void mfma_tile64(const double *P, const double *Q, f64x4 (&acc)[2][2]) {
+    const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int wm = 32 * (w >> 1), wn = 32 * (w & 1);
+#pragma unroll 4
+    for (int kk = 0; kk < kPanel; kk += 4) {
+        double a[2], b[2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) a[m] = P[(wm + 16 * m + (l & 15)) * kLd + kk + (l >> 4)];
+#pragma unroll
+        for (int n = 0; n < 2; ++n) b[n] = Q[(wn + 16 * n + (l & 15)) * kLd + kk + (l >> 4)];
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int n = 0; n < 2; ++n) acc[m][n] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[m], b[n], acc[m][n], 0, 0, 0);
+    }
+}
+
+// Row and column (within the 64 x 64 tile) of result register q of tile (m, n) in this lane.
+__device__ __forceinline__ int tile_row(int m, int q) {
+    return 32 * ((threadIdx.x >> 6) >> 1) + 16 * m + 4 * q + ((threadIdx.x & 63) >> 4);
+}
+__device__ __forceinline__ int tile_col(int n) { return 32 * ((threadIdx.x >> 6) & 1) + 16 * n + (threadIdx.x & 15); }
 
 __global__ __launch_bounds__(kPrepThreads) void k_gptq_prep(const double *__restrict__ H, int64_t K, double percdamp,
                                                             double *__restrict__ damp, uint8_t *__restrict__ dead,
@@ -179,7 +213,7 @@ __global__ __launch_bounds__(64) void k_chol_trsm(double *__restrict__ A, int64_
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             const int c = 16 * cgs + v;
-            const double xv = x[v] / L[c * kLd + c];
+            const double xv = x[v] * (1.0 / L[c * kLd + c]);  // the reciprocal does not wait for x
             if (cg == cgs) x[v] = xv;
             const double xc = __shfl(xv, rr + 16 * cgs);
             // unmasked (a zero multiplier leaves earlier columns exactly as they are), so the 16 LDS
@@ -216,35 +250,42 @@ __global__ __launch_bounds__(256) void k_chol_update(double *__restrict__ A, int
         Pj, A, [&](int r, int t) { return (j0 + r) * K + p0 + t; }, [&](int r, int t) { return j0 + r < K && t < nb; },
         zero, at);
     __syncthreads();
-    const int ty = tid / 16, tx = tid % 16;
-    double acc[4][4] = {};
-    for (int t = 0; t < kPanel; ++t) {
-        double a[4], b[4];
+    f64x4 acc[2][2] = {};
+    mfma_tile64(Pi, Pj, acc);
+    double old[2][2][4];  // all loads issued before the stores
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            a[u] = Pi[(ty + 16 * u) * kLd + t];
-            b[u] = Pj[(tx + 16 * u) * kLd + t];
-        }
+    for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int n = 0; n < 2; ++n)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) acc[u][v] = fma(a[u], b[v], acc[u][v]);
-    }
-    double old[4][4];  // all 16 loads issued before the stores
+            for (int q = 0; q < 4; ++q) {
+                const int64_t i = i0 + tile_row(m, q), j = j0 + tile_col(n);
+                old[m][n][q] = A[i < K && j <= i ? i * K + j : 0];
+            }
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int64_t i = i0 + ty + 16 * u, j = j0 + tx + 16 * v;
-            old[u][v] = A[i < K && j <= i ? i * K + j : 0];
-        }
+        for (int n = 0; n < 2; ++n)
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int64_t i = i0 + ty + 16 * u, j = j0 + tx + 16 * v;
-            if (i < K && j <= i) A[i * K + j] = old[u][v] - acc[u][v];
-        }
+            for (int q = 0; q < 4; ++q) {
+                const int64_t i = i0 + tile_row(m, q), j = j0 + tile_col(n);
+                if (i < K && j <= i) A[i * K + j] = old[m][n][q] - acc[m][n][q];
+            }
+}
+
+// The diagonal 64 x 64 blocks of V, packed contiguously for the column sweep: Vb[b][i][j] = V_(64b+i, 64b+j)
+// for i <= j < nb, identity padding, zeros below the diagonal. One work-group per block.
+__global__ __launch_bounds__(256) void k_gptq_pack_v(const double *__restrict__ A, int64_t K, double *__restrict__ Vb) {
+    __shared__ double T[kPanel * kLd];
+    const int64_t b0 = (int64_t)blockIdx.x * kPanel;
+    const int nb = (int)min<int64_t>(kPanel, K - b0);
+    load_tile(
+        T, A, [&](int i, int j) { return (K - 1 - b0 - i) * K + (K - 1 - b0 - j); },
+        [&](int i, int j) { return j < nb && i <= j; }, [](int i, int j) { return i == j ? 1.0 : 0.0; },
+        [](int i, int j) { return i * kLd + j; });
+    __syncthreads();
+    double *dst = Vb + b0 * kPanel;
+    for (int idx = threadIdx.x; idx < kPanel * kPanel; idx += 256) dst[idx] = T[(idx >> 6) * kLd + (idx & 63)];
 }
 
 // E2M1 index of the nearest magnitude to a >= 0 (ties to the even index, 6 beyond 5).
@@ -259,15 +300,16 @@ __device__ __forceinline__ uint32_t e2m1_index64(double a) {
 // later columns. No barriers after the load of V.
 template <bool F32>
 __global__ __launch_bounds__(64) void k_gptq_cols(const void *__restrict__ W, int64_t R, int64_t K, int64_t b0,
-                                                  int nb, const double *__restrict__ A,
+                                                  int nb, const double *__restrict__ Vb,
                                                   const uint8_t *__restrict__ dead,
                                                   const uint8_t *__restrict__ scales,
                                                   const float *__restrict__ alpha_p, const double *__restrict__ S,
-                                                  double *__restrict__ E, uint8_t *__restrict__ codes) {
+                                                  double *__restrict__ E, int ldE, int ecol0,
+                                                  uint8_t *__restrict__ codes) {
     __shared__ double V[kPanel * kLd];  // V[i][j] = V_(b0+i, b0+j) for i <= j, identity padding
     load_tile_wave(
-        V, A, [&](int i, int j) { return (K - 1 - b0 - i) * K + (K - 1 - b0 - j); },
-        [&](int i, int j) { return j < nb && i <= j; }, [](int i, int j) { return i == j ? 1.0 : 0.0; });
+        V, Vb + (b0 / kPanel) * kPanel * kPanel, [](int i, int j) { return i * kPanel + j; },
+        [](int, int) { return true; }, [](int, int) { return 0.0; });
     const int lane = threadIdx.x, rr = lane & 15, cg = lane >> 4;
     const int64_t row = (int64_t)blockIdx.x * 16 + rr;
     const bool in = row < R && 16 * cg < nb;  // nb % 16 == 0: a chunk is whole or absent
@@ -314,7 +356,7 @@ __global__ __launch_bounds__(64) void k_gptq_cols(const void *__restrict__ W, in
         for (int v = 0; v < 16; ++v) {
             const int j = 16 * cgs + v;
             // branch-free: a block scale that is not positive (s = 0, or NaN) gives code 0 and no dequantised value
-            const double t = w[v] + acc[v] / V[j * kLd + j];
+            const double t = w[v] + acc[v] * (1.0 / V[j * kLd + j]);  // the reciprocal does not wait for acc
             const bool live = s > 0.0;
             const double x = t / (live ? s : 1.0);
             const uint32_t idx = live ? e2m1_index64(fabs(x)) : 0u;
@@ -338,59 +380,55 @@ __global__ __launch_bounds__(64) void k_gptq_cols(const void *__restrict__ W, in
         }
     }
     if (in) {
-        double *ep = E + row * kPanel + 16 * cg;
+        double *ep = E + row * ldE + ecol0 + 16 * cg;
 #pragma unroll
         for (int v = 0; v < 16; ++v) ep[v] = ev[v];
         *reinterpret_cast<uint2 *>(codes + base / 2) = make_uint2(packed[0], packed[1]);  // 8-byte aligned
     }
 }
 
-// S[r][k] (=, or += after block 0) sum_{i < nb} E[r][i] V_(b0+i, k) for k in [b0 + nb, K), 64 x 64 tiles.
-__global__ __launch_bounds__(256) void k_gptq_update(const double *__restrict__ E, const double *__restrict__ A,
-                                                     double *__restrict__ S, int64_t R, int64_t K, int64_t b0,
-                                                     int nb) {
+// S[r][k] (=, when the reduction starts at column 0, else +=) sum_{i < depth} E[r][ecol0 + i] V_(vrow0+i, k)
+// for k in [kbeg, kend), in 64 x 64 tiles on the fp64 matrix cores, the reduction in 64-deep steps.
+__global__ __launch_bounds__(256) void k_gptq_update(const double *__restrict__ E, int ldE, int ecol0,
+                                                     const double *__restrict__ A, double *__restrict__ S, int64_t R,
+                                                     int64_t K, int64_t vrow0, int depth, int64_t kbeg, int64_t kend) {
     __shared__ double Et[kTile * kLd], Vt[kTile * kLd];
-    const int64_t r0 = (int64_t)blockIdx.y * kTile, k0 = b0 + nb + (int64_t)blockIdx.x * kTile;
-    const int tid = threadIdx.x;
+    const int64_t r0 = (int64_t)blockIdx.y * kTile, k0 = kbeg + (int64_t)blockIdx.x * kTile;
     const auto zero = [](int, int) { return 0.0; };
-    load_tile(
-        Et, E, [&](int a, int i) { return (r0 + a) * kPanel + i; }, [&](int a, int i) { return r0 + a < R && i < nb; },
-        zero, [](int a, int i) { return a * kLd + i; });
-    // row i of the block, consecutive threads on consecutive (descending) A columns; stored transposed
-    load_tile(
-        Vt, A, [&](int i, int kk) { return (K - 1 - b0 - i) * K + (K - 1 - k0 - kk); },
-        [&](int i, int kk) { return k0 + kk < K && i < nb; }, zero, [](int i, int kk) { return kk * kLd + i; });
-    __syncthreads();
-    const int ty = tid / 16, tx = tid % 16;
-    double acc[4][4] = {};
-    for (int i = 0; i < kPanel; ++i) {
-        double a[4], b[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            a[u] = Et[(ty + 16 * u) * kLd + i];
-            b[u] = Vt[(tx + 16 * u) * kLd + i];
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) acc[u][v] = fma(a[u], b[v], acc[u][v]);
+    f64x4 acc[2][2] = {};
+    for (int d0 = 0; d0 < depth; d0 += kPanel) {
+        const int dn = min(kPanel, depth - d0);
+        if (d0 > 0) __syncthreads();  // the previous step's reads are done
+        load_tile(
+            Et, E, [&](int a, int i) { return (r0 + a) * ldE + ecol0 + d0 + i; },
+            [&](int a, int i) { return r0 + a < R && i < dn; }, zero, [](int a, int i) { return a * kLd + i; });
+        // reduction row i, consecutive threads on consecutive (descending) A columns; stored transposed
+        load_tile(
+            Vt, A, [&](int i, int kk) { return (K - 1 - vrow0 - d0 - i) * K + (K - 1 - k0 - kk); },
+            [&](int i, int kk) { return k0 + kk < kend && i < dn; }, zero, [](int i, int kk) { return kk * kLd + i; });
+        __syncthreads();
+        mfma_tile64(Et, Vt, acc);
     }
-    const bool first = b0 == 0;
-    double old[4][4];  // all 16 loads issued before the stores
+    const bool first = vrow0 == 0;
+    double old[2][2][4];  // all loads issued before the stores
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int64_t r = r0 + ty + 16 * u, k = k0 + tx + 16 * v;
-            old[u][v] = first ? 0.0 : S[r < R && k < K ? r * K + k : 0];
-        }
+        for (int n = 0; n < 2; ++n)
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+            for (int q = 0; q < 4; ++q) {
+                const int64_t r = r0 + tile_row(m, q), k = k0 + tile_col(n);
+                old[m][n][q] = first ? 0.0 : S[r < R && k < kend ? r * K + k : 0];
+            }
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int64_t r = r0 + ty + 16 * u, k = k0 + tx + 16 * v;
-            if (r < R && k < K) S[r * K + k] = first ? acc[u][v] : old[u][v] + acc[u][v];
-        }
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t r = r0 + tile_row(m, q), k = k0 + tile_col(n);
+                if (r < R && k < kend) S[r * K + k] = old[m][n][q] + acc[m][n][q];
+            }
 }
 
 // A failed factorisation (a pivot not positive and finite): alpha = NaN and every code 0. n8 = the
@@ -407,7 +445,9 @@ __global__ __launch_bounds__(256) void k_gptq_finish(const int *__restrict__ fla
 
 size_t gptq_workspace_bytes(int64_t R, int64_t K) {
     auto up = [](size_t b) { return (b + 255) / 256 * 256; };
-    return up((size_t)K * K * 8) + up((size_t)R * K * 8) + up((size_t)R * kPanel * 8) + up((size_t)K) + 256 +
+    const size_t nblocks = (size_t)(K + kPanel - 1) / kPanel;
+    return up((size_t)K * K * 8) + up((size_t)R * K * 8) + up((size_t)R * kSuper * 8) +
+           up(nblocks * kPanel * kPanel * 8) + up((size_t)K) + 256 +
            workspace_bytes(R * K / 16, NVFP4_MODE_FOUR_OVER_SIX);
 }
 
@@ -420,7 +460,10 @@ hipError_t launch_gptq(const void *W, bool f32, int64_t R, int64_t K, const doub
     double *S = reinterpret_cast<double *>(p);
     p += up((size_t)R * K * 8);
     double *E = reinterpret_cast<double *>(p);
-    p += up((size_t)R * kPanel * 8);
+    p += up((size_t)R * kSuper * 8);
+    const int64_t nblocks = (K + kPanel - 1) / kPanel;
+    double *Vb = reinterpret_cast<double *>(p);
+    p += up((size_t)nblocks * kPanel * kPanel * 8);
     uint8_t *dead = reinterpret_cast<uint8_t *>(p);
     p += up((size_t)K);
     double *damp = reinterpret_cast<double *>(p);
@@ -451,20 +494,27 @@ hipError_t launch_gptq(const void *W, bool f32, int64_t R, int64_t K, const doub
             hipLaunchKernelGGL(k_chol_update, dim3(t, t), dim3(256), 0, stream, A, K, p0, nb);
         }
     }
+    hipLaunchKernelGGL(k_gptq_pack_v, dim3((unsigned)nblocks), dim3(256), 0, stream, A, K, Vb);
+    // Column blocks of 64, grouped by 4 (the last group may be shorter). E holds the group's errors. After a
+    // block, S is updated only for the rest of its group; after the group's last block, for every later
+    // column at once, with the group's whole error block as the reduction.
+    const unsigned row_tiles = (unsigned)((R + kTile - 1) / kTile);
     for (int64_t b0 = 0; b0 < K; b0 += kPanel) {
         const int nb = (int)std::min<int64_t>(kPanel, K - b0);
+        const int64_t sb0 = b0 / kSuper * kSuper, sb1 = std::min<int64_t>(sb0 + kSuper, K), b1 = b0 + nb;
         const dim3 grid((unsigned)((R + 15) / 16));
         if (f32)
-            hipLaunchKernelGGL(k_gptq_cols<true>, grid, dim3(64), 0, stream, W, R, K, b0, nb, A, dead, scales, alpha,
-                               S, E, codes);
+            hipLaunchKernelGGL(k_gptq_cols<true>, grid, dim3(64), 0, stream, W, R, K, b0, nb, Vb, dead, scales, alpha,
+                               S, E, kSuper, (int)(b0 - sb0), codes);
         else
-            hipLaunchKernelGGL(k_gptq_cols<false>, grid, dim3(64), 0, stream, W, R, K, b0, nb, A, dead, scales, alpha,
-                               S, E, codes);
-        const int64_t later = K - b0 - nb;
-        if (later > 0)
-            hipLaunchKernelGGL(k_gptq_update,
-                               dim3((unsigned)((later + kTile - 1) / kTile), (unsigned)((R + kTile - 1) / kTile)),
-                               dim3(256), 0, stream, E, A, S, R, K, b0, nb);
+            hipLaunchKernelGGL(k_gptq_cols<false>, grid, dim3(64), 0, stream, W, R, K, b0, nb, Vb, dead, scales, alpha,
+                               S, E, kSuper, (int)(b0 - sb0), codes);
+        if (b1 < sb1)
+            hipLaunchKernelGGL(k_gptq_update, dim3((unsigned)((sb1 - b1 + kTile - 1) / kTile), row_tiles), dim3(256), 0,
+                               stream, E, kSuper, (int)(b0 - sb0), A, S, R, K, b0, nb, b1, sb1);
+        else if (sb1 < K)
+            hipLaunchKernelGGL(k_gptq_update, dim3((unsigned)((K - sb1 + kTile - 1) / kTile), row_tiles), dim3(256), 0,
+                               stream, E, kSuper, 0, A, S, R, K, sb0, (int)(sb1 - sb0), sb1, K);
     }
     const int64_t n8 = R * K / 16;
     hipLaunchKernelGGL(k_gptq_finish, dim3((unsigned)std::max<int64_t>(1, (n8 + 255) / 256)), dim3(256), 0, stream,
