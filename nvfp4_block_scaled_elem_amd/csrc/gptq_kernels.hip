@@ -157,11 +157,12 @@ __global__ __launch_bounds__(256) void k_gptq_reverse(const double *__restrict__
 }
 
 // Diagonal block of panel [p0, p0 + nb), factored by one wave: lane r holds row r in registers
-// (padded to 64 with an identity). Column c: the pivot and the column's entries come from their lanes
-// by readlane, so no step waits on LDS or a barrier. Entries above the diagonal are computed and
-// discarded. A pivot that is not positive and finite sets *flag.
+// (padded to 64 with an identity). Column c: the pivot and the column's entries come from their lanes by
+// readlane (an LDS broadcast of the column measured slower). Entries above the diagonal are computed and
+// discarded. The factor is written back into A and, packed column-major with zeros above the diagonal,
+// to Lp for the row solve. A pivot that is not positive and finite sets *flag.
 __global__ __launch_bounds__(64) void k_chol_diag(double *__restrict__ A, int64_t K, int64_t p0,
-                                                  int *__restrict__ flag) {
+                                                  double *__restrict__ Lp, int *__restrict__ flag) {
     const int nb = (int)min<int64_t>(kPanel, K - p0);
     const int r = threadIdx.x;
     double a[kPanel];
@@ -187,20 +188,28 @@ __global__ __launch_bounds__(64) void k_chol_diag(double *__restrict__ A, int64_
     }
     if (bad && r == 0) flag[0] = 1;
 #pragma unroll
-    for (int c = 0; c < kPanel; ++c)
-        if (r < nb && c <= r) A[(p0 + r) * K + p0 + c] = a[c];
+    for (int c = 0; c < kPanel; ++c) {
+        const bool low = c <= r;
+        Lp[c * kPanel + r] = low ? a[c] : 0.0;  // column-major: each store is 512 contiguous bytes
+        if (r < nb && low) A[(p0 + r) * K + p0 + c] = a[c];
+    }
 }
 
 // Rows below the diagonal block of panel [p0, p0 + nb): L21 = A21 L11^-T. One wave per 16 rows: lane
 // (rr, cg) = (lane % 16, lane / 16) holds columns 16 cg .. 16 cg + 15 of row rr. Column c: its holders
 // divide by L_cc, the finished value goes to the row's other lanes by shuffle, and every lane subtracts
-// it from its later columns. No barriers after the load of L11.
-__global__ __launch_bounds__(64) void k_chol_trsm(double *__restrict__ A, int64_t K, int64_t p0) {
+// it from its later columns. No barriers after the load of L11 (packed by k_chol_diag).
+__global__ __launch_bounds__(64) void k_chol_trsm(double *__restrict__ A, int64_t K, int64_t p0,
+                                                  const double *__restrict__ Lp) {
     __shared__ double L[kPanel * kLd];
     const int nb = (int)min<int64_t>(kPanel, K - p0);
-    load_tile_wave(
-        L, A, [&](int r, int c) { return (p0 + r) * K + p0 + c; }, [&](int r, int c) { return r < nb && c <= r; },
-        [](int r, int c) { return r == c ? 1.0 : 0.0; });
+    {  // L11 from its column-major copy: lane = row, each load 512 contiguous bytes
+        double v[kPanel];
+#pragma unroll
+        for (int c = 0; c < kPanel; ++c) v[c] = Lp[c * kPanel + threadIdx.x];
+#pragma unroll
+        for (int c = 0; c < kPanel; ++c) L[threadIdx.x * kLd + c] = v[c];
+    }
     const int lane = threadIdx.x, rr = lane & 15, cg = lane >> 4;
     const int64_t row = p0 + nb + (int64_t)blockIdx.x * 16 + rr;
     const bool in = row < K && 16 * cg < nb;  // nb % 16 == 0: a chunk is whole or absent
@@ -447,7 +456,7 @@ size_t gptq_workspace_bytes(int64_t R, int64_t K) {
     auto up = [](size_t b) { return (b + 255) / 256 * 256; };
     const size_t nblocks = (size_t)(K + kPanel - 1) / kPanel;
     return up((size_t)K * K * 8) + up((size_t)R * K * 8) + up((size_t)R * kSuper * 8) +
-           up(nblocks * kPanel * kPanel * 8) + up((size_t)K) + 256 +
+           up(nblocks * kPanel * kPanel * 8) + up((size_t)kPanel * kPanel * 8) + up((size_t)K) + 256 +
            workspace_bytes(R * K / 16, NVFP4_MODE_FOUR_OVER_SIX);
 }
 
@@ -464,6 +473,8 @@ hipError_t launch_gptq(const void *W, bool f32, int64_t R, int64_t K, const doub
     const int64_t nblocks = (K + kPanel - 1) / kPanel;
     double *Vb = reinterpret_cast<double *>(p);
     p += up((size_t)nblocks * kPanel * kPanel * 8);
+    double *Lp = reinterpret_cast<double *>(p);
+    p += up((size_t)kPanel * kPanel * 8);
     uint8_t *dead = reinterpret_cast<uint8_t *>(p);
     p += up((size_t)K);
     double *damp = reinterpret_cast<double *>(p);
@@ -487,9 +498,9 @@ hipError_t launch_gptq(const void *W, bool f32, int64_t R, int64_t K, const doub
     for (int64_t p0 = 0; p0 < K; p0 += kPanel) {
         const int nb = (int)std::min<int64_t>(kPanel, K - p0);
         const int64_t below = K - p0 - nb;
-        hipLaunchKernelGGL(k_chol_diag, dim3(1), dim3(64), 0, stream, A, K, p0, flag);
+        hipLaunchKernelGGL(k_chol_diag, dim3(1), dim3(64), 0, stream, A, K, p0, Lp, flag);
         if (below > 0) {
-            hipLaunchKernelGGL(k_chol_trsm, dim3((unsigned)((below + 15) / 16)), dim3(64), 0, stream, A, K, p0);
+            hipLaunchKernelGGL(k_chol_trsm, dim3((unsigned)((below + 15) / 16)), dim3(64), 0, stream, A, K, p0, Lp);
             const unsigned t = (unsigned)((below + kTile - 1) / kTile);
             hipLaunchKernelGGL(k_chol_update, dim3(t, t), dim3(256), 0, stream, A, K, p0, nb);
         }
