@@ -20,8 +20,9 @@
 //   k_gptq_prep     dead inputs (zero diagonal) and the damping lambda = percdamp * mean(diag)
 //   k_gptq_reverse  A = P (H with dead diagonals 1, + lambda I) P, lower triangle
 //   k_chol_diag,    blocked right-looking Cholesky of A in place, panels of 64 columns: the diagonal
-//   k_chol_trsm,    block (one wave, rows in registers), the rows below it (a wave per 16 rows), then
-//   k_chol_update   the trailing lower triangle (64 x 64 tiles on the fp64 matrix cores)
+//   k_chol_trsm,    block (one work-group, 4 x 4 register tiles), the rows below it (a wave per 16 rows), then
+//   k_chol_update   the trailing lower triangle (64 x 64 tiles on the fp64 matrix cores); the update's first
+//                   work-group also factors the next diagonal block, so only the first has its own launch
 //   k_gptq_pack_v   V's diagonal 64 x 64 blocks, packed contiguously for the sweep
 //   k_gptq_cols     columns [b0, b0 + 64), a wave per 16 rows, in order (target, E2M1 code, error e_j),
 //                   each column's errors folded into the block's later columns at once
@@ -156,43 +157,79 @@ __global__ __launch_bounds__(256) void k_gptq_reverse(const double *__restrict__
     }
 }
 
-// Diagonal block of panel [p0, p0 + nb), factored by one wave: lane r holds row r in registers
-// (padded to 64 with an identity). Column c: the pivot and the column's entries come from their lanes by
-// readlane (an LDS broadcast of the column measured slower). Entries above the diagonal are computed and
-// discarded. The factor is written back into A and, packed column-major with zeros above the diagonal,
-// to Lp for the row solve. A pivot that is not positive and finite sets *flag.
-__global__ __launch_bounds__(64) void k_chol_diag(double *__restrict__ A, int64_t K, int64_t p0,
-                                                  double *__restrict__ Lp, int *__restrict__ flag) {
-    const int nb = (int)min<int64_t>(kPanel, K - p0);
-    const int r = threadIdx.x;
-    double a[kPanel];
+// Factors the diagonal block of panel [p0, p0 + nb) with the 256 threads of a work-group (padded to 64 with
+// an identity). T is the block's lower triangle in LDS (row stride kLd). Thread (tx, ty) = (tid / 16,
+// tid % 16) holds rows ty + 16u and columns tx + 16v (u, v < 4) in registers, so the 16 threads of a column
+// are lanes of one wave. Column c: its holders take the pivot from its lane by shuffle, scale the column
+// and publish it (a double-buffered LDS slot, one barrier); then every thread subtracts l_rc l_tc from its
+// entries in later columns. Entries above the diagonal are computed and discarded. The factor is written
+// back into A and, packed column-major with zeros above the diagonal, to Lp for the row solve. A pivot that
+// is not positive and finite sets *flag.
+__device__ __forceinline__ void chol_diag_block(const double *T, int nb, double *__restrict__ A, int64_t K,
+                                                int64_t p0, double *__restrict__ Lp, int *__restrict__ flag) {
+    __shared__ double col[2][kPanel];
+    const int tid = threadIdx.x, tx = tid >> 4, ty = tid & 15;
+    double a[4][4];
 #pragma unroll
-    for (int c = 0; c < kPanel; ++c) {
-        const bool ok = r < nb && c <= r;
-        a[c] = A[ok ? (p0 + r) * K + p0 + c : 0];
-    }
+    for (int u = 0; u < 4; ++u)
 #pragma unroll
-    for (int c = 0; c < kPanel; ++c) {
-        const bool ok = r < nb && c <= r;
-        a[c] = ok ? a[c] : (r == c ? 1.0 : 0.0);
-    }
+        for (int v = 0; v < 4; ++v) {
+            const int r = ty + 16 * u, t = tx + 16 * v;
+            a[u][v] = r < nb && t <= r ? T[r * kLd + t] : (r == t ? 1.0 : 0.0);
+        }
     bool bad = false;
 #pragma unroll
-    for (int c = 0; c < kPanel; ++c) {
-        const double s = readlane_f64(a[c], c);  // a_cc after the earlier columns
-        bad = bad || !(s > 0.0) || !(s < INFINITY);
-        const double d = sqrt(s);
-        a[c] = r == c ? d : a[c] / d;  // l_rc for r > c
+    for (int cb = 0; cb < 4; ++cb)
+        for (int cc = 0; cc < 16; ++cc) {
+            const int c = 16 * cb + cc;
+            // a_cc sits in thread (tx, ty) = (cc, cc), lane 16 (cc % 4) + cc of the column's wave
+            const double s = __shfl(a[cb][cb], 16 * (cc & 3) + cc);
+            if (tx == cc) {
+                if (ty == cc && (!(s > 0.0) || !(s < INFINITY))) bad = true;
+                const double d = sqrt(s);
 #pragma unroll
-        for (int t = c + 1; t < kPanel; ++t) a[t] = fma(-a[c], readlane_f64(a[c], t), a[t]);  // a_rt -= l_rc l_tc
-    }
-    if (bad && r == 0) flag[0] = 1;
+                for (int u = 0; u < 4; ++u) {
+                    const int r = ty + 16 * u;
+                    const double l = r == c ? d : a[u][cb] / d;  // l_rc below the diagonal
+                    a[u][cb] = l;
+                    col[c & 1][r] = l;
+                }
+            }
+            __syncthreads();
+            const double *lc = col[c & 1];
+            double lr[4], lt[4];
 #pragma unroll
-    for (int c = 0; c < kPanel; ++c) {
-        const bool low = c <= r;
-        Lp[c * kPanel + r] = low ? a[c] : 0.0;  // column-major: each store is 512 contiguous bytes
-        if (r < nb && low) A[(p0 + r) * K + p0 + c] = a[c];
-    }
+            for (int u = 0; u < 4; ++u) lr[u] = lc[ty + 16 * u];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) lt[v] = lc[tx + 16 * v];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const double m = tx + 16 * v > c ? -lt[v] : 0.0;  // later columns only
+#pragma unroll
+                for (int u = 0; u < 4; ++u) a[u][v] = fma(m, lr[u], a[u][v]);
+            }
+        }
+    if (bad) flag[0] = 1;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int r = ty + 16 * u, t = tx + 16 * v;
+            Lp[t * kPanel + r] = t <= r ? a[u][v] : 0.0;
+            if (r < nb && t <= r) A[(p0 + r) * K + p0 + t] = a[u][v];
+        }
+}
+
+// The first panel's diagonal block (later ones are factored by the trailing update before them).
+__global__ __launch_bounds__(256) void k_chol_diag(double *__restrict__ A, int64_t K, double *__restrict__ Lp,
+                                                   int *__restrict__ flag) {
+    __shared__ double T[kPanel * kLd];
+    const int nb = (int)min<int64_t>(kPanel, K);
+    load_tile(
+        T, A, [&](int r, int c) { return (int64_t)r * K + c; }, [&](int r, int c) { return r < nb && c <= r; },
+        [](int, int) { return 0.0; }, [](int r, int c) { return r * kLd + c; });
+    __syncthreads();
+    chol_diag_block(T, nb, A, K, 0, Lp, flag);
 }
 
 // Rows below the diagonal block of panel [p0, p0 + nb): L21 = A21 L11^-T. One wave per 16 rows: lane
@@ -243,8 +280,10 @@ __global__ __launch_bounds__(64) void k_chol_trsm(double *__restrict__ A, int64_
 }
 
 // Trailing update after panel [p0, p1): A[i][j] -= sum_t A[i][p0+t] A[j][p0+t] for p1 <= j <= i < K.
-// 64 x 64 tiles of the lower triangle (tiles above it exit at once).
-__global__ __launch_bounds__(256) void k_chol_update(double *__restrict__ A, int64_t K, int64_t p0, int nb) {
+// 64 x 64 tiles of the lower triangle (tiles above it exit at once). Work-group (0, 0), dispatched first, holds
+// the next panel's diagonal block and goes on to factor it.
+__global__ __launch_bounds__(256) void k_chol_update(double *__restrict__ A, int64_t K, int64_t p0, int nb,
+                                                     double *__restrict__ Lp, int *__restrict__ flag) {
     const int ti = blockIdx.y, tj = blockIdx.x;
     if (tj > ti) return;
     __shared__ double Pi[kTile * kLd], Pj[kTile * kLd];
@@ -280,6 +319,18 @@ __global__ __launch_bounds__(256) void k_chol_update(double *__restrict__ A, int
                 const int64_t i = i0 + tile_row(m, q), j = j0 + tile_col(n);
                 if (i < K && j <= i) A[i * K + j] = old[m][n][q] - acc[m][n][q];
             }
+    if (ti == 0 && tj == 0) {
+        // this tile is the next panel's diagonal block, now final: factor it here, from LDS
+        __syncthreads();  // every thread is done with Pi
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int n = 0; n < 2; ++n)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) Pi[tile_row(m, q) * kLd + tile_col(n)] = old[m][n][q] - acc[m][n][q];
+        __syncthreads();
+        chol_diag_block(Pi, (int)min<int64_t>(kPanel, K - p1), A, K, p1, Lp, flag);
+    }
 }
 
 // The diagonal 64 x 64 blocks of V, packed contiguously for the column sweep: Vb[b][i][j] = V_(64b+i, 64b+j)
@@ -495,14 +546,14 @@ hipError_t launch_gptq(const void *W, bool f32, int64_t R, int64_t K, const doub
     hipLaunchKernelGGL(k_gptq_prep, dim3(1), dim3(kPrepThreads), 0, stream, H, K, percdamp, damp, dead, flag);
     hipLaunchKernelGGL(k_gptq_reverse, dim3((unsigned)((K + 255) / 256), (unsigned)K), dim3(256), 0, stream, H, K,
                        damp, dead, A);
+    hipLaunchKernelGGL(k_chol_diag, dim3(1), dim3(256), 0, stream, A, K, Lp, flag);
     for (int64_t p0 = 0; p0 < K; p0 += kPanel) {
         const int nb = (int)std::min<int64_t>(kPanel, K - p0);
         const int64_t below = K - p0 - nb;
-        hipLaunchKernelGGL(k_chol_diag, dim3(1), dim3(64), 0, stream, A, K, p0, Lp, flag);
         if (below > 0) {
             hipLaunchKernelGGL(k_chol_trsm, dim3((unsigned)((below + 15) / 16)), dim3(64), 0, stream, A, K, p0, Lp);
             const unsigned t = (unsigned)((below + kTile - 1) / kTile);
-            hipLaunchKernelGGL(k_chol_update, dim3(t, t), dim3(256), 0, stream, A, K, p0, nb);
+            hipLaunchKernelGGL(k_chol_update, dim3(t, t), dim3(256), 0, stream, A, K, p0, nb, Lp, flag);
         }
     }
     hipLaunchKernelGGL(k_gptq_pack_v, dim3((unsigned)nblocks), dim3(256), 0, stream, A, K, Vb);
