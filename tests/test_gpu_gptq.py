@@ -115,3 +115,52 @@ def test_gptq_full_size_sample():
     assert a == ref["alpha"] and np.array_equal(s, ref["scales"])
     diff = np.sum(c[rows] != ref["codes"])
     assert diff == 0, f"{diff} code bytes differ"
+
+
+def test_gptq_graph_replays_match_eager():
+    """nvfp4_gptq with caller buffers captured in a graph (its kernels clear nothing with memsets),
+    replayed three times with eager work in between: every replay equals the eager call."""
+    say("gptq graph capture")
+    W = dev_w(synth.normal_bf16(96, 320, 13))
+    H = torch.from_numpy(synth.hessian(320, 13)).cuda()
+    ws = torch.empty(nv.gptq_workspace_bytes(96, 320), dtype=torch.uint8, device="cuda")
+    ref = [t.clone() for t in nv.gptq(W, H, workspace=ws)]
+    torch.cuda.synchronize()
+    outs = (torch.empty_like(ref[0]), torch.empty_like(ref[1]), torch.empty_like(ref[2]))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        nv.gptq(W, H, codes=outs[0], scales=outs[1], alpha=outs[2], workspace=ws)
+    for rep in range(3):
+        for t in outs:
+            t.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(outs, ref):
+            assert torch.equal(a, b), rep
+        nv.quantize(W, "max")  # eager work between replays
+        torch.cuda.synchronize()
+
+
+def test_gptq_mlp_shape_sample():
+    """11008 x 4096 bf16 (an MLP up/gate projection of the 7B-shaped workload): every 97th row against
+    the oracle."""
+    say("gptq 11008x4096")
+    W = synth.c5(0, "gate")
+    H = synth.hessian(4096, 14, n=4096)
+    c, s, a = run_gpu(W, H)
+    rows = np.arange(0, W.shape[0], 97)
+    ref = og.gptq(W, H, 0.01, rows=rows)
+    assert a == ref["alpha"] and np.array_equal(s, ref["scales"])
+    assert np.array_equal(c[rows], ref["codes"])
+
+
+def test_gptq_long_rows_ragged_group():
+    """cols = 6160: 96 full column blocks and a 16-column one, the last group of 4 blocks incomplete."""
+    say("gptq 256x6160")
+    W = synth.normal_bf16(256, 6160, 15)
+    H = synth.hessian(6160, 15, n=4096)
+    c, s, a = run_gpu(W, H)
+    rows = np.arange(0, 256, 5)
+    ref = og.gptq(W, H, 0.01, rows=rows)
+    assert a == ref["alpha"] and np.array_equal(s, ref["scales"])
+    assert np.array_equal(c[rows], ref["codes"])
