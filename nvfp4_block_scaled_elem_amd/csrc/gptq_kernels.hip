@@ -255,11 +255,14 @@ __global__ __launch_bounds__(64) void k_chol_trsm(double *__restrict__ A, int64_
 #pragma unroll
     for (int v = 0; v < 16; ++v) x[v] = src[v];
     __syncthreads();
+    __shared__ double rl[kPanel];  // 1 / L_cc, once per work-group, so no step waits for a division by it
+    rl[lane] = 1.0 / L[lane * kLd + lane];
+    __syncthreads();
     for (int cgs = 0; 16 * cgs < nb; ++cgs) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             const int c = 16 * cgs + v;
-            const double xv = x[v] * (1.0 / L[c * kLd + c]);  // the reciprocal does not wait for x
+            const double xv = x[v] * rl[c];
             if (cg == cgs) x[v] = xv;
             const double xc = __shfl(xv, rr + 16 * cgs);
             // unmasked (a zero multiplier leaves earlier columns exactly as they are), so the 16 LDS
@@ -409,6 +412,9 @@ __global__ __launch_bounds__(64) void k_gptq_cols(const void *__restrict__ W, in
     }
     const double s = in ? (double)(alpha * e4m3_value(sb)) : 0.0;  // fl32(alpha Delta) of the lane's block
     __syncthreads();
+    __shared__ double rv[kPanel];  // 1 / V_jj, once per work-group, so no step waits for a division by it
+    rv[lane] = 1.0 / V[lane * kLd + lane];
+    __syncthreads();
     double ev[16] = {};
     uint32_t packed[2] = {0u, 0u};
     for (int cgs = 0; 16 * cgs < nb; ++cgs) {
@@ -416,7 +422,7 @@ __global__ __launch_bounds__(64) void k_gptq_cols(const void *__restrict__ W, in
         for (int v = 0; v < 16; ++v) {
             const int j = 16 * cgs + v;
             // branch-free: a block scale that is not positive (s = 0, or NaN) gives code 0 and no dequantised value
-            const double t = w[v] + acc[v] * (1.0 / V[j * kLd + j]);  // the reciprocal does not wait for acc
+            const double t = w[v] + acc[v] * rv[j];
             const bool live = s > 0.0;
             const double x = t / (live ? s : 1.0);
             const uint32_t idx = live ? e2m1_index64(fabs(x)) : 0u;
