@@ -81,14 +81,6 @@ __device__ __forceinline__ void load_tile_wave(double *lds, const double *__rest
     for (int r = 0; r < kPanel; ++r) lds[r * kLd + c] = ok(r, c) ? v[r] : fill(r, c);
 }
 
-// x of lane `lane` (a compile-time constant after unrolling) in every lane.
-__device__ __forceinline__ double readlane_f64(double x, int lane) {
-    const unsigned long long u = __double_as_longlong(x);
-    const unsigned lo = __builtin_amdgcn_readlane((int)(unsigned)u, lane);
-    const unsigned hi = __builtin_amdgcn_readlane((int)(unsigned)(u >> 32), lane);
-    return __longlong_as_double(((unsigned long long)hi << 32) | lo);
-}
-
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 // One 64-deep step of a 64 x 64 output tile on the fp64 matrix cores: out[r][c] += sum_i P[r][i] Q[c][i]
@@ -291,7 +283,6 @@ __global__ __launch_bounds__(256) void k_chol_update(double *__restrict__ A, int
     if (tj > ti) return;
     __shared__ double Pi[kTile * kLd], Pj[kTile * kLd];
     const int64_t p1 = p0 + nb, i0 = p1 + (int64_t)ti * kTile, j0 = p1 + (int64_t)tj * kTile;
-    const int tid = threadIdx.x;
     const auto zero = [](int, int) { return 0.0; };
     const auto at = [](int r, int t) { return r * kLd + t; };
     load_tile(

@@ -341,7 +341,6 @@ __global__ __launch_bounds__(kQuantThreads) __attribute__((amdgpu_waves_per_eu(4
             bool m4 = false;
             const float a = B.amax();
             const uint32_t d6 = e4m3_rne(max_rule_quotient(a, alpha));
-            const float v6 = e4m3_value(d6);
             sc = d6;
             if constexpr (!FOS) {
                 const float r = T.r[d6];
