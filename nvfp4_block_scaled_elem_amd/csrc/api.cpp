@@ -5,6 +5,9 @@
 //   MAX / FourOverSix : k_amax -> k_quant
 //   CJSO(T)           : k_amax -> k_cjso_init -> T x k_cjso_iter
 //   SOAR(T)           : CJSO(T) -> k_soar
+//   GPTQ (nvfp4_gptq) : k_amax -> k_quant (the FourOverSix frame) -> k_gptq_prep -> k_gptq_reverse ->
+//                       k_chol_diag -> per panel {k_chol_trsm, k_chol_update} -> k_gptq_pack_v ->
+//                       per column block {k_gptq_cols, k_gptq_update} -> k_gptq_finish
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>

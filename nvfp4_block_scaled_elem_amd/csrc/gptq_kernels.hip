@@ -29,6 +29,7 @@
 //   k_gptq_update   S[:, k] += sum over a run of blocks of e_i V_ik for later columns k (fp64 matrix
 //                   cores, 64 x 64 tiles): after each block for the rest of its group of 4 blocks, after a
 //                   group for every column beyond it
+//   k_gptq_finish   a failed factorisation (a pivot that is not positive and finite): alpha = NaN, codes 0
 // S holds sum_{i<b0} e_i V_ik for the columns not yet reached. The updates whose reduction starts at column 0
 // write it, so it needs no clearing.
 #include <hip/hip_runtime.h>
