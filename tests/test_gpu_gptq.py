@@ -164,3 +164,29 @@ def test_gptq_long_rows_ragged_group():
     ref = og.gptq(W, H, 0.01, rows=rows)
     assert a == ref["alpha"] and np.array_equal(s, ref["scales"])
     assert np.array_equal(c[rows], ref["codes"])
+
+
+@pytest.mark.parametrize("case", ["zero_w", "zero_h", "inf_w"])
+def test_gptq_degenerate_inputs(case):
+    """All-zero weights (alpha 0, every code 0), an all-zero H (every input dead: every weight counts as
+    zero) and a weight that is infinite (FourOverSix's in-band result: alpha NaN, zero codes and scales),
+    each against the oracle."""
+    say(f"gptq degenerate {case}")
+    W = synth.normal_bf16(24, 96, 16)
+    H = synth.hessian(96, 16)
+    if case == "zero_w":
+        W = np.zeros_like(W)
+    elif case == "zero_h":
+        H = np.zeros_like(H)
+    else:
+        W = W.copy()
+        W[3, 17] = 0x7F80  # +inf in bf16
+    with np.errstate(all="ignore"):  # the oracle's sweep carries the infinity through its arithmetic
+        ref = og.gptq(W, H, 0.01)
+    c, s, a = run_gpu(W, H)
+    assert np.array_equal(c, ref["codes"]) and np.array_equal(s, ref["scales"])
+    assert (np.isnan(a) and np.isnan(ref["alpha"])) or a == ref["alpha"]
+    if case != "inf_w":
+        assert not c.any()
+    else:
+        assert np.isnan(a) and not c.any() and not s.any()
