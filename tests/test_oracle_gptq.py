@@ -52,9 +52,10 @@ def prepared(H, percdamp):
     return H, dead
 
 
-@pytest.mark.parametrize("R,K,seed,dead", [(5, 48, 1, 0), (3, 64, 2, 4), (4, 32, 3, 0)])
-def test_targets_are_the_conditional_optimum(R, K, seed, dead):
-    W = synth.normal_bf16(R, K, seed)
+@pytest.mark.parametrize("R,K,seed,dead,f32", [(5, 48, 1, 0, False), (3, 64, 2, 4, False), (4, 32, 3, 0, False),
+                                               (4, 48, 11, 2, True)])
+def test_targets_are_the_conditional_optimum(R, K, seed, dead, f32):
+    W = synth.normal_f32(R, K, seed) if f32 else synth.normal_bf16(R, K, seed)
     H = synth.hessian(K, seed, dead=dead)
     o = og.gptq(W, H, 0.01, trace=True)
     Hd, dead_cols = prepared(H, 0.01)
@@ -145,3 +146,16 @@ def test_gptq_lowers_the_weighted_error():
 def test_rejects_bad_shapes():
     with pytest.raises(ValueError):
         og.gptq(synth.normal_bf16(2, 32, 0), np.eye(16))
+
+
+def test_calibration_second_moment_is_a_valid_input():
+    """The generator's H: exactly symmetric, positive semi-definite (to rounding), dead inputs are whole
+    zero rows and columns, and it is the scaled Gram matrix of its activations."""
+    H = synth.hessian(80, 3, n=120, dead=3)
+    assert np.array_equal(H, H.T)
+    ev = np.linalg.eigvalsh(H)
+    assert ev.min() > -1e-10 * ev.max()
+    dead = np.flatnonzero(np.diag(H) == 0.0)
+    assert dead.size == 3 and not H[dead].any() and not H[:, dead].any()
+    X = synth.activations(120, 80, 3, dead=3)
+    np.testing.assert_allclose(H, X.T @ X / 120, rtol=1e-12, atol=1e-12 * np.abs(H).max())
