@@ -82,6 +82,25 @@ __device__ __forceinline__ void load_tile_wave(double *lds, const double *__rest
     for (int r = 0; r < kPanel; ++r) lds[r * kLd + c] = ok(r, c) ? v[r] : fill(r, c);
 }
 
+// x of lane k (0..3) of this lane's quad, by DPP quad_perm [k, k, k, k] (a few cycles; a shuffle goes
+// through the LDS crossbar). k must fold to a constant after unrolling.
+template <int Q>
+__device__ __forceinline__ double quad_bcast_k(double x) {
+    constexpr int ctrl = Q | (Q << 2) | (Q << 4) | (Q << 6);
+    const unsigned long long u = __double_as_longlong(x);
+    const int lo = __builtin_amdgcn_mov_dpp((int)(unsigned)u, ctrl, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_mov_dpp((int)(unsigned)(u >> 32), ctrl, 0xF, 0xF, false);
+    return __longlong_as_double(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
+}
+__device__ __forceinline__ double quad_bcast(double x, int k) {
+    switch (k) {
+        case 0: return quad_bcast_k<0>(x);
+        case 1: return quad_bcast_k<1>(x);
+        case 2: return quad_bcast_k<2>(x);
+        default: return quad_bcast_k<3>(x);
+    }
+}
+
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 // One 64-deep step of a 64 x 64 output tile on the fp64 matrix cores: out[r][c] += sum_i P[r][i] Q[c][i]
@@ -226,9 +245,9 @@ __global__ __launch_bounds__(256) void k_chol_diag(double *__restrict__ A, int64
 }
 
 // Rows below the diagonal block of panel [p0, p0 + nb): L21 = A21 L11^-T. One wave per 16 rows: lane
-// (rr, cg) = (lane % 16, lane / 16) holds columns 16 cg .. 16 cg + 15 of row rr. Column c: its holders
-// divide by L_cc, the finished value goes to the row's other lanes by shuffle, and every lane subtracts
-// it from its later columns. No barriers after the load of L11 (packed by k_chol_diag).
+// (rr, cg) = (lane / 4, lane % 4) holds columns 16 cg .. 16 cg + 15 of row rr. Column c: its holders
+// divide by L_cc, the finished value goes to the row's other lanes (its quad) by DPP, and every lane
+// subtracts it from its later columns. No barriers after the load of L11 (packed by k_chol_diag).
 __global__ __launch_bounds__(64) void k_chol_trsm(double *__restrict__ A, int64_t K, int64_t p0,
                                                   const double *__restrict__ Lp) {
     __shared__ double L[kPanel * kLd];
@@ -240,7 +259,7 @@ __global__ __launch_bounds__(64) void k_chol_trsm(double *__restrict__ A, int64_
 #pragma unroll
         for (int c = 0; c < kPanel; ++c) L[threadIdx.x * kLd + c] = v[c];
     }
-    const int lane = threadIdx.x, rr = lane & 15, cg = lane >> 4;
+    const int lane = threadIdx.x, rr = lane >> 2, cg = lane & 3;  // a row's four lanes form a quad
     const int64_t row = p0 + nb + (int64_t)blockIdx.x * 16 + rr;
     const bool in = row < K && 16 * cg < nb;  // nb % 16 == 0: a chunk is whole or absent
     const double *src = A + (in ? row * K + p0 + 16 * cg : 0);
@@ -251,13 +270,15 @@ __global__ __launch_bounds__(64) void k_chol_trsm(double *__restrict__ A, int64_
     __shared__ double rl[kPanel];  // 1 / L_cc, once per work-group, so no step waits for a division by it
     rl[lane] = 1.0 / L[lane * kLd + lane];
     __syncthreads();
-    for (int cgs = 0; 16 * cgs < nb; ++cgs) {
+#pragma unroll
+    for (int cgs = 0; cgs < 4; ++cgs) {
+        if (16 * cgs >= nb) break;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             const int c = 16 * cgs + v;
             const double xv = x[v] * rl[c];
             if (cg == cgs) x[v] = xv;
-            const double xc = __shfl(xv, rr + 16 * cgs);
+            const double xc = quad_bcast(xv, cgs);
             // unmasked (a zero multiplier leaves earlier columns exactly as they are), so the 16 LDS
             // reads are issued together
 #pragma unroll
@@ -348,11 +369,11 @@ __device__ __forceinline__ uint32_t e2m1_index64(double a) {
     return (uint32_t)(a > 0.25) + (a >= 0.75) + (a > 1.25) + (a >= 1.75) + (a > 2.5) + (a >= 3.5) + (a > 5.0);
 }
 
-// Columns [b0, b0 + nb), one wave per 16 rows. Lane (rr, cg) = (lane % 16, lane / 16) holds columns
+// Columns [b0, b0 + nb), one wave per 16 rows. Lane (rr, cg) = (lane / 4, lane % 4) holds columns
 // b0 + 16 cg .. + 15 of row rr (one NVFP4 block, so one scale): their weights and running sums
 // acc = S + sum over the block's earlier columns of e_i V_ik. Column j: its holders turn their sum into the
-// target, code and error e_j; e_j reaches the row's other lanes by shuffle; every lane adds e_j V_jk to its
-// later columns. No barriers after the load of V.
+// target, code and error e_j; e_j reaches the row's other lanes (its quad) by DPP; every lane adds e_j V_jk
+// to its later columns. No barriers after the load of V.
 template <bool F32>
 __global__ __launch_bounds__(64) void k_gptq_cols(const void *__restrict__ W, int64_t R, int64_t K, int64_t b0,
                                                   int nb, const double *__restrict__ Vb,
@@ -365,7 +386,7 @@ __global__ __launch_bounds__(64) void k_gptq_cols(const void *__restrict__ W, in
     load_tile_wave(
         V, Vb + (b0 / kPanel) * kPanel * kPanel, [](int i, int j) { return i * kPanel + j; },
         [](int, int) { return true; }, [](int, int) { return 0.0; });
-    const int lane = threadIdx.x, rr = lane & 15, cg = lane >> 4;
+    const int lane = threadIdx.x, rr = lane >> 2, cg = lane & 3;  // a row's four lanes form a quad
     const int64_t row = (int64_t)blockIdx.x * 16 + rr;
     const bool in = row < R && 16 * cg < nb;  // nb % 16 == 0: a chunk is whole or absent
     const int64_t base = in ? row * K + b0 + 16 * cg : 0;  // element index, a multiple of 16
@@ -409,7 +430,9 @@ __global__ __launch_bounds__(64) void k_gptq_cols(const void *__restrict__ W, in
     __syncthreads();
     double ev[16] = {};
     uint32_t packed[2] = {0u, 0u};
-    for (int cgs = 0; 16 * cgs < nb; ++cgs) {
+#pragma unroll
+    for (int cgs = 0; cgs < 4; ++cgs) {
+        if (16 * cgs >= nb) break;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             const int j = 16 * cgs + v;
@@ -426,7 +449,7 @@ __global__ __launch_bounds__(64) void k_gptq_cols(const void *__restrict__ W, in
             const bool own = cg == cgs;
             ev[v] = own ? e : ev[v];
             packed[v / 8] |= (own ? code : 0u) << (4 * (v % 8));
-            const double ej = __shfl(e, rr + 16 * cgs);
+            const double ej = quad_bcast(e, cgs);
             // unmasked (a zero multiplier leaves earlier columns exactly as they are), so the 16 LDS
             // reads are issued together
 #pragma unroll
