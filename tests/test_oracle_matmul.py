@@ -23,7 +23,7 @@ def dequant_indep(codes, scales, alpha, n, k):
 
 @pytest.mark.parametrize("m,n,k,mode", [(3, 32, 64, "4o6"), (5, 48, 160, "soar"), (1, 16, 1024, "max")])
 def test_matches_numpy_product_of_independent_dequantisation(m, n, k, mode):
-    codes, scales, alpha = weights(n, k, seed=m + n)
+    codes, scales, alpha = weights(n, k, seed=m + n, mode=mode)
     X = synth.normal_bf16(m, k, seed=7 * m)
     Y = oracle.matmul(X, codes, scales, alpha, n)
     x = indep.as_f32(X).astype(np.float64)
