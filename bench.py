@@ -232,7 +232,10 @@ def w4a16_pass(torch, nv, dev, W):
     """The consumer of the format: Y = X @ What.T with the 4096 x 4096 weights quantised (FourOverSix)
     and bf16 activations, one case per kernel shape: M = 1 (one token, the GEMV: bound by reading 0.5625 B
     per weight), M = 16 and 64 (the skinny MFMA kernel), M = 256 (128 x 64 MFMA tiles with K split),
-    M = 1024 (128 x 128 tiles) and M = 4096 (256 x 128 tiles, bf16 MFMA-bound). Times are HIP-event averages over a graph of repeated calls on the current stream."""
+    M = 1024 (128 x 128 tiles) and M = 4096 (256 x 128 tiles, bf16 MFMA-bound). Times are HIP-event
+    averages on the current stream: over a graph of repeated calls for M <= 64 (calls of a few microseconds,
+    where host enqueue would dominate), over repeated eager calls for the tiled kernels (tens of
+    microseconds and more per call, so the device stays busy), with the K-split scratch preallocated."""
     codes, scales, alpha = nv.quantize(W, "4o6")
     n, k = W.shape
     # context: torch's dense bf16 product (hipBLASLt) on the dequantised weights, same shapes and timing
@@ -261,15 +264,30 @@ def w4a16_pass(torch, nv, dev, W):
     kernels = {1: "k_w4a16_gemv", 16: "k_w4a16_skinny", 64: "k_w4a16_skinny (4 tiles of X)",
                256: "k_w4a16_gemm 128x64 tiles + k_w4a16_reduce (K split)", 1024: "k_w4a16_gemm 128x128 tiles",
                4096: "k_w4a16_gemm 256x128 tiles"}
+    def eager_ms(call, reps):
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
     for m in (1, 16, 64, 256, 1024, 4096):
         X = (torch.randn((m, k), device=dev) * 0.5).to(torch.bfloat16)
         Y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        need = nv.matmul_workspace_bytes(m, k, n)
+        ws = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
         reps = 200 if m <= 64 else 20
-        ms = graph_ms(lambda: nv.matmul(X, codes, scales, alpha, out=Y), Y, reps)
+        timer = graph_ms if m <= 64 else (lambda call, Y, reps: eager_ms(call, reps))
+        ms = timer(lambda: nv.matmul(X, codes, scales, alpha, out=Y, workspace=ws), Y, reps)
         if ms is None:
             raise RuntimeError(f"W4A16 product, M={m}: a graph replay differs from the eager call")
         Yd = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
-        dense_ms = graph_ms(lambda: torch.matmul(X, WT, out=Yd), Yd, reps)
+        dense_ms = timer(lambda: torch.matmul(X, WT, out=Yd), Yd, reps)
         wbytes = n * k // 2 + n * k // 16
         moved = wbytes + m * k * 2 + m * n * 2
         flops = 2.0 * m * n * k

@@ -195,6 +195,25 @@ int nvfp4_error_stats(const void *W, int dtype, int64_t rows, int64_t cols, cons
 int nvfp4_matmul(const void *X, int64_t M, int64_t K, const uint8_t *codes, const uint8_t *scales,
                  const float *alpha, int64_t N, void *Y, int y_dtype, void *stream);
 
+/* nvfp4_matmul with caller-supplied scratch for the K split: `workspace` (device memory, 256-byte aligned,
+ * nullable) of `workspace_bytes` >= nvfp4_matmul_workspace_bytes(M, K, N) bytes. With a workspace nothing
+ * is allocated, so the call may be captured into a HIP graph as plain kernel nodes; the workspace must then
+ * stay allocated while the graph may run. NULL behaves as nvfp4_matmul. NVFP4_ERR_WORKSPACE if it is too
+ * small. Same arithmetic, layout and errors as nvfp4_matmul. */
+int nvfp4_matmul_ex(const void *X, int64_t M, int64_t K, const uint8_t *codes, const uint8_t *scales,
+                    const float *alpha, int64_t N, void *Y, int y_dtype, void *workspace, size_t workspace_bytes,
+                    void *stream);
+
+/* Scratch bytes nvfp4_matmul_ex needs for these shapes: slices * M * N * 4 when K is split, else 0 (also 0
+ * for shapes nvfp4_matmul rejects). */
+size_t nvfp4_matmul_workspace_bytes(int64_t M, int64_t K, int64_t N);
+
+/* The launch nvfp4_matmul takes for these shapes, for tests and tuning (no device work): plan_out[10] gets
+ * {kernel (0 GEMV, 1 skinny MFMA, 2 tiled MFMA), tile rows (tiled; the rows of X compiled for, skinny),
+ * tile columns, tiles along N, tiles, K slices, K per slice, work-groups, reduction work-groups, scratch
+ * bytes}. Returns NVFP4_ERR_INVALID_ARG for a null pointer, a dimension <= 0 or K % 16 != 0. */
+int nvfp4_matmul_plan(int64_t M, int64_t K, int64_t N, int64_t *plan_out);
+
 /* GPTQ with the FourOverSix block scales fixed first (FourOverSix write-up, section 03: every block's
  * scale and its M = 6 / M = 4 choice are settled before GPTQ's weight iterations, which then run inside
  * that frame; GPTQ as published by Frantar, Ashkboos, Hoefler and Alistarh, 2022).

@@ -60,6 +60,12 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_error_stats.restype = i32
         L.nvfp4_matmul.argtypes = [vp, i64, i64, vp, vp, vp, i64, vp, i32, vp]
         L.nvfp4_matmul.restype = i32
+        L.nvfp4_matmul_ex.argtypes = [vp, i64, i64, vp, vp, vp, i64, vp, i32, vp, ctypes.c_size_t, vp]
+        L.nvfp4_matmul_ex.restype = i32
+        L.nvfp4_matmul_workspace_bytes.argtypes = [i64, i64, i64]
+        L.nvfp4_matmul_workspace_bytes.restype = ctypes.c_size_t
+        L.nvfp4_matmul_plan.argtypes = [i64, i64, i64, vp]
+        L.nvfp4_matmul_plan.restype = i32
         L.nvfp4_quantize_ex.argtypes = [ctypes.POINTER(_Args)]
         L.nvfp4_quantize_ex.restype = i32
         L.nvfp4_quantize.argtypes = [vp, i64, i64, i32, i32, vp, vp, vp, vp]
@@ -115,6 +121,16 @@ def _check_buffer(t, name: str, nbytes: int, dev, dtype=None) -> None:
         raise NVFP4Error(f"{name} holds {t.numel() * t.element_size()} bytes, {nbytes} needed")
 
 
+def _scratch(nbytes: int, dev, stream) -> torch.Tensor:
+    """A uint8 scratch tensor for one call on `stream` (the current stream when None). Torch's allocator
+    may hand the memory out again once the tensor is dropped; recording the call's stream keeps it from
+    doing so before the work enqueued on that stream has run."""
+    t = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    if stream is not None:
+        t.record_stream(stream)
+    return t
+
+
 def _stream_ptr(stream, device) -> int:
     if stream is None:
         stream = torch.cuda.current_stream(device)
@@ -158,7 +174,7 @@ def quantize(W: torch.Tensor, mode: str, iters: int = 0, *, codes=None, scales=N
         _check_buffer(workspace, "workspace", 0, dev)
     need = workspace_bytes(rows, cols, mode) if cols % 16 == 0 and rows > 0 else 0
     if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        workspace = _scratch(need, dev, stream)
     a = _Args()
     a.W = W.data_ptr()
     a.dtype = DTYPES[W.dtype]
@@ -227,7 +243,7 @@ def gptq(W: torch.Tensor, H: torch.Tensor, percdamp: float = 0.01, *, codes=None
         _check_buffer(workspace, "workspace", 0, dev)
     need = gptq_workspace_bytes(rows, cols)
     if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        workspace = _scratch(need, dev, stream)
     with torch.cuda.device(dev):
         _check(lib().nvfp4_gptq(W.data_ptr(), DTYPES[W.dtype], rows, cols, H.data_ptr(), float(percdamp),
                                 codes.data_ptr(), scales.data_ptr(), alpha.data_ptr(),
@@ -287,11 +303,28 @@ def error_stats(W: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, alph
     return sse, hist
 
 
+def matmul_workspace_bytes(M: int, K: int, N: int) -> int:
+    return int(lib().nvfp4_matmul_workspace_bytes(M, K, N))
+
+
+PLAN_FIELDS = ("kind", "tm", "tn", "tiles_n", "tiles", "slices", "kslice", "grid", "reduce_grid", "part_bytes")
+
+
+def matmul_plan(M: int, K: int, N: int) -> dict:
+    """The launch nvfp4_matmul takes for these shapes (host only): kernel kind (0 GEMV, 1 skinny, 2 tiled),
+    tile shape, K split and grid sizes."""
+    out = (ctypes.c_int64 * len(PLAN_FIELDS))()
+    _check(lib().nvfp4_matmul_plan(M, K, N, ctypes.cast(out, ctypes.c_void_p)))
+    return dict(zip(PLAN_FIELDS, (int(v) for v in out)))
+
+
 def matmul(X: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, alpha: torch.Tensor,
-           out_dtype=torch.bfloat16, stream=None, out: torch.Tensor = None) -> torch.Tensor:
+           out_dtype=torch.bfloat16, stream=None, out: torch.Tensor = None, workspace=None) -> torch.Tensor:
     """W4A16 product Y = X @ What.T with NVFP4 weights (codes [N, K/2], scales [N, K/16], alpha [1] as
     quantize returns them for an [N, K] matrix) and bf16 activations X [M, K]; Y is [M, N] bf16 or fp32,
-    written into `out` when one is given (contiguous, on X's device, of that shape and out_dtype)."""
+    written into `out` when one is given (contiguous, on X's device, of that shape and out_dtype). The
+    K-split scratch (matmul_workspace_bytes) is a torch tensor: the caller's uint8 `workspace`, or one
+    allocated here, so the library itself never allocates (a graph capture records kernels only)."""
     if X.dim() != 2 or not X.is_cuda or not X.is_contiguous() or X.dtype != torch.bfloat16:
         raise NVFP4Error("X must be a contiguous 2-D bf16 CUDA tensor")
     M, K = X.shape
@@ -311,7 +344,15 @@ def matmul(X: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, alpha: to
                 or not out.is_contiguous()):
             raise NVFP4Error("out must be a contiguous [M, N] tensor of out_dtype on X's device")
         Y = out
+    need = matmul_workspace_bytes(M, K, N)
+    if workspace is not None:
+        _check_buffer(workspace, "workspace", need, dev)
+    elif need:
+        workspace = _scratch(need, dev, stream)
     with torch.cuda.device(dev):
-        _check(lib().nvfp4_matmul(X.data_ptr(), M, K, codes.data_ptr(), scales.data_ptr(), alpha.data_ptr(), N,
-                                  Y.data_ptr(), DTYPES[out_dtype], _stream_ptr(stream, dev)))
+        _check(lib().nvfp4_matmul_ex(X.data_ptr(), M, K, codes.data_ptr(), scales.data_ptr(), alpha.data_ptr(), N,
+                                     Y.data_ptr(), DTYPES[out_dtype],
+                                     workspace.data_ptr() if workspace is not None else None,
+                                     workspace.numel() * workspace.element_size() if workspace is not None else 0,
+                                     _stream_ptr(stream, dev)))
     return Y

@@ -212,8 +212,9 @@ NVFP4_API int nvfp4_error_stats(const void *W, int dtype, int64_t rows, int64_t 
     return ok ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 
-NVFP4_API int nvfp4_matmul(const void *X, int64_t M, int64_t K, const uint8_t *codes, const uint8_t *scales,
-                           const float *alpha, int64_t N, void *Y, int y_dtype, void *stream) {
+namespace {
+int matmul_check(const void *X, int64_t M, int64_t K, const uint8_t *codes, const uint8_t *scales, const float *alpha,
+                 int64_t N, void *Y, int y_dtype) {
     if (!X || !codes || !scales || !alpha || !Y || M <= 0 || K <= 0 || N <= 0) return NVFP4_ERR_INVALID_ARG;
     if (y_dtype != NVFP4_DTYPE_BF16 && y_dtype != NVFP4_DTYPE_F32) return NVFP4_ERR_INVALID_ARG;
     if (K % 16 != 0 || N > ((int64_t)1 << 25) || N > kMaxElems / K || M > kMaxElems / K || M > kMaxElems / N ||
@@ -222,10 +223,54 @@ NVFP4_API int nvfp4_matmul(const void *X, int64_t M, int64_t K, const uint8_t *c
     if (((uintptr_t)X & 15u) != 0 || ((uintptr_t)codes & 15u) != 0 || ((uintptr_t)Y & 15u) != 0 ||
         ((uintptr_t)alpha & 3u) != 0)
         return NVFP4_ERR_INVALID_ARG;
-    return nvfp4::launch_w4a16(static_cast<const uint16_t *>(X), M, K, codes, scales, alpha, N, Y,
-                               y_dtype == NVFP4_DTYPE_F32, static_cast<hipStream_t>(stream)) == hipSuccess
-               ? NVFP4_OK
-               : NVFP4_ERR_HIP;
+    return NVFP4_OK;
+}
+}  // namespace
+
+NVFP4_API size_t nvfp4_matmul_workspace_bytes(int64_t M, int64_t K, int64_t N) {
+    if (M <= 0 || K <= 0 || N <= 0 || K % 16 != 0 || N > ((int64_t)1 << 25) || N > kMaxElems / K ||
+        M > kMaxElems / K || M > kMaxElems / N || ((M + 255) / 256) * ((N + 127) / 128) >= ((int64_t)1 << 24))
+        return 0;
+    return nvfp4::plan_w4a16(M, K, N).part_bytes;
+}
+
+NVFP4_API int nvfp4_matmul_plan(int64_t M, int64_t K, int64_t N, int64_t *plan_out) {
+    if (!plan_out || M <= 0 || K <= 0 || N <= 0 || K % 16 != 0) return NVFP4_ERR_INVALID_ARG;
+    const nvfp4::W4a16Plan p = nvfp4::plan_w4a16(M, K, N);
+    const int64_t v[10] = {p.kind, p.tm, p.tn, p.tiles_n, p.tiles, p.slices, p.kslice, p.grid, p.reduce_grid,
+                           (int64_t)p.part_bytes};
+    for (int i = 0; i < 10; ++i) plan_out[i] = v[i];
+    return NVFP4_OK;
+}
+
+NVFP4_API int nvfp4_matmul_ex(const void *X, int64_t M, int64_t K, const uint8_t *codes, const uint8_t *scales,
+                              const float *alpha, int64_t N, void *Y, int y_dtype, void *workspace,
+                              size_t workspace_bytes, void *stream) {
+    const int c = matmul_check(X, M, K, codes, scales, alpha, N, Y, y_dtype);
+    if (c != NVFP4_OK) return c;
+    if (workspace && ((uintptr_t)workspace & 255u) != 0) return NVFP4_ERR_INVALID_ARG;
+    const size_t need = nvfp4::plan_w4a16(M, K, N).part_bytes;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const bool f32 = y_dtype == NVFP4_DTYPE_F32;
+    const uint16_t *x = static_cast<const uint16_t *>(X);
+    if (need == 0 || workspace) {
+        if (need > 0 && workspace_bytes < need) return NVFP4_ERR_WORKSPACE;
+        return nvfp4::launch_w4a16(x, M, K, codes, scales, alpha, N, Y, f32, static_cast<float *>(workspace), st) ==
+                       hipSuccess
+                   ? NVFP4_OK
+                   : NVFP4_ERR_HIP;
+    }
+    void *ws = nullptr;
+    if (hipMallocAsync(&ws, need, st) != hipSuccess) return NVFP4_ERR_HIP;
+    const bool ok =
+        nvfp4::launch_w4a16(x, M, K, codes, scales, alpha, N, Y, f32, static_cast<float *>(ws), st) == hipSuccess;
+    if (hipFreeAsync(ws, st) != hipSuccess) return NVFP4_ERR_HIP;
+    return ok ? NVFP4_OK : NVFP4_ERR_HIP;
+}
+
+NVFP4_API int nvfp4_matmul(const void *X, int64_t M, int64_t K, const uint8_t *codes, const uint8_t *scales,
+                           const float *alpha, int64_t N, void *Y, int y_dtype, void *stream) {
+    return nvfp4_matmul_ex(X, M, K, codes, scales, alpha, N, Y, y_dtype, nullptr, 0, stream);
 }
 
 namespace {

@@ -531,24 +531,66 @@ void split_k(int64_t tiles, int64_t M, int64_t N, int64_t K, int64_t &slices, in
     slices = (K + kslice - 1) / kslice;
 }
 
-hipError_t launch_w4a16(const uint16_t *X, int64_t M, int64_t K, const uint8_t *codes, const uint8_t *scales,
-                        const float *alpha, int64_t N, void *Y, bool out_f32, hipStream_t stream) {
+#ifndef NVFP4_NARROW_MAX_M
+#define NVFP4_NARROW_MAX_M 512
+#endif
+
+// The launch the product takes for these shapes (what launch_w4a16 runs): the kernel, the tile shape,
+// the K split and the grid. Tile shape by the rows of X (timed on 4096 x 4096 weights): 128 x 64 up to
+// 512 rows (four times the tiles of 256 x 128, so K is split into a quarter as many, longer slices:
+// 25-30 % faster at 65 <= M <= 256); above that 256 x 128 when those tiles alone give two work-groups
+// per CU, else 128 x 128 (three work-groups per CU and no split: 7 % faster at M = 1024, 16-17 % at 2048
+// and 3072; 256 x 128 is 20-25 % faster than 128 x 128 once it fills the GPU, M = 4096 and 8192).
+W4a16Plan plan_w4a16(int64_t M, int64_t K, int64_t N) {
+    W4a16Plan p = {};
     const int64_t chunks = (K + 2047) / 2048;  // 2048 k per chunk: 32 per lane
     if (M <= kGemvMaxM && gemv_lds_bytes(M, K) <= kGemvMaxLds && chunks <= 8) {
+        p.kind = kW4a16Gemv;
         const int64_t waves = (N + kGemvRows - 1) / kGemvRows;
-        const dim3 grid((unsigned)((waves + kGemvThreads / 64 - 1) / (kGemvThreads / 64)));
-        const size_t lds = gemv_lds_bytes(M, K);
+        p.grid = (waves + kGemvThreads / 64 - 1) / (kGemvThreads / 64);
+        p.chunks = chunks <= 2 ? 2 : chunks <= 4 ? 4 : 8;
+        p.lds = gemv_lds_bytes(M, K);
+        return p;
+    }
+    if (M <= kSkinnyMaxM) {
+        p.kind = kW4a16Skinny;
+        p.grid = (N + 15) / 16;
+        p.tm = 16 * (int)((M + 15) / 16);  // rows of X the kernel is compiled for
+        return p;
+    }
+    p.kind = kW4a16Gemm;
+    const bool narrow = M <= NVFP4_NARROW_MAX_M;
+    const bool tall = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN) >= 512;
+    p.tm = tall && !narrow ? kBM : 128;
+    p.tn = narrow ? 64 : kBN;
+    p.tiles_n = (N + p.tn - 1) / p.tn;
+    p.tiles = p.tiles_n * ((M + p.tm - 1) / p.tm);
+    split_k(p.tiles, M, N, K, p.slices, p.kslice);
+    p.grid = p.tiles * p.slices;
+    if (p.slices > 1) {
+        p.part_bytes = (size_t)(p.slices * M * N) * sizeof(float);
+        const int64_t n = M * N;
+        p.reduce_grid = std::min<int64_t>((n + kReduceThreads - 1) / kReduceThreads, 4096);
+    }
+    return p;
+}
+
+hipError_t launch_w4a16(const uint16_t *X, int64_t M, int64_t K, const uint8_t *codes, const uint8_t *scales,
+                        const float *alpha, int64_t N, void *Y, bool out_f32, float *part, hipStream_t stream) {
+    const W4a16Plan p = plan_w4a16(M, K, N);
+    if (p.kind == kW4a16Gemv) {
+        const dim3 grid((unsigned)p.grid);
         const int m = (int)M;
         static_assert(kGemvMaxM <= 4, "the GEMV is compiled for 1 to 4 rows of X");
         switch (M) {
-            case 1: return gemv_dispatch<1>(chunks, out_f32, grid, lds, stream, X, m, K, codes, scales, alpha, N, Y);
-            case 2: return gemv_dispatch<2>(chunks, out_f32, grid, lds, stream, X, m, K, codes, scales, alpha, N, Y);
-            case 3: return gemv_dispatch<3>(chunks, out_f32, grid, lds, stream, X, m, K, codes, scales, alpha, N, Y);
-            default: return gemv_dispatch<4>(chunks, out_f32, grid, lds, stream, X, m, K, codes, scales, alpha, N, Y);
+            case 1: return gemv_dispatch<1>(p.chunks, out_f32, grid, p.lds, stream, X, m, K, codes, scales, alpha, N, Y);
+            case 2: return gemv_dispatch<2>(p.chunks, out_f32, grid, p.lds, stream, X, m, K, codes, scales, alpha, N, Y);
+            case 3: return gemv_dispatch<3>(p.chunks, out_f32, grid, p.lds, stream, X, m, K, codes, scales, alpha, N, Y);
+            default: return gemv_dispatch<4>(p.chunks, out_f32, grid, p.lds, stream, X, m, K, codes, scales, alpha, N, Y);
         }
     }
-    if (M <= kSkinnyMaxM) {
-        const dim3 grid((unsigned)((N + 15) / 16)), block(kSkinnyThreads);
+    if (p.kind == kW4a16Skinny) {
+        const dim3 grid((unsigned)p.grid), block(kSkinnyThreads);
         const int m = (int)M;
 #define NVFP4_SKINNY(MT)                                                                                          \
     do {                                                                                                          \
@@ -559,7 +601,7 @@ hipError_t launch_w4a16(const uint16_t *X, int64_t M, int64_t K, const uint8_t *
             hipLaunchKernelGGL((k_w4a16_skinny<MT, false>), grid, block, 0, stream, X, m, K, codes, scales, alpha,   \
                                N, Y);                                                                             \
     } while (0)
-        switch ((M + 15) / 16) {
+        switch (p.tm / 16) {
             case 1: NVFP4_SKINNY(1); break;
             case 2: NVFP4_SKINNY(2); break;
             case 3: NVFP4_SKINNY(3); break;
@@ -568,59 +610,36 @@ hipError_t launch_w4a16(const uint16_t *X, int64_t M, int64_t K, const uint8_t *
 #undef NVFP4_SKINNY
         return hipGetLastError();
     }
-#ifndef NVFP4_NARROW_MAX_M
-#define NVFP4_NARROW_MAX_M 512
-#endif
-    // Tile shape by the rows of X (timed on 4096 x 4096 weights): 128 x 64 up to 512 rows (four times the
-    // tiles of 256 x 128, so K is split into a quarter as many, longer slices: 25-30 % faster at
-    // 65 <= M <= 256); above that 256 x 128 when those tiles alone give two work-groups per CU, else
-    // 128 x 128 (three work-groups per CU and no split: 7 % faster at M = 1024, 16-17 % at 2048 and
-    // 3072; 256 x 128 is 20-25 % faster than 128 x 128 once it fills the GPU, M = 4096 and 8192).
-    const bool narrow = M <= NVFP4_NARROW_MAX_M;
-    const bool tall = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN) >= 512;
-    const int tm = tall && !narrow ? kBM : 128;
-    const int tn = narrow ? 64 : kBN;
-    const int64_t tiles_n = (N + tn - 1) / tn, tiles_m = (M + tm - 1) / tm, tiles = tiles_n * tiles_m;
-    int64_t slices = 1, kslice = K;
-    split_k(tiles, M, N, K, slices, kslice);
-    float *part = nullptr;
-    if (slices > 1) {
-        if (hipMallocAsync(reinterpret_cast<void **>(&part), (size_t)(slices * M * N) * sizeof(float), stream) !=
-            hipSuccess)
-            return hipErrorOutOfMemory;
-    }
-    const dim3 grid((unsigned)(tiles * slices)), block(kGemmThreads);
+    if (p.slices > 1 && !part) return hipErrorInvalidValue;
+    float *const pp = p.slices > 1 ? part : nullptr;
+    const dim3 grid((unsigned)p.grid), block(kGemmThreads);
 #define NVFP4_GEMM(TM, TN)                                                                                    \
     do {                                                                                                      \
         if (out_f32)                                                                                          \
             hipLaunchKernelGGL((k_w4a16_gemm<TM, TN, true>), grid, block, 0, stream, X, M, K, codes, scales, alpha, \
-                               N, Y, (unsigned)tiles_n, (unsigned)tiles, kslice, part);                         \
+                               N, Y, (unsigned)p.tiles_n, (unsigned)p.tiles, p.kslice, pp);                     \
         else                                                                                                  \
             hipLaunchKernelGGL((k_w4a16_gemm<TM, TN, false>), grid, block, 0, stream, X, M, K, codes, scales,      \
-                               alpha, N, Y, (unsigned)tiles_n, (unsigned)tiles, kslice, part);                  \
+                               alpha, N, Y, (unsigned)p.tiles_n, (unsigned)p.tiles, p.kslice, pp);              \
     } while (0)
-    if (tn == 64)
+    if (p.tn == 64)
         NVFP4_GEMM(128, 64);
-    else if (tm == 128)
+    else if (p.tm == 128)
         NVFP4_GEMM(128, 128);
     else
         NVFP4_GEMM(256, 128);
 #undef NVFP4_GEMM
     hipError_t err = hipGetLastError();
-    if (slices > 1) {
-        if (err == hipSuccess) {
-            const int64_t n = M * N;
-            const dim3 rgrid((unsigned)std::min<int64_t>((n + kReduceThreads - 1) / kReduceThreads, 4096));
-            if (out_f32)
-                hipLaunchKernelGGL(k_w4a16_reduce<true>, rgrid, dim3(kReduceThreads), 0, stream, part, (int)slices,
-                                   n, alpha, Y);
-            else
-                hipLaunchKernelGGL(k_w4a16_reduce<false>, rgrid, dim3(kReduceThreads), 0, stream, part,
-                                   (int)slices, n, alpha, Y);
-            err = hipGetLastError();
-        }
-        const hipError_t ferr = hipFreeAsync(part, stream);
-        if (err == hipSuccess) err = ferr;
+    if (err == hipSuccess && p.slices > 1) {
+        const int64_t n = M * N;
+        const dim3 rgrid((unsigned)p.reduce_grid);
+        if (out_f32)
+            hipLaunchKernelGGL(k_w4a16_reduce<true>, rgrid, dim3(kReduceThreads), 0, stream, pp, (int)p.slices, n,
+                               alpha, Y);
+        else
+            hipLaunchKernelGGL(k_w4a16_reduce<false>, rgrid, dim3(kReduceThreads), 0, stream, pp, (int)p.slices, n,
+                               alpha, Y);
+        err = hipGetLastError();
     }
     return err;
 }

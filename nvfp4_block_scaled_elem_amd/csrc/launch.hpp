@@ -73,8 +73,20 @@ hipError_t launch_soar(const void *W, bool f32, int64_t nblk, const float *alpha
                        const uint16_t *brackets, bool full_search, int num0, int den, int count, int rule,
                        hipStream_t stream);
 hipError_t launch_encode_e2m1(const float *x, int64_t n, uint8_t *codes, hipStream_t stream);
+// The W4A16 product's launch for given shapes: which kernel, its tile shape, the K split and the grid.
+enum { kW4a16Gemv = 0, kW4a16Skinny = 1, kW4a16Gemm = 2 };
+struct W4a16Plan {
+    int kind;             // kW4a16*
+    int tm, tn;           // output tile (gemm); tm = rows of X compiled for (skinny)
+    int64_t tiles_n, tiles, slices, kslice, grid, reduce_grid;
+    int64_t chunks;       // gemv: 2048-k chunks compiled for
+    size_t lds;           // gemv: dynamic LDS bytes
+    size_t part_bytes;    // fp32 partial sums of the K slices (0 without a split)
+};
+W4a16Plan plan_w4a16(int64_t M, int64_t K, int64_t N);
+// `part` holds plan.part_bytes (256-byte aligned) when the plan splits K; otherwise it is unused.
 hipError_t launch_w4a16(const uint16_t *X, int64_t M, int64_t K, const uint8_t *codes, const uint8_t *scales,
-                        const float *alpha, int64_t N, void *Y, bool out_f32, hipStream_t stream);
+                        const float *alpha, int64_t N, void *Y, bool out_f32, float *part, hipStream_t stream);
 size_t stats_workspace_bytes();
 hipError_t launch_stats(const void *W, bool f32, int64_t nblk, const uint8_t *codes, const uint8_t *scales,
                         const float *alpha, double *sse_out, unsigned long long *hist_out, void *workspace,

@@ -127,6 +127,22 @@ def test_matmul_rejects(L):
     assert f(FAKE, 1, 32, FAKE, FAKE, FAKE, 8, FAKE + 8, 0, None) == INVALID
 
 
+def test_matmul_ex_rejects(L):
+    f = L.nvfp4_matmul_ex
+    assert f(None, 1, 32, FAKE, FAKE, FAKE, 8, FAKE, 0, None, 0, None) == INVALID
+    assert f(FAKE, 1, 24, FAKE, FAKE, FAKE, 8, FAKE, 0, None, 0, None) == SHAPE
+    # K split at 1024 x 1024 x 256: too small a workspace, a misaligned one
+    need = L.nvfp4_matmul_workspace_bytes(1024, 1024, 256)
+    assert need > 0
+    assert f(FAKE, 1024, 1024, FAKE, FAKE, FAKE, 256, FAKE, 0, FAKE, need - 1, None) == WORKSPACE
+    assert f(FAKE, 1024, 1024, FAKE, FAKE, FAKE, 256, FAKE, 0, FAKE + 16, need, None) == INVALID
+    plan = (ctypes.c_int64 * 10)()
+    assert L.nvfp4_matmul_plan(1024, 1024, 256, None) == INVALID
+    assert L.nvfp4_matmul_plan(1024, 1000, 256, ctypes.cast(plan, ctypes.c_void_p)) == INVALID
+    assert L.nvfp4_matmul_plan(1024, 1024, 256, ctypes.cast(plan, ctypes.c_void_p)) == OK
+    assert plan[9] == need
+
+
 def test_sizes_and_counts(L):
     assert L.nvfp4_workspace_bytes(4096, 4096, 0) > 0
     assert L.nvfp4_workspace_bytes(4096, 4096, 3) >= L.nvfp4_workspace_bytes(4096, 4096, 2) + 2 * 4096 * 256

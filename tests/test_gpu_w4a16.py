@@ -148,9 +148,9 @@ def test_w4a16_graph_replays_match_eager():
 
 
 @pytest.mark.skip(reason="this capture (128 x 128 tiles with and without K split, 256 x 128 tiles) ended "
-                         "in a GPU memory fault once; a host emulation of every kernel address for these "
-                         "shapes finds none out of bounds, and no cause has been shown, so it stays off "
-                         "the GPU until one is")
+                         "in a GPU memory fault once; the host emulation of every kernel address for these "
+                         "shapes (tests/test_w4a16_launch_emulation.py) finds none out of bounds, and no "
+                         "cause has been shown, so it stays off the GPU until one is")
 def test_w4a16_graph_replays_match_eager_large_tiles():
     graph_replays_match_eager([(1, 1024), (1024, 1024), (2100, 128), (65536, 128)])
 
