@@ -226,6 +226,27 @@ def test_plain_entry_point_matches_ex():
         assert np.array_equal(codes.cpu().numpy(), r["codes"]) and np.array_equal(scales.cpu().numpy(), r["scales"])
 
 
+def test_f32_entry_point_matches_oracle():
+    """nvfp4_quantize_f32 (the plain binary32 entry point) with valid arguments, every mode, against the
+    oracle bit for bit."""
+    W = synth.normal_f32(48, 1040, seed=14)
+    W[3, 5] *= 40.0  # an outlier sets alpha
+    Wd = to_dev(W)
+    L = nv.lib()
+    for mode, name in enumerate(["max", "4o6", "cjso", "soar"]):
+        codes = torch.empty((48, 520), dtype=torch.uint8, device="cuda")
+        scales = torch.empty((48, 65), dtype=torch.uint8, device="cuda")
+        alpha = torch.empty(1, dtype=torch.float32, device="cuda")
+        say(f"plain nvfp4_quantize_f32 mode={mode}")
+        st = L.nvfp4_quantize_f32(Wd.data_ptr(), 48, 1040, mode, 3, codes.data_ptr(), scales.data_ptr(),
+                                  alpha.data_ptr(), torch.cuda.current_stream().cuda_stream)
+        assert st == 0
+        torch.cuda.synchronize()
+        r = oracle.quantize(W, name, 3)
+        assert np.array_equal(codes.cpu().numpy(), r["codes"]) and np.array_equal(scales.cpu().numpy(), r["scales"])
+        assert f32_bits(float(alpha.cpu()[0])) == f32_bits(r["alpha"])
+
+
 def test_graph_capture_replays_match_eager():
     W = synth.c2(1, rows=256, cols=1024)
     Wd = to_dev(W)
@@ -298,6 +319,31 @@ def test_encode_e2m1_matches_oracle():
     say(f"encode_e2m1 n={x.size}")
     got = nv.encode_e2m1(torch.from_numpy(x).cuda()).cpu().numpy()
     assert np.array_equal(got, oracle.e2m1_codes(x))
+
+
+def test_encode_e2m1_exhaustive():
+    """Every binary32 bit pattern (2^32, in 16 chunks) through nvfp4_encode_e2m1, against a threshold
+    encoder written with torch's own elementwise operations: magnitude index = number of thresholds
+    passed (0.25 <, 0.75 <=, 1.25 <, 1.75 <=, 2.5 <, 3.5 <=, 5 <: nearest value, ties to the even code,
+    saturating at 6; NaN passes none), sign bit only on nonzero codes."""
+    chunk = 1 << 28
+    for c in range(16):
+        lo = c * chunk
+        say(f"encode_e2m1 exhaustive chunk {c}/16")
+        bits = torch.arange(lo, lo + chunk, dtype=torch.int64, device="cuda")
+        bits = torch.where(bits >= 1 << 31, bits - (1 << 32), bits).to(torch.int32)
+        x = bits.view(torch.float32)
+        got = nv.encode_e2m1(x)
+        a = x.abs()
+        idx = (a > 0.25).to(torch.uint8)
+        for t, strict in ((0.75, False), (1.25, True), (1.75, False), (2.5, True), (3.5, False), (5.0, True)):
+            idx += (a > t) if strict else (a >= t)
+        neg = torch.signbit(x) & (idx > 0)
+        want = idx | (neg.to(torch.uint8) << 3)
+        bad = torch.nonzero(got != want)
+        assert bad.numel() == 0, f"chunk {c}: {bad.numel()} mismatches, first bits {int(bits[bad[0, 0]]) & 0xFFFFFFFF:#x}"
+        del bits, x, got, a, idx, neg, want
+    torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("mode", ["4o6", "soar"])
