@@ -79,7 +79,9 @@ enum nvfp4_error {
                                    iters outside [0, 1000] */
     NVFP4_ERR_SHAPE = -2,       /* cols % 16 != 0, or more than 2^35 elements */
     NVFP4_ERR_WORKSPACE = -3,   /* caller workspace smaller than nvfp4_workspace_bytes() */
-    NVFP4_ERR_HIP = -4          /* a HIP call failed */
+    NVFP4_ERR_HIP = -4,         /* a HIP call failed */
+    NVFP4_ERR_TOO_LARGE = -5    /* nvfp4_quantize_noalloc: the call needs more scratch than its fixed
+                                   device array holds */
 };
 
 /* In-band status bits, written to nvfp4_stats_t.status by the device. */
@@ -145,6 +147,25 @@ typedef struct nvfp4_args {
 #define NVFP4_FLAG_INIT_4O6 2u
 
 int nvfp4_quantize_ex(const nvfp4_args_t *args);
+
+/* nvfp4_quantize_ex for callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation. It allocates nothing (no hipMalloc, hipMallocAsync or
+ * hipFree, neither here nor in any library it calls): its scratch is a fixed device array inside the
+ * library, of nvfp4_noalloc_scratch_bytes() = 16 MiB, that every GPU the library runs on holds until the
+ * process ends. The array of the current device is used, so the current device must be the stream's.
+ * Same arguments, outputs and errors as nvfp4_quantize_ex, except:
+ *   - args->workspace must be NULL and args->workspace_bytes 0 (else NVFP4_ERR_INVALID_ARG);
+ *   - NVFP4_ERR_TOO_LARGE when nvfp4_workspace_bytes(rows, cols, mode) exceeds the array: MAX,
+ *     FourOverSix and CJSO need 35 KB whatever the size; SOAR needs 2 more bytes per 16-element block,
+ *     which caps it at about 134 million elements;
+ *   - the first call on a device looks up that device's address of the array (NVFP4_ERR_HIP if that
+ *     fails).
+ * All calls on one GPU share its array: two calls that may overlap on one GPU (other streams, other
+ * threads) race and must be ordered by the caller. Nothing in the array needs clearing between calls. */
+int nvfp4_quantize_noalloc(const nvfp4_args_t *args);
+
+/* Size in bytes of the fixed device array nvfp4_quantize_noalloc uses. */
+size_t nvfp4_noalloc_scratch_bytes(void);
 
 /* Number of kernels one call of this mode enqueues (MAX and FourOverSix: 2; CJSO: iters + 2; SOAR:
  * iters + 3; the last SOAR kernel is the decoupled search), or -1 for an unknown mode or bad iters. */

@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libnvfp4.so")
-SOURCES = ["quant_kernels.hip", "soar_kernel.hip", "gemm_kernels.hip", "gptq_kernels.hip", "api.cpp"]
+SOURCES = ["quant_kernels.hip", "soar_kernel.hip", "gemm_kernels.hip", "gptq_kernels.hip", "api.cpp", "noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

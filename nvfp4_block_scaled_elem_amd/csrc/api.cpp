@@ -23,6 +23,10 @@ constexpr int kMaxIters = 1000;
 // 8 values then stay below 2^32 threads per grid.
 constexpr int64_t kMaxElems = (int64_t)1 << 35;
 
+}  // namespace
+
+namespace nvfp4 {
+
 int kernel_count(int mode, int iters) {
     if (iters < 0 || iters > kMaxIters) return -1;
     switch (mode) {
@@ -34,7 +38,7 @@ int kernel_count(int mode, int iters) {
     }
 }
 
-int check(const nvfp4_args_t *a) {
+int check_args(const nvfp4_args_t *a) {
     if (!a || !a->W || !a->codes_out || !a->scales_out || !a->alpha_out) return NVFP4_ERR_INVALID_ARG;
     if (a->rows <= 0 || a->cols <= 0) return NVFP4_ERR_INVALID_ARG;
     if (a->mode < NVFP4_MODE_MAX || a->mode > NVFP4_MODE_SOAR) return NVFP4_ERR_INVALID_ARG;
@@ -70,8 +74,7 @@ bool mark(const nvfp4_args_t *a, int j) {
            hipSuccess;
 }
 
-int run(const nvfp4_args_t *a, void *ws_base) {
-    using namespace nvfp4;
+int run_quantize(const nvfp4_args_t *a, void *ws_base) {
     hipStream_t st = static_cast<hipStream_t>(a->stream);
     const bool f32 = a->dtype == NVFP4_DTYPE_F32;
     const int64_t n = a->rows * a->cols, nblk = n / 16;
@@ -113,9 +116,9 @@ int run(const nvfp4_args_t *a, void *ws_base) {
     return NVFP4_OK;
 }
 
-}  // namespace
+}  // namespace nvfp4
 
-NVFP4_API int nvfp4_kernel_count(int mode, int iters) { return kernel_count(mode, iters); }
+NVFP4_API int nvfp4_kernel_count(int mode, int iters) { return nvfp4::kernel_count(mode, iters); }
 
 NVFP4_API size_t nvfp4_workspace_bytes(int64_t rows, int64_t cols, int mode) {
     if (rows <= 0 || cols <= 0 || cols % 16 != 0 || rows > kMaxElems / cols) return 0;
@@ -124,17 +127,17 @@ NVFP4_API size_t nvfp4_workspace_bytes(int64_t rows, int64_t cols, int mode) {
 }
 
 NVFP4_API int nvfp4_quantize_ex(const nvfp4_args_t *a) {
-    const int c = check(a);
+    const int c = nvfp4::check_args(a);
     if (c != NVFP4_OK) return c;
     const size_t need = nvfp4::workspace_bytes(a->rows * a->cols / 16, a->mode);
     if (a->workspace) {
         if (a->workspace_bytes < need) return NVFP4_ERR_WORKSPACE;
-        return run(a, a->workspace);
+        return nvfp4::run_quantize(a, a->workspace);
     }
     hipStream_t st = static_cast<hipStream_t>(a->stream);
     void *ws = nullptr;
     if (hipMallocAsync(&ws, need, st) != hipSuccess) return NVFP4_ERR_HIP;
-    const int r = run(a, ws);
+    const int r = nvfp4::run_quantize(a, ws);
     if (hipFreeAsync(ws, st) != hipSuccess) return NVFP4_ERR_HIP;
     return r;
 }
@@ -323,6 +326,7 @@ NVFP4_API const char *nvfp4_status_string(int status) {
         case NVFP4_ERR_SHAPE: return "unsupported shape (a dimension that must be a multiple of 16 is not, or a size limit is exceeded)";
         case NVFP4_ERR_WORKSPACE: return "workspace too small";
         case NVFP4_ERR_HIP: return "HIP launch or allocation failed";
+        case NVFP4_ERR_TOO_LARGE: return "the call needs more scratch than the library's fixed device array holds";
         default: return "unknown status";
     }
 }

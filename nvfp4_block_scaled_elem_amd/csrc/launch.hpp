@@ -34,6 +34,10 @@ namespace nvfp4 {
 #ifndef NVFP4_CJSO_DEPTH
 #define NVFP4_CJSO_DEPTH 1
 #endif
+// Size of the fixed device array behind nvfp4_quantize_noalloc (16 MiB).
+#ifndef NVFP4_NOALLOC_SCRATCH_BYTES
+#define NVFP4_NOALLOC_SCRATCH_BYTES (16u << 20)
+#endif
 constexpr int kAmaxThreads = 256;
 constexpr int kAmaxMaxGroups = 512;
 constexpr int kQuantThreads = NVFP4_QUANT_THREADS;
@@ -57,6 +61,12 @@ struct Workspace {
     uint32_t *m4_part;    // [kQuantGroups] FourOverSix M=4 counts per work-group (same offset)
 };
 size_t workspace_bytes(int64_t nblk, int mode);
+
+// The quantiser's host side (api.cpp): argument checks (NVFP4_OK or an nvfp4_error) and the kernel
+// sequence of a mode, enqueued on a->stream with `ws` as scratch (workspace_bytes of it).
+int kernel_count(int mode, int iters);
+int check_args(const nvfp4_args_t *a);
+int run_quantize(const nvfp4_args_t *a, void *ws);
 Workspace carve(void *base, int64_t nblk);
 
 hipError_t launch_amax(const void *W, bool f32, int64_t n, uint32_t *amax_part, int groups, nvfp4_stats_t *stats,
