@@ -363,12 +363,14 @@ def c5_pass(torch, nv, dev, streams):
         run(mode, iters)
         torch.cuda.synchronize()
         dt = time.perf_counter() - t0
-        out["modes"][mode] = {"total_ms": round(dt * 1e3, 3), "GBps": round(total_bytes / dt / 1e9, 2)}
+        out["modes"][mode] = {"total_ms": round(dt * 1e3, 3), "GBps": round(total_bytes / dt / 1e9, 2),
+                              "frac_hbm_peak": round(total_bytes / dt / PEAK_HBM, 4)}
         t0 = time.perf_counter()
         run(mode, iters, square)
         torch.cuda.synchronize()
         dq = time.perf_counter() - t0
-        out["square_4096"]["modes"][mode] = {"total_ms": round(dq * 1e3, 3), "GBps": round(sq_bytes / dq / 1e9, 2)}
+        out["square_4096"]["modes"][mode] = {"total_ms": round(dq * 1e3, 3), "GBps": round(sq_bytes / dq / 1e9, 2),
+                                             "frac_hbm_peak": round(sq_bytes / dq / PEAK_HBM, 4)}
         log(f"c5 {mode}: {dt * 1e3:.1f} ms; square matrices {dq * 1e3:.1f} ms")
     del mats
     torch.cuda.empty_cache()
@@ -483,20 +485,24 @@ def round_anatomy(torch, nv, dev, nk_cjso) -> dict:
             "method": "two heights, 4096 columns, GPU-drawn Student-t(5) weights; rounds 1..7 span / 7"}
 
 
-def cold_warm_pass(torch, nv, W, outs) -> dict:
-    """One call per mode on the first matrix, timed with HIP events around the call: "cold" after a 1 GiB
-    fill has evicted the Infinity Cache and the L2s (outside the timed region), "warm" for the same call
-    repeated at once. Median of 10 of each."""
+def cold_warm_pass(torch, nv, W, outs, reps=25) -> dict:
+    """One call per mode on the first matrix, timed with HIP events around the call: "cold" after a
+    read-only pass over 1 GiB has evicted the Infinity Cache and the L2s (outside the timed region; a
+    read leaves no dirty lines behind whose write-back would land in the timed call), "warm" for the
+    same call repeated at once. Median of `reps` of each."""
     dev = W.device
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    flush = torch.ones((1 << 30) // 4, dtype=torch.float32, device=dev)
+    sink = torch.empty(1, dtype=torch.float32, device=dev)
+    torch.amax(flush, dim=0, out=sink)  # the fill's dirty lines leave before the first timed call
+    torch.cuda.synchronize()
     res = {}
     for mode, iters in MODES:
         o = outs[mode]
         call = lambda: nv.quantize(W, mode, iters, codes=o["codes"], scales=o["scales"],  # noqa: E731
                                    alpha=o["alpha"], mchoice=o["mchoice"], workspace=o["workspace"])
         cold, warm = [], []
-        for r in range(10):
-            flush.fill_(r)
+        for r in range(reps):
+            torch.amax(flush, dim=0, out=sink)
             torch.cuda.synchronize()
             ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
             ev[0].record()
@@ -511,9 +517,51 @@ def cold_warm_pass(torch, nv, W, outs) -> dict:
         c, w = float(np.median(cold)), float(np.median(warm))
         res[mode] = {"cold_ms": round(c, 5), "warm_ms": round(w, 5),
                      "cold_GBps": round(W.numel() * 2 / (c * 1e-3) / 1e9, 1),
-                     "warm_GBps": round(W.numel() * 2 / (w * 1e-3) / 1e9, 1)}
+                     "warm_GBps": round(W.numel() * 2 / (w * 1e-3) / 1e9, 1),
+                     "cold_frac_hbm_peak": round(W.numel() * 2 / (c * 1e-3) / PEAK_HBM, 4),
+                     "warm_frac_hbm_peak": round(W.numel() * 2 / (w * 1e-3) / PEAK_HBM, 4)}
+    res["method"] = (f"HIP events around one call, median of {reps}; cold = after a read-only pass over 1 GiB, "
+                     "warm = the same call repeated at once")
     del flush
     torch.cuda.empty_cache()
+    return res
+
+
+def graph_mode_pass(torch, nv, mats, outs, reps=24) -> dict:
+    """Per-mode device time without host overhead: `reps` calls of one mode, on the resident matrices in
+    turn (each visited twice, so most calls find their matrix in no cache), captured in one HIP graph;
+    HIP events around a replay. A replay must reproduce the eager outputs of its last call."""
+    res = {}
+    for mode, iters in MODES:
+        o = outs[mode]
+
+        def call(W):
+            nv.quantize(W, mode, iters, codes=o["codes"], scales=o["scales"], alpha=o["alpha"],
+                        mchoice=o["mchoice"], workspace=o["workspace"])
+        last = mats[(reps - 1) % len(mats)]
+        call(last)
+        torch.cuda.synchronize()
+        want = (o["codes"].clone(), o["scales"].clone(), o["alpha"].clone())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for r in range(reps):
+                call(mats[r % len(mats)])
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        if not (torch.equal(o["codes"], want[0]) and torch.equal(o["scales"], want[1]) and
+                torch.equal(o["alpha"], want[2])):
+            raise RuntimeError(f"{mode}: a graph replay differs from the eager call")
+        ms = e0.elapsed_time(e1) / reps
+        gbps = ROWS * COLS * 2 / (ms * 1e-3) / 1e9
+        res[mode] = {"ms": round(ms, 5), "GBps": round(gbps, 1), "frac_hbm_peak": round(gbps * 1e9 / PEAK_HBM, 4)}
+        del g
+    res["method"] = (f"{reps} calls per mode on the {len(mats)} resident matrices in turn, one HIP graph, "
+                     "events around a replay")
     return res
 
 
@@ -540,25 +588,33 @@ def fp32_pass(torch, nv, W) -> dict:
 
 
 def hbm_attainable(torch, dev) -> dict:
-    """A plain 1 GiB device copy (torch's copy kernel), median of 10: read + write bytes per second."""
+    """What a plain streaming kernel reaches on this box: a 1 GiB device copy (torch's copy kernel;
+    read + write bytes per second) and a read-only pass over 1 GiB (torch's max reduction; bytes read per
+    second). Median of 10 each."""
     n = (1 << 30) // 4
     src = torch.ones(n, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
-    for _ in range(3):
-        dst.copy_(src)
-    ts = []
-    for _ in range(10):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        dst.copy_(src)
-        e1.record()
-        torch.cuda.synchronize()
-        ts.append(e0.elapsed_time(e1) * 1e-3)
-    t = sorted(ts)[len(ts) // 2]
+    sink = torch.empty(1, dtype=torch.float32, device=dev)
+
+    def med(fn):
+        for _ in range(3):
+            fn()
+        ts = []
+        for _ in range(10):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        return sorted(ts)[len(ts) // 2]
+    t_copy = med(lambda: dst.copy_(src))
+    t_read = med(lambda: torch.amax(src, dim=0, out=sink))
     del src, dst
     torch.cuda.empty_cache()
-    return {"copy_GBps": round(2 * n * 4 / t / 1e9, 1), "frac_of_peak": round(2 * n * 4 / t / PEAK_HBM, 4),
-            "kind": "1 GiB device copy, read + write bytes, median of 10"}
+    return {"copy_GBps": round(2 * n * 4 / t_copy / 1e9, 1), "frac_of_peak": round(2 * n * 4 / t_copy / PEAK_HBM, 4),
+            "read_GBps": round(n * 4 / t_read / 1e9, 1), "read_frac_of_peak": round(n * 4 / t_read / PEAK_HBM, 4),
+            "kind": "1 GiB device copy (read + write bytes) and 1 GiB read-only max reduction, median of 10"}
 
 
 def main():
@@ -754,6 +810,11 @@ def main():
                 "avg_launch_ms": round(t_round * 1e3, 5), "launches_per_step": 2 * (ITERS - 1)}
 
     cold_warm = cold_warm_pass(torch, nv, mats[0], outs[0])
+    graph_modes = graph_mode_pass(torch, nv, mats, outs[0])
+    for mode, _ in MODES:
+        per_mode[mode]["graph_ms"] = graph_modes[mode]["ms"]
+        per_mode[mode]["graph_GBps"] = graph_modes[mode]["GBps"]
+        per_mode[mode]["graph_frac_hbm_peak"] = graph_modes[mode]["frac_hbm_peak"]
     fp32 = fp32_pass(torch, nv, mats[0])
     w4a16 = w4a16_pass(torch, nv, dev, mats[0])
     gptq = gptq_pass(torch, nv, dev, mats[0])
@@ -763,6 +824,7 @@ def main():
     attainable = hbm_attainable(torch, dev)
     # the same rate against what a plain copy reaches on this machine (context for the fraction of peak)
     roofline["frac_of_attainable"] = round(round_gbps / attainable["copy_GBps"], 4)
+    roofline["frac_of_read_attainable"] = round(round_gbps / attainable["read_GBps"], 4)
     if anatomy is not None:
         anatomy["marginal_frac_of_attainable"] = round(anatomy["marginal_GBps"] / attainable["copy_GBps"], 4)
         roofline["anatomy"] = anatomy
@@ -793,6 +855,7 @@ def main():
         "step_roofline": step_roofline,
     }
     line["cold_warm"] = cold_warm
+    line["graph_modes"] = graph_modes
     line["fp32_input"] = fp32
     line["w4a16"] = w4a16
     line["gptq"] = gptq

@@ -79,10 +79,11 @@ int run_quantize(const nvfp4_args_t *a, void *ws_base) {
     const bool f32 = a->dtype == NVFP4_DTYPE_F32;
     const int64_t n = a->rows * a->cols, nblk = n / 16;
     const Workspace ws = carve(ws_base, nblk);
-    const int ga = amax_groups(n * (f32 ? 4 : 2) / 16);
+    const bool cjso = a->mode == NVFP4_MODE_CJSO || a->mode == NVFP4_MODE_SOAR;
+    int ga = 0;
     int j = 0;
     if (!mark(a, j++)) return NVFP4_ERR_HIP;
-    if (launch_amax(a->W, f32, n, ws.amax_part, ga, a->stats_out, st) != hipSuccess || !mark(a, j++))
+    if (launch_amax(a->W, f32, nblk, cjso, ws.amax_part, ga, a->stats_out, st) != hipSuccess || !mark(a, j++))
         return NVFP4_ERR_HIP;
     if (a->mode == NVFP4_MODE_MAX || a->mode == NVFP4_MODE_FOUR_OVER_SIX) {
         const bool fos = a->mode == NVFP4_MODE_FOUR_OVER_SIX;

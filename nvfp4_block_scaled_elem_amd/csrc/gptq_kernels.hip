@@ -557,8 +557,8 @@ hipError_t launch_gptq(const void *W, bool f32, int64_t R, int64_t K, const doub
 
     // the FourOverSix frame: scales and alpha (and codes, overwritten below)
     const int64_t n = R * K;
-    const int ga = amax_groups(n * (f32 ? 4 : 2) / 16);
-    hipError_t err = launch_amax(W, f32, n, q.amax_part, ga, nullptr, stream);
+    int ga = 0;
+    hipError_t err = launch_amax(W, f32, nblk, false, q.amax_part, ga, nullptr, stream);
     if (err == hipSuccess)
         err = launch_quant(W, f32, true, nblk, q.amax_part, ga, codes, scales, alpha, nullptr, nullptr, q.m4_part,
                            stream);

@@ -38,23 +38,22 @@ namespace nvfp4 {
 #ifndef NVFP4_NOALLOC_SCRATCH_BYTES
 #define NVFP4_NOALLOC_SCRATCH_BYTES (16u << 20)
 #endif
-constexpr int kAmaxThreads = 256;
-constexpr int kAmaxMaxGroups = 512;
 constexpr int kQuantThreads = NVFP4_QUANT_THREADS;
 constexpr int kQuantGroups = NVFP4_QUANT_GROUPS;
 constexpr int kQuantDepth = NVFP4_QUANT_DEPTH;
 constexpr int kCjsoThreads = NVFP4_CJSO_THREADS;
 constexpr int kCjsoGroups = NVFP4_CJSO_GROUPS;
 constexpr int kCjsoDepth = NVFP4_CJSO_DEPTH;
+// the max pass runs on the grid of its consumer (k_quant or k_cjso_init)
+constexpr int kAmaxMaxGroups = kQuantGroups > kCjsoGroups ? kQuantGroups : kCjsoGroups;
 constexpr int kMinBlocksPerThread = 2;
 
-int amax_groups(int64_t nchunks);
 int quant_groups(int64_t nblk);
 int cjso_groups(int64_t nblk);
 
 // Scratch layout inside the workspace (byte offsets, 256-byte aligned pieces).
 struct Workspace {
-    uint32_t *amax_part;  // [kAmaxMaxGroups]   max |w| bits per work-group
+    uint32_t *amax_part;  // [kAmaxMaxGroups]   max |w| bits per work-group of the max pass
     float *alpha_state;   // [2]                alpha of the previous / current CJSO round
     double *cjso_part;    // [2][kCjsoGroups][4] (N.hi, N.lo, D.hi, D.lo) per work-group
     uint16_t *brackets;   // [nblk]             E4M3 codes lo | hi << 8 around the unrounded CJSO scale (SOAR)
@@ -69,8 +68,10 @@ int check_args(const nvfp4_args_t *a);
 int run_quantize(const nvfp4_args_t *a, void *ws);
 Workspace carve(void *base, int64_t nblk);
 
-hipError_t launch_amax(const void *W, bool f32, int64_t n, uint32_t *amax_part, int groups, nvfp4_stats_t *stats,
-                       hipStream_t stream);
+// The global max pass, on the grid of the pass that consumes it (k_cjso_init when for_cjso, else k_quant);
+// `groups` gets the number of per-work-group partials written.
+hipError_t launch_amax(const void *W, bool f32, int64_t nblk, bool for_cjso, uint32_t *amax_part, int &groups,
+                       nvfp4_stats_t *stats, hipStream_t stream);
 hipError_t launch_quant(const void *W, bool f32, bool four_over_six, int64_t nblk, const uint32_t *amax_part,
                         int amax_n, uint8_t *codes, uint8_t *scales, float *alpha_out, uint8_t *mchoice,
                         nvfp4_stats_t *stats, uint32_t *m4_part, hipStream_t stream);

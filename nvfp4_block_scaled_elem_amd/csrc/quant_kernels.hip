@@ -75,26 +75,33 @@ __device__ __forceinline__ uint32_t wg_max(uint32_t m) {
     return m;
 }
 
-// Work-group sum (T threads) of two double-doubles (fixed order); the result is valid in thread 0.
+// Work-group sum (T threads) of two double-doubles in a fixed order. Waves 1.. hand their lanes' values
+// to wave 0 through LDS; wave 0 adds them lane by lane and then reduces across its lanes, so only one
+// wave runs the long dependent chain of double-double additions. The result is valid in thread kSumLane.
+constexpr int kSumLane = 63;
 template <int T>
 __device__ __forceinline__ void wg_sum_dd2(dd &N, dd &D) {
-    __shared__ double red[T / 64][4];
-    wave_sum_dd2(N, D);
-    if ((threadIdx.x & 63) == 63) {
-        red[threadIdx.x >> 6][0] = N.hi;
-        red[threadIdx.x >> 6][1] = N.lo;
-        red[threadIdx.x >> 6][2] = D.hi;
-        red[threadIdx.x >> 6][3] = D.lo;
-    }
-    lds_barrier();
-    if (threadIdx.x == 0) {
-        N = {red[0][0], red[0][1]};
-        D = {red[0][2], red[0][3]};
-        for (int i = 1; i < T / 64; ++i) {
-            N = dd_add(N, dd{red[i][0], red[i][1]});
-            D = dd_add(D, dd{red[i][2], red[i][3]});
+    constexpr int NW = T / 64;
+    static_assert(T % 64 == 0 && NW >= 1, "whole waves");
+    if constexpr (NW > 1) {
+        __shared__ double buf[NW - 1][4][64];  // [wave - 1][N.hi, N.lo, D.hi, D.lo][lane]
+        const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+        if (w > 0) {
+            buf[w - 1][0][l] = N.hi;
+            buf[w - 1][1][l] = N.lo;
+            buf[w - 1][2][l] = D.hi;
+            buf[w - 1][3][l] = D.lo;
+        }
+        lds_barrier();
+        if (w == 0) {
+#pragma unroll
+            for (int i = 0; i < NW - 1; ++i) {
+                N = dd_add(N, dd{buf[i][0][l], buf[i][1][l]});
+                D = dd_add(D, dd{buf[i][2][l], buf[i][3][l]});
+            }
         }
     }
+    if (threadIdx.x < 64) wave_sum_dd2(N, D);
 }
 
 // A kernel's prologue reads the previous kernel's per-work-group partials. Each thread loads its share
@@ -143,7 +150,7 @@ struct CjsoShare {
             D = dd_add(D, dd{v[k][2], v[k][3]});
         }
         wg_sum_dd2<T>(N, D);
-        if (threadIdx.x == 0) {
+        if (threadIdx.x == kSumLane) {
             tot[0] = N.hi;
             tot[1] = N.lo;
             tot[2] = D.hi;
@@ -178,66 +185,73 @@ __device__ __forceinline__ void store_codes(uint8_t *codes, int64_t b, uint32_t 
     *reinterpret_cast<uint2 *>(codes + 8 * b) = make_uint2(e2m1_clear_negzero(c0), e2m1_clear_negzero(c1));
 }
 
-// Visit this thread's blocks b = gid, gid + S, gid + 2S, ... (S = all T * gridDim threads) through a
-// ring of DEPTH blocks in registers: the loads of block i + DEPTH are issued as soon as block i has been
-// unpacked, so DEPTH blocks are in flight while one is processed (indices past the end are clamped to
-// the last block, a cached re-read). The ring is unrolled, so no register copy waits on a load. `pre`
-// issues the prologue's own loads, then the first DEPTH blocks are requested, then `post` (run by every
-// thread of the work-group) finishes the prologue; it returns false to skip the blocks (the function
-// then returns false). f(b, B, sc) gets the block and, when `sc_in` is given, its scale byte.
+// Visit this thread's blocks b = gid, gid + S, gid + 2S, ... (S = all T * gridDim threads), in that order
+// or, with `reverse`, from the last one down, through a ring of DEPTH blocks in registers: the loads of
+// block i + DEPTH are issued as soon as block i has been unpacked, so DEPTH blocks are in flight while one
+// is processed (a prefetch past the thread's last block re-reads its first one, a cached read). The ring is
+// unrolled, so no register copy waits on a load. `pre` issues the prologue's own loads, then the first DEPTH
+// blocks are requested, then `post` (run by every thread of the work-group) finishes the prologue; it
+// returns false to skip the blocks (the function then returns false). f(b, B, sc) gets the block and, when
+// `sc_in` is given, its scale byte.
+//
+// A work-group runs on the XCD blockIdx.x % 8, and every pass over W with the same grid hands the same
+// blocks to the same work-group, so a pass that visits them in the opposite order to the pass before it
+// starts on the blocks that pass read last, which its XCD's L2 still holds.
 template <int T, int DEPTH, bool F32, class Pre, class Post, class F>
 __device__ __forceinline__ bool for_my_blocks(const void *__restrict__ W, const uint8_t *__restrict__ sc_in,
-                                              int64_t nblk, Pre &&pre, Post &&post, F &&f) {
+                                              int64_t nblk, bool reverse, Pre &&pre, Post &&post, F &&f) {
     constexpr int D = DEPTH;
     const int64_t stride = (int64_t)gridDim.x * T;
-    int64_t b = (int64_t)blockIdx.x * T + threadIdx.x;
-    const int64_t last = nblk - 1;
+    const int64_t first = (int64_t)blockIdx.x * T + threadIdx.x;
+    const int64_t n = first < nblk ? (nblk - 1 - first) / stride + 1 : 0;  // blocks of this thread
+    const int64_t start = reverse && n > 0 ? first + (n - 1) * stride : first;
+    const int64_t step = reverse ? -stride : stride;
+    const int64_t safe = n > 0 ? start : nblk - 1;  // a valid block to prefetch past the end
     Raw<F32> r[D];
     uint32_t sc[D];
     pre();
 #pragma unroll
     for (int k = 0; k < D; ++k) {
-        const int64_t bk = b + k * stride;
-        const int64_t c = bk < last ? bk : last;
+        const int64_t c = k < n ? start + k * step : safe;
         r[k].load(W, c);
         sc[k] = sc_in ? (uint32_t)sc_in[c] : 0u;
     }
     if (!post()) return false;
-    if (b >= nblk) return true;
-    for (;;) {
+    int64_t b = start;
+    for (int64_t i = 0; i < n;) {
 #pragma unroll
         for (int k = 0; k < D; ++k) {
             Blk<F32> B;
             B.set(r[k]);
             const uint32_t s = sc[k];
-            const int64_t bn = b + D * stride;
-            const int64_t c = bn < last ? bn : last;
+            const int64_t c = i + D < n ? b + D * step : safe;
             r[k].load(W, c);
             if (sc_in) sc[k] = sc_in[c];
             f(b, B, s);
-            b += stride;
-            if (b >= nblk) return true;
+            b += step;
+            if (++i >= n) return true;
         }
     }
+    return true;
 }
 
 // ---------------------------------------------------------------------------------- global max
 
 // Per work-group max of |w| as binary32 bits (bf16 bits are widened), plus the non-finite test
-// (any NaN or infinity makes the max >= 0x7F800000). Zeroes the stats for this call.
-template <bool F32>
-__global__ __launch_bounds__(kAmaxThreads) void k_amax(const uint4 *__restrict__ W, int64_t nchunks,
-                                                       uint32_t *__restrict__ part, nvfp4_stats_t *stats) {
+// (any NaN or infinity makes the max >= 0x7F800000). Zeroes the stats for this call. The work-groups
+// and threads are laid out exactly as in the pass that consumes the max (T threads, the same grid, thread
+// b of the grid visiting blocks b, b + S, ...), so each block is read twice by the same work-group on
+// the same XCD; the consumer visits its blocks in the opposite order and starts on those still in L2.
+template <bool F32, int T>
+__global__ __launch_bounds__(T) void k_amax(const void *__restrict__ W, int64_t nblk, uint32_t *__restrict__ part,
+                                            nvfp4_stats_t *stats) {
+    constexpr int U = 4;  // blocks in flight per thread
+    constexpr int NV = F32 ? 4 : 2;
     uint32_t m = 0u;
-    const int64_t stride = (int64_t)gridDim.x * kAmaxThreads;
-    int64_t i = (int64_t)blockIdx.x * kAmaxThreads + threadIdx.x;
-    for (; i + 3 * stride < nchunks; i += 4 * stride) {
-        uint4 v[4];
+    auto fold = [&](const Raw<F32> &r) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = W[i + u * stride];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const uint32_t d[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+        for (int v = 0; v < NV; ++v) {
+            const uint32_t d[4] = {r.v[v].x, r.v[v].y, r.v[v].z, r.v[v].w};
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 if (F32) {
@@ -250,29 +264,28 @@ __global__ __launch_bounds__(kAmaxThreads) void k_amax(const uint4 *__restrict__
                 }
             }
         }
-    }
-    for (; i < nchunks; i += stride) {
-        const uint4 v = W[i];
-        const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+    };
+    const int64_t stride = (int64_t)gridDim.x * T;
+    int64_t b = (int64_t)blockIdx.x * T + threadIdx.x;
+    for (; b + (U - 1) * stride < nblk; b += U * stride) {
+        Raw<F32> r[U];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            if (F32) {
-                const uint32_t a = d[k] & 0x7FFFFFFFu;
-                m = a > m ? a : m;
-            } else {
-                const uint32_t lo = (d[k] & 0x7FFFu) << 16, hi = d[k] & 0x7FFF0000u;
-                m = lo > m ? lo : m;
-                m = hi > m ? hi : m;
-            }
-        }
+        for (int u = 0; u < U; ++u) r[u].load(W, b + u * stride);
+#pragma unroll
+        for (int u = 0; u < U; ++u) fold(r[u]);
     }
-    __shared__ uint32_t red[kAmaxThreads / 64];
+    for (; b < nblk; b += stride) {
+        Raw<F32> r;
+        r.load(W, b);
+        fold(r);
+    }
+    __shared__ uint32_t red[T / 64];
     m = wave_max_u32(m);
     if ((threadIdx.x & 63) == 63) red[threadIdx.x >> 6] = m;
     __syncthreads();
     if (threadIdx.x == 0) {
         m = red[0];
-        for (int k = 1; k < kAmaxThreads / 64; ++k) m = red[k] > m ? red[k] : m;
+        for (int k = 1; k < T / 64; ++k) m = red[k] > m ? red[k] : m;
         part[blockIdx.x] = m;
         if (blockIdx.x == 0 && stats) {
             stats->status = 0u;
@@ -335,7 +348,8 @@ __global__ __launch_bounds__(kQuantThreads) __attribute__((amdgpu_waves_per_eu(4
         build_scale_tab<kQuantThreads>(T, alpha);
         return true;
     };
-    const bool finite = for_my_blocks<kQuantThreads, kQuantDepth, F32>(W, nullptr, nblk, pre, post,
+    // the opposite order to k_amax, which read the same blocks in the same work-group just before
+    const bool finite = for_my_blocks<kQuantThreads, kQuantDepth, F32>(W, nullptr, nblk, true, pre, post,
                                            [&](int64_t b, const Blk<F32> &B, uint32_t) {
             uint32_t c0, c1, sc;
             bool m4 = false;
@@ -427,7 +441,8 @@ __global__ __launch_bounds__(kCjsoThreads) __attribute__((amdgpu_waves_per_eu(4)
         build_scale_tab<kCjsoThreads>(T, alpha);
         return true;
     };
-    const bool finite = for_my_blocks<kCjsoThreads, kCjsoDepth, F32>(W, nullptr, nblk, pre, post,
+    // the opposite order to k_amax, which read the same blocks in the same work-group just before
+    const bool finite = for_my_blocks<kCjsoThreads, kCjsoDepth, F32>(W, nullptr, nblk, true, pre, post,
                                            [&](int64_t b, const Blk<F32> &B, uint32_t) {
         const float a = B.amax();
         const double q = max_rule_quotient(a, alpha);
@@ -472,7 +487,7 @@ __global__ __launch_bounds__(kCjsoThreads) __attribute__((amdgpu_waves_per_eu(4)
     }
     if (ROUNDS) {
         wg_sum_dd2<kCjsoThreads>(N, D);
-        if (threadIdx.x == 0) {
+        if (threadIdx.x == kSumLane) {
             part_out[4 * blockIdx.x + 0] = N.hi;
             part_out[4 * blockIdx.x + 1] = N.lo;
             part_out[4 * blockIdx.x + 2] = D.hi;
@@ -515,7 +530,9 @@ __global__ __launch_bounds__(kCjsoThreads) __attribute__((amdgpu_waves_per_eu(4)
         build_scale_tab<kCjsoThreads>(T, alpha);
         return true;
     };
-    if (!for_my_blocks<kCjsoThreads, kCjsoDepth, F32>(W, scales, nblk, pre, post, [&](int64_t b, const Blk<F32> &B, uint32_t d) {
+    // forward: round 1 starts on the blocks k_cjso_init (which runs backwards) read last; alternating the
+    // order of later rounds as well was timed and gained nothing (their time is spent on arithmetic)
+    if (!for_my_blocks<kCjsoThreads, kCjsoDepth, F32>(W, scales, nblk, false, pre, post, [&](int64_t b, const Blk<F32> &B, uint32_t d) {
         const float v = e4m3_value(d);
         uint32_t c0, c1;
         double sw, sq;
@@ -550,7 +567,7 @@ __global__ __launch_bounds__(kCjsoThreads) __attribute__((amdgpu_waves_per_eu(4)
         return;
     if (!LAST) {
         wg_sum_dd2<kCjsoThreads>(Nn, Dn);
-        if (threadIdx.x == 0) {
+        if (threadIdx.x == kSumLane) {
             part_out[4 * blockIdx.x + 0] = Nn.hi;
             part_out[4 * blockIdx.x + 1] = Nn.lo;
             part_out[4 * blockIdx.x + 2] = Dn.hi;
@@ -689,7 +706,7 @@ __global__ __launch_bounds__(kStatThreads) void k_stats(const void *__restrict__
     }
     wg_sum_dd2<kStatThreads>(S, Z);
     lds_barrier();
-    if (threadIdx.x == 0) {
+    if (threadIdx.x == kSumLane) {
         part[2 * blockIdx.x] = S.hi;
         part[2 * blockIdx.x + 1] = S.lo;
     }
@@ -722,7 +739,7 @@ __global__ __launch_bounds__(kStatThreads) void k_stats_final(const double *__re
     dd S = {0.0, 0.0}, Z = {0.0, 0.0};
     for (int g = threadIdx.x; g < groups; g += kStatThreads) S = dd_add(S, dd{part[2 * g], part[2 * g + 1]});
     wg_sum_dd2<kStatThreads>(S, Z);
-    if (threadIdx.x == 0) *sse_out = S.hi + S.lo;
+    if (threadIdx.x == kSumLane) *sse_out = S.hi + S.lo;
     if (threadIdx.x < 16) {
         unsigned long long t = 0ull;
 #pragma unroll
@@ -732,11 +749,6 @@ __global__ __launch_bounds__(kStatThreads) void k_stats_final(const double *__re
 }
 
 // ------------------------------------------------------------------------------------ launchers
-
-int amax_groups(int64_t nchunks) {
-    int64_t g = (nchunks + kAmaxThreads * 4 - 1) / (kAmaxThreads * 4);
-    return (int)(g < 1 ? 1 : (g > kAmaxMaxGroups ? kAmaxMaxGroups : g));
-}
 
 static int stream_groups(int64_t nblk, int threads, int max_groups) {
     int64_t g = (nblk + (int64_t)threads * kMinBlocksPerThread - 1) / ((int64_t)threads * kMinBlocksPerThread);
@@ -770,15 +782,25 @@ Workspace carve(void *base, int64_t nblk) {
     return w;
 }
 
-hipError_t launch_amax(const void *W, bool f32, int64_t n, uint32_t *amax_part, int groups, nvfp4_stats_t *stats,
-                       hipStream_t stream) {
-    const int64_t nchunks = n * (f32 ? 4 : 2) / 16;
-    if (f32)
-        hipLaunchKernelGGL(k_amax<true>, dim3(groups), dim3(kAmaxThreads), 0, stream, (const uint4 *)W, nchunks,
-                           amax_part, stats);
-    else
-        hipLaunchKernelGGL(k_amax<false>, dim3(groups), dim3(kAmaxThreads), 0, stream, (const uint4 *)W, nchunks,
-                           amax_part, stats);
+hipError_t launch_amax(const void *W, bool f32, int64_t nblk, bool for_cjso, uint32_t *amax_part, int &groups,
+                       nvfp4_stats_t *stats, hipStream_t stream) {
+    if (for_cjso) {
+        groups = cjso_groups(nblk);
+        if (f32)
+            hipLaunchKernelGGL((k_amax<true, kCjsoThreads>), dim3(groups), dim3(kCjsoThreads), 0, stream, W, nblk,
+                               amax_part, stats);
+        else
+            hipLaunchKernelGGL((k_amax<false, kCjsoThreads>), dim3(groups), dim3(kCjsoThreads), 0, stream, W, nblk,
+                               amax_part, stats);
+    } else {
+        groups = quant_groups(nblk);
+        if (f32)
+            hipLaunchKernelGGL((k_amax<true, kQuantThreads>), dim3(groups), dim3(kQuantThreads), 0, stream, W, nblk,
+                               amax_part, stats);
+        else
+            hipLaunchKernelGGL((k_amax<false, kQuantThreads>), dim3(groups), dim3(kQuantThreads), 0, stream, W,
+                               nblk, amax_part, stats);
+    }
     return hipGetLastError();
 }
 
