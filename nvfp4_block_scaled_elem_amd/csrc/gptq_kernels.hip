@@ -556,7 +556,6 @@ hipError_t launch_gptq(const void *W, bool f32, int64_t R, int64_t K, const doub
     const Workspace q = carve(p, nblk);
 
     // the FourOverSix frame: scales and alpha (and codes, overwritten below)
-    const int64_t n = R * K;
     int ga = 0;
     hipError_t err = launch_amax(W, f32, nblk, false, q.amax_part, ga, nullptr, stream);
     if (err == hipSuccess)

@@ -102,8 +102,8 @@ __device__ __forceinline__ void scan(const Blk<F32> &B, const float *__restrict_
 // binary32 dot products (exact there), fp32 blocks in binary64 (each product has at most 26 significant
 // bits and the sums stay on a lattice of about 40 bits, so they are exact too).
 template <bool F32>
-__device__ __forceinline__ double eval_s(const Blk<F32> &B, float s, double h, uint32_t &c0, uint32_t &c1) {
-    encode16(B.w, 1.0f / s, c0, c1);
+__device__ __forceinline__ double eval_r(const Blk<F32> &B, float r, double h, uint32_t &c0, uint32_t &c1) {
+    encode16(B.w, r, c0, c1);
     if constexpr (F32) {
         double sw, sq;
         sums_f64(c0, c1, B.w, sw, sq);
@@ -113,6 +113,11 @@ __device__ __forceinline__ double eval_s(const Blk<F32> &B, float s, double h, u
         sums_bf16(c0, c1, B.p, sw, sq);
         return fma(h, (double)sq, -(double)sw);
     }
+}
+
+template <bool F32>
+__device__ __forceinline__ double eval_s(const Blk<F32> &B, float s, double h, uint32_t &c0, uint32_t &c1) {
+    return eval_r<F32>(B, 1.0f / s, h, c0, c1);
 }
 
 template <bool F32>
@@ -285,16 +290,55 @@ __global__ __launch_bounds__(kSoarThreads) void k_soar(const void *__restrict__ 
     }
     {
         if (windowed) {
-            // the incumbent, then the first minimiser of A_d in each reconstruct scale's window
+            // the incumbent
             const double sd_c = c_is_lo ? slo : shi, h_c = c_is_lo ? hlo : hhi;
             uint32_t i0, i1;
-            a_c = eval_s(B, sc, h_c, i0, i1);
-            // own window (d = Delta_c) first, then the other scale's
+            const float rc = 1.0f / sc;
+            a_c = eval_r(B, rc, h_c, i0, i1);
             const float vo = c_is_lo ? vhi : vlo;
             const double sd_o = c_is_lo ? shi : slo, h_o = c_is_lo ? hhi : hlo;
-            Pick pc, po;
             int kA, kB;
             const GridGuess gg{g.count - 1, (float)g.den, (float)g.num0};
+            // Are the incumbent's codes the nearest E2M1 values of the exact quotients |w| / (alpha Delta_c)?
+            // Its computed x = fl(w fl(1/fl(alpha Delta_c))) is within 3 * 2^-24 of the quotient u, so
+            // codes computed with the reciprocal moved by 2^-21 down and up bracket those of u; where both
+            // equal the incumbent's, so do those of u (the rounding is monotone). Then every element's
+            // error term under Delta_d = Delta_c is already the least that scale allows: no candidate with
+            // that reconstruct scale is strictly better than the incumbent, and only the other scale's
+            // window can win (first minimiser in scan order: the window's first minimiser, whose codes
+            // every earlier k with the same error shares). This holds for all but a few blocks in a million,
+            // which take the full window comparison below.
+            uint32_t u0, u1, l0, l1;
+            encode16(B.w, rc * (1.0f + 0x1p-21f), u0, u1);
+            encode16(B.w, rc * (1.0f - 0x1p-21f), l0, l1);
+            if (((u0 ^ i0) | (u1 ^ i1) | (l0 ^ i0) | (l1 ^ i1)) == 0u && (dc == lo || dc == hi)) {
+                uint32_t o0 = i0, o1 = i1;
+                db = dc;
+                if (lo != hi) {
+                    window(alpha, vc, vo, sd_o, ftab, gg, kA, kB);
+                    double best = INFINITY;
+                    uint32_t b0 = 0u, b1 = 0u;
+                    for (int k = kA; k <= kB; ++k) {
+                        uint32_t d0, d1;
+                        const double v = eval_k(B, alpha, vc, ftab, k, h_o, d0, d1);
+                        if (v < best) {
+                            best = v;
+                            b0 = d0;
+                            b1 = d1;
+                        }
+                    }
+                    if (dd_less(two_prod(sd_o, best), two_prod(sd_c, a_c))) {
+                        o0 = b0;
+                        o1 = b1;
+                        db = c_is_lo ? hi : lo;
+                    }
+                }
+                *reinterpret_cast<uint2 *>(codes + 8 * b) = make_uint2(e2m1_clear_negzero(o0), e2m1_clear_negzero(o1));
+                scales[b] = (uint8_t)db;
+                return;
+            }
+            // otherwise the first minimiser of A_d in each reconstruct scale's window, own scale first
+            Pick pc, po;
             window(alpha, vc, vc, sd_c, ftab, gg, kA, kB);
             pc.a = INFINITY;
             pc.k = kA;
