@@ -152,6 +152,7 @@ def cpu_baseline(W0: np.ndarray) -> dict:
     dtn = time.perf_counter() - t0
     alln = len(MODES) * sum(x.nbytes for x in samples) / dtn
     gptq_leg = gptq_cpu_sample(W0)
+    per_config = oracle_per_config(W0)
     model = ""
     try:
         with open("/proc/cpuinfo") as f:
@@ -164,7 +165,49 @@ def cpu_baseline(W0: np.ndarray) -> dict:
             "single_thread": {"value": round(one / 1e9, 6), "unit": "GB/s",
                               "sample": f"rows 0-255, all four modes, {dt1:.1f} s"},
             "gptq": gptq_leg,
+            "per_config": per_config,
             "host": {"nproc": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)), "cpu_model": model}}
+
+
+def oracle_per_config(W0: np.ndarray) -> dict:
+    """The oracle, one thread, on a bounded row sample of every workload, extrapolated to the whole
+    workload by its element count (labelled so): C1 in full (MAX and FourOverSix); C2 (the 4096 x 4096
+    matrix; MAX and FourOverSix) from 64 rows; C3 (14336 x 4096 and 4096 x 14336; FourOverSix and CJSO(8))
+    from 32 rows of each; C4 (the C2 matrix; SOAR(8)) from 32 rows; C5 (one 7B-shaped layer of 7
+    matrices; FourOverSix and SOAR(8)) from 16 rows of each, times 32 layers."""
+    import oracle
+    import synth
+
+    def timed(W, runs):
+        t0 = time.perf_counter()
+        for mode, iters in runs:
+            oracle.quantize(np.ascontiguousarray(W), mode, iters)
+        return time.perf_counter() - t0
+
+    out = {}
+    W1 = synth.c1(0)
+    out["C1"] = {"seconds": round(timed(W1, [("max", 0), ("4o6", 0)]), 3), "sample": "whole matrix",
+                 "modes": "max, 4o6"}
+    dt = timed(W0[:64], [("max", 0), ("4o6", 0)])
+    out["C2"] = {"seconds_extrapolated": round(dt * 4096 / 64, 2), "sample": "rows 0-63", "modes": "max, 4o6"}
+    tot = 0.0
+    for which in (0, 1):
+        W = synth.c3(which, 0, rows=32)  # the first 32 rows of the matrix
+        dt = timed(W, [("4o6", 0), ("cjso", ITERS)])
+        tot += dt * (14336, 4096)[which] / 32
+    out["C3"] = {"seconds_extrapolated": round(tot, 2), "sample": "rows 0-31 of each matrix",
+                 "modes": f"4o6, cjso({ITERS})"}
+    dt = timed(W0[:32], [("soar", ITERS)])
+    out["C4"] = {"seconds_extrapolated": round(dt * 4096 / 32, 2), "sample": "rows 0-31", "modes": f"soar({ITERS})"}
+    tot = 0.0
+    for name in synth.C5_ORDER:
+        W = synth.c5(0, name, rows=16)  # the first 16 rows of the matrix
+        dt = timed(W, [("4o6", 0), ("soar", ITERS)])
+        tot += dt * synth.C5_SHAPES[name][0] / 16
+    out["C5"] = {"seconds_extrapolated": round(tot * 32, 1), "layer0_seconds_extrapolated": round(tot, 2),
+                 "sample": "rows 0-15 of each matrix of layer 0, times 32 layers", "modes": f"4o6, soar({ITERS})"}
+    out["threads"] = 1
+    return out
 
 
 def gptq_cpu_sample(W0: np.ndarray, rows: int = 32) -> dict:
@@ -491,9 +534,8 @@ def cold_warm_pass(torch, nv, W, outs, reps=25) -> dict:
     read leaves no dirty lines behind whose write-back would land in the timed call), "warm" for the
     same call repeated at once. Median of `reps` of each."""
     dev = W.device
-    flush = torch.ones((1 << 30) // 4, dtype=torch.float32, device=dev)
-    sink = torch.empty(1, dtype=torch.float32, device=dev)
-    torch.amax(flush, dim=0, out=sink)  # the fill's dirty lines leave before the first timed call
+    flush = torch.ones((1 << 30) // 4, dtype=torch.float32, device=dev).view(-1, 4096)
+    flush.amax(dim=1)  # the fill's dirty lines leave before the first timed call
     torch.cuda.synchronize()
     res = {}
     for mode, iters in MODES:
@@ -502,7 +544,7 @@ def cold_warm_pass(torch, nv, W, outs, reps=25) -> dict:
                                    alpha=o["alpha"], mchoice=o["mchoice"], workspace=o["workspace"])
         cold, warm = [], []
         for r in range(reps):
-            torch.amax(flush, dim=0, out=sink)
+            flush.amax(dim=1)
             torch.cuda.synchronize()
             ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
             ev[0].record()
@@ -589,12 +631,12 @@ def fp32_pass(torch, nv, W) -> dict:
 
 def hbm_attainable(torch, dev) -> dict:
     """What a plain streaming kernel reaches on this box: a 1 GiB device copy (torch's copy kernel;
-    read + write bytes per second) and a read-only pass over 1 GiB (torch's max reduction; bytes read per
-    second). Median of 10 each."""
+    read + write bytes per second) and a read-only pass over 1 GiB (torch's max reduction over rows of
+    4096 values, which keeps every CU streaming; bytes read per second). Median of 10 each."""
     n = (1 << 30) // 4
     src = torch.ones(n, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
-    sink = torch.empty(1, dtype=torch.float32, device=dev)
+    rows = src.view(-1, 4096)
 
     def med(fn):
         for _ in range(3):
@@ -609,12 +651,12 @@ def hbm_attainable(torch, dev) -> dict:
             ts.append(e0.elapsed_time(e1) * 1e-3)
         return sorted(ts)[len(ts) // 2]
     t_copy = med(lambda: dst.copy_(src))
-    t_read = med(lambda: torch.amax(src, dim=0, out=sink))
+    t_read = med(lambda: rows.amax(dim=1))
     del src, dst
     torch.cuda.empty_cache()
     return {"copy_GBps": round(2 * n * 4 / t_copy / 1e9, 1), "frac_of_peak": round(2 * n * 4 / t_copy / PEAK_HBM, 4),
             "read_GBps": round(n * 4 / t_read / 1e9, 1), "read_frac_of_peak": round(n * 4 / t_read / PEAK_HBM, 4),
-            "kind": "1 GiB device copy (read + write bytes) and 1 GiB read-only max reduction, median of 10"}
+            "kind": "1 GiB device copy (read + write bytes) and 1 GiB read-only row-max reduction, median of 10"}
 
 
 def main():

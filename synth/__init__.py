@@ -66,15 +66,19 @@ def c2(seed: int = 0, rows: int = 4096, cols: int = 4096) -> np.ndarray:
     return bf16_bits(w.astype(np.float32))
 
 
-def c3(which: int, seed: int = 0) -> np.ndarray:
-    rows, cols = ((14336, 4096), (4096, 14336))[which]
+def c3(which: int, seed: int = 0, rows: int = 0) -> np.ndarray:
+    """`rows` > 0: only the first rows of the matrix (the same values; the draws are made in row order)."""
+    full, cols = ((14336, 4096), (4096, 14336))[which]
+    rows = rows or full
     g = rng(seed, which)
     sigma = 0.015 * np.exp2(rng(seed, which, 1).uniform(-1.0, 1.0, size=(rows, 1)))
     return bf16_bits((g.standard_normal((rows, cols)) * sigma).astype(np.float32))
 
 
-def c5(layer: int, name: str) -> np.ndarray:
-    rows, cols = C5_SHAPES[name]
+def c5(layer: int, name: str, rows: int = 0) -> np.ndarray:
+    """`rows` > 0: only the first rows of the matrix (the same values; the draws are made in row order)."""
+    full, cols = C5_SHAPES[name]
+    rows = rows or full
     g = rng(layer, C5_ORDER.index(name))
     return bf16_bits(student_t(g, 5.0, (rows, cols), 0.02).astype(np.float32))
 
