@@ -16,6 +16,8 @@ Workloads (weights of real models are not available; these stand in for them):
     multiplied by 2^U(-1, 1), i.e. log-uniform on [0.5, 2].
   * ``c5``: one linear layer of a 7B-shaped transformer (q, k, v, o 4096 x 4096; gate, up 11008 x 4096;
     down 4096 x 11008) bf16, Student-t (nu = 5) scaled to std 0.02, seeded by the layer index.
+  * ``soar_tie_matrix``: fp32 blocks constructed so that the decoupled search ends in an exact tie
+    between its two reconstruct scales (described at the function).
   * ``activations`` / ``hessian``: calibration inputs of a linear layer for GPTQ (no real activations
     are available): per-feature scales 2^U(-2, 2), a rank-8 component shared by all features so that
     they correlate, optionally some features that are always zero; ``hessian`` returns their second
@@ -89,6 +91,38 @@ def normal_bf16(rows: int, cols: int, seed: int, std: float = 0.02) -> np.ndarra
 
 def normal_f32(rows: int, cols: int, seed: int, std: float = 0.02) -> np.ndarray:
     return (rng(seed, 8).standard_normal((rows, cols)) * std).astype(np.float32)
+
+
+# Two blocks in units of alpha = 2^-12, eta = 2^-18 (every value is a binary32 number). Under the max rule
+# (no CJSO rounds) block A gets Delta_c = 15 with the reconstruct pair {15, 16}, block B Delta_c = 15 with
+# {14, 15}. The element 52.5 - eta lies just below the E2M1 midpoint 3.5 at scale 15; binary32 rounding of
+# its scaled value lands on 3.5, so the incumbent codes it 4 where 3 is nearer, and candidates with
+# Delta_q slightly above 15 beat the incumbent. The other elements are chosen so that the least error at
+# either reconstruct scale is exactly the same number: the eta terms cancel (the 3 eta and -11 eta
+# elements) and the remaining squares balance (the 30 and 15s in A, the 60 and 45 in B).
+_ETA = 2.0 ** -18
+SOAR_TIE_BLOCKS = {
+    "A": [91.0, 52.5 - _ETA, 17.0 + 3 * _ETA, 30.0] + [15.0] * 11 + [0.0],
+    "B": [89.0, 52.5 - _ETA, 12.0 - 11 * _ETA, 60.0, 45.0] + [0.0] * 11,
+}
+SOAR_TIE_ALPHA = 2.0 ** -12
+
+
+def soar_tie_matrix(seed: int = 0, rows: int = 8, cols: int = 256):
+    """fp32 [rows, cols] whose global max is 6 * 448 * 2^-12 (so the max rule's alpha is exactly 2^-12),
+    holding copies of SOAR_TIE_BLOCKS (elements permuted, signs drawn per element) between N(0, 0.02^2)
+    blocks. Returns (W, kinds) with kinds[b] = "A", "B" or "" for block b in row-major block order."""
+    g = rng(seed, 10)
+    nb = rows * cols // 16
+    kinds = g.choice(np.array(["A", "B", ""]), size=nb, p=[0.4, 0.4, 0.2])
+    kinds[0] = ""
+    W = (g.standard_normal((nb, 16)) * 0.02).astype(np.float32)
+    for b in range(nb):
+        if kinds[b]:
+            v = np.array(SOAR_TIE_BLOCKS[kinds[b]], np.float64)[g.permutation(16)]
+            W[b] = (v * g.choice([-1.0, 1.0], size=16) * SOAR_TIE_ALPHA).astype(np.float32)
+    W[0, int(g.integers(16))] = np.float32(6 * 448 * SOAR_TIE_ALPHA) * np.float32(g.choice([-1.0, 1.0]))
+    return W.reshape(rows, cols), [str(k) for k in kinds]
 
 
 def activations(n: int, cols: int, seed: int, dead: int = 0) -> np.ndarray:

@@ -436,6 +436,18 @@ def test_soar_tie_prone_inputs_match_oracle(gen, seed):
     compare_live(np.ascontiguousarray(indep.as_f32(W)), "soar", 8)  # the same values as fp32 input
 
 
+@pytest.mark.parametrize("seed,rows,cols", [(0, 8, 256), (1, 64, 1024)])
+def test_soar_exact_tie_blocks_match_oracle(seed, rows, cols):
+    """fp32 blocks whose search ends in an exact tie between the two reconstruct scales, below the
+    incumbent (synth.soar_tie_matrix; tests/test_oracle_soar_tie.py shows they are): the windowed search
+    takes its equal-error branch there, and it and the full scan keep the first candidate in scan order."""
+    W, kinds = synth.soar_tie_matrix(seed, rows, cols)
+    say(f"tie blocks: {kinds.count('A')} A, {kinds.count('B')} B")
+    compare_live(W, "soar", 0)
+    g = run(W, "soar", 0, full_search=True)
+    assert_exact(g, oracle.quantize(W, "soar", 0), "soar")
+
+
 # ------------------------------------------------------------------- CJSO / SOAR from FourOverSix
 
 INIT_CASES = {
