@@ -15,7 +15,10 @@ namespace nvfp4 {
 // each thread walking at least kMinBlocksPerThread blocks) and keep D blocks per thread in flight in a
 // register ring. The MAX/FourOverSix pass (k_quant) and the CJSO passes (k_cjso_init, k_cjso_iter) are
 // tuned separately: the defaults are the fastest of the settings timed on an MI355X for a 4096 x 4096
-// matrix, and the macros exist so that other settings can be built and timed.
+// matrix, and the macros exist so that other settings can be built and timed. For the CJSO passes that
+// weighs a call alone against calls on three streams at once: 1024 x 256 is 6 % faster alone but, at
+// 16 waves per CU with up to 105 VGPRs each, leaves no room for another stream's work-groups and loses
+// 18 % over three streams; 512 x 256 is 3 % faster alone than 256 x 512 and as fast over three streams.
 #ifndef NVFP4_QUANT_THREADS
 #define NVFP4_QUANT_THREADS 512
 #endif
@@ -26,13 +29,21 @@ namespace nvfp4 {
 #define NVFP4_QUANT_DEPTH 2
 #endif
 #ifndef NVFP4_CJSO_THREADS
-#define NVFP4_CJSO_THREADS 256
+#define NVFP4_CJSO_THREADS 512
 #endif
 #ifndef NVFP4_CJSO_GROUPS
-#define NVFP4_CJSO_GROUPS 512
+#define NVFP4_CJSO_GROUPS 256
 #endif
 #ifndef NVFP4_CJSO_DEPTH
 #define NVFP4_CJSO_DEPTH 1
+#endif
+#ifndef NVFP4_CJSO_WAVES
+#define NVFP4_CJSO_WAVES 4
+#endif
+// How a work-group's waves combine their double-double sums (see wg_sum_dd2): 0 through wave 0,
+// 1 per-wave first, 2 a tree across waves.
+#ifndef NVFP4_WG_SUM
+#define NVFP4_WG_SUM 2
 #endif
 // Size of the fixed device array behind nvfp4_quantize_noalloc (16 MiB).
 #ifndef NVFP4_NOALLOC_SCRATCH_BYTES

@@ -75,18 +75,58 @@ __device__ __forceinline__ uint32_t wg_max(uint32_t m) {
     return m;
 }
 
-// Work-group sum (T threads) of two double-doubles in a fixed order. Waves 1.. hand their lanes' values
-// to wave 0 through LDS; wave 0 adds them lane by lane and then reduces across its lanes, so only one
-// wave runs the long dependent chain of double-double additions. The result is valid in thread kSumLane.
+// Work-group sum (T threads) of two double-doubles in a fixed order, over the values of the first TA
+// threads (a multiple of 64; the other threads only take part in the barriers). The result is valid
+// in thread kSumLane. Schemes for combining the waves (NVFP4_WG_SUM): 0, waves 1.. hand their lanes'
+// values to wave 0 through LDS and wave 0 adds them lane by lane; 1, every wave reduces its own lanes
+// and wave 0 reduces their totals; 2, a tree across waves through LDS (the upper half of the remaining
+// waves hands its values to the lower half, once per level). Wave 0 then reduces across its lanes.
 constexpr int kSumLane = 63;
-template <int T>
+template <int T, int TA = T>
 __device__ __forceinline__ void wg_sum_dd2(dd &N, dd &D) {
-    constexpr int NW = T / 64;
-    static_assert(T % 64 == 0 && NW >= 1, "whole waves");
-    if constexpr (NW > 1) {
+    constexpr int NW = TA / 64;
+    static_assert(T % 64 == 0 && TA % 64 == 0 && NW >= 1 && TA <= T, "whole waves");
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    if constexpr (NW > 1 && NVFP4_WG_SUM == 1) {
+        __shared__ double tot[4][NW];  // [N.hi, N.lo, D.hi, D.lo][wave]
+        if (w < NW) {
+            wave_sum_dd2(N, D);
+            if (l == 63) {
+                tot[0][w] = N.hi;
+                tot[1][w] = N.lo;
+                tot[2][w] = D.hi;
+                tot[3][w] = D.lo;
+            }
+        }
+        lds_barrier();
+        if (w == 0) {
+            N = l < NW ? dd{tot[0][l], tot[1][l]} : dd{0.0, 0.0};
+            D = l < NW ? dd{tot[2][l], tot[3][l]} : dd{0.0, 0.0};
+            wave_sum_dd2(N, D);
+        }
+        return;
+    } else if constexpr (NW > 1 && NVFP4_WG_SUM == 2) {
+        static_assert((NW & (NW - 1)) == 0, "a power of two of waves");
+        __shared__ double buf[NW - 1][4][64];  // level with h waves receiving: rows h - 1 .. 2h - 2
+#pragma unroll
+        for (int h = NW / 2; h >= 1; h >>= 1) {
+            if (w >= h && w < 2 * h) {
+                double *r = &buf[h - 1 + (w - h)][0][0];
+                r[l] = N.hi;
+                r[64 + l] = N.lo;
+                r[128 + l] = D.hi;
+                r[192 + l] = D.lo;
+            }
+            lds_barrier();
+            if (w < h) {
+                const double *r = &buf[h - 1 + w][0][0];
+                N = dd_add(N, dd{r[l], r[64 + l]});
+                D = dd_add(D, dd{r[128 + l], r[192 + l]});
+            }
+        }
+    } else if constexpr (NW > 1) {
         __shared__ double buf[NW - 1][4][64];  // [wave - 1][N.hi, N.lo, D.hi, D.lo][lane]
-        const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-        if (w > 0) {
+        if (w > 0 && w < NW) {
             buf[w - 1][0][l] = N.hi;
             buf[w - 1][1][l] = N.lo;
             buf[w - 1][2][l] = D.hi;
@@ -101,7 +141,7 @@ __device__ __forceinline__ void wg_sum_dd2(dd &N, dd &D) {
             }
         }
     }
-    if (threadIdx.x < 64) wave_sum_dd2(N, D);
+    if (w == 0) wave_sum_dd2(N, D);
 }
 
 // A kernel's prologue reads the previous kernel's per-work-group partials. Each thread loads its share
@@ -149,7 +189,8 @@ struct CjsoShare {
             N = dd_add(N, dd{v[k][0], v[k][1]});
             D = dd_add(D, dd{v[k][2], v[k][3]});
         }
-        wg_sum_dd2<T>(N, D);
+        // only the first min(T, G) threads hold partials
+        wg_sum_dd2<T, (G < T ? (G + 63) / 64 * 64 : T)>(N, D);
         if (threadIdx.x == kSumLane) {
             tot[0] = N.hi;
             tot[1] = N.lo;
@@ -414,7 +455,7 @@ __global__ __launch_bounds__(kCountThreads) void k_count(const uint32_t *__restr
 // SOAR the E4M3 bracket of the unrounded block scale: max|w|/(6 alpha), or 1.5*Delta6 where FourOverSix
 // took M=4) are final.
 template <bool F32, bool SOAR, bool ROUNDS, bool FOS>
-__global__ __launch_bounds__(kCjsoThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_cjso_init(const void *__restrict__ W, int64_t nblk,
+__global__ __launch_bounds__(kCjsoThreads) __attribute__((amdgpu_waves_per_eu(NVFP4_CJSO_WAVES))) void k_cjso_init(const void *__restrict__ W, int64_t nblk,
                                                               const uint32_t *__restrict__ amax_part, int amax_n,
                                                               uint8_t *__restrict__ codes,
                                                               uint8_t *__restrict__ scales,
@@ -500,7 +541,7 @@ __global__ __launch_bounds__(kCjsoThreads) __attribute__((amdgpu_waves_per_eu(4)
 // page, block-scale closed form, rounded to E4M3), re-quantise; then the sums for round t+1, or, in the
 // last round (LAST), the codes (and for SOAR the E4M3 bracket of the unrounded block scale).
 template <bool F32, bool SOAR, bool LAST>
-__global__ __launch_bounds__(kCjsoThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_cjso_iter(const void *__restrict__ W, int64_t nblk, int t,
+__global__ __launch_bounds__(kCjsoThreads) __attribute__((amdgpu_waves_per_eu(NVFP4_CJSO_WAVES))) void k_cjso_iter(const void *__restrict__ W, int64_t nblk, int t,
                                                               const double *__restrict__ part_in, int n_part,
                                                               double *__restrict__ part_out, float *alpha_state,
                                                               float *__restrict__ alpha_out,
