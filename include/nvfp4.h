@@ -179,6 +179,14 @@ size_t nvfp4_workspace_bytes(int64_t rows, int64_t cols, int mode);
  * code 0). x and codes are device pointers; n <= 2^35 (else NVFP4_ERR_SHAPE). */
 int nvfp4_encode_e2m1(const float *x, int64_t n, uint8_t *codes, void *stream);
 
+/* The binary32 reciprocal the decoupled search uses for its quantisation scales (the candidates
+ * x = w * fl(1/s) of the SOAR page's decoupled search), element-wise: r[i] = fl(1/s[i]), the correctly
+ * rounded reciprocal for every input (for 2^-125 <= s < 2^125 it is computed from the hardware's
+ * approximate reciprocal and one residual correction; elsewhere by IEEE division). Exported so that the
+ * equality with IEEE division can be checked on the device. s and r are device pointers (4-byte
+ * aligned, may not overlap); n <= 2^35 (else NVFP4_ERR_SHAPE). */
+int nvfp4_reciprocal_f32(const float *s, int64_t n, float *r, void *stream);
+
 /* Dequantise codes/scales/alpha (device pointers, layout above; alpha is a device pointer to one
  * float) into out [rows][cols] as bf16 (out_dtype 0) or fp32 (out_dtype 1):
  * out = e2m1(code) * e4m3(scale) * alpha, rounded once to the output type (SOAR page, dequantisation

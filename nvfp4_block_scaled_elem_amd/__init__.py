@@ -78,6 +78,8 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_kernel_count.restype = i32
         L.nvfp4_encode_e2m1.argtypes = [vp, i64, vp, vp]
         L.nvfp4_encode_e2m1.restype = i32
+        L.nvfp4_reciprocal_f32.argtypes = [vp, i64, vp, vp]
+        L.nvfp4_reciprocal_f32.restype = i32
         L.nvfp4_dequantize.argtypes = [vp, vp, vp, i64, i64, vp, i32, vp]
         L.nvfp4_dequantize.restype = i32
         L.nvfp4_gptq.argtypes = [vp, i32, i64, i64, vp, ctypes.c_double, vp, vp, vp, vp, ctypes.c_size_t, vp]
@@ -261,6 +263,16 @@ def encode_e2m1(x: torch.Tensor, stream=None) -> torch.Tensor:
     with torch.cuda.device(x.device):
         _check(lib().nvfp4_encode_e2m1(x.data_ptr(), x.numel(), out.data_ptr(), _stream_ptr(stream, x.device)))
     return out.view(x.shape)
+
+
+def reciprocal_f32(s: torch.Tensor, stream=None) -> torch.Tensor:
+    """fl(1/s) element-wise by the reciprocal the search kernel uses (contiguous fp32 CUDA tensor)."""
+    if not s.is_cuda or s.dtype != torch.float32 or not s.is_contiguous():
+        raise NVFP4Error("s must be a contiguous fp32 CUDA tensor")
+    out = torch.empty_like(s)
+    with torch.cuda.device(s.device):
+        _check(lib().nvfp4_reciprocal_f32(s.data_ptr(), s.numel(), out.data_ptr(), _stream_ptr(stream, s.device)))
+    return out
 
 
 def dequantize(codes: torch.Tensor, scales: torch.Tensor, alpha: torch.Tensor, dtype=torch.bfloat16,

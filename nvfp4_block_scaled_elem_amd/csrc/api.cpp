@@ -184,6 +184,15 @@ NVFP4_API int nvfp4_encode_e2m1(const float *x, int64_t n, uint8_t *codes, void 
                                                                                                    : NVFP4_ERR_HIP;
 }
 
+NVFP4_API int nvfp4_reciprocal_f32(const float *s, int64_t n, float *r, void *stream) {
+    if (!s || !r || n < 0) return NVFP4_ERR_INVALID_ARG;
+    if (n > kMaxElems) return NVFP4_ERR_SHAPE;
+    if (((uintptr_t)s & 3u) != 0 || ((uintptr_t)r & 3u) != 0) return NVFP4_ERR_INVALID_ARG;
+    if (n == 0) return NVFP4_OK;
+    return nvfp4::launch_reciprocal(s, n, r, static_cast<hipStream_t>(stream)) == hipSuccess ? NVFP4_OK
+                                                                                           : NVFP4_ERR_HIP;
+}
+
 NVFP4_API int nvfp4_dequantize(const uint8_t *codes, const uint8_t *scales, const float *alpha, int64_t rows,
                                int64_t cols, void *out, int out_dtype, void *stream) {
     if (!codes || !scales || !alpha || !out || rows <= 0 || cols <= 0) return NVFP4_ERR_INVALID_ARG;

@@ -96,6 +96,22 @@ __device__ __forceinline__ uint32_t e2m1_soft(float x) {
     return (i != 0u && __builtin_signbit(x)) ? (i | 8u) : i;
 }
 
+// ------------------------------------------------------------------------------- reciprocal
+
+// fl(1/s), the correctly rounded binary32 reciprocal, for any s. For 2^-125 <= s < 2^125 it is formed
+// as y = v_rcp_f32(s) (about 1 ulp) plus one correction by the exact residual, y + y*(1 - s*y) with both
+// steps fused; that equals the IEEE quotient 1/s for every binary32 s in the range (checked on the
+// device for every binary32 value in [2^-125, 2^126), and by a GPU test through nvfp4_reciprocal_f32
+// over every mantissa at several exponents). Outside the range it is the IEEE division.
+// The range test is taken per wave (a ballot), so the common case is straight-line code.
+__device__ __forceinline__ float recip_rn(float s) {
+    const float y = __builtin_amdgcn_rcpf(s);
+    const float r = __builtin_fmaf(__builtin_fmaf(-s, y, 1.0f), y, y);
+    const bool fast = s >= 0x1p-125f && s < 0x1p125f;
+    if (__builtin_amdgcn_ballot_w64(!fast) != 0) return fast ? r : 1.0f / s;
+    return r;
+}
+
 // ------------------------------------------------------------------------ exact double-double
 
 struct dd {

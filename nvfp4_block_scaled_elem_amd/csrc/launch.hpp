@@ -95,6 +95,7 @@ hipError_t launch_soar(const void *W, bool f32, int64_t nblk, const float *alpha
                        const uint16_t *brackets, bool full_search, int num0, int den, int count, int rule,
                        hipStream_t stream);
 hipError_t launch_encode_e2m1(const float *x, int64_t n, uint8_t *codes, hipStream_t stream);
+hipError_t launch_reciprocal(const float *s, int64_t n, float *r, hipStream_t stream);
 // The W4A16 product's launch for given shapes: which kernel, its tile shape, the K split and the grid.
 enum { kW4a16Gemv = 0, kW4a16Skinny = 1, kW4a16Gemm = 2 };
 struct W4a16Plan {

@@ -925,6 +925,17 @@ hipError_t launch_encode_e2m1(const float *x, int64_t n, uint8_t *codes, hipStre
     return hipGetLastError();
 }
 
+// The reciprocal the search uses (recip_rn), element-wise; for the self-check entry point.
+__global__ __launch_bounds__(256) void k_reciprocal(const float *__restrict__ s, int64_t n, float *__restrict__ r) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) r[i] = recip_rn(s[i]);
+}
+
+hipError_t launch_reciprocal(const float *s, int64_t n, float *r, hipStream_t stream) {
+    hipLaunchKernelGGL(k_reciprocal, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, s, n, r);
+    return hipGetLastError();
+}
+
 size_t stats_workspace_bytes() {
     return align256(sizeof(double) * 2 * kStatMaxGroups) + align256(sizeof(uint32_t) * 16 * kStatMaxGroups);
 }

@@ -51,7 +51,7 @@ struct SearchCfg {
 __device__ __forceinline__ float quant_scale(float alpha, float vc, const float *ftab, int k) {
     return alpha * (vc * ftab[k]);
 }
-__device__ __forceinline__ float recip(float s) { return s == 0.0f ? 0.0f : 1.0f / s; }
+__device__ __forceinline__ float recip(float s) { return s == 0.0f ? 0.0f : recip_rn(s); }
 
 template <bool F32, bool FAST>
 __device__ __forceinline__ void block_sums_k(const Blk<F32> &B, float r, bool rfin, double &sw, double &sq) {
@@ -117,7 +117,7 @@ __device__ __forceinline__ double eval_r(const Blk<F32> &B, float r, double h, u
 
 template <bool F32>
 __device__ __forceinline__ double eval_s(const Blk<F32> &B, float s, double h, uint32_t &c0, uint32_t &c1) {
-    return eval_r<F32>(B, 1.0f / s, h, c0, c1);
+    return eval_r<F32>(B, recip_rn(s), h, c0, c1);
 }
 
 template <bool F32>
@@ -159,7 +159,7 @@ __device__ __forceinline__ int plateau_start(const Blk<F32> &B, float alpha, flo
     int k = kA;
     while (k > 0) {
         uint32_t d0, d1;
-        encode16(B.w, 1.0f / quant_scale(alpha, vc, ftab, k - 1), d0, d1);
+        encode16(B.w, recip_rn(quant_scale(alpha, vc, ftab, k - 1)), d0, d1);
         if (d0 != c0 || d1 != c1) break;
         --k;
     }
@@ -293,7 +293,7 @@ __global__ __launch_bounds__(kSoarThreads) void k_soar(const void *__restrict__ 
             // the incumbent
             const double sd_c = c_is_lo ? slo : shi, h_c = c_is_lo ? hlo : hhi;
             uint32_t i0, i1;
-            const float rc = 1.0f / sc;
+            const float rc = recip_rn(sc);
             a_c = eval_r(B, rc, h_c, i0, i1);
             const float vo = c_is_lo ? vhi : vlo;
             const double sd_o = c_is_lo ? shi : slo, h_o = c_is_lo ? hhi : hlo;

@@ -95,6 +95,10 @@ def test_plain_entry_points_reject(L):
     assert L.nvfp4_encode_e2m1(None, 10, FAKE, None) == INVALID
     assert L.nvfp4_encode_e2m1(FAKE, 10, FAKE + 1, None) == INVALID
     assert L.nvfp4_encode_e2m1(FAKE, 0, FAKE, None) == OK  # nothing to do
+    assert L.nvfp4_reciprocal_f32(None, 10, FAKE, None) == INVALID
+    assert L.nvfp4_reciprocal_f32(FAKE, 10, FAKE + 2, None) == INVALID
+    assert L.nvfp4_reciprocal_f32(FAKE, (1 << 35) + 1, FAKE, None) == SHAPE
+    assert L.nvfp4_reciprocal_f32(FAKE, 0, FAKE, None) == OK
     assert L.nvfp4_encode_e2m1(FAKE, (1 << 35) + 1, FAKE, None) == SHAPE
     assert L.nvfp4_dequantize(FAKE, FAKE, FAKE, 4, 24, FAKE, 0, None) == SHAPE
     assert L.nvfp4_dequantize(FAKE, FAKE, FAKE, 4, 32, FAKE, 3, None) == INVALID

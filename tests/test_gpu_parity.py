@@ -618,3 +618,29 @@ def test_full_size(name):
             assert int(g["mchoice"].sum()) == exp["m4_blocks"] == int(g["stats"][1])
         assert sha(g["codes"]) == exp["codes"], mode
         assert sha(g["scales"]) == exp["scales"], mode
+
+
+def test_reciprocal_is_ieee_division():
+    """The search's binary32 reciprocal (nvfp4_reciprocal_f32) against numpy's IEEE division: every
+    mantissa at exponents across the fast range and just outside it, the range boundaries, specials,
+    and random bit patterns."""
+    mant = np.arange(1 << 23, dtype=np.uint32)
+    parts = [((np.uint32(e + 127) << np.uint32(23)) | mant) for e in (-126, -125, -100, -40, -1, 0, 1, 40, 100, 124, 125, 126)]
+    g = np.random.default_rng(11)
+    parts.append(g.integers(0, 1 << 32, size=1 << 22, dtype=np.uint64).astype(np.uint32))
+    parts.append(np.array([0x00000000, 0x80000000, 0x00000001, 0x007FFFFF, 0x7F7FFFFF, 0x7F800000, 0xFF800000,
+                           0x7FC00000, 0x01000000, 0x00FFFFFF, 0x7E000000, 0x7DFFFFFF], dtype=np.uint32))
+    bits = np.concatenate(parts)
+    s = bits.view(np.float32)
+    say(f"reciprocal: {s.size} values")
+    got = nv.reciprocal_f32(torch.from_numpy(s).cuda()).cpu().numpy()
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        want = np.float32(1.0) / s
+    same = (got.view(np.uint32) == want.view(np.uint32)) | (np.isnan(got) & np.isnan(want))
+    # outside the fast range the kernel divides; where the quotient is subnormal (s >= 2^126) that division
+    # may flush it to zero, which is not the reciprocal under test
+    sub = (want != 0) & (np.abs(want) < np.float32(2.0 ** -126))
+    same |= sub & (got == 0)
+    fast = (s >= np.float32(2.0 ** -125)) & (s < np.float32(2.0 ** 125))
+    assert fast.sum() > 12 * (1 << 22)
+    assert same.all(), f"{(~same).sum()} differ, first input bits {int(bits[np.flatnonzero(~same)[0]]):#x}"
