@@ -80,8 +80,10 @@ enum nvfp4_error {
     NVFP4_ERR_SHAPE = -2,       /* cols % 16 != 0, or more than 2^35 elements */
     NVFP4_ERR_WORKSPACE = -3,   /* caller workspace smaller than nvfp4_workspace_bytes() */
     NVFP4_ERR_HIP = -4,         /* a HIP call failed */
-    NVFP4_ERR_TOO_LARGE = -5    /* nvfp4_quantize_noalloc: the call needs more scratch than its fixed
+    NVFP4_ERR_TOO_LARGE = -5,   /* nvfp4_quantize_noalloc: the call needs more scratch than its fixed
                                    device array holds */
+    NVFP4_ERR_UNSUPPORTED = -6  /* nvfp4_matmul / nvfp4_matmul_ex on a capturing stream with a shape
+                                   that takes the 128 x 128 or 256 x 128 output tiles */
 };
 
 /* In-band status bits, written to nvfp4_stats_t.status by the device. */
@@ -228,7 +230,12 @@ int nvfp4_matmul(const void *X, int64_t M, int64_t K, const uint8_t *codes, cons
  * nullable) of `workspace_bytes` >= nvfp4_matmul_workspace_bytes(M, K, N) bytes. With a workspace nothing
  * is allocated, so the call may be captured into a HIP graph as plain kernel nodes; the workspace must then
  * stay allocated while the graph may run. NULL behaves as nvfp4_matmul. NVFP4_ERR_WORKSPACE if it is too
- * small. Same arithmetic, layout and errors as nvfp4_matmul. */
+ * small. Same arithmetic, layout and errors as nvfp4_matmul.
+ * Stream capture: shapes whose plan takes the 128 x 128 or 256 x 128 output tiles (nvfp4_matmul_plan:
+ * kernel 2, tile columns 128) are refused on a capturing stream with NVFP4_ERR_UNSUPPORTED (nothing is
+ * enqueued): one graph-captured run of those forms ended in a device memory fault whose cause has not been
+ * found. The GEMV, the skinny kernel and the 128 x 64 tiles (with or without the K split) may be
+ * captured. Eager calls of every shape are unaffected. */
 int nvfp4_matmul_ex(const void *X, int64_t M, int64_t K, const uint8_t *codes, const uint8_t *scales,
                     const float *alpha, int64_t N, void *Y, int y_dtype, void *workspace, size_t workspace_bytes,
                     void *stream);

@@ -262,12 +262,19 @@ NVFP4_API int nvfp4_matmul_ex(const void *X, int64_t M, int64_t K, const uint8_t
     const int c = matmul_check(X, M, K, codes, scales, alpha, N, Y, y_dtype);
     if (c != NVFP4_OK) return c;
     if (workspace && ((uintptr_t)workspace & 255u) != 0) return NVFP4_ERR_INVALID_ARG;
-    const size_t need = nvfp4::plan_w4a16(M, K, N).part_bytes;
+    const nvfp4::W4a16Plan plan = nvfp4::plan_w4a16(M, K, N);
+    const size_t need = plan.part_bytes;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (workspace && need > 0 && workspace_bytes < need) return NVFP4_ERR_WORKSPACE;
+    if (plan.kind == nvfp4::kW4a16Gemm && plan.tn == 128) {
+        // The 128 x 128 and 256 x 128 tile forms are not run under stream capture (see the header).
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(st, &cs) != hipSuccess) return NVFP4_ERR_HIP;
+        if (cs != hipStreamCaptureStatusNone) return NVFP4_ERR_UNSUPPORTED;
+    }
     const bool f32 = y_dtype == NVFP4_DTYPE_F32;
     const uint16_t *x = static_cast<const uint16_t *>(X);
     if (need == 0 || workspace) {
-        if (need > 0 && workspace_bytes < need) return NVFP4_ERR_WORKSPACE;
         return nvfp4::launch_w4a16(x, M, K, codes, scales, alpha, N, Y, f32, static_cast<float *>(workspace), st) ==
                        hipSuccess
                    ? NVFP4_OK
@@ -337,6 +344,7 @@ NVFP4_API const char *nvfp4_status_string(int status) {
         case NVFP4_ERR_WORKSPACE: return "workspace too small";
         case NVFP4_ERR_HIP: return "HIP launch or allocation failed";
         case NVFP4_ERR_TOO_LARGE: return "the call needs more scratch than the library's fixed device array holds";
+        case NVFP4_ERR_UNSUPPORTED: return "not supported under stream capture for this shape (128 x 128 or 256 x 128 product tiles)";
         default: return "unknown status";
     }
 }

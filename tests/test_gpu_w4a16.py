@@ -155,6 +155,27 @@ def test_w4a16_graph_replays_match_eager_large_tiles():
     graph_replays_match_eager([(1, 1024), (1024, 1024), (2100, 128), (65536, 128)])
 
 
+@pytest.mark.parametrize("M,K", [(1024, 1024), (2100, 128), (65536, 128)])
+def test_w4a16_large_tiles_are_refused_under_capture(M, K):
+    """The 128 x 128 and 256 x 128 tile forms return NVFP4_ERR_UNSUPPORTED on a capturing stream and
+    enqueue nothing: no product runs here (these are the shapes of the skipped capture test, which also ran
+    them eagerly before it faulted)."""
+    n = 256
+    plan = nv.matmul_plan(M, K, n)
+    assert plan["kind"] == 2 and plan["tn"] == 128, plan
+    codes, scales, alpha = encoded_weights(n, K, 31)
+    X = bf16_dev(synth.normal_bf16(M, K, seed=5, std=1.0))
+    out = torch.empty((M, n), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(max(1, nv.matmul_workspace_bytes(M, K, n)), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        with pytest.raises(nv.NVFP4Error, match=r"\(-6\)"):
+            nv.matmul(X, codes, scales, alpha, out=out, workspace=ws)
+    del g
+    torch.cuda.synchronize()
+
+
 def test_w4a16_on_a_side_stream():
     n, k = 200, 512
     codes, scales, alpha = encoded_weights(n, k, 22)
