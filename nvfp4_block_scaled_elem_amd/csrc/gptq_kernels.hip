@@ -19,12 +19,14 @@
 // Kernels, all binary64:
 //   k_gptq_prep     dead inputs (zero diagonal) and the damping lambda = percdamp * mean(diag)
 //   k_gptq_reverse  A = P (H with dead diagonals 1, + lambda I) P, lower triangle
-//   k_chol_diag,    blocked right-looking Cholesky of A in place, panels of 64 columns: the diagonal
-//   k_chol_trsm,    block (one work-group, 4 x 4 register tiles), the rows below it (a wave per 16 rows), then
-//   k_chol_update   the trailing lower triangle (64 x 64 tiles on the fp64 matrix cores); the update's first
-//                   work-group also factors the next diagonal block, so only the first has its own launch
+//   k_chol_diag,    blocked Cholesky of A in place, panels of 64 columns: the diagonal block (one
+//   k_chol_trsm,    work-group, 4 x 4 register tiles), the rows below it (16 lanes per row), and the updates
+//   k_chol_update   (64 x 64 tiles on the fp64 matrix cores), delayed over groups of 4 panels: a panel's stripe
+//                   takes its group's earlier panels just before it is factored, the trailing triangle the whole
+//                   group after it; an update's first work-group also factors the diagonal block it completes,
+//                   so only the first has its own launch
 //   k_gptq_pack_v   V's diagonal 64 x 64 blocks, packed contiguously for the sweep
-//   k_gptq_cols     columns [b0, b0 + 64), a wave per 16 rows, in order (target, E2M1 code, error e_j),
+//   k_gptq_cols     columns [b0, b0 + 64), 16 lanes per row, in order (target, E2M1 code, error e_j),
 //                   each column's errors folded into the block's later columns at once
 //   k_gptq_update   S[:, k] += sum over a run of blocks of e_i V_ik for later columns k (fp64 matrix
 //                   cores, 64 x 64 tiles): after each block for the rest of its group of 4 blocks, after a
@@ -37,6 +39,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "codec.hpp"
 #include "launch.hpp"
@@ -70,35 +73,53 @@ __device__ __forceinline__ void load_tile(double *lds, const double *__restrict_
     }
 }
 
-// The same for a 64-thread work-group (one wave): all 64 loads of a lane issued before any is used.
-template <class Off, class Ok, class Fill>
-__device__ __forceinline__ void load_tile_wave(double *lds, const double *__restrict__ src, Off off, Ok ok,
-                                               Fill fill) {
-    const int c = threadIdx.x;
-    double v[kPanel];
-#pragma unroll
-    for (int r = 0; r < kPanel; ++r) v[r] = src[ok(r, c) ? off(r, c) : 0];
-#pragma unroll
-    for (int r = 0; r < kPanel; ++r) lds[r * kLd + c] = ok(r, c) ? v[r] : fill(r, c);
-}
-
-// x of lane k (0..3) of this lane's quad, by DPP quad_perm [k, k, k, k] (a few cycles; a shuffle goes
-// through the LDS crossbar). k must fold to a constant after unrolling.
-template <int Q>
-__device__ __forceinline__ double quad_bcast_k(double x) {
-    constexpr int ctrl = Q | (Q << 2) | (Q << 4) | (Q << 6);
+// x of lane N (0..15) of this lane's DPP row (16 lanes), by row_newbcast (gfx90a and later): a few cycles,
+// where a shuffle goes through the LDS crossbar. n must fold to a constant after unrolling.
+template <int N>
+__device__ __forceinline__ double row_bcast_k(double x) {
     const unsigned long long u = __double_as_longlong(x);
-    const int lo = __builtin_amdgcn_mov_dpp((int)(unsigned)u, ctrl, 0xF, 0xF, false);
-    const int hi = __builtin_amdgcn_mov_dpp((int)(unsigned)(u >> 32), ctrl, 0xF, 0xF, false);
+    const int lo = __builtin_amdgcn_mov_dpp((int)(unsigned)u, 0x150 + N, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_mov_dpp((int)(unsigned)(u >> 32), 0x150 + N, 0xF, 0xF, false);
     return __longlong_as_double(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
 }
-__device__ __forceinline__ double quad_bcast(double x, int k) {
-    switch (k) {
-        case 0: return quad_bcast_k<0>(x);
-        case 1: return quad_bcast_k<1>(x);
-        case 2: return quad_bcast_k<2>(x);
-        default: return quad_bcast_k<3>(x);
+__device__ __forceinline__ double row_bcast(double x, int n) {
+    switch (n) {
+        case 0: return row_bcast_k<0>(x);
+        case 1: return row_bcast_k<1>(x);
+        case 2: return row_bcast_k<2>(x);
+        case 3: return row_bcast_k<3>(x);
+        case 4: return row_bcast_k<4>(x);
+        case 5: return row_bcast_k<5>(x);
+        case 6: return row_bcast_k<6>(x);
+        case 7: return row_bcast_k<7>(x);
+        case 8: return row_bcast_k<8>(x);
+        case 9: return row_bcast_k<9>(x);
+        case 10: return row_bcast_k<10>(x);
+        case 11: return row_bcast_k<11>(x);
+        case 12: return row_bcast_k<12>(x);
+        case 13: return row_bcast_k<13>(x);
+        case 14: return row_bcast_k<14>(x);
+        default: return row_bcast_k<15>(x);
     }
+}
+
+// A 64 x 64 tile of doubles stored contiguously (row stride 64) into LDS with the same layout, by 256
+// threads in 16-byte pieces, all 8 loads of a thread issued before any store.
+__device__ __forceinline__ void copy_tile256(double *lds, const double *__restrict__ src) {
+    const double2 *s2 = reinterpret_cast<const double2 *>(src);
+    double2 *d2 = reinterpret_cast<double2 *>(lds);
+    double2 v[8];
+#pragma unroll
+    for (int it = 0; it < 8; ++it) v[it] = s2[threadIdx.x + 256 * it];
+#pragma unroll
+    for (int it = 0; it < 8; ++it) d2[threadIdx.x + 256 * it] = v[it];
+}
+
+// Entries 4 c .. 4 c + 3 of row j of a row-stride-64 LDS tile (two 16-byte reads).
+__device__ __forceinline__ void lds_row4(const double *T, int j, int c, double (&out)[4]) {
+    const double2 *p = reinterpret_cast<const double2 *>(T + j * kPanel + 4 * c);
+    const double2 a = p[0], b = p[1];
+    out[0] = a.x, out[1] = a.y, out[2] = b.x, out[3] = b.y;
 }
 
 typedef double f64x4 __attribute__((ext_vector_type(4)));
@@ -169,153 +190,223 @@ __global__ __launch_bounds__(256) void k_gptq_reverse(const double *__restrict__
     }
 }
 
-// Factors the diagonal block of panel [p0, p0 + nb) with the 256 threads of a work-group (padded to 64 with
-// an identity). T is the block's lower triangle in LDS (row stride kLd). Thread (tx, ty) = (tid / 16,
-// tid % 16) holds rows ty + 16u and columns tx + 16v (u, v < 4) in registers, so the 16 threads of a column
-// are lanes of one wave. Column c: its holders take the pivot from its lane by shuffle, scale the column
-// and publish it (a double-buffered LDS slot, one barrier); then every thread subtracts l_rc l_tc from its
-// entries in later columns. Entries above the diagonal are computed and discarded. The factor is written
-// back into A and, packed column-major with zeros above the diagonal, to Lp for the row solve. A pivot that
-// is not positive and finite sets *flag.
-__device__ __forceinline__ void chol_diag_block(const double *T, int nb, double *__restrict__ A, int64_t K,
+// x of lane `lane` (a constant after unrolling) in every lane.
+__device__ __forceinline__ double readlane_f64(double x, int lane) {
+    const unsigned long long u = __double_as_longlong(x);
+    const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)u, lane);
+    const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(u >> 32), lane);
+    return __longlong_as_double(((unsigned long long)hi << 32) | lo);
+}
+
+// 1 / sqrt(p): the hardware estimate and two Newton steps y += y (1 - p y^2) / 2, each doubling the correct bits.
+__device__ __forceinline__ double rsqrt_nr(double p) {
+    double y = __builtin_amdgcn_rsq(p);
+#pragma unroll
+    for (int it = 0; it < 2; ++it) y = fma(0.5 * y, fma(-(p * y), y, 1.0), y);
+    return y;
+}
+
+// 1 / p: the hardware estimate and two Newton steps y += y (1 - p y).
+__device__ __forceinline__ double rcp_nr(double p) {
+    double y = __builtin_amdgcn_rcp(p);
+#pragma unroll
+    for (int it = 0; it < 2; ++it) y = fma(y, fma(-p, y, 1.0), y);
+    return y;
+}
+
+// Factors the diagonal block of panel [p0, p0 + nb), held in T (LDS, row stride kLd, lower triangle), as
+// A = L~ D L~^T (then L = L~ D^(1/2)), so that the chain from one pivot to the next holds a reciprocal and no
+// square root. The 64 columns form 8 groups of 8; wave w holds groups w and w + 4, lane r the entries of row r
+// of the symmetric Schur complement S in those columns (padded to 64 with an identity). Group g: its wave runs
+// the 8 steps. Step c: the pivot p_c = S_cc comes from lane c by readlane, every lane takes m_r = S_rc / p_c and
+// subtracts m_r S_ck from its group's later columns k, S_ck read from lane c. The lanes r <= c take part
+// unmasked: what they change lies above their diagonal, which no later step reads, and a row's entries at and
+// below its diagonal are final once its own step is done (S_rc at step c, and p_r). The wave then publishes
+// S_rc and m_r of the group in LDS, and after a barrier every wave applies the rank-8 update to its later
+// groups, the next group first. At the end, L_rc = S_rc / sqrt(p_c) and L_rr = sqrt(p_r). The factor goes back
+// into T, then into A, and packed column-major with zeros above the diagonal into Lp for the row solve. A pivot
+// that is not positive and finite sets *flag. Called by all 256 threads of the work-group.
+constexpr int kPubDoubles = 4 * kPanel * 8;  // LDS the factorisation of a diagonal block publishes its groups in
+
+__device__ __forceinline__ void chol_diag_block(double *T, double *pub, int nb, double *__restrict__ A, int64_t K,
                                                 int64_t p0, double *__restrict__ Lp, int *__restrict__ flag) {
-    __shared__ double col[2][kPanel];
-    const int tid = threadIdx.x, tx = tid >> 4, ty = tid & 15;
-    double a[4][4];
+    constexpr int kG = 8;
+    // the published group, double-buffered by group parity: [buf][row][i] = S_(row, c0 + i), m_(row, i), in
+    // pub (kPubDoubles, 16-byte aligned)
+    double(*s_pub)[kPanel * kG] = reinterpret_cast<double(*)[kPanel * kG]>(pub);
+    double(*m_pub)[kPanel * kG] = reinterpret_cast<double(*)[kPanel * kG]>(pub + 2 * kPanel * kG);
+    const int r = threadIdx.x & 63, w = threadIdx.x >> 6;
+    double a[2][kG];  // groups w and w + 4
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int r = ty + 16 * u, t = tx + 16 * v;
-            a[u][v] = r < nb && t <= r ? T[r * kLd + t] : (r == t ? 1.0 : 0.0);
+        for (int i = 0; i < kG; ++i) {
+            const int k = kG * (w + 4 * j) + i;
+            const int hi = k > r ? k : r, lo = k > r ? r : k;  // the lower triangle, mirrored
+            a[j][i] = hi < nb ? T[hi * kLd + lo] : (r == k ? 1.0 : 0.0);
         }
     bool bad = false;
+    // Group g (a runtime index: one loop per slot J of the group in its wave, so the register arrays keep
+    // constant indices and each pass is one straight-line body).
+    const auto group = [&](int g, auto slot) {
+        constexpr int J = decltype(slot)::value;
+        if (w == g % 4) {
+            double mb[kG];
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
-        for (int cc = 0; cc < 16; ++cc) {
-            const int c = 16 * cb + cc;
-            // a_cc sits in thread (tx, ty) = (cc, cc), lane 16 (cc % 4) + cc of the column's wave
-            const double s = __shfl(a[cb][cb], 16 * (cc & 3) + cc);
-            if (tx == cc) {
-                if (ty == cc && (!(s > 0.0) || !(s < INFINITY))) bad = true;
-                const double d = sqrt(s);
+            for (int i = 0; i < kG; ++i) {
+                const int c = kG * g + i;
+                const double p = readlane_f64(a[J][i], c);  // the same in every lane
+                bad = bad || !(p > 0.0) || !(p < INFINITY);
+                const double m = a[J][i] * rcp_nr(p);
+                mb[i] = m;
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int r = ty + 16 * u;
-                    const double l = r == c ? d : a[u][cb] / d;  // l_rc below the diagonal
-                    a[u][cb] = l;
-                    col[c & 1][r] = l;
+                for (int i2 = i + 1; i2 < kG; ++i2) a[J][i2] = fma(-m, readlane_f64(a[J][i2], c), a[J][i2]);
+            }
+            double2 *ds = reinterpret_cast<double2 *>(s_pub[g & 1] + r * kG);
+            double2 *dm = reinterpret_cast<double2 *>(m_pub[g & 1] + r * kG);
+#pragma unroll
+            for (int i = 0; i < kG; i += 2) {
+                ds[i / 2] = make_double2(a[J][i], a[J][i + 1]);
+                dm[i / 2] = make_double2(mb[i], mb[i + 1]);
+            }
+        }
+        if (g + 1 == kPanel / kG) return;
+        __syncthreads();
+        // rank-8 update of this wave's later groups: slot 0 (group w) if w > g, slot 1 (group w + 4) if w + 4 > g
+        double mr[kG];
+        {
+            const double2 *sm = reinterpret_cast<const double2 *>(m_pub[g & 1] + r * kG);
+#pragma unroll
+            for (int i = 0; i < kG; i += 2) {
+                const double2 v = sm[i / 2];
+                mr[i] = v.x, mr[i + 1] = v.y;
+            }
+        }
+        const auto update = [&](double(&x)[kG], int k0) {
+#pragma unroll
+            for (int i2 = 0; i2 < kG; ++i2) {
+                const double2 *sk = reinterpret_cast<const double2 *>(s_pub[g & 1] + (k0 + i2) * kG);
+                double e = x[i2], o = 0.0;
+#pragma unroll
+                for (int i = 0; i < kG; i += 2) {
+                    const double2 v = sk[i / 2];
+                    e = fma(-mr[i], v.x, e);
+                    o = fma(-mr[i + 1], v.y, o);
                 }
+                x[i2] = e + o;
             }
-            __syncthreads();
-            const double *lc = col[c & 1];
-            double lr[4], lt[4];
+        };
+        if (J == 0 && w > g) update(a[0], kG * w);
+        if (w + 4 > g) update(a[1], kG * (w + 4));
+    };
+#pragma unroll 1
+    for (int g = 0; g < 4; ++g) group(g, std::integral_constant<int, 0>());
+#pragma unroll 1
+    for (int g = 4; g < kPanel / kG; ++g) group(g, std::integral_constant<int, 1>());
+    if (bad) flag[0] = 1;  // uniform within the wave that found it
 #pragma unroll
-            for (int u = 0; u < 4; ++u) lr[u] = lc[ty + 16 * u];
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) lt[v] = lc[tx + 16 * v];
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const double m = tx + 16 * v > c ? -lt[v] : 0.0;  // later columns only
-#pragma unroll
-                for (int u = 0; u < 4; ++u) a[u][v] = fma(m, lr[u], a[u][v]);
-            }
+        for (int i = 0; i < kG; ++i) {
+            const int c = kG * (w + 4 * j) + i;
+            const double p = readlane_f64(a[j][i], c);
+            const double y = rsqrt_nr(p);
+            const double v = c < r ? a[j][i] * y : (c == r ? p * y : 0.0);
+            T[r * kLd + c] = v;
+            Lp[c * kPanel + r] = v;  // lanes on consecutive addresses
         }
-    if (bad) flag[0] = 1;
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int r = ty + 16 * u, t = tx + 16 * v;
-            Lp[t * kPanel + r] = t <= r ? a[u][v] : 0.0;
-            if (r < nb && t <= r) A[(p0 + r) * K + p0 + t] = a[u][v];
-        }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < kPanel * kPanel; idx += 256) {
+        const int rr = idx >> 6, k = idx & 63;
+        if (rr < nb && k <= rr) A[(p0 + rr) * K + p0 + k] = T[rr * kLd + k];
+    }
 }
 
 // The first panel's diagonal block (later ones are factored by the trailing update before them).
 __global__ __launch_bounds__(256) void k_chol_diag(double *__restrict__ A, int64_t K, double *__restrict__ Lp,
                                                    int *__restrict__ flag) {
     __shared__ double T[kPanel * kLd];
+    __shared__ __align__(16) double pub[kPubDoubles];
     const int nb = (int)min<int64_t>(kPanel, K);
     load_tile(
         T, A, [&](int r, int c) { return (int64_t)r * K + c; }, [&](int r, int c) { return r < nb && c <= r; },
         [](int, int) { return 0.0; }, [](int r, int c) { return r * kLd + c; });
     __syncthreads();
-    chol_diag_block(T, nb, A, K, 0, Lp, flag);
+    chol_diag_block(T, pub, nb, A, K, 0, Lp, flag);
 }
 
-// Rows below the diagonal block of panel [p0, p0 + nb): L21 = A21 L11^-T. One wave per 16 rows: lane
-// (rr, cg) = (lane / 4, lane % 4) holds columns 16 cg .. 16 cg + 15 of row rr. Column c: its holders
-// divide by L_cc, the finished value goes to the row's other lanes (its quad) by DPP, and every lane
-// subtracts it from its later columns. No barriers after the load of L11 (packed by k_chol_diag).
-__global__ __launch_bounds__(64) void k_chol_trsm(double *__restrict__ A, int64_t K, int64_t p0,
-                                                  const double *__restrict__ Lp) {
-    __shared__ double L[kPanel * kLd];
+// Rows below the diagonal block of panel [p0, p0 + nb): L21 = A21 L11^-T, 16 rows per work-group. A row's 16
+// lanes form one DPP row; lane c holds columns 4 c .. 4 c + 3. Column t: its holder scales it by 1 / L_tt, the
+// finished value goes to the row's other lanes by DPP, and every lane subtracts it times L_kt from its
+// columns k > t. No barriers after the load of L11 (packed column-major by the diagonal factorisation).
+__global__ __launch_bounds__(256) void k_chol_trsm(double *__restrict__ A, int64_t K, int64_t p0,
+                                                   const double *__restrict__ Lp) {
+    __shared__ double LT[kPanel * kPanel];  // LT[t][k] = L_kt: zero above the diagonal, identity padding
+    copy_tile256(LT, Lp);
     const int nb = (int)min<int64_t>(kPanel, K - p0);
-    {  // L11 from its column-major copy: lane = row, each load 512 contiguous bytes
-        double v[kPanel];
-#pragma unroll
-        for (int c = 0; c < kPanel; ++c) v[c] = Lp[c * kPanel + threadIdx.x];
-#pragma unroll
-        for (int c = 0; c < kPanel; ++c) L[threadIdx.x * kLd + c] = v[c];
-    }
-    const int lane = threadIdx.x, rr = lane >> 2, cg = lane & 3;  // a row's four lanes form a quad
-    const int64_t row = p0 + nb + (int64_t)blockIdx.x * 16 + rr;
-    const bool in = row < K && 16 * cg < nb;  // nb % 16 == 0: a chunk is whole or absent
-    const double *src = A + (in ? row * K + p0 + 16 * cg : 0);
-    double x[16];
-#pragma unroll
-    for (int v = 0; v < 16; ++v) x[v] = src[v];
+    const int c = threadIdx.x & 15;
+    const int64_t row = p0 + nb + (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+    const bool in = row < K && 4 * c < nb;  // nb % 16 == 0: a lane's four columns are whole or absent
+    double2 *src = reinterpret_cast<double2 *>(A + (in ? row * K + p0 + 4 * c : 0));  // 32-byte aligned
+    const double2 x01 = src[0], x23 = src[1];
+    double x[4] = {x01.x, x01.y, x23.x, x23.y};
     __syncthreads();
-    __shared__ double rl[kPanel];  // 1 / L_cc, once per work-group, so no step waits for a division by it
-    rl[lane] = 1.0 / L[lane * kLd + lane];
-    __syncthreads();
+    double rl[4];  // 1 / L_kk of the lane's own columns, so no step waits for a division
 #pragma unroll
-    for (int cgs = 0; cgs < 4; ++cgs) {
-        if (16 * cgs >= nb) break;
+    for (int v = 0; v < 4; ++v) rl[v] = 1.0 / LT[(4 * c + v) * kPanel + 4 * c + v];
+    double l[4];
+    lds_row4(LT, 0, c, l);
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int c = 16 * cgs + v;
-            const double xv = x[v] * rl[c];
-            if (cg == cgs) x[v] = xv;
-            const double xc = quad_bcast(xv, cgs);
-            // unmasked (a zero multiplier leaves earlier columns exactly as they are), so the 16 LDS
-            // reads are issued together
+    for (int cb = 0; cb < 4; ++cb) {
+        if (16 * cb >= nb) break;
 #pragma unroll
-            for (int v2 = 0; v2 < 16; ++v2) {
-                const int k = 16 * cg + v2;
-                const double lkc = L[k * kLd + c];
-                x[v2] = fma(k > c ? -xc : 0.0, lkc, x[v2]);
-            }
+        for (int u = 0; u < 16; ++u) {
+            const int t = 16 * cb + u, h = t >> 2, v = t & 3;
+            double ln[4];  // the next column's entries, read ahead
+            lds_row4(LT, (t + 1) & 63, c, ln);
+            const double xv = x[v] * rl[v];  // final in the holder (h == c); discarded elsewhere
+            if (c == h) x[v] = xv;
+            const double xt = row_bcast(xv, h);
+            const double mlater = c > h ? -xt : 0.0, mfrom = c >= h ? -xt : 0.0;
+#pragma unroll
+            for (int v2 = 0; v2 < 4; ++v2) x[v2] = fma(v2 > v ? mfrom : mlater, l[v2], x[v2]);  // k = 4c + v2 > t
+#pragma unroll
+            for (int v2 = 0; v2 < 4; ++v2) l[v2] = ln[v2];
         }
     }
     if (in) {
-        double *dst = A + row * K + p0 + 16 * cg;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) dst[v] = x[v];
+        src[0] = make_double2(x[0], x[1]);
+        src[1] = make_double2(x[2], x[3]);
     }
 }
 
-// Trailing update after panel [p0, p1): A[i][j] -= sum_t A[i][p0+t] A[j][p0+t] for p1 <= j <= i < K.
-// 64 x 64 tiles of the lower triangle (tiles above it exit at once). Work-group (0, 0), dispatched first, holds
-// the next panel's diagonal block and goes on to factor it.
-__global__ __launch_bounds__(256) void k_chol_update(double *__restrict__ A, int64_t K, int64_t p0, int nb,
-                                                     double *__restrict__ Lp, int *__restrict__ flag) {
+// A[i][j] -= sum_{t in [s0, s0 + depth)} A[i][t] A[j][t] for o0 <= j <= i < K, in 64 x 64 tiles of the lower
+// triangle at (o0 + 64 y, o0 + 64 x) (tiles above it exit at once), the reduction in 64-deep steps on the fp64
+// matrix cores. Columns [s0, s0 + depth) are final factor columns. The grid's x extent bounds the columns: the
+// whole trailing triangle, or one stripe of 64. Work-group (0, 0), dispatched first, holds the diagonal block at
+// o0, which these columns complete, and goes on to factor it.
+__global__ __launch_bounds__(256) void k_chol_update(double *__restrict__ A, int64_t K, int64_t s0, int depth,
+                                                     int64_t o0, double *__restrict__ Lp, int *__restrict__ flag) {
     const int ti = blockIdx.y, tj = blockIdx.x;
     if (tj > ti) return;
-    __shared__ double Pi[kTile * kLd], Pj[kTile * kLd];
-    const int64_t p1 = p0 + nb, i0 = p1 + (int64_t)ti * kTile, j0 = p1 + (int64_t)tj * kTile;
+    __shared__ __align__(16) double Pi[kTile * kLd], Pj[kTile * kLd];
+    static_assert(kPubDoubles <= kTile * kLd, "the published groups reuse Pj");
+    const int64_t i0 = o0 + (int64_t)ti * kTile, j0 = o0 + (int64_t)tj * kTile;
     const auto zero = [](int, int) { return 0.0; };
     const auto at = [](int r, int t) { return r * kLd + t; };
-    load_tile(
-        Pi, A, [&](int r, int t) { return (i0 + r) * K + p0 + t; }, [&](int r, int t) { return i0 + r < K && t < nb; },
-        zero, at);
-    load_tile(
-        Pj, A, [&](int r, int t) { return (j0 + r) * K + p0 + t; }, [&](int r, int t) { return j0 + r < K && t < nb; },
-        zero, at);
-    __syncthreads();
     f64x4 acc[2][2] = {};
-    mfma_tile64(Pi, Pj, acc);
+    for (int d0 = 0; d0 < depth; d0 += kPanel) {
+        if (d0 > 0) __syncthreads();  // the previous step's reads are done
+        const int64_t c0 = s0 + d0;
+        load_tile(
+            Pi, A, [&](int r, int t) { return (i0 + r) * K + c0 + t; }, [&](int r, int) { return i0 + r < K; }, zero,
+            at);
+        load_tile(
+            Pj, A, [&](int r, int t) { return (j0 + r) * K + c0 + t; }, [&](int r, int) { return j0 + r < K; }, zero,
+            at);
+        __syncthreads();
+        mfma_tile64(Pi, Pj, acc);
+    }
     double old[2][2][4];  // all loads issued before the stores
 #pragma unroll
     for (int m = 0; m < 2; ++m)
@@ -336,7 +427,7 @@ __global__ __launch_bounds__(256) void k_chol_update(double *__restrict__ A, int
                 if (i < K && j <= i) A[i * K + j] = old[m][n][q] - acc[m][n][q];
             }
     if (ti == 0 && tj == 0) {
-        // this tile is the next panel's diagonal block, now final: factor it here, from LDS
+        // this tile is the diagonal block at o0, now final: factor it here, from LDS
         __syncthreads();  // every thread is done with Pi
 #pragma unroll
         for (int m = 0; m < 2; ++m)
@@ -345,7 +436,7 @@ __global__ __launch_bounds__(256) void k_chol_update(double *__restrict__ A, int
 #pragma unroll
                 for (int q = 0; q < 4; ++q) Pi[tile_row(m, q) * kLd + tile_col(n)] = old[m][n][q] - acc[m][n][q];
         __syncthreads();
-        chol_diag_block(Pi, (int)min<int64_t>(kPanel, K - p1), A, K, p1, Lp, flag);
+        chol_diag_block(Pi, Pj, (int)min<int64_t>(kPanel, K - o0), A, K, o0, Lp, flag);
     }
 }
 
@@ -364,107 +455,108 @@ __global__ __launch_bounds__(256) void k_gptq_pack_v(const double *__restrict__ 
     for (int idx = threadIdx.x; idx < kPanel * kPanel; idx += 256) dst[idx] = T[(idx >> 6) * kLd + (idx & 63)];
 }
 
-// E2M1 index of the nearest magnitude to a >= 0 (ties to the even index, 6 beyond 5).
-__device__ __forceinline__ uint32_t e2m1_index64(double a) {
-    return (uint32_t)(a > 0.25) + (a >= 0.75) + (a > 1.25) + (a >= 1.75) + (a > 2.5) + (a >= 3.5) + (a > 5.0);
-}
-
-// Columns [b0, b0 + nb), one wave per 16 rows. Lane (rr, cg) = (lane / 4, lane % 4) holds columns
-// b0 + 16 cg .. + 15 of row rr (one NVFP4 block, so one scale): their weights and running sums
-// acc = S + sum over the block's earlier columns of e_i V_ik. Column j: its holders turn their sum into the
-// target, code and error e_j; e_j reaches the row's other lanes (its quad) by DPP; every lane adds e_j V_jk
-// to its later columns. No barriers after the load of V.
+// Columns [b0, b0 + nb), 16 rows per work-group, in order. A row's 16 lanes form one DPP row; lane c holds
+// columns b0 + 4 c .. 4 c + 3 (a quarter of an NVFP4 block) with their weights and running sums
+// acc = S + sum over the panel's earlier columns of e_i V_ik. Column j: its holder forms the target
+// t = w + acc / V_jj, the code and the error e_j = w - q_j; e_j goes to the row's other lanes by DPP, and every
+// lane adds e_j V_jk to its columns. No barriers after the load of V.
+//
+// The code is the nearest E2M1 value to t / s, ties to the even index, s = fl32(alpha Delta) of the block. The
+// quotient is never formed: |t| is compared with the decision points times s, products that binary64 holds
+// exactly (three significant bits times a binary32 value), so each comparison is that of the exact t / s.
+// A block scale that is not positive (0, or NaN) gives code 0 and no dequantised value.
 template <bool F32>
-__global__ __launch_bounds__(64) void k_gptq_cols(const void *__restrict__ W, int64_t R, int64_t K, int64_t b0,
-                                                  int nb, const double *__restrict__ Vb,
-                                                  const uint8_t *__restrict__ dead,
-                                                  const uint8_t *__restrict__ scales,
-                                                  const float *__restrict__ alpha_p, const double *__restrict__ S,
-                                                  double *__restrict__ E, int ldE, int ecol0,
-                                                  uint8_t *__restrict__ codes) {
-    __shared__ double V[kPanel * kLd];  // V[i][j] = V_(b0+i, b0+j) for i <= j, identity padding
-    load_tile_wave(
-        V, Vb + (b0 / kPanel) * kPanel * kPanel, [](int i, int j) { return i * kPanel + j; },
-        [](int, int) { return true; }, [](int, int) { return 0.0; });
-    const int lane = threadIdx.x, rr = lane >> 2, cg = lane & 3;  // a row's four lanes form a quad
-    const int64_t row = (int64_t)blockIdx.x * 16 + rr;
-    const bool in = row < R && 16 * cg < nb;  // nb % 16 == 0: a chunk is whole or absent
-    const int64_t base = in ? row * K + b0 + 16 * cg : 0;  // element index, a multiple of 16
+__global__ __launch_bounds__(256) void k_gptq_cols(const void *__restrict__ W, int64_t R, int64_t K, int64_t b0,
+                                                   int nb, const double *__restrict__ Vb,
+                                                   const uint8_t *__restrict__ dead,
+                                                   const uint8_t *__restrict__ scales,
+                                                   const float *__restrict__ alpha_p, const double *__restrict__ S,
+                                                   double *__restrict__ E, int ldE, int ecol0,
+                                                   uint8_t *__restrict__ codes) {
+    __shared__ double V[kPanel * kPanel];  // V[i][k] = V_(b0+i, b0+k): zero below the diagonal, identity padding
+    copy_tile256(V, Vb + (b0 / kPanel) * kPanel * kPanel);
+    const int c = threadIdx.x & 15;
+    const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+    const bool in = row < R && 4 * c < nb;  // nb % 16 == 0: a lane's four columns are whole or absent
+    const int64_t base = in ? row * K + b0 + 4 * c : 0;  // element index, a multiple of 4
     // every load of the lane issued before any is used (masked lanes read element 0 and discard it)
-    double acc[16], w[16];
-    const double *sp = S + (b0 > 0 ? base : 0);
-#pragma unroll
-    for (int v = 0; v < 16; ++v) acc[v] = sp[v];
-    uint32_t wr[16];
+    const double2 *sp = reinterpret_cast<const double2 *>(S + (b0 > 0 ? base : 0));  // 32-byte aligned
+    const double2 s01 = sp[0], s23 = sp[1];
+    uint32_t wr[4];
     if (F32) {
-        const uint4 *wp = reinterpret_cast<const uint4 *>(static_cast<const float *>(W) + base);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const uint4 t = wp[q];
-            wr[4 * q] = t.x, wr[4 * q + 1] = t.y, wr[4 * q + 2] = t.z, wr[4 * q + 3] = t.w;
-        }
+        const uint4 t = *reinterpret_cast<const uint4 *>(static_cast<const float *>(W) + base);
+        wr[0] = t.x, wr[1] = t.y, wr[2] = t.z, wr[3] = t.w;
     } else {
-        const uint4 *wp = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(W) + base);
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const uint4 t = wp[q];
-            const uint32_t d[4] = {t.x, t.y, t.z, t.w};
-#pragma unroll
-            for (int h = 0; h < 4; ++h) wr[8 * q + 2 * h] = d[h] << 16, wr[8 * q + 2 * h + 1] = d[h] & 0xFFFF0000u;
-        }
+        const uint2 t = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(W) + base);
+        wr[0] = t.x << 16, wr[1] = t.x & 0xFFFF0000u, wr[2] = t.y << 16, wr[3] = t.y & 0xFFFF0000u;
     }
-    const uint4 dd = *reinterpret_cast<const uint4 *>(dead + (in ? b0 + 16 * cg : 0));
-    const uint32_t sb = scales[in ? base / 16 : 0];
+    const uint32_t dd = *reinterpret_cast<const uint32_t *>(dead + (in ? b0 + 4 * c : 0));
+    const uint32_t sb = scales[base / 16];
     const float alpha = *alpha_p;
-    const uint32_t dw[4] = {dd.x, dd.y, dd.z, dd.w};
+    const double sv[4] = {s01.x, s01.y, s23.x, s23.y};
+    double acc[4], w[4];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-        const bool isdead = ((dw[v / 4] >> (8 * (v % 4))) & 0xFFu) != 0;
-        acc[v] = in && b0 > 0 ? acc[v] : 0.0;
-        w[v] = in && !isdead ? (double)__uint_as_float(wr[v]) : 0.0;
+    for (int v = 0; v < 4; ++v) {
+        acc[v] = in && b0 > 0 ? sv[v] : 0.0;
+        w[v] = in && ((dd >> (8 * v)) & 0xFFu) == 0 ? (double)__uint_as_float(wr[v]) : 0.0;
     }
-    const double s = in ? (double)(alpha * e4m3_value(sb)) : 0.0;  // fl32(alpha Delta) of the lane's block
+    const double s = in ? (double)(alpha * e4m3_value(sb)) : 0.0;
+    const bool live = s > 0.0;
+    // decision points between E2M1 magnitudes k and k + 1, times s; ties go to the even index, so the
+    // comparison is > where k is even and >= where k is odd. Without a live scale they are NaN, so every
+    // comparison fails (code 0), and the half-step is 0 (no dequantised value).
+    const double sd = live ? s : __builtin_nan(""), hs = live ? 0.5 * s : 0.0;
+    const double d0 = 0.25 * sd, d1 = 0.75 * sd, d2 = 1.25 * sd, d3 = 1.75 * sd, d4 = 2.5 * sd, d5 = 3.5 * sd,
+                 d6 = 5.0 * sd;
     __syncthreads();
-    __shared__ double rv[kPanel];  // 1 / V_jj, once per work-group, so no step waits for a division by it
-    rv[lane] = 1.0 / V[lane * kLd + lane];
-    __syncthreads();
-    double ev[16] = {};
-    uint32_t packed[2] = {0u, 0u};
+    double rv[4];  // 1 / V_kk of the lane's own columns, so no step waits for a division
 #pragma unroll
-    for (int cgs = 0; cgs < 4; ++cgs) {
-        if (16 * cgs >= nb) break;
+    for (int v = 0; v < 4; ++v) rv[v] = 1.0 / V[(4 * c + v) * kPanel + 4 * c + v];
+    double ev[4] = {}, eg[4], vj[4];
+    uint32_t packed = 0u, cg[4];
+    lds_row4(V, 0, c, vj);
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int j = 16 * cgs + v;
-            // branch-free: a block scale that is not positive (s = 0, or NaN) gives code 0 and no dequantised value
-            const double t = w[v] + acc[v] * rv[j];
-            const bool live = s > 0.0;
-            const double x = t / (live ? s : 1.0);
-            const uint32_t idx = live ? e2m1_index64(fabs(x)) : 0u;
-            const bool neg = x < 0.0 && idx > 0;
-            const uint32_t code = idx | (neg ? 8u : 0u);
-            const double mag = idx < 4 ? 0.5 * idx : (idx == 7 ? 6.0 : (double)(idx - 2));
-            const double deq = live ? (neg ? -mag : mag) * s : 0.0;
-            const double e = w[v] - deq;
-            const bool own = cg == cgs;
-            ev[v] = own ? e : ev[v];
-            packed[v / 8] |= (own ? code : 0u) << (4 * (v % 8));
-            const double ej = quad_bcast(e, cgs);
-            // unmasked (a zero multiplier leaves earlier columns exactly as they are), so the 16 LDS
-            // reads are issued together
+    for (int cb = 0; cb < 4; ++cb) {
+        if (16 * cb >= nb) break;
 #pragma unroll
-            for (int v2 = 0; v2 < 16; ++v2) {
-                const int k = 16 * cg + v2;
-                const double vjk = V[j * kLd + k];
-                acc[v2] = fma(k > j ? ej : 0.0, vjk, acc[v2]);
+        for (int u = 0; u < 16; ++u) {
+            const int j = 16 * cb + u, h = j >> 2, v = j & 3;
+            double vn[4];  // the next column's row of V, read ahead of this column's arithmetic
+            lds_row4(V, (j + 1) & 63, c, vn);
+            // the holder's (h == c) column; other lanes' results are discarded
+            const double t = fma(acc[v], rv[v], w[v]);
+            const double a = fabs(t);
+            const uint32_t idx =
+                (uint32_t)(a > d0) + (a >= d1) + (a > d2) + (a >= d3) + (a > d4) + (a >= d5) + (a > d6);
+            // twice the magnitude: idx below 4, then 4, 6, 8, 12
+            const uint32_t m2 = idx + (max(idx, 4u) - 4u) + 2u * (max(idx, 6u) - 6u);
+            const uint32_t thi = (uint32_t)(__double_as_longlong(t) >> 32);
+            // the dequantised value carries t's sign (a zero one too, which leaves e = w)
+            const double q = __longlong_as_double(__double_as_longlong((double)m2 * hs) |
+                                                  ((long long)(thi & 0x80000000u) << 32));
+            eg[v] = w[v] - q;
+            cg[v] = idx | ((thi >> 28) & (idx + 7u) & 8u);  // the sign bit only with a nonzero magnitude
+            const double ej = row_bcast(eg[v], h);
+            // unmasked: V_jk = 0 below the diagonal, and a column's sum is not read after its own step
+#pragma unroll
+            for (int v2 = 0; v2 < 4; ++v2) acc[v2] = fma(ej, vj[v2], acc[v2]);
+#pragma unroll
+            for (int v2 = 0; v2 < 4; ++v2) vj[v2] = vn[v2];
+            if (v == 3) {  // the end of lane h's columns: keep them in the holder
+                const bool own = c == h;
+#pragma unroll
+                for (int v2 = 0; v2 < 4; ++v2) {
+                    ev[v2] = own ? eg[v2] : ev[v2];
+                    packed |= (own ? cg[v2] : 0u) << (4 * v2);
+                }
             }
         }
     }
     if (in) {
-        double *ep = E + row * ldE + ecol0 + 16 * cg;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) ep[v] = ev[v];
-        *reinterpret_cast<uint2 *>(codes + base / 2) = make_uint2(packed[0], packed[1]);  // 8-byte aligned
+        double2 *ep = reinterpret_cast<double2 *>(E + row * ldE + ecol0 + 4 * c);  // 32-byte aligned
+        ep[0] = make_double2(ev[0], ev[1]);
+        ep[1] = make_double2(ev[2], ev[3]);
+        *reinterpret_cast<uint16_t *>(codes + base / 2) = (uint16_t)packed;  // 2-byte aligned
     }
 }
 
@@ -566,14 +658,25 @@ hipError_t launch_gptq(const void *W, bool f32, int64_t R, int64_t K, const doub
     hipLaunchKernelGGL(k_gptq_prep, dim3(1), dim3(kPrepThreads), 0, stream, H, K, percdamp, damp, dead, flag);
     hipLaunchKernelGGL(k_gptq_reverse, dim3((unsigned)((K + 255) / 256), (unsigned)K), dim3(256), 0, stream, H, K,
                        damp, dead, A);
+    // Cholesky with the updates delayed over groups of 4 panels: within a group, a panel's column stripe takes
+    // the updates of the group's earlier panels just before it is factored; after the group, the rest of the
+    // trailing triangle takes the whole group's update at once (reduction depth 256).
     hipLaunchKernelGGL(k_chol_diag, dim3(1), dim3(256), 0, stream, A, K, Lp, flag);
-    for (int64_t p0 = 0; p0 < K; p0 += kPanel) {
-        const int nb = (int)std::min<int64_t>(kPanel, K - p0);
-        const int64_t below = K - p0 - nb;
-        if (below > 0) {
-            hipLaunchKernelGGL(k_chol_trsm, dim3((unsigned)((below + 15) / 16)), dim3(64), 0, stream, A, K, p0, Lp);
-            const unsigned t = (unsigned)((below + kTile - 1) / kTile);
-            hipLaunchKernelGGL(k_chol_update, dim3(t, t), dim3(256), 0, stream, A, K, p0, nb, Lp, flag);
+    for (int64_t g0 = 0; g0 < K; g0 += kSuper) {
+        const int64_t g1 = std::min<int64_t>(g0 + kSuper, K);
+        for (int64_t p0 = g0; p0 < g1; p0 += kPanel) {
+            if (p0 > g0)
+                hipLaunchKernelGGL(k_chol_update, dim3(1, (unsigned)((K - p0 + kTile - 1) / kTile)), dim3(256), 0,
+                                   stream, A, K, g0, (int)(p0 - g0), p0, Lp, flag);
+            const int64_t below = K - p0 - std::min<int64_t>(kPanel, K - p0);
+            if (below > 0)
+                hipLaunchKernelGGL(k_chol_trsm, dim3((unsigned)((below + 15) / 16)), dim3(256), 0, stream, A, K, p0,
+                                   Lp);
+        }
+        if (g1 < K) {
+            const unsigned t = (unsigned)((K - g1 + kTile - 1) / kTile);
+            hipLaunchKernelGGL(k_chol_update, dim3(t, t), dim3(256), 0, stream, A, K, g0, (int)(g1 - g0), g1, Lp,
+                               flag);
         }
     }
     hipLaunchKernelGGL(k_gptq_pack_v, dim3((unsigned)nblocks), dim3(256), 0, stream, A, K, Vb);
@@ -586,10 +689,10 @@ hipError_t launch_gptq(const void *W, bool f32, int64_t R, int64_t K, const doub
         const int64_t sb0 = b0 / kSuper * kSuper, sb1 = std::min<int64_t>(sb0 + kSuper, K), b1 = b0 + nb;
         const dim3 grid((unsigned)((R + 15) / 16));
         if (f32)
-            hipLaunchKernelGGL(k_gptq_cols<true>, grid, dim3(64), 0, stream, W, R, K, b0, nb, Vb, dead, scales, alpha,
+            hipLaunchKernelGGL(k_gptq_cols<true>, grid, dim3(256), 0, stream, W, R, K, b0, nb, Vb, dead, scales, alpha,
                                S, E, kSuper, (int)(b0 - sb0), codes);
         else
-            hipLaunchKernelGGL(k_gptq_cols<false>, grid, dim3(64), 0, stream, W, R, K, b0, nb, Vb, dead, scales, alpha,
+            hipLaunchKernelGGL(k_gptq_cols<false>, grid, dim3(256), 0, stream, W, R, K, b0, nb, Vb, dead, scales, alpha,
                                S, E, kSuper, (int)(b0 - sb0), codes);
         if (b1 < sb1)
             hipLaunchKernelGGL(k_gptq_update, dim3((unsigned)((sb1 - b1 + kTile - 1) / kTile), row_tiles), dim3(256), 0,
