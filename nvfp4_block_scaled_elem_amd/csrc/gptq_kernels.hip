@@ -25,15 +25,16 @@
 //                   takes its group's earlier panels just before it is factored, the trailing triangle the whole
 //                   group after it; an update's first work-group also factors the diagonal block it completes,
 //                   so only the first has its own launch
-//   k_gptq_pack_v   V's diagonal 64 x 64 blocks, packed contiguously for the sweep
+//   k_gptq_pack_v   the 64 x 64 blocks of V the sweep reads (each column block's diagonal block and the
+//                   blocks above it within its group), packed contiguously
 //   k_gptq_cols     columns [b0, b0 + 64), 16 lanes per row, in order (target, E2M1 code, error e_j),
 //                   each column's errors folded into the block's later columns at once
-//   k_gptq_update   S[:, k] += sum over a run of blocks of e_i V_ik for later columns k (fp64 matrix
-//                   cores, 64 x 64 tiles): after each block for the rest of its group of 4 blocks, after a
-//                   group for every column beyond it
+//   k_gptq_update   after each group of 4 blocks, S[:, k] += sum over the group of e_i V_ik for every
+//                   column k beyond it (fp64 matrix cores, 64 x 64 tiles); within a group, the sweep adds the
+//                   group's earlier blocks itself
 //   k_gptq_finish   a failed factorisation (a pivot that is not positive and finite): alpha = NaN, codes 0
-// S holds sum_{i<b0} e_i V_ik for the columns not yet reached. The updates whose reduction starts at column 0
-// write it, so it needs no clearing.
+// S holds sum_{i<g0} e_i V_ik for the columns not yet reached, g0 the start of the current group. The update
+// after the first group writes it, so it needs no clearing.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -248,6 +249,28 @@ __device__ __forceinline__ void chol_diag_block(double *T, double *pub, int nb, 
     bool bad = false;
     // Group g (a runtime index: one loop per slot J of the group in its wave, so the register arrays keep
     // constant indices and each pass is one straight-line body).
+    // A rank-8 update of columns [k0, k0 + 8) of this wave with group g's published values.
+    const auto update = [&](double(&x)[kG], int k0, int g) {
+        double mr[kG];
+        const double2 *sm = reinterpret_cast<const double2 *>(m_pub[g & 1] + r * kG);
+#pragma unroll
+        for (int i = 0; i < kG; i += 2) {
+            const double2 v = sm[i / 2];
+            mr[i] = v.x, mr[i + 1] = v.y;
+        }
+#pragma unroll
+        for (int i2 = 0; i2 < kG; ++i2) {
+            const double2 *sk = reinterpret_cast<const double2 *>(s_pub[g & 1] + (k0 + i2) * kG);
+            double e = x[i2], o = 0.0;
+#pragma unroll
+            for (int i = 0; i < kG; i += 2) {
+                const double2 v = sk[i / 2];
+                e = fma(-mr[i], v.x, e);
+                o = fma(-mr[i + 1], v.y, o);
+            }
+            x[i2] = e + o;
+        }
+    };
     const auto group = [&](int g, auto slot) {
         constexpr int J = decltype(slot)::value;
         if (w == g % 4) {
@@ -269,35 +292,17 @@ __device__ __forceinline__ void chol_diag_block(double *T, double *pub, int nb, 
                 ds[i / 2] = make_double2(a[J][i], a[J][i + 1]);
                 dm[i / 2] = make_double2(mb[i], mb[i + 1]);
             }
+            // the owner's slot-1 update with the previous group, left until now (its values stay published
+            // until the barrier after this group)
+            if (J == 0 && g > 0) update(a[1], kG * (w + 4), g - 1);
         }
         if (g + 1 == kPanel / kG) return;
         __syncthreads();
-        // rank-8 update of this wave's later groups: slot 0 (group w) if w > g, slot 1 (group w + 4) if w + 4 > g
-        double mr[kG];
-        {
-            const double2 *sm = reinterpret_cast<const double2 *>(m_pub[g & 1] + r * kG);
-#pragma unroll
-            for (int i = 0; i < kG; i += 2) {
-                const double2 v = sm[i / 2];
-                mr[i] = v.x, mr[i + 1] = v.y;
-            }
-        }
-        const auto update = [&](double(&x)[kG], int k0) {
-#pragma unroll
-            for (int i2 = 0; i2 < kG; ++i2) {
-                const double2 *sk = reinterpret_cast<const double2 *>(s_pub[g & 1] + (k0 + i2) * kG);
-                double e = x[i2], o = 0.0;
-#pragma unroll
-                for (int i = 0; i < kG; i += 2) {
-                    const double2 v = sk[i / 2];
-                    e = fma(-mr[i], v.x, e);
-                    o = fma(-mr[i + 1], v.y, o);
-                }
-                x[i2] = e + o;
-            }
-        };
-        if (J == 0 && w > g) update(a[0], kG * w);
-        if (w + 4 > g) update(a[1], kG * (w + 4));
+        // rank-8 update of this wave's later groups: slot 0 (group w) if w > g, slot 1 (group w + 4) if
+        // w + 4 > g. The next group's wave updates that group only, runs its steps first, and then the rest.
+        const bool next_owner = w == (g + 1) % 4;
+        if (J == 0 && w > g) update(a[0], kG * w, g);
+        if (w + 4 > g && !(next_owner && J == 0 && w > g)) update(a[1], kG * (w + 4), g);
     };
 #pragma unroll 1
     for (int g = 0; g < 4; ++g) group(g, std::integral_constant<int, 0>());
@@ -440,24 +445,32 @@ __global__ __launch_bounds__(256) void k_chol_update(double *__restrict__ A, int
     }
 }
 
-// The diagonal 64 x 64 blocks of V, packed contiguously for the column sweep: Vb[b][i][j] = V_(64b+i, 64b+j)
-// for i <= j < nb, identity padding, zeros below the diagonal. One work-group per block.
+// The 64 x 64 blocks of V the column sweep reads, packed contiguously: for column block b (columns
+// [64 b, 64 b + 64)) at position q in its group of 4, slot t <= q holds V_(64 (b - q + t) + i, 64 b + k): the
+// group's earlier blocks (t < q) whole, the diagonal block (t = q) for i <= k with identity padding and zeros
+// below. Columns beyond K are zero. One work-group per (block, slot).
 __global__ __launch_bounds__(256) void k_gptq_pack_v(const double *__restrict__ A, int64_t K, double *__restrict__ Vb) {
     __shared__ double T[kPanel * kLd];
     const int64_t b0 = (int64_t)blockIdx.x * kPanel;
+    const int t = blockIdx.y, q = (int)((b0 % kSuper) / kPanel);
+    if (t > q) return;
+    const int64_t pb = b0 - (int64_t)(q - t) * kPanel;  // the slot's first row of V
     const int nb = (int)min<int64_t>(kPanel, K - b0);
+    const bool diag = t == q;
     load_tile(
-        T, A, [&](int i, int j) { return (K - 1 - b0 - i) * K + (K - 1 - b0 - j); },
-        [&](int i, int j) { return j < nb && i <= j; }, [](int i, int j) { return i == j ? 1.0 : 0.0; },
-        [](int i, int j) { return i * kLd + j; });
+        T, A, [&](int i, int j) { return (K - 1 - pb - i) * K + (K - 1 - b0 - j); },
+        [&](int i, int j) { return j < nb && (!diag || i <= j); },
+        [&](int i, int j) { return diag && i == j ? 1.0 : 0.0; }, [](int i, int j) { return i * kLd + j; });
     __syncthreads();
-    double *dst = Vb + b0 * kPanel;
+    double *dst = Vb + ((int64_t)blockIdx.x * 4 + t) * kPanel * kPanel;
     for (int idx = threadIdx.x; idx < kPanel * kPanel; idx += 256) dst[idx] = T[(idx >> 6) * kLd + (idx & 63)];
 }
 
 // Columns [b0, b0 + nb), 16 rows per work-group, in order. A row's 16 lanes form one DPP row; lane c holds
 // columns b0 + 4 c .. 4 c + 3 (a quarter of an NVFP4 block) with their weights and running sums
-// acc = S + sum over the panel's earlier columns of e_i V_ik. Column j: its holder forms the target
+// acc = S + sum over the earlier columns of the group of 4 blocks of e_i V_ik (S holds the groups before; the
+// group's earlier blocks are added here, each 64 x 64 block of V staged in LDS, the errors of a row going to
+// its lanes by DPP) + sum over the panel's earlier columns of e_i V_ik. Column j: its holder forms the target
 // t = w + acc / V_jj, the code and the error e_j = w - q_j; e_j goes to the row's other lanes by DPP, and every
 // lane adds e_j V_jk to its columns. No barriers after the load of V.
 //
@@ -473,14 +486,14 @@ __global__ __launch_bounds__(256) void k_gptq_cols(const void *__restrict__ W, i
                                                    const float *__restrict__ alpha_p, const double *__restrict__ S,
                                                    double *__restrict__ E, int ldE, int ecol0,
                                                    uint8_t *__restrict__ codes) {
-    __shared__ double V[kPanel * kPanel];  // V[i][k] = V_(b0+i, b0+k): zero below the diagonal, identity padding
-    copy_tile256(V, Vb + (b0 / kPanel) * kPanel * kPanel);
+    __shared__ __align__(16) double V[kPanel * kPanel];  // a 64 x 64 block of V, row stride 64
     const int c = threadIdx.x & 15;
     const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
     const bool in = row < R && 4 * c < nb;  // nb % 16 == 0: a lane's four columns are whole or absent
     const int64_t base = in ? row * K + b0 + 4 * c : 0;  // element index, a multiple of 4
+    const int64_t sb0 = b0 / kSuper * kSuper;           // the group's first column
     // every load of the lane issued before any is used (masked lanes read element 0 and discard it)
-    const double2 *sp = reinterpret_cast<const double2 *>(S + (b0 > 0 ? base : 0));  // 32-byte aligned
+    const double2 *sp = reinterpret_cast<const double2 *>(S + (sb0 > 0 ? base : 0));  // 32-byte aligned
     const double2 s01 = sp[0], s23 = sp[1];
     uint32_t wr[4];
     if (F32) {
@@ -497,9 +510,42 @@ __global__ __launch_bounds__(256) void k_gptq_cols(const void *__restrict__ W, i
     double acc[4], w[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-        acc[v] = in && b0 > 0 ? sv[v] : 0.0;
+        acc[v] = in && sb0 > 0 ? sv[v] : 0.0;
         w[v] = in && ((dd >> (8 * v)) & 0xFFu) == 0 ? (double)__uint_as_float(wr[v]) : 0.0;
     }
+    // the group's earlier blocks: acc_k += sum_i e_i V_ik, i over block [pb, pb + 64), from the packed slots
+    // of this column block (slot q, the last, is the diagonal block)
+    const int q = (int)((b0 - sb0) / kPanel);
+    const double *vt = Vb + (b0 / kPanel) * 4 * kPanel * kPanel;
+    for (int t = 0; t < q; ++t) {
+        // (the earlier blocks are whole: every lane of a row in range holds four of their errors)
+        const double2 *ep = reinterpret_cast<const double2 *>(E + (row < R ? row * ldE + kPanel * t + 4 * c : 0));
+        const double2 e01 = ep[0], e23 = ep[1];
+        if (t > 0) __syncthreads();  // the previous slot's reads are done
+        copy_tile256(V, vt + t * kPanel * kPanel);
+        __syncthreads();
+        const double ee[4] = {e01.x, e01.y, e23.x, e23.y};  // the row's errors in block columns 4c .. 4c + 3
+        // rows of V read two steps ahead of their use; two sums per column, so a step does not wait for the last
+        double vr[3][4], acc2[4] = {0.0, 0.0, 0.0, 0.0};
+        lds_row4(V, 0, c, vr[0]);
+        lds_row4(V, 1, c, vr[1]);
+#pragma unroll
+        for (int i = 0; i < kPanel; ++i) {
+            if (i + 2 < kPanel) lds_row4(V, i + 2, c, vr[(i + 2) % 3]);
+            const double ei = row_bcast(ee[i & 3], i >> 2);
+#pragma unroll
+            for (int v2 = 0; v2 < 4; ++v2) {
+                if (i & 1)
+                    acc2[v2] = fma(ei, vr[i % 3][v2], acc2[v2]);
+                else
+                    acc[v2] = fma(ei, vr[i % 3][v2], acc[v2]);
+            }
+        }
+#pragma unroll
+        for (int v2 = 0; v2 < 4; ++v2) acc[v2] += acc2[v2];
+    }
+    if (q > 0) __syncthreads();  // done with the last earlier slot
+    copy_tile256(V, vt + q * kPanel * kPanel);  // the diagonal block
     const double s = in ? (double)(alpha * e4m3_value(sb)) : 0.0;
     const bool live = s > 0.0;
     // decision points between E2M1 magnitudes k and k + 1, times s; ties go to the even index, so the
@@ -620,7 +666,7 @@ size_t gptq_workspace_bytes(int64_t R, int64_t K) {
     auto up = [](size_t b) { return (b + 255) / 256 * 256; };
     const size_t nblocks = (size_t)(K + kPanel - 1) / kPanel;
     return up((size_t)K * K * 8) + up((size_t)R * K * 8) + up((size_t)R * kSuper * 8) +
-           up(nblocks * kPanel * kPanel * 8) + up((size_t)kPanel * kPanel * 8) + up((size_t)K) + 256 +
+           up(nblocks * 4 * kPanel * kPanel * 8) + up((size_t)kPanel * kPanel * 8) + up((size_t)K) + 256 +
            workspace_bytes(R * K / 16, NVFP4_MODE_FOUR_OVER_SIX);
 }
 
@@ -636,7 +682,7 @@ hipError_t launch_gptq(const void *W, bool f32, int64_t R, int64_t K, const doub
     p += up((size_t)R * kSuper * 8);
     const int64_t nblocks = (K + kPanel - 1) / kPanel;
     double *Vb = reinterpret_cast<double *>(p);
-    p += up((size_t)nblocks * kPanel * kPanel * 8);
+    p += up((size_t)nblocks * 4 * kPanel * kPanel * 8);
     double *Lp = reinterpret_cast<double *>(p);
     p += up((size_t)kPanel * kPanel * 8);
     uint8_t *dead = reinterpret_cast<uint8_t *>(p);
@@ -679,25 +725,22 @@ hipError_t launch_gptq(const void *W, bool f32, int64_t R, int64_t K, const doub
                                flag);
         }
     }
-    hipLaunchKernelGGL(k_gptq_pack_v, dim3((unsigned)nblocks), dim3(256), 0, stream, A, K, Vb);
-    // Column blocks of 64, grouped by 4 (the last group may be shorter). E holds the group's errors. After a
-    // block, S is updated only for the rest of its group; after the group's last block, for every later
-    // column at once, with the group's whole error block as the reduction.
+    hipLaunchKernelGGL(k_gptq_pack_v, dim3((unsigned)nblocks, 4), dim3(256), 0, stream, A, K, Vb);
+    // Column blocks of 64, grouped by 4 (the last group may be shorter). E holds the group's errors. Within a
+    // group, each block's sweep adds the group's earlier blocks to its sums itself; after the group's last
+    // block, S takes every later column at once, with the group's whole error block as the reduction.
     const unsigned row_tiles = (unsigned)((R + kTile - 1) / kTile);
     for (int64_t b0 = 0; b0 < K; b0 += kPanel) {
         const int nb = (int)std::min<int64_t>(kPanel, K - b0);
         const int64_t sb0 = b0 / kSuper * kSuper, sb1 = std::min<int64_t>(sb0 + kSuper, K), b1 = b0 + nb;
         const dim3 grid((unsigned)((R + 15) / 16));
         if (f32)
-            hipLaunchKernelGGL(k_gptq_cols<true>, grid, dim3(256), 0, stream, W, R, K, b0, nb, Vb, dead, scales, alpha,
-                               S, E, kSuper, (int)(b0 - sb0), codes);
+            hipLaunchKernelGGL(k_gptq_cols<true>, grid, dim3(256), 0, stream, W, R, K, b0, nb, Vb, dead, scales,
+                               alpha, S, E, kSuper, (int)(b0 - sb0), codes);
         else
-            hipLaunchKernelGGL(k_gptq_cols<false>, grid, dim3(256), 0, stream, W, R, K, b0, nb, Vb, dead, scales, alpha,
-                               S, E, kSuper, (int)(b0 - sb0), codes);
-        if (b1 < sb1)
-            hipLaunchKernelGGL(k_gptq_update, dim3((unsigned)((sb1 - b1 + kTile - 1) / kTile), row_tiles), dim3(256), 0,
-                               stream, E, kSuper, (int)(b0 - sb0), A, S, R, K, b0, nb, b1, sb1);
-        else if (sb1 < K)
+            hipLaunchKernelGGL(k_gptq_cols<false>, grid, dim3(256), 0, stream, W, R, K, b0, nb, Vb, dead, scales,
+                               alpha, S, E, kSuper, (int)(b0 - sb0), codes);
+        if (b1 == sb1 && sb1 < K)
             hipLaunchKernelGGL(k_gptq_update, dim3((unsigned)((K - sb1 + kTile - 1) / kTile), row_tiles), dim3(256), 0,
                                stream, E, kSuper, 0, A, S, R, K, sb0, (int)(sb1 - sb0), sb1, K);
     }
