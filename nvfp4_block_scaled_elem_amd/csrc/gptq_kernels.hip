@@ -74,6 +74,25 @@ __device__ __forceinline__ void load_tile(double *lds, const double *__restrict_
     }
 }
 
+// load_tile in two halves, so that the next tile's global loads can be in flight while the current one is
+// used: fetch_tile issues the 16 loads of a thread, put_tile stores them.
+template <class Off, class Ok>
+__device__ __forceinline__ void fetch_tile(double (&v)[16], const double *__restrict__ src, Off off, Ok ok) {
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+        const int idx = threadIdx.x + 256 * it, r = idx >> 6, c = idx & 63;
+        v[it] = src[ok(r, c) ? off(r, c) : 0];
+    }
+}
+template <class Ok, class Pos>
+__device__ __forceinline__ void put_tile(double *lds, const double (&v)[16], Ok ok, Pos pos) {
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+        const int idx = threadIdx.x + 256 * it, r = idx >> 6, c = idx & 63;
+        lds[pos(r, c)] = ok(r, c) ? v[it] : 0.0;
+    }
+}
+
 // x of lane N (0..15) of this lane's DPP row (16 lanes), by row_newbcast (gfx90a and later): a few cycles,
 // where a shuffle goes through the LDS crossbar. n must fold to a constant after unrolling.
 template <int N>
@@ -217,29 +236,31 @@ __device__ __forceinline__ double rcp_nr(double p) {
 
 // Factors the diagonal block of panel [p0, p0 + nb), held in T (LDS, row stride kLd, lower triangle), as
 // A = L~ D L~^T (then L = L~ D^(1/2)), so that the chain from one pivot to the next holds a reciprocal and no
-// square root. The 64 columns form 8 groups of 8; wave w holds groups w and w + 4, lane r the entries of row r
+// square root. The 64 columns form groups of kG; wave w holds groups w, w + 4, ..., lane r the entries of row r
 // of the symmetric Schur complement S in those columns (padded to 64 with an identity). Group g: its wave runs
-// the 8 steps. Step c: the pivot p_c = S_cc comes from lane c by readlane, every lane takes m_r = S_rc / p_c and
+// the kG steps. Step c: the pivot p_c = S_cc comes from lane c by readlane, every lane takes m_r = S_rc / p_c and
 // subtracts m_r S_ck from its group's later columns k, S_ck read from lane c. The lanes r <= c take part
 // unmasked: what they change lies above their diagonal, which no later step reads, and a row's entries at and
 // below its diagonal are final once its own step is done (S_rc at step c, and p_r). The wave then publishes
-// S_rc and m_r of the group in LDS, and after a barrier every wave applies the rank-8 update to its later
-// groups, the next group first. At the end, L_rc = S_rc / sqrt(p_c) and L_rr = sqrt(p_r). The factor goes back
-// into T, then into A, and packed column-major with zeros above the diagonal into Lp for the row solve. A pivot
-// that is not positive and finite sets *flag. Called by all 256 threads of the work-group.
+// S_rc and m_r of the group in LDS, and after a barrier every wave applies the rank-kG update to its later
+// groups; the next group's wave updates that group first and the rest after its steps. At the end,
+// L_rc = S_rc / sqrt(p_c) and L_rr = sqrt(p_r). The factor goes back into T, then into A, and packed
+// column-major with zeros above the diagonal into Lp for the row solve. A pivot that is not positive and finite
+// sets *flag. Called by all 256 threads of the work-group; pub is LDS that the caller no longer needs.
 constexpr int kPubDoubles = 4 * kPanel * 8;  // LDS the factorisation of a diagonal block publishes its groups in
 
-__device__ __forceinline__ void chol_diag_block(double *T, double *pub, int nb, double *__restrict__ A, int64_t K,
-                                                int64_t p0, double *__restrict__ Lp, int *__restrict__ flag) {
-    constexpr int kG = 8;
+template <int kG>
+__device__ __forceinline__ void chol_diag_block_g(double *T, double *pub, int nb, double *__restrict__ A, int64_t K,
+                                                  int64_t p0, double *__restrict__ Lp, int *__restrict__ flag) {
+    constexpr int kS = kPanel / kG / 4;  // groups per wave
     // the published group, double-buffered by group parity: [buf][row][i] = S_(row, c0 + i), m_(row, i), in
-    // pub (kPubDoubles, 16-byte aligned)
+    // pub (at least 4 * 64 * kG doubles, 16-byte aligned)
     double(*s_pub)[kPanel * kG] = reinterpret_cast<double(*)[kPanel * kG]>(pub);
     double(*m_pub)[kPanel * kG] = reinterpret_cast<double(*)[kPanel * kG]>(pub + 2 * kPanel * kG);
     const int r = threadIdx.x & 63, w = threadIdx.x >> 6;
-    double a[2][kG];  // groups w and w + 4
+    double a[kS][kG];  // slot j: group w + 4 j
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < kS; ++j)
 #pragma unroll
         for (int i = 0; i < kG; ++i) {
             const int k = kG * (w + 4 * j) + i;
@@ -247,9 +268,7 @@ __device__ __forceinline__ void chol_diag_block(double *T, double *pub, int nb, 
             a[j][i] = hi < nb ? T[hi * kLd + lo] : (r == k ? 1.0 : 0.0);
         }
     bool bad = false;
-    // Group g (a runtime index: one loop per slot J of the group in its wave, so the register arrays keep
-    // constant indices and each pass is one straight-line body).
-    // A rank-8 update of columns [k0, k0 + 8) of this wave with group g's published values.
+    // The rank-kG update of columns [k0, k0 + kG) of this wave with group g's published values.
     const auto update = [&](double(&x)[kG], int k0, int g) {
         double mr[kG];
         const double2 *sm = reinterpret_cast<const double2 *>(m_pub[g & 1] + r * kG);
@@ -271,6 +290,8 @@ __device__ __forceinline__ void chol_diag_block(double *T, double *pub, int nb, 
             x[i2] = e + o;
         }
     };
+    // Group g, held in slot J of wave g % 4. The group index is a runtime value (one loop per slot), so the
+    // register arrays keep constant indices and each pass is one straight-line body.
     const auto group = [&](int g, auto slot) {
         constexpr int J = decltype(slot)::value;
         if (w == g % 4) {
@@ -292,25 +313,36 @@ __device__ __forceinline__ void chol_diag_block(double *T, double *pub, int nb, 
                 ds[i / 2] = make_double2(a[J][i], a[J][i + 1]);
                 dm[i / 2] = make_double2(mb[i], mb[i + 1]);
             }
-            // the owner's slot-1 update with the previous group, left until now (its values stay published
-            // until the barrier after this group)
-            if (J == 0 && g > 0) update(a[1], kG * (w + 4), g - 1);
+            // this wave's later slots take the previous group's update now (left from before these steps; its
+            // values stay published until the barrier after this group)
+            if (g > 0) {
+#pragma unroll
+                for (int jj = J + 1; jj < kS; ++jj) update(a[jj], kG * (w + 4 * jj), g - 1);
+            }
         }
         if (g + 1 == kPanel / kG) return;
         __syncthreads();
-        // rank-8 update of this wave's later groups: slot 0 (group w) if w > g, slot 1 (group w + 4) if
-        // w + 4 > g. The next group's wave updates that group only, runs its steps first, and then the rest.
+        // the update of this wave's later groups; the next group's wave updates that group only, runs its steps
+        // first, and then the rest
         const bool next_owner = w == (g + 1) % 4;
-        if (J == 0 && w > g) update(a[0], kG * w, g);
-        if (w + 4 > g && !(next_owner && J == 0 && w > g)) update(a[1], kG * (w + 4), g);
+#pragma unroll
+        for (int jj = 0; jj < kS; ++jj) {
+            if (w + 4 * jj <= g || (next_owner && jj > (g + 1) / 4)) continue;
+            update(a[jj], kG * (w + 4 * jj), g);
+        }
     };
+    const auto pass = [&](auto slot) {
+        constexpr int J = decltype(slot)::value;
 #pragma unroll 1
-    for (int g = 0; g < 4; ++g) group(g, std::integral_constant<int, 0>());
-#pragma unroll 1
-    for (int g = 4; g < kPanel / kG; ++g) group(g, std::integral_constant<int, 1>());
+        for (int g = 4 * J; g < 4 * J + 4; ++g) group(g, slot);
+    };
+    pass(std::integral_constant<int, 0>());
+    if constexpr (kS > 1) pass(std::integral_constant<int, 1>());
+    if constexpr (kS > 2) pass(std::integral_constant<int, 2>());
+    if constexpr (kS > 3) pass(std::integral_constant<int, 3>());
     if (bad) flag[0] = 1;  // uniform within the wave that found it
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < kS; ++j)
 #pragma unroll
         for (int i = 0; i < kG; ++i) {
             const int c = kG * (w + 4 * j) + i;
@@ -325,6 +357,14 @@ __device__ __forceinline__ void chol_diag_block(double *T, double *pub, int nb, 
         const int rr = idx >> 6, k = idx & 63;
         if (rr < nb && k <= rr) A[(p0 + rr) * K + p0 + k] = T[rr * kLd + k];
     }
+}
+
+#ifndef NVFP4_CHOL_GROUP
+#define NVFP4_CHOL_GROUP 8
+#endif
+__device__ __forceinline__ void chol_diag_block(double *T, double *pub, int nb, double *__restrict__ A, int64_t K,
+                                                int64_t p0, double *__restrict__ Lp, int *__restrict__ flag) {
+    chol_diag_block_g<NVFP4_CHOL_GROUP>(T, pub, nb, A, K, p0, Lp, flag);
 }
 
 // The first panel's diagonal block (later ones are factored by the trailing update before them).
@@ -608,24 +648,32 @@ __global__ __launch_bounds__(256) void k_gptq_cols(const void *__restrict__ W, i
 
 // S[r][k] (=, when the reduction starts at column 0, else +=) sum_{i < depth} E[r][ecol0 + i] V_(vrow0+i, k)
 // for k in [kbeg, kend), in 64 x 64 tiles on the fp64 matrix cores, the reduction in 64-deep steps.
-__global__ __launch_bounds__(256) void k_gptq_update(const double *__restrict__ E, int ldE, int ecol0,
-                                                     const double *__restrict__ A, double *__restrict__ S, int64_t R,
-                                                     int64_t K, int64_t vrow0, int depth, int64_t kbeg, int64_t kend) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_gptq_update(
+    const double *__restrict__ E, int ldE, int ecol0, const double *__restrict__ A, double *__restrict__ S, int64_t R,
+    int64_t K, int64_t vrow0, int depth, int64_t kbeg, int64_t kend) {
     __shared__ double Et[kTile * kLd], Vt[kTile * kLd];
     const int64_t r0 = (int64_t)blockIdx.y * kTile, k0 = kbeg + (int64_t)blockIdx.x * kTile;
-    const auto zero = [](int, int) { return 0.0; };
     f64x4 acc[2][2] = {};
+    // step d0's tiles: E rows r0.., reduction columns d0..; V reduction rows d0.. (consecutive threads on
+    // consecutive, descending, A columns), stored transposed
+    const auto e_off = [&](int d0) { return [=](int a, int i) { return (r0 + a) * ldE + ecol0 + d0 + i; }; };
+    const auto e_ok = [&](int d0) { return [=](int a, int i) { return r0 + a < R && i < depth - d0; }; };
+    const auto v_off = [&](int d0) {
+        return [=](int i, int kk) { return (K - 1 - vrow0 - d0 - i) * K + (K - 1 - k0 - kk); };
+    };
+    const auto v_ok = [&](int d0) { return [=](int i, int kk) { return k0 + kk < kend && i < depth - d0; }; };
+    double fe[16], fv[16];  // the next step's tiles, in flight while the current one is multiplied
+    fetch_tile(fe, E, e_off(0), e_ok(0));
+    fetch_tile(fv, A, v_off(0), v_ok(0));
     for (int d0 = 0; d0 < depth; d0 += kPanel) {
-        const int dn = min(kPanel, depth - d0);
         if (d0 > 0) __syncthreads();  // the previous step's reads are done
-        load_tile(
-            Et, E, [&](int a, int i) { return (r0 + a) * ldE + ecol0 + d0 + i; },
-            [&](int a, int i) { return r0 + a < R && i < dn; }, zero, [](int a, int i) { return a * kLd + i; });
-        // reduction row i, consecutive threads on consecutive (descending) A columns; stored transposed
-        load_tile(
-            Vt, A, [&](int i, int kk) { return (K - 1 - vrow0 - d0 - i) * K + (K - 1 - k0 - kk); },
-            [&](int i, int kk) { return k0 + kk < kend && i < dn; }, zero, [](int i, int kk) { return kk * kLd + i; });
+        put_tile(Et, fe, e_ok(d0), [](int a, int i) { return a * kLd + i; });
+        put_tile(Vt, fv, v_ok(d0), [](int i, int kk) { return kk * kLd + i; });
         __syncthreads();
+        if (d0 + kPanel < depth) {
+            fetch_tile(fe, E, e_off(d0 + kPanel), e_ok(d0 + kPanel));
+            fetch_tile(fv, A, v_off(d0 + kPanel), v_ok(d0 + kPanel));
+        }
         mfma_tile64(Et, Vt, acc);
     }
     const bool first = vrow0 == 0;
