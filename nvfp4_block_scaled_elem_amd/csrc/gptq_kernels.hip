@@ -359,12 +359,10 @@ __device__ __forceinline__ void chol_diag_block_g(double *T, double *pub, int nb
     }
 }
 
-#ifndef NVFP4_CHOL_GROUP
-#define NVFP4_CHOL_GROUP 8
-#endif
+// Groups of 8 (groups of 4 measured the same; the pivot chain, not the group count, sets the time).
 __device__ __forceinline__ void chol_diag_block(double *T, double *pub, int nb, double *__restrict__ A, int64_t K,
                                                 int64_t p0, double *__restrict__ Lp, int *__restrict__ flag) {
-    chol_diag_block_g<NVFP4_CHOL_GROUP>(T, pub, nb, A, K, p0, Lp, flag);
+    chol_diag_block_g<8>(T, pub, nb, A, K, p0, Lp, flag);
 }
 
 // The first panel's diagonal block (later ones are factored by the trailing update before them).
