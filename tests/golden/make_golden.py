@@ -5,10 +5,11 @@ comes from the GPU path. The oracle takes minutes at these sizes (CJSO(8) on a 1
 about two), too slow for a test, so this script runs it once and stores:
   * full_size.json: per workload, the SHA-256 of the input bytes, and per mode alpha (binary32 bits),
     the SHA-256 of the codes and of the scales, the FourOverSix M=4 block count and the MSE;
-  * <workload>_soar_sample.npz: for the SOAR search, the expected codes and scales of a fixed sample of
-    blocks (the oracle runs the search block by block from its own CJSO state), and for the workloads
-    in SEARCH_VARIANTS the same for other search grids and reconstruct-pair rules (keys
-    <variant>_codes, <variant>_scales).
+  * for SOAR, the SHA-256 of the codes and scales of every block (the oracle runs the search block by
+    block from its own CJSO state; the blocks are shared out over the worker processes), and
+    <workload>_soar_sample.npz, the expected codes and scales of a fixed sample of blocks, which tells
+    how many blocks differ when a digest does not match; for the workloads in SEARCH_VARIANTS the same
+    for other search grids and reconstruct-pair rules (keys <variant>_codes, <variant>_scales).
 
 Run from the repository root:  python tests/golden/make_golden.py  [-j 8] [--only c2:soar ...]
 (--only reruns the named jobs and keeps the other entries of full_size.json.)
@@ -90,8 +91,9 @@ def job(name: str, mode: str):
         out.update(alpha=f32_hex(r["alpha"]), codes=sha(r["codes"]), scales=sha(r["scales"]),
                    alpha_trace=[f32_hex(a) for a in r["alpha_trace"]],
                    mse=oracle.mse(W, r["codes"], r["scales"], r["alpha"]))
-    else:  # soar: CJSO state of the whole matrix, then the search on sampled blocks
+    else:  # soar: CJSO state of the whole matrix, then the search on sampled blocks (every block: full_search)
         r = oracle.quantize(W, "cjso", ITERS)
+        out["state"] = {"alpha": r["alpha"], "scales": r["scales"], "dstar": r["dstar"]}
         blocks = sample_blocks(r["scales"].size)
         c, s = oracle.soar_blocks(W, r["alpha"], r["scales"], r["dstar"], blocks)
         fname = f"{name}_soar_sample.npz"
@@ -110,6 +112,30 @@ def job(name: str, mode: str):
     return name, mode, out
 
 
+_W_CACHE = {}
+
+
+def search_chunk(name, alpha, scales, dstar, lo, hi, grid, rule):
+    if name not in _W_CACHE:  # one workload per worker process at a time
+        _W_CACHE.clear()
+        _W_CACHE[name] = workloads()[name]()
+    W = _W_CACHE[name]
+    blocks = np.arange(lo, hi, dtype=np.int64)
+    kw = {} if grid is None else {"grid": grid, "dd_rule": rule}
+    return oracle.soar_blocks(W, alpha, scales, dstar, blocks, **kw)
+
+
+def full_search(ex, name, st, grid, rule, jobs):
+    """The oracle's search on every block from the CJSO state st, in contiguous chunks over the workers;
+    codes [blocks][8] and scales in block order."""
+    nblk = st["scales"].size
+    step = (nblk + 4 * jobs - 1) // (4 * jobs)
+    bounds = [(lo, min(lo + step, nblk)) for lo in range(0, nblk, step)]
+    parts = list(ex.map(search_chunk, *zip(*[(name, st["alpha"], st["scales"], st["dstar"], lo, hi, grid, rule)
+                                               for lo, hi in bounds])))
+    return np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts])
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("-j", type=int, default=4)
@@ -122,12 +148,23 @@ def main():
         with open(os.path.join(HERE, "full_size.json")) as f:
             result = json.load(f)
     with ProcessPoolExecutor(max_workers=args.j) as ex:
+        states = []
         for name, mode, out in ex.map(job, *zip(*jobs)):
             result.setdefault(name, {"modes": {}})
             result[name]["input_sha256"] = out.pop("input_sha256")
             result[name]["shape"] = out.pop("shape")
+            if "state" in out:
+                states.append((name, out.pop("state")))
             result[name]["modes"][mode] = out
             print(name, mode, out.get("alpha"), flush=True)
+        for name, st in states:  # the search on every block, blocks shared out over the workers
+            exp = result[name]["modes"]["soar"]
+            c, s = full_search(ex, name, st, None, None, args.j)
+            exp["codes"], exp["scales"] = sha(c), sha(s)
+            for vname, v in exp.get("search_variants", {}).items():
+                c, s = full_search(ex, name, st, tuple(v["grid"]), v["dd_rule"], args.j)
+                v["codes_all"], v["scales_all"] = sha(c), sha(s)
+            print(name, "soar, every block", exp["codes"][:12], flush=True)
     with open(os.path.join(HERE, "full_size.json"), "w") as f:
         json.dump(result, f, indent=1, sort_keys=True)
 
