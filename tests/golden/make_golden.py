@@ -41,9 +41,8 @@ def workloads():
         "c2": lambda: synth.c2(0),
         "c3_up": lambda: synth.c3(0, 0),
         "c3_down": lambda: synth.c3(1, 0),
-        "c5_l0_q": lambda: synth.c5(0, "q"),
-        "c5_l0_gate": lambda: synth.c5(0, "gate"),
-        "c5_l0_down": lambda: synth.c5(0, "down"),
+        **{f"c5_l{layer}_{m}": (lambda layer=layer, m=m: synth.c5(layer, m))
+           for layer in (0, 31) for m in synth.C5_ORDER},
     }
 
 
@@ -52,9 +51,9 @@ PLAN = {
     "c2": ["max", "4o6", "cjso", "soar"],
     "c3_up": ["4o6", "cjso"],
     "c3_down": ["4o6", "cjso"],
-    "c5_l0_q": ["4o6", "soar"],
-    "c5_l0_gate": ["4o6", "soar"],
-    "c5_l0_down": ["4o6", "soar"],
+    # every matrix of the first layer in both of C5's modes, every matrix of the last layer in FourOverSix
+    **{f"c5_l0_{m}": ["4o6", "soar"] for m in synth.C5_ORDER},
+    **{f"c5_l31_{m}": ["4o6"] for m in synth.C5_ORDER},
 }
 
 

@@ -579,9 +579,7 @@ WORKLOADS = {
     "c2": lambda: synth.c2(0),
     "c3_up": lambda: synth.c3(0, 0),
     "c3_down": lambda: synth.c3(1, 0),
-    "c5_l0_q": lambda: synth.c5(0, "q"),
-    "c5_l0_gate": lambda: synth.c5(0, "gate"),
-    "c5_l0_down": lambda: synth.c5(0, "down"),
+    **{f"c5_l{layer}_{m}": (lambda layer=layer, m=m: synth.c5(layer, m)) for layer in (0, 31) for m in synth.C5_ORDER},
 }
 
 
