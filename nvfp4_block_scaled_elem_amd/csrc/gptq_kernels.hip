@@ -20,7 +20,8 @@
 //   k_gptq_prep     dead inputs (zero diagonal) and the damping lambda = percdamp * mean(diag)
 //   k_gptq_reverse  A = P (H with dead diagonals 1, + lambda I) P, lower triangle
 //   k_chol_diag,    blocked Cholesky of A in place, panels of 64 columns: the diagonal block (one
-//   k_chol_trsm,    work-group, 4 x 4 register tiles), the rows below it (16 lanes per row), and the updates
+//   k_chol_trsm,    work-group, LDL^T by four waves in groups of 8 columns), the rows below it (16 lanes per
+//                   row), and the updates
 //   k_chol_update   (64 x 64 tiles on the fp64 matrix cores), delayed over groups of 4 panels: a panel's stripe
 //                   takes its group's earlier panels just before it is factored, the trailing triangle the whole
 //                   group after it; an update's first work-group also factors the diagonal block it completes,
