@@ -6,8 +6,10 @@
 //   CJSO(T)           : k_amax -> k_cjso_init -> T x k_cjso_iter
 //   SOAR(T)           : CJSO(T) -> k_soar
 //   GPTQ (nvfp4_gptq) : k_amax -> k_quant (the FourOverSix frame) -> k_gptq_prep -> k_gptq_reverse ->
-//                       k_chol_diag -> per panel {k_chol_trsm, k_chol_update} -> k_gptq_pack_v ->
-//                       per column block {k_gptq_cols, k_gptq_update} -> k_gptq_finish
+//                       k_chol_diag -> per group of 4 panels {per panel: k_chol_update (its stripe, but
+//                       not for the group's first), k_chol_trsm; then k_chol_update (the trailing triangle)}
+//                       -> k_gptq_pack_v -> per group of 4 column blocks {4 x k_gptq_cols, k_gptq_update}
+//                       -> k_gptq_finish
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
