@@ -46,6 +46,32 @@ __device__ __forceinline__ uint32_t e4m3_rne(double v) {
     return c > 0x7Eu ? 0x7Eu : c;
 }
 
+// e4m3_rne(x / y) for x >= 0, y > 0 whose binary32 roundings are within 2^-24 of them, decided from the
+// binary32 estimate q = fl(x) * rcp(fl(y)) where that is safe; returns false (code unset) otherwise. The
+// estimate is within 5 binary32 ulps of x / y (two roundings of the operands, v_rcp_f32's 1 ulp, the
+// product's rounding), and every E4M3 midpoint in the normal range has the binary32 pattern ...m m m 1
+// followed by 19 zero bits. So when q lies in [2^-6, 2^10) and more than 32 ulps from such a pattern,
+// x / y lies on the same side of every midpoint as q, and rounding q's significand to 3 bits (add half an
+// E4M3 step, truncate; no tie is possible) gives the code of x / y, clamped to 448.
+__device__ __forceinline__ bool e4m3_quotient_est(float x, float y, uint32_t &code) {
+    const float q = x * __builtin_amdgcn_rcpf(y);
+    const uint32_t u = __float_as_uint(q);
+    const bool far = ((u + 0x80000u + 32u) & 0xFFFFFu) >= 64u;
+    const uint32_t c = ((u + 0x80000u) >> 20) - 960u;  // (biased exponent, 3 bits) minus E4M3's bias
+    code = c < 0x7Eu ? c : 0x7Eu;
+    return far && q >= 0x1p-6f && q < 0x1p10f;
+}
+
+// e4m3_rne(v) for a binary32 v in E4M3's normal range (v >= 2^-6; false, code unset, below it): the
+// significand rounded to 3 bits with ties to even (add 2^19 - 1 plus the kept last bit, truncate), clamped
+// to 448.
+__device__ __forceinline__ bool e4m3_rne_normal(float v, uint32_t &code) {
+    const uint32_t u = __float_as_uint(v);
+    const uint32_t c = ((u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20) - 960u;
+    code = c < 0x7Eu ? c : 0x7Eu;
+    return v >= 0x1p-6f;
+}
+
 // The E4M3 codes around v >= 0: lo = largest value <= v, hi = smallest value >= v (both 448 when
 // v >= 448, both 0 when v <= 0).
 __device__ __forceinline__ void e4m3_bracket(double v, uint32_t &lo, uint32_t &hi) {

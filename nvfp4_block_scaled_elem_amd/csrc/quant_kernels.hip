@@ -276,6 +276,56 @@ __device__ __forceinline__ bool for_my_blocks(const void *__restrict__ W, const 
     return true;
 }
 
+// The same visit, two blocks at a time: f2(b, A, da, b', B, db) gets two consecutive blocks of this thread
+// (b' = b + S, or b - S with `reverse`) and their scale bytes (0 without `sc_in`), so that their independent
+// arithmetic can be interleaved; an odd last block goes to f1(b, A, da). The next pair's loads are issued
+// before a pair is processed.
+template <int T, bool F32, class Pre, class Post, class F2, class F1>
+__device__ __forceinline__ bool for_my_pairs(const void *__restrict__ W, const uint8_t *__restrict__ sc_in,
+                                             int64_t nblk, bool reverse, Pre &&pre, Post &&post, F2 &&f2, F1 &&f1) {
+    const int64_t stride = (int64_t)gridDim.x * T;
+    const int64_t first = (int64_t)blockIdx.x * T + threadIdx.x;
+    const int64_t n = first < nblk ? (nblk - 1 - first) / stride + 1 : 0;  // blocks of this thread
+    const int64_t start = reverse && n > 0 ? first + (n - 1) * stride : first;
+    const int64_t step = reverse ? -stride : stride;
+    const int64_t safe = n > 0 ? start : nblk - 1;  // a valid block to prefetch past the end
+    Raw<F32> r0, r1;
+    uint32_t s0 = 0u, s1 = 0u;
+    pre();
+    {
+        const int64_t c0 = safe, c1 = n > 1 ? start + step : safe;
+        r0.load(W, c0);
+        r1.load(W, c1);
+        if (sc_in) {
+            s0 = sc_in[c0];
+            s1 = sc_in[c1];
+        }
+    }
+    if (!post()) return false;
+    int64_t b = start, i = 0;
+    for (; i + 1 < n; i += 2) {
+        Blk<F32> A, B;
+        A.set(r0);
+        B.set(r1);
+        const uint32_t da = s0, db = s1;
+        const int64_t c0 = i + 2 < n ? b + 2 * step : safe, c1 = i + 3 < n ? b + 3 * step : safe;
+        r0.load(W, c0);
+        r1.load(W, c1);
+        if (sc_in) {
+            s0 = sc_in[c0];
+            s1 = sc_in[c1];
+        }
+        f2(b, A, da, b + step, B, db);
+        b += 2 * step;
+    }
+    if (i < n) {
+        Blk<F32> A;
+        A.set(r0);
+        f1(b, A, s0);
+    }
+    return true;
+}
+
 // ---------------------------------------------------------------------------------- global max
 
 // Per work-group max of |w| as binary32 bits (bf16 bits are widened), plus the non-finite test
@@ -366,6 +416,69 @@ __device__ __forceinline__ bool fos_choice(const Blk<F32> &B, float a, const Sca
     return m4;
 }
 
+// The max rule's code E4M3(max|w| / (6 alpha)) of a block (six_alpha = fl(6 alpha)): decided by the binary32
+// estimate where it can be, else by the binary64 quotient. Returns whether the estimate decided it; the
+// caller then skips the binary64 form (kept out of this function so that two blocks' estimates stay side by
+// side).
+__device__ __forceinline__ bool max_rule_est(float a, float six_alpha, uint32_t &d) {
+    return e4m3_quotient_est(a, six_alpha, d);
+}
+
+// One candidate scale of a bf16 block: its codes and exact sums.
+struct Cand {
+    uint32_t c0, c1;
+    double sw, sq;
+};
+
+// The common case of quant_sums_r for a bf16 block: hardware codes for the reciprocal r of s and the
+// binary32 sums. Returns whether those sums are exact (quant_sums_r's own test); when not, the caller
+// redoes the candidate with quant_sums_r.
+__device__ __forceinline__ bool cand_fast(const Blk<false> &B, float a, float s, float r, Cand &k) {
+    encode16(B.w, r, k.c0, k.c1);
+    float fw, fq;
+    sums_bf16(k.c0, k.c1, B.p, fw, fq);
+    k.sw = fw;
+    k.sq = fq;
+    return finite_pos(r) && a <= 32.0f * s && a <= 0x1p100f;
+}
+
+// fos_choice's comparison: whether M=4 (scale v4, candidate k4) has the strictly smaller squared error.
+__device__ __forceinline__ bool fos_m4(float alpha, float v6, float v4, const Cand &k6, const Cand &k4) {
+    const double sd6 = (double)alpha * (double)v6, sd4 = (double)alpha * (double)v4;
+    const dd j6 = two_prod(sd6, fma(sd6, k6.sq, -2.0 * k6.sw));
+    const dd j4 = two_prod(sd4, fma(sd4, k4.sq, -2.0 * k4.sw));
+    return dd_less(j4, j6);
+}
+
+// fos_choice for two bf16 blocks A and B (max-rule codes dA6, dB6), their four candidates written out side by
+// side; the rare cases (M=4 scale below E4M3's normal range, sums outside the binary32 window) take the
+// general forms. Out: each block's chosen scale, its candidate, and whether M=4 was taken.
+__device__ __forceinline__ void fos_pair(const Blk<false> &A, float aA, uint32_t dA6, const Blk<false> &B, float aB,
+                                         uint32_t dB6, const ScaleTab &T, float alpha, uint32_t &dA, Cand &kA,
+                                         bool &mA, uint32_t &dB, Cand &kB, bool &mB) {
+    const float vA6 = e4m3_value(dA6), vB6 = e4m3_value(dB6);
+    uint32_t dA4, dB4;
+    const bool nA = e4m3_rne_normal(1.5f * vA6, dA4), nB = e4m3_rne_normal(1.5f * vB6, dB4);  // 1.5 v exact
+    if (!nA) dA4 = e4m3_rne(1.5 * (double)vA6);
+    if (!nB) dB4 = e4m3_rne(1.5 * (double)vB6);
+    const float sA6 = T.s[dA6], rA6 = T.r[dA6], sA4 = T.s[dA4], rA4 = T.r[dA4];
+    const float sB6 = T.s[dB6], rB6 = T.r[dB6], sB4 = T.s[dB4], rB4 = T.r[dB4];
+    Cand A6, A4, B6, B4;
+    const bool fA6 = cand_fast(A, aA, sA6, rA6, A6), fA4 = cand_fast(A, aA, sA4, rA4, A4);
+    const bool fB6 = cand_fast(B, aB, sB6, rB6, B6), fB4 = cand_fast(B, aB, sB4, rB4, B4);
+    // the reciprocals pass opaquely, so that the compiler keeps these encodings apart from the ones above
+    if (!fA6) quant_sums_r(A, aA, sA6, opaque(rA6), A6.c0, A6.c1, A6.sw, A6.sq);
+    if (!fA4) quant_sums_r(A, aA, sA4, opaque(rA4), A4.c0, A4.c1, A4.sw, A4.sq);
+    if (!fB6) quant_sums_r(B, aB, sB6, opaque(rB6), B6.c0, B6.c1, B6.sw, B6.sq);
+    if (!fB4) quant_sums_r(B, aB, sB4, opaque(rB4), B4.c0, B4.c1, B4.sw, B4.sq);
+    mA = fos_m4(alpha, vA6, e4m3_value(dA4), A6, A4);
+    mB = fos_m4(alpha, vB6, e4m3_value(dB4), B6, B4);
+    dA = mA ? dA4 : dA6;
+    kA = mA ? A4 : A6;
+    dB = mB ? dB4 : dB6;
+    kB = mB ? B4 : B6;
+}
+
 template <bool F32, bool FOS>
 __global__ __launch_bounds__(kQuantThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_quant(const void *__restrict__ W, int64_t nblk,
                                                           const uint32_t *__restrict__ amax_part, int amax_n,
@@ -374,13 +487,14 @@ __global__ __launch_bounds__(kQuantThreads) __attribute__((amdgpu_waves_per_eu(4
                                                           nvfp4_stats_t *stats, uint32_t *__restrict__ m4_part) {
     __shared__ ScaleTab T;
     AmaxShare<kQuantThreads> am;
-    float alpha = 0.0f;
+    float alpha = 0.0f, six_alpha = 0.0f;
     uint32_t m4count = 0u;
     auto pre = [&] { am.load(amax_part, amax_n); };
     auto post = [&] {
         const uint32_t abits = am.reduce();
         const bool nonfinite = abits >= 0x7F800000u;
         alpha = max_rule_alpha(abits);
+        six_alpha = 6.0f * alpha;
         if (blockIdx.x == 0 && threadIdx.x == 0) {
             *alpha_out = nonfinite ? __builtin_nanf("") : alpha;
             if (stats) stats->status = nonfinite ? NVFP4_STATUS_NONFINITE : 0u;
@@ -389,29 +503,67 @@ __global__ __launch_bounds__(kQuantThreads) __attribute__((amdgpu_waves_per_eu(4
         build_scale_tab<kQuantThreads>(T, alpha);
         return true;
     };
-    // the opposite order to k_amax, which read the same blocks in the same work-group just before
-    const bool finite = for_my_blocks<kQuantThreads, kQuantDepth, F32>(W, nullptr, nblk, true, pre, post,
-                                           [&](int64_t b, const Blk<F32> &B, uint32_t) {
-            uint32_t c0, c1, sc;
-            bool m4 = false;
-            const float a = B.amax();
-            const uint32_t d6 = e4m3_rne(max_rule_quotient(a, alpha));
-            sc = d6;
-            if constexpr (!FOS) {
-                const float r = T.r[d6];
-                if (finite_pos(r))
-                    encode16(B.w, r, c0, c1);
-                else
-                    encode16_soft(B.w, r, c0, c1);
-            } else {
-                double sw, sq;
-                m4 = fos_choice(B, a, T, alpha, d6, sc, c0, c1, sw, sq);
-                if (mchoice) mchoice[b] = m4 ? 1 : 0;
-                m4count += m4 ? 1u : 0u;
+    const auto one = [&](int64_t b, const Blk<F32> &B, uint32_t) {
+        uint32_t c0, c1, sc;
+        bool m4 = false;
+        const float a = B.amax();
+        const uint32_t d6 = e4m3_rne(max_rule_quotient(a, alpha));
+        sc = d6;
+        if constexpr (!FOS) {
+            const float r = T.r[d6];
+            if (finite_pos(r))
+                encode16(B.w, r, c0, c1);
+            else
+                encode16_soft(B.w, r, c0, c1);
+        } else {
+            double sw, sq;
+            m4 = fos_choice(B, a, T, alpha, d6, sc, c0, c1, sw, sq);
+            if (mchoice) mchoice[b] = m4 ? 1 : 0;
+            m4count += m4 ? 1u : 0u;
+        }
+        store_codes(codes, b, c0, c1);
+        scales[b] = (uint8_t)sc;
+    };
+    // two bf16 blocks with their common path side by side (see k_cjso_iter), the rare cases per block
+    const auto two = [&](int64_t bA, const auto &A, uint32_t, int64_t bB, const auto &B, uint32_t) {
+        const float aA = A.amax(), aB = B.amax();
+        uint32_t dA, dB;
+        const bool eA = max_rule_est(aA, six_alpha, dA), eB = max_rule_est(aB, six_alpha, dB);
+        if (!eA) dA = e4m3_rne(max_rule_quotient(aA, alpha));
+        if (!eB) dB = e4m3_rne(max_rule_quotient(aB, alpha));
+        if constexpr (!FOS) {
+            const float rA = T.r[dA], rB = T.r[dB];
+            uint32_t cA0, cA1, cB0, cB1;
+            encode16(A.w, rA, cA0, cA1);
+            encode16(B.w, rB, cB0, cB1);
+            if (!finite_pos(rA)) encode16_soft(A.w, opaque(rA), cA0, cA1);
+            if (!finite_pos(rB)) encode16_soft(B.w, opaque(rB), cB0, cB1);
+            store_codes(codes, bA, cA0, cA1);
+            store_codes(codes, bB, cB0, cB1);
+            scales[bA] = (uint8_t)dA;
+            scales[bB] = (uint8_t)dB;
+        } else {
+            uint32_t sA, sB;
+            Cand kA, kB;
+            bool mA, mB;
+            fos_pair(A, aA, dA, B, aB, dB, T, alpha, sA, kA, mA, sB, kB, mB);
+            if (mchoice) {
+                mchoice[bA] = mA ? 1 : 0;
+                mchoice[bB] = mB ? 1 : 0;
             }
-            store_codes(codes, b, c0, c1);
-            scales[b] = (uint8_t)sc;
-        });
+            m4count += (mA ? 1u : 0u) + (mB ? 1u : 0u);
+            store_codes(codes, bA, kA.c0, kA.c1);
+            store_codes(codes, bB, kB.c0, kB.c1);
+            scales[bA] = (uint8_t)sA;
+            scales[bB] = (uint8_t)sB;
+        }
+    };
+    // the opposite order to k_amax, which read the same blocks in the same work-group just before
+    bool finite;
+    if constexpr (F32)
+        finite = for_my_blocks<kQuantThreads, kQuantDepth, F32>(W, nullptr, nblk, true, pre, post, one);
+    else
+        finite = for_my_pairs<kQuantThreads, F32>(W, nullptr, nblk, true, pre, post, two, one);
     if (!finite) {  // non-finite input: all-zero codes and scales
         const int64_t stride = (int64_t)gridDim.x * kQuantThreads;
         for (int64_t b = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x; b < nblk; b += stride) {
@@ -465,13 +617,14 @@ __global__ __launch_bounds__(kCjsoThreads) __attribute__((amdgpu_waves_per_eu(NV
                                                               uint16_t *__restrict__ brackets, nvfp4_stats_t *stats) {
     __shared__ ScaleTab T;
     AmaxShare<kCjsoThreads> am;
-    float alpha = 0.0f;
+    float alpha = 0.0f, six_alpha = 0.0f;
     dd N = {0.0, 0.0}, D = {0.0, 0.0};
     auto pre = [&] { am.load(amax_part, amax_n); };
     auto post = [&] {
         const uint32_t abits = am.reduce();
         const bool nonfinite = abits >= 0x7F800000u;
         alpha = max_rule_alpha(abits);
+        six_alpha = 6.0f * alpha;
         if (blockIdx.x == 0 && threadIdx.x == 0) {
             const float av = nonfinite ? __builtin_nanf("") : alpha;
             alpha_state[0] = av;
@@ -482,9 +635,7 @@ __global__ __launch_bounds__(kCjsoThreads) __attribute__((amdgpu_waves_per_eu(NV
         build_scale_tab<kCjsoThreads>(T, alpha);
         return true;
     };
-    // the opposite order to k_amax, which read the same blocks in the same work-group just before
-    const bool finite = for_my_blocks<kCjsoThreads, kCjsoDepth, F32>(W, nullptr, nblk, true, pre, post,
-                                           [&](int64_t b, const Blk<F32> &B, uint32_t) {
+    const auto one = [&](int64_t b, const Blk<F32> &B, uint32_t) {
         const float a = B.amax();
         const double q = max_rule_quotient(a, alpha);
         uint32_t d = e4m3_rne(q);
@@ -517,7 +668,61 @@ __global__ __launch_bounds__(kCjsoThreads) __attribute__((amdgpu_waves_per_eu(NV
             acc2(N, t.hi, t.lo);
             acc2(D, (double)v * (double)v * sq, 0.0);
         }
-    });
+    };
+    // two bf16 blocks with their common path side by side (see k_cjso_iter), the rare cases per block
+    const auto two = [&](int64_t bA, const auto &A, uint32_t, int64_t bB, const auto &B, uint32_t) {
+        const float aA = A.amax(), aB = B.amax();
+        uint32_t dA, dB;
+        const bool eA = max_rule_est(aA, six_alpha, dA), eB = max_rule_est(aB, six_alpha, dB);
+        if (!eA) dA = e4m3_rne(max_rule_quotient(aA, alpha));
+        if (!eB) dB = e4m3_rne(max_rule_quotient(aB, alpha));
+        const uint32_t dA6 = dA, dB6 = dB;
+        Cand kA, kB;
+        bool mA = false, mB = false;
+        if constexpr (FOS) {
+            fos_pair(A, aA, dA6, B, aB, dB6, T, alpha, dA, kA, mA, dB, kB, mB);
+        } else if constexpr (ROUNDS) {
+            const float sA = T.s[dA], rA = T.r[dA], sB = T.s[dB], rB = T.r[dB];
+            const bool fA = cand_fast(A, aA, sA, rA, kA), fB = cand_fast(B, aB, sB, rB, kB);
+            if (!fA) quant_sums_r(A, aA, sA, opaque(rA), kA.c0, kA.c1, kA.sw, kA.sq);
+            if (!fB) quant_sums_r(B, aB, sB, opaque(rB), kB.c0, kB.c1, kB.sw, kB.sq);
+        } else {
+            const float rA = T.r[dA], rB = T.r[dB];
+            encode16(A.w, rA, kA.c0, kA.c1);
+            encode16(B.w, rB, kB.c0, kB.c1);
+            if (!finite_pos(rA)) encode16_soft(A.w, opaque(rA), kA.c0, kA.c1);
+            if (!finite_pos(rB)) encode16_soft(B.w, opaque(rB), kB.c0, kB.c1);
+        }
+        scales[bA] = (uint8_t)dA;
+        scales[bB] = (uint8_t)dB;
+        if constexpr (!ROUNDS) {
+            store_codes(codes, bA, kA.c0, kA.c1);
+            store_codes(codes, bB, kB.c0, kB.c1);
+            if (SOAR) {
+                const double sA = mA ? 1.5 * (double)e4m3_value(dA6) : max_rule_quotient(aA, alpha);
+                const double sB = mB ? 1.5 * (double)e4m3_value(dB6) : max_rule_quotient(aB, alpha);
+                uint32_t lo, hi;
+                e4m3_bracket(sA, lo, hi);
+                brackets[bA] = (uint16_t)(lo | (hi << 8));
+                e4m3_bracket(sB, lo, hi);
+                brackets[bB] = (uint16_t)(lo | (hi << 8));
+            }
+        } else {
+            const float vA = e4m3_value(dA), vB = e4m3_value(dB);
+            const dd tA = two_prod((double)vA, kA.sw);
+            acc2(N, tA.hi, tA.lo);
+            acc2(D, (double)vA * (double)vA * kA.sq, 0.0);
+            const dd tB = two_prod((double)vB, kB.sw);
+            acc2(N, tB.hi, tB.lo);
+            acc2(D, (double)vB * (double)vB * kB.sq, 0.0);
+        }
+    };
+    // the opposite order to k_amax, which read the same blocks in the same work-group just before
+    bool finite;
+    if constexpr (F32)
+        finite = for_my_blocks<kCjsoThreads, kCjsoDepth, F32>(W, nullptr, nblk, true, pre, post, one);
+    else
+        finite = for_my_pairs<kCjsoThreads, F32>(W, nullptr, nblk, true, pre, post, two, one);
     if (!finite) {  // non-finite input: all-zero outputs; the rounds see alpha = NaN and stop
         const int64_t stride = (int64_t)gridDim.x * kCjsoThreads;
         for (int64_t b = (int64_t)blockIdx.x * kCjsoThreads + threadIdx.x; b < nblk; b += stride) {
@@ -571,28 +776,29 @@ __global__ __launch_bounds__(kCjsoThreads) __attribute__((amdgpu_waves_per_eu(NV
         build_scale_tab<kCjsoThreads>(T, alpha);
         return true;
     };
-    // forward: round 1 starts on the blocks k_cjso_init (which runs backwards) read last; alternating the
-    // order of later rounds as well was timed and gained nothing (their time is spent on arithmetic)
-    if (!for_my_blocks<kCjsoThreads, kCjsoDepth, F32>(W, scales, nblk, false, pre, post, [&](int64_t b, const Blk<F32> &B, uint32_t d) {
-        const float v = e4m3_value(d);
-        uint32_t c0, c1;
-        double sw, sq;
-        const float a = B.amax();
-        quant_sums_r(B, a, T.s[d], T.r[d], c0, c1, sw, sq);
-        double dstar = (double)v;
-        uint32_t dn = d;
-        if (sq > 0.0) {
-            dstar = sw / ((double)alpha * sq);
-            dn = e4m3_rne(dstar);
+    // The Delta-step's E4M3 code (and, where the search's bracket needs it, its unrounded quotient); a block
+    // whose codes are all zero keeps its scale. Elsewhere the code comes from a binary32 estimate where that
+    // decides it, and from the binary64 quotient where it does not.
+    const auto delta_step = [&](double sw, double sq, uint32_t d, double &dstar, uint32_t &dn) {
+        const bool pos = sq > 0.0;
+        if constexpr (LAST && SOAR) {
+            const double q = sw / ((double)alpha * sq);  // not used when sq = 0
+            dstar = pos ? q : (double)e4m3_value(d);
+            dn = pos ? e4m3_rne(q) : d;
+        } else {
+            uint32_t c;
+            const bool ok = e4m3_quotient_est((float)sw, alpha * (float)sq, c);
+            dstar = 0.0;  // not used
+            dn = pos ? c : d;
+            if (pos && !ok) dn = e4m3_rne(sw / ((double)alpha * sq));
         }
-        scales[b] = (uint8_t)dn;
-        const float vn = e4m3_value(dn);
-        // an unchanged scale re-quantises to the same codes and sums (the common case once the rounds
-        // settle; a wave skips this when none of its blocks changed)
-        if (dn != d) quant_sums_r(B, a, T.s[dn], T.r[dn], c0, c1, sw, sq);
+    };
+    // After the block's last re-quantisation: the sums of the next alpha-step, or the final outputs.
+    const auto finish = [&](int64_t b, uint32_t dn, double dstar, uint32_t c0, uint32_t c1, double sw, double sq) {
         if (!LAST) {
             // vn has 4 significant bits, S_wq at most 53 and S_qq at most 12: v*S_wq needs the exact
             // product, v^2*S_qq is exact in binary64
+            const float vn = e4m3_value(dn);
             const dd tn = two_prod((double)vn, sw);
             acc2(Nn, tn.hi, tn.lo);
             acc2(Dn, (double)vn * (double)vn * sq, 0.0);
@@ -604,8 +810,54 @@ __global__ __launch_bounds__(kCjsoThreads) __attribute__((amdgpu_waves_per_eu(NV
                 brackets[b] = (uint16_t)(lo | (hi << 8));
             }
         }
-    }))
-        return;
+    };
+    const auto one = [&](int64_t b, const Blk<F32> &B, uint32_t d) {
+        uint32_t c0, c1, dn;
+        double sw, sq, dstar;
+        const float a = B.amax();
+        quant_sums_r(B, a, T.s[d], T.r[d], c0, c1, sw, sq);
+        delta_step(sw, sq, d, dstar, dn);
+        scales[b] = (uint8_t)dn;
+        // an unchanged scale re-quantises to the same codes and sums (the common case once the rounds
+        // settle; a wave skips this when none of its blocks changed)
+        if (dn != d) quant_sums_r(B, a, T.s[dn], T.r[dn], c0, c1, sw, sq);
+        finish(b, dn, dstar, c0, c1, sw, sq);
+    };
+    // Two blocks with their common path written out side by side (hardware codes, binary32 sums, the
+    // Delta-step), so that one block's arithmetic fills the other's latencies; a block outside the binary32
+    // sums' exactness window redoes its first pass on the general path (its reciprocal passed opaquely, so
+    // that the compiler does not merge the two encodings into one branch between the blocks).
+    const auto two = [&](int64_t bA, const auto &A, uint32_t dA, int64_t bB, const auto &B, uint32_t dB) {
+        const float aA = A.amax(), aB = B.amax();
+        const float sA = T.s[dA], rA = T.r[dA], sB = T.s[dB], rB = T.r[dB];
+        uint32_t cA0, cA1, cB0, cB1;
+        encode16(A.w, rA, cA0, cA1);
+        encode16(B.w, rB, cB0, cB1);
+        float fwA, fqA, fwB, fqB;
+        sums_bf16(cA0, cA1, A.p, fwA, fqA);
+        sums_bf16(cB0, cB1, B.p, fwB, fqB);
+        double swA = fwA, sqA = fqA, swB = fwB, sqB = fqB;
+        if (!(finite_pos(rA) && aA <= 32.0f * sA && aA <= 0x1p100f)) quant_sums_r(A, aA, sA, opaque(rA), cA0, cA1, swA, sqA);
+        if (!(finite_pos(rB) && aB <= 32.0f * sB && aB <= 0x1p100f)) quant_sums_r(B, aB, sB, opaque(rB), cB0, cB1, swB, sqB);
+        uint32_t dnA, dnB;
+        double dsA, dsB;
+        delta_step(swA, sqA, dA, dsA, dnA);
+        delta_step(swB, sqB, dB, dsB, dnB);
+        scales[bA] = (uint8_t)dnA;
+        scales[bB] = (uint8_t)dnB;
+        if (dnA != dA) quant_sums_r(A, aA, T.s[dnA], T.r[dnA], cA0, cA1, swA, sqA);
+        if (dnB != dB) quant_sums_r(B, aB, T.s[dnB], T.r[dnB], cB0, cB1, swB, sqB);
+        finish(bA, dnA, dsA, cA0, cA1, swA, sqA);
+        finish(bB, dnB, dsB, cB0, cB1, swB, sqB);
+    };
+    // forward: round 1 starts on the blocks k_cjso_init (which runs backwards) read last; alternating the
+    // order of later rounds as well was timed and gained nothing (their time is spent on arithmetic)
+    bool went;
+    if constexpr (F32)
+        went = for_my_blocks<kCjsoThreads, kCjsoDepth, F32>(W, scales, nblk, false, pre, post, one);
+    else
+        went = for_my_pairs<kCjsoThreads, F32>(W, scales, nblk, false, pre, post, two, one);
+    if (!went) return;
     if (!LAST) {
         wg_sum_dd2<kCjsoThreads>(Nn, Dn);
         if (threadIdx.x == kSumLane) {
