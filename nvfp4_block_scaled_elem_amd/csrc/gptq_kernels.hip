@@ -278,15 +278,23 @@ __device__ __forceinline__ void chol_diag_block_g(double *T, double *pub, int nb
             const double2 v = sm[i / 2];
             mr[i] = v.x, mr[i + 1] = v.y;
         }
+        // every load is issued before the first product (the scheduler barrier keeps them there), so their
+        // latencies overlap instead of adding up
+        double2 sv[kG][kG / 2];
 #pragma unroll
         for (int i2 = 0; i2 < kG; ++i2) {
             const double2 *sk = reinterpret_cast<const double2 *>(s_pub[g & 1] + (k0 + i2) * kG);
+#pragma unroll
+            for (int i = 0; i < kG; i += 2) sv[i2][i / 2] = sk[i / 2];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i2 = 0; i2 < kG; ++i2) {
             double e = x[i2], o = 0.0;
 #pragma unroll
             for (int i = 0; i < kG; i += 2) {
-                const double2 v = sk[i / 2];
-                e = fma(-mr[i], v.x, e);
-                o = fma(-mr[i + 1], v.y, o);
+                e = fma(-mr[i], sv[i2][i / 2].x, e);
+                o = fma(-mr[i + 1], sv[i2][i / 2].y, o);
             }
             x[i2] = e + o;
         }
