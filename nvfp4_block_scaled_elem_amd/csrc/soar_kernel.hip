@@ -115,6 +115,35 @@ __device__ __forceinline__ double eval_r(const Blk<F32> &B, float r, double h, u
     }
 }
 
+// eval_r for the incumbent, which also reports whether each computed x = fl(w r) lies more than 8 binary32
+// ulps from every binary32 value whose low 21 significand bits are zero. Every E2M1 decision point (0.25,
+// 0.75, 1.25, 1.75, 2.5, 3.5, 5) is such a value, so for those x any u within 2^-21 |u| of x rounds to the
+// same code as x (ties included: x is not at a decision point). Per element: add 8 to the bit pattern,
+// shift out the sign, exponent and top two significand bits, and keep the least; far means that least is at
+// least 17 << 11.
+template <bool F32>
+__device__ __forceinline__ double eval_r_far(const Blk<F32> &B, float r, double h, uint32_t &c0, uint32_t &c1,
+                                             bool &far) {
+    float x[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) x[j] = B.w[j] * r;
+    c0 = e2m1_pack8(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]);
+    c1 = e2m1_pack8(x[8], x[9], x[10], x[11], x[12], x[13], x[14], x[15]);
+    uint32_t m = 0xFFFFFFFFu;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) m = min(m, (__float_as_uint(x[j]) + 8u) << 11);
+    far = m >= (17u << 11);
+    if constexpr (F32) {
+        double sw, sq;
+        sums_f64(c0, c1, B.w, sw, sq);
+        return fma(h, sq, -sw);
+    } else {
+        float sw, sq;
+        sums_bf16(c0, c1, B.p, sw, sq);
+        return fma(h, (double)sq, -(double)sw);
+    }
+}
+
 template <bool F32>
 __device__ __forceinline__ double eval_s(const Blk<F32> &B, float s, double h, uint32_t &c0, uint32_t &c1) {
     return eval_r<F32>(B, recip_rn(s), h, c0, c1);
@@ -294,24 +323,22 @@ __global__ __launch_bounds__(kSoarThreads) void k_soar(const void *__restrict__ 
             const double sd_c = c_is_lo ? slo : shi, h_c = c_is_lo ? hlo : hhi;
             uint32_t i0, i1;
             const float rc = recip_rn(sc);
-            a_c = eval_r(B, rc, h_c, i0, i1);
+            bool far;
+            a_c = eval_r_far(B, rc, h_c, i0, i1, far);
             const float vo = c_is_lo ? vhi : vlo;
             const double sd_o = c_is_lo ? shi : slo, h_o = c_is_lo ? hhi : hlo;
             int kA, kB;
             const GridGuess gg{g.count - 1, (float)g.den, (float)g.num0};
             // Are the incumbent's codes the nearest E2M1 values of the exact quotients |w| / (alpha Delta_c)?
-            // Its computed x = fl(w fl(1/fl(alpha Delta_c))) is within 3 * 2^-24 of the quotient u, so
-            // codes computed with the reciprocal moved by 2^-21 down and up bracket those of u; where both
-            // equal the incumbent's, so do those of u (the rounding is monotone). Then every element's
-            // error term under Delta_d = Delta_c is already the least that scale allows: no candidate with
-            // that reconstruct scale is strictly better than the incumbent, and only the other scale's
-            // window can win (first minimiser in scan order: the window's first minimiser, whose codes
-            // every earlier k with the same error shares). This holds for all but a few blocks in a million,
-            // which take the full window comparison below.
-            uint32_t u0, u1, l0, l1;
-            encode16(B.w, rc * (1.0f + 0x1p-21f), u0, u1);
-            encode16(B.w, rc * (1.0f - 0x1p-21f), l0, l1);
-            if (((u0 ^ i0) | (u1 ^ i1) | (l0 ^ i0) | (l1 ^ i1)) == 0u && (dc == lo || dc == hi)) {
+            // Its computed x = fl(w fl(1/fl(alpha Delta_c))) is within 3 * 2^-24 of the quotient u (three
+            // roundings), so where every x is far from the decision points (eval_r_far), u has x's code.
+            // Then every element's error term under Delta_d = Delta_c is already the least that scale allows:
+            // no candidate with that reconstruct scale is strictly better than the incumbent, and only the
+            // other scale's window can win (first minimiser in scan order: the window's first minimiser,
+            // whose codes every earlier k with the same error shares). This holds for all but about one
+            // block in 10^4 (an element near a decision point, or an exact zero), which take the full window
+            // comparison below.
+            if (far && (dc == lo || dc == hi)) {
                 uint32_t o0 = i0, o1 = i1;
                 db = dc;
                 if (lo != hi) {

@@ -1,4 +1,4 @@
-"""The binary32 shortcuts the quantiser kernels take for E4M3 roundings, checked on the CPU.
+"""The binary32 shortcuts the quantiser kernels take for E4M3 roundings and E2M1 certificates, checked on the CPU.
 
 Two shortcuts replace a binary64 division and rounding in the common case:
 
@@ -8,6 +8,11 @@ Two shortcuts replace a binary64 division and rounding in the common case:
   the binary64 quotient.
 * e4m3_rne_normal (codec.hpp): the E4M3 rounding (ties to even) of an exact binary32 value in E4M3's
   normal range by integer arithmetic on its bits (FourOverSix's E4M3(1.5 Delta6)).
+
+A third one decides, in the decoupled search (soar_kernel.hip, eval_r_far), that a block's codes are the
+nearest E2M1 values of the exact quotients |w| / (alpha Delta): every computed x = fl(w fl(1/fl(alpha Delta)))
+(within 3 * 2^-24 of its quotient) must lie more than 8 binary32 ulps from every value whose low 21
+significand bits are zero, which every E2M1 decision point is.
 
 The device instructions are modelled here in numpy binary32 arithmetic, v_rcp_f32 as the correctly rounded
 reciprocal and one ulp either side of it. The reference is the E4M3 rule itself (nearest value, ties to
@@ -115,3 +120,31 @@ def test_rne_normal_on_every_five_bit_value_and_more():
     claimed, code = rne_normal(v)
     assert np.array_equal(claimed, v >= np.float32(2.0 ** -6))
     assert np.array_equal(code[claimed], e4m3_rne(v.astype(np.float64))[claimed])
+
+
+def e2m1_magnitude_code(a):
+    """E2M1 magnitude code of |a|: nearest of 0, .5, 1, 1.5, 2, 3, 4, 6, ties to the even code, saturating."""
+    a = np.abs(np.asarray(a, dtype=np.float64))
+    return ((a > 0.25).astype(int) + (a >= 0.75) + (a > 1.25) + (a >= 1.75) + (a > 2.5) + (a >= 3.5) + (a > 5.0))
+
+
+def certificate_far(x32, margin=8):
+    """Model of eval_r_far's test: ((bits + margin) << 11) mod 2^32 >= (2 margin + 1) << 11."""
+    u = x32.view(np.uint32).astype(np.uint64)
+    return (((u + margin) << 11) & 0xFFFFFFFF) >= ((2 * margin + 1) << 11)
+
+
+def test_e2m1_certificate_keeps_codes_within_the_rounding_bound():
+    # every binary32 value within 4096 ulps of each decision point, both signs, and random magnitudes up to 8
+    vals = [np.arange(int(np.float32(t).view(np.uint32)) - 4096, int(np.float32(t).view(np.uint32)) + 4097,
+                      dtype=np.int64).astype(np.uint32).view(np.float32)
+            for t in (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0)]
+    vals.append(np.random.default_rng(5).uniform(0, 8, 1_000_000).astype(np.float32))
+    x = np.concatenate(vals)
+    x = np.concatenate([x, -x])
+    far = certificate_far(x)
+    for rel in (3 * 2.0 ** -24, -3 * 2.0 ** -24):  # the exact quotient u with |u - x| <= 3 * 2^-24 |u|
+        u = x.astype(np.float64) / (1 - rel)
+        assert np.array_equal(e2m1_magnitude_code(u)[far], e2m1_magnitude_code(x)[far])
+    assert not certificate_far(np.array([0.25, -0.75, 5.0, 0.0], dtype=np.float32)).any()
+    assert far.mean() > 0.99  # values near a decision point are the rare ones
