@@ -32,7 +32,7 @@
 //                   each column's errors folded into the block's later columns at once
 //   k_gptq_update   after each group of 4 blocks, S[:, k] += sum over the group of e_i V_ik for every
 //                   column k beyond it (fp64 matrix cores, 64 x 64 tiles); within a group, the sweep adds the
-//                   group's earlier blocks itself
+//                   group's earlier blocks itself (fp64 matrix cores, operands read straight from memory)
 //   k_gptq_finish   a failed factorisation (a pivot that is not positive and finite): alpha = NaN, codes 0
 // S holds sum_{i<g0} e_i V_ik for the columns not yet reached, g0 the start of the current group. The update
 // after the first group writes it, so it needs no clearing.
@@ -560,38 +560,43 @@ __global__ __launch_bounds__(256) void k_gptq_cols(const void *__restrict__ W, i
         acc[v] = in && sb0 > 0 ? sv[v] : 0.0;
         w[v] = in && ((dd >> (8 * v)) & 0xFFu) == 0 ? (double)__uint_as_float(wr[v]) : 0.0;
     }
-    // the group's earlier blocks: acc_k += sum_i e_i V_ik, i over block [pb, pb + 64), from the packed slots
-    // of this column block (slot q, the last, is the diagonal block)
+    // the group's earlier blocks: acc_k += sum_i e_i V_ik, i over blocks [pb, pb + 64) before this one, from
+    // the packed slots of this column block (slot q, the last, is the diagonal block). On the fp64 matrix
+    // cores: the work-group's 16 rows of errors (the A operand, from E) times each earlier block of V (the B
+    // operand); wave wv takes the columns 16 wv .. 16 wv + 15 of the block. Both operands of every earlier
+    // block are read straight from global memory, all at once, so their latencies overlap (through LDS, one
+    // block at a time, each block cost a load-to-use latency of its own).
     const int q = (int)((b0 - sb0) / kPanel);
     const double *vt = Vb + (b0 / kPanel) * 4 * kPanel * kPanel;
-    for (int t = 0; t < q; ++t) {
-        // (the earlier blocks are whole: every lane of a row in range holds four of their errors)
-        const double2 *ep = reinterpret_cast<const double2 *>(E + (row < R ? row * ldE + kPanel * t + 4 * c : 0));
-        const double2 e01 = ep[0], e23 = ep[1];
-        if (t > 0) __syncthreads();  // the previous slot's reads are done
-        copy_tile256(V, vt + t * kPanel * kPanel);
-        __syncthreads();
-        const double ee[4] = {e01.x, e01.y, e23.x, e23.y};  // the row's errors in block columns 4c .. 4c + 3
-        // rows of V read two steps ahead of their use; two sums per column, so a step does not wait for the last
-        double vr[3][4], acc2[4] = {0.0, 0.0, 0.0, 0.0};
-        lds_row4(V, 0, c, vr[0]);
-        lds_row4(V, 1, c, vr[1]);
+    if (q > 0) {
+        const int l = threadIdx.x & 63, wv = threadIdx.x >> 6;
+        const int64_t arow = (int64_t)blockIdx.x * 16 + (l & 15);  // the A row of this lane
+        // A[r][4 s + l / 16] = E[row r][64 t + 4 s + l / 16], B[4 s + l / 16][n] = V_t[4 s + l / 16][16 wv + n]
+        // for the 16 steps s of block t (rows past R and blocks t >= q read as 0; the earlier blocks are whole)
+        double ea[kSuper / kPanel - 1][16], vb[kSuper / kPanel - 1][16];
+        const double *ep = E + (arow < R ? arow * ldE + (l >> 4) : 0);
+        const double *bp = vt + (l >> 4) * kPanel + 16 * wv + (l & 15);
 #pragma unroll
-        for (int i = 0; i < kPanel; ++i) {
-            if (i + 2 < kPanel) lds_row4(V, i + 2, c, vr[(i + 2) % 3]);
-            const double ei = row_bcast(ee[i & 3], i >> 2);
+        for (int t = 0; t < kSuper / kPanel - 1; ++t)
 #pragma unroll
-            for (int v2 = 0; v2 < 4; ++v2) {
-                if (i & 1)
-                    acc2[v2] = fma(ei, vr[i % 3][v2], acc2[v2]);
-                else
-                    acc[v2] = fma(ei, vr[i % 3][v2], acc[v2]);
+            for (int st = 0; st < 16; ++st) {
+                ea[t][st] = t < q && arow < R ? ep[kPanel * t + 4 * st] : 0.0;
+                vb[t][st] = t < q ? bp[t * kPanel * kPanel + 4 * st * kPanel] : 0.0;
             }
-        }
+        f64x4 g = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-        for (int v2 = 0; v2 < 4; ++v2) acc[v2] += acc2[v2];
+        for (int t = 0; t < kSuper / kPanel - 1; ++t)
+            if (t < q)
+#pragma unroll
+                for (int st = 0; st < 16; ++st) g = __builtin_amdgcn_mfma_f64_16x16x4f64(ea[t][st], vb[t][st], g, 0, 0, 0);
+        // to the sweep's layout through LDS: register qq holds row 4 qq + l / 16, column 16 wv + l % 16
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) V[(4 * qq + (l >> 4)) * kPanel + 16 * wv + (l & 15)] = g[qq];
+        __syncthreads();
+#pragma unroll
+        for (int v2 = 0; v2 < 4; ++v2) acc[v2] += V[(threadIdx.x >> 4) * kPanel + 4 * c + v2];
+        __syncthreads();  // done with the sums before the diagonal block replaces them
     }
-    if (q > 0) __syncthreads();  // done with the last earlier slot
     copy_tile256(V, vt + q * kPanel * kPanel);  // the diagonal block
     const double s = in ? (double)(alpha * e4m3_value(sb)) : 0.0;
     const bool live = s > 0.0;
