@@ -744,7 +744,8 @@ __global__ __launch_bounds__(kCjsoThreads) __attribute__((amdgpu_waves_per_eu(NV
 
 // CJSO round t (1..iters): alpha-step from the previous round's sums, re-quantise, Delta-step (SOAR
 // page, block-scale closed form, rounded to E4M3), re-quantise; then the sums for round t+1, or, in the
-// last round (LAST), the codes (and for SOAR the E4M3 bracket of the unrounded block scale).
+// last round (LAST), the codes (before the SOAR search: the E4M3 bracket of the unrounded block scale
+// instead, since the search writes every block's codes).
 template <bool F32, bool SOAR, bool LAST>
 __global__ __launch_bounds__(kCjsoThreads) __attribute__((amdgpu_waves_per_eu(NVFP4_CJSO_WAVES))) void k_cjso_iter(const void *__restrict__ W, int64_t nblk, int t,
                                                               const double *__restrict__ part_in, int n_part,
@@ -793,7 +794,9 @@ __global__ __launch_bounds__(kCjsoThreads) __attribute__((amdgpu_waves_per_eu(NV
             if (pos && !ok) dn = e4m3_rne(sw / ((double)alpha * sq));
         }
     };
-    // After the block's last re-quantisation: the sums of the next alpha-step, or the final outputs.
+    // After the block's last re-quantisation: the sums of the next alpha-step, or the final outputs. Before the
+    // search (SOAR) the last round writes only the scale and the bracket: the search writes every block's codes.
+    constexpr bool kRequant = !(LAST && SOAR);  // whether the codes and sums after the Delta-step are used
     const auto finish = [&](int64_t b, uint32_t dn, double dstar, uint32_t c0, uint32_t c1, double sw, double sq) {
         if (!LAST) {
             // vn has 4 significant bits, S_wq at most 53 and S_qq at most 12: v*S_wq needs the exact
@@ -802,13 +805,12 @@ __global__ __launch_bounds__(kCjsoThreads) __attribute__((amdgpu_waves_per_eu(NV
             const dd tn = two_prod((double)vn, sw);
             acc2(Nn, tn.hi, tn.lo);
             acc2(Dn, (double)vn * (double)vn * sq, 0.0);
+        } else if (SOAR) {
+            uint32_t lo, hi;
+            e4m3_bracket(dstar, lo, hi);
+            brackets[b] = (uint16_t)(lo | (hi << 8));
         } else {
             store_codes(codes, b, c0, c1);
-            if (SOAR) {
-                uint32_t lo, hi;
-                e4m3_bracket(dstar, lo, hi);
-                brackets[b] = (uint16_t)(lo | (hi << 8));
-            }
         }
     };
     const auto one = [&](int64_t b, const Blk<F32> &B, uint32_t d) {
@@ -820,7 +822,7 @@ __global__ __launch_bounds__(kCjsoThreads) __attribute__((amdgpu_waves_per_eu(NV
         scales[b] = (uint8_t)dn;
         // an unchanged scale re-quantises to the same codes and sums (the common case once the rounds
         // settle; a wave skips this when none of its blocks changed)
-        if (dn != d) quant_sums_r(B, a, T.s[dn], T.r[dn], c0, c1, sw, sq);
+        if (kRequant && dn != d) quant_sums_r(B, a, T.s[dn], T.r[dn], c0, c1, sw, sq);
         finish(b, dn, dstar, c0, c1, sw, sq);
     };
     // Two blocks with their common path written out side by side (hardware codes, binary32 sums, the
@@ -845,8 +847,8 @@ __global__ __launch_bounds__(kCjsoThreads) __attribute__((amdgpu_waves_per_eu(NV
         delta_step(swB, sqB, dB, dsB, dnB);
         scales[bA] = (uint8_t)dnA;
         scales[bB] = (uint8_t)dnB;
-        if (dnA != dA) quant_sums_r(A, aA, T.s[dnA], T.r[dnA], cA0, cA1, swA, sqA);
-        if (dnB != dB) quant_sums_r(B, aB, T.s[dnB], T.r[dnB], cB0, cB1, swB, sqB);
+        if (kRequant && dnA != dA) quant_sums_r(A, aA, T.s[dnA], T.r[dnA], cA0, cA1, swA, sqA);
+        if (kRequant && dnB != dB) quant_sums_r(B, aB, T.s[dnB], T.r[dnB], cB0, cB1, swB, sqB);
         finish(bA, dnA, dsA, cA0, cA1, swA, sqA);
         finish(bB, dnB, dsB, cB0, cB1, swB, sqB);
     };

@@ -261,7 +261,10 @@ __global__ __launch_bounds__(kSoarThreads) void k_soar(const void *__restrict__ 
     const int64_t b = (int64_t)blockIdx.x * kSoarThreads + threadIdx.x;
     if (b >= nblk) return;
     const uint32_t dc = scales[b];
-    if (dc == 0u) return;  // Delta_c = 0: every candidate quantises to 0 and ties; codes and scale stay 0
+    if (dc == 0u) {  // Delta_c = 0: every candidate quantises to 0 and ties; the scale stays 0, the codes are 0
+        *reinterpret_cast<uint2 *>(codes + 8 * b) = make_uint2(0u, 0u);
+        return;
+    }
     Blk<F32> B;
     B.load(W, b);
     const float a = B.amax();

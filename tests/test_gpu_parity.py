@@ -176,6 +176,35 @@ def test_zero_and_tiny(mode):
     compare_live(big, mode, 1)
 
 
+@pytest.mark.parametrize("mode,iters", [("max", 0), ("4o6", 0), ("cjso", 3), ("soar", 0), ("soar", 3)])
+def test_every_output_byte_written(mode, iters):
+    """Outputs start as a pattern no quantiser writes (0xA5), so a block the kernels skip shows. The matrix
+    has whole zero blocks (scale 0, whose codes the search leaves to nobody else), a zero row and
+    ordinary blocks, over enough blocks for several loop iterations per thread."""
+    W = synth.normal_bf16(96, 4096, 31)
+    W[5, :] = 0
+    W[7, 16:48] = 0
+    W[9, 4080:] = 0
+    W[40:42, ::7] = 0
+    Wd = to_dev(W)
+    rows, cols = W.shape
+    codes = torch.full((rows, cols // 2), 0xA5, dtype=torch.uint8, device="cuda")
+    scales = torch.full((rows, cols // 16), 0xA5, dtype=torch.uint8, device="cuda")
+    alpha = torch.full((1,), float("nan"), dtype=torch.float32, device="cuda")
+    mch = torch.full((rows, cols // 16), 0xA5, dtype=torch.uint8, device="cuda") if mode == "4o6" else None
+    stats = torch.zeros(4, dtype=torch.int32, device="cuda")
+    say(f"gpu quantize (outputs pre-filled) mode={mode} iters={iters} shape={W.shape}")
+    nv.quantize(Wd, mode, iters, codes=codes, scales=scales, alpha=alpha, mchoice=mch, stats=stats)
+    torch.cuda.synchronize()
+    g = {"codes": codes.cpu().numpy(), "scales": scales.cpu().numpy(), "alpha": float(alpha.cpu()[0]),
+         "stats": stats.cpu().numpy()}
+    if mch is not None:
+        g["mchoice"] = mch.cpu().numpy()
+    r = oracle.quantize(W, mode, iters)
+    assert (g["scales"][5] == 0).all() and (g["codes"][5] == 0).all()
+    assert_exact(g, r, mode)
+
+
 def test_saturating_and_subnormal_scales():
     # blocks whose max-rule scale lands on 320..416 (FourOverSix M=4 scale saturates) and blocks whose
     # scales are E4M3 subnormals
