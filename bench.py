@@ -90,8 +90,9 @@ STEP_KERNEL_BYTES_PER_ELEM = {
     "4o6": [2, 2 + 1 / 2 + 1 / 16 + 1 / 16],  # k_amax; k_quant: codes, scale and the M=4 map
     # k_amax; k_cjso_init: new scale; ITERS-1 rounds; the last round: read scale, write scale and codes
     "cjso": [2, 2 + 1 / 16] + [ROUND_BYTES_PER_ELEM] * (ITERS - 1) + [2 + 1 / 16 + 1 / 16 + 1 / 2],
-    # as CJSO, the last round also writes the bracket; then the search
-    "soar": [2, 2 + 1 / 16] + [ROUND_BYTES_PER_ELEM] * (ITERS - 1) + [2 + 1 / 16 + 1 / 16 + 1 / 2 + 2 / 16,
+    # as CJSO, but the last round writes the bracket instead of the codes (the search writes them); then the
+    # search
+    "soar": [2, 2 + 1 / 16] + [ROUND_BYTES_PER_ELEM] * (ITERS - 1) + [2 + 1 / 16 + 1 / 16 + 2 / 16,
                                                                       SEARCH_BYTES_PER_ELEM],
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_k_cjso_iter_4096x4096.txt")
