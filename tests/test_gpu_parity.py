@@ -205,6 +205,46 @@ def test_every_output_byte_written(mode, iters):
     assert_exact(g, r, mode)
 
 
+def edge_rows_bf16(seed: int) -> np.ndarray:
+    """16 x 4096 bf16 rows of the blocks the quantisers treat apart: ordinary Student-t blocks, a row scaled
+    down until its scales fall below E4M3's normal range, whole zero blocks and a zero row, blocks with one
+    large element among small ones (their least-squares scale is far below max|w| / 6, so the binary32 sums
+    leave their exactness window), outliers, and rows at other magnitudes."""
+    x = synth.student_t(synth.rng(seed, 7), 4.0, (16, 4096), 0.02).astype(np.float32)
+    x[1] *= 1e-2  # scales in E4M3's subnormal range
+    x[2, 256:512] = 0.0
+    blk = x[3].reshape(-1, 16)
+    blk[::2, 1:] *= 1e-3
+    x[4, ::97] *= 300.0
+    x[5] = 0.0
+    x[6] *= 3e-3
+    x[7, ::5] = 0.0
+    x[8] *= 1e-6  # scales that round to zero
+    return synth.bf16_bits(x)
+
+
+@pytest.mark.parametrize("case", ["mixed", "tiny"])
+@pytest.mark.parametrize("mode,iters", [("max", 0), ("4o6", 0), ("cjso", 3), ("soar", 3)])
+def test_tiled_edge_blocks_two_per_thread(case, mode, iters):
+    """The edge blocks at a size where every pass gives each thread two or more blocks, so the paired
+    common path and its per-block fallbacks run: the 16 x 4096 rows above, tiled 128 times by rows (2048 x
+    4096). Tiling by whole rows leaves alpha unchanged in every mode (the global max is the same; the CJSO
+    sums all scale by the tile count, so their quotient does not move), and each block's outputs depend
+    only on the block and alpha, so the result must be the oracle's result for the small matrix, tiled.
+    "tiny" scales everything by 1e-36, so alpha is subnormal and the scales' reciprocals overflow."""
+    small = edge_rows_bf16(11)
+    if case == "tiny":
+        small = synth.bf16_bits(synth.bf16_to_f32(small) * np.float32(1e-36))
+    r = oracle.quantize(small, mode, iters)
+    big = np.tile(small, (128, 1))
+    g = run(big, mode, iters)
+    assert f32_bits(g["alpha"]) == f32_bits(r["alpha"])
+    for key in ("codes", "scales") + (("mchoice",) if mode == "4o6" else ()):
+        want = np.tile(r[key], (128, 1))
+        bad = np.flatnonzero(np.any((g[key] != want).reshape(g[key].shape[0], -1), axis=1))
+        assert bad.size == 0, f"{key}: rows {bad[:8]} differ"
+
+
 def test_saturating_and_subnormal_scales():
     # blocks whose max-rule scale lands on 320..416 (FourOverSix M=4 scale saturates) and blocks whose
     # scales are E4M3 subnormals
