@@ -27,10 +27,13 @@ __device__ __forceinline__ bf16x2 as_bf16x2(uint32_t d) { return __builtin_bit_c
 
 // ---------------------------------------------------------------------------------------- E4M3
 
-// Value of a non-negative finite E4M3 code (0x00..0x7E).
+// Value of a non-negative finite E4M3 code (0x00..0x7E). A normal code c = 8e + m (e >= 1) is the binary32
+// pattern with exponent field e + 120 and m in the top three significand bits, i.e. (c + 960) << 20; a
+// subnormal one is m * 2^-9. Both are formed and one is selected (no branch).
 __device__ __forceinline__ float e4m3_value(uint32_t c) {
-    uint32_t e = c >> 3, m = c & 7u;
-    return e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
+    const float nor = __uint_as_float((c << 20) + 0x3C000000u);
+    const float sub = (float)c * 0x1p-9f;
+    return c >= 8u ? nor : sub;
 }
 
 // Nearest E4M3 value to v >= 0 (ties to the even code), values >= 448 saturate to 448. Exact for any

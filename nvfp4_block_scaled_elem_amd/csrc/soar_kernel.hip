@@ -47,6 +47,18 @@ struct SearchCfg {
     int rule;              // NVFP4_DD_*
 };
 
+// The page's grid f_k = (50 + k) / 100, k = 0..100, as the kernels compute it for any grid (the binary64
+// quotient, correctly rounded, then rounded to binary32), evaluated once at compile time.
+struct PageGrid {
+    float f[101];
+};
+constexpr PageGrid make_page_grid() {
+    PageGrid g{};
+    for (int k = 0; k < 101; ++k) g.f[k] = (float)((double)(50 + k) / 100.0);
+    return g;
+}
+__constant__ PageGrid kPageGrid = make_page_grid();
+
 // s_k = fl(alpha * fl(Delta_c * f_k)) and its reciprocal (0 for a zero scale: every code is then 0).
 __device__ __forceinline__ float quant_scale(float alpha, float vc, const float *ftab, int k) {
     return alpha * (vc * ftab[k]);
@@ -253,26 +265,47 @@ __global__ __launch_bounds__(kSoarThreads) void k_soar(const void *__restrict__ 
     if constexpr (KIND == kPagesSearch) g = SearchCfg{50, 100, 101, NVFP4_DD_CJSO};
     __shared__ float ftab[kMaxGrid];
     const float alpha = *alpha_p;
-    if (alpha != alpha) return;  // non-finite input: outputs already zero
-    for (int i = threadIdx.x; i < g.count; i += kSoarThreads)
-        ftab[i] = (float)((double)(g.num0 + i) / (double)g.den);
+    const int64_t b = (int64_t)blockIdx.x * kSoarThreads + threadIdx.x;
+    const bool mine = b < nblk;
+    // the grid table's entry, the block, its scale and its bracket are all requested before any is used, with
+    // no branch around the loads (a lane past the end reads the last block and returns after the barrier);
+    // the loaded words pass an empty asm statement before the barrier, so that the compiler cannot move the
+    // loads (of read-only memory) past it into the branches that use them: all of them land together
+    float f0 = 0.0f;
+    if constexpr (KIND == kPagesSearch) f0 = kPageGrid.f[min((int)threadIdx.x, 100)];
+    const int64_t bl = mine ? b : nblk - 1;
+    Raw<F32> raw;
+    uint32_t dc = scales[bl];
+    uint32_t br = 0u;
+    if constexpr (!RULES) br = brackets[bl];
+    raw.load(W, bl);
+#pragma unroll
+    for (int k = 0; k < (F32 ? 4 : 2); ++k)
+        asm volatile("" : "+v"(raw.v[k].x), "+v"(raw.v[k].y), "+v"(raw.v[k].z), "+v"(raw.v[k].w));
+    asm volatile("" : "+v"(dc), "+v"(br));
+    if constexpr (KIND == kPagesSearch) {
+        static_assert(kSoarThreads <= kMaxGrid, "one table slot per thread");
+        ftab[threadIdx.x] = f0;  // slots past 100 are never read
+    } else {
+        for (int i = threadIdx.x; i < g.count; i += kSoarThreads)
+            ftab[i] = (float)((double)(g.num0 + i) / (double)g.den);
+    }
     __syncthreads();
 
-    const int64_t b = (int64_t)blockIdx.x * kSoarThreads + threadIdx.x;
-    if (b >= nblk) return;
-    const uint32_t dc = scales[b];
+    if (alpha != alpha || !mine) return;  // a non-finite input (alpha NaN) has its outputs zeroed already
     if (dc == 0u) {  // Delta_c = 0: every candidate quantises to 0 and ties; the scale stays 0, the codes are 0
         *reinterpret_cast<uint2 *>(codes + 8 * b) = make_uint2(0u, 0u);
         return;
     }
     Blk<F32> B;
-    B.load(W, b);
+    B.set(raw);
     const float a = B.amax();
     const float vc = e4m3_value(dc);
     const float sc = alpha * vc;  // the incumbent's quantisation scale (Delta_q = Delta_c)
     // the smallest quantisation scale of the search: the multipliers increase with k
     const float smin = fminf(quant_scale(alpha, vc, ftab, 0), sc);
-    const bool rfin = finite_pos(recip(smin));  // bounds every reciprocal
+    // every reciprocal is finite (recip(0) is 0): fl(1/s) overflows exactly when s <= 2^-128
+    const bool rfin = !(smin > 0.0f && smin <= 0x1p-128f);
     uint32_t c0, c1;  // codes of the chosen candidate
     uint32_t db;
 
@@ -298,7 +331,6 @@ __global__ __launch_bounds__(kSoarThreads) void k_soar(const void *__restrict__ 
         return;
     } else {
 
-    const uint32_t br = brackets[b];
     const uint32_t lo = br & 0xFFu, hi = br >> 8;
     // s_d = alpha * Delta_d exactly; errors are compared through s_d * A_d
     const float vlo = e4m3_value(lo), vhi = e4m3_value(hi);
@@ -315,8 +347,10 @@ __global__ __launch_bounds__(kSoarThreads) void k_soar(const void *__restrict__ 
     // multiple of 2^(ilogb(s_d / 2) - 29) (alpha * Delta_d has at most 28 bits, S_qq is a multiple of 1/4).
     bool windowed = false;
     {
-        const int L = min(ilogb(hlo) - 29, ilogbf(smin) - (F32 ? 27 : 11));
-        const int M = max(ilogb(hhi) + 11, ilogbf(a) + 8);
+        // ilogb(v) = frexp exponent - 1 for finite v != 0; hlo, hhi and smin are checked positive and finite,
+        // and a = 0 only raises M (a stricter test)
+        const int L = min(__builtin_amdgcn_frexp_exp(hlo) - 30, __builtin_amdgcn_frexp_expf(smin) - (F32 ? 28 : 12));
+        const int M = max(__builtin_amdgcn_frexp_exp(hhi) + 10, __builtin_amdgcn_frexp_expf(a) + 7);
         windowed = !full_search && rfin && a <= 32.0f * smin && a <= 0x1p100f && hlo > 0.0 && smin > 0.0f &&
                    M - L <= 53;
     }
