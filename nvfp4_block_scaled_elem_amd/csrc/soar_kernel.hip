@@ -193,6 +193,35 @@ __device__ __forceinline__ void window(float alpha, float vc, float vd, double s
     kB = k2 < last ? k2 : last;
 }
 
+// The window's first minimiser of A_d for reconstruct scale s_d (the certified incumbent's other scale), with its
+// codes: K1 as in window(), then the candidates from max(K1, 0) up, each s_k formed once, until the first k > K1
+// with s_d < s_k (1 - 2^-20) (K2) or the last k. These are the candidates of window()'s [kA, kB], in order.
+template <bool F32>
+__device__ __forceinline__ double window_best(const Blk<F32> &B, float alpha, float vc, float vd, double sd,
+                                              double h, const float *ftab, const GridGuess &g, uint32_t &b0,
+                                              uint32_t &b1) {
+    const double up = 1.0 + 0x1p-20, dn = 1.0 - 0x1p-20;
+    const int last = g.last;
+    const float guess = floorf(g.den * (vd * __builtin_amdgcn_rcpf(vc))) - g.num0;
+    int k1 = guess < -1.0f ? -1 : (guess > (float)last ? last : (int)guess);
+    while (k1 < last && sd > (double)quant_scale(alpha, vc, ftab, k1 + 1) * up) ++k1;
+    while (k1 >= 0 && !(sd > (double)quant_scale(alpha, vc, ftab, k1) * up)) --k1;
+    double best = INFINITY;
+    b0 = b1 = 0u;
+    for (int k = k1 > 0 ? k1 : 0; k <= last; ++k) {
+        const float s = quant_scale(alpha, vc, ftab, k);
+        uint32_t d0, d1;
+        const double v = eval_r(B, recip_rn(s), h, d0, d1);
+        if (v < best) {
+            best = v;
+            b0 = d0;
+            b1 = d1;
+        }
+        if (k > k1 && sd < (double)s * dn) break;
+    }
+    return best;
+}
+
 // First k <= kA whose codes equal those at kA (the start of A_d's plateau ending at kA).
 template <bool F32>
 __device__ __forceinline__ int plateau_start(const Blk<F32> &B, float alpha, float vc, const float *ftab, int kA,
@@ -379,18 +408,8 @@ __global__ __launch_bounds__(kSoarThreads) void k_soar(const void *__restrict__ 
                 uint32_t o0 = i0, o1 = i1;
                 db = dc;
                 if (lo != hi) {
-                    window(alpha, vc, vo, sd_o, ftab, gg, kA, kB);
-                    double best = INFINITY;
-                    uint32_t b0 = 0u, b1 = 0u;
-                    for (int k = kA; k <= kB; ++k) {
-                        uint32_t d0, d1;
-                        const double v = eval_k(B, alpha, vc, ftab, k, h_o, d0, d1);
-                        if (v < best) {
-                            best = v;
-                            b0 = d0;
-                            b1 = d1;
-                        }
-                    }
+                    uint32_t b0, b1;
+                    const double best = window_best(B, alpha, vc, vo, sd_o, h_o, ftab, gg, b0, b1);
                     if (dd_less(two_prod(sd_o, best), two_prod(sd_c, a_c))) {
                         o0 = b0;
                         o1 = b1;
@@ -409,9 +428,8 @@ __global__ __launch_bounds__(kSoarThreads) void k_soar(const void *__restrict__ 
             pc.kA = kA;
             pc.c0 = pc.c1 = 0u;
             for (int k = kA; k <= kB; ++k) {
-                uint32_t d0 = i0, d1 = i1;
-                // a multiplier of exactly 1 reproduces the incumbent
-                const double v = quant_scale(alpha, vc, ftab, k) == sc ? a_c : eval_k(B, alpha, vc, ftab, k, h_c, d0, d1);
+                uint32_t d0, d1;
+                const double v = eval_k(B, alpha, vc, ftab, k, h_c, d0, d1);
                 if (v < pc.a) {
                     pc.a = v;
                     pc.k = k;
@@ -436,14 +454,19 @@ __global__ __launch_bounds__(kSoarThreads) void k_soar(const void *__restrict__ 
             }
             const Pick &pl = c_is_lo ? pc : po;
             const Pick &ph = c_is_lo ? po : pc;
-            const dd jc = two_prod(sd_c, a_c);
+            // bf16: the incumbent's error and codes formed again (its reciprocal passed opaquely, so that the
+            // compiler does not keep the first evaluation's registers through both windows); fp32 keeps them
+            uint32_t ic0 = i0, ic1 = i1;
+            double ac = a_c;
+            if constexpr (!F32) ac = eval_r(B, recip_rn(opaque(sc)), h_c, ic0, ic1);
+            const dd jc = two_prod(sd_c, ac);
             const dd jlo = two_prod(slo, pl.a);
             const dd jhi = two_prod(shi, ph.a);
             const dd jmin = dd_less(jhi, jlo) ? jhi : jlo;
             if (!dd_less(jmin, jc)) {  // no candidate is strictly better than the incumbent
                 db = dc;
-                c0 = i0;
-                c1 = i1;
+                c0 = ic0;
+                c1 = ic1;
             } else if (dd_less(jlo, jhi)) {
                 db = lo;
                 c0 = pl.c0;
