@@ -245,6 +245,31 @@ def test_tiled_edge_blocks_two_per_thread(case, mode, iters):
         assert bad.size == 0, f"{key}: rows {bad[:8]} differ"
 
 
+@pytest.mark.parametrize("case", ["mixed", "tiny"])
+@pytest.mark.parametrize("variant", ["full_scan", "grid", "quant", "lsq"])
+def test_tiled_edge_blocks_search_variants(case, variant):
+    """The same tiled edge rows through the search's other forms: the full scan (against the page's search
+    in the oracle), another grid, and the two variant reconstruct-pair rules (against the oracle's
+    configurable search). Each form has its own instantiation with its own prologue."""
+    small = edge_rows_bf16(11)
+    if case == "tiny":
+        small = synth.bf16_bits(synth.bf16_to_f32(small) * np.float32(1e-36))
+    kw = {"full_scan": dict(full_search=True), "grid": dict(grid=(100, 200, 201)),
+          "quant": dict(dd_rule="quant"), "lsq": dict(dd_rule="lsq")}[variant]
+    if variant == "full_scan":
+        r = oracle.quantize(small, "soar", 3)
+    else:
+        r = oracle.quantize_search(small, 3, grid=kw.get("grid", oracle.PAGES_GRID),
+                                   dd_rule=kw.get("dd_rule", "cjso"))
+    big = np.tile(small, (128, 1))
+    g = run(big, "soar", 3, **kw)
+    assert f32_bits(g["alpha"]) == f32_bits(r["alpha"])
+    for key in ("codes", "scales"):
+        want = np.tile(r[key], (128, 1))
+        bad = np.flatnonzero(np.any((g[key] != want).reshape(g[key].shape[0], -1), axis=1))
+        assert bad.size == 0, f"{key}: rows {bad[:8]} differ"
+
+
 def test_saturating_and_subnormal_scales():
     # blocks whose max-rule scale lands on 320..416 (FourOverSix M=4 scale saturates) and blocks whose
     # scales are E4M3 subnormals
