@@ -127,13 +127,13 @@ __device__ __forceinline__ double eval_r(const Blk<F32> &B, float r, double h, u
     }
 }
 
-// eval_r for the incumbent, which also reports whether each computed x = fl(w r) lies more than 8 binary32
-// ulps from every binary32 value whose low 21 significand bits are zero. Every E2M1 decision point (0.25,
-// 0.75, 1.25, 1.75, 2.5, 3.5, 5) is such a value, so for those x any u within 2^-21 |u| of x rounds to the
-// same code as x (ties included: x is not at a decision point). Per element: add 8 to the bit pattern,
-// shift out the sign, exponent and top two significand bits, and keep the least; far means that least is at
-// least 17 << 11.
-template <bool F32>
+// eval_r which also reports whether each computed x = fl(w r) lies more than MARGIN binary32 ulps from every
+// binary32 value whose low 21 significand bits are zero. Every E2M1 decision point (0.25, 0.75, 1.25, 1.75, 2.5,
+// 3.5, 5) is such a value, so for those x any u within MARGIN * 2^-24 |u| of x rounds to the same code as x (ties
+// included: x is not at a decision point); 8 ulps cover the incumbent's three roundings, 32 a band candidate's
+// (window_best). Per element: add MARGIN to the bit pattern, shift out the sign, exponent and top two
+// significand bits, and keep the least; far means that least is at least (2 MARGIN + 1) << 11.
+template <bool F32, uint32_t MARGIN = 8>
 __device__ __forceinline__ double eval_r_far(const Blk<F32> &B, float r, double h, uint32_t &c0, uint32_t &c1,
                                              bool &far) {
     float x[16];
@@ -143,8 +143,8 @@ __device__ __forceinline__ double eval_r_far(const Blk<F32> &B, float r, double 
     c1 = e2m1_pack8(x[8], x[9], x[10], x[11], x[12], x[13], x[14], x[15]);
     uint32_t m = 0xFFFFFFFFu;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) m = min(m, (__float_as_uint(x[j]) + 8u) << 11);
-    far = m >= (17u << 11);
+    for (int j = 0; j < 16; ++j) m = min(m, (__float_as_uint(x[j]) + MARGIN) << 11);
+    far = m >= ((2u * MARGIN + 1u) << 11);
     if constexpr (F32) {
         double sw, sq;
         sums_f64(c0, c1, B.w, sw, sq);
@@ -194,8 +194,14 @@ __device__ __forceinline__ void window(float alpha, float vc, float vd, double s
 }
 
 // The window's first minimiser of A_d for reconstruct scale s_d (the certified incumbent's other scale), with its
-// codes: K1 as in window(), then the candidates from max(K1, 0) up, each s_k formed once, until the first k > K1
-// with s_d < s_k (1 - 2^-20) (K2) or the last k. These are the candidates of window()'s [kA, kB], in order.
+// codes. K1 is found as in window(); the window's candidates are max(K1, 0) up to K2, the first k > K1 with
+// s_d < s_k (1 - 2^-20), or the last k. The candidate after K1 is a band candidate when s_k lies within 2^-20 of
+// s_d (neither below nor above): its window holds three candidates, the others two, so a wave used to evaluate
+// three. Each lane now first evaluates its band candidate, or else max(K1, 0), with the bit test of eval_r_far at
+// a 32-ulp margin. A band candidate's x = fl(w fl(1/s_k)) lies within 2^-20 + 2^-23 + 2^-40 of u = |w| / s_d,
+// so if every x is far from the decision points its codes are the unique nearest codes of every u: its error
+// is the least any candidate can have, and any candidate with that error has the same codes. It is the answer
+// on its own. The other lanes go on in k order, and a band lane that fails the test restarts at max(K1, 0).
 template <bool F32>
 __device__ __forceinline__ double window_best(const Blk<F32> &B, float alpha, float vc, float vd, double sd,
                                               double h, const float *ftab, const GridGuess &g, uint32_t &b0,
@@ -206,10 +212,22 @@ __device__ __forceinline__ double window_best(const Blk<F32> &B, float alpha, fl
     int k1 = guess < -1.0f ? -1 : (guess > (float)last ? last : (int)guess);
     while (k1 < last && sd > (double)quant_scale(alpha, vc, ftab, k1 + 1) * up) ++k1;
     while (k1 >= 0 && !(sd > (double)quant_scale(alpha, vc, ftab, k1) * up)) --k1;
-    double best = INFINITY;
-    b0 = b1 = 0u;
-    for (int k = k1 > 0 ? k1 : 0; k <= last; ++k) {
-        const float s = quant_scale(alpha, vc, ftab, k);
+    const int k0 = k1 > 0 ? k1 : 0;
+    const bool band = k1 < last && !(sd < (double)quant_scale(alpha, vc, ftab, k1 + 1) * dn);
+    int k = band ? k1 + 1 : k0;
+    float s = quant_scale(alpha, vc, ftab, k);
+    bool far;
+    double best = eval_r_far<F32, 32>(B, recip_rn(s), h, b0, b1, far);
+    if (band) {
+        if (far) return best;
+        best = INFINITY;
+        k = k0;
+    } else {
+        if (k > k1 && sd < (double)s * dn) return best;
+        ++k;
+    }
+    for (; k <= last; ++k) {
+        s = quant_scale(alpha, vc, ftab, k);
         uint32_t d0, d1;
         const double v = eval_r(B, recip_rn(s), h, d0, d1);
         if (v < best) {

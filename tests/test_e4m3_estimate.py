@@ -148,3 +148,24 @@ def test_e2m1_certificate_keeps_codes_within_the_rounding_bound():
         assert np.array_equal(e2m1_magnitude_code(u)[far], e2m1_magnitude_code(x)[far])
     assert not certificate_far(np.array([0.25, -0.75, 5.0, 0.0], dtype=np.float32)).any()
     assert far.mean() > 0.99  # values near a decision point are the rare ones
+
+
+def test_e2m1_certificate_with_the_band_margin():
+    # the search's band candidate: its scale s_k lies within 2^-20 of the reconstruct scale s_d, so x = fl(w fl(1/s_k))
+    # is within (1 + 2^-20)(1 + 2^-24)^2 - 1 < 2^-20 + 2^-23 + 2^-40 of u = |w| / s_d; a 32-ulp margin (at least 2^-19
+    # relative) must keep x's code for every such u, and an 8-ulp one must not
+    vals = [np.arange(int(np.float32(t).view(np.uint32)) - 8192, int(np.float32(t).view(np.uint32)) + 8193,
+                      dtype=np.int64).astype(np.uint32).view(np.float32)
+            for t in (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0)]
+    vals.append(np.random.default_rng(6).uniform(0, 8, 1_000_000).astype(np.float32))
+    x = np.concatenate(vals)
+    x = np.concatenate([x, -x])
+    bound = 2.0 ** -20 + 2.0 ** -23 + 2.0 ** -40
+    far = certificate_far(x, margin=32)
+    for rel in (bound, -bound):
+        u = x.astype(np.float64) / (1 - rel)
+        assert np.array_equal(e2m1_magnitude_code(u)[far], e2m1_magnitude_code(x)[far])
+    narrow = certificate_far(x, margin=8)
+    u = x.astype(np.float64) / (1 - bound)
+    assert not np.array_equal(e2m1_magnitude_code(u)[narrow], e2m1_magnitude_code(x)[narrow])
+    assert far.mean() > 0.99
