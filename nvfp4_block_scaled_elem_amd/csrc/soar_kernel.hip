@@ -210,12 +210,23 @@ __device__ __forceinline__ double window_best(const Blk<F32> &B, float alpha, fl
     const int last = g.last;
     const float guess = floorf(g.den * (vd * __builtin_amdgcn_rcpf(vc))) - g.num0;
     int k1 = guess < -1.0f ? -1 : (guess > (float)last ? last : (int)guess);
-    while (k1 < last && sd > (double)quant_scale(alpha, vc, ftab, k1 + 1) * up) ++k1;
-    while (k1 >= 0 && !(sd > (double)quant_scale(alpha, vc, ftab, k1) * up)) --k1;
+    // the walk to K1 carries s_K1 (s_lo) and s_K1+1 (s_hi), so that each is formed once
+    const auto qs = [&](int k) { return quant_scale(alpha, vc, ftab, k); };
+    float s_hi = k1 < last ? qs(k1 + 1) : 0.0f;
+    while (k1 < last && sd > (double)s_hi * up) {
+        ++k1;
+        s_hi = k1 < last ? qs(k1 + 1) : 0.0f;
+    }
+    float s_lo = k1 >= 0 ? qs(k1) : 0.0f;
+    while (k1 >= 0 && !(sd > (double)s_lo * up)) {
+        s_hi = s_lo;
+        --k1;
+        s_lo = k1 >= 0 ? qs(k1) : 0.0f;
+    }
     const int k0 = k1 > 0 ? k1 : 0;
-    const bool band = k1 < last && !(sd < (double)quant_scale(alpha, vc, ftab, k1 + 1) * dn);
+    const bool band = k1 < last && !(sd < (double)s_hi * dn);
     int k = band ? k1 + 1 : k0;
-    float s = quant_scale(alpha, vc, ftab, k);
+    float s = band ? s_hi : (k1 >= 0 ? s_lo : qs(0));
     bool far;
     double best = eval_r_far<F32, 32>(B, recip_rn(s), h, b0, b1, far);
     if (band) {
