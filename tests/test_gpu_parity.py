@@ -542,6 +542,88 @@ def test_soar_exact_tie_blocks_match_oracle(seed, rows, cols):
     assert_exact(g, oracle.quantize(W, "soar", 0), "soar")
 
 
+def band_restart_model(W, r):
+    """binary32 model of the search's path choice: per block, whether its other reconstruct scale has a band
+    candidate (s_k within 2^-20 of s_d) whose scaled weights fail the 32-ulp test while the incumbent's pass the
+    8-ulp one (so the search certifies the incumbent, then walks the band window in k order); and the band
+    candidate's scale."""
+    alpha = np.float32(r["alpha"])
+    w = W.reshape(-1, 16).astype(np.float32)
+    dc = r["scales"].reshape(-1).astype(np.int64)
+    br = np.array([oracle.e4m3_bracket(v) for v in r["dstar"].reshape(-1)])
+    lo, hi = br[:, 0], br[:, 1]
+    ev = np.array([oracle.e4m3_value(int(c)) for c in range(127)], np.float32)
+    f = np.array([oracle.search_multiplier(k) for k in range(101)], np.float32)
+    pair = (dc > 0) & (lo != hi) & ((dc == lo) | (dc == hi))
+    vc, vo = ev[dc], ev[np.where(dc == lo, hi, lo)]
+
+    def far(x, margin):
+        u = x.view(np.uint32).astype(np.uint64)
+        return (((u + margin) << 11) & 0xFFFFFFFF).min(1) >= ((2 * margin + 1) << 11)
+
+    with np.errstate(divide="ignore"):
+        xc = (w * (np.float32(1) / (alpha * vc).astype(np.float32))[:, None]).astype(np.float32)
+        s = (alpha * (vc[:, None] * f[None, :]).astype(np.float32)).astype(np.float32)
+        in_band = np.abs(np.float64(alpha) * vo.astype(np.float64)[:, None] / s.astype(np.float64) - 1) <= 2.0 ** -20
+        sb = s[np.arange(len(s)), in_band.argmax(1)]
+        xb = (w * (np.float32(1) / sb)[:, None]).astype(np.float32)
+    band = pair & in_band.any(1)
+    return band & far(xc, 8) & ~far(xb, 32), band, sb
+
+
+def band_restart_rows(seed: int):
+    """fp32 rows whose search walks band windows in k order. Rows 8..15 are scaled by 1/64 (normal E4M3 scales,
+    a negligible share of alpha's sums). In each of their band blocks one element is set 3 binary32 ulps from
+    fl(1.75 s_b), s_b the band scale, on the side that puts its scaled value x_b and its quotient u = |w| / s_d
+    on opposite sides of the decision point 1.75: the band candidate's code for it is then not the nearest one,
+    and its 32-ulp test fails. The oracle is run again and the elements placed again, three times, until alpha
+    no longer moves."""
+    W = synth.student_t(synth.rng(seed, 11), 4.0, (16, 4096), 0.02).astype(np.float32)
+    W[8:] *= np.float32(1.0 / 64)
+    wb = W.reshape(-1, 16)
+    probe = np.arange(wb.shape[0]) >= wb.shape[0] // 2
+    slot = {}
+    for _ in range(3):
+        r = oracle.quantize(W, "soar", 3)
+        _, band, sb = band_restart_model(W, r)
+        alpha = np.float64(np.float32(r["alpha"]))
+        dc, dstar = r["scales"].reshape(-1), r["dstar"].reshape(-1)
+        for i in np.flatnonzero(band & probe):
+            lo, hi = oracle.e4m3_bracket(dstar[i])
+            sd = alpha * oracle.e4m3_value(int(hi if dc[i] == lo else lo))
+            up = sd > np.float64(sb[i])  # u = x_b s_b / s_d: below x_b when s_d > s_b
+            k = slot.setdefault(i, (int(np.argmax(np.abs(wb[i]))) + 1) % 16)
+            t = np.float32(1.75) * sb[i]
+            for _ in range(3):
+                t = np.nextafter(t, np.float32(np.inf) if up else np.float32(0), dtype=np.float32)
+            wb[i, k] = np.copysign(t, wb[i, k] if wb[i, k] != 0 else np.float32(1))
+    return W
+
+
+def test_soar_band_windows_walked_in_order_match_oracle():
+    """The search's band candidates whose codes cannot be certified: those lanes walk their three-candidate window
+    in k order after the other lanes' first candidate. The rows are built so that over a hundred blocks take that
+    path (the binary32 model says which; seeded workload rows almost never do), and so that in at least twenty of
+    them the other scale wins with codes that differ from the band candidate's: a search that took an uncertified
+    band candidate as its answer would get those blocks wrong."""
+    W = band_restart_rows(3)
+    r = oracle.quantize(W, "soar", 3)
+    walked, band, sb = band_restart_model(W, r)
+    xb = (W.reshape(-1, 16) * (np.float32(1) / sb)[:, None]).astype(np.float32)
+    band_codes = oracle.e2m1_codes(xb.reshape(-1)).reshape(-1, 16)
+    out_codes = oracle.unpack_codes(r["codes"]).reshape(-1, 16)
+    br = np.array([oracle.e4m3_bracket(v) for v in r["dstar"].reshape(-1)])
+    dc = oracle.quantize(W, "cjso", 3)["scales"].reshape(-1)  # the search's incumbent scales
+    other_won = r["scales"].reshape(-1) == np.where(dc == br[:, 0], br[:, 1], br[:, 0])
+    telling = walked & other_won & np.any(band_codes != out_codes, axis=1)
+    say(f"band lanes {int(band.sum())}, walked in order {int(walked.sum())}, telling {int(telling.sum())}")
+    assert walked.sum() >= 100 and telling.sum() >= 20
+    g = run(W, "soar", 3)
+    assert_exact(g, r, "soar")
+    f = run(W, "soar", 3, full_search=True)
+    assert_exact(f, r, "soar")
+
+
 # ------------------------------------------------------------------- CJSO / SOAR from FourOverSix
 
 INIT_CASES = {
