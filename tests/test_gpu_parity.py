@@ -665,7 +665,8 @@ SEARCH_CASES = {
 }
 SEARCHES = [((50, 100, 101), "quant"), ((50, 100, 101), "lsq"), ((1, 4, 7), "cjso"), ((100, 200, 201), "cjso"),
             ((1, 1, 16), "lsq"), ((45, 100, 13), "quant"), ((12345, 16777213, 9), "cjso"),
-            ((1, 20, 60), "lsq")]
+            ((1, 20, 60), "lsq"),
+            ((4473412, 4194304, 1024), "cjso")]  # steps of 2^-22 around 16/15: several candidates in a band window
 
 
 @pytest.mark.parametrize("grid,rule", SEARCHES)
@@ -678,7 +679,8 @@ def test_search_variants_match_oracle(name, grid, rule):
     assert_exact(g, r, "soar")
 
 
-@pytest.mark.parametrize("grid", [(1, 4, 7), (100, 200, 201), (12345, 16777213, 9), (1, 20, 60), (7, 7, 1)])
+@pytest.mark.parametrize("grid", [(1, 4, 7), (100, 200, 201), (12345, 16777213, 9), (1, 20, 60), (7, 7, 1),
+                                  (4473412, 4194304, 1024)])
 @pytest.mark.parametrize("name", ["c2_4096x4096", "coarse_1", "on_grid", "ragged_3x48"])
 def test_search_grid_window_equals_full_scan(name, grid):
     """The windowed search stays exact on other grids: it only needs the multipliers to increase."""
