@@ -30,6 +30,9 @@
 // first minimiser, unless that is K1 itself: then every k < K1 with A_d(k) = A_d(K1) has exactly the same
 // codes (a larger magnitude strictly raises psi_j there), so it only matters when the two reconstruct
 // scales tie exactly, and that rare case walks down to the first k with the codes of K1.
+// Two bit-pattern certificates shorten the common case: when the incumbent's scaled weights are all far
+// from the E2M1 decision points its own scale's window cannot beat it (eval_r_far), and a window
+// candidate within 2^-20 of s_d whose scaled weights are far from them ends its window alone (window_best).
 // The full scan over k remains for blocks outside the exactness window of the block sums or of
 // binary64 A_d, and for the two variant rules.
 #include <float.h>
