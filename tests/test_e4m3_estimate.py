@@ -12,7 +12,11 @@ Two shortcuts replace a binary64 division and rounding in the common case:
 A third one decides, in the decoupled search (soar_kernel.hip, eval_r_far), that a block's codes are the
 nearest E2M1 values of the exact quotients |w| / (alpha Delta): every computed x = fl(w fl(1/fl(alpha Delta)))
 (within 3 * 2^-24 of its quotient) must lie more than 8 binary32 ulps from every value whose low 21
-significand bits are zero, which every E2M1 decision point is.
+significand bits are zero, which every E2M1 decision point is. The search's band candidates (window_best)
+use the same test with a 32-ulp margin, for quotients within 2^-20 + 2^-23 + 2^-40 of x.
+
+Two exact rewrites are checked as well: the branch-free E4M3 decode (e4m3_value) over every code, and the
+search's test that every reciprocal is finite, !(0 < s <= 2^-128), against binary32 division.
 
 The device instructions are modelled here in numpy binary32 arithmetic, v_rcp_f32 as the correctly rounded
 reciprocal and one ulp either side of it. The reference is the E4M3 rule itself (nearest value, ties to
@@ -169,3 +173,27 @@ def test_e2m1_certificate_with_the_band_margin():
     u = x.astype(np.float64) / (1 - bound)
     assert not np.array_equal(e2m1_magnitude_code(u)[narrow], e2m1_magnitude_code(x)[narrow])
     assert far.mean() > 0.99
+
+
+def test_e4m3_decode_without_a_branch():
+    # e4m3_value (codec.hpp): a normal code c >= 8 is the binary32 pattern (c << 20) + 0x3C000000, a subnormal
+    # one c * 2^-9; against the format's definition for every code 0..126
+    c = np.arange(127, dtype=np.uint32)
+    normal = ((c << 20) + np.uint32(0x3C000000)).view(np.float32)
+    sub = c.astype(np.float32) * np.float32(2.0 ** -9)
+    got = np.where(c >= 8, normal, sub).astype(np.float64)
+    e, m = c // 8, c % 8
+    want = np.where(e > 0, (1 + m / 8.0) * 2.0 ** (e.astype(np.int64) - 7), m * 2.0 ** -9)
+    assert np.array_equal(got, want)
+    assert got[126] == 448.0 and got[8] == 2.0 ** -6 and got[1] == 2.0 ** -9
+
+
+def test_reciprocal_finite_exactly_above_two_to_minus_128():
+    # the search's "every reciprocal is finite" test, !(0 < s <= 2^-128), against fl(1/s) in binary32 over every
+    # binary32 value from 2^-131 to 2^-125 (and zero, whose reciprocal the search takes as 0)
+    lo, hi = np.float32(2.0 ** -131).view(np.uint32), np.float32(2.0 ** -125).view(np.uint32)
+    s = np.arange(int(lo), int(hi) + 1, dtype=np.uint32).view(np.float32)
+    with np.errstate(over="ignore", divide="ignore"):
+        finite = np.isfinite(np.float32(1) / s)
+        assert not np.isfinite(np.float32(1) / np.float32(2.0 ** -128))
+    assert np.array_equal(finite, ~((s > 0) & (s <= np.float32(2.0 ** -128))))
